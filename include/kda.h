@@ -1,0 +1,149 @@
+/*
+ * libkda — Kimi Delta Attention (KDA) forward on AMD MI355X (gfx950).
+ *
+ * C ABI. Plain pointers and sizes only; every tensor pointer is device memory
+ * owned by the caller. The library never allocates or frees device memory and
+ * never synchronises inside kda_chunk_fwd or kda_decode_step: all work is
+ * enqueued on the caller's HIP stream and the call returns at once.
+ *
+ * What is computed (FlashInfer "kda_backward" page, "Supported contract"; the
+ * kda-neuron-kernels commit log for the per-key-channel decay): for every
+ * sequence and head, a value-first fp32 state S[V][K] evolves token by token as
+ *
+ *   qh = q / sqrt(|q|^2 + 1e-6) * scale        kh = k / sqrt(|k|^2 + 1e-6)
+ *   alpha_c = exp(lower_bound * sigmoid(exp(A_log[h]) * (g_c + dt_bias[h,c])))
+ *   b = sigmoid(beta_raw)
+ *   S <- S diag(alpha)                          decay each key channel (column)
+ *   S <- S + b (v - S kh) kh^T                  delta-rule write
+ *   o  = S qh                                   read after the write
+ *
+ * Layouts (row-major, packed along the token axis, B = 1 for prefill):
+ *   q, k, g : [T, H, K]      v, o : [T, H, V]      beta_raw : [T, H]
+ *   A_log   : [H] fp32       dt_bias : [H, K] fp32
+ *   states  : [N, H, V, K] fp32 (value-first)
+ * K and V must both be 128 (the contract's head dimension). g, beta_raw,
+ * A_log, dt_bias and the states are always fp32; q, k and v share the input
+ * dtype; o has its own dtype.
+ *
+ * Errors: every entry point returns a status. Argument checks run on the host
+ * before any HIP call; a failed check enqueues nothing. kda_last_error() gives
+ * a human-readable detail for the last failure on the calling thread.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_INVALID_ARG = 1,   /* NULL pointer, negative size, bad scale or bound */
+    KDA_ERR_UNSUPPORTED = 2,   /* K or V != 128, chunk not in {16,32,64}, bad dtype */
+    KDA_ERR_WORKSPACE = 3,     /* workspace NULL or smaller than required */
+    KDA_ERR_HIP = 4            /* a HIP launch or runtime call failed */
+} kda_status_t;
+
+typedef enum {
+    KDA_F32 = 0,
+    KDA_BF16 = 1
+} kda_dtype_t;
+
+/* Library ABI version (major * 100 + minor). */
+int kda_version(void);
+
+/* Static text for a status code. */
+const char *kda_status_string(kda_status_t status);
+
+/* Detail of the last non-OK status returned on this thread ("" if none). */
+const char *kda_last_error(void);
+
+/*
+ * Bytes of device workspace kda_chunk_fwd needs for these sizes, or 0 if the
+ * arguments are invalid (then kda_last_error() says why). The workspace holds
+ * the per-chunk intermediates of the chunkwise form (one record per chunk slot
+ * and head; there are floor(T / chunk_size) + num_seqs slots) and is fully
+ * rewritten by every call, so it may be reused across calls on one stream.
+ */
+size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t num_seqs,
+                                    int32_t H, int32_t K, int32_t V,
+                                    int32_t chunk_size, kda_dtype_t in_dtype);
+
+/*
+ * Chunkwise prefill over packed variable-length sequences.
+ * (kimi_k3 FusedKDAChunkwise page, "Exact upstream call contract": the
+ * chunk_kda call with in-kernel L2 normalisation, gate and sigmoid beta, safe
+ * gate, lower bound, chunk size and value-first state; FlashInfer kda_backward
+ * page for dtypes, layouts and packed int64 offsets.)
+ *
+ * q, k, v      : [T, H, 128] in in_dtype (KDA_BF16 or KDA_F32)
+ * g            : [T, H, 128] fp32 raw gate;  beta_raw : [T, H] fp32
+ * A_log        : [H] fp32;  dt_bias : [H, 128] fp32
+ * scale        : output scale (> 0), normally 1/sqrt(128)
+ * lower_bound  : gate floor in [-5, 0); -5 in the contract
+ * cu_seqlens   : DEVICE pointer to num_seqs + 1 int64 offsets with cu[0] = 0,
+ *                non-decreasing, cu[num_seqs] = total_tokens. The values are a
+ *                precondition and are not checked here (see
+ *                kda_check_cu_seqlens); the kernels read them directly.
+ * initial_state: [num_seqs, H, 128, 128] fp32, or NULL for zero states
+ * final_state  : [num_seqs, H, 128, 128] fp32, or NULL to skip. May alias
+ *                initial_state (each workgroup reads its slice before writing).
+ * o            : [T, H, 128] in o_dtype (KDA_BF16 or KDA_F32), rounded to
+ *                nearest even when bf16
+ * chunk_size   : 16, 32 or 64 (the model validator admits 32 and 64; 16 is
+ *                also accepted). The result does not depend on it beyond
+ *                rounding.
+ * workspace    : device memory of at least kda_chunk_fwd_workspace_size(...)
+ *                bytes, 256-byte aligned; contents on entry are ignored.
+ * stream       : hipStream_t to enqueue on (NULL = default stream).
+ * A zero-length sequence writes no output rows and copies its initial state
+ * (or zeros) to its final state. total_tokens = 0 is allowed.
+ */
+kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v,
+                           const float *g, const float *beta_raw,
+                           const float *A_log, const float *dt_bias,
+                           float scale, float lower_bound,
+                           const int64_t *cu_seqlens, int32_t num_seqs,
+                           int64_t total_tokens, int32_t H, int32_t K, int32_t V,
+                           int32_t chunk_size, kda_dtype_t in_dtype,
+                           const float *initial_state, float *final_state,
+                           void *o, kda_dtype_t o_dtype,
+                           void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
+ * One T=1 decode step for B independent requests, all heads in one launch.
+ * (kda-neuron-kernels commit log: batched multi-(request, head) decode and the
+ * one-pass "key-fold" recurrent step; same transforms as above.)
+ *
+ * q, k, v  : [B, H, 128] in in_dtype;  g : [B, H, 128] fp32;  beta_raw : [B, H]
+ * state    : [B, H, 128, 128] fp32, read and updated in place
+ * o        : [B, H, 128] in o_dtype
+ * The state is read once and written once per step.
+ */
+kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
+                             const float *g, const float *beta_raw,
+                             const float *A_log, const float *dt_bias,
+                             float scale, float lower_bound,
+                             float *state, void *o, kda_dtype_t o_dtype,
+                             int32_t B, int32_t H, int32_t K, int32_t V,
+                             kda_dtype_t in_dtype, void *stream);
+
+/*
+ * Opt-in check of packed offsets (FlashInfer kda_backward page: offsets are
+ * validated by one eager synchronisation, the launch path then trusts them).
+ * Copies cu_seqlens to the host on `stream`, synchronises that stream and
+ * returns KDA_OK if cu[0] == 0, the values never decrease and
+ * cu[num_seqs] == total_tokens, else KDA_ERR_INVALID_ARG.
+ */
+kda_status_t kda_check_cu_seqlens(const int64_t *cu_seqlens, int32_t num_seqs,
+                                  int64_t total_tokens, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */
