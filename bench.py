@@ -1,0 +1,242 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA forward hot path on one MI355X.
+
+One step = the whole path once: a chunkwise prefill of T=8192 tokens x H=96
+heads (bf16 q/k/v, chunk 64, random fp32 initial states; intra-chunk kernel
+then inter-chunk kernel) followed by one batched decode step of 256 requests x
+32 heads (fp32 state updated in place). Decode inputs cycle through 64
+pre-generated token sets (64 consecutive steps). Inputs are seeded synthetic
+tensors already resident in HBM when timing starts.
+
+Prints one JSON line: value = tokens processed per second over the timed steps
+(8192 prefill + 256 decode tokens per step), per-kernel HIP-event timings, the
+roofline of the dominant kernel and of each kernel, and the fp64 CPU oracle
+timed on the host as a baseline.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
+D = 128
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_sha(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "kimi_delta_attention_05_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "intra_kernel": ("kda_prefill.hip", "kda_common.h", "kda_internal.h"),
+    "inter_kernel": ("kda_prefill.hip", "kda_common.h", "kda_internal.h"),
+    "decode_step_kernel": ("kda_decode.hip", "kda_common.h", "kda_internal.h"),
+}
+
+
+def measured_traffic(kernel):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE
+    summary, or None when absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f).get(kernel)
+    except (OSError, ValueError):
+        return None
+    if not t or t.get("source_sha") != source_sha(*KERNEL_SOURCES[kernel]):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def prefill_flops_per_token_head(C):
+    # W S^T, qg S^T, state update (2 d^2 each); A; M; T v; T (k e^G); M U; inverse
+    return 6 * D * D + (C - 1) * D + 4 * (C + 1) * D + C * C / 3.0
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (--gpus 1); multi-GPU runs are "
+              "not part of it", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import kda_inputs
+    import kimi_delta_attention_05_amd as kda
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log("generating inputs ...")
+    p = kda_inputs.large()
+    dd = kda_inputs.decode(64)
+    T, H, N, C = p.T, p.H, p.N, p.chunk
+    q, k, v = p.q.to(dev), p.k.to(dev), p.v.to(dev)
+    g, beta_raw = p.g.to(dev), p.beta_raw.to(dev)
+    A_log, dt_bias, cu = p.A_log.to(dev), p.dt_bias.to(dev), p.cu_seqlens.to(dev)
+    h0 = p.h0.to(dev)
+    o = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    ht = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    ws = kda.Workspace(dev)
+    B, HD = 256, 32
+    dstate = dd.state.to(dev)
+    dA, ddt = dd.A_log.to(dev), dd.dt_bias.to(dev)
+    dsteps = [{kk: vv.to(dev) for kk, vv in st.items()} for st in dd.steps]
+    dout = torch.empty((B, HD, D), dtype=torch.bfloat16, device=dev)
+    torch.cuda.synchronize()
+
+    def prefill(stage):
+        kda.chunk_fwd(q, k, v, g, beta_raw, A_log, dt_bias, cu, scale=p.scale, chunk_size=C,
+                      initial_state=h0, out=o, final_state=ht, workspace=ws, stage=stage)
+
+    def decode(i):
+        st = dsteps[i % len(dsteps)]
+        kda.decode_step(st["q"], st["k"], st["v"], st["g"], st["beta_raw"], dA, ddt, dstate,
+                        scale=dd.scale, out=dout)
+
+    def step(i, ev=None):
+        if ev is not None:
+            ev[0].record()
+        prefill("intra")
+        if ev is not None:
+            ev[1].record()
+        prefill("inter")
+        if ev is not None:
+            ev[2].record()
+        decode(i)
+        if ev is not None:
+            ev[3].record()
+
+    log("warmup %d steps ..." % args.warmup)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    log("timed %d steps in %.3f s" % (K, wall))
+
+    intra_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / K
+    inter_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / K
+    decode_ms = sum(e[2].elapsed_time(e[3]) for e in evs) / K
+    prefill_ms = intra_ms + inter_ms
+
+    th = T * H
+    kernels = {
+        # algorithmic bytes each kernel must move: inputs it reads, outputs it writes
+        "intra_kernel": dict(ms=intra_ms, bytes=th * (3 * 2 * D + 4 * D + 4)),
+        "inter_kernel": dict(ms=inter_ms, bytes=th * 2 * D + 2 * N * H * D * D * 4),
+        "decode_step_kernel": dict(ms=decode_ms, bytes=B * HD * (2 * D * D * 4 + 3 * 2 * D + 4 * D + 4
+                                                                 + 2 * D)),
+    }
+    for name, kd in kernels.items():
+        kd["achieved_GBs"] = kd["bytes"] / (kd["ms"] * 1e-3) / 1e9
+        kd["frac"] = kd["achieved_GBs"] / HBM_PEAK_GBS
+        kd["traffic"] = measured_traffic(name)
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    kd = kernels[dom]
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(kd["achieved_GBs"], 1),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(kd["frac"], 4),
+                "traffic": kd["traffic"]}
+
+    prefill_bytes = th * (4 * 2 * D + 4 * D + 4) + 2 * N * H * D * D * 4
+    prefill_flops = th * prefill_flops_per_token_head(C)
+    tokens_per_step = T + B
+    value = tokens_per_step * K / wall
+
+    line = {
+        "metric": "KDA fwd tokens/s (T=8192,H=96 prefill; decode bs=256) + % MFMA/HBM roofline",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall / K * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in; fp16 MFMA operands, fp32 accumulate/state",
+        "data": "synthetic (seeded N(0,1) tokens, N(0,2^2) gates, U(0,ln16) A_log, U(-1,1) dt_bias)",
+        "config": {"workload": "prefill T=8192 H=96 K=V=128 chunk 64 bf16 + decode B=256 H=32 "
+                               "T=1, one of each per step",
+                   "prefill_tokens_per_step": T, "decode_tokens_per_step": B,
+                   "heads_prefill": H, "heads_decode": HD, "chunk": C},
+        "prefill": {"ms": round(prefill_ms, 4), "tokens_per_s": round(T / (prefill_ms * 1e-3), 1),
+                    "hbm_frac_path": round(prefill_bytes / (prefill_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "mfma_frac_path": round(prefill_flops / (prefill_ms * 1e-3) / 1e12
+                                            / MFMA_BF16_PEAK_TFLOPS, 4)},
+        "decode": {"us": round(decode_ms * 1e3, 2), "tokens_per_s": round(B / (decode_ms * 1e-3), 1),
+                   "hbm_frac": round(kernels["decode_step_kernel"]["frac"], 4)},
+        "kernels": {n: {"us": round(x["ms"] * 1e3, 2), "alg_bytes": int(x["bytes"]),
+                        "achieved_GBs": round(x["achieved_GBs"], 1), "frac": round(x["frac"], 4),
+                        "traffic": x["traffic"]} for n, x in kernels.items()},
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(p, dd)
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline(p, dd):
+    """The fp64 oracle as it stands, on the host cores: the same prefill
+    (T=8192, H=96) once and two decode steps of the same batch."""
+    import numpy as np
+    import torch
+    import oracle
+    f32 = lambda x: np.ascontiguousarray(x.float().numpy())
+    args = [f32(x) for x in (p.q, p.k, p.v, p.g, p.beta_raw, p.A_log, p.dt_bias)]
+    h0 = p.h0.double().numpy()
+    cu = p.cu_seqlens.numpy()
+    threads = oracle.max_threads()
+    log("cpu baseline: oracle prefill on %d threads ..." % threads)
+    t0 = time.perf_counter()
+    oracle.kda_recurrent(*args, cu, scale=p.scale, h0=h0)
+    t_prefill = time.perf_counter() - t0
+    state = dd.state.double().numpy()
+    B = state.shape[0]
+    cud = np.arange(B + 1, dtype=np.int64)
+    dsteps = [[f32(st[n]) for n in ("q", "k", "v", "g", "beta_raw")] for st in dd.steps[:2]]
+    dA, ddt = f32(dd.A_log), f32(dd.dt_bias)
+    log("cpu baseline: oracle decode ...")
+    t0 = time.perf_counter()
+    for st in dsteps:
+        _, state = oracle.kda_recurrent(*st, dA, ddt, cud, scale=dd.scale, h0=state)
+    t_decode = (time.perf_counter() - t0) / len(dsteps)
+    tokens = p.T + B
+    return {"value": round(tokens / (t_prefill + t_decode), 1), "unit": "tokens/s",
+            "cores": threads, "kind": "oracle",
+            "sample": "one full prefill T=8192 H=96 (%.2f s) + mean of 2 decode steps "
+                      "B=256 H=32 (%.2f s/step), fp64, OpenMP over (sequence, head) chains"
+                      % (t_prefill, t_decode)}
+
+
+if __name__ == "__main__":
+    main()

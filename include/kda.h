@@ -115,6 +115,41 @@ kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v,
                            void *stream);
 
 /*
+ * The two stages of kda_chunk_fwd, callable separately with the same
+ * arguments and the same workspace (kda_chunk_fwd = intra, then inter, on one
+ * stream). kda_chunk_fwd_intra reads q, k, v, g, beta_raw, A_log, dt_bias and
+ * cu_seqlens and fills the workspace with the per-chunk intermediates; it is
+ * parallel over all chunks and heads. kda_chunk_fwd_inter reads the workspace,
+ * cu_seqlens and initial_state and writes o and final_state; it walks the
+ * chunks of each sequence in order (the "all chunks in one launch, state kept
+ * on chip" design of the kda-neuron-kernels fused chunked forward). Between
+ * the two calls the workspace must not be modified. Splitting lets a caller
+ * overlap the intra stage with other work or time the stages separately.
+ */
+kda_status_t kda_chunk_fwd_intra(const void *q, const void *k, const void *v,
+                                 const float *g, const float *beta_raw,
+                                 const float *A_log, const float *dt_bias,
+                                 float scale, float lower_bound,
+                                 const int64_t *cu_seqlens, int32_t num_seqs,
+                                 int64_t total_tokens, int32_t H, int32_t K, int32_t V,
+                                 int32_t chunk_size, kda_dtype_t in_dtype,
+                                 const float *initial_state, float *final_state,
+                                 void *o, kda_dtype_t o_dtype,
+                                 void *workspace, size_t workspace_bytes,
+                                 void *stream);
+kda_status_t kda_chunk_fwd_inter(const void *q, const void *k, const void *v,
+                                 const float *g, const float *beta_raw,
+                                 const float *A_log, const float *dt_bias,
+                                 float scale, float lower_bound,
+                                 const int64_t *cu_seqlens, int32_t num_seqs,
+                                 int64_t total_tokens, int32_t H, int32_t K, int32_t V,
+                                 int32_t chunk_size, kda_dtype_t in_dtype,
+                                 const float *initial_state, float *final_state,
+                                 void *o, kda_dtype_t o_dtype,
+                                 void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/*
  * One T=1 decode step for B independent requests, all heads in one launch.
  * (kda-neuron-kernels commit log: batched multi-(request, head) decode and the
  * one-pass "key-fold" recurrent step; same transforms as above.)

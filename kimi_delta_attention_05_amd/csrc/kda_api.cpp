@@ -1,0 +1,215 @@
+// libkda C ABI: argument validation (host only, before any HIP call),
+// workspace sizing and kernel launches. See include/kda.h for the contract.
+#include "kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <string>
+#include <vector>
+
+#include "kda_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kda_status_t fail(kda_status_t st, const std::string &msg) {
+    g_last_error = msg;
+    return st;
+}
+
+kda_status_t ok() {
+    g_last_error.clear();
+    return KDA_OK;
+}
+
+bool valid_dtype(kda_dtype_t d) { return d == KDA_F32 || d == KDA_BF16; }
+
+// Checks shared by both entry points. Returns KDA_OK or an error with detail.
+kda_status_t check_common(int64_t H, int32_t K, int32_t V, float scale, float lower_bound,
+                          kda_dtype_t in_dtype, kda_dtype_t o_dtype) {
+    if (H < 1) return fail(KDA_ERR_INVALID_ARG, "H must be >= 1");
+    if (K != 128 || V != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "only K = V = 128 is supported (got K=" +
+                                             std::to_string(K) + ", V=" + std::to_string(V) + ")");
+    if (!(scale > 0.0f) || !std::isfinite(scale))
+        return fail(KDA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (!(lower_bound >= -5.0f && lower_bound < 0.0f))
+        return fail(KDA_ERR_INVALID_ARG, "lower_bound must lie in [-5, 0)");
+    if (!valid_dtype(in_dtype)) return fail(KDA_ERR_UNSUPPORTED, "unknown input dtype");
+    if (!valid_dtype(o_dtype)) return fail(KDA_ERR_UNSUPPORTED, "unknown output dtype");
+    return KDA_OK;
+}
+
+kda_status_t hip_fail(hipError_t e, const char *where) {
+    return fail(KDA_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_version(void) { return 100; }
+
+const char *kda_status_string(kda_status_t s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_INVALID_ARG: return "invalid argument";
+        case KDA_ERR_UNSUPPORTED: return "unsupported configuration";
+        case KDA_ERR_WORKSPACE: return "workspace missing or too small";
+        case KDA_ERR_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char *kda_last_error(void) { return g_last_error.c_str(); }
+
+size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H,
+                                    int32_t K, int32_t V, int32_t chunk_size,
+                                    kda_dtype_t in_dtype) {
+    if (total_tokens < 0 || num_seqs < 1 || H < 1) {
+        fail(KDA_ERR_INVALID_ARG, "need total_tokens >= 0, num_seqs >= 1, H >= 1");
+        return 0;
+    }
+    if (K != 128 || V != 128) { fail(KDA_ERR_UNSUPPORTED, "only K = V = 128 is supported"); return 0; }
+    if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) {
+        fail(KDA_ERR_UNSUPPORTED, "chunk_size must be 16, 32 or 64");
+        return 0;
+    }
+    if (!valid_dtype(in_dtype)) { fail(KDA_ERR_UNSUPPORTED, "unknown input dtype"); return 0; }
+    const size_t rec = kda::record_bytes(chunk_size, in_dtype == KDA_F32);
+    const int64_t slots = kda::num_slots(total_tokens, num_seqs, chunk_size);
+    g_last_error.clear();
+    return (size_t)slots * (size_t)H * rec + 256;
+}
+
+}  // extern "C"
+
+namespace {
+
+kda_status_t chunk_fwd_stages(int stages, const char *name,
+                              const void *q, const void *k, const void *v,
+                              const float *g, const float *beta_raw,
+                              const float *A_log, const float *dt_bias,
+                              float scale, float lower_bound,
+                              const int64_t *cu_seqlens, int32_t num_seqs,
+                              int64_t total_tokens, int32_t H, int32_t K, int32_t V,
+                              int32_t chunk_size, kda_dtype_t in_dtype,
+                              const float *initial_state, float *final_state,
+                              void *o, kda_dtype_t o_dtype,
+                              void *workspace, size_t workspace_bytes,
+                              void *stream) {
+    if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 1");
+    if (total_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens must be >= 0");
+    kda_status_t st = check_common(H, K, V, scale, lower_bound, in_dtype, o_dtype);
+    if (st != KDA_OK) return st;
+    if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64)
+        return fail(KDA_ERR_UNSUPPORTED, "chunk_size must be 16, 32 or 64");
+    if (!cu_seqlens || !A_log || !dt_bias)
+        return fail(KDA_ERR_INVALID_ARG, "cu_seqlens, A_log and dt_bias must not be NULL");
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta_raw || !o))
+        return fail(KDA_ERR_INVALID_ARG, "q, k, v, g, beta_raw and o must not be NULL");
+    if ((int64_t)num_seqs * H > (int64_t)1 << 28)
+        return fail(KDA_ERR_INVALID_ARG, "num_seqs * H too large");
+    if (kda::num_slots(total_tokens, num_seqs, chunk_size) > ((int64_t)1 << 31) - 1)
+        return fail(KDA_ERR_INVALID_ARG, "too many chunks for one launch");
+    const size_t need = kda_chunk_fwd_workspace_size(total_tokens, num_seqs, H, K, V, chunk_size,
+                                                     in_dtype);
+    if (!workspace || workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes, got " +
+                                           std::to_string(workspace_bytes));
+    if (((uintptr_t)workspace & 255) != 0)
+        return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+
+    kda::PrefillArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta_raw = beta_raw; a.A_log = A_log; a.dt_bias = dt_bias;
+    a.scale = scale; a.lower_bound = lower_bound;
+    a.cu_seqlens = cu_seqlens; a.N = num_seqs; a.T = total_tokens; a.H = H; a.chunk = chunk_size;
+    a.h0 = initial_state; a.ht = final_state; a.o = o;
+    a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = o_dtype == KDA_BF16;
+    a.ws = (unsigned char *)workspace;
+    a.stream = (hipStream_t)stream;
+    a.stages = stages;
+    hipError_t e = kda::launch_prefill(a);
+    if (e != hipSuccess) return hip_fail(e, name);
+    return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+#define KDA_CHUNK_ARGS                                                                     \
+    q, k, v, g, beta_raw, A_log, dt_bias, scale, lower_bound, cu_seqlens, num_seqs,       \
+        total_tokens, H, K, V, chunk_size, in_dtype, initial_state, final_state, o,        \
+        o_dtype, workspace, workspace_bytes, stream
+#define KDA_CHUNK_PARAMS                                                                   \
+    const void *q, const void *k, const void *v, const float *g, const float *beta_raw,    \
+        const float *A_log, const float *dt_bias, float scale, float lower_bound,          \
+        const int64_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens, int32_t H,      \
+        int32_t K, int32_t V, int32_t chunk_size, kda_dtype_t in_dtype,                    \
+        const float *initial_state, float *final_state, void *o, kda_dtype_t o_dtype,      \
+        void *workspace, size_t workspace_bytes, void *stream
+
+kda_status_t kda_chunk_fwd(KDA_CHUNK_PARAMS) {
+    return chunk_fwd_stages(3, "kda_chunk_fwd", KDA_CHUNK_ARGS);
+}
+
+kda_status_t kda_chunk_fwd_intra(KDA_CHUNK_PARAMS) {
+    return chunk_fwd_stages(1, "kda_chunk_fwd_intra", KDA_CHUNK_ARGS);
+}
+
+kda_status_t kda_chunk_fwd_inter(KDA_CHUNK_PARAMS) {
+    return chunk_fwd_stages(2, "kda_chunk_fwd_inter", KDA_CHUNK_ARGS);
+}
+
+kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
+                             const float *g, const float *beta_raw,
+                             const float *A_log, const float *dt_bias,
+                             float scale, float lower_bound,
+                             float *state, void *o, kda_dtype_t o_dtype,
+                             int32_t B, int32_t H, int32_t K, int32_t V,
+                             kda_dtype_t in_dtype, void *stream) {
+    if (B < 1) return fail(KDA_ERR_INVALID_ARG, "B must be >= 1");
+    kda_status_t st = check_common(H, K, V, scale, lower_bound, in_dtype, o_dtype);
+    if (st != KDA_OK) return st;
+    if (!q || !k || !v || !g || !beta_raw || !A_log || !dt_bias || !state || !o)
+        return fail(KDA_ERR_INVALID_ARG, "a required pointer is NULL");
+    if ((int64_t)B * H > ((int64_t)1 << 31) - 1)
+        return fail(KDA_ERR_INVALID_ARG, "B * H too large");
+    if (((uintptr_t)state & 15) != 0)
+        return fail(KDA_ERR_INVALID_ARG, "state must be 16-byte aligned");
+
+    kda::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta_raw = beta_raw; a.A_log = A_log; a.dt_bias = dt_bias;
+    a.scale = scale; a.lower_bound = lower_bound; a.state = state; a.o = o;
+    a.B = B; a.H = H; a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = o_dtype == KDA_BF16;
+    a.stream = (hipStream_t)stream;
+    hipError_t e = kda::launch_decode(a);
+    if (e != hipSuccess) return hip_fail(e, "kda_decode_step launch");
+    return ok();
+}
+
+kda_status_t kda_check_cu_seqlens(const int64_t *cu_seqlens, int32_t num_seqs,
+                                  int64_t total_tokens, void *stream) {
+    if (!cu_seqlens || num_seqs < 1 || total_tokens < 0)
+        return fail(KDA_ERR_INVALID_ARG, "need cu_seqlens != NULL, num_seqs >= 1, total_tokens >= 0");
+    std::vector<int64_t> h((size_t)num_seqs + 1);
+    hipStream_t s = (hipStream_t)stream;
+    hipError_t e = hipMemcpyAsync(h.data(), cu_seqlens, h.size() * sizeof(int64_t),
+                                  hipMemcpyDeviceToHost, s);
+    if (e != hipSuccess) return hip_fail(e, "kda_check_cu_seqlens copy");
+    e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e, "kda_check_cu_seqlens sync");
+    if (h[0] != 0) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens[0] != 0");
+    for (int32_t i = 0; i < num_seqs; ++i)
+        if (h[i + 1] < h[i])
+            return fail(KDA_ERR_INVALID_ARG, "cu_seqlens decreases at index " + std::to_string(i));
+    if (h[num_seqs] != total_tokens)
+        return fail(KDA_ERR_INVALID_ARG, "cu_seqlens[num_seqs] != total_tokens");
+    return ok();
+}
+
+}  // extern "C"

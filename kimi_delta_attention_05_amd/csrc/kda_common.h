@@ -1,0 +1,156 @@
+// Internal helpers shared by the libkda kernels (gfx950 / CDNA4, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kHeadDim = 128;          // K = V = 128 (the contract's only head size)
+constexpr float kL2Eps = 1e-6f;        // q/k L2 normalisation epsilon
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ---- element conversion ------------------------------------------------------
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(__bf16 x) { return static_cast<float>(x); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) {
+    return static_cast<__bf16>(x);      // round to nearest even
+}
+template <> __device__ __forceinline__ _Float16 from_f32<_Float16>(float x) {
+    return static_cast<_Float16>(x);    // round to nearest even
+}
+
+// 2^x and 1/x on the hardware transcendental unit.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// Logistic function for any finite x: exp2 of a non-positive argument only.
+__device__ __forceinline__ float sigmoid_f(float x) {
+    float z = fast_exp2(-fabsf(x) * kLog2e);          // in (0, 1]
+    float r = fast_rcp(1.0f + z);
+    return x >= 0.0f ? r : z * r;
+}
+
+// ---- cross-lane reductions ---------------------------------------------------
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane of the row gets the sum.
+__device__ __forceinline__ float row16_sum(float x) {
+    x += dpp_f<0xB1>(x);    // quad_perm [1,0,3,2]
+    x += dpp_f<0x4E>(x);    // quad_perm [2,3,0,1]
+    x += dpp_f<0x141>(x);   // row_half_mirror
+    x += dpp_f<0x140>(x);   // row_mirror
+    return x;
+}
+
+// Max of |x| over the 16 lanes of a DPP row.
+__device__ __forceinline__ float row16_max(float x) {
+    x = fmaxf(x, dpp_f<0xB1>(x));
+    x = fmaxf(x, dpp_f<0x4E>(x));
+    x = fmaxf(x, dpp_f<0x141>(x));
+    x = fmaxf(x, dpp_f<0x140>(x));
+    return x;
+}
+
+// Max over all 64 lanes of the wave (every lane gets it).
+__device__ __forceinline__ float wave_max(float x) {
+    x = row16_max(x);
+    x = fmaxf(x, __shfl_xor(x, 16));
+    x = fmaxf(x, __shfl_xor(x, 32));
+    return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+    x = row16_sum(x);
+    x += __shfl_xor(x, 16);
+    x += __shfl_xor(x, 32);
+    return x;
+}
+
+// ---- MFMA 16x16x32 -----------------------------------------------------------
+//
+// A fragment: lane l holds row (l % 16) and 8 k-values; B fragment: lane l holds
+// column (l % 16) and 8 k-values; lanes l and l' with the same l / 16 pair their
+// k-values position by position, so any fixed assignment of logical k to
+// (l / 16, position) gives the same product. Accumulator: lane l holds
+// D[4 * (l / 16) + i][l % 16] for i = 0..3.
+//
+// The k order used throughout libkda for operands that also come out of an
+// accumulator is  k(g, e) = (e < 4) ? 4g + e : 16 + 4g + (e - 4)  within each
+// 32-wide k-step, g = l / 16: it is exactly what two vertically stacked 16x16
+// accumulator tiles hold in one lane.
+
+__device__ __forceinline__ int kperm(int g, int e) {
+    return (e < 4) ? (4 * g + e) : (16 + 4 * g + (e - 4));
+}
+
+__device__ __forceinline__ f32x4 mfma_f16(const float (&a)[8], const float (&b)[8], f32x4 acc) {
+    half8 ha, hb;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { ha[e] = (_Float16)a[e]; hb[e] = (_Float16)b[e]; }
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(ha, hb, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_h(const half8 &a, const half8 &b, f32x4 acc) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc, 0, 0, 0);
+}
+
+// Three-product bf16 split: x = hi + lo with hi = bf16(x), lo = bf16(x - hi);
+// a.b ~= ah.bh + ah.bl + al.bh (relative error ~2^-16, full fp32 exponent range).
+__device__ __forceinline__ f32x4 mfma_x3(const float (&a)[8], const float (&b)[8], f32x4 acc) {
+    bf16x8 ah, al, bh, bl;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        __bf16 t = (__bf16)a[e]; ah[e] = t; al[e] = (__bf16)(a[e] - (float)t);
+        __bf16 u = (__bf16)b[e]; bh[e] = u; bl[e] = (__bf16)(b[e] - (float)u);
+    }
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, acc, 0, 0, 0);
+    return acc;
+}
+
+// fp32 product on the fp32 MFMA (v_mfma_f32_16x16x4f32): each of the 8
+// positions is one 4-deep step across the four lane groups, so the 8 calls
+// together cover the same 32 k-values in the same pairing as above.
+__device__ __forceinline__ f32x4 mfma_f32x8(const float (&a)[8], const float (&b)[8], f32x4 acc) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[e], b[e], acc, 0, 0, 0);
+    return acc;
+}
+
+// 8 consecutive elements as fp32 (16- or 32-byte vector loads).
+__device__ __forceinline__ void load8(const float *p, float (&x)[8]) {
+    const f32x4 a = ((const f32x4 *)p)[0], b = ((const f32x4 *)p)[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[e + 4] = b[e]; }
+}
+__device__ __forceinline__ void load8(const __bf16 *p, float (&x)[8]) {
+    const bf16x8 a = *(const bf16x8 *)p;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
+}
+
+// Power of two 2^e with e = ceil(log2(m)) - target, so that m * 2^-e <= 2^target;
+// returns 1 for m == 0 or non-finite m.
+__device__ __forceinline__ float pow2_scale_for(float m, int target) {
+    if (!(m > 0.0f) || !(m < 3.0e38f)) return 1.0f;
+    int e = ((int)((__float_as_uint(m) >> 23) & 0xFF)) - 127 + 1 - target;
+    e = e < -126 ? -126 : (e > 127 ? 127 : e);
+    return __uint_as_float((uint32_t)(e + 127) << 23);
+}
+
+}  // namespace kda

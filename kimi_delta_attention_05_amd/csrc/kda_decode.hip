@@ -1,0 +1,121 @@
+// Batched T=1 KDA decode step: one workgroup per (request, head), one pass
+// over the fp32 state.
+//
+// Per (request b, head h) the value-first state S[128][128] is read once and
+// written once. Every state row v is independent given the per-token vectors:
+//   s   = S[v,:] * alpha                 (decay per key channel)
+//   a_v = s . qh,   p_v = s . kh         (both dot products in the same pass)
+//   u_v = beta (v_v - p_v)
+//   S[v,:] = s + u_v kh                  (delta-rule write, in place)
+//   o_v = a_v + u_v (kh . qh)            (= (S_new qh)_v, read after the write)
+// Folding the read-out into the update pass through the scalar kh.qh is the
+// one-pass "key-fold" reading of the kda-neuron-kernels commit log's recurrent
+// forward; batching every (request, head) pair into one launch follows its
+// batched decode. Transforms per the FlashInfer kda_backward contract.
+//
+// Thread layout: 256 threads = 4 waves; a DPP row of 16 lanes covers one state
+// row (8 consecutive fp32 per lane, two 16-byte loads); a wave covers 4 rows, the
+// workgroup 16 rows per iteration, 8 iterations for the 128 rows. All 16 loads of
+// a lane are issued before any arithmetic so that 64 KB per workgroup is in flight.
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <typename Tin, typename Tout>
+__global__ __launch_bounds__(256) void decode_step_kernel(
+    const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
+    const float *__restrict__ g, const float *__restrict__ beta_raw,
+    const float *__restrict__ A_log, const float *__restrict__ dt_bias,
+    float scale, float lower_bound, float *__restrict__ state, Tout *__restrict__ o,
+    int H)
+{
+    const int bh = blockIdx.x;                 // request * H + head
+    const int h = bh % H;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int j = lane & 15;                   // channel group: channels 8j .. 8j+7
+    const int r = lane >> 4;                   // row within the wave's 4 rows
+    const int c0 = 8 * j;
+
+    f32x4 *S4 = reinterpret_cast<f32x4 *>(state + (size_t)bh * (kHeadDim * kHeadDim));
+
+    // Issue the state loads first: rows 16*it + 4*wave + r, columns c0..c0+7.
+    f32x4 st[8][2];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int row = 16 * it + 4 * wave + r;
+        st[it][0] = __builtin_nontemporal_load(S4 + row * 32 + 2 * j);
+        st[it][1] = __builtin_nontemporal_load(S4 + row * 32 + 2 * j + 1);
+    }
+
+    // Per-token vectors for this lane's 8 channels (each 16-lane row holds all 128).
+    const size_t tb = (size_t)bh * kHeadDim;
+    float qv[8], kv[8], al[8];
+    const float a_gate = fast_exp2(A_log[h] * kLog2e);
+    float sqq = 0.f, skk = 0.f, sqk = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        qv[e] = to_f32(q[tb + c0 + e]);
+        kv[e] = to_f32(k[tb + c0 + e]);
+        sqq += qv[e] * qv[e];
+        skk += kv[e] * kv[e];
+        sqk += qv[e] * kv[e];
+        const float x = a_gate * (g[tb + c0 + e] + dt_bias[h * kHeadDim + c0 + e]);
+        al[e] = fast_exp2(lower_bound * sigmoid_f(x) * kLog2e);   // alpha = e^lambda
+    }
+    sqq = row16_sum(sqq);
+    skk = row16_sum(skk);
+    sqk = row16_sum(sqk);
+    const float rq = rsqrtf(sqq + kL2Eps) * scale;
+    const float rk = rsqrtf(skk + kL2Eps);
+    const float kq = sqk * rq * rk;                                // kh . qh
+    float qh[8], kh[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { qh[e] = qv[e] * rq; kh[e] = kv[e] * rk; }
+    const float beta = sigmoid_f(beta_raw[bh]);
+
+    float vrow[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) vrow[it] = to_f32(v[tb + 16 * it + 4 * wave + r]);
+
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int row = 16 * it + 4 * wave + r;
+        float s[8] = {st[it][0][0], st[it][0][1], st[it][0][2], st[it][0][3],
+                      st[it][1][0], st[it][1][1], st[it][1][2], st[it][1][3]};
+        float a = 0.f, p = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            s[e] *= al[e];
+            a += s[e] * qh[e];
+            p += s[e] * kh[e];
+        }
+        a = row16_sum(a);
+        p = row16_sum(p);
+        const float u = beta * (vrow[it] - p);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s[e] += u * kh[e];
+        const f32x4 s0 = {s[0], s[1], s[2], s[3]}, s1 = {s[4], s[5], s[6], s[7]};
+        __builtin_nontemporal_store(s0, S4 + row * 32 + 2 * j);
+        __builtin_nontemporal_store(s1, S4 + row * 32 + 2 * j + 1);
+        if (j == 0) o[tb + row] = from_f32<Tout>(a + u * kq);
+    }
+}
+
+template <typename Tin, typename Tout>
+static hipError_t launch_decode_t(const DecodeArgs &a) {
+    dim3 grid((unsigned)(a.B * a.H));
+    decode_step_kernel<Tin, Tout><<<grid, 256, 0, a.stream>>>(
+        (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v, a.g, a.beta_raw,
+        a.A_log, a.dt_bias, a.scale, a.lower_bound, a.state, (Tout *)a.o, a.H);
+    return hipGetLastError();
+}
+
+hipError_t launch_decode(const DecodeArgs &a) {
+    if (a.in_bf16)
+        return a.out_bf16 ? launch_decode_t<__bf16, __bf16>(a) : launch_decode_t<__bf16, float>(a);
+    return a.out_bf16 ? launch_decode_t<float, __bf16>(a) : launch_decode_t<float, float>(a);
+}
+
+}  // namespace kda

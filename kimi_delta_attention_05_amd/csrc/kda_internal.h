@@ -1,0 +1,83 @@
+// Internal interfaces of libkda: launch arguments and the workspace record layout.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const float *g, *beta_raw, *A_log, *dt_bias;
+    float scale, lower_bound;
+    float *state;
+    void *o;
+    int B, H;
+    bool in_bf16, out_bf16;
+    hipStream_t stream;
+};
+
+struct PrefillArgs {
+    const void *q, *k, *v;
+    const float *g, *beta_raw, *A_log, *dt_bias;
+    float scale, lower_bound;
+    const int64_t *cu_seqlens;
+    int N;
+    int64_t T;
+    int H;
+    int chunk;
+    const float *h0;
+    float *ht;
+    void *o;
+    bool in_bf16, out_bf16;
+    unsigned char *ws;
+    hipStream_t stream;
+    int stages;          // bit 0: intra-chunk kernel, bit 1: inter-chunk kernel
+};
+
+// Geometry of one chunk of C rows (C = 16, 32 or 64).
+template <int C>
+struct ChunkGeom {
+    static constexpr int NB = C / 16;            // 16-row blocks
+    static constexpr int CP = C < 32 ? 32 : C;   // t extent rounded up to whole 32-wide k-steps
+    static constexpr int CS = CP / 32;           // 32-wide k-steps over t
+};
+
+// One workspace record per (chunk slot, head). Everything the inter-chunk
+// kernel needs, stored in MFMA operand order so that each lane reads 16 (or 32)
+// contiguous bytes per fragment:
+//   W    [NB tb][4 s][64 lane][8]   rows t, k over key channels   (Tst)
+//   qg   [NB tb][4 s][64 lane][8]   rows t, k over key channels   (Tst)
+//   kgT  [8 kb][CS s][64 lane][8]   rows key channel, k over t    (Tst)
+//   M    [NB tb][CS s][64 lane][8]  rows t, k over t'             (Tst)
+//   GamC [128]                      fp32 total decay of the chunk
+//   Ub   [8 vb][NB tb][64 lane][4]  fp32 accumulator tiles of T V
+// Tst is fp16 when the inputs are bf16 (all four are bounded by 1 in
+// magnitude) and fp32 when the inputs are fp32.
+template <int C, bool PRECISE>
+struct Record {
+    using G = ChunkGeom<C>;
+    static constexpr size_t ELT = PRECISE ? 4 : 2;
+    static constexpr size_t FRAG = 64 * 8 * ELT;
+    static constexpr size_t W_OFF = 0;
+    static constexpr size_t QG_OFF = W_OFF + (size_t)G::NB * 4 * FRAG;
+    static constexpr size_t KG_OFF = QG_OFF + (size_t)G::NB * 4 * FRAG;
+    static constexpr size_t M_OFF = KG_OFF + (size_t)8 * G::CS * FRAG;
+    static constexpr size_t GC_OFF = M_OFF + (size_t)G::NB * G::CS * FRAG;
+    static constexpr size_t SHARED_BYTES = GC_OFF + 128 * 4;
+    static constexpr size_t UB_OFF = SHARED_BYTES;
+    static constexpr size_t UB_VB_BYTES = (size_t)G::NB * 64 * 16;
+    static constexpr size_t BYTES = UB_OFF + 8 * UB_VB_BYTES;
+};
+
+size_t record_bytes(int chunk, bool precise);
+
+// Number of chunk slots: chunk j of sequence n lives in slot floor(cu[n]/C) + n + j,
+// which is unique and below floor(T/C) + N for any valid offsets.
+inline int64_t num_slots(int64_t T, int N, int chunk) { return T / chunk + N; }
+
+hipError_t launch_decode(const DecodeArgs &a);
+hipError_t launch_prefill(const PrefillArgs &a);
+
+}  // namespace kda

@@ -1,0 +1,225 @@
+"""Thin ctypes binding over libkda (include/kda.h).
+
+Argument marshalling only: this module checks tensor placement, dtype, shape
+and contiguity, allocates outputs and the caller-owned workspace with torch,
+and passes raw device pointers plus the current HIP stream to the library.
+Every step of the computation runs in libkda's HIP kernels. There is no CPU
+fallback: if libkda.so is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_OK, KDA_ERR_INVALID_ARG, KDA_ERR_UNSUPPORTED, KDA_ERR_WORKSPACE, KDA_ERR_HIP = range(5)
+KDA_F32, KDA_BF16 = 0, 1
+
+# Every symbol include/kda.h declares.
+EXPORTS = ("kda_version", "kda_status_string", "kda_last_error",
+           "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_intra",
+           "kda_chunk_fwd_inter", "kda_decode_step", "kda_check_cu_seqlens")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("libkda.so not found at %s: build it with "
+                      "`python -c 'import __graft_entry__ as g; g.build()'`" % LIB_PATH)
+
+_lib = ctypes.CDLL(LIB_PATH)
+_P = ctypes.c_void_p
+_i32, _i64, _f32, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+
+_lib.kda_version.restype = ctypes.c_int
+_lib.kda_version.argtypes = []
+_lib.kda_status_string.restype = ctypes.c_char_p
+_lib.kda_status_string.argtypes = [ctypes.c_int]
+_lib.kda_last_error.restype = ctypes.c_char_p
+_lib.kda_last_error.argtypes = []
+_lib.kda_chunk_fwd_workspace_size.restype = _sz
+_lib.kda_chunk_fwd_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, ctypes.c_int]
+for _name in ("kda_chunk_fwd", "kda_chunk_fwd_intra", "kda_chunk_fwd_inter"):
+    getattr(_lib, _name).restype = ctypes.c_int
+    getattr(_lib, _name).argtypes = [_P, _P, _P, _P, _P, _P, _P, _f32, _f32, _P, _i32, _i64,
+                                     _i32, _i32, _i32, _i32, ctypes.c_int, _P, _P, _P,
+                                     ctypes.c_int, _P, _sz, _P]
+_STAGE_FN = {None: _lib.kda_chunk_fwd, "intra": _lib.kda_chunk_fwd_intra,
+             "inter": _lib.kda_chunk_fwd_inter}
+_lib.kda_decode_step.restype = ctypes.c_int
+_lib.kda_decode_step.argtypes = [_P, _P, _P, _P, _P, _P, _P, _f32, _f32, _P, _P, ctypes.c_int,
+                                 _i32, _i32, _i32, _i32, ctypes.c_int, _P]
+_lib.kda_check_cu_seqlens.restype = ctypes.c_int
+_lib.kda_check_cu_seqlens.argtypes = [_P, _i32, _i64, _P]
+
+lib = _lib
+
+
+class KDAError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        detail = _lib.kda_last_error().decode()
+        super().__init__("%s: %s (%s)" % (where, _lib.kda_status_string(status).decode(), detail))
+
+
+def _check(status: int, where: str):
+    if status != KDA_OK:
+        raise KDAError(status, where)
+
+
+def version() -> int:
+    return int(_lib.kda_version())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError("unsupported dtype %s (bf16 or fp32)" % t.dtype)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise RuntimeError("%s must be a GPU tensor (libkda has no CPU path)" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    return t.data_ptr()
+
+
+def _stream_ptr(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def workspace_size(total_tokens: int, num_seqs: int, H: int, chunk_size: int,
+                   in_dtype=torch.bfloat16, K: int = 128, V: int = 128) -> int:
+    d = KDA_BF16 if in_dtype == torch.bfloat16 else KDA_F32
+    n = int(_lib.kda_chunk_fwd_workspace_size(int(total_tokens), int(num_seqs), int(H), int(K),
+                                              int(V), int(chunk_size), d))
+    if n == 0:
+        raise ValueError("kda_chunk_fwd_workspace_size: " + _lib.kda_last_error().decode())
+    return n
+
+
+class Workspace:
+    """Caller-owned device scratch for chunk_fwd, grown on demand and reused.
+
+    Reuse is safe on one stream: every call rewrites what it reads.
+    """
+
+    def __init__(self, device=None):
+        self.device = torch.device(device) if device is not None else torch.device("cuda")
+        self.buf: Optional[torch.Tensor] = None
+
+    def get(self, nbytes: int) -> torch.Tensor:
+        if self.buf is None or self.buf.numel() < nbytes:
+            self.buf = torch.empty(int(nbytes), dtype=torch.uint8, device=self.device)
+        return self.buf
+
+
+def chunk_fwd(q, k, v, g, beta_raw, A_log, dt_bias, cu_seqlens, *, scale: float = None,
+              chunk_size: int = 64, lower_bound: float = -5.0,
+              initial_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
+              o_dtype=None, out: Optional[torch.Tensor] = None,
+              final_state: Optional[torch.Tensor] = None,
+              workspace: Optional[Workspace] = None,
+              stage: Optional[str] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunkwise KDA prefill over packed sequences (libkda kda_chunk_fwd).
+
+    q, k, v: [T, H, 128] bf16 or fp32 (same dtype); g: [T, H, 128] fp32;
+    beta_raw: [T, H] fp32; A_log: [H] fp32; dt_bias: [H, 128] fp32;
+    cu_seqlens: [N+1] int64 on the GPU; initial_state: [N, H, 128, 128] fp32 or None.
+    Returns (o [T, H, 128] in o_dtype (default: q's dtype), final_state or None).
+    stage: None runs both kernels; "intra" / "inter" run one stage (kda_chunk_fwd_intra /
+    kda_chunk_fwd_inter), which must share the same workspace and arguments.
+    """
+    T, H, K = q.shape
+    V = v.shape[2]
+    N = cu_seqlens.numel() - 1
+    in_dt = _dt(q)
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    _dev(q, "q", shape=(T, H, K))
+    _dev(k, "k", dtype=q.dtype, shape=(T, H, K))
+    _dev(v, "v", dtype=q.dtype, shape=(T, H, V))
+    _dev(g, "g", torch.float32, (T, H, K))
+    _dev(beta_raw, "beta_raw", torch.float32, (T, H))
+    _dev(A_log, "A_log", torch.float32, (H,))
+    _dev(dt_bias, "dt_bias", torch.float32, (H, K))
+    _dev(cu_seqlens, "cu_seqlens", torch.int64, (N + 1,))
+    device = q.device
+    h0_ptr = None
+    if initial_state is not None:
+        h0_ptr = _dev(initial_state, "initial_state", torch.float32, (N, H, V, K))
+    o_dtype = q.dtype if o_dtype is None else o_dtype
+    if out is None:
+        out = torch.empty((T, H, V), dtype=o_dtype, device=device)
+    o_ptr = _dev(out, "out", o_dtype, (T, H, V))
+    ht_ptr = None
+    if output_final_state:
+        if final_state is None:
+            final_state = torch.empty((N, H, V, K), dtype=torch.float32, device=device)
+        ht_ptr = _dev(final_state, "final_state", torch.float32, (N, H, V, K))
+    else:
+        final_state = None
+    need = workspace_size(T, N, H, chunk_size, q.dtype, K, V)
+    ws = (workspace or Workspace(device)).get(need)
+    fn = _STAGE_FN[stage]
+    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                            beta_raw.data_ptr(), A_log.data_ptr(), dt_bias.data_ptr(),
+                            float(scale), float(lower_bound), cu_seqlens.data_ptr(), N, T,
+                            H, K, V, int(chunk_size), in_dt, h0_ptr, ht_ptr, o_ptr,
+                            _dt(out), ws.data_ptr(), ws.numel(), _stream_ptr(device))
+    _check(st, fn.__name__)
+    return out, final_state
+
+
+def decode_step(q, k, v, g, beta_raw, A_log, dt_bias, state, *, scale: float = None,
+                lower_bound: float = -5.0, o_dtype=None,
+                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One T=1 decode step for B requests; `state` [B, H, 128, 128] fp32 is updated in place.
+
+    q, k, v: [B, H, 128] bf16 or fp32; g: [B, H, 128] fp32; beta_raw: [B, H] fp32.
+    Returns o [B, H, 128] in o_dtype (default: q's dtype).
+    """
+    B, H, K = q.shape
+    V = v.shape[2]
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    _dev(q, "q", shape=(B, H, K))
+    _dev(k, "k", dtype=q.dtype, shape=(B, H, K))
+    _dev(v, "v", dtype=q.dtype, shape=(B, H, V))
+    _dev(g, "g", torch.float32, (B, H, K))
+    _dev(beta_raw, "beta_raw", torch.float32, (B, H))
+    _dev(A_log, "A_log", torch.float32, (H,))
+    _dev(dt_bias, "dt_bias", torch.float32, (H, K))
+    _dev(state, "state", torch.float32, (B, H, V, K))
+    o_dtype = q.dtype if o_dtype is None else o_dtype
+    if out is None:
+        out = torch.empty((B, H, V), dtype=o_dtype, device=q.device)
+    _dev(out, "out", o_dtype, (B, H, V))
+    st = _lib.kda_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                              beta_raw.data_ptr(), A_log.data_ptr(), dt_bias.data_ptr(),
+                              float(scale), float(lower_bound), state.data_ptr(),
+                              out.data_ptr(), _dt(out), B, H, K, V, _dt(q),
+                              _stream_ptr(q.device))
+    _check(st, "kda_decode_step")
+    return out
+
+
+def check_cu_seqlens(cu_seqlens: torch.Tensor, total_tokens: int) -> None:
+    """Validate packed offsets (synchronises the current stream); raises on bad values."""
+    N = cu_seqlens.numel() - 1
+    _dev(cu_seqlens, "cu_seqlens", torch.int64, (N + 1,))
+    st = _lib.kda_check_cu_seqlens(cu_seqlens.data_ptr(), N, int(total_tokens),
+                                   _stream_ptr(cu_seqlens.device))
+    _check(st, "kda_check_cu_seqlens")

@@ -1,0 +1,122 @@
+"""C-ABI checks that need no GPU: the library loads, exports every declared
+symbol, and rejects invalid arguments with the documented status before any
+HIP call (validation is host-only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    src = open(os.path.join(ROOT, "include", "kda.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import kimi_delta_attention_05_amd.kda as m
+    return m
+
+
+def test_library_exports_every_declared_symbol(kda):
+    syms = declared_symbols()
+    assert set(syms) == set(kda.EXPORTS)
+    for s in syms:
+        assert hasattr(kda.lib, s), s
+    assert kda.version() == 100
+
+
+def test_status_strings(kda):
+    for code in range(5):
+        assert kda.lib.kda_status_string(code)
+    assert kda.lib.kda_status_string(99) == b"unknown status"
+
+
+FAKE = 0x10000     # never dereferenced: every call below fails validation first
+
+
+def chunk_call(kda, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, scale=0.088,
+                lb=-5.0, cu=FAKE, N=1, T=17, H=1, K=128, V=128, C=16, dt=kda.KDA_F32, h0=None,
+                ht=None, o=FAKE, odt=kda.KDA_F32, ws=0x100000, wsb=1 << 40, stream=None)
+    args.update(kw)
+    return kda.lib.kda_chunk_fwd(args["q"], args["k"], args["v"], args["g"], args["beta"],
+                                 args["A_log"], args["dt_bias"], args["scale"], args["lb"],
+                                 args["cu"], args["N"], args["T"], args["H"], args["K"], args["V"],
+                                 args["C"], args["dt"], args["h0"], args["ht"], args["o"],
+                                 args["odt"], args["ws"], args["wsb"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=64), 2), (dict(V=256), 2), (dict(C=48), 2), (dict(C=128), 2), (dict(dt=7), 2),
+    (dict(odt=3), 2),
+    (dict(N=0), 1), (dict(T=-1), 1), (dict(H=0), 1), (dict(scale=0.0), 1),
+    (dict(scale=float("nan")), 1), (dict(lb=0.0), 1), (dict(lb=-5.5), 1), (dict(lb=0.5), 1),
+    (dict(cu=None), 1), (dict(A_log=None), 1), (dict(q=None), 1), (dict(o=None), 1),
+    (dict(ws=None), 3), (dict(wsb=1024), 3), (dict(ws=0x100010), 3),
+])
+def test_chunk_fwd_rejects(kda, kw, status):
+    assert chunk_call(kda, **kw) == status
+    assert kda.lib.kda_last_error()
+
+
+def decode_call(kda, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, scale=0.088,
+             lb=-5.0, state=FAKE, o=FAKE, odt=kda.KDA_BF16, B=4, H=2, K=128, V=128,
+             dt=kda.KDA_BF16, stream=None)
+    a.update(kw)
+    return kda.lib.kda_decode_step(a["q"], a["k"], a["v"], a["g"], a["beta"], a["A_log"],
+                                   a["dt_bias"], a["scale"], a["lb"], a["state"], a["o"],
+                                   a["odt"], a["B"], a["H"], a["K"], a["V"], a["dt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=129), 2), (dict(V=64), 2), (dict(dt=5), 2), (dict(B=0), 1), (dict(H=-1), 1),
+    (dict(state=None), 1), (dict(q=None), 1), (dict(lb=-6.0), 1), (dict(scale=-1.0), 1),
+    (dict(state=FAKE + 4), 1),
+])
+def test_decode_rejects(kda, kw, status):
+    assert decode_call(kda, **kw) == status
+
+
+def test_workspace_size_arithmetic(kda):
+    # one record per (slot, head); slots = floor(T / C) + N
+    for T, N, H, C in [(8192, 1, 96, 64), (8192, 6, 96, 64), (17, 1, 1, 16), (115, 3, 4, 32), (0, 2, 3, 64)]:
+        a = kda.workspace_size(T, N, H, C, in_dtype=__import__("torch").bfloat16)
+        b = kda.workspace_size(T + C, N, H, C, in_dtype=__import__("torch").bfloat16)
+        per = (b - a) // H
+        assert (b - a) % H == 0 and per > 0
+        assert a == (T // C + N) * H * per + 256
+    import torch
+    assert kda.workspace_size(64, 1, 1, 64, torch.float32) > kda.workspace_size(64, 1, 1, 64, torch.bfloat16)
+    with pytest.raises(ValueError):
+        kda.workspace_size(64, 1, 1, 48)
+    with pytest.raises(ValueError):
+        kda.workspace_size(64, 0, 1, 64)
+
+
+def test_check_cu_seqlens_rejects_null(kda):
+    assert kda.lib.kda_check_cu_seqlens(None, 1, 10, None) == 1
+
+
+def test_binding_requires_gpu_tensors(kda):
+    import torch
+    import kda_inputs
+    p = kda_inputs.small()
+    with pytest.raises(RuntimeError):
+        kda.chunk_fwd(p.q, p.k, p.v, p.g, p.beta_raw, p.A_log, p.dt_bias, p.cu_seqlens,
+                      scale=p.scale, chunk_size=16)
+
+
+def test_no_cpu_fallback_in_product():
+    """The product package never imports the oracle and has no CPU compute path."""
+    pkg = os.path.join(ROOT, "kimi_delta_attention_05_amd")
+    for name in os.listdir(pkg):
+        if name.endswith(".py"):
+            src = open(os.path.join(pkg, name)).read()
+            assert "oracle" not in src, name
+            assert "kda_inputs" not in src, name
