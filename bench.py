@@ -75,7 +75,12 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py: this build measures one GPU only (--gpus 1); multi-GPU runs are "
               "not part of it", file=sys.stderr)
@@ -203,6 +208,20 @@ def main():
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(p, dd)
     print(json.dumps(line), flush=True)
+
+
+def copy_calibration(nbytes=1 << 30, reps=3):
+    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counter readings
+    give the factor that converts those counters to bytes on this GPU."""
+    import torch
+    src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}),
+          flush=True)
 
 
 def cpu_baseline(p, dd):
