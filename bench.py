@@ -217,10 +217,15 @@ def copy_calibration(nbytes=1 << 30, reps=3):
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
-    for _ in range(reps):
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for i in range(reps):
         dst.copy_(src)
+        ev[i + 1].record()
     torch.cuda.synchronize()
-    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps}),
+    ms = min(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps,
+                      "best_ms": round(ms, 4), "GBs_read_plus_write": round(2 * nbytes / ms / 1e6, 1)}),
           flush=True)
 
 

@@ -39,6 +39,56 @@ __device__ __forceinline__ float sigmoid_f(float x) {
     return x >= 0.0f ? r : z * r;
 }
 
+// Workgroup barrier that orders LDS only: this wave's LDS operations complete,
+// then all waves meet. __syncthreads() also fences global memory, which on gfx9
+// waits for every outstanding global load, store and global->LDS copy
+// (vmcnt(0)); the kernels here communicate within a workgroup through LDS
+// only, so prefetches and output stores stay in flight across barriers. The
+// "memory" clobbers keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until this wave's outstanding global loads (including global->LDS
+// copies) have landed.
+__device__ __forceinline__ void wait_vmem() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+
+// Asynchronous copy of 16 bytes per lane from global memory straight into LDS
+// (gfx950 global_load_lds_dwordx4): lane i of the wave writes lds_wave_base +
+// 16 i, so a wave fills one contiguous 1 KiB block. lds_wave_base must be the
+// same for the whole wave.
+__device__ __forceinline__ void copy16_to_lds(const void *src, void *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_wave_base, 16, 0, 0);
+}
+__device__ __forceinline__ void copy4_to_lds(const void *src, void *lds_wave_base) {
+    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_wave_base, 4, 0, 0);
+}
+
+// 8 consecutive input elements kept in their storage format (prefetch buffers).
+template <typename T> struct Vec8;
+template <> struct Vec8<__bf16> {
+    bf16x8 v;
+    __device__ __forceinline__ void load(const __bf16 *p) { v = *(const bf16x8 *)p; }
+    __device__ __forceinline__ void zero() {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
+    }
+    __device__ __forceinline__ float operator[](int e) const { return (float)v[e]; }
+};
+template <> struct Vec8<float> {
+    f32x4 a, b;
+    __device__ __forceinline__ void load(const float *p) {
+        a = ((const f32x4 *)p)[0];
+        b = ((const f32x4 *)p)[1];
+    }
+    __device__ __forceinline__ void zero() { a = f32x4{0.f, 0.f, 0.f, 0.f}; b = a; }
+    __device__ __forceinline__ float operator[](int e) const { return e < 4 ? a[e] : b[e - 4]; }
+};
+
 // ---- cross-lane reductions ---------------------------------------------------
 
 template <int CTRL>

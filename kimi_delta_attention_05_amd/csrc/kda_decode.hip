@@ -75,6 +75,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     for (int e = 0; e < 8; ++e) { qh[e] = qv[e] * rq; kh[e] = kv[e] * rk; }
     const float beta = sigmoid_f(beta_raw[bh]);
 
+    __shared__ float so[kHeadDim];             // outputs, stored coalesced at the end
     float vrow[8];
 #pragma unroll
     for (int it = 0; it < 8; ++it) vrow[it] = to_f32(v[tb + 16 * it + 4 * wave + r]);
@@ -99,7 +100,13 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         const f32x4 s0 = {s[0], s[1], s[2], s[3]}, s1 = {s[4], s[5], s[6], s[7]};
         __builtin_nontemporal_store(s0, S4 + row * 32 + 2 * j);
         __builtin_nontemporal_store(s1, S4 + row * 32 + 2 * j + 1);
-        if (j == 0) o[tb + row] = from_f32<Tout>(a + u * kq);
+        if (j == 0) so[row] = a + u * kq;
+    }
+    lds_barrier();
+    if (threadIdx.x < kHeadDim / 2) {
+        const int i = 2 * threadIdx.x;
+        o[tb + i] = from_f32<Tout>(so[i]);
+        o[tb + i + 1] = from_f32<Tout>(so[i + 1]);
     }
 }
 

@@ -52,9 +52,11 @@ struct ChunkGeom {
 //   kgT  [8 kb][CS s][64 lane][8]   rows key channel, k over t    (Tst)
 //   M    [NB tb][CS s][64 lane][8]  rows t, k over t'             (Tst)
 //   GamC [128]                      fp32 total decay of the chunk
-//   Ub   [8 vb][NB tb][64 lane][4]  fp32 accumulator tiles of T V
-// Tst is fp16 when the inputs are bf16 (all four are bounded by 1 in
-// magnitude) and fp32 when the inputs are fp32.
+//   UbSc [4]                        fp32; [0] = power-of-two scale of Ub
+//   Ub   [8 vb][NB tb][64 lane][4]  accumulator tiles of T V / UbSc[0] (Tub)
+// Tst and Tub are fp16 when the inputs are bf16 (W, qg, kg, M are bounded by 1
+// in magnitude; Ub is stored scaled so that it is bounded by 2^15) and fp32
+// when the inputs are fp32.
 template <int C, bool PRECISE>
 struct Record {
     using G = ChunkGeom<C>;
@@ -65,9 +67,11 @@ struct Record {
     static constexpr size_t KG_OFF = QG_OFF + (size_t)G::NB * 4 * FRAG;
     static constexpr size_t M_OFF = KG_OFF + (size_t)8 * G::CS * FRAG;
     static constexpr size_t GC_OFF = M_OFF + (size_t)G::NB * G::CS * FRAG;
-    static constexpr size_t SHARED_BYTES = GC_OFF + 128 * 4;
+    static constexpr size_t UBS_OFF = GC_OFF + 128 * 4;
+    static constexpr size_t SHARED_BYTES = UBS_OFF + 16;
     static constexpr size_t UB_OFF = SHARED_BYTES;
-    static constexpr size_t UB_VB_BYTES = (size_t)G::NB * 64 * 16;
+    static constexpr size_t UB_ELT = PRECISE ? 4 : 2;
+    static constexpr size_t UB_VB_BYTES = (size_t)G::NB * 64 * 4 * UB_ELT;
     static constexpr size_t BYTES = UB_OFF + 8 * UB_VB_BYTES;
 };
 

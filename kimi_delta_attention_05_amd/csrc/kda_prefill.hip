@@ -31,8 +31,8 @@
 // Precision: bf16 inputs run the products on fp16 MFMA with fp32
 // accumulation; operands that are not bounded by 1 (the state, U, v) are
 // scaled by a power of two chosen from their wavefront / tile maximum, which is
-// exact. Diagonal sub-chunk blocks (factors up to e^{75}) use a three-product
-// bf16 split. fp32 inputs run every product on the fp32 MFMA.
+// exact. Diagonal sub-chunk blocks (factors up to e^{75}) run on the fp32
+// MFMA. fp32 inputs run every product on the fp32 MFMA.
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -121,353 +121,509 @@ __device__ __forceinline__ bool locate_slot(const int64_t *__restrict__ cu, int 
 }
 
 // =============================================================================
-// Intra-chunk kernel: one workgroup (8 waves) per (chunk slot, head).
+// Intra-chunk kernel: persistent workgroups (8 waves) over the (chunk slot,
+// head) tiles; tile i is record i of the workspace (slot * H + head).
 //
-// LDS holds three [C][128] fp32 tiles that are rewritten in place as the phases
-// go: sQ = qh -> qh*P -> v (scaled); sK = kh -> kh*P; sP = alpha -> P -> kh/P,
+// LDS holds three [C][128] fp32 tiles rewritten in place as the phases go:
+// sQ = qh -> qh*P;  sK = kh -> kh*P;  sP = alpha -> P -> kh/P -> v (scaled),
 // with P_t the block-local prefix product of alpha. Every operand of A and M is
-// then one of those rows times at most one per-(block, channel) factor.
+// one of those rows times at most one per-(block, channel) factor. Once the
+// W/Ub operands are in registers the three tiles are free: the next tile's raw
+// inputs are copied there (global->LDS, no registers) during the inverse and
+// the W/Ub products (bf16 inputs; fp32 inputs do not fit and are read directly).
 // =============================================================================
 constexpr int kIntraWaves = 8;
 
+template <int C, typename Tin>
+struct RawLayout {                    // raw inputs of one tile inside the three LDS tiles
+    static constexpr size_t Q = 0;
+    static constexpr size_t K = Q + (size_t)C * kHeadDim * sizeof(Tin);
+    static constexpr size_t V = K + (size_t)C * kHeadDim * sizeof(Tin);
+    static constexpr size_t G = V + (size_t)C * kHeadDim * sizeof(Tin);
+    static constexpr size_t B = G + (size_t)C * kHeadDim * 4;
+    static constexpr size_t BYTES = B + (size_t)C * 4;
+    static constexpr int NQ16 = (int)((size_t)C * kHeadDim * sizeof(Tin) / 16);  // 16-B pieces
+    static constexpr int NG16 = C * kHeadDim * 4 / 16;
+    static constexpr int PER = (3 * NQ16 + NG16 + 64 * kIntraWaves - 1) / (64 * kIntraWaves);
+    static constexpr bool FITS = BYTES <= (size_t)3 * C * (kHeadDim + 4) * 4;
+};
+
+// Start copying one tile's raw inputs into LDS (layout RawLayout): 16-byte
+// pieces of q, k, v (row-major [C][128]) and g, plus beta, as asynchronous
+// global->LDS copies; piece idx = tid + NT * i lands at byte 16 idx, so each
+// wave fills contiguous 1 KiB blocks. Rows past the chunk end copy the chunk's
+// last row (in bounds for a valid tile) and are masked where used. The caller
+// waits (wait_vmem + lds_barrier) before reading.
+template <int C, typename Tin>
+__device__ __forceinline__ void stage_raw(const PrefillArgs &p, int h, int64_t t0, int L, int tid,
+                                          unsigned char *lds) {
+    using RL = RawLayout<C, Tin>;
+    constexpr int NT = 64 * kIntraWaves;
+    constexpr int PPR = kHeadDim * (int)sizeof(Tin) / 16;   // pieces per q/k/v row
+    const int wave = tid >> 6;
+#pragma unroll
+    for (int i = 0; i < RL::PER; ++i) {
+        const int idx = tid + NT * i;
+        const int wbase = 64 * wave + NT * i;                   // first piece of this wave
+        if (wbase >= 3 * RL::NQ16 + RL::NG16) break;            // whole wave past the end
+        const void *src;
+        if (idx < 3 * RL::NQ16) {
+            const int arr = idx / RL::NQ16, w = idx % RL::NQ16;
+            int t = w / PPR;
+            t = t < L ? t : L - 1;
+            const unsigned char *base = (const unsigned char *)(arr == 0 ? p.q : arr == 1 ? p.k : p.v);
+            src = base + ((size_t)(t0 + t) * p.H + h) * kHeadDim * sizeof(Tin) + (size_t)(w % PPR) * 16;
+        } else {
+            const int w = idx - 3 * RL::NQ16;
+            int t = w / 32;
+            t = t < L ? t : L - 1;
+            src = p.g + ((size_t)(t0 + t) * p.H + h) * kHeadDim + (w % 32) * 4;
+        }
+        copy16_to_lds(src, lds + (size_t)wbase * 16);
+    }
+    if (wave == 0) {                                             // beta, one float per row
+        const int t = tid < L ? tid : L - 1;
+        if (tid < C) copy4_to_lds(p.beta_raw + (size_t)(t0 + t) * p.H + h, lds + RL::B);
+    }
+}
+
+// 8 entries of a row of T = X diag(beta): X from LDS scaled by beta per column.
+__device__ __forceinline__ void load_T_row(const float *x, const float *beta, float (&t)[8]) {
+    float b[8];
+    load8(x, t);
+    load8(beta, b);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] *= b[e];
+}
+
+// Phase-2 work order. Jobs 0 .. NB*CS-1 are the M fragments (a, s); the rest
+// write qg and kg^T fragments. Slot k goes to wave k % 8 and waves w, w + 4
+// share a SIMD, so for C = 64 the four jobs with a diagonal (fp32 MFMA) block
+// land on four different SIMDs and the two lightest M jobs on the busiest ones.
+template <int C>
+__device__ __forceinline__ int intra_job_order(int slot) {
+    if constexpr (C == 64) {
+        // M job a*2+s: 0 = D, 1 = zero, 2 = O+D, 3 = zero, 4 = O+O, 5 = D, 6 = O+O, 7 = O+D
+        // (D: a diagonal block on the fp32 MFMA, O: an off-diagonal fp16 block)
+        constexpr int first[8] = {2, 7, 0, 5, 1, 3, 4, 6};
+        return slot < 8 ? first[slot] : slot;
+    } else {
+        return slot;
+    }
+}
+
 template <int C, typename Tin, bool PRECISE>
-__global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p)
+__global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, int64_t ntiles)
 {
     using G = ChunkGeom<C>;
     using R = Record<C, PRECISE>;
     using F = Frag<PRECISE>;
+    using RL = RawLayout<C, Tin>;
+    constexpr bool PF = RL::FITS;              // park the next tile's inputs in LDS
+    constexpr int RG = C / 4, RIT = (RG + kIntraWaves - 1) / kIntraWaves;
     constexpr int NB = G::NB, CS = G::CS, NW = kIntraWaves, NT = 64 * NW;
     constexpr int AP = C + 4;
     constexpr int NPO = NB * (NB - 1) / 2 + 1;   // off-diagonal block pairs (+1: never empty)
 
-    __shared__ __align__(16) float sQ[C][KP];
-    __shared__ __align__(16) float sK[C][KP];
-    __shared__ __align__(16) float sP[C][KP];
+    __shared__ __align__(16) float sBig[3][C][KP];
+    float (*sQ)[KP] = sBig[0];
+    float (*sK)[KP] = sBig[1];
+    float (*sP)[KP] = sBig[2];
+    unsigned char *sRaw = (unsigned char *)&sBig[0][0][0];
     __shared__ __align__(16) float sA[C][AP];   // A, strictly lower, beta-scaled
-    __shared__ __align__(16) float sT[C][AP];   // M (staging), then T
+    __shared__ __align__(16) float sT[C][AP];   // T
     __shared__ __align__(16) float sA0[NB][kHeadDim];  // alpha of each block's first row
     __shared__ __align__(16) float sPe[NB][kHeadDim];  // P at each block's last row
     __shared__ __align__(16) float sQF[NB][kHeadDim];  // prod alpha over rows 0 .. 16b
     __shared__ __align__(16) float sKF[NB][kHeadDim];  // prod alpha over rows 16b+1 .. C-1
     __shared__ __align__(16) float sEF[NPO][kHeadDim]; // prod alpha over rows 16b+1 .. 16a
-    __shared__ float sBeta[C];
+    __shared__ __align__(16) float sBeta[C];
     __shared__ float sInv[3][16][17];
     __shared__ float sVmax[NW];
 
     const int H = p.H;
-    const int h = blockIdx.y;
-    int n, L;
-    int64_t t0;
-    if (!locate_slot<C>(p.cu_seqlens, p.N, blockIdx.x, n, t0, L)) return;
-
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int lr = lane & 15, lg = lane >> 4;
-    unsigned char *rec = p.ws + ((size_t)blockIdx.x * H + h) * R::BYTES;
-
-    // ---- phase 1: rows; a DPP row of 16 lanes holds one token (8 channels per lane)
-    constexpr int RG = C / 4;                   // groups of 4 rows
-    constexpr int RIT = (RG + NW - 1) / NW;     // groups per wave
     const int c8 = 8 * lr;
-    const float agate = fast_exp2(p.A_log[h] * kLog2e);
     const float lb2 = p.lower_bound * kLog2e;
-    float db[8];
-    load8(p.dt_bias + h * kHeadDim + c8, db);
-    float vreg[RIT][8];
-    float vmax = 0.f;
-#pragma unroll
-    for (int it = 0; it < RIT; ++it) {
-        const int grp = wave + NW * it;
-        if (grp >= RG) break;
-        const int t = 4 * grp + lg;
-        const bool valid = t < L;
-        float qv[8], kv[8], gv[8];
-        if (valid) {
-            const size_t base = ((size_t)(t0 + t) * H + h) * kHeadDim + c8;
-            load8((const Tin *)p.q + base, qv);
-            load8((const Tin *)p.k + base, kv);
-            load8((const Tin *)p.v + base, vreg[it]);
-            load8(p.g + base, gv);
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) qv[e] = kv[e] = vreg[it][e] = gv[e] = 0.f;
-        }
-        float sq = 0.f, sk = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { sq += qv[e] * qv[e]; sk += kv[e] * kv[e]; }
-        sq = row16_sum(sq);
-        sk = row16_sum(sk);
-        const float fq = rsqrtf(sq + kL2Eps) * p.scale, fk = rsqrtf(sk + kL2Eps);
-        float al[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            qv[e] *= fq;
-            kv[e] *= fk;
-            // alpha = e^lambda; padding rows have lambda = 0
-            al[e] = valid ? fast_exp2(lb2 * sigmoid_f(agate * (gv[e] + db[e]))) : 1.f;
-            vmax = fmaxf(vmax, fabsf(vreg[it][e]));
-        }
-        *(f32x4 *)&sQ[t][c8] = f32x4{qv[0], qv[1], qv[2], qv[3]};
-        *(f32x4 *)&sQ[t][c8 + 4] = f32x4{qv[4], qv[5], qv[6], qv[7]};
-        *(f32x4 *)&sK[t][c8] = f32x4{kv[0], kv[1], kv[2], kv[3]};
-        *(f32x4 *)&sK[t][c8 + 4] = f32x4{kv[4], kv[5], kv[6], kv[7]};
-        *(f32x4 *)&sP[t][c8] = f32x4{al[0], al[1], al[2], al[3]};
-        *(f32x4 *)&sP[t][c8 + 4] = f32x4{al[4], al[5], al[6], al[7]};
-        if (lr == 0) sBeta[t] = valid ? sigmoid_f(p.beta_raw[(size_t)(t0 + t) * H + h]) : 0.f;
-    }
-    vmax = wave_max(vmax);
-    if (lane == 0) sVmax[wave] = vmax;
-    __syncthreads();
 
-    // ---- phase 1b: block-local prefix products P_t = prod alpha_{16b+1 .. t} --
-    if (tid < NB * kHeadDim) {
-        const int b = tid / kHeadDim, c = tid % kHeadDim;
-        float a[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) a[i] = sP[16 * b + i][c];
-        sA0[b][c] = a[0];
-        float run = 1.f;
-        sP[16 * b][c] = 1.f;
-#pragma unroll
-        for (int i = 1; i < 16; ++i) { run *= a[i]; sP[16 * b + i][c] = run; }
-        sPe[b][c] = run;
+    int64_t ti = blockIdx.x;
+    int n = 0, L = 0;
+    int64_t t0 = 0;
+    bool valid = ti < ntiles && locate_slot<C>(p.cu_seqlens, p.N, ti / H, n, t0, L);
+    if constexpr (PF) {
+        if (valid) stage_raw<C, Tin>(p, (int)(ti % H), t0, L, tid, sRaw);
+        wait_vmem();
+        lds_barrier();
     }
-    __syncthreads();
 
-    // ---- phase 1c: per-channel block factors; qh*P, kh*P, kh/P in place --------
-    if (tid < kHeadDim) {
-        const int c = tid;
-        float tot[NB];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) tot[b] = sA0[b][c] * sPe[b][c];
-        float pre = 1.f;
-#pragma unroll
-        for (int b = 0; b < NB; ++b) { sQF[b][c] = pre * sA0[b][c]; pre *= tot[b]; }
-        float suf = 1.f;
-#pragma unroll
-        for (int b = NB - 1; b >= 0; --b) { sKF[b][c] = sPe[b][c] * suf; suf *= tot[b]; }
-#pragma unroll
-        for (int a = 1; a < NB; ++a) {
-            float e = sA0[a][c];
-#pragma unroll
-            for (int b = a - 1; b >= 0; --b) {
-                sEF[a * (a - 1) / 2 + b][c] = sPe[b][c] * e;
-                e *= tot[b];
+    for (; ti < ntiles; ) {
+        const int64_t next = ti + gridDim.x;
+        if (!valid) {                            // unused slot: nothing to compute
+            ti = next;
+            valid = ti < ntiles && locate_slot<C>(p.cu_seqlens, p.N, ti / H, n, t0, L);
+            if constexpr (PF) {
+                if (valid) stage_raw<C, Tin>(p, (int)(ti % H), t0, L, tid, sRaw);
+                wait_vmem();
+                lds_barrier();
             }
+            continue;
         }
-        ((float *)(rec + R::GC_OFF))[c] = pre;     // total decay of the chunk
-    }
-    for (int idx = tid; idx < C * (kHeadDim / 4); idx += NT) {
-        const int t = idx / (kHeadDim / 4), c = 4 * (idx % (kHeadDim / 4));
-        const f32x4 pp = *(const f32x4 *)&sP[t][c];
-        const f32x4 kk = *(const f32x4 *)&sK[t][c];
-        const f32x4 qq = *(const f32x4 *)&sQ[t][c];
-        f32x4 kr;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) kr[e] = kk[e] * fast_rcp(pp[e]);
-        *(f32x4 *)&sQ[t][c] = qq * pp;
-        *(f32x4 *)&sK[t][c] = kk * pp;
-        *(f32x4 *)&sP[t][c] = kr;
-    }
-    __syncthreads();
+        const int h = (int)(ti % H);
+        const int Lc = L;
+        const int64_t t0c = t0;
+        unsigned char *rec = p.ws + (size_t)ti * R::BYTES;
 
-    // ---- phase 2: A and M blocks; qg and kgT fragments ------------------------
-    {
-        constexpr int NP = NB * (NB + 1) / 2;
-        for (int pi = wave; pi < NP; pi += NW) {
-            int a = 0, b = pi;                       // pair index -> (a, b), b <= a
-            while (b > a) { b -= a + 1; ++a; }
-            const int il = 16 * a + lr, jr = 16 * b + lr;
-            const float *ef = sEF[a * (a - 1) / 2 + b];   // only read when b < a
-            f32x4 accA = {0.f, 0.f, 0.f, 0.f}, accM = {0.f, 0.f, 0.f, 0.f};
+        // ---- phase 1: a DPP row of 16 lanes per token, 8 channels per lane -------
+        // gate: sigmoid(a (g + db)) = 1 / (1 + 2^(ga g + gb)), ga = -a log2e, gb = ga db;
+        // 2^x overflows to inf for very negative arguments and 1/inf = 0, so this
+        // form is exact at both ends.
+        const float ga = -fast_exp2(p.A_log[h] * kLog2e) * kLog2e;
+        float gb[8];
+        load8(p.dt_bias + h * kHeadDim + c8, gb);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int c = 32 * s + 8 * lg;
-                float aK[8], aQ[8], bK[8];
-                load8(&sK[il][c], aK);              // kh e^{G_i - G_16a}
-                load8(&sQ[il][c], aQ);              // qh e^{G_i - G_16a}
-                load8(&sP[jr][c], bK);              // kh / P_j
-                if (a != b) {                        // e^{G_16a - G_j} = EF / P_j
-                    float f[8];
-                    load8(ef + c, f);
+        for (int e = 0; e < 8; ++e) gb[e] *= ga;
+        float vreg[RIT][8], qv[RIT][8], kv[RIT][8], al[RIT][8], bet[RIT];
+        float vmax = 0.f;
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) bK[e] *= f[e];
+        for (int it = 0; it < RIT; ++it) {
+            const int grp = wave + NW * it;
+            if (grp >= RG) break;
+            const int t = 4 * grp + lg;
+            const bool rv = t < Lc;
+            Vec8<Tin> rq, rk, rvv;
+            Vec8<float> rg;
+            float rb;
+            if constexpr (PF) {
+                rq.load((const Tin *)(sRaw + RL::Q) + t * kHeadDim + c8);
+                rk.load((const Tin *)(sRaw + RL::K) + t * kHeadDim + c8);
+                rvv.load((const Tin *)(sRaw + RL::V) + t * kHeadDim + c8);
+                rg.load((const float *)(sRaw + RL::G) + t * kHeadDim + c8);
+                rb = ((const float *)(sRaw + RL::B))[t];
+            } else {
+                const int tc = rv ? t : Lc - 1;
+                const size_t row = (size_t)(t0c + tc) * H + h;
+                rq.load((const Tin *)p.q + row * kHeadDim + c8);
+                rk.load((const Tin *)p.k + row * kHeadDim + c8);
+                rvv.load((const Tin *)p.v + row * kHeadDim + c8);
+                rg.load(p.g + row * kHeadDim + c8);
+                rb = p.beta_raw[row];
+            }
+            // padding rows (t >= L) act as q = k = v = 0, lambda = 0, beta = 0
+            float sq = 0.f, sk = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                qv[it][e] = rv ? rq[e] : 0.f;
+                kv[it][e] = rv ? rk[e] : 0.f;
+                vreg[it][e] = rv ? rvv[e] : 0.f;
+                sq += qv[it][e] * qv[it][e];
+                sk += kv[it][e] * kv[it][e];
+            }
+            sq = row16_sum(sq);
+            sk = row16_sum(sk);
+            const float fq = rsqrtf(sq + kL2Eps) * p.scale, fk = rsqrtf(sk + kL2Eps);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                qv[it][e] *= fq;
+                kv[it][e] *= fk;
+                const float sg = fast_rcp(1.0f + fast_exp2(fmaf(rg[e], ga, gb[e])));
+                al[it][e] = rv ? fast_exp2(lb2 * sg) : 1.f;
+                vmax = fmaxf(vmax, fabsf(vreg[it][e]));
+            }
+            bet[it] = rv ? sigmoid_f(rb) : 0.f;
+        }
+        vmax = wave_max(vmax);
+        if constexpr (PF) lds_barrier();       // all raw rows read before they are overwritten
+#pragma unroll
+        for (int it = 0; it < RIT; ++it) {
+            const int grp = wave + NW * it;
+            if (grp >= RG) break;
+            const int t = 4 * grp + lg;
+            *(f32x4 *)&sQ[t][c8] = f32x4{qv[it][0], qv[it][1], qv[it][2], qv[it][3]};
+            *(f32x4 *)&sQ[t][c8 + 4] = f32x4{qv[it][4], qv[it][5], qv[it][6], qv[it][7]};
+            *(f32x4 *)&sK[t][c8] = f32x4{kv[it][0], kv[it][1], kv[it][2], kv[it][3]};
+            *(f32x4 *)&sK[t][c8 + 4] = f32x4{kv[it][4], kv[it][5], kv[it][6], kv[it][7]};
+            *(f32x4 *)&sP[t][c8] = f32x4{al[it][0], al[it][1], al[it][2], al[it][3]};
+            *(f32x4 *)&sP[t][c8 + 4] = f32x4{al[it][4], al[it][5], al[it][6], al[it][7]};
+            if (lr == 0) sBeta[t] = bet[it];
+        }
+        if (lane == 0) sVmax[wave] = vmax;
+        lds_barrier();
+
+        // ---- phase 1b: block-local prefix products P_t = prod alpha_{16b+1 .. t};
+        //      a thread per (16-row block, channel) also forms qh*P, kh*P and kh/P
+        if (tid < NB * kHeadDim) {
+            const int b = tid / kHeadDim, c = tid % kHeadDim;
+            float a[16], kk[16], qq[16];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                a[i] = sP[16 * b + i][c];
+                kk[i] = sK[16 * b + i][c];
+                qq[i] = sQ[16 * b + i][c];
+            }
+            sA0[b][c] = a[0];
+            float run = 1.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (i > 0) run *= a[i];
+                sQ[16 * b + i][c] = qq[i] * run;
+                sK[16 * b + i][c] = kk[i] * run;
+                sP[16 * b + i][c] = kk[i] * fast_rcp(run);
+            }
+            sPe[b][c] = run;
+        }
+        lds_barrier();
+
+        // ---- phase 1c: per-channel block factors ---------------------------------
+        if (tid < kHeadDim) {
+            const int c = tid;
+            float tot[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) tot[b] = sA0[b][c] * sPe[b][c];
+            float pre = 1.f;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) { sQF[b][c] = pre * sA0[b][c]; pre *= tot[b]; }
+            float suf = 1.f;
+#pragma unroll
+            for (int b = NB - 1; b >= 0; --b) { sKF[b][c] = sPe[b][c] * suf; suf *= tot[b]; }
+#pragma unroll
+            for (int a = 1; a < NB; ++a) {
+                float e = sA0[a][c];
+#pragma unroll
+                for (int b = a - 1; b >= 0; --b) {
+                    sEF[a * (a - 1) / 2 + b][c] = sPe[b][c] * e;
+                    e *= tot[b];
                 }
-                if constexpr (PRECISE) {
-                    accA = mfma_f32x8(aK, bK, accA);
-                    accM = mfma_f32x8(aQ, bK, accM);
-                } else if (a == b) {                 // right factors up to e^75
-                    accA = mfma_x3(aK, bK, accA);
-                    accM = mfma_x3(aQ, bK, accM);
-                } else {                             // all factors <= 1
-                    accA = mfma_f16(aK, bK, accA);
-                    accM = mfma_f16(aQ, bK, accM);
+            }
+            ((float *)(rec + R::GC_OFF))[c] = pre;     // total decay of the chunk
+        }
+        for (int idx = tid; idx < C * C; idx += NT) {   // zero the blocks of T above the diagonal
+            const int i = idx / C, j = idx % C;
+            if ((j >> 4) > (i >> 4)) sT[i][j] = 0.0f;
+        }
+        lds_barrier();
+
+        // ---- phase 2: A^T and M^T blocks (MFMA); M, qg and kgT fragments ----------
+        // M fragment (a, s) holds rows 16a..16a+15 and columns 32s .. 32s+31, i.e. the
+        // transposed blocks (2s, a) and (2s+1, a): computing M^T makes the accumulator
+        // layout the fragment layout.
+        {
+            constexpr int NMJ = NB * CS;
+            constexpr int NQ = NB * 4, NKG = 8 * CS;
+            for (int slot = wave; slot < NMJ + NQ + NKG; slot += NW) {
+                const int job = intra_job_order<C>(slot);
+                if (job < NMJ) {
+                    const int a = job / CS, s = job % CS;
+                    const int il = 16 * a + lr;          // B operand row (left factor side)
+                    float xm[8];
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+                        const int b = 2 * s + half;
+                        float accM[4] = {0.f, 0.f, 0.f, 0.f};
+                        if (b <= a && b < NB) {
+                            const int jr = 16 * b + lr;  // A operand row (right factor side)
+                            const float *ef = sEF[a * (a - 1) / 2 + b];
+                            f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aM = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                            for (int ks = 0; ks < 4; ++ks) {
+                                const int c = 32 * ks + 8 * lg;
+                                float bK[8], bQ[8], aR[8];
+                                load8(&sK[il][c], bK);   // kh e^{G_i - G_16a}
+                                load8(&sQ[il][c], bQ);   // qh e^{G_i - G_16a}
+                                load8(&sP[jr][c], aR);   // kh / P_j
+                                if (a != b) {            // e^{G_16a - G_j} = EF / P_j
+                                    float f[8];
+                                    load8(ef + c, f);
+#pragma unroll
+                                    for (int e = 0; e < 8; ++e) aR[e] *= f[e];
+                                }
+                                if (PRECISE || a == b) { // diagonal: right factors up to e^75
+                                    aA = mfma_f32x8(aR, bK, aA);
+                                    aM = mfma_f32x8(aR, bQ, aM);
+                                } else {                 // all factors <= 1
+                                    aA = mfma_f16(aR, bK, aA);
+                                    aM = mfma_f16(aR, bQ, aM);
+                                }
+                            }
+                            // lane holds A[i][j] / M[i][j] for i = 16a + lr, j = 16b + 4lg + ii
+#pragma unroll
+                            for (int ii = 0; ii < 4; ++ii) {
+                                const int j = 16 * b + 4 * lg + ii;
+                                sA[il][j] = (il > j) ? sBeta[il] * aA[ii] : 0.f;
+                                accM[ii] = (j <= il) ? aM[ii] : 0.f;
+                            }
+                        }
+#pragma unroll
+                        for (int ii = 0; ii < 4; ++ii) xm[4 * half + ii] = accM[ii];
+                    }
+                    F::store(rec + R::M_OFF + ((size_t)(a * CS + s) * 64 + lane) * F::BYTES, xm);
+                    if (a >> 1 == s) {
+                        // This wave wrote the diagonal block A_aa: invert I + A_aa by
+                        // forward substitution, one column per lane (LDS accesses of a
+                        // wave complete in order, so its own writes are visible).
+                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                        if (lg == 0) {
+                            const int o = 16 * a, c = lr;
+                            float x[16];
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) {
+                                float acc0 = (i == c) ? 1.0f : 0.0f, acc1 = 0.f;
+#pragma unroll
+                                for (int jj = 0; jj < i; jj += 2) {
+                                    acc0 -= sA[o + i][o + jj] * x[jj];
+                                    if (jj + 1 < i) acc1 -= sA[o + i][o + jj + 1] * x[jj + 1];
+                                }
+                                x[i] = (i < c) ? 0.0f : acc0 + acc1;
+                            }
+#pragma unroll
+                            for (int i = 0; i < 16; ++i) sT[o + i][o + c] = x[i];
+                        }
+                    }
+                } else if (job < NMJ + NQ) {         // qg = qh e^{G_t} = (qh P_t) QF
+                    const int f = job - NMJ;
+                    const int tb = f >> 2, s = f & 3;
+                    const int t = 16 * tb + lr;
+                    const int c0 = 32 * s + 4 * lg;
+                    const f32x4 q0 = *(const f32x4 *)&sQ[t][c0], q1 = *(const f32x4 *)&sQ[t][c0 + 16];
+                    const f32x4 f0 = *(const f32x4 *)&sQF[tb][c0], f1 = *(const f32x4 *)&sQF[tb][c0 + 16];
+                    float x[8];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) { x[e] = q0[e] * f0[e]; x[e + 4] = q1[e] * f1[e]; }
+                    F::store(rec + R::QG_OFF + ((size_t)(tb * 4 + s) * 64 + lane) * F::BYTES, x);
+                } else {                             // kg = kh e^{G_C - G_t} = (kh / P_t) KF
+                    const int f = job - NMJ - NQ;
+                    const int kb = f / CS, s = f % CS;
+                    const int c = 16 * kb + lr;
+                    float x[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int t = 32 * s + kperm(lg, e);
+                        x[e] = (t < C) ? sP[t][c] * sKF[t >> 4][c] : 0.f;
+                    }
+                    F::store(rec + R::KG_OFF + ((size_t)(kb * CS + s) * 64 + lane) * F::BYTES, x);
                 }
             }
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const int io = 16 * a + 4 * lg + ii, jo = 16 * b + lr;
-                sA[io][jo] = (io > jo) ? sBeta[io] * accA[ii] : 0.f;
-                sT[io][jo] = (io >= jo) ? accM[ii] : 0.f;
-            }
         }
-        constexpr int NQ = NB * 4, NKG = 8 * CS;
-        for (int f = wave; f < NQ + NKG; f += NW) {
+        // power-of-two scale of v for the fp16 product T v (exact)
+        float vscale = 1.0f;
+        if constexpr (!PRECISE) {
+            float m = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) m = fmaxf(m, sVmax[w]);
+            vscale = pow2_scale_for(m, 9);          // |T v / vscale| <= 64 * 2^9 = 2^15
+        }
+        const float vinv = inv_pow2(vscale);
+        lds_barrier();
+
+        // ---- phase 3: v (scaled) into sP ----------------------------------------
+#pragma unroll
+        for (int it = 0; it < RIT; ++it) {
+            const int grp = wave + NW * it;
+            if (grp >= RG) break;
+            const int t = 4 * grp + lg;
             float x[8];
-            unsigned char *dst;
-            if (f < NQ) {                            // qg = qh e^{G_t} = (qh P_t) QF
-                const int tb = f >> 2, s = f & 3;
-                const int t = 16 * tb + lr;
-                const int c0 = 32 * s + 4 * lg;
-                const f32x4 q0 = *(const f32x4 *)&sQ[t][c0], q1 = *(const f32x4 *)&sQ[t][c0 + 16];
-                const f32x4 f0 = *(const f32x4 *)&sQF[tb][c0], f1 = *(const f32x4 *)&sQF[tb][c0 + 16];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) { x[e] = q0[e] * f0[e]; x[e + 4] = q1[e] * f1[e]; }
-                dst = rec + R::QG_OFF + ((size_t)(tb * 4 + s) * 64 + lane) * F::BYTES;
-            } else {                                 // kg = kh e^{G_C - G_t} = (kh / P_t) KF
-                const int kb = (f - NQ) / CS, s = (f - NQ) % CS;
-                const int c = 16 * kb + lr;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int t = 32 * s + kperm(lg, e);
-                    x[e] = (t < C) ? sP[t][c] * sKF[t >> 4][c] : 0.f;
-                }
-                dst = rec + R::KG_OFF + ((size_t)(kb * CS + s) * 64 + lane) * F::BYTES;
-            }
-            F::store(dst, x);
+            for (int e = 0; e < 8; ++e) x[e] = vreg[it][e] * vinv;
+            *(f32x4 *)&sP[t][c8] = f32x4{x[0], x[1], x[2], x[3]};
+            *(f32x4 *)&sP[t][c8 + 4] = f32x4{x[4], x[5], x[6], x[7]};
         }
-    }
-    // power-of-two scale of v for the fp16 product T v (exact)
-    float vscale = 1.0f;
-    if constexpr (!PRECISE) {
-        float m = 0.f;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) m = fmaxf(m, sVmax[w]);
-        vscale = pow2_scale_for(m, 12);
-    }
-    const float vinv = inv_pow2(vscale);
-    __syncthreads();
+        if (tid == 0) *(float *)(rec + R::UBS_OFF) = vscale;
+        lds_barrier();
 
-    // ---- phase 3: M fragments out; v (scaled) into sQ --------------------------
-    for (int f = wave; f < NB * CS; f += NW) {
-        const int tb = f / CS, s = f % CS;
-        const int t = 16 * tb + lr;
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int tp = 32 * s + kperm(lg, e);
-            x[e] = (tp <= t && tp < C) ? sT[t][tp] : 0.f;
-        }
-        F::store(rec + R::M_OFF + ((size_t)(tb * CS + s) * 64 + lane) * F::BYTES, x);
-    }
-#pragma unroll
-    for (int it = 0; it < RIT; ++it) {
-        const int grp = wave + NW * it;
-        if (grp >= RG) break;
-        const int t = 4 * grp + lg;
-        float x[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = vreg[it][e] * vinv;
-        *(f32x4 *)&sQ[t][c8] = f32x4{x[0], x[1], x[2], x[3]};
-        *(f32x4 *)&sQ[t][c8 + 4] = f32x4{x[4], x[5], x[6], x[7]};
-    }
-    __syncthreads();
-
-    // ---- phase 4: T = (I + A)^-1 diag(beta) by blocked forward substitution ---
-    if (tid < 16 * NB) {                       // diagonal 16x16 blocks, one column each
-        const int a = tid >> 4, c = tid & 15, o = 16 * a;
-        float x[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            float acc = (i == c) ? 1.0f : 0.0f;
-#pragma unroll
-            for (int jj = 0; jj < i; ++jj) acc -= sA[o + i][o + jj] * x[jj];
-            x[i] = (i < c) ? 0.0f : acc;
-        }
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sT[o + i][o + c] = x[i];
-    }
-    for (int idx = tid; idx < C * C; idx += NT) {   // zero the blocks above the diagonal
-        const int i = idx / C, j = idx % C;
-        if ((j >> 4) > (i >> 4)) sT[i][j] = 0.0f;
-    }
-    __syncthreads();
-    for (int d = 1; d < NB; ++d) {
-        const int ii = (tid >> 4) & 15, jj = tid & 15;
-        const bool act = tid < 256;
-        for (int a = d; act && a < NB; ++a) {     // P = sum_{c=b}^{a-1} A_ac X_cb
-            const int b = a - d;
-            float acc = 0.f;
-            for (int c = b; c < a; ++c)
-#pragma unroll
-                for (int m = 0; m < 16; ++m) acc += sA[16 * a + ii][16 * c + m] * sT[16 * c + m][16 * b + jj];
-            sInv[a - d][ii][jj] = acc;
-        }
-        __syncthreads();
-        for (int a = d; act && a < NB; ++a) {     // X_ab = -X_aa P
-            const int b = a - d;
-            float acc = 0.f;
-#pragma unroll
-            for (int m = 0; m < 16; ++m) acc += sT[16 * a + ii][16 * a + m] * sInv[a - d][m][jj];
-            sT[16 * a + ii][16 * b + jj] = -acc;
-        }
-        __syncthreads();
-    }
-    for (int idx = tid; idx < C * C; idx += NT) {   // T = X diag(beta)
-        const int i = idx / C, j = idx % C;
-        sT[i][j] *= sBeta[j];
-    }
-    __syncthreads();
-
-    // ---- phase 5: W^T = (kh e^G)^T T^T and Ub = T v (MFMA) --------------------
-    {
-        // W^T: wave owns channel blocks 2s, 2s+1 (s = wave % 4), i.e. both halves
-        // of W's operand fragment for k-step s, for row blocks tb = 2 (wave / 4) + {0, 1}.
-        const int s = wave & 3;
-        const int ca = 32 * s + lr, cb = ca + 16;
-        float a0[CS][8], a1[CS][8];
-#pragma unroll
-        for (int sp = 0; sp < CS; ++sp)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {        // e^{G_j} kh_j = (kh P_j) QF
-                const int jx = 32 * sp + 8 * lg + e;
-                a0[sp][e] = (jx < C) ? sK[jx][ca] * sQF[jx >> 4][ca] : 0.f;
-                a1[sp][e] = (jx < C) ? sK[jx][cb] * sQF[jx >> 4][cb] : 0.f;
-            }
-        for (int tb = 2 * (wave >> 2); tb < NB && tb < 2 * (wave >> 2) + 2; ++tb) {
-            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-            const int i = 16 * tb + lr;
-#pragma unroll
-            for (int sp = 0; sp < CS; ++sp) {
-                if (32 * sp > 16 * tb + 15) continue;      // T is lower triangular
-                float bT[8];
-                const int j0 = 32 * sp + 8 * lg;
-                if (j0 < C) load8(&sT[i][j0], bT);
-                else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) bT[e] = 0.f;
-                }
-                if constexpr (PRECISE) {
-                    acc0 = mfma_f32x8(a0[sp], bT, acc0);
-                    acc1 = mfma_f32x8(a1[sp], bT, acc1);
-                } else {
-                    acc0 = mfma_f16(a0[sp], bT, acc0);
-                    acc1 = mfma_f16(a1[sp], bT, acc1);
-                }
-            }
-            float x[8] = {acc0[0], acc0[1], acc0[2], acc0[3], acc1[0], acc1[1], acc1[2], acc1[3]};
-            F::store(rec + R::W_OFF + ((size_t)(tb * 4 + s) * 64 + lane) * F::BYTES, x);
-        }
-        // Ub tiles (tb, vb = wave): T rows against the (scaled) v columns
-        const int vb = wave;
-        const int col = 16 * vb + lr;
-        float bV[CS][8];
+        // phase-5 operands that do not depend on T, built before the inverse ends:
+        // W^T A operand (kh e^{G_j} = (kh P_j) QF, channel blocks 2s', 2s'+1 with
+        // s' = wave % 4) and the Ub B operand (v columns of block vb = wave).
+        const int sw = wave & 3;
+        const int ca = 32 * sw + lr, cb = ca + 16;
+        const int col = 16 * wave + lr;
+        float a0[CS][8], a1[CS][8], bV[CS][8];
 #pragma unroll
         for (int sp = 0; sp < CS; ++sp)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int jx = 32 * sp + 8 * lg + e;
-                bV[sp][e] = (jx < C) ? sQ[jx][col] : 0.f;
+                const bool in = jx < C;
+                const int bj = in ? (jx >> 4) : 0;
+                a0[sp][e] = in ? sK[jx][ca] * sQF[bj][ca] : 0.f;
+                a1[sp][e] = in ? sK[jx][cb] * sQF[bj][cb] : 0.f;
+                bV[sp][e] = in ? sP[jx][col] : 0.f;
             }
+
+        // next tile: its raw inputs load during the inverse and the W / Ub products
+        ti = next;
+        valid = ti < ntiles && locate_slot<C>(p.cu_seqlens, p.N, ti / H, n, t0, L);
+        if constexpr (PF) {
+            lds_barrier();                      // the three tiles are free from here on
+            if (valid) stage_raw<C, Tin>(p, (int)(ti % H), t0, L, tid, sRaw);
+        }
+
+        // ---- phase 4: off-diagonal blocks X_ab = -X_aa sum_{c=b}^{a-1} A_ac X_cb ----
+        // One wave per block pair of a diagonal d = a - b, as 16x16x16 fp32 MFMA
+        // products (four 16x16x4 steps: lane l supplies row/column l % 16 and
+        // k = 4 kk + l / 16).
+#pragma unroll
+        for (int d = 1; d < NB; ++d) {
+            const int a = d + wave, b = wave;
+            if (a < NB) {                          // P = sum_c A_ac X_cb  -> sInv[wave]
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < NB; ++c) {
+                    if (c < b || c >= a) continue;
+#pragma unroll
+                    for (int kk = 0; kk < 4; ++kk)
+                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                            sA[16 * a + lr][16 * c + 4 * kk + lg], sT[16 * c + 4 * kk + lg][16 * b + lr],
+                            acc, 0, 0, 0);
+                }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sInv[wave][4 * lg + i][lr] = acc[i];
+            }
+            lds_barrier();
+            if (a < NB) {                          // X_ab = -X_aa P
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk)
+                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                        sT[16 * a + lr][16 * a + 4 * kk + lg], sInv[wave][4 * kk + lg][lr], acc, 0, 0, 0);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) sT[16 * a + 4 * lg + i][16 * b + lr] = -acc[i];
+            }
+            lds_barrier();
+        }
+
+        // ---- phase 5: W^T = (kh e^G)^T T^T and Ub = T v (MFMA) --------------------
+        // Results stay in registers until the next tile's copies have landed, so
+        // that the wait below does not also wait for these stores.
+        float wres[2][8];
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+            const int tb = 2 * (wave >> 2) + q2;
+            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+            if (tb < NB) {
+                const int i = 16 * tb + lr;
+#pragma unroll
+                for (int sp = 0; sp < CS; ++sp) {
+                    if (32 * sp > 16 * tb + 15) continue;      // T is lower triangular
+                    float bT[8];
+                    const int j0 = 32 * sp + 8 * lg;
+                    if (j0 < C) load_T_row(&sT[i][j0], &sBeta[j0], bT);     // T = X diag(beta)
+                    else {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) bT[e] = 0.f;
+                    }
+                    if constexpr (PRECISE) {
+                        acc0 = mfma_f32x8(a0[sp], bT, acc0);
+                        acc1 = mfma_f32x8(a1[sp], bT, acc1);
+                    } else {
+                        acc0 = mfma_f16(a0[sp], bT, acc0);
+                        acc1 = mfma_f16(a1[sp], bT, acc1);
+                    }
+                }
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) { wres[q2][e] = acc0[e]; wres[q2][e + 4] = acc1[e]; }
+        }
+        f32x4 ures[NB];
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb) {
             const int i = 16 * tb + lr;
@@ -477,7 +633,7 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p)
                 if (32 * sp > 16 * tb + 15) continue;
                 float aT[8];
                 const int j0 = 32 * sp + 8 * lg;
-                if (j0 < C) load8(&sT[i][j0], aT);
+                if (j0 < C) load_T_row(&sT[i][j0], &sBeta[j0], aT);
                 else {
 #pragma unroll
                     for (int e = 0; e < 8; ++e) aT[e] = 0.f;
@@ -485,7 +641,26 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p)
                 if constexpr (PRECISE) acc = mfma_f32x8(aT, bV[sp], acc);
                 else acc = mfma_f16(aT, bV[sp], acc);
             }
-            *(f32x4 *)(rec + R::UB_OFF + ((size_t)(vb * NB + tb) * 64 + lane) * 16) = acc * vscale;
+            ures[tb] = acc;
+        }
+        if constexpr (PF) wait_vmem();        // the next tile's inputs have landed
+        lds_barrier();                      // LDS is reused by the next tile
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+            const int tb = 2 * (wave >> 2) + q2;
+            if (tb < NB)
+                F::store(rec + R::W_OFF + ((size_t)(tb * 4 + sw) * 64 + lane) * F::BYTES, wres[q2]);
+        }
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) {
+            unsigned char *dst = rec + R::UB_OFF + ((size_t)(wave * NB + tb) * 64 + lane) * 4 * R::UB_ELT;
+            if constexpr (PRECISE) {
+                *(f32x4 *)dst = ures[tb];
+            } else {
+                typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+                *(half4 *)dst = half4{(_Float16)ures[tb][0], (_Float16)ures[tb][1],
+                                      (_Float16)ures[tb][2], (_Float16)ures[tb][3]};
+            }
         }
     }
 }
@@ -570,7 +745,7 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
     if (nch > 0) {
         fetch(0);
         commit(0);
-        __syncthreads();
+        lds_barrier();
     }
     for (int jc = 0; jc < nch; ++jc) {
         const int buf = (CFG::NBUF == 2) ? (jc & 1) : 0;
@@ -608,8 +783,18 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
                 aw = F::mma(F::load(B + R::W_OFF + fo), bS[s], aw);
                 aq = F::mma(F::load(B + R::QG_OFF + fo), bS[s], aq);
             }
-            const f32x4 ub = *(const f32x4 *)(B + R::SHARED_BYTES +
-                                              ((size_t)(wave * NB + tb) * 64 + lane) * 16);
+            const unsigned char *ubp = B + R::SHARED_BYTES +
+                                       ((size_t)(wave * NB + tb) * 64 + lane) * 4 * R::UB_ELT;
+            f32x4 ub;
+            if constexpr (PRECISE) {
+                ub = *(const f32x4 *)ubp;
+            } else {
+                typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+                const half4 hv = *(const half4 *)ubp;
+                const float us = *(const float *)(B + R::UBS_OFF);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ub[i] = (float)hv[i] * us;
+            }
             U[tb] = ub - aw * sscale;
             O[tb] = aq * sscale;
         }
@@ -669,11 +854,11 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
 
         if (jc + 1 < nch) {
             if (CFG::NBUF == 1) {
-                __syncthreads();            // everyone is done with the single buffer
+                lds_barrier();            // everyone is done with the single buffer
                 fetch(jc + 1);
             }
             commit(CFG::NBUF == 2 ? ((jc + 1) & 1) : 0);
-            __syncthreads();
+            lds_barrier();
         }
     }
 
@@ -691,9 +876,20 @@ static hipError_t launch_prefill_t(const PrefillArgs &a) {
     constexpr bool PRECISE = std::is_same<Tin, float>::value;
     const int64_t slots = num_slots(a.T, a.N, C);
     if ((a.stages & 1) && slots > 0) {
-        dim3 grid((unsigned)slots, (unsigned)a.H);
-        intra_kernel<C, Tin, PRECISE><<<grid, 64 * kIntraWaves, 0, a.stream>>>(a);
-        hipError_t e = hipGetLastError();
+        // persistent workgroups: one per CU (the LDS footprint allows one), each
+        // walking tiles blockIdx.x, blockIdx.x + gridDim.x, ...
+        int dev = 0, cus = 0;
+        hipError_t e = hipGetDevice(&dev);
+        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return e;
+        const int64_t ntiles = slots * a.H;
+#ifdef KDA_INTRA_ONE_TILE_PER_GROUP
+        const int64_t grid = ntiles;
+#else
+        const int64_t grid = ntiles < (int64_t)cus ? ntiles : (int64_t)cus;
+#endif
+        intra_kernel<C, Tin, PRECISE><<<(unsigned)grid, 64 * kIntraWaves, 0, a.stream>>>(a, ntiles);
+        e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     const int nchains = a.N * a.H;

@@ -219,7 +219,10 @@ def unpack_record(raw: np.ndarray, C: int, precise: bool):
     Wf, Qf, Kf, Mf = take(NB * 4), take(NB * 4), take(8 * CS), take(NB * CS)
     gam = raw[off:off + 512].view(np.float32).astype(np.float64)
     off += 512
-    ub = raw[off:off + 8 * NB * 64 * 16].view(np.float32).astype(np.float64).reshape(8, NB, 64, 4)
+    ub_scale = float(raw[off:off + 4].view(np.float32)[0])
+    off += 16
+    ub = (raw[off:off + 8 * NB * 64 * 4 * esz].view(elt).astype(np.float64).reshape(8, NB, 64, 4)
+          * ub_scale)
     W = np.zeros((C, 128)); QG = np.zeros((C, 128)); KG = np.zeros((CP, 128)); M = np.zeros((C, CP))
     UB = np.zeros((C, 128))
     for lane in range(64):
