@@ -25,6 +25,10 @@
  * A_log, dt_bias and the states are always fp32; q, k and v share the input
  * dtype; o has its own dtype.
  *
+ * Alignment: q, k, v, g, dt_bias, o and the states must be 16-byte aligned,
+ * beta_raw and A_log 4-byte aligned (any allocation from hipMalloc is);
+ * a misaligned pointer is rejected with KDA_ERR_INVALID_ARG.
+ *
  * Errors: every entry point returns a status. Argument checks run on the host
  * before any HIP call; a failed check enqueues nothing. kda_last_error() gives
  * a human-readable detail for the last failure on the calling thread.

@@ -6,6 +6,8 @@
 
 #include <cmath>
 #include <cstdio>
+#include <initializer_list>
+#include <utility>
 #include <string>
 #include <vector>
 
@@ -40,6 +42,16 @@ kda_status_t check_common(int64_t H, int32_t K, int32_t V, float scale, float lo
         return fail(KDA_ERR_INVALID_ARG, "lower_bound must lie in [-5, 0)");
     if (!valid_dtype(in_dtype)) return fail(KDA_ERR_UNSUPPORTED, "unknown input dtype");
     if (!valid_dtype(o_dtype)) return fail(KDA_ERR_UNSUPPORTED, "unknown output dtype");
+    return KDA_OK;
+}
+
+// Vector loads and stores and the global->LDS copies move 16 bytes per lane,
+// so every tensor pointer except the scalar per-token/per-head arrays
+// (beta_raw, A_log) must be 16-byte aligned. NULL passes.
+kda_status_t check_aligned16(std::initializer_list<std::pair<const void *, const char *>> ptrs) {
+    for (const auto &pn : ptrs)
+        if (((uintptr_t)pn.first & 15) != 0)
+            return fail(KDA_ERR_INVALID_ARG, std::string(pn.second) + " must be 16-byte aligned");
     return KDA_OK;
 }
 
@@ -122,6 +134,12 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
                                            std::to_string(workspace_bytes));
     if (((uintptr_t)workspace & 255) != 0)
         return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    st = check_aligned16({{q, "q"}, {k, "k"}, {v, "v"}, {g, "g"}, {dt_bias, "dt_bias"},
+                          {initial_state, "initial_state"}, {final_state, "final_state"},
+                          {o, "o"}});
+    if (st != KDA_OK) return st;
+    if (((uintptr_t)beta_raw & 3) != 0 || ((uintptr_t)A_log & 3) != 0)
+        return fail(KDA_ERR_INVALID_ARG, "beta_raw and A_log must be 4-byte aligned");
 
     kda::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta_raw = beta_raw; a.A_log = A_log; a.dt_bias = dt_bias;
@@ -179,8 +197,11 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
         return fail(KDA_ERR_INVALID_ARG, "a required pointer is NULL");
     if ((int64_t)B * H > ((int64_t)1 << 31) - 1)
         return fail(KDA_ERR_INVALID_ARG, "B * H too large");
-    if (((uintptr_t)state & 15) != 0)
-        return fail(KDA_ERR_INVALID_ARG, "state must be 16-byte aligned");
+    st = check_aligned16({{q, "q"}, {k, "k"}, {v, "v"}, {g, "g"}, {dt_bias, "dt_bias"},
+                          {state, "state"}, {o, "o"}});
+    if (st != KDA_OK) return st;
+    if (((uintptr_t)beta_raw & 3) != 0 || ((uintptr_t)A_log & 3) != 0)
+        return fail(KDA_ERR_INVALID_ARG, "beta_raw and A_log must be 4-byte aligned");
 
     kda::DecodeArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta_raw = beta_raw; a.A_log = A_log; a.dt_bias = dt_bias;

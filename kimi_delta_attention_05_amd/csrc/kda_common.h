@@ -123,6 +123,29 @@ __device__ __forceinline__ float wave_max(float x) {
     return x;
 }
 
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xF, 0xF, true);
+}
+
+// Max over the 64 lanes of a non-negative x, returned wave-uniform. For
+// non-negative IEEE floats the unsigned order of the bit patterns is the
+// numeric order, so the cross-lane part runs on integers: DPP within each row
+// of 16 lanes, then the four row maxima through scalar registers (no LDS
+// round trip).
+__device__ __forceinline__ float wave_max_nonneg(float x) {
+    uint32_t u = __float_as_uint(x);
+    u = max(u, dpp_u<0xB1>(u));     // quad_perm [1,0,3,2]
+    u = max(u, dpp_u<0x4E>(u));     // quad_perm [2,3,0,1]
+    u = max(u, dpp_u<0x141>(u));    // row_half_mirror
+    u = max(u, dpp_u<0x140>(u));    // row_mirror
+    const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)u, 0);
+    const uint32_t b = (uint32_t)__builtin_amdgcn_readlane((int)u, 16);
+    const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)u, 32);
+    const uint32_t d = (uint32_t)__builtin_amdgcn_readlane((int)u, 48);
+    return __uint_as_float(max(max(a, b), max(c, d)));
+}
+
 __device__ __forceinline__ float wave_sum(float x) {
     x = row16_sum(x);
     x += __shfl_xor(x, 16);

@@ -666,19 +666,34 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
 }
 
 // =============================================================================
-// Inter-chunk kernel: one workgroup (4 waves) per (sequence, head, 64-row half
-// of the state); each wave owns 16 state rows held in MFMA accumulators as S^T.
-// Shared per-chunk operands are staged through LDS (double-buffered when they
-// fit) while the previous chunk computes.
+// Inter-chunk kernel: two workgroups (4 waves each) per (sequence, head), one
+// per 64-row half of the state; each wave owns 16 state rows, held in
+// registers as S^T accumulator tiles. The per-chunk operands are copied
+// global -> LDS by the DMA path (no register staging), one chunk ahead into a
+// second buffer when two fit.
 // =============================================================================
 template <int C, bool PRECISE>
 struct InterCfg {
     using R = Record<C, PRECISE>;
-    static constexpr size_t BUF = R::SHARED_BYTES + 4 * R::UB_VB_BYTES;
+    static constexpr int SH_BLOCKS = (int)((R::SHARED_BYTES + 1023) / 1024);   // 1 KiB copies
+    static constexpr size_t UB_LDS = (size_t)SH_BLOCKS * 1024;   // this half's Ub in LDS
+    static constexpr int UB_BLOCKS = (int)(4 * R::UB_VB_BYTES / 1024);
+    static constexpr int BLOCKS = SH_BLOCKS + UB_BLOCKS;
+    static constexpr size_t BUF = (size_t)BLOCKS * 1024;
     static constexpr int NBUF = (2 * BUF <= 160 * 1024) ? 2 : 1;
-    static constexpr int N16 = (int)(BUF / 16);
-    static constexpr int PER = (N16 + 255) / 256;
+    static_assert(4 * R::UB_VB_BYTES % 1024 == 0, "the Ub half is whole 1 KiB blocks");
+    // The last shared block reads past SHARED_BYTES into the record's own Ub area.
+    static_assert(UB_LDS <= R::BYTES, "shared-block over-read stays inside the record");
 };
+
+template <typename T> __device__ __forceinline__ void store4(T *p, const f32x4 &x);
+template <> __device__ __forceinline__ void store4<float>(float *p, const f32x4 &x) {
+    *(f32x4 *)p = x;
+}
+template <> __device__ __forceinline__ void store4<__bf16>(__bf16 *p, const f32x4 &x) {
+    typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+    *(bf16x4 *)p = bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
+}
 
 template <int C, typename Tout, bool PRECISE>
 __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
@@ -698,7 +713,8 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
     const int H = p.H;
     const int n = chain / H, h = chain % H;
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int lr = lane & 15, lg = lane >> 4;
     const int vb = 4 * vg + wave;
     const int vrow = 16 * vb + lr;               // this lane's state row
@@ -717,44 +733,43 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
         else S[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    auto rec_of = [&](int jc) -> const unsigned char * {
-        return p.ws + ((size_t)(slot0 + jc) * H + h) * R::BYTES;
-    };
-    f32x4 stage[CFG::PER];
-    auto fetch = [&](int jc) {
-        const unsigned char *r = rec_of(jc);
-        const f32x4 *sh = (const f32x4 *)r;
-        const f32x4 *ub = (const f32x4 *)(r + R::UB_OFF + (size_t)4 * vg * R::UB_VB_BYTES);
-        constexpr int SH16 = (int)(R::SHARED_BYTES / 16);
+    // DMA copy of chunk jc's record into LDS buffer buf: the shared operands,
+    // then this half's Ub blocks; wave w copies the 1 KiB blocks w, w + 4, ...
+    // Addresses are a wave-uniform base plus the lane's 16-byte offset.
+    const unsigned char *rec0 = p.ws + ((size_t)slot0 * H + h) * R::BYTES + 1024 * wave;
+    const size_t rec_step = (size_t)H * R::BYTES;
+    const uint32_t lane16 = 16u * (uint32_t)lane;
+    auto fetch = [&](int jc, int buf) {
+        const unsigned char *r = rec0 + (size_t)jc * rec_step;
+        const unsigned char *u = r + R::UB_OFF + (size_t)4 * vg * R::UB_VB_BYTES;
+        unsigned char *dst = smem + (size_t)buf * CFG::BUF + 1024 * wave;
 #pragma unroll
-        for (int i = 0; i < CFG::PER; ++i) {
-            const int idx = tid + 256 * i;
-            if (idx < CFG::N16) stage[i] = (idx < SH16) ? sh[idx] : ub[idx - SH16];
-        }
-    };
-    auto commit = [&](int buf) {
-        f32x4 *dst = (f32x4 *)(smem + (size_t)buf * CFG::BUF);
+        for (int i = 0; i < (CFG::SH_BLOCKS + 3) / 4; ++i)
+            if (4 * i + 3 < CFG::SH_BLOCKS || 4 * i + wave < CFG::SH_BLOCKS)
+                copy16_to_lds(r + 4096 * i + lane16, dst + 4096 * i);
 #pragma unroll
-        for (int i = 0; i < CFG::PER; ++i) {
-            const int idx = tid + 256 * i;
-            if (idx < CFG::N16) dst[idx] = stage[i];
-        }
+        for (int i = 0; i < (CFG::UB_BLOCKS + 3) / 4; ++i)
+            if (4 * i + 3 < CFG::UB_BLOCKS || 4 * i + wave < CFG::UB_BLOCKS)
+                copy16_to_lds(u + 4096 * i + lane16, dst + CFG::UB_LDS + 4096 * i);
     };
 
-    Tout *__restrict__ o = (Tout *)p.o;
+    // this lane writes o[t][h][16 vb + 4 lg .. + 3] for t = chunk start + 16 tb + lr
+    Tout *__restrict__ o = (Tout *)p.o + ((size_t)(s0 + lr) * H + h) * kHeadDim + 16 * vb + 4 * lg;
+    const size_t o_tb = (size_t)16 * H * kHeadDim;
+
     if (nch > 0) {
-        fetch(0);
-        commit(0);
+        fetch(0, 0);
+        wait_vmem();
         lds_barrier();
     }
     for (int jc = 0; jc < nch; ++jc) {
         const int buf = (CFG::NBUF == 2) ? (jc & 1) : 0;
-        if (CFG::NBUF == 2 && jc + 1 < nch) fetch(jc + 1);
+        if (CFG::NBUF == 2 && jc + 1 < nch) fetch(jc + 1, buf ^ 1);
         const unsigned char *B = smem + (size_t)buf * CFG::BUF;
-        const int64_t t0 = s0 + (int64_t)jc * C;
         const int L = (len - (int64_t)jc * C) < C ? (int)(len - (int64_t)jc * C) : C;
 
-        // B operand from the state: k-step s covers channels 32s + kperm(lg, e)
+        // state operand: k-step s covers channels 32 s + kperm(lg, e); it is the
+        // B operand of W S^T (columns v) and the A operand of S qg^T (rows v)
         float sscale = 1.0f;
         if constexpr (!PRECISE) {
             float m = 0.f;
@@ -762,7 +777,7 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
             for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(S[kb][i]));
-            sscale = pow2_scale_for(wave_max(m), 14);
+            sscale = pow2_scale_for(wave_max_nonneg(m), 14);
         }
         typename F::T bS[4];
 #pragma unroll
@@ -772,7 +787,8 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
             bS[s] = F::make(x, inv_pow2(sscale));
         }
 
-        // U = Ub - W S^T ; O1 = qg S^T
+        // U = Ub - W S^T  (tile [t][v]: lane holds t = 16 tb + 4 lg + i, v = vrow)
+        // O^T = S qg^T    (tile [v][t]: lane holds v = 16 vb + 4 lg + i, t = 16 tb + lr)
         f32x4 U[NB], O[NB];
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb) {
@@ -781,9 +797,9 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
             for (int s = 0; s < 4; ++s) {
                 const size_t fo = ((size_t)(tb * 4 + s) * 64 + lane) * F::BYTES;
                 aw = F::mma(F::load(B + R::W_OFF + fo), bS[s], aw);
-                aq = F::mma(F::load(B + R::QG_OFF + fo), bS[s], aq);
+                aq = F::mma(bS[s], F::load(B + R::QG_OFF + fo), aq);
             }
-            const unsigned char *ubp = B + R::SHARED_BYTES +
+            const unsigned char *ubp = B + CFG::UB_LDS +
                                        ((size_t)(wave * NB + tb) * 64 + lane) * 4 * R::UB_ELT;
             f32x4 ub;
             if constexpr (PRECISE) {
@@ -796,10 +812,11 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
                 for (int i = 0; i < 4; ++i) ub[i] = (float)hv[i] * us;
             }
             U[tb] = ub - aw * sscale;
-            O[tb] = aq * sscale;
+            O[tb] = aq;
         }
 
-        // B operand from U: k-step s over t covers rows 32s + kperm(lg, e)
+        // U operand: k-step s over t covers rows 32 s + kperm(lg, e); it is the
+        // B operand of kg^T U (columns v) and the A operand of U^T M^T (rows v)
         float uscale = 1.0f;
         if constexpr (!PRECISE) {
             float m = 0.f;
@@ -807,7 +824,7 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
             for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(U[tb][i]));
-            uscale = pow2_scale_for(wave_max(m), 14);
+            uscale = pow2_scale_for(wave_max_nonneg(m), 14);
         }
         typename F::T bU[CS];
 #pragma unroll
@@ -821,22 +838,18 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
             bU[s] = F::make(x, inv_pow2(uscale));
         }
 
-        // O += M U, then store the valid rows
+        // O^T += U^T M^T; the lane stores four consecutive channels of row t
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb) {
             f32x4 am = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < CS; ++s) {
                 if (32 * s > 16 * tb + 15) continue;       // M is lower triangular
-                am = F::mma(F::load(B + R::M_OFF + ((size_t)(tb * CS + s) * 64 + lane) * F::BYTES),
-                            bU[s], am);
+                am = F::mma(bU[s], F::load(B + R::M_OFF + ((size_t)(tb * CS + s) * 64 + lane) * F::BYTES),
+                            am);
             }
-            const f32x4 out = O[tb] + am * uscale;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int t = 16 * tb + 4 * lg + i;
-                if (t < L) o[((size_t)(t0 + t) * H + h) * kHeadDim + vrow] = from_f32<Tout>(out[i]);
-            }
+            const f32x4 out = O[tb] * sscale + am * uscale;
+            if (16 * tb + lr < L) store4<Tout>(o + tb * o_tb, out);
         }
 
         // S^T <- diag(GamC) S^T + kg^T U
@@ -852,13 +865,14 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
             S[kb] = S[kb] * gv + acc * uscale;
         }
 
+        o += (size_t)C * H * kHeadDim;
         if (jc + 1 < nch) {
             if (CFG::NBUF == 1) {
                 lds_barrier();            // everyone is done with the single buffer
-                fetch(jc + 1);
+                fetch(jc + 1, 0);
             }
-            commit(CFG::NBUF == 2 ? ((jc + 1) & 1) : 0);
-            lds_barrier();
+            wait_vmem();                  // this wave's copies have landed ...
+            lds_barrier();                // ... and everyone else's
         }
     }
 
