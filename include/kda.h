@@ -21,7 +21,7 @@
  *   q, k, g : [T, H, K]      v, o : [T, H, V]      beta_raw : [T, H]
  *   A_log   : [H] fp32       dt_bias : [H, K] fp32
  *   states  : [N, H, V, K] fp32 (value-first)
- * K and V must both be 128 (the contract's head dimension). g, beta_raw,
+ * K and V must both be 128 (the contract's head dimension); 1 <= H <= 65536. g, beta_raw,
  * A_log, dt_bias and the states are always fp32; q, k and v share the input
  * dtype; o has its own dtype.
  *

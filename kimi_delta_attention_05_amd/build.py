@@ -18,6 +18,10 @@ def hipcc_command(out: str) -> list:
              "-fPIC", "-shared", "-I", os.path.join(ROOT, "include"), "-I", CSRC,
              # packed fp32 VALU forms are kept out of generated code
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             # MFMA accumulators in ordinary VGPRs: the state and the tiles that
+             # VALU code rescales every chunk would otherwise be copied between
+             # the accumulation registers and the VGPRs on each use
+             "-mllvm", "-amdgpu-mfma-vgpr-form=true",
              "-Wno-unused-result", "-o", out]
             + [os.path.join(CSRC, s) for s in SOURCES])
 

@@ -32,7 +32,7 @@ bool valid_dtype(kda_dtype_t d) { return d == KDA_F32 || d == KDA_BF16; }
 // Checks shared by both entry points. Returns KDA_OK or an error with detail.
 kda_status_t check_common(int64_t H, int32_t K, int32_t V, float scale, float lower_bound,
                           kda_dtype_t in_dtype, kda_dtype_t o_dtype) {
-    if (H < 1) return fail(KDA_ERR_INVALID_ARG, "H must be >= 1");
+    if (H < 1 || H > 65536) return fail(KDA_ERR_INVALID_ARG, "H must lie in [1, 65536]");
     if (K != 128 || V != 128)
         return fail(KDA_ERR_UNSUPPORTED, "only K = V = 128 is supported (got K=" +
                                              std::to_string(K) + ", V=" + std::to_string(V) + ")");
@@ -81,8 +81,8 @@ const char *kda_last_error(void) { return g_last_error.c_str(); }
 size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H,
                                     int32_t K, int32_t V, int32_t chunk_size,
                                     kda_dtype_t in_dtype) {
-    if (total_tokens < 0 || num_seqs < 1 || H < 1) {
-        fail(KDA_ERR_INVALID_ARG, "need total_tokens >= 0, num_seqs >= 1, H >= 1");
+    if (total_tokens < 0 || num_seqs < 1 || H < 1 || H > 65536) {
+        fail(KDA_ERR_INVALID_ARG, "need total_tokens >= 0, num_seqs >= 1, 1 <= H <= 65536");
         return 0;
     }
     if (K != 128 || V != 128) { fail(KDA_ERR_UNSUPPORTED, "only K = V = 128 is supported"); return 0; }

@@ -50,22 +50,42 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Wait until this wave's outstanding global loads (including global->LDS
-// copies) have landed.
+// copies) have landed. Issued through the builtin (gfx9 encoding: vmcnt = 0,
+// expcnt and lgkmcnt left at their maxima) rather than inline asm, so that the
+// compiler's own wait insertion sees it and does not add another vmcnt(0)
+// before the next LDS read of copied data, which would also wait for every
+// store issued since.
 __device__ __forceinline__ void wait_vmem() {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("" ::: "memory");
 }
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
-// Asynchronous copy of 16 bytes per lane from global memory straight into LDS
-// (gfx950 global_load_lds_dwordx4): lane i of the wave writes lds_wave_base +
-// 16 i, so a wave fills one contiguous 1 KiB block. lds_wave_base must be the
-// same for the whole wave.
-__device__ __forceinline__ void copy16_to_lds(const void *src, void *lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_wave_base, 16, 0, 0);
+// Asynchronous copies from global memory straight into LDS (global->LDS DMA,
+// no registers); completion is tracked by vmcnt like any vector load.
+// Buffer resource for the byte range [base, base + bytes), gfx9 word-3 format
+// bits; a read outside the range returns zeros instead of faulting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                             0x00020000);
 }
-__device__ __forceinline__ void copy4_to_lds(const void *src, void *lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)lds_wave_base, 4, 0, 0);
+
+// 16 bytes per lane through a buffer resource (buffer_load_dwordx4 ... lds):
+// lane i reads rsrc + voffset_i + soffset and writes lds_wave_base + 16 i, so a
+// wave fills one contiguous 1 KiB block; lds_wave_base must be wave-uniform.
+// The buffer (MUBUF) form is used rather than the global one because the
+// compiler treats a FLAT-encoded copy as a possible out-of-order LDS access
+// and then drops every later LDS wait to a count of zero.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
+                                              uint32_t soffset, void *lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave_base, 16, voffset, soffset, 0, 0);
+}
+
+__device__ __forceinline__ void copy4_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
+                                             uint32_t soffset, void *lds_wave_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave_base, 4, voffset, soffset, 0, 0);
 }
 
 // 8 consecutive input elements kept in their storage format (prefetch buffers).

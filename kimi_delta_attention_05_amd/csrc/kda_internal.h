@@ -47,12 +47,14 @@ struct ChunkGeom {
 // One workspace record per (chunk slot, head). Everything the inter-chunk
 // kernel needs, stored in MFMA operand order so that each lane reads 16 (or 32)
 // contiguous bytes per fragment:
-//   W    [NB tb][4 s][64 lane][8]   rows t, k over key channels   (Tst)
+//   -W   [NB tb][4 s][64 lane][8]   rows t, k over key channels   (Tst), negated
+//                                   so that U = Ub + (-W) S^T is one accumulation
 //   qg   [NB tb][4 s][64 lane][8]   rows t, k over key channels   (Tst)
 //   kgT  [8 kb][CS s][64 lane][8]   rows key channel, k over t    (Tst)
 //   M    [NB tb][CS s][64 lane][8]  rows t, k over t'             (Tst)
 //   GamC [128]                      fp32 total decay of the chunk
-//   UbSc [4]                        fp32; [0] = power-of-two scale of Ub
+//   UbSc [4]                        fp32; [0] = power-of-two scale of Ub, 0 if
+//                                   every v of the chunk is zero
 //   Ub   [8 vb][NB tb][64 lane][4]  accumulator tiles of T V / UbSc[0] (Tub)
 // Tst and Tub are fp16 when the inputs are bf16 (W, qg, kg, M are bounded by 1
 // in magnitude; Ub is stored scaled so that it is bounded by 2^15) and fp32

@@ -102,8 +102,12 @@ __device__ __forceinline__ float inv_pow2(float s) {   // exact 1/s for s = 2^e
 
 // Locate chunk `slot` of the packed batch: returns false for an unused slot.
 template <int C>
-__device__ __forceinline__ bool locate_slot(const int64_t *__restrict__ cu, int N, int64_t slot,
+__device__ __forceinline__ bool locate_slot(const int64_t *cu_ptr, int N, int64_t slot,
                                             int &n, int64_t &t0, int &L) {
+    // the offsets are read-only for the whole launch: the constant address
+    // space lets these wave-uniform reads go through the scalar cache
+    const __attribute__((address_space(4))) int64_t *cu =
+        (const __attribute__((address_space(4))) int64_t *)cu_ptr;
     if (N <= 0) return false;
     int lo = 0, hi = N - 1;
     while (lo < hi) {                     // largest n with floor(cu[n]/C) + n <= slot
@@ -141,7 +145,8 @@ struct RawLayout {                    // raw inputs of one tile inside the three
     static constexpr size_t V = K + (size_t)C * kHeadDim * sizeof(Tin);
     static constexpr size_t G = V + (size_t)C * kHeadDim * sizeof(Tin);
     static constexpr size_t B = G + (size_t)C * kHeadDim * 4;
-    static constexpr size_t BYTES = B + (size_t)C * 4;
+    static constexpr size_t DT = B + (size_t)C * 4;              // dt_bias row of the head
+    static constexpr size_t BYTES = DT + (size_t)kHeadDim * 4;
     static constexpr int NQ16 = (int)((size_t)C * kHeadDim * sizeof(Tin) / 16);  // 16-B pieces
     static constexpr int NG16 = C * kHeadDim * 4 / 16;
     static constexpr int PER = (3 * NQ16 + NG16 + 64 * kIntraWaves - 1) / (64 * kIntraWaves);
@@ -149,7 +154,8 @@ struct RawLayout {                    // raw inputs of one tile inside the three
 };
 
 // Start copying one tile's raw inputs into LDS (layout RawLayout): 16-byte
-// pieces of q, k, v (row-major [C][128]) and g, plus beta, as asynchronous
+// pieces of q, k, v (row-major [C][128]) and g, plus beta and the head's
+// dt_bias, as asynchronous
 // global->LDS copies; piece idx = tid + NT * i lands at byte 16 idx, so each
 // wave fills contiguous 1 KiB blocks. Rows past the chunk end copy the chunk's
 // last row (in bounds for a valid tile) and are masked where used. The caller
@@ -159,31 +165,43 @@ __device__ __forceinline__ void stage_raw(const PrefillArgs &p, int h, int64_t t
                                           unsigned char *lds) {
     using RL = RawLayout<C, Tin>;
     constexpr int NT = 64 * kIntraWaves;
-    constexpr int PPR = kHeadDim * (int)sizeof(Tin) / 16;   // pieces per q/k/v row
-    const int wave = tid >> 6;
+    constexpr uint32_t RB = kHeadDim * (uint32_t)sizeof(Tin);   // bytes per q/k/v row
+    constexpr int PPR = (int)RB / 16;                            // pieces per q/k/v row
+    static_assert(RL::NQ16 % 64 == 0 && RL::NG16 % 64 == 0, "a wave's pieces stay in one array");
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    // resources over rows t0 .. t0 + L - 1 of head h (token stride H rows)
+    const size_t row0 = (size_t)t0 * p.H + h;
+    const uint32_t hq = (uint32_t)p.H * RB, hg = (uint32_t)p.H * 512u;
+    const uint32_t span = (uint32_t)(L - 1);
+    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const unsigned char *)p.q + row0 * RB, span * hq + RB);
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const unsigned char *)p.k + row0 * RB, span * hq + RB);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const unsigned char *)p.v + row0 * RB, span * hq + RB);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g + row0 * kHeadDim, span * hg + 512u);
 #pragma unroll
     for (int i = 0; i < RL::PER; ++i) {
-        const int idx = tid + NT * i;
         const int wbase = 64 * wave + NT * i;                   // first piece of this wave
         if (wbase >= 3 * RL::NQ16 + RL::NG16) break;            // whole wave past the end
-        const void *src;
-        if (idx < 3 * RL::NQ16) {
-            const int arr = idx / RL::NQ16, w = idx % RL::NQ16;
-            int t = w / PPR;
-            t = t < L ? t : L - 1;
-            const unsigned char *base = (const unsigned char *)(arr == 0 ? p.q : arr == 1 ? p.k : p.v);
-            src = base + ((size_t)(t0 + t) * p.H + h) * kHeadDim * sizeof(Tin) + (size_t)(w % PPR) * 16;
+        const uint32_t idx = (uint32_t)(wbase + lane);
+        if (wbase < 3 * RL::NQ16) {
+            const int arr = wbase / RL::NQ16;
+            const uint32_t w = idx % (uint32_t)RL::NQ16;
+            const uint32_t t = min(w / (uint32_t)PPR, span);
+            const uint32_t off = t * hq + (w % (uint32_t)PPR) * 16u;
+            copy16_to_lds(arr == 0 ? rq : arr == 1 ? rk : rv, off, 0, lds + (size_t)wbase * 16);
         } else {
-            const int w = idx - 3 * RL::NQ16;
-            int t = w / 32;
-            t = t < L ? t : L - 1;
-            src = p.g + ((size_t)(t0 + t) * p.H + h) * kHeadDim + (w % 32) * 4;
+            const uint32_t w = idx - 3u * RL::NQ16;
+            const uint32_t t = min(w / 32u, span);
+            copy16_to_lds(rg, t * hg + (w % 32u) * 16u, 0, lds + (size_t)wbase * 16);
         }
-        copy16_to_lds(src, lds + (size_t)wbase * 16);
     }
     if (wave == 0) {                                             // beta, one float per row
-        const int t = tid < L ? tid : L - 1;
-        if (tid < C) copy4_to_lds(p.beta_raw + (size_t)(t0 + t) * p.H + h, lds + RL::B);
+        const __amdgpu_buffer_rsrc_t rb =
+            make_rsrc(p.beta_raw + row0, span * (uint32_t)p.H * 4u + 4u);
+        const uint32_t t = min((uint32_t)tid, span);
+        if (tid < C) copy4_to_lds(rb, t * (uint32_t)p.H * 4u, 0, lds + RL::B);
+    } else if (wave == 1) {                                      // dt_bias[h], 512 bytes
+        const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dt_bias + (size_t)h * kHeadDim, 512u);
+        if (lane < 32) copy16_to_lds(rd, 16u * (uint32_t)lane, 0, lds + RL::DT);
     }
 }
 
@@ -205,8 +223,8 @@ __device__ __forceinline__ int intra_job_order(int slot) {
     if constexpr (C == 64) {
         // M job a*2+s: 0 = D, 1 = zero, 2 = O+D, 3 = zero, 4 = O+O, 5 = D, 6 = O+O, 7 = O+D
         // (D: a diagonal block on the fp32 MFMA, O: an off-diagonal fp16 block)
-        constexpr int first[8] = {2, 7, 0, 5, 1, 3, 4, 6};
-        return slot < 8 ? first[slot] : slot;
+        // first[8] = {2, 7, 0, 5, 1, 3, 4, 6}, one nibble per slot
+        return slot < 8 ? (int)((0x64315072u >> (4 * slot)) & 15u) : slot;
     } else {
         return slot;
     }
@@ -242,7 +260,8 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
     __shared__ float sVmax[NW];
 
     const int H = p.H;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
     const int lr = lane & 15, lg = lane >> 4;
     const int c8 = 8 * lr;
     const float lb2 = p.lower_bound * kLog2e;
@@ -273,14 +292,20 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
         const int Lc = L;
         const int64_t t0c = t0;
         unsigned char *rec = p.ws + (size_t)ti * R::BYTES;
+        // where the next tile lies, resolved now while nothing is in flight
+        int n_nx = 0, L_nx = 0;
+        int64_t t0_nx = 0;
+        const bool valid_nx = next < ntiles && locate_slot<C>(p.cu_seqlens, p.N, next / H, n_nx, t0_nx, L_nx);
 
         // ---- phase 1: a DPP row of 16 lanes per token, 8 channels per lane -------
         // gate: sigmoid(a (g + db)) = 1 / (1 + 2^(ga g + gb)), ga = -a log2e, gb = ga db;
         // 2^x overflows to inf for very negative arguments and 1/inf = 0, so this
         // form is exact at both ends.
-        const float ga = -fast_exp2(p.A_log[h] * kLog2e) * kLog2e;
+        const float alog = *(const __attribute__((address_space(4))) float *)(p.A_log + h);
+        const float ga = -fast_exp2(alog * kLog2e) * kLog2e;
         float gb[8];
-        load8(p.dt_bias + h * kHeadDim + c8, gb);
+        if constexpr (PF) load8((const float *)(sRaw + RL::DT) + c8, gb);   // staged with the tile
+        else load8(p.dt_bias + h * kHeadDim + c8, gb);
 #pragma unroll
         for (int e = 0; e < 8; ++e) gb[e] *= ga;
         float vreg[RIT][8], qv[RIT][8], kv[RIT][8], al[RIT][8], bet[RIT];
@@ -506,11 +531,13 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
         }
         // power-of-two scale of v for the fp16 product T v (exact)
         float vscale = 1.0f;
+        bool vinv_zero = false;                   // all v of the chunk are zero: Ub = 0
         if constexpr (!PRECISE) {
             float m = 0.f;
 #pragma unroll
             for (int w = 0; w < NW; ++w) m = fmaxf(m, sVmax[w]);
             vscale = pow2_scale_for(m, 9);          // |T v / vscale| <= 64 * 2^9 = 2^15
+            vinv_zero = !(m > 0.f);
         }
         const float vinv = inv_pow2(vscale);
         lds_barrier();
@@ -527,7 +554,7 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
             *(f32x4 *)&sP[t][c8] = f32x4{x[0], x[1], x[2], x[3]};
             *(f32x4 *)&sP[t][c8 + 4] = f32x4{x[4], x[5], x[6], x[7]};
         }
-        if (tid == 0) *(float *)(rec + R::UBS_OFF) = vscale;
+        if (tid == 0) *(float *)(rec + R::UBS_OFF) = (vinv_zero ? 0.0f : vscale);
         lds_barrier();
 
         // phase-5 operands that do not depend on T, built before the inverse ends:
@@ -551,7 +578,10 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
 
         // next tile: its raw inputs load during the inverse and the W / Ub products
         ti = next;
-        valid = ti < ntiles && locate_slot<C>(p.cu_seqlens, p.N, ti / H, n, t0, L);
+        valid = valid_nx;
+        n = n_nx;
+        t0 = t0_nx;
+        L = L_nx;
         if constexpr (PF) {
             lds_barrier();                      // the three tiles are free from here on
             if (valid) stage_raw<C, Tin>(p, (int)(ti % H), t0, L, tid, sRaw);
@@ -648,8 +678,12 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
 #pragma unroll
         for (int q2 = 0; q2 < 2; ++q2) {
             const int tb = 2 * (wave >> 2) + q2;
-            if (tb < NB)
-                F::store(rec + R::W_OFF + ((size_t)(tb * 4 + sw) * 64 + lane) * F::BYTES, wres[q2]);
+            if (tb < NB) {                      // stored negated: U = Ub + (-W) S^T
+                float x[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) x[e] = -wres[q2][e];
+                F::store(rec + R::W_OFF + ((size_t)(tb * 4 + sw) * 64 + lane) * F::BYTES, x);
+            }
         }
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb) {
@@ -701,6 +735,7 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
     using G = ChunkGeom<C>;
     using R = Record<C, PRECISE>;
     using F = Frag<PRECISE>;
+    using FT = typename F::T;
     using CFG = InterCfg<C, PRECISE>;
     constexpr int NB = G::NB, CS = G::CS;
     extern __shared__ __align__(16) unsigned char smem[];
@@ -724,8 +759,11 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
     const int nch = (int)((len + C - 1) / C);
     const int64_t slot0 = s0 / C + n;
 
-    // state S^T tiles: lane holds S[vrow][16 kb + 4 lg + i]
+    // State S^T tiles: lane holds S[vrow][16 kb + 4 lg + i]. On the fp16 path the
+    // registers hold S / sigma for a wave-uniform power of two sigma, chosen so
+    // that S / sigma converts to fp16 without overflow and U / sigma too.
     f32x4 S[8];
+    float sigma = 1.0f;
     const size_t sbase = ((size_t)chain * kHeadDim + vrow) * kHeadDim;
 #pragma unroll
     for (int kb = 0; kb < 8; ++kb) {
@@ -733,100 +771,169 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
         else S[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
-    // DMA copy of chunk jc's record into LDS buffer buf: the shared operands,
-    // then this half's Ub blocks; wave w copies the 1 KiB blocks w, w + 4, ...
-    // Addresses are a wave-uniform base plus the lane's 16-byte offset.
-    const unsigned char *rec0 = p.ws + ((size_t)slot0 * H + h) * R::BYTES + 1024 * wave;
+    // DMA copy of chunk jc's record into LDS buffer buf, in parts spread over
+    // the chunk: the shared operands, then this half's Ub blocks; wave w copies
+    // the 1 KiB blocks w, w + 4, ... through a buffer resource covering exactly
+    // the record, with the wave-uniform part of each offset in soffset.
+    constexpr int SHI = (CFG::SH_BLOCKS + 3) / 4, UBI = (CFG::UB_BLOCKS + 3) / 4;
+    constexpr int NCP = SHI + UBI;
+    const unsigned char *rec0 = p.ws + ((size_t)slot0 * H + h) * R::BYTES;
     const size_t rec_step = (size_t)H * R::BYTES;
     const uint32_t lane16 = 16u * (uint32_t)lane;
-    auto fetch = [&](int jc, int buf) {
-        const unsigned char *r = rec0 + (size_t)jc * rec_step;
-        const unsigned char *u = r + R::UB_OFF + (size_t)4 * vg * R::UB_VB_BYTES;
+    const uint32_t ub_off = (uint32_t)(R::UB_OFF + (size_t)4 * vg * R::UB_VB_BYTES);
+    auto fetch = [&](int jc, int buf, int k0, int k1) {
+        const __amdgpu_buffer_rsrc_t r = make_rsrc(rec0 + (size_t)jc * rec_step, (uint32_t)R::BYTES);
         unsigned char *dst = smem + (size_t)buf * CFG::BUF + 1024 * wave;
 #pragma unroll
-        for (int i = 0; i < (CFG::SH_BLOCKS + 3) / 4; ++i)
-            if (4 * i + 3 < CFG::SH_BLOCKS || 4 * i + wave < CFG::SH_BLOCKS)
-                copy16_to_lds(r + 4096 * i + lane16, dst + 4096 * i);
-#pragma unroll
-        for (int i = 0; i < (CFG::UB_BLOCKS + 3) / 4; ++i)
-            if (4 * i + 3 < CFG::UB_BLOCKS || 4 * i + wave < CFG::UB_BLOCKS)
-                copy16_to_lds(u + 4096 * i + lane16, dst + CFG::UB_LDS + 4096 * i);
+        for (int k = 0; k < NCP; ++k) {
+            if (k < k0 || k >= k1) continue;
+            if (k < SHI) {
+                if (4 * k + 3 < CFG::SH_BLOCKS || 4 * k + wave < CFG::SH_BLOCKS)
+                    copy16_to_lds(r, lane16, 1024u * wave + 4096u * k, dst + 4096 * k);
+            } else {
+                const int i = k - SHI;
+                if (4 * i + 3 < CFG::UB_BLOCKS || 4 * i + wave < CFG::UB_BLOCKS)
+                    copy16_to_lds(r, lane16, ub_off + 1024u * wave + 4096u * i,
+                                  dst + CFG::UB_LDS + 4096 * i);
+            }
+        }
     };
 
-    // this lane writes o[t][h][16 vb + 4 lg .. + 3] for t = chunk start + 16 tb + lr
+    // this lane writes o[t][h][16 vb + 4 lg .. + 3] for t = chunk start + 16 tb + lr;
+    // a chunk's outputs are stored while the next chunk computes
     Tout *__restrict__ o = (Tout *)p.o + ((size_t)(s0 + lr) * H + h) * kHeadDim + 16 * vb + 4 * lg;
-    const size_t o_tb = (size_t)16 * H * kHeadDim;
+    const size_t o_tb = (size_t)16 * H * kHeadDim, o_chunk = (size_t)C * H * kHeadDim;
+    f32x4 pend[NB];
+    int Lp = 0;
+    auto store_pending = [&](Tout *dst) {
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+            if (16 * tb + lr < Lp) store4<Tout>(dst + tb * o_tb, pend[tb]);
+    };
 
     if (nch > 0) {
-        fetch(0, 0);
+        fetch(0, 0, 0, NCP);
         wait_vmem();
         lds_barrier();
     }
     for (int jc = 0; jc < nch; ++jc) {
         const int buf = (CFG::NBUF == 2) ? (jc & 1) : 0;
-        if (CFG::NBUF == 2 && jc + 1 < nch) fetch(jc + 1, buf ^ 1);
+        const bool ahead = CFG::NBUF == 2 && jc + 1 < nch;
         const unsigned char *B = smem + (size_t)buf * CFG::BUF;
         const int L = (len - (int64_t)jc * C) < C ? (int)(len - (int64_t)jc * C) : C;
+        if (ahead) fetch(jc + 1, buf ^ 1, 0, NCP);
 
-        // state operand: k-step s covers channels 32 s + kperm(lg, e); it is the
-        // B operand of W S^T (columns v) and the A operand of S qg^T (rows v)
-        float sscale = 1.0f;
+        // operands are requested one 16-row tile ahead of the products using them
+        auto frag = [&](size_t off, int idx) { return F::load(B + off + ((size_t)idx * 64 + lane) * F::BYTES); };
+        FT fw[2][4], fq[2][4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) { fw[0][s] = frag(R::W_OFF, s); fq[0][s] = frag(R::QG_OFF, s); }
+        f32x4 ub[NB];
+        float us = 1.0f;
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) {
+            const unsigned char *ubp = B + CFG::UB_LDS +
+                                       ((size_t)(wave * NB + tb) * 64 + lane) * 4 * R::UB_ELT;
+            if constexpr (PRECISE) {
+                ub[tb] = *(const f32x4 *)ubp;
+            } else {
+                typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+                const half4 hv = *(const half4 *)ubp;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) ub[tb][i] = (float)hv[i];
+            }
+        }
+        if constexpr (!PRECISE) us = *(const float *)(B + R::UBS_OFF);
+
+        if (jc > 0) store_pending(o - o_chunk);
+
+        // rescale the state when S / sigma leaves [2^4, 2^14] or sigma < us
+        // (|Ub| / sigma <= 2^15 needs sigma >= us); both are powers of two
         if constexpr (!PRECISE) {
             float m = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(S[kb][i]));
-            sscale = pow2_scale_for(wave_max_nonneg(m), 14);
+            m = wave_max_nonneg(m);
+            float tgt = (m > 0.f) ? sigma * pow2_scale_for(m, 14) : (us > 0.f ? us : sigma);
+            if (tgt < us) tgt = us;
+            if (m > 16384.f || sigma < us || (m < 16.f && tgt < sigma)) {
+                const float r = sigma / tgt;
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) S[kb] *= r;
+                sigma = tgt;
+            }
         }
-        typename F::T bS[4];
+        // state operand: k-step s covers channels 32 s + kperm(lg, e); it is the
+        // B operand of W S^T (columns v) and the A operand of S qg^T (rows v)
+        FT bS[4];
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             float x[8] = {S[2 * s][0], S[2 * s][1], S[2 * s][2], S[2 * s][3],
                           S[2 * s + 1][0], S[2 * s + 1][1], S[2 * s + 1][2], S[2 * s + 1][3]};
-            bS[s] = F::make(x, inv_pow2(sscale));
+            bS[s] = F::make(x, 1.0f);
         }
 
-        // U = Ub - W S^T  (tile [t][v]: lane holds t = 16 tb + 4 lg + i, v = vrow)
-        // O^T = S qg^T    (tile [v][t]: lane holds v = 16 vb + 4 lg + i, t = 16 tb + lr)
+        // U / sigma = Ub / sigma + (-W) S^T / sigma  (tile [t][v]: t = 16 tb + 4 lg + i, v = vrow)
+        // O / sigma = S qg^T / sigma                 (tile [v][t]: v = 16 vb + 4 lg + i, t = 16 tb + lr)
+        const float ubf = us / sigma;
         f32x4 U[NB], O[NB];
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb) {
-            f32x4 aw = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+            if (tb + 1 < NB) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) {
+                    fw[(tb + 1) & 1][s] = frag(R::W_OFF, (tb + 1) * 4 + s);
+                    fq[(tb + 1) & 1][s] = frag(R::QG_OFF, (tb + 1) * 4 + s);
+                }
+            }
+            f32x4 aw = ub[tb] * ubf, aq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
-                const size_t fo = ((size_t)(tb * 4 + s) * 64 + lane) * F::BYTES;
-                aw = F::mma(F::load(B + R::W_OFF + fo), bS[s], aw);
-                aq = F::mma(bS[s], F::load(B + R::QG_OFF + fo), aq);
+                aw = F::mma(fw[tb & 1][s], bS[s], aw);
+                aq = F::mma(bS[s], fq[tb & 1][s], aq);
             }
-            const unsigned char *ubp = B + CFG::UB_LDS +
-                                       ((size_t)(wave * NB + tb) * 64 + lane) * 4 * R::UB_ELT;
-            f32x4 ub;
-            if constexpr (PRECISE) {
-                ub = *(const f32x4 *)ubp;
-            } else {
-                typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-                const half4 hv = *(const half4 *)ubp;
-                const float us = *(const float *)(B + R::UBS_OFF);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) ub[i] = (float)hv[i] * us;
-            }
-            U[tb] = ub - aw * sscale;
+            U[tb] = aw;
             O[tb] = aq;
         }
 
-        // U operand: k-step s over t covers rows 32 s + kperm(lg, e); it is the
-        // B operand of kg^T U (columns v) and the A operand of U^T M^T (rows v)
-        float uscale = 1.0f;
+        // operands of the second products: M, then kg^T two key blocks ahead
+        FT fm[NB][CS], fk[3][CS];
+        f32x4 gv[8];
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb)
+#pragma unroll
+            for (int s = 0; s < CS; ++s)
+                if (32 * s <= 16 * tb + 15)                // M is lower triangular
+                    fm[tb][s] = frag(R::M_OFF, tb * CS + s);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int s = 0; s < CS; ++s) fk[kb][s] = frag(R::KG_OFF, kb * CS + s);
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) gv[kb] = *(const f32x4 *)(B + R::GC_OFF + 4 * (16 * kb + 4 * lg));
+
+        // U / sigma must fit fp16: otherwise raise sigma (rare)
         if constexpr (!PRECISE) {
             float m = 0.f;
 #pragma unroll
             for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(U[tb][i]));
-            uscale = pow2_scale_for(wave_max_nonneg(m), 14);
+            m = wave_max_nonneg(m);
+            if (m > 32768.f) {
+                const float f = pow2_scale_for(m, 14), r = inv_pow2(f);
+#pragma unroll
+                for (int tb = 0; tb < NB; ++tb) { U[tb] *= r; O[tb] *= r; }
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb) S[kb] *= r;
+                sigma *= f;
+            }
         }
-        typename F::T bU[CS];
+        // U operand: k-step s over t covers rows 32 s + kperm(lg, e); it is the
+        // B operand of kg^T U (columns v) and the A operand of U^T M^T (rows v)
+        FT bU[CS];
 #pragma unroll
         for (int s = 0; s < CS; ++s) {
             float x[8];
@@ -835,51 +942,48 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
                 x[e] = (2 * s < NB) ? U[2 * s][e] : 0.f;
                 x[e + 4] = (2 * s + 1 < NB) ? U[2 * s + 1][e] : 0.f;
             }
-            bU[s] = F::make(x, inv_pow2(uscale));
+            bU[s] = F::make(x, 1.0f);
         }
 
-        // O^T += U^T M^T; the lane stores four consecutive channels of row t
+        // O^T += U^T M^T
 #pragma unroll
-        for (int tb = 0; tb < NB; ++tb) {
-            f32x4 am = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < CS; ++s) {
-                if (32 * s > 16 * tb + 15) continue;       // M is lower triangular
-                am = F::mma(bU[s], F::load(B + R::M_OFF + ((size_t)(tb * CS + s) * 64 + lane) * F::BYTES),
-                            am);
-            }
-            const f32x4 out = O[tb] * sscale + am * uscale;
-            if (16 * tb + lr < L) store4<Tout>(o + tb * o_tb, out);
-        }
-
-        // S^T <- diag(GamC) S^T + kg^T U
-        const float *gc = (const float *)(B + R::GC_OFF);
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
             for (int s = 0; s < CS; ++s)
-                acc = F::mma(F::load(B + R::KG_OFF + ((size_t)(kb * CS + s) * 64 + lane) * F::BYTES),
-                             bU[s], acc);
-            const f32x4 gv = *(const f32x4 *)(gc + 16 * kb + 4 * lg);
-            S[kb] = S[kb] * gv + acc * uscale;
+                if (32 * s <= 16 * tb + 15) O[tb] = F::mma(bU[s], fm[tb][s], O[tb]);
+
+        // S^T <- diag(GamC) S^T + kg^T U
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+            if (kb + 2 < 8) {
+#pragma unroll
+                for (int s = 0; s < CS; ++s) fk[(kb + 2) % 3][s] = frag(R::KG_OFF, (kb + 2) * CS + s);
+            }
+            f32x4 acc = S[kb] * gv[kb];
+#pragma unroll
+            for (int s = 0; s < CS; ++s) acc = F::mma(fk[kb % 3][s], bU[s], acc);
+            S[kb] = acc;
         }
 
-        o += (size_t)C * H * kHeadDim;
+#pragma unroll
+        for (int tb = 0; tb < NB; ++tb) pend[tb] = O[tb] * sigma;
+        Lp = L;
+        o += o_chunk;
         if (jc + 1 < nch) {
             if (CFG::NBUF == 1) {
                 lds_barrier();            // everyone is done with the single buffer
-                fetch(jc + 1, 0);
+                fetch(jc + 1, 0, 0, NCP);
             }
             wait_vmem();                  // this wave's copies have landed ...
             lds_barrier();                // ... and everyone else's
         }
     }
+    if (nch > 0) store_pending(o - o_chunk);
 
     if (p.ht) {
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb)
-            *(f32x4 *)(p.ht + sbase + 16 * kb + 4 * lg) = S[kb];
+            *(f32x4 *)(p.ht + sbase + 16 * kb + 4 * lg) = S[kb] * sigma;
     }
 }
 

@@ -231,7 +231,7 @@ def unpack_record(raw: np.ndarray, C: int, precise: bool):
             kk = _kperm(g, e)
             for tb in range(NB):
                 for s in range(4):
-                    W[16 * tb + r, 32 * s + kk] = Wf[tb * 4 + s, lane, e]
+                    W[16 * tb + r, 32 * s + kk] = -Wf[tb * 4 + s, lane, e]   # stored negated
                     QG[16 * tb + r, 32 * s + kk] = Qf[tb * 4 + s, lane, e]
                 for s in range(CS):
                     M[16 * tb + r, 32 * s + kk] = Mf[tb * CS + s, lane, e]
