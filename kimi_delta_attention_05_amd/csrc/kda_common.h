@@ -65,27 +65,43 @@ typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 // Asynchronous copies from global memory straight into LDS (global->LDS DMA,
 // no registers); completion is tracked by vmcnt like any vector load.
-// Buffer resource for the byte range [base, base + bytes), gfx9 word-3 format
-// bits; a read outside the range returns zeros instead of faulting.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             0x00020000);
+//
+// A buffer resource for the byte range [base, base + bytes) (gfx9 word-3 format
+// bits); a read outside the range returns zeros instead of faulting.
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ i32x4 make_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t a = (uint64_t)(uintptr_t)base;
+    return i32x4{(int)(uint32_t)a, (int)((a >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
 }
 
-// 16 bytes per lane through a buffer resource (buffer_load_dwordx4 ... lds):
-// lane i reads rsrc + voffset_i + soffset and writes lds_wave_base + 16 i, so a
-// wave fills one contiguous 1 KiB block; lds_wave_base must be wave-uniform.
-// The buffer (MUBUF) form is used rather than the global one because the
-// compiler treats a FLAT-encoded copy as a possible out-of-order LDS access
-// and then drops every later LDS wait to a count of zero.
-__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
-                                              uint32_t soffset, void *lds_wave_base) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave_base, 16, voffset, soffset, 0, 0);
+// buffer_load_dword{,x4} ... lds: lane i reads rsrc + voffset_i + soffset and
+// writes lds_wave_base + SIZE * i, so a wave fills one contiguous block;
+// lds_wave_base, rsrc and soffset must be wave-uniform. Issued as inline asm
+// (M0, which addresses the LDS side, is saved and restored around it): the
+// compiler then does not see an LDS write in flight and adds no vmcnt waits of
+// its own before later LDS accesses. Every reader of the copied bytes waits
+// explicitly (wait_vmem, then a barrier).
+template <int SIZE>
+__device__ __forceinline__ void buffer_copy_to_lds(const i32x4 &r, uint32_t voffset, uint32_t soffset,
+                                                   const void *lds_wave_base) {
+    const uint32_t la = (uint32_t)(uintptr_t)(lds_ptr_t)lds_wave_base;
+    uint32_t saved;
+    if constexpr (SIZE == 16)
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\ts_nop 0\n\t"
+                     "buffer_load_dwordx4 %1, %2, %3 offen lds\n\ts_mov_b32 m0, %0"
+                     : "=&s"(saved) : "v"(voffset), "s"(r), "s"(soffset), "s"(la) : "memory");
+    else
+        asm volatile("s_mov_b32 %0, m0\n\ts_mov_b32 m0, %4\n\ts_nop 0\n\t"
+                     "buffer_load_dword %1, %2, %3 offen lds\n\ts_mov_b32 m0, %0"
+                     : "=&s"(saved) : "v"(voffset), "s"(r), "s"(soffset), "s"(la) : "memory");
 }
-
-__device__ __forceinline__ void copy4_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voffset,
-                                             uint32_t soffset, void *lds_wave_base) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds_wave_base, 4, voffset, soffset, 0, 0);
+__device__ __forceinline__ void copy16_to_lds(const i32x4 &r, uint32_t voffset, uint32_t soffset,
+                                              void *lds_wave_base) {
+    buffer_copy_to_lds<16>(r, voffset, soffset, lds_wave_base);
+}
+__device__ __forceinline__ void copy4_to_lds(const i32x4 &r, uint32_t voffset, uint32_t soffset,
+                                             void *lds_wave_base) {
+    buffer_copy_to_lds<4>(r, voffset, soffset, lds_wave_base);
 }
 
 // 8 consecutive input elements kept in their storage format (prefetch buffers).

@@ -51,7 +51,9 @@ struct ChunkGeom {
 //                                   so that U = Ub + (-W) S^T is one accumulation
 //   qg   [NB tb][4 s][64 lane][8]   rows t, k over key channels   (Tst)
 //   kgT  [8 kb][CS s][64 lane][8]   rows key channel, k over t    (Tst)
-//   M    [NB tb][CS s][64 lane][8]  rows t, k over t'             (Tst)
+//   M    [NB tb][CS s][64 lane][8]  rows t, k over t'             (Tst); fragments
+//                                   with 2 s > tb lie above the diagonal, are
+//                                   never read and are left unwritten
 //   GamC [128]                      fp32 total decay of the chunk
 //   UbSc [4]                        fp32; [0] = power-of-two scale of Ub, 0 if
 //                                   every v of the chunk is zero

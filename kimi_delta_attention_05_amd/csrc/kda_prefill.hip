@@ -65,6 +65,10 @@ template <> struct Frag<false> {
     static __device__ __forceinline__ void store(void *p, const float (&x)[8]) {
         *(T *)p = make(x, 1.0f);
     }
+    static __device__ __forceinline__ void store_half(void *p, const float (&x)[8]) {   // x[0..3]
+        typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+        *(half4 *)p = half4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
+    }
     static __device__ __forceinline__ f32x4 mma(const T &a, const T &b, f32x4 c) {
         return mfma_h(a, b, c);
     }
@@ -90,6 +94,9 @@ template <> struct Frag<true> {
         ((f32x4 *)p)[0] = f32x4{x[0], x[1], x[2], x[3]};
         ((f32x4 *)p)[1] = f32x4{x[4], x[5], x[6], x[7]};
     }
+    static __device__ __forceinline__ void store_half(void *p, const float (&x)[8]) {   // x[0..3]
+        *(f32x4 *)p = f32x4{x[0], x[1], x[2], x[3]};
+    }
     static __device__ __forceinline__ f32x4 mma(const T &a, const T &b, f32x4 c) {
         return mfma_f32x8(a.v, b.v, c);
     }
@@ -98,6 +105,30 @@ template <> struct Frag<true> {
 
 __device__ __forceinline__ float inv_pow2(float s) {   // exact 1/s for s = 2^e
     return __uint_as_float((uint32_t)(254 - (int)((__float_as_uint(s) >> 23) & 0xFF)) << 23);
+}
+
+// 16x16x16 fp32 product on the fp32 MFMA (four 16x16x4 steps). `a` holds row
+// lr of the left factor at columns 4 lg .. 4 lg + 3, `b` holds rows
+// 4 lg .. 4 lg + 3 of the right factor at column lr: exactly what an
+// accumulator tile holds, so a product can feed the next one as its right
+// factor without leaving registers (lr = lane % 16, lg = lane / 16).
+__device__ __forceinline__ f32x4 mm16(const f32x4 &a, const f32x4 &b, f32x4 acc) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk], b[kk], acc, 0, 0, 0);
+    return acc;
+}
+// Left-factor operand of a 16x16 LDS block (row stride ld floats, 16-byte aligned rows).
+__device__ __forceinline__ f32x4 lds_left16(const float *blk, int ld, int lr, int lg) {
+    return *(const f32x4 *)(blk + lr * ld + 4 * lg);
+}
+// Right-factor operand (accumulator layout) of a 16x16 LDS block.
+__device__ __forceinline__ f32x4 lds_right16(const float *blk, int ld, int lr, int lg) {
+    return f32x4{blk[(4 * lg) * ld + lr], blk[(4 * lg + 1) * ld + lr], blk[(4 * lg + 2) * ld + lr],
+                 blk[(4 * lg + 3) * ld + lr]};
+}
+__device__ __forceinline__ void lds_store16(float *blk, int ld, const f32x4 &d, int lr, int lg) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) blk[(4 * lg + i) * ld + lr] = d[i];
 }
 
 // Locate chunk `slot` of the packed batch: returns false for an unused slot.
@@ -160,7 +191,7 @@ struct RawLayout {                    // raw inputs of one tile inside the three
 // wave fills contiguous 1 KiB blocks. Rows past the chunk end copy the chunk's
 // last row (in bounds for a valid tile) and are masked where used. The caller
 // waits (wait_vmem + lds_barrier) before reading.
-template <int C, typename Tin>
+template <int C, typename Tin, int PART = 2>
 __device__ __forceinline__ void stage_raw(const PrefillArgs &p, int h, int64_t t0, int L, int tid,
                                           unsigned char *lds) {
     using RL = RawLayout<C, Tin>;
@@ -168,19 +199,22 @@ __device__ __forceinline__ void stage_raw(const PrefillArgs &p, int h, int64_t t
     constexpr uint32_t RB = kHeadDim * (uint32_t)sizeof(Tin);   // bytes per q/k/v row
     constexpr int PPR = (int)RB / 16;                            // pieces per q/k/v row
     static_assert(RL::NQ16 % 64 == 0 && RL::NG16 % 64 == 0, "a wave's pieces stay in one array");
+    // PART 0: q and k; PART 1: v, g, beta and dt_bias; PART 2: everything
+    constexpr int P0 = PART == 1 ? 2 * RL::NQ16 : 0;
+    constexpr int P1 = PART == 0 ? 2 * RL::NQ16 : 3 * RL::NQ16 + RL::NG16;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     // resources over rows t0 .. t0 + L - 1 of head h (token stride H rows)
     const size_t row0 = (size_t)t0 * p.H + h;
     const uint32_t hq = (uint32_t)p.H * RB, hg = (uint32_t)p.H * 512u;
     const uint32_t span = (uint32_t)(L - 1);
-    const __amdgpu_buffer_rsrc_t rq = make_rsrc((const unsigned char *)p.q + row0 * RB, span * hq + RB);
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc((const unsigned char *)p.k + row0 * RB, span * hq + RB);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc((const unsigned char *)p.v + row0 * RB, span * hq + RB);
-    const __amdgpu_buffer_rsrc_t rg = make_rsrc(p.g + row0 * kHeadDim, span * hg + 512u);
+    const i32x4 rq = make_rsrc((const unsigned char *)p.q + row0 * RB, span * hq + RB);
+    const i32x4 rk = make_rsrc((const unsigned char *)p.k + row0 * RB, span * hq + RB);
+    const i32x4 rv = make_rsrc((const unsigned char *)p.v + row0 * RB, span * hq + RB);
+    const i32x4 rg = make_rsrc(p.g + row0 * kHeadDim, span * hg + 512u);
 #pragma unroll
-    for (int i = 0; i < RL::PER; ++i) {
-        const int wbase = 64 * wave + NT * i;                   // first piece of this wave
-        if (wbase >= 3 * RL::NQ16 + RL::NG16) break;            // whole wave past the end
+    for (int i = 0; i < (P1 - P0 + NT - 1) / NT; ++i) {
+        const int wbase = P0 + 64 * wave + NT * i;              // first piece of this wave
+        if (wbase >= P1) break;                                 // whole wave past the end
         const uint32_t idx = (uint32_t)(wbase + lane);
         if (wbase < 3 * RL::NQ16) {
             const int arr = wbase / RL::NQ16;
@@ -194,14 +228,15 @@ __device__ __forceinline__ void stage_raw(const PrefillArgs &p, int h, int64_t t
             copy16_to_lds(rg, t * hg + (w % 32u) * 16u, 0, lds + (size_t)wbase * 16);
         }
     }
-    if (wave == 0) {                                             // beta, one float per row
-        const __amdgpu_buffer_rsrc_t rb =
-            make_rsrc(p.beta_raw + row0, span * (uint32_t)p.H * 4u + 4u);
-        const uint32_t t = min((uint32_t)tid, span);
-        if (tid < C) copy4_to_lds(rb, t * (uint32_t)p.H * 4u, 0, lds + RL::B);
-    } else if (wave == 1) {                                      // dt_bias[h], 512 bytes
-        const __amdgpu_buffer_rsrc_t rd = make_rsrc(p.dt_bias + (size_t)h * kHeadDim, 512u);
-        if (lane < 32) copy16_to_lds(rd, 16u * (uint32_t)lane, 0, lds + RL::DT);
+    if constexpr (PART != 0) {
+        if (wave == 0) {                                         // beta, one float per row
+            const i32x4 rb = make_rsrc(p.beta_raw + row0, span * (uint32_t)p.H * 4u + 4u);
+            const uint32_t t = min((uint32_t)tid, span);
+            if (tid < C) copy4_to_lds(rb, t * (uint32_t)p.H * 4u, 0, lds + RL::B);
+        } else if (wave == 1) {                                  // dt_bias[h], 512 bytes
+            const i32x4 rd = make_rsrc(p.dt_bias + (size_t)h * kHeadDim, 512u);
+            if (lane < 32) copy16_to_lds(rd, 16u * (uint32_t)lane, 0, lds + RL::DT);
+        }
     }
 }
 
@@ -212,22 +247,6 @@ __device__ __forceinline__ void load_T_row(const float *x, const float *beta, fl
     load8(beta, b);
 #pragma unroll
     for (int e = 0; e < 8; ++e) t[e] *= b[e];
-}
-
-// Phase-2 work order. Jobs 0 .. NB*CS-1 are the M fragments (a, s); the rest
-// write qg and kg^T fragments. Slot k goes to wave k % 8 and waves w, w + 4
-// share a SIMD, so for C = 64 the four jobs with a diagonal (fp32 MFMA) block
-// land on four different SIMDs and the two lightest M jobs on the busiest ones.
-template <int C>
-__device__ __forceinline__ int intra_job_order(int slot) {
-    if constexpr (C == 64) {
-        // M job a*2+s: 0 = D, 1 = zero, 2 = O+D, 3 = zero, 4 = O+O, 5 = D, 6 = O+O, 7 = O+D
-        // (D: a diagonal block on the fp32 MFMA, O: an off-diagonal fp16 block)
-        // first[8] = {2, 7, 0, 5, 1, 3, 4, 6}, one nibble per slot
-        return slot < 8 ? (int)((0x64315072u >> (4 * slot)) & 15u) : slot;
-    } else {
-        return slot;
-    }
 }
 
 template <int C, typename Tin, bool PRECISE>
@@ -256,7 +275,7 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
     __shared__ __align__(16) float sKF[NB][kHeadDim];  // prod alpha over rows 16b+1 .. C-1
     __shared__ __align__(16) float sEF[NPO][kHeadDim]; // prod alpha over rows 16b+1 .. 16a
     __shared__ __align__(16) float sBeta[C];
-    __shared__ float sInv[3][16][17];
+    __shared__ __align__(16) float sX[NB][16][20];   // per diagonal block: inverse scratch
     __shared__ float sVmax[NW];
 
     const int H = p.H;
@@ -428,104 +447,155 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
         }
         lds_barrier();
 
-        // ---- phase 2: A^T and M^T blocks (MFMA); M, qg and kgT fragments ----------
-        // M fragment (a, s) holds rows 16a..16a+15 and columns 32s .. 32s+31, i.e. the
-        // transposed blocks (2s, a) and (2s+1, a): computing M^T makes the accumulator
-        // layout the fragment layout.
+        // ---- phase 2: A and M blocks (MFMA); M, qg and kgT fragments -------------
+        // Block (a, b), b <= a, of A = beta_i kh_i . kh_j e^{G_i - G_j} and of
+        // M = qh_i . kh_j e^{G_i - G_j} is a K = 128 contraction of the rows of
+        // qh*P / kh*P (block a) with kh/P (block b) scaled by the block factor EF
+        // (a != b), computed transposed (M^T, A^T) so that the accumulator tile is
+        // one half of M fragment (a, b / 2): block b fills positions 4 (b & 1) .. + 3
+        // of each lane's 8 entries. Waves 0 .. NB-1 take the diagonal blocks (fp32
+        // MFMA: right factors reach e^75) and invert I + A_aa; the other waves take
+        // the off-diagonal blocks (fp16 MFMA: every factor is at most 1) and the qg
+        // and kgT fragments.
         {
-            constexpr int NMJ = NB * CS;
-            constexpr int NQ = NB * 4, NKG = 8 * CS;
-            for (int slot = wave; slot < NMJ + NQ + NKG; slot += NW) {
-                const int job = intra_job_order<C>(slot);
-                if (job < NMJ) {
-                    const int a = job / CS, s = job % CS;
-                    const int il = 16 * a + lr;          // B operand row (left factor side)
-                    float xm[8];
+            auto block = [&](int a, int b) {
+                const int il = 16 * a + lr, jr = 16 * b + lr;
+                const float *ef = sEF[a > b ? a * (a - 1) / 2 + b : 0];
+                f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aM = {0.f, 0.f, 0.f, 0.f};
+                if (PRECISE || a == b) {
+                    float bK[4][8], bQ[4][8], aR[4][8];
 #pragma unroll
-                    for (int half = 0; half < 2; ++half) {
-                        const int b = 2 * s + half;
-                        float accM[4] = {0.f, 0.f, 0.f, 0.f};
-                        if (b <= a && b < NB) {
-                            const int jr = 16 * b + lr;  // A operand row (right factor side)
-                            const float *ef = sEF[a * (a - 1) / 2 + b];
-                            f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aM = {0.f, 0.f, 0.f, 0.f};
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const int c = 32 * ks + 8 * lg;
+                        load8(&sK[il][c], bK[ks]);       // kh e^{G_i - G_16a}
+                        load8(&sQ[il][c], bQ[ks]);       // qh e^{G_i - G_16a}
+                        load8(&sP[jr][c], aR[ks]);       // kh / P_j
+                        if (a != b) {                    // e^{G_16a - G_j} = EF / P_j
+                            float f[8];
+                            load8(ef + c, f);
 #pragma unroll
-                            for (int ks = 0; ks < 4; ++ks) {
-                                const int c = 32 * ks + 8 * lg;
-                                float bK[8], bQ[8], aR[8];
-                                load8(&sK[il][c], bK);   // kh e^{G_i - G_16a}
-                                load8(&sQ[il][c], bQ);   // qh e^{G_i - G_16a}
-                                load8(&sP[jr][c], aR);   // kh / P_j
-                                if (a != b) {            // e^{G_16a - G_j} = EF / P_j
-                                    float f[8];
-                                    load8(ef + c, f);
-#pragma unroll
-                                    for (int e = 0; e < 8; ++e) aR[e] *= f[e];
-                                }
-                                if (PRECISE || a == b) { // diagonal: right factors up to e^75
-                                    aA = mfma_f32x8(aR, bK, aA);
-                                    aM = mfma_f32x8(aR, bQ, aM);
-                                } else {                 // all factors <= 1
-                                    aA = mfma_f16(aR, bK, aA);
-                                    aM = mfma_f16(aR, bQ, aM);
-                                }
-                            }
-                            // lane holds A[i][j] / M[i][j] for i = 16a + lr, j = 16b + 4lg + ii
-#pragma unroll
-                            for (int ii = 0; ii < 4; ++ii) {
-                                const int j = 16 * b + 4 * lg + ii;
-                                sA[il][j] = (il > j) ? sBeta[il] * aA[ii] : 0.f;
-                                accM[ii] = (j <= il) ? aM[ii] : 0.f;
-                            }
-                        }
-#pragma unroll
-                        for (int ii = 0; ii < 4; ++ii) xm[4 * half + ii] = accM[ii];
-                    }
-                    F::store(rec + R::M_OFF + ((size_t)(a * CS + s) * 64 + lane) * F::BYTES, xm);
-                    if (a >> 1 == s) {
-                        // This wave wrote the diagonal block A_aa: invert I + A_aa by
-                        // forward substitution, one column per lane (LDS accesses of a
-                        // wave complete in order, so its own writes are visible).
-                        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-                        if (lg == 0) {
-                            const int o = 16 * a, c = lr;
-                            float x[16];
-#pragma unroll
-                            for (int i = 0; i < 16; ++i) {
-                                float acc0 = (i == c) ? 1.0f : 0.0f, acc1 = 0.f;
-#pragma unroll
-                                for (int jj = 0; jj < i; jj += 2) {
-                                    acc0 -= sA[o + i][o + jj] * x[jj];
-                                    if (jj + 1 < i) acc1 -= sA[o + i][o + jj + 1] * x[jj + 1];
-                                }
-                                x[i] = (i < c) ? 0.0f : acc0 + acc1;
-                            }
-#pragma unroll
-                            for (int i = 0; i < 16; ++i) sT[o + i][o + c] = x[i];
+                            for (int e = 0; e < 8; ++e) aR[ks][e] *= f[e];
                         }
                     }
-                } else if (job < NMJ + NQ) {         // qg = qh e^{G_t} = (qh P_t) QF
-                    const int f = job - NMJ;
-                    const int tb = f >> 2, s = f & 3;
-                    const int t = 16 * tb + lr;
-                    const int c0 = 32 * s + 4 * lg;
-                    const f32x4 q0 = *(const f32x4 *)&sQ[t][c0], q1 = *(const f32x4 *)&sQ[t][c0 + 16];
-                    const f32x4 f0 = *(const f32x4 *)&sQF[tb][c0], f1 = *(const f32x4 *)&sQF[tb][c0 + 16];
-                    float x[8];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) { x[e] = q0[e] * f0[e]; x[e + 4] = q1[e] * f1[e]; }
-                    F::store(rec + R::QG_OFF + ((size_t)(tb * 4 + s) * 64 + lane) * F::BYTES, x);
-                } else {                             // kg = kh e^{G_C - G_t} = (kh / P_t) KF
-                    const int f = job - NMJ - NQ;
-                    const int kb = f / CS, s = f % CS;
-                    const int c = 16 * kb + lr;
-                    float x[8];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int t = 32 * s + kperm(lg, e);
-                        x[e] = (t < C) ? sP[t][c] * sKF[t >> 4][c] : 0.f;
+                    for (int ks = 0; ks < 4; ++ks) {
+                        aA = mfma_f32x8(aR[ks], bK[ks], aA);
+                        aM = mfma_f32x8(aR[ks], bQ[ks], aM);
                     }
-                    F::store(rec + R::KG_OFF + ((size_t)(kb * CS + s) * 64 + lane) * F::BYTES, x);
+                } else {
+                    half8 hK[4], hQ[4], hR[4];
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        const int c = 32 * ks + 8 * lg;
+                        float bK[8], bQ[8], aR[8], f[8];
+                        load8(&sK[il][c], bK);
+                        load8(&sQ[il][c], bQ);
+                        load8(&sP[jr][c], aR);
+                        load8(ef + c, f);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            hK[ks][e] = (_Float16)bK[e];
+                            hQ[ks][e] = (_Float16)bQ[e];
+                            hR[ks][e] = (_Float16)(aR[e] * f[e]);
+                        }
+                    }
+#pragma unroll
+                    for (int ks = 0; ks < 4; ++ks) {
+                        aA = mfma_h(hR[ks], hK[ks], aA);
+                        aM = mfma_h(hR[ks], hQ[ks], aM);
+                    }
+                }
+                // lane holds A[i][j] / M[i][j] for i = 16a + lr, j = 16b + 4lg + ii
+                float xm[8];
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const int j = 16 * b + 4 * lg + ii;
+                    sA[il][j] = (il > j) ? sBeta[il] * aA[ii] : 0.f;
+                    xm[ii] = (j <= il) ? aM[ii] : 0.f;
+                    xm[ii + 4] = 0.f;
+                }
+                unsigned char *mf = rec + R::M_OFF + ((size_t)(a * CS + (b >> 1)) * 64 + lane) * F::BYTES;
+                if ((b & 1) == 0 && a == b) F::store(mf, xm);      // with the zero block b + 1
+                else F::store_half(mf + (b & 1) * (F::BYTES / 2), xm);
+            };
+
+            if (wave < NB) {
+                const int a = wave;
+                block(a, a);
+                // invert I + A_aa (strictly lower, written above by this wave; a
+                // wave's LDS accesses complete in order, so the other lanes' entries
+                // are visible to its later reads)
+                const float *Ab = &sA[16 * a][16 * a];
+                float *Xb = &sT[16 * a][16 * a];
+                if constexpr (!PRECISE) {
+                    // (I + A)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8) since A^16 = 0
+                    float *Sx = &sX[a][0][0];
+                    const f32x4 p1 = lds_right16(Ab, AP, lr, lg);
+                    f32x4 z;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) z[i] = ((4 * lg + i == lr) ? 1.0f : 0.0f) - p1[i];
+                    f32x4 pw = mm16(lds_left16(Ab, AP, lr, lg), p1, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+                    for (int m = 0; m < 3; ++m) {
+                        lds_store16(Sx, 20, pw, lr, lg);
+                        const f32x4 lp = lds_left16(Sx, 20, lr, lg);
+                        z = mm16(lp, z, z);                          // z += A^(2^(m+1)) z
+                        if (m < 2) pw = mm16(lp, pw, f32x4{0.f, 0.f, 0.f, 0.f});
+                    }
+                    lds_store16(Xb, AP, z, lr, lg);
+                } else if (lg == 0) {
+                    // forward substitution, one column per lane (backward stable)
+                    const int c = lr;
+                    float x[16];
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        float acc0 = (i == c) ? 1.0f : 0.0f, acc1 = 0.f;
+#pragma unroll
+                        for (int jj = 0; jj < i; jj += 2) {
+                            acc0 -= Ab[i * AP + jj] * x[jj];
+                            if (jj + 1 < i) acc1 -= Ab[i * AP + jj + 1] * x[jj + 1];
+                        }
+                        x[i] = (i < c) ? 0.0f : acc0 + acc1;
+                    }
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) Xb[i * AP + c] = x[i];
+                }
+            }
+            {
+                // light jobs: the first NJ - 2 NB over the other waves, the last
+                // 2 NB (fragment jobs) to the diagonal waves once they are done
+                constexpr int NOFF = NB * (NB - 1) / 2, NQ = NB * 4, NKG = 8 * CS;
+                constexpr int NJ = NOFF + NQ + NKG, NJL = NJ - 2 * NB;
+                const int j0 = wave < NB ? NJL + wave : wave - NB;
+                const int js = wave < NB ? NB : NW - NB;
+                const int j1 = wave < NB ? NJ : NJL;
+                for (int j = j0; j < j1; j += js) {
+                    if (j < NOFF) {                      // off-diagonal block (a, b), a > b
+                        const int a = j < 1 ? 1 : (j < 3 ? 2 : 3);
+                        block(a, j - a * (a - 1) / 2);
+                    } else if (j < NOFF + NQ) {          // qg = qh e^{G_t} = (qh P_t) QF
+                        const int f = j - NOFF;
+                        const int tb = f >> 2, s = f & 3;
+                        const int t = 16 * tb + lr;
+                        const int c0 = 32 * s + 4 * lg;
+                        const f32x4 q0 = *(const f32x4 *)&sQ[t][c0], q1 = *(const f32x4 *)&sQ[t][c0 + 16];
+                        const f32x4 f0 = *(const f32x4 *)&sQF[tb][c0], f1 = *(const f32x4 *)&sQF[tb][c0 + 16];
+                        float x[8];
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) { x[e] = q0[e] * f0[e]; x[e + 4] = q1[e] * f1[e]; }
+                        F::store(rec + R::QG_OFF + ((size_t)(tb * 4 + s) * 64 + lane) * F::BYTES, x);
+                    } else {                             // kg = kh e^{G_C - G_t} = (kh / P_t) KF
+                        const int f = j - NOFF - NQ;
+                        const int kb = f / CS, s = f % CS;
+                        const int c = 16 * kb + lr;
+                        float x[8];
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            const int t = 32 * s + kperm(lg, e);
+                            x[e] = (t < C) ? sP[t][c] * sKF[t >> 4][c] : 0.f;
+                        }
+                        F::store(rec + R::KG_OFF + ((size_t)(kb * CS + s) * 64 + lane) * F::BYTES, x);
+                    }
                 }
             }
         }
@@ -541,6 +611,11 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
         }
         const float vinv = inv_pow2(vscale);
         lds_barrier();
+        // the qh*P tile is free from here on: the next tile's q and k go there
+        if constexpr (PF) {
+            static_assert(RawLayout<C, Tin>::V <= sizeof(float) * C * KP, "q, k fit the qh*P tile");
+            if (valid_nx) stage_raw<C, Tin, 0>(p, (int)(next % H), t0_nx, L_nx, tid, sRaw);
+        }
 
         // ---- phase 3: v (scaled) into sP ----------------------------------------
 #pragma unroll
@@ -584,39 +659,44 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
         L = L_nx;
         if constexpr (PF) {
             lds_barrier();                      // the three tiles are free from here on
-            if (valid) stage_raw<C, Tin>(p, (int)(ti % H), t0, L, tid, sRaw);
+            if (valid) stage_raw<C, Tin, 1>(p, (int)(ti % H), t0, L, tid, sRaw);
         }
 
         // ---- phase 4: off-diagonal blocks X_ab = -X_aa sum_{c=b}^{a-1} A_ac X_cb ----
-        // One wave per block pair of a diagonal d = a - b, as 16x16x16 fp32 MFMA
-        // products (four 16x16x4 steps: lane l supplies row/column l % 16 and
-        // k = 4 kk + l / 16).
-#pragma unroll
-        for (int d = 1; d < NB; ++d) {
-            const int a = d + wave, b = wave;
-            if (a < NB) {                          // P = sum_c A_ac X_cb  -> sInv[wave]
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int c = 0; c < NB; ++c) {
-                    if (c < b || c >= a) continue;
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                            sA[16 * a + lr][16 * c + 4 * kk + lg], sT[16 * c + 4 * kk + lg][16 * b + lr],
-                            acc, 0, 0, 0);
-                }
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sInv[wave][4 * lg + i][lr] = acc[i];
+        // in two levels of independent 16x16 fp32 MFMA chains (products feed the
+        // next one from registers): first X_10 and X_32, then, with
+        // Y_rc = A_r0 X_0c + A_r1 X_1c (X_01 = 0), X_2c = -X_22 Y_2c and
+        // X_3c = -(X_32 Y_2c + X_33 Y_3c), which is the substitution above with
+        // X_32 = -X_33 A_32 X_22 folded in.
+        if constexpr (NB >= 2) {
+            if (wave < NB / 2) {
+                const int a = 2 * wave + 1, b = 2 * wave;
+                const f32x4 y = mm16(lds_left16(&sA[16 * a][16 * b], AP, lr, lg),
+                                     lds_right16(&sT[16 * b][16 * b], AP, lr, lg), f32x4{0.f, 0.f, 0.f, 0.f});
+                const f32x4 x = mm16(lds_left16(&sT[16 * a][16 * a], AP, lr, lg), y, f32x4{0.f, 0.f, 0.f, 0.f});
+                lds_store16(&sT[16 * a][16 * b], AP, -x, lr, lg);
             }
             lds_barrier();
-            if (a < NB) {                          // X_ab = -X_aa P
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk)
-                    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                        sT[16 * a + lr][16 * a + 4 * kk + lg], sInv[wave][4 * kk + lg][lr], acc, 0, 0, 0);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) sT[16 * a + 4 * lg + i][16 * b + lr] = -acc[i];
+        }
+        if constexpr (NB == 4) {
+            if (wave < 4) {
+                const int r = 2 + (wave >> 1), c = wave & 1;
+                const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+                const f32x4 x1c = lds_right16(&sT[16][16 * c], AP, lr, lg);    // X_1c
+                f32x4 x00 = zero;
+                if (c == 0) x00 = lds_right16(&sT[0][0], AP, lr, lg);
+                f32x4 y2 = mm16(lds_left16(&sA[32][16], AP, lr, lg), x1c, zero);            // A_21 X_1c
+                if (c == 0) y2 = mm16(lds_left16(&sA[32][0], AP, lr, lg), x00, y2);         // + A_20 X_00
+                f32x4 x;
+                if (r == 2) {
+                    x = mm16(lds_left16(&sT[32][32], AP, lr, lg), y2, zero);                // X_22 Y_2c
+                } else {
+                    f32x4 y3 = mm16(lds_left16(&sA[48][16], AP, lr, lg), x1c, zero);        // A_31 X_1c
+                    if (c == 0) y3 = mm16(lds_left16(&sA[48][0], AP, lr, lg), x00, y3);     // + A_30 X_00
+                    x = mm16(lds_left16(&sT[48][32], AP, lr, lg), y2, zero);                // X_32 Y_2c
+                    x = mm16(lds_left16(&sT[48][48], AP, lr, lg), y3, x);                   // + X_33 Y_3c
+                }
+                lds_store16(&sT[16 * r][16 * c], AP, -x, lr, lg);
             }
             lds_barrier();
         }
@@ -782,7 +862,7 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
     const uint32_t lane16 = 16u * (uint32_t)lane;
     const uint32_t ub_off = (uint32_t)(R::UB_OFF + (size_t)4 * vg * R::UB_VB_BYTES);
     auto fetch = [&](int jc, int buf, int k0, int k1) {
-        const __amdgpu_buffer_rsrc_t r = make_rsrc(rec0 + (size_t)jc * rec_step, (uint32_t)R::BYTES);
+        const i32x4 r = make_rsrc(rec0 + (size_t)jc * rec_step, (uint32_t)R::BYTES);
         unsigned char *dst = smem + (size_t)buf * CFG::BUF + 1024 * wave;
 #pragma unroll
         for (int k = 0; k < NCP; ++k) {
@@ -799,6 +879,30 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
         }
     };
 
+    // L2 prefetch two chunks ahead: one 4-byte load per 128-byte line of this
+    // workgroup's share of a record (the two halves of a chain split the shared
+    // operands). The values are never used; they stay in registers until the
+    // end-of-chunk wait so that no earlier wait is placed on them.
+    constexpr int SHL = (int)((R::SHARED_BYTES + 127) / 128), SHL2 = (SHL + 1) / 2;
+    constexpr int UBL = (int)(4 * R::UB_VB_BYTES / 128);
+    constexpr int NTOUCH = (SHL2 + UBL + 255) / 256;
+    const unsigned char *touch_base[NTOUCH];
+#pragma unroll
+    for (int i = 0; i < NTOUCH; ++i) {
+        const int li = tid + 256 * i;
+        const int sh = vg * SHL2 + li;
+        touch_base[i] = (li < SHL2) ? ((sh < SHL) ? rec0 + 128 * sh : nullptr)
+                      : (li < SHL2 + UBL ? rec0 + ub_off + 128 * (li - SHL2) : nullptr);
+    }
+    uint32_t touched[NTOUCH];
+#pragma unroll
+    for (int i = 0; i < NTOUCH; ++i) touched[i] = 0;
+    auto touch = [&](int jc) {
+#pragma unroll
+        for (int i = 0; i < NTOUCH; ++i)
+            if (touch_base[i]) touched[i] = *(const uint32_t *)(touch_base[i] + (size_t)jc * rec_step);
+    };
+
     // this lane writes o[t][h][16 vb + 4 lg .. + 3] for t = chunk start + 16 tb + lr;
     // a chunk's outputs are stored while the next chunk computes
     Tout *__restrict__ o = (Tout *)p.o + ((size_t)(s0 + lr) * H + h) * kHeadDim + 16 * vb + 4 * lg;
@@ -813,6 +917,7 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
 
     if (nch > 0) {
         fetch(0, 0, 0, NCP);
+        if (nch > 1) touch(1);
         wait_vmem();
         lds_barrier();
     }
@@ -822,6 +927,7 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
         const unsigned char *B = smem + (size_t)buf * CFG::BUF;
         const int L = (len - (int64_t)jc * C) < C ? (int)(len - (int64_t)jc * C) : C;
         if (ahead) fetch(jc + 1, buf ^ 1, 0, NCP);
+        if (jc + 2 < nch) touch(jc + 2);
 
         // operands are requested one 16-row tile ahead of the products using them
         auto frag = [&](size_t off, int idx) { return F::load(B + off + ((size_t)idx * 64 + lane) * F::BYTES); };
@@ -977,6 +1083,8 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
             wait_vmem();                  // this wave's copies have landed ...
             lds_barrier();                // ... and everyone else's
         }
+#pragma unroll
+        for (int i = 0; i < NTOUCH; ++i) asm volatile("" ::"v"(touched[i]));
     }
     if (nch > 0) store_pending(o - o_chunk);
 

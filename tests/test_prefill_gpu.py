@@ -234,7 +234,8 @@ def unpack_record(raw: np.ndarray, C: int, precise: bool):
                     W[16 * tb + r, 32 * s + kk] = -Wf[tb * 4 + s, lane, e]   # stored negated
                     QG[16 * tb + r, 32 * s + kk] = Qf[tb * 4 + s, lane, e]
                 for s in range(CS):
-                    M[16 * tb + r, 32 * s + kk] = Mf[tb * CS + s, lane, e]
+                    if 2 * s <= tb:          # fragments above the diagonal are not stored
+                        M[16 * tb + r, 32 * s + kk] = Mf[tb * CS + s, lane, e]
             for kb in range(8):
                 for s in range(CS):
                     KG[32 * s + kk, 16 * kb + r] = Kf[kb * CS + s, lane, e]
