@@ -277,6 +277,7 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
     __shared__ __align__(16) float sBeta[C];
     __shared__ __align__(16) float sX[NB][16][20];   // per diagonal block: inverse scratch
     __shared__ float sVmax[NW];
+    __shared__ int sJob;                                // next unclaimed light job of phase 2
 
     const int H = p.H;
     const int tid = threadIdx.x, lane = tid & 63;
@@ -441,6 +442,7 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
             }
             ((float *)(rec + R::GC_OFF))[c] = pre;     // total decay of the chunk
         }
+        if (tid == 0) sJob = 0;
         for (int idx = tid; idx < C * C; idx += NT) {   // zero the blocks of T above the diagonal
             const int i = idx / C, j = idx % C;
             if ((j >> 4) > (i >> 4)) sT[i][j] = 0.0f;
@@ -463,24 +465,28 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
                 const float *ef = sEF[a > b ? a * (a - 1) / 2 + b : 0];
                 f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aM = {0.f, 0.f, 0.f, 0.f};
                 if (PRECISE || a == b) {
-                    float bK[4][8], bQ[4][8], aR[4][8];
+                    constexpr int KH = PRECISE ? 2 : 4;  // k-steps whose operands are loaded together
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        const int c = 32 * ks + 8 * lg;
-                        load8(&sK[il][c], bK[ks]);       // kh e^{G_i - G_16a}
-                        load8(&sQ[il][c], bQ[ks]);       // qh e^{G_i - G_16a}
-                        load8(&sP[jr][c], aR[ks]);       // kh / P_j
-                        if (a != b) {                    // e^{G_16a - G_j} = EF / P_j
-                            float f[8];
-                            load8(ef + c, f);
+                    for (int k0 = 0; k0 < 4; k0 += KH) {
+                        float bK[KH][8], bQ[KH][8], aR[KH][8];
 #pragma unroll
-                            for (int e = 0; e < 8; ++e) aR[ks][e] *= f[e];
+                        for (int kq = 0; kq < KH; ++kq) {
+                            const int c = 32 * (k0 + kq) + 8 * lg;
+                            load8(&sK[il][c], bK[kq]);   // kh e^{G_i - G_16a}
+                            load8(&sQ[il][c], bQ[kq]);   // qh e^{G_i - G_16a}
+                            load8(&sP[jr][c], aR[kq]);   // kh / P_j
+                            if (a != b) {                // e^{G_16a - G_j} = EF / P_j
+                                float f[8];
+                                load8(ef + c, f);
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) aR[kq][e] *= f[e];
+                            }
                         }
-                    }
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        aA = mfma_f32x8(aR[ks], bK[ks], aA);
-                        aM = mfma_f32x8(aR[ks], bQ[ks], aM);
+                        for (int kq = 0; kq < KH; ++kq) {
+                            aA = mfma_f32x8(aR[kq], bK[kq], aA);
+                            aM = mfma_f32x8(aR[kq], bQ[kq], aM);
+                        }
                     }
                 } else {
                     half8 hK[4], hQ[4], hR[4];
@@ -562,39 +568,51 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
                 }
             }
             {
-                // light jobs: the first NJ - 2 NB over the other waves, the last
-                // 2 NB (fragment jobs) to the diagonal waves once they are done
-                constexpr int NOFF = NB * (NB - 1) / 2, NQ = NB * 4, NKG = 8 * CS;
-                constexpr int NJ = NOFF + NQ + NKG, NJL = NJ - 2 * NB;
-                const int j0 = wave < NB ? NJL + wave : wave - NB;
-                const int js = wave < NB ? NB : NW - NB;
-                const int j1 = wave < NB ? NJ : NJL;
-                for (int j = j0; j < j1; j += js) {
+                // light jobs (off-diagonal blocks first, then the fragments), claimed
+                // one at a time from a shared counter by whichever wave is free
+                constexpr int NOFF = NB * (NB - 1) / 2;
+                constexpr int NJ = NOFF + NB + 8;      // + qg row blocks + kg^T key blocks
+                for (;;) {
+                    int claim = 0;
+                    if (lane == 0) claim = atomicAdd(&sJob, 1);
+                    const int j = __builtin_amdgcn_readfirstlane(claim);
+                    if (j >= NJ) break;
                     if (j < NOFF) {                      // off-diagonal block (a, b), a > b
                         const int a = j < 1 ? 1 : (j < 3 ? 2 : 3);
                         block(a, j - a * (a - 1) / 2);
-                    } else if (j < NOFF + NQ) {          // qg = qh e^{G_t} = (qh P_t) QF
-                        const int f = j - NOFF;
-                        const int tb = f >> 2, s = f & 3;
+                    } else if (j < NOFF + NB) {          // qg = qh e^{G_t} = (qh P_t) QF, rows of block tb
+                        const int tb = j - NOFF;
                         const int t = 16 * tb + lr;
-                        const int c0 = 32 * s + 4 * lg;
-                        const f32x4 q0 = *(const f32x4 *)&sQ[t][c0], q1 = *(const f32x4 *)&sQ[t][c0 + 16];
-                        const f32x4 f0 = *(const f32x4 *)&sQF[tb][c0], f1 = *(const f32x4 *)&sQF[tb][c0 + 16];
-                        float x[8];
+                        f32x4 q[8], f[8];
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) { x[e] = q0[e] * f0[e]; x[e + 4] = q1[e] * f1[e]; }
-                        F::store(rec + R::QG_OFF + ((size_t)(tb * 4 + s) * 64 + lane) * F::BYTES, x);
-                    } else {                             // kg = kh e^{G_C - G_t} = (kh / P_t) KF
-                        const int f = j - NOFF - NQ;
-                        const int kb = f / CS, s = f % CS;
-                        const int c = 16 * kb + lr;
-                        float x[8];
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            const int t = 32 * s + kperm(lg, e);
-                            x[e] = (t < C) ? sP[t][c] * sKF[t >> 4][c] : 0.f;
+                        for (int h2 = 0; h2 < 8; ++h2) {     // channels 16 h2 + 4 lg .. + 3
+                            q[h2] = *(const f32x4 *)&sQ[t][16 * h2 + 4 * lg];
+                            f[h2] = *(const f32x4 *)&sQF[tb][16 * h2 + 4 * lg];
                         }
-                        F::store(rec + R::KG_OFF + ((size_t)(kb * CS + s) * 64 + lane) * F::BYTES, x);
+#pragma unroll
+                        for (int s = 0; s < 4; ++s) {        // fragment (tb, s): channels 32 s + kperm
+                            float x[8];
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) {
+                                x[e] = q[2 * s][e] * f[2 * s][e];
+                                x[e + 4] = q[2 * s + 1][e] * f[2 * s + 1][e];
+                            }
+                            F::store(rec + R::QG_OFF + ((size_t)(tb * 4 + s) * 64 + lane) * F::BYTES, x);
+                        }
+                    } else {                             // kg = kh e^{G_C - G_t} = (kh / P_t) KF
+                        const int kb = j - NOFF - NB;
+                        const int c = 16 * kb + lr;
+                        float x[CS][8];
+#pragma unroll
+                        for (int s = 0; s < CS; ++s)
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                const int t = 32 * s + kperm(lg, e);
+                                x[s][e] = (t < C) ? sP[t][c] * sKF[t >> 4][c] : 0.f;
+                            }
+#pragma unroll
+                        for (int s = 0; s < CS; ++s)
+                            F::store(rec + R::KG_OFF + ((size_t)(kb * CS + s) * 64 + lane) * F::BYTES, x[s]);
                     }
                 }
             }
