@@ -58,6 +58,11 @@ def chunk_call(kda, **kw):
     (dict(scale=float("nan")), 1), (dict(lb=0.0), 1), (dict(lb=-5.5), 1), (dict(lb=0.5), 1),
     (dict(cu=None), 1), (dict(A_log=None), 1), (dict(q=None), 1), (dict(o=None), 1),
     (dict(ws=None), 3), (dict(wsb=1024), 3), (dict(ws=0x100010), 3),
+    # 16-byte alignment of tensor pointers, 4-byte for beta / A_log; head count cap
+    (dict(q=FAKE + 8), 1), (dict(k=FAKE + 2), 1), (dict(v=FAKE + 4), 1), (dict(g=FAKE + 4), 1),
+    (dict(dt_bias=FAKE + 4), 1), (dict(o=FAKE + 8), 1), (dict(h0=FAKE + 4), 1),
+    (dict(ht=FAKE + 12), 1), (dict(beta=FAKE + 2), 1), (dict(A_log=FAKE + 1), 1),
+    (dict(H=65537), 1),
 ])
 def test_chunk_fwd_rejects(kda, kw, status):
     assert chunk_call(kda, **kw) == status
@@ -77,7 +82,8 @@ def decode_call(kda, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(K=129), 2), (dict(V=64), 2), (dict(dt=5), 2), (dict(B=0), 1), (dict(H=-1), 1),
     (dict(state=None), 1), (dict(q=None), 1), (dict(lb=-6.0), 1), (dict(scale=-1.0), 1),
-    (dict(state=FAKE + 4), 1),
+    (dict(state=FAKE + 4), 1), (dict(q=FAKE + 8), 1), (dict(o=FAKE + 4), 1),
+    (dict(beta=FAKE + 2), 1), (dict(H=70000), 1),
 ])
 def test_decode_rejects(kda, kw, status):
     assert decode_call(kda, **kw) == status
