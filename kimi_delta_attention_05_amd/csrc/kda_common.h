@@ -4,11 +4,14 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace kda {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kHeadDim = 128;          // K = V = 128 (the contract's only head size)
 constexpr float kL2Eps = 1e-6f;        // q/k L2 normalisation epsilon

@@ -58,6 +58,9 @@ struct ChunkGeom {
 //   UbSc [4]                        fp32; [0] = power-of-two scale of Ub, 0 if
 //                                   every v of the chunk is zero
 //   Ub   [8 vb][NB tb][64 lane][4]  accumulator tiles of T V / UbSc[0] (Tub)
+// Rows past the end of a partial chunk are zero in -W, kgT and Ub (so they add
+// nothing to U or the state); in qg and M they are unspecified (they reach
+// only output rows that are never stored).
 // Tst and Tub are fp16 when the inputs are bf16 (W, qg, kg, M are bounded by 1
 // in magnitude; Ub is stored scaled so that it is bounded by 2^15) and fp32
 // when the inputs are fp32.

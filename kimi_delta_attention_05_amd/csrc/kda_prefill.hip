@@ -296,6 +296,29 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
         lds_barrier();
     }
 
+    // W and Ub fragments of the previous tile, stored during the next tile's
+    // phase 1 (VALU-bound, the memory queue idle) rather than at the end of
+    // their own tile, where they would queue behind the input copies
+    typedef std::conditional_t<PRECISE, f32x4, half4_t> UbT;
+    typename F::T pend_w[2];
+    UbT pend_u[NB];
+    unsigned char *pend_rec = nullptr;
+    auto flush = [&]() {
+        if (pend_rec) {
+#pragma unroll
+            for (int q2 = 0; q2 < 2; ++q2) {
+                const int tb = 2 * (wave >> 2) + q2;
+                if (tb < NB)
+                    *(typename F::T *)(pend_rec + R::W_OFF + ((size_t)(tb * 4 + (wave & 3)) * 64 + lane) * F::BYTES) =
+                        pend_w[q2];
+            }
+#pragma unroll
+            for (int tb = 0; tb < NB; ++tb)
+                *(UbT *)(pend_rec + R::UB_OFF + ((size_t)(wave * NB + tb) * 64 + lane) * 4 * R::UB_ELT) = pend_u[tb];
+            pend_rec = nullptr;
+        }
+    };
+
     for (; ti < ntiles; ) {
         const int64_t next = ti + gridDim.x;
         if (!valid) {                            // unused slot: nothing to compute
@@ -317,6 +340,7 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
         int64_t t0_nx = 0;
         const bool valid_nx = next < ntiles && locate_slot<C>(p.cu_seqlens, p.N, next / H, n_nx, t0_nx, L_nx);
 
+        flush();
         // ---- phase 1: a DPP row of 16 lanes per token, 8 channels per lane -------
         // gate: sigmoid(a (g + db)) = 1 / (1 + 2^(ga g + gb)), ga = -a log2e, gb = ga db;
         // 2^x overflows to inf for very negative arguments and 1/inf = 0, so this
@@ -354,19 +378,22 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
                 rg.load(p.g + row * kHeadDim + c8);
                 rb = p.beta_raw[row];
             }
-            // padding rows (t >= L) act as q = k = v = 0, lambda = 0, beta = 0
+            // padding rows (t >= L, holding a copy of the last row) act as k = 0,
+            // lambda = 0 and beta = 0: their rows of A, W and U_base are then zero
+            // (T's row is beta_t e_t), so their q and v reach nothing that is
+            // stored, and the chunk's total decay ignores them
             float sq = 0.f, sk = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                qv[it][e] = rv ? rq[e] : 0.f;
-                kv[it][e] = rv ? rk[e] : 0.f;
-                vreg[it][e] = rv ? rvv[e] : 0.f;
+                qv[it][e] = rq[e];
+                kv[it][e] = rk[e];
+                vreg[it][e] = rvv[e];
                 sq += qv[it][e] * qv[it][e];
                 sk += kv[it][e] * kv[it][e];
             }
             sq = row16_sum(sq);
             sk = row16_sum(sk);
-            const float fq = rsqrtf(sq + kL2Eps) * p.scale, fk = rsqrtf(sk + kL2Eps);
+            const float fq = rsqrtf(sq + kL2Eps) * p.scale, fk = rv ? rsqrtf(sk + kL2Eps) : 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 qv[it][e] *= fq;
@@ -774,27 +801,21 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
         if constexpr (PF) wait_vmem();        // the next tile's inputs have landed
         lds_barrier();                      // LDS is reused by the next tile
 #pragma unroll
-        for (int q2 = 0; q2 < 2; ++q2) {
-            const int tb = 2 * (wave >> 2) + q2;
-            if (tb < NB) {                      // stored negated: U = Ub + (-W) S^T
-                float x[8];
+        for (int q2 = 0; q2 < 2; ++q2) {        // W stored negated: U = Ub + (-W) S^T
+            float x[8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) x[e] = -wres[q2][e];
-                F::store(rec + R::W_OFF + ((size_t)(tb * 4 + sw) * 64 + lane) * F::BYTES, x);
-            }
+            for (int e = 0; e < 8; ++e) x[e] = -wres[q2][e];
+            pend_w[q2] = F::make(x, 1.0f);
         }
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb) {
-            unsigned char *dst = rec + R::UB_OFF + ((size_t)(wave * NB + tb) * 64 + lane) * 4 * R::UB_ELT;
-            if constexpr (PRECISE) {
-                *(f32x4 *)dst = ures[tb];
-            } else {
-                typedef _Float16 half4 __attribute__((ext_vector_type(4)));
-                *(half4 *)dst = half4{(_Float16)ures[tb][0], (_Float16)ures[tb][1],
+            if constexpr (PRECISE) pend_u[tb] = ures[tb];
+            else pend_u[tb] = half4_t{(_Float16)ures[tb][0], (_Float16)ures[tb][1],
                                       (_Float16)ures[tb][2], (_Float16)ures[tb][3]};
-            }
         }
+        pend_rec = rec;
     }
+    flush();
 }
 
 // =============================================================================
@@ -864,9 +885,10 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
     float sigma = 1.0f;
     const size_t sbase = ((size_t)chain * kHeadDim + vrow) * kHeadDim;
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-        if (p.h0) S[kb] = *(const f32x4 *)(p.h0 + sbase + 16 * kb + 4 * lg);
-        else S[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < 8; ++kb) S[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (p.h0) {
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) S[kb] = *(const f32x4 *)(p.h0 + sbase + 16 * kb + 4 * lg);
     }
 
     // DMA copy of chunk jc's record into LDS buffer buf, in parts spread over
@@ -1127,11 +1149,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &a) {
         if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
         const int64_t ntiles = slots * a.H;
-#ifdef KDA_INTRA_ONE_TILE_PER_GROUP
-        const int64_t grid = ntiles;
-#else
         const int64_t grid = ntiles < (int64_t)cus ? ntiles : (int64_t)cus;
-#endif
         intra_kernel<C, Tin, PRECISE><<<(unsigned)grid, 64 * kIntraWaves, 0, a.stream>>>(a, ntiles);
         e = hipGetLastError();
         if (e != hipSuccess) return e;

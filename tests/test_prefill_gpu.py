@@ -274,7 +274,10 @@ def test_intra_stage_matches_chunk_form(kda, dtype, chunk):
             scale = max(np.max(np.abs(want)), 1e-30)
             err = np.max(np.abs(got - want)) / scale
             assert err < tol, (n, j, h, name, err)
-            assert np.all(rec[name][L:] == 0.0), (n, j, h, name, "padding rows not zero")
+            if name in ("W", "kg", "U_base"):
+                # padding rows must not reach U or the state; those of qg and M only
+                # feed output rows that are never stored, and are left unspecified
+                assert np.all(rec[name][L:] == 0.0), (n, j, h, name, "padding rows not zero")
         err = np.max(np.abs(rec["Gamma_C"] - it["Gamma_C"])) / max(np.max(it["Gamma_C"]), 1e-30)
         assert err < tol, (n, j, h, "Gamma_C", err)
 
