@@ -14,9 +14,11 @@
 // batched decode. Transforms per the FlashInfer kda_backward contract.
 //
 // Thread layout: 256 threads = 4 waves; a DPP row of 16 lanes covers one state
-// row (8 consecutive fp32 per lane, two 16-byte loads); a wave covers 4 rows, the
-// workgroup 16 rows per iteration, 8 iterations for the 128 rows. All 16 loads of
-// a lane are issued before any arithmetic so that 64 KB per workgroup is in flight.
+// row, lane j holding channels 4j .. 4j+3 and 64+4j .. 64+4j+3, so that each of
+// the two 16-byte loads (and stores) of a row covers 256 contiguous bytes: whole
+// cache lines per instruction. A wave covers 4 rows, the workgroup 16 rows per
+// iteration, 8 iterations for the 128 rows. All 16 loads of a lane are issued
+// before any arithmetic so that 64 KB per workgroup is in flight.
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -34,34 +36,35 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const int h = bh % H;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
-    const int j = lane & 15;                   // channel group: channels 8j .. 8j+7
+    const int j = lane & 15;                   // channels 4j .. 4j+3 and 64+4j .. 64+4j+3
     const int r = lane >> 4;                   // row within the wave's 4 rows
-    const int c0 = 8 * j;
 
     f32x4 *S4 = reinterpret_cast<f32x4 *>(state + (size_t)bh * (kHeadDim * kHeadDim));
 
-    // Issue the state loads first: rows 16*it + 4*wave + r, columns c0..c0+7.
+    // Issue the state loads first: rows 16*it + 4*wave + r, 16-byte pieces j and 16+j.
     f32x4 st[8][2];
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
         const int row = 16 * it + 4 * wave + r;
-        st[it][0] = __builtin_nontemporal_load(S4 + row * 32 + 2 * j);
-        st[it][1] = __builtin_nontemporal_load(S4 + row * 32 + 2 * j + 1);
+        st[it][0] = __builtin_nontemporal_load(S4 + row * 32 + j);
+        st[it][1] = __builtin_nontemporal_load(S4 + row * 32 + 16 + j);
     }
 
-    // Per-token vectors for this lane's 8 channels (each 16-lane row holds all 128).
+    // Per-token vectors for this lane's 8 channels (each 16-lane row holds all 128):
+    // entry e is channel ch(e) = 4j + e for e < 4 and 64 + 4j + (e - 4) otherwise.
     const size_t tb = (size_t)bh * kHeadDim;
     float qv[8], kv[8], al[8];
     const float a_gate = fast_exp2(A_log[h] * kLog2e);
     float sqq = 0.f, skk = 0.f, sqk = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        qv[e] = to_f32(q[tb + c0 + e]);
-        kv[e] = to_f32(k[tb + c0 + e]);
+        const int ch = (e < 4) ? 4 * j + e : 64 + 4 * j + (e - 4);
+        qv[e] = to_f32(q[tb + ch]);
+        kv[e] = to_f32(k[tb + ch]);
         sqq += qv[e] * qv[e];
         skk += kv[e] * kv[e];
         sqk += qv[e] * kv[e];
-        const float x = a_gate * (g[tb + c0 + e] + dt_bias[h * kHeadDim + c0 + e]);
+        const float x = a_gate * (g[tb + ch] + dt_bias[h * kHeadDim + ch]);
         al[e] = fast_exp2(lower_bound * sigmoid_f(x) * kLog2e);   // alpha = e^lambda
     }
     sqq = row16_sum(sqq);
@@ -98,8 +101,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 #pragma unroll
         for (int e = 0; e < 8; ++e) s[e] += u * kh[e];
         const f32x4 s0 = {s[0], s[1], s[2], s[3]}, s1 = {s[4], s[5], s[6], s[7]};
-        __builtin_nontemporal_store(s0, S4 + row * 32 + 2 * j);
-        __builtin_nontemporal_store(s1, S4 + row * 32 + 2 * j + 1);
+        __builtin_nontemporal_store(s0, S4 + row * 32 + j);
+        __builtin_nontemporal_store(s1, S4 + row * 32 + 16 + j);
         if (j == 0) so[row] = a + u * kq;
     }
     lds_barrier();
