@@ -64,6 +64,16 @@ __device__ __forceinline__ void wait_vmem() {
     asm volatile("" ::: "memory");
 }
 
+// The same, except that the N newest vector memory operations of this wave may
+// still be in flight (loads and stores complete in issue order for this counter).
+template <int N>
+__device__ __forceinline__ void wait_vmem_except() {
+    static_assert(N >= 0 && N < 16, "vmcnt immediate (low field)");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+    asm volatile("" ::: "memory");
+}
+
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 
 // Asynchronous copies from global memory straight into LDS (global->LDS DMA,

@@ -86,7 +86,7 @@ size_t record_bytes(int chunk, bool precise);
 
 // Number of chunk slots: chunk j of sequence n lives in slot floor(cu[n]/C) + n + j,
 // which is unique and below floor(T/C) + N for any valid offsets.
-inline int64_t num_slots(int64_t T, int N, int chunk) { return T / chunk + N; }
+__host__ __device__ inline int64_t num_slots(int64_t T, int N, int chunk) { return T / chunk + N; }
 
 hipError_t launch_decode(const DecodeArgs &a);
 hipError_t launch_prefill(const PrefillArgs &a);

@@ -922,38 +922,36 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
     // L2 prefetch two chunks ahead: one 4-byte load per 128-byte line of this
     // workgroup's share of a record (the two halves of a chain split the shared
     // operands). The values are never used; they stay in registers until the
-    // end-of-chunk wait so that no earlier wait is placed on them.
+    // end-of-chunk wait so that no earlier wait is placed on them. Every lane
+    // issues every load (lanes past the share re-touch line 0), so that each
+    // wave issues the same known number of memory instructions per chunk.
     constexpr int SHL = (int)((R::SHARED_BYTES + 127) / 128), SHL2 = (SHL + 1) / 2;
     constexpr int UBL = (int)(4 * R::UB_VB_BYTES / 128);
     constexpr int NTOUCH = (SHL2 + UBL + 255) / 256;
-    const unsigned char *touch_base[NTOUCH];
+    uint32_t touch_off[NTOUCH];
 #pragma unroll
     for (int i = 0; i < NTOUCH; ++i) {
         const int li = tid + 256 * i;
         const int sh = vg * SHL2 + li;
-        touch_base[i] = (li < SHL2) ? ((sh < SHL) ? rec0 + 128 * sh : nullptr)
-                      : (li < SHL2 + UBL ? rec0 + ub_off + 128 * (li - SHL2) : nullptr);
+        touch_off[i] = (li < SHL2) ? ((sh < SHL) ? 128u * sh : 0u)
+                     : (li < SHL2 + UBL ? ub_off + 128u * (li - SHL2) : 0u);
     }
     uint32_t touched[NTOUCH];
 #pragma unroll
     for (int i = 0; i < NTOUCH; ++i) touched[i] = 0;
     auto touch = [&](int jc) {
+        const unsigned char *r = rec0 + (size_t)jc * rec_step;
 #pragma unroll
-        for (int i = 0; i < NTOUCH; ++i)
-            if (touch_base[i]) touched[i] = *(const uint32_t *)(touch_base[i] + (size_t)jc * rec_step);
+        for (int i = 0; i < NTOUCH; ++i) touched[i] = *(const uint32_t *)(r + touch_off[i]);
     };
 
-    // this lane writes o[t][h][16 vb + 4 lg .. + 3] for t = chunk start + 16 tb + lr;
-    // a chunk's outputs are stored while the next chunk computes
+    // this lane writes o[t][h][16 vb + 4 lg .. + 3] for t = chunk start + 16 tb + lr,
+    // at the end of the chunk; lanes whose row lies past the sequence end write
+    // the same 16 bytes of the workspace's spare tail instead, so that every
+    // lane issues every store (the end-of-chunk wait counts them)
     Tout *__restrict__ o = (Tout *)p.o + ((size_t)(s0 + lr) * H + h) * kHeadDim + 16 * vb + 4 * lg;
+    Tout *const o_spare = (Tout *)(p.ws + (size_t)num_slots(p.T, p.N, C) * H * R::BYTES);
     const size_t o_tb = (size_t)16 * H * kHeadDim, o_chunk = (size_t)C * H * kHeadDim;
-    f32x4 pend[NB];
-    int Lp = 0;
-    auto store_pending = [&](Tout *dst) {
-#pragma unroll
-        for (int tb = 0; tb < NB; ++tb)
-            if (16 * tb + lr < Lp) store4<Tout>(dst + tb * o_tb, pend[tb]);
-    };
 
     if (nch > 0) {
         fetch(0, 0, 0, NCP);
@@ -967,7 +965,7 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
         const unsigned char *B = smem + (size_t)buf * CFG::BUF;
         const int L = (len - (int64_t)jc * C) < C ? (int)(len - (int64_t)jc * C) : C;
         if (ahead) fetch(jc + 1, buf ^ 1, 0, NCP);
-        if (jc + 2 < nch) touch(jc + 2);
+        touch(jc + 2 < nch ? jc + 2 : jc);
 
         // operands are requested one 16-row tile ahead of the products using them
         auto frag = [&](size_t off, int idx) { return F::load(B + off + ((size_t)idx * 64 + lane) * F::BYTES); };
@@ -991,7 +989,6 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
         }
         if constexpr (!PRECISE) us = *(const float *)(B + R::UBS_OFF);
 
-        if (jc > 0) store_pending(o - o_chunk);
 
         // rescale the state when S / sigma leaves [2^4, 2^14] or sigma < us
         // (|Ub| / sigma <= 2^15 needs sigma >= us); both are powers of two
@@ -1112,21 +1109,24 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
         }
 
 #pragma unroll
-        for (int tb = 0; tb < NB; ++tb) pend[tb] = O[tb] * sigma;
-        Lp = L;
+        for (int tb = 0; tb < NB; ++tb)
+            store4<Tout>(16 * tb + lr < L ? o + tb * o_tb : o_spare, O[tb] * sigma);
         o += o_chunk;
         if (jc + 1 < nch) {
             if (CFG::NBUF == 1) {
                 lds_barrier();            // everyone is done with the single buffer
                 fetch(jc + 1, 0, 0, NCP);
+                wait_vmem();
+            } else {
+                // the copies and touches issued at the chunk start have landed; the
+                // NB output stores issued since (the newest) may still be in flight
+                wait_vmem_except<NB>();
             }
-            wait_vmem();                  // this wave's copies have landed ...
             lds_barrier();                // ... and everyone else's
         }
 #pragma unroll
         for (int i = 0; i < NTOUCH; ++i) asm volatile("" ::"v"(touched[i]));
     }
-    if (nch > 0) store_pending(o - o_chunk);
 
     if (p.ht) {
 #pragma unroll
