@@ -219,6 +219,16 @@ __device__ __forceinline__ int kperm(int g, int e) {
     return (e < 4) ? (4 * g + e) : (16 + 4 * g + (e - 4));
 }
 
+// Key channels follow a different order, chosen so that each lane's 8 channels
+// of a k-step are contiguous in memory (one 16-byte load of bf16 inputs): the
+// channel at k-index (g, e) of step s is 32 s + 8 g + e. Accumulator tiles
+// whose rows are key channels (the state S^T, kg^T) therefore hold, in tile kb,
+// row r = 4 g + i, the channel tile_chan(kb, r) below -- two consecutive tiles
+// 2s, 2s+1 stack into exactly the k-step s operand order.
+__device__ __forceinline__ int tile_chan(int kb, int r) {
+    return 32 * (kb >> 1) + 8 * (r >> 2) + 4 * (kb & 1) + (r & 3);
+}
+
 __device__ __forceinline__ f32x4 mfma_f16(const float (&a)[8], const float (&b)[8], f32x4 acc) {
     half8 ha, hb;
 #pragma unroll

@@ -51,6 +51,11 @@ struct ChunkGeom {
 //                                   so that U = Ub + (-W) S^T is one accumulation
 //   qg   [NB tb][4 s][64 lane][8]   rows t, k over key channels   (Tst)
 //   kgT  [8 kb][CS s][64 lane][8]   rows key channel, k over t    (Tst)
+// A fragment's lane l holds row l % 16; its 8 k-values are, for k over key
+// channels, the channels 32 s + 8 (l / 16) + e, and for k over t the rows
+// 32 s + kperm(l / 16, e) (kda_common.h). Row r of kgT tile kb is the key
+// channel tile_chan(kb, r), so that the state tiles the inter-chunk kernel
+// accumulates from it stack into the channel order of W and qg.
 //   M    [NB tb][CS s][64 lane][8]  rows t, k over t'             (Tst); fragments
 //                                   with 2 s > tb lie above the diagonal, are
 //                                   never read and are left unwritten

@@ -612,12 +612,13 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
                         const int t = 16 * tb + lr;
                         f32x4 q[8], f[8];
 #pragma unroll
-                        for (int h2 = 0; h2 < 8; ++h2) {     // channels 16 h2 + 4 lg .. + 3
-                            q[h2] = *(const f32x4 *)&sQ[t][16 * h2 + 4 * lg];
-                            f[h2] = *(const f32x4 *)&sQF[tb][16 * h2 + 4 * lg];
+                        for (int h2 = 0; h2 < 8; ++h2) {     // channels 32 (h2/2) + 8 lg + 4 (h2%2) .. + 3
+                            const int c = 32 * (h2 >> 1) + 8 * lg + 4 * (h2 & 1);
+                            q[h2] = *(const f32x4 *)&sQ[t][c];
+                            f[h2] = *(const f32x4 *)&sQF[tb][c];
                         }
 #pragma unroll
-                        for (int s = 0; s < 4; ++s) {        // fragment (tb, s): channels 32 s + kperm
+                        for (int s = 0; s < 4; ++s) {        // fragment (tb, s): channels 32 s + 8 lg + e
                             float x[8];
 #pragma unroll
                             for (int e = 0; e < 4; ++e) {
@@ -628,7 +629,7 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
                         }
                     } else {                             // kg = kh e^{G_C - G_t} = (kh / P_t) KF
                         const int kb = j - NOFF - NB;
-                        const int c = 16 * kb + lr;
+                        const int c = tile_chan(kb, lr);
                         float x[CS][8];
 #pragma unroll
                         for (int s = 0; s < CS; ++s)
@@ -678,10 +679,10 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
         lds_barrier();
 
         // phase-5 operands that do not depend on T, built before the inverse ends:
-        // W^T A operand (kh e^{G_j} = (kh P_j) QF, channel blocks 2s', 2s'+1 with
+        // W^T A operand (kh e^{G_j} = (kh P_j) QF, channel tiles 2s', 2s'+1 with
         // s' = wave % 4) and the Ub B operand (v columns of block vb = wave).
         const int sw = wave & 3;
-        const int ca = 32 * sw + lr, cb = ca + 16;
+        const int ca = tile_chan(2 * sw, lr), cb = tile_chan(2 * sw + 1, lr);
         const int col = 16 * wave + lr;
         float a0[CS][8], a1[CS][8], bV[CS][8];
 #pragma unroll
@@ -878,7 +879,8 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
     const int nch = (int)((len + C - 1) / C);
     const int64_t slot0 = s0 / C + n;
 
-    // State S^T tiles: lane holds S[vrow][16 kb + 4 lg + i]. On the fp16 path the
+    // State S^T tiles: lane holds S[vrow][tile_chan(kb, 4 lg + i)] (the row order
+    // of the kg^T tiles it accumulates from). On the fp16 path the
     // registers hold S / sigma for a wave-uniform power of two sigma, chosen so
     // that S / sigma converts to fp16 without overflow and U / sigma too.
     f32x4 S[8];
@@ -888,7 +890,7 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
     for (int kb = 0; kb < 8; ++kb) S[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (p.h0) {
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) S[kb] = *(const f32x4 *)(p.h0 + sbase + 16 * kb + 4 * lg);
+        for (int kb = 0; kb < 8; ++kb) S[kb] = *(const f32x4 *)(p.h0 + sbase + tile_chan(kb, 4 * lg));
     }
 
     // DMA copy of chunk jc's record into LDS buffer buf, in parts spread over
@@ -1008,7 +1010,7 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
                 sigma = tgt;
             }
         }
-        // state operand: k-step s covers channels 32 s + kperm(lg, e); it is the
+        // state operand: k-step s covers channels 32 s + 8 lg + e (tiles 2s, 2s+1); it is the
         // B operand of W S^T (columns v) and the A operand of S qg^T (rows v)
         FT bS[4];
 #pragma unroll
@@ -1055,7 +1057,7 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
 #pragma unroll
             for (int s = 0; s < CS; ++s) fk[kb][s] = frag(R::KG_OFF, kb * CS + s);
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) gv[kb] = *(const f32x4 *)(B + R::GC_OFF + 4 * (16 * kb + 4 * lg));
+        for (int kb = 0; kb < 8; ++kb) gv[kb] = *(const f32x4 *)(B + R::GC_OFF + 4 * tile_chan(kb, 4 * lg));
 
         // U / sigma must fit fp16: otherwise raise sigma (rare)
         if constexpr (!PRECISE) {
@@ -1131,7 +1133,507 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
     if (p.ht) {
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb)
-            *(f32x4 *)(p.ht + sbase + 16 * kb + 4 * lg) = S[kb] * sigma;
+            *(f32x4 *)(p.ht + sbase + tile_chan(kb, 4 * lg)) = S[kb] * sigma;
+    }
+}
+
+// =============================================================================
+// Intra-chunk kernel for 64-row chunks with bf16 inputs (fp16 records): four
+// waves per workgroup, wave b holding rows 16b .. 16b+15 of the tile in
+// registers in the MFMA operand layout -- lane (lr, lg) holds row lr at the key
+// channels 32 s + 8 lg + e, s = 0..3, e = 0..7 (16 contiguous bytes of a bf16
+// row per k-step, one load each) -- so that the norms, gates
+// and decay factors are computed where the products consume them. About 74 KiB
+// of LDS, so two workgroups share a CU and one's barriers and memory waits
+// overlap the other's arithmetic.
+//
+// Decay factors come from block-local cumulative log-decays (log2 units):
+// Lam_r = sum_{s=1..r} lambda_{16b+s}, a prefix sum over the 16 lanes of a DPP
+// row; P_r = 2^Lam_r and 1/P_r = 2^-Lam_r are within 2^+-108 (normal fp32), and
+// the factors across blocks are products of per-block totals, each at most 1.
+// Transposes between the row layout and the time-major operands of the W, Ub
+// and kg^T products go through MFMA with an identity factor (exact for fp16).
+// =============================================================================
+struct IntraRB {
+    static constexpr int AP = 68;                         // sA / sT row pitch (floats)
+    static constexpr int TP = 72;                         // KE^T / V^T row pitch (halves)
+    static constexpr int NFV = 6;                         // factor vectors per wave
+    static constexpr size_t SA = 0;                       // float [64][AP]: A (beta-scaled, strictly lower)
+    static constexpr size_t ST = SA + (size_t)64 * AP * 4;     // float [64][AP]: X = (I + A)^-1
+    static constexpr size_t SL0 = ST + (size_t)64 * AP * 4;    // float [4][128]: lambda of each block's row 0
+    static constexpr size_t SLE = SL0 + 4 * 128 * 4;           // float [4][128]: Lam at each block's row 15
+    static constexpr size_t SBETA = SLE + 4 * 128 * 4;         // float [64]
+    static constexpr size_t SVMAX = SBETA + 64 * 4;            // float [4]
+    static constexpr size_t U = SVMAX + 64;                    // union of two uses:
+    static constexpr size_t FV = U;                            //  per-wave factor vectors [4][NFV][128]
+    static constexpr size_t RP = FV + (size_t)4 * NFV * 128 * 4;   //  R' fragments half8 [3][4][64]
+    static constexpr size_t SX = RP + (size_t)3 * 4 * 64 * 16;     //  inverse scratch [4][16][20]
+    static constexpr size_t U1_END = SX + (size_t)4 * 16 * 20 * 4;
+    static constexpr size_t KET = U;                           //  KE^T fp16 [128][TP] (after the inverse)
+    static constexpr size_t VT = KET + (size_t)128 * TP * 2;   //  V^T  fp16 [128][TP]
+    static constexpr size_t U2_END = VT + (size_t)128 * TP * 2;
+    static constexpr size_t BYTES = U1_END > U2_END ? U1_END : U2_END;
+};
+
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+template <typename Tin>
+__global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t ntiles)
+{
+    constexpr int C = 64, NB = 4, CS = 2;
+    using R = Record<C, false>;
+    using LY = IntraRB;
+    static_assert(std::is_same<Tin, __bf16>::value, "bf16 inputs");
+
+    __shared__ __align__(16) unsigned char smem[LY::BYTES];
+    float (*sA)[LY::AP] = (float (*)[LY::AP])(smem + LY::SA);
+    float (*sT)[LY::AP] = (float (*)[LY::AP])(smem + LY::ST);
+    float *sL0 = (float *)(smem + LY::SL0);
+    float *sLE = (float *)(smem + LY::SLE);
+    float *sBeta = (float *)(smem + LY::SBETA);
+    float *sVmax = (float *)(smem + LY::SVMAX);
+    half8 *sRP = (half8 *)(smem + LY::RP);
+    _Float16 *sKET = (_Float16 *)(smem + LY::KET);
+    _Float16 *sVT = (_Float16 *)(smem + LY::VT);
+
+    const int H = p.H;
+    const float lb2 = p.lower_bound * kLog2e;
+
+    // blocks (0,1) and (2,3) of T lie above the diagonal but inside the k-steps
+    // that the W / Ub products read: zero once (nothing else writes them)
+    for (int idx = threadIdx.x; idx < 512; idx += 256) {
+        const int blk = idx >> 8, e = idx & 255;
+        sT[32 * blk + (e >> 4)][32 * blk + 16 + (e & 15)] = 0.0f;
+    }
+
+    // W and Ub results of the previous tile, stored once the next tile's loads are issued
+    half8 pw[4];
+    half4_t pu[8];
+    unsigned char *prec = nullptr;
+
+    for (int64_t ti = blockIdx.x; ti < ntiles; ti += gridDim.x) {
+        // lane and wave indices are re-derived every tile (opaque to the
+        // compiler), so that the many per-lane addresses below are formed where
+        // they are used instead of being hoisted out of the loop into registers
+        int tid = threadIdx.x, bw = tid >> 6;
+        asm volatile("" : "+v"(tid));
+        bw = __builtin_amdgcn_readfirstlane(bw);
+        asm volatile("" : "+s"(bw));
+        const int b = bw;                           // this wave's 16-row block
+        const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
+        float *fv = (float *)(smem + LY::FV) + (size_t)b * LY::NFV * 128;   // this wave's factor vectors
+        // identity selectors: column c of tile 2s + half picks channel tile_chan(2s + half, c),
+        // i.e. k-index (c / 4, 4 half + c % 4) of step s
+        half8 id0, id1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            id0[e] = (_Float16)((lg == (lr >> 2) && e == (lr & 3)) ? 1.0f : 0.0f);
+            id1[e] = (_Float16)((lg == (lr >> 2) && e == 4 + (lr & 3)) ? 1.0f : 0.0f);
+        }
+        // channel offset of entry (s, half) of this lane: 32 s + 8 lg + 4 half
+        auto chan = [&](int s, int hf) { return 32 * s + 8 * lg + 4 * hf; };
+
+        int n = 0, L = 0;
+        int64_t t0 = 0;
+        if (!locate_slot<C>(p.cu_seqlens, p.N, ti / H, n, t0, L)) continue;   // unused slot
+        const int h = (int)(ti % H);
+        unsigned char *rec = p.ws + (size_t)ti * R::BYTES;
+
+        // ---- loads: gates first (consumed first), then q, k, v, beta ----------------
+        const int r = 16 * b + lr;                  // tile row of this lane
+        const bool rv = r < L;
+        const size_t row = (size_t)(t0 + (rv ? r : L - 1)) * H + h;
+        const float *gr = p.g + row * kHeadDim;
+        const float *dtr = p.dt_bias + (size_t)h * kHeadDim;
+        f32x4 graw[4][2], draw[4][2];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                graw[s][hf] = *(const f32x4 *)(gr + chan(s, hf));
+                draw[s][hf] = *(const f32x4 *)(dtr + chan(s, hf));
+            }
+        const Tin *qr = (const Tin *)p.q + row * kHeadDim;
+        const Tin *kr = (const Tin *)p.k + row * kHeadDim;
+        const Tin *vr = (const Tin *)p.v + row * kHeadDim;
+        bf16x8 qraw[4], kraw[4], vraw[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            qraw[s] = *(const bf16x8 *)(qr + chan(s, 0));
+            kraw[s] = *(const bf16x8 *)(kr + chan(s, 0));
+            vraw[s] = *(const bf16x8 *)(vr + chan(s, 0));
+        }
+        const float braw = p.beta_raw[row];
+        const float alog = *(const __attribute__((address_space(4))) float *)(p.A_log + h);
+
+        // the previous tile's W / Ub, now behind this tile's loads in the memory queue
+        if (prec) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                *(half8 *)(prec + R::W_OFF + ((size_t)(b * 4 + s) * 64 + lane) * 16) = pw[s];
+#pragma unroll
+            for (int vb = 0; vb < 8; ++vb)
+                *(half4_t *)(prec + R::UB_OFF + ((size_t)(vb * NB + b) * 64 + lane) * 8) = pu[vb];
+            prec = nullptr;
+        }
+
+        // ---- gates and block-local cumulative log-decay ------------------------------
+        // sigmoid(a (g + db)) = 1 / (1 + 2^(ga g + ga db)), ga = -a log2e; lambda in
+        // log2 units = lb2 * sigmoid; rows past the chunk end get lambda = 0
+        const float ga = -fast_exp2(alog * kLog2e) * kLog2e;
+        float lam[4][8];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float sg = fast_rcp(1.0f + fast_exp2(fmaf(graw[s][hf][i], ga, ga * draw[s][hf][i])));
+                    lam[s][4 * hf + i] = rv ? lb2 * sg : 0.0f;
+                }
+        if (lr == 0) {                               // lambda of the block's first row
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+                    *(f32x4 *)(sL0 + b * 128 + chan(s, hf)) =
+                        f32x4{lam[s][4 * hf], lam[s][4 * hf + 1], lam[s][4 * hf + 2], lam[s][4 * hf + 3]};
+        }
+        // Lam_r = sum_{s=1..r} lambda_s over the block: inclusive prefix sum across
+        // the 16 lanes of the DPP row (row_shr d, out-of-row lanes read 0)
+        float Lm[4][8];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Lm[s][e] = (lr == 0) ? 0.0f : lam[s][e];
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Lm[s][e] += dpp_f<0x111>(Lm[s][e]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Lm[s][e] += dpp_f<0x112>(Lm[s][e]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Lm[s][e] += dpp_f<0x114>(Lm[s][e]);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Lm[s][e] += dpp_f<0x118>(Lm[s][e]);
+        if (lr == 15) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+                    *(f32x4 *)(sLE + b * 128 + chan(s, hf)) =
+                        f32x4{Lm[s][4 * hf], Lm[s][4 * hf + 1], Lm[s][4 * hf + 2], Lm[s][4 * hf + 3]};
+        }
+        float vmax = 0.0f;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) vmax = fmaxf(vmax, fabsf((float)vraw[s][4 * hf + i]));
+        vmax = wave_max_nonneg(vmax);
+        if (lane == 0) sVmax[b] = vmax;
+        lds_barrier();                                                     // B1
+
+        // ---- per-channel factors (lane: channels 2 lane, 2 lane + 1) ------------------
+        //   QF_b = e^{G_16b}                      (chunk-relative, row 16b included)
+        //   KF_b = prod of the block totals after b
+        //   Pe_b = 2^Lam_15 of block b
+        //   X_bc = e^{G_16b - G_16c+15}, c < b
+        {
+            float tot[NB][2], l0b[2], leb[2];
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb) {
+                const float2 x0 = *(const float2 *)(sL0 + bb * 128 + 2 * lane);
+                const float2 xe = *(const float2 *)(sLE + bb * 128 + 2 * lane);
+                tot[bb][0] = x0.x + xe.x;
+                tot[bb][1] = x0.y + xe.y;
+                if (bb == b) { l0b[0] = x0.x; l0b[1] = x0.y; leb[0] = xe.x; leb[1] = xe.y; }
+            }
+            float qf[2], kf[2], xs[NB][2], all[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                float pre = 0.f, suf = 0.f, sum = 0.f;
+#pragma unroll
+                for (int bb = 0; bb < NB; ++bb) {
+                    if (bb < b) pre += tot[bb][i];
+                    if (bb > b) suf += tot[bb][i];
+                    sum += tot[bb][i];
+                }
+                qf[i] = pre + l0b[i];
+                kf[i] = suf;
+                all[i] = sum;
+                // X_bc: lambda of row 16b plus the totals of the blocks strictly between
+                float run = l0b[i];
+#pragma unroll
+                for (int c = NB - 1; c >= 0; --c) {
+                    if (c < b) {
+                        xs[c][i] = run;
+                        run += tot[c][i];
+                    }
+                }
+            }
+            *(float2 *)(fv + 0 * 128 + 2 * lane) = float2{fast_exp2(qf[0]), fast_exp2(qf[1])};
+            *(float2 *)(fv + 1 * 128 + 2 * lane) = float2{fast_exp2(kf[0]), fast_exp2(kf[1])};
+            *(float2 *)(fv + 2 * 128 + 2 * lane) = float2{fast_exp2(leb[0]), fast_exp2(leb[1])};
+#pragma unroll
+            for (int c = 0; c < NB - 1; ++c)
+                if (c < b)
+                    *(float2 *)(fv + (3 + c) * 128 + 2 * lane) = float2{fast_exp2(xs[c][0]), fast_exp2(xs[c][1])};
+            if (b == 0)                              // total decay of the chunk
+                *(float2 *)(rec + R::GC_OFF + 8 * lane) = float2{fast_exp2(all[0]), fast_exp2(all[1])};
+        }
+        if (lg == 0) sBeta[r] = rv ? sigmoid_f(braw) : 0.0f;
+        const float beta = rv ? sigmoid_f(braw) : 0.0f;
+        // power-of-two scale of v for the fp16 product T v (exact)
+        float vscale, vinv;
+        {
+            const float m = fmaxf(fmaxf(sVmax[0], sVmax[1]), fmaxf(sVmax[2], sVmax[3]));
+            vscale = pow2_scale_for(m, 9);          // |T v / vscale| <= 64 * 2^9 = 2^15
+            vinv = inv_pow2(vscale);
+            if (tid == 0) *(float *)(rec + R::UBS_OFF) = (m > 0.f) ? vscale : 0.0f;
+        }
+
+        // ---- row quantities: norms, decay products, fp16 operands ---------------------
+        float KP[4][8], QP[4][8], RI[4][8];
+        half8 ke16[4], v16[4];
+        {
+            float sq = 0.f, sk = 0.f;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float qx = (float)qraw[s][4 * hf + i], kx = (float)kraw[s][4 * hf + i];
+                        sq = fmaf(qx, qx, sq);
+                        sk = fmaf(kx, kx, sk);
+                    }
+            sq += __shfl_xor(sq, 16);
+            sq += __shfl_xor(sq, 32);
+            sk += __shfl_xor(sk, 16);
+            sk += __shfl_xor(sk, 32);
+            const float fq = rsqrtf(sq + kL2Eps) * p.scale, fk = rv ? rsqrtf(sk + kL2Eps) : 0.0f;
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const int e = 4 * hf + i;
+                        const float ep = fast_exp2(Lm[s][e]), em = fast_exp2(-Lm[s][e]);
+                        const float kh = (float)kraw[s][e] * fk;
+                        KP[s][e] = kh * ep;                               // kh e^{G_t - G_16b}
+                        QP[s][e] = (float)qraw[s][e] * fq * ep;           // qh e^{G_t - G_16b}
+                        RI[s][e] = kh * em;                               // kh e^{G_16b - G_t}
+                        v16[s][e] = (_Float16)((float)vraw[s][e] * vinv);
+                    }
+        }
+        // qg, kg^T, KE and the R' operands of the off-diagonal blocks
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            float qf[8], kf[8], pe[8];
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const f32x4 a = *(const f32x4 *)(fv + 0 * 128 + chan(s, hf));
+                const f32x4 k = *(const f32x4 *)(fv + 1 * 128 + chan(s, hf));
+                const f32x4 e = *(const f32x4 *)(fv + 2 * 128 + chan(s, hf));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) { qf[4 * hf + i] = a[i]; kf[4 * hf + i] = k[i]; pe[4 * hf + i] = e[i]; }
+            }
+            half8 qg, kg, rp;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float rpe = RI[s][e] * pe[e];          // kh e^{G_16b+15 - G_t} <= |kh|
+                rp[e] = (_Float16)rpe;
+                kg[e] = (_Float16)(rpe * kf[e]);             // kh e^{G_C - G_t}
+                qg[e] = (_Float16)(QP[s][e] * qf[e]);        // qh e^{G_t}
+                ke16[s][e] = (_Float16)(KP[s][e] * qf[e]);   // kh e^{G_t}
+            }
+            if (b < NB - 1) sRP[(b * 4 + s) * 64 + lane] = rp;
+            *(half8 *)(rec + R::QG_OFF + ((size_t)(b * 4 + s) * 64 + lane) * 16) = qg;
+            // kg^T fragments (tile 2s + half, k-step b / 2): this block's rows are
+            // positions 4 (b & 1) .. + 3 of each lane's 8
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const f32x4 t = mfma_h(kg, hf ? id1 : id0, f32x4{0.f, 0.f, 0.f, 0.f});
+                *(half4_t *)(rec + R::KG_OFF + ((size_t)((2 * s + hf) * CS + (b >> 1)) * 64 + lane) * 16 + 8 * (b & 1)) =
+                    half4_t{(_Float16)t[0], (_Float16)t[1], (_Float16)t[2], (_Float16)t[3]};
+            }
+        }
+        lds_barrier();                                                     // B2: R' visible
+
+        // ---- A and M blocks of row block b ------------------------------------------
+        // lane holds A[i][j] / M[i][j] for i = 16b + lr, j = 16c + 4lg + ii
+        {
+            f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aM = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {               // diagonal block: fp32 MFMA (factors up to 2^108)
+                aA = mfma_f32x8(RI[s], KP[s], aA);
+                aM = mfma_f32x8(RI[s], QP[s], aM);
+            }
+            f32x4 av;
+            float xm[8];
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii) {
+                const int j = 4 * lg + ii;
+                av[ii] = (lr > j) ? beta * aA[ii] : 0.0f;
+                xm[ii] = (j <= lr) ? aM[ii] : 0.0f;
+                xm[ii + 4] = 0.0f;
+            }
+            *(f32x4 *)&sA[16 * b + lr][16 * b + 4 * lg] = av;
+            unsigned char *mf = rec + R::M_OFF + ((size_t)(b * CS + (b >> 1)) * 64 + lane) * 16;
+            if ((b & 1) == 0)
+                *(half8 *)mf = half8{(_Float16)xm[0], (_Float16)xm[1], (_Float16)xm[2], (_Float16)xm[3],
+                                     (_Float16)0.f, (_Float16)0.f, (_Float16)0.f, (_Float16)0.f};
+            else
+                *(half4_t *)(mf + 8) = half4_t{(_Float16)xm[0], (_Float16)xm[1], (_Float16)xm[2], (_Float16)xm[3]};
+        }
+        for (int c = 0; c < b; ++c) {                   // off-diagonal blocks (b, c), c < b: fp16
+            f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aM = {0.f, 0.f, 0.f, 0.f};
+            const float *xf = fv + (3 + c) * 128;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const half8 rpc = sRP[(c * 4 + s) * 64 + lane];
+                const f32x4 x0 = *(const f32x4 *)(xf + chan(s, 0)), x1 = *(const f32x4 *)(xf + chan(s, 1));
+                half8 lk, lq;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    lk[i] = (_Float16)(KP[s][i] * x0[i]);
+                    lk[i + 4] = (_Float16)(KP[s][i + 4] * x1[i]);
+                    lq[i] = (_Float16)(QP[s][i] * x0[i]);
+                    lq[i + 4] = (_Float16)(QP[s][i + 4] * x1[i]);
+                }
+                aA = mfma_h(rpc, lk, aA);
+                aM = mfma_h(rpc, lq, aM);
+            }
+            *(f32x4 *)&sA[16 * b + lr][16 * c + 4 * lg] = aA * beta;
+            *(half4_t *)(rec + R::M_OFF + ((size_t)(b * CS + (c >> 1)) * 64 + lane) * 16 + 8 * (c & 1)) =
+                half4_t{(_Float16)aM[0], (_Float16)aM[1], (_Float16)aM[2], (_Float16)aM[3]};
+        }
+        // diagonal block of (I + A)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8) (A^16 = 0);
+        // this wave wrote A_bb above and its LDS accesses complete in order
+        {
+            const float *Ab = &sA[16 * b][16 * b];
+            float *Sx = (float *)(smem + LY::SX) + b * 16 * 20;
+            const f32x4 p1 = lds_right16(Ab, LY::AP, lr, lg);
+            f32x4 z;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) z[i] = ((4 * lg + i == lr) ? 1.0f : 0.0f) - p1[i];
+            f32x4 pw2 = mm16(lds_left16(Ab, LY::AP, lr, lg), p1, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+            for (int m = 0; m < 3; ++m) {
+                lds_store16(Sx, 20, pw2, lr, lg);
+                const f32x4 lp = lds_left16(Sx, 20, lr, lg);
+                z = mm16(lp, z, z);                          // z += A^(2^(m+1)) z
+                if (m < 2) pw2 = mm16(lp, pw2, f32x4{0.f, 0.f, 0.f, 0.f});
+            }
+            lds_store16(&sT[16 * b][16 * b], LY::AP, z, lr, lg);
+        }
+        lds_barrier();                                                     // B3
+
+        // ---- off-diagonal blocks of X, level 1: X_10, X_32 ----------------------------
+        if (b < 2) {
+            const int a = 2 * b + 1, c = 2 * b;
+            const f32x4 y = mm16(lds_left16(&sA[16 * a][16 * c], LY::AP, lr, lg),
+                                 lds_right16(&sT[16 * c][16 * c], LY::AP, lr, lg), f32x4{0.f, 0.f, 0.f, 0.f});
+            const f32x4 x = mm16(lds_left16(&sT[16 * a][16 * a], LY::AP, lr, lg), y, f32x4{0.f, 0.f, 0.f, 0.f});
+            lds_store16(&sT[16 * a][16 * c], LY::AP, -x, lr, lg);
+        }
+        // KE^T and V^T (time-major fp16 rows per channel) for the W and Ub products
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int hf = 0; hf < 2; ++hf) {
+                const int ch = tile_chan(2 * s + hf, lr);
+                const f32x4 tk = mfma_h(ke16[s], hf ? id1 : id0, f32x4{0.f, 0.f, 0.f, 0.f});
+                const f32x4 tv = mfma_h(v16[s], hf ? id1 : id0, f32x4{0.f, 0.f, 0.f, 0.f});
+                *(half4_t *)(sKET + ch * LY::TP + 16 * b + 4 * lg) =
+                    half4_t{(_Float16)tk[0], (_Float16)tk[1], (_Float16)tk[2], (_Float16)tk[3]};
+                *(half4_t *)(sVT + ch * LY::TP + 16 * b + 4 * lg) =
+                    half4_t{(_Float16)tv[0], (_Float16)tv[1], (_Float16)tv[2], (_Float16)tv[3]};
+            }
+        lds_barrier();                                                     // B4
+
+        // ---- level 2: X_20, X_21, X_30, X_31 (one per wave) ---------------------------
+        {
+            const int rr = 2 + (b >> 1), c = b & 1;
+            const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 x1c = lds_right16(&sT[16][16 * c], LY::AP, lr, lg);    // X_1c
+            f32x4 x00 = zero;
+            if (c == 0) x00 = lds_right16(&sT[0][0], LY::AP, lr, lg);
+            f32x4 y2 = mm16(lds_left16(&sA[32][16], LY::AP, lr, lg), x1c, zero);            // A_21 X_1c
+            if (c == 0) y2 = mm16(lds_left16(&sA[32][0], LY::AP, lr, lg), x00, y2);         // + A_20 X_00
+            f32x4 x;
+            if (rr == 2) {
+                x = mm16(lds_left16(&sT[32][32], LY::AP, lr, lg), y2, zero);                // X_22 Y_2c
+            } else {
+                f32x4 y3 = mm16(lds_left16(&sA[48][16], LY::AP, lr, lg), x1c, zero);        // A_31 X_1c
+                if (c == 0) y3 = mm16(lds_left16(&sA[48][0], LY::AP, lr, lg), x00, y3);     // + A_30 X_00
+                x = mm16(lds_left16(&sT[48][32], LY::AP, lr, lg), y2, zero);                // X_32 Y_2c
+                x = mm16(lds_left16(&sT[48][48], LY::AP, lr, lg), y3, x);                   // + X_33 Y_3c
+            }
+            lds_store16(&sT[16 * rr][16 * c], LY::AP, -x, lr, lg);
+        }
+        lds_barrier();                                                     // B5: T complete
+
+        // ---- W^T = KE^T T^T and Ub = T V for this wave's rows ---------------------------
+        {
+            const int ns = (b < 2) ? 1 : 2;            // k-steps over t that T's rows reach
+            half8 tf[CS];
+#pragma unroll
+            for (int sp = 0; sp < CS; ++sp) {
+                float bt[8];
+                if (sp < ns) load_T_row(&sT[16 * b + lr][32 * sp + 8 * lg], &sBeta[32 * sp + 8 * lg], bt);
+                else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) bt[e] = 0.f;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) tf[sp][e] = (_Float16)bt[e];
+            }
+            f32x4 aw[8];
+#pragma unroll
+            for (int cb = 0; cb < 8; ++cb) {
+                aw[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int sp = 0; sp < CS; ++sp)
+                    if (sp < ns)
+                        aw[cb] = mfma_h(*(const half8 *)(sKET + tile_chan(cb, lr) * LY::TP + 32 * sp + 8 * lg), tf[sp], aw[cb]);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s)                 // W stored negated: U = Ub + (-W) S^T
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    pw[s][i] = (_Float16)(-aw[2 * s][i]);
+                    pw[s][i + 4] = (_Float16)(-aw[2 * s + 1][i]);
+                }
+#pragma unroll
+            for (int vb = 0; vb < 8; ++vb) {
+                f32x4 au = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int sp = 0; sp < CS; ++sp)
+                    if (sp < ns)
+                        au = mfma_h(tf[sp], *(const half8 *)(sVT + (16 * vb + lr) * LY::TP + 32 * sp + 8 * lg), au);
+                pu[vb] = half4_t{(_Float16)au[0], (_Float16)au[1], (_Float16)au[2], (_Float16)au[3]};
+            }
+            prec = rec;
+        }
+    }
+    if (prec) {
+        const int lane = threadIdx.x & 63, b = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            *(half8 *)(prec + R::W_OFF + ((size_t)(b * 4 + s) * 64 + lane) * 16) = pw[s];
+#pragma unroll
+        for (int vb = 0; vb < 8; ++vb)
+            *(half4_t *)(prec + R::UB_OFF + ((size_t)(vb * NB + b) * 64 + lane) * 8) = pu[vb];
     }
 }
 
@@ -1142,15 +1644,20 @@ static hipError_t launch_prefill_t(const PrefillArgs &a) {
     constexpr bool PRECISE = std::is_same<Tin, float>::value;
     const int64_t slots = num_slots(a.T, a.N, C);
     if ((a.stages & 1) && slots > 0) {
-        // persistent workgroups: one per CU (the LDS footprint allows one), each
-        // walking tiles blockIdx.x, blockIdx.x + gridDim.x, ...
+        // persistent workgroups walking tiles blockIdx.x, blockIdx.x + gridDim.x, ...
         int dev = 0, cus = 0;
         hipError_t e = hipGetDevice(&dev);
         if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
         if (e != hipSuccess) return e;
         const int64_t ntiles = slots * a.H;
-        const int64_t grid = ntiles < (int64_t)cus ? ntiles : (int64_t)cus;
-        intra_kernel<C, Tin, PRECISE><<<(unsigned)grid, 64 * kIntraWaves, 0, a.stream>>>(a, ntiles);
+        if constexpr (C == 64 && !PRECISE) {
+            // register-blocked kernel: two workgroups per CU
+            const int64_t grid = ntiles < 2 * (int64_t)cus ? ntiles : 2 * (int64_t)cus;
+            intra64_kernel<Tin><<<(unsigned)grid, 256, 0, a.stream>>>(a, ntiles);
+        } else {
+            const int64_t grid = ntiles < (int64_t)cus ? ntiles : (int64_t)cus;
+            intra_kernel<C, Tin, PRECISE><<<(unsigned)grid, 64 * kIntraWaves, 0, a.stream>>>(a, ntiles);
+        }
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -201,6 +201,11 @@ def _kperm(g, e):
     return 4 * g + e if e < 4 else 16 + 4 * g + (e - 4)
 
 
+def _tile_chan(kb, r):
+    """Key channel of row r of a kg^T tile kb (record layout)."""
+    return 32 * (kb // 2) + 8 * (r // 4) + 4 * (kb % 2) + r % 4
+
+
 def unpack_record(raw: np.ndarray, C: int, precise: bool):
     """Decode one workspace record (layout documented in csrc/kda_internal.h)."""
     NB, CP = C // 16, max(C, 32)
@@ -228,17 +233,18 @@ def unpack_record(raw: np.ndarray, C: int, precise: bool):
     for lane in range(64):
         r, g = lane % 16, lane // 16
         for e in range(8):
-            kk = _kperm(g, e)
+            kk = _kperm(g, e)                # k over t
+            kc = 8 * g + e                   # k over key channels
             for tb in range(NB):
                 for s in range(4):
-                    W[16 * tb + r, 32 * s + kk] = -Wf[tb * 4 + s, lane, e]   # stored negated
-                    QG[16 * tb + r, 32 * s + kk] = Qf[tb * 4 + s, lane, e]
+                    W[16 * tb + r, 32 * s + kc] = -Wf[tb * 4 + s, lane, e]   # stored negated
+                    QG[16 * tb + r, 32 * s + kc] = Qf[tb * 4 + s, lane, e]
                 for s in range(CS):
                     if 2 * s <= tb:          # fragments above the diagonal are not stored
                         M[16 * tb + r, 32 * s + kk] = Mf[tb * CS + s, lane, e]
             for kb in range(8):
                 for s in range(CS):
-                    KG[32 * s + kk, 16 * kb + r] = Kf[kb * CS + s, lane, e]
+                    KG[32 * s + kk, _tile_chan(kb, r)] = Kf[kb * CS + s, lane, e]
         for vb in range(8):
             for tb in range(NB):
                 for i in range(4):
