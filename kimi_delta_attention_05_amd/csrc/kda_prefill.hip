@@ -1164,7 +1164,8 @@ struct IntraRB {
     static constexpr size_t SLE = SL0 + 4 * 128 * 4;           // float [4][128]: Lam at each block's row 15
     static constexpr size_t SBETA = SLE + 4 * 128 * 4;         // float [64]
     static constexpr size_t SVMAX = SBETA + 64 * 4;            // float [4]
-    static constexpr size_t U = SVMAX + 64;                    // union of two uses:
+    static constexpr size_t SGB = SVMAX + 64;                  // float [4 waves][128]: gate offsets
+    static constexpr size_t U = SGB + 4 * 128 * 4;             // union of two uses:
     static constexpr size_t FV = U;                            //  per-wave factor vectors [4][NFV][128]
     static constexpr size_t RP = FV + (size_t)4 * NFV * 128 * 4;   //  R' fragments half8 [3][4][64]
     static constexpr size_t SX = RP + (size_t)3 * 4 * 64 * 16;     //  inverse scratch [4][16][20]
@@ -1244,15 +1245,12 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
         const bool rv = r < L;
         const size_t row = (size_t)(t0 + (rv ? r : L - 1)) * H + h;
         const float *gr = p.g + row * kHeadDim;
-        const float *dtr = p.dt_bias + (size_t)h * kHeadDim;
-        f32x4 graw[4][2], draw[4][2];
+        f32x4 graw[4][2];
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf) {
-                graw[s][hf] = *(const f32x4 *)(gr + chan(s, hf));
-                draw[s][hf] = *(const f32x4 *)(dtr + chan(s, hf));
-            }
+            for (int hf = 0; hf < 2; ++hf) graw[s][hf] = *(const f32x4 *)(gr + chan(s, hf));
+        const float2 dt2 = *(const float2 *)(p.dt_bias + (size_t)h * kHeadDim + 2 * lane);
         const Tin *qr = (const Tin *)p.q + row * kHeadDim;
         const Tin *kr = (const Tin *)p.k + row * kHeadDim;
         const Tin *vr = (const Tin *)p.v + row * kHeadDim;
@@ -1266,31 +1264,27 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
         const float braw = p.beta_raw[row];
         const float alog = *(const __attribute__((address_space(4))) float *)(p.A_log + h);
 
-        // the previous tile's W / Ub, now behind this tile's loads in the memory queue
-        if (prec) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                *(half8 *)(prec + R::W_OFF + ((size_t)(b * 4 + s) * 64 + lane) * 16) = pw[s];
-#pragma unroll
-            for (int vb = 0; vb < 8; ++vb)
-                *(half4_t *)(prec + R::UB_OFF + ((size_t)(vb * NB + b) * 64 + lane) * 8) = pu[vb];
-            prec = nullptr;
-        }
 
         // ---- gates and block-local cumulative log-decay ------------------------------
         // sigmoid(a (g + db)) = 1 / (1 + 2^(ga g + ga db)), ga = -a log2e; lambda in
         // log2 units = lb2 * sigmoid; rows past the chunk end get lambda = 0
         const float ga = -fast_exp2(alog * kLog2e) * kLog2e;
+        // ga * dt_bias per channel, spread to this lane's channels through this
+        // wave's own LDS row (its LDS accesses complete in order)
+        float *sgb = (float *)(smem + LY::SGB) + b * 128;
+        *(float2 *)(sgb + 2 * lane) = float2{ga * dt2.x, ga * dt2.y};
         float lam[4][8];
 #pragma unroll
         for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
+            for (int hf = 0; hf < 2; ++hf) {
+                const f32x4 gb = *(const f32x4 *)(sgb + chan(s, hf));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const float sg = fast_rcp(1.0f + fast_exp2(fmaf(graw[s][hf][i], ga, ga * draw[s][hf][i])));
+                    const float sg = fast_rcp(1.0f + fast_exp2(fmaf(graw[s][hf][i], ga, gb[i])));
                     lam[s][4 * hf + i] = rv ? lb2 * sg : 0.0f;
                 }
+            }
         if (lr == 0) {                               // lambda of the block's first row
 #pragma unroll
             for (int s = 0; s < 4; ++s)
@@ -1340,6 +1334,16 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
         vmax = wave_max_nonneg(vmax);
         if (lane == 0) sVmax[b] = vmax;
         lds_barrier();                                                     // B1
+        // the previous tile's W / Ub, now behind this tile's loads in the memory queue
+        if (prec) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                *(half8 *)(prec + R::W_OFF + ((size_t)(b * 4 + s) * 64 + lane) * 16) = pw[s];
+#pragma unroll
+            for (int vb = 0; vb < 8; ++vb)
+                *(half4_t *)(prec + R::UB_OFF + ((size_t)(vb * NB + b) * 64 + lane) * 8) = pu[vb];
+            prec = nullptr;
+        }
 
         // ---- per-channel factors (lane: channels 2 lane, 2 lane + 1) ------------------
         //   QF_b = e^{G_16b}                      (chunk-relative, row 16b included)
