@@ -1169,7 +1169,8 @@ struct IntraRB {
     static constexpr size_t FV = U;                            //  per-wave factor vectors [4][NFV][128]
     static constexpr size_t RP = FV + (size_t)4 * NFV * 128 * 4;   //  R' fragments half8 [3][4][64]
     static constexpr size_t SX = RP + (size_t)3 * 4 * 64 * 16;     //  inverse scratch [4][16][20]
-    static constexpr size_t U1_END = SX + (size_t)4 * 16 * 20 * 4;
+    static constexpr size_t KQ = SX + (size_t)4 * 16 * 20 * 4;     //  KP, QP fragments of block 3, half8 [2][4][64]
+    static constexpr size_t U1_END = KQ + (size_t)2 * 4 * 64 * 16;
     static constexpr size_t KET = U;                           //  KE^T fp16 [128][TP] (after the inverse)
     static constexpr size_t VT = KET + (size_t)128 * TP * 2;   //  V^T  fp16 [128][TP]
     static constexpr size_t U2_END = VT + (size_t)128 * TP * 2;
@@ -1194,6 +1195,7 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
     float *sBeta = (float *)(smem + LY::SBETA);
     float *sVmax = (float *)(smem + LY::SVMAX);
     half8 *sRP = (half8 *)(smem + LY::RP);
+    half8 *sKQ = (half8 *)(smem + LY::KQ);
     _Float16 *sKET = (_Float16 *)(smem + LY::KET);
     _Float16 *sVT = (_Float16 *)(smem + LY::VT);
 
@@ -1211,6 +1213,16 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
     half8 pw[4];
     half4_t pu[8];
     unsigned char *prec = nullptr;
+    auto flush = [&](int b, int lane) {
+        if (!prec) return;
+#pragma unroll
+        for (int s = 0; s < 4; ++s)
+            *(half8 *)(prec + R::W_OFF + ((size_t)(b * 4 + s) * 64 + lane) * 16) = pw[s];
+#pragma unroll
+        for (int vb = 0; vb < 8; ++vb)
+            *(half4_t *)(prec + R::UB_OFF + ((size_t)(vb * NB + b) * 64 + lane) * 8) = pu[vb];
+        prec = nullptr;
+    };
 
     for (int64_t ti = blockIdx.x; ti < ntiles; ti += gridDim.x) {
         // lane and wave indices are re-derived every tile (opaque to the
@@ -1335,15 +1347,7 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
         if (lane == 0) sVmax[b] = vmax;
         lds_barrier();                                                     // B1
         // the previous tile's W / Ub, now behind this tile's loads in the memory queue
-        if (prec) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-                *(half8 *)(prec + R::W_OFF + ((size_t)(b * 4 + s) * 64 + lane) * 16) = pw[s];
-#pragma unroll
-            for (int vb = 0; vb < 8; ++vb)
-                *(half4_t *)(prec + R::UB_OFF + ((size_t)(vb * NB + b) * 64 + lane) * 8) = pu[vb];
-            prec = nullptr;
-        }
+        flush(b, lane);
 
         // ---- per-channel factors (lane: channels 2 lane, 2 lane + 1) ------------------
         //   QF_b = e^{G_16b}                      (chunk-relative, row 16b included)
@@ -1461,6 +1465,13 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
                 ke16[s][e] = (_Float16)(KP[s][e] * qf[e]);   // kh e^{G_t}
             }
             if (b < NB - 1) sRP[(b * 4 + s) * 64 + lane] = rp;
+            if (b == NB - 1) {          // left operands of the blocks (3, 0), (3, 1), computed by waves 0, 1
+                half8 kq, qq;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) { kq[e] = (_Float16)KP[s][e]; qq[e] = (_Float16)QP[s][e]; }
+                sKQ[s * 64 + lane] = kq;
+                sKQ[(4 + s) * 64 + lane] = qq;
+            }
             *(half8 *)(rec + R::QG_OFF + ((size_t)(b * 4 + s) * 64 + lane) * 16) = qg;
             // kg^T fragments (tile 2s + half, k-step b / 2): this block's rows are
             // positions 4 (b & 1) .. + 3 of each lane's 8
@@ -1499,7 +1510,10 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
             else
                 *(half4_t *)(mf + 8) = half4_t{(_Float16)xm[0], (_Float16)xm[1], (_Float16)xm[2], (_Float16)xm[3]};
         }
-        for (int c = 0; c < b; ++c) {                   // off-diagonal blocks (b, c), c < b: fp16
+        // off-diagonal blocks (b, c), c < b, on fp16 MFMA: by the row owner b, except
+        // (3, 0) and (3, 1), which the column owners 0 and 1 take (two blocks per
+        // wave at most instead of three)
+        for (int c = (b == NB - 1 ? 2 : 0); c < b; ++c) {
             f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aM = {0.f, 0.f, 0.f, 0.f};
             const float *xf = fv + (3 + c) * 128;
 #pragma unroll
@@ -1519,6 +1533,28 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
             }
             *(f32x4 *)&sA[16 * b + lr][16 * c + 4 * lg] = aA * beta;
             *(half4_t *)(rec + R::M_OFF + ((size_t)(b * CS + (c >> 1)) * 64 + lane) * 16 + 8 * (c & 1)) =
+                half4_t{(_Float16)aM[0], (_Float16)aM[1], (_Float16)aM[2], (_Float16)aM[3]};
+        }
+        if (b < 2) {                                    // block (3, b) by its column owner
+            constexpr int a = NB - 1;
+            f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aM = {0.f, 0.f, 0.f, 0.f};
+            const float *xf = (const float *)(smem + LY::FV) + (size_t)a * LY::NFV * 128 + (3 + b) * 128;
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const f32x4 x0 = *(const f32x4 *)(xf + chan(s, 0)), x1 = *(const f32x4 *)(xf + chan(s, 1));
+                const f32x4 p0 = *(const f32x4 *)(fv + 2 * 128 + chan(s, 0)), p1 = *(const f32x4 *)(fv + 2 * 128 + chan(s, 1));
+                half8 rr;                                   // kh_j e^{G_48 - G_j}
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    rr[i] = (_Float16)(RI[s][i] * (p0[i] * x0[i]));
+                    rr[i + 4] = (_Float16)(RI[s][i + 4] * (p1[i] * x1[i]));
+                }
+                aA = mfma_h(rr, sKQ[s * 64 + lane], aA);
+                aM = mfma_h(rr, sKQ[(4 + s) * 64 + lane], aM);
+            }
+            // lane holds A[i][j] / M[i][j] for i = 48 + lr, j = 16b + 4lg + ii
+            *(f32x4 *)&sA[16 * a + lr][16 * b + 4 * lg] = aA * sBeta[16 * a + lr];
+            *(half4_t *)(rec + R::M_OFF + ((size_t)(a * CS + (b >> 1)) * 64 + lane) * 16 + 8 * (b & 1)) =
                 half4_t{(_Float16)aM[0], (_Float16)aM[1], (_Float16)aM[2], (_Float16)aM[3]};
         }
         // diagonal block of (I + A)^-1 = (I - A)(I + A^2)(I + A^4)(I + A^8) (A^16 = 0);
@@ -1590,17 +1626,22 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
         // ---- W^T = KE^T T^T and Ub = T V for this wave's rows ---------------------------
         {
             const int ns = (b < 2) ? 1 : 2;            // k-steps over t that T's rows reach
+            auto t_frag = [&](int tb, int sp) {         // T row fragment, rows of block tb
+                float bt[8];
+                load_T_row(&sT[16 * tb + lr][32 * sp + 8 * lg], &sBeta[32 * sp + 8 * lg], bt);
+                half8 f;
+#pragma unroll
+                for (int e = 0; e < 8; ++e) f[e] = (_Float16)bt[e];
+                return f;
+            };
             half8 tf[CS];
 #pragma unroll
             for (int sp = 0; sp < CS; ++sp) {
-                float bt[8];
-                if (sp < ns) load_T_row(&sT[16 * b + lr][32 * sp + 8 * lg], &sBeta[32 * sp + 8 * lg], bt);
+                if (sp < ns) tf[sp] = t_frag(b, sp);
                 else {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) bt[e] = 0.f;
+                    for (int e = 0; e < 8; ++e) tf[sp][e] = (_Float16)0.0f;
                 }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) tf[sp][e] = (_Float16)bt[e];
             }
             f32x4 aw[8];
 #pragma unroll
@@ -1630,15 +1671,7 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
             prec = rec;
         }
     }
-    if (prec) {
-        const int lane = threadIdx.x & 63, b = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-            *(half8 *)(prec + R::W_OFF + ((size_t)(b * 4 + s) * 64 + lane) * 16) = pw[s];
-#pragma unroll
-        for (int vb = 0; vb < 8; ++vb)
-            *(half4_t *)(prec + R::UB_OFF + ((size_t)(vb * NB + b) * 64 + lane) * 8) = pu[vb];
-    }
+    flush(__builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6), threadIdx.x & 63);
 }
 
 // ---- launchers ----------------------------------------------------------------
