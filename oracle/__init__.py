@@ -4,11 +4,13 @@ Only the tests, the smoke check and the benchmark's CPU-baseline leg may
 import this package. It never imports the HIP package and shares no code with
 it; both sides take their inputs from the seeded generators in kda_inputs.py.
 
-Two independent formulations live here:
+Formulations here:
   * `kda_recurrent` — the token-by-token recurrence (kda_oracle.c), the plain
     definition of what the method computes;
   * `kda_chunked`   — the chunkwise WY form (chunked.py), derived separately and
-    used to pin the recurrence and to check the GPU's intra-chunk stage.
+    used to pin the recurrence and to check the GPU's intra-chunk stage;
+  * `output_norm_gate` — the output epilogue (epilogue.py): per-head RMS norm
+    and sigmoid output gate applied to the recurrence's outputs.
 """
 from __future__ import annotations
 
@@ -162,6 +164,7 @@ def kda_decode_steps(steps, state, A_log, dt_bias, *, scale: float,
 
 
 from .chunked import kda_chunked  # noqa: E402  (pure numpy, no library)
+from .epilogue import output_norm_gate  # noqa: E402  (pure numpy, no library)
 
 __all__ = ["build", "kda_recurrent", "kda_decode_steps", "kda_chunked",
-           "max_threads", "LOWER_BOUND", "L2_EPS"]
+           "output_norm_gate", "max_threads", "LOWER_BOUND", "L2_EPS"]
