@@ -205,9 +205,57 @@ def main():
         "cpu_baseline": None,
     }
 
+    line["epilogue"] = epilogue_timing(kda, o, dsteps, dA, ddt, dstate, dd.scale, dout)
+
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(p, dd)
     print(json.dumps(line), flush=True)
+
+
+def epilogue_timing(kda, o, dsteps, dA, ddt, dstate, dscale, dout, reps=20):
+    """The output epilogue (per-head RMS norm + sigmoid gate), measured beside the
+    step and not part of it: the standalone kernel over the prefill output
+    (T*H rows of 128 bf16, y written in place of a copy of o) and the decode step
+    with the epilogue fused, against the plain decode step."""
+    import torch
+    import kda_inputs
+    T, H, Dv = o.shape
+    z, w = kda_inputs.make_epilogue((T, H, Dv), seed=2001)
+    z, w = z.to(o.device), w.to(o.device)
+    y = torch.empty_like(o)
+    B, HD = dout.shape[0], dout.shape[1]
+    zd, wd = kda_inputs.make_epilogue((B, HD, Dv), seed=2002)
+    zd, wd = zd.to(o.device), wd.to(o.device)
+
+    def timed(fn):
+        for _ in range(3):
+            fn(0)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for i in range(reps):
+            ev[2 * i].record()
+            fn(i)
+            ev[2 * i + 1].record()
+        torch.cuda.synchronize()
+        return sum(ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(reps)) / reps
+
+    ms_ng = timed(lambda i: kda.output_norm_gate(o, z, w, out=y))
+    rows = T * H
+    ng_bytes = rows * 3 * Dv * 2 + Dv * 4                 # o, z read, y written (bf16)
+
+    def dec(i, gated):
+        st = dsteps[i % len(dsteps)]
+        kw = dict(gate=zd, norm_weight=wd) if gated else {}
+        kda.decode_step(st["q"], st["k"], st["v"], st["g"], st["beta_raw"], dA, ddt, dstate,
+                        scale=dscale, out=dout, **kw)
+
+    ms_plain = timed(lambda i: dec(i, False))
+    ms_gated = timed(lambda i: dec(i, True))
+    gb = ng_bytes / (ms_ng * 1e-3) / 1e9
+    return {"norm_gate_kernel": {"rows": rows, "us": round(ms_ng * 1e3, 2), "alg_bytes": ng_bytes,
+                                 "achieved_GBs": round(gb, 1), "frac": round(gb / HBM_PEAK_GBS, 4)},
+            "decode_step_gated_us": round(ms_gated * 1e3, 2),
+            "decode_step_plain_us": round(ms_plain * 1e3, 2)}
 
 
 def copy_calibration(nbytes=1 << 30, reps=3):

@@ -172,6 +172,46 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
                              kda_dtype_t in_dtype, void *stream);
 
 /*
+ * kda_decode_step with the output epilogue of kda_output_norm_gate fused into
+ * its output store (each (request, head) row of 128 outputs is normalised,
+ * weighted and gated before it is written; the same arithmetic as running
+ * kda_output_norm_gate on o afterwards, without the extra pass over o).
+ *
+ * z           : [B, H, 128] gate logits in in_dtype, 16-byte aligned, not NULL
+ * norm_weight : [128] fp32, 16-byte aligned;  norm_eps : finite and > 0
+ * Every other argument as for kda_decode_step.
+ */
+kda_status_t kda_decode_step_gated(const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta_raw,
+                                   const float *A_log, const float *dt_bias,
+                                   float scale, float lower_bound,
+                                   float *state, void *o, kda_dtype_t o_dtype,
+                                   int32_t B, int32_t H, int32_t K, int32_t V,
+                                   kda_dtype_t in_dtype,
+                                   const void *z, const float *norm_weight, float norm_eps,
+                                   void *stream);
+/*
+ * Output epilogue of the attention block (kimi_k3 FusedKDAChunkwise page,
+ * "Output handling": the per-head output norm, then the sigmoid output gate
+ * whose logits are a projection of the hidden states; that projection and the
+ * output projection after it need model weights and are not part of libkda).
+ * For each row r of D = 128 features:
+ *
+ *   y[r, c] = o[r, c] / sqrt(mean_c' o[r, c']^2 + eps) * weight[c] * sigmoid(z[r, c])
+ *
+ * computed in fp32 and rounded to nearest even when bf16. For a prefill output
+ * rows = total_tokens * H ([T, H, 128] viewed as [T * H, 128]).
+ *
+ * o, z, y : [rows, 128] in io_dtype (KDA_BF16 or KDA_F32), 16-byte aligned;
+ *           y may alias o
+ * weight  : [128] fp32 (one weight vector shared by all heads), 16-byte aligned
+ * eps     : finite and > 0 (the page gives no value)
+ * rows    : >= 0 (0 enqueues nothing and accepts NULL pointers);  D : must be 128
+ */
+kda_status_t kda_output_norm_gate(const void *o, const void *z, const float *weight, float eps,
+                                  int64_t rows, int32_t D, kda_dtype_t io_dtype, void *y,
+                                  void *stream);
+/*
  * Opt-in check of packed offsets (FlashInfer kda_backward page: offsets are
  * validated by one eager synchronisation, the launch path then trusts them).
  * Copies cu_seqlens to the host on `stream`, synchronises that stream and

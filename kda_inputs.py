@@ -16,6 +16,8 @@ stated for the five standard configurations:
   large      : B=1, T=8192, H=96, bf16, g ~ N(0, 2^2), chunk 64, h0 ~ N(0, 0.1^2)
   large_varlen: packed lengths [1300, 547, 2048, 963, 271, 3063], H=96, as large
   decode     : 256 requests, H=32, 64 consecutive T=1 steps, state ~ N(0, 0.1^2)
+  epilogue   : output-gate logits ~ N(0, 2^2) in the token dtype and an output-norm
+               weight ~ U(0.5, 1.5) (stand-ins for the model's projection and weight)
 
 "N(0, s)" in the configuration text is read as standard deviation s.
 All values are drawn in fp32 from a CPU `torch.Generator` seeded with the
@@ -168,3 +170,13 @@ def large_varlen():
 def decode(n_steps=64):
     return make_decode(256, 32, n_steps, seed=1004,
                        name="decode B=256 H=32 T=1")
+
+
+def make_epilogue(shape, *, token_dtype=torch.bfloat16, z_std=2.0, seed=0, D=V_DIM):
+    """Synthetic inputs of the output epilogue: gate logits z (shape `shape`, last
+    axis D, in the token dtype, ~ N(0, z_std)) and the norm weight [D] fp32 ~ U(0.5, 1.5).
+    The gate projection and the trained norm weight need model weights; these stand in."""
+    gen = torch.Generator().manual_seed(int(seed))
+    z = _randn(gen, tuple(shape), z_std).to(token_dtype)
+    w = _uniform(gen, (D,), 0.5, 1.5)
+    return z, w

@@ -1,11 +1,13 @@
 """Kimi Delta Attention forward for AMD MI355X: Python binding of libkda.
 
-`chunk_fwd` (chunkwise prefill over packed sequences) and `decode_step`
-(batched T=1 step) call the HIP kernels in libkda.so through its C ABI
-(include/kda.h). Importing the package fails if the library is not built.
+`chunk_fwd` (chunkwise prefill over packed sequences), `decode_step` (batched
+T=1 step, optionally with the output epilogue fused) and `output_norm_gate`
+(the output epilogue: per-head RMS norm and sigmoid gate) call the HIP kernels
+in libkda.so through its C ABI (include/kda.h). Importing the package fails if
+the library is not built.
 """
-from .kda import (KDAError, Workspace, check_cu_seqlens, chunk_fwd, decode_step, version,
-                  workspace_size, LIB_PATH)
+from .kda import (KDAError, Workspace, check_cu_seqlens, chunk_fwd, decode_step,
+                  output_norm_gate, version, workspace_size, LIB_PATH, NORM_EPS)
 
-__all__ = ["KDAError", "Workspace", "check_cu_seqlens", "chunk_fwd", "decode_step", "version",
-           "workspace_size", "LIB_PATH"]
+__all__ = ["KDAError", "Workspace", "check_cu_seqlens", "chunk_fwd", "decode_step",
+           "output_norm_gate", "version", "workspace_size", "LIB_PATH", "NORM_EPS"]

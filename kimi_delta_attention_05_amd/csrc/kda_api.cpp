@@ -59,11 +59,53 @@ kda_status_t hip_fail(hipError_t e, const char *where) {
     return fail(KDA_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
 }
 
+// The decode step with an optional fused output epilogue (z == NULL: none).
+kda_status_t decode_step_impl(const void *q, const void *k, const void *v,
+                              const float *g, const float *beta_raw,
+                              const float *A_log, const float *dt_bias,
+                              float scale, float lower_bound,
+                              float *state, void *o, kda_dtype_t o_dtype,
+                              int32_t B, int32_t H, int32_t K, int32_t V,
+                              kda_dtype_t in_dtype, void *stream,
+                              const void *z, const float *norm_weight, float norm_eps,
+                              const char *name) {
+    if (B < 1) return fail(KDA_ERR_INVALID_ARG, "B must be >= 1");
+    kda_status_t st = check_common(H, K, V, scale, lower_bound, in_dtype, o_dtype);
+    if (st != KDA_OK) return st;
+    if (!q || !k || !v || !g || !beta_raw || !A_log || !dt_bias || !state || !o)
+        return fail(KDA_ERR_INVALID_ARG, "a required pointer is NULL");
+    if ((int64_t)B * H > ((int64_t)1 << 31) - 1)
+        return fail(KDA_ERR_INVALID_ARG, "B * H too large");
+    st = check_aligned16({{q, "q"}, {k, "k"}, {v, "v"}, {g, "g"}, {dt_bias, "dt_bias"},
+                          {state, "state"}, {o, "o"}});
+    if (st != KDA_OK) return st;
+    if (((uintptr_t)beta_raw & 3) != 0 || ((uintptr_t)A_log & 3) != 0)
+        return fail(KDA_ERR_INVALID_ARG, "beta_raw and A_log must be 4-byte aligned");
+
+    if (z) {
+        if (!norm_weight) return fail(KDA_ERR_INVALID_ARG, "norm_weight is NULL");
+        if (!(norm_eps > 0.0f) || !std::isfinite(norm_eps))
+            return fail(KDA_ERR_INVALID_ARG, "norm_eps must be finite and > 0");
+        st = check_aligned16({{z, "z"}, {norm_weight, "norm_weight"}});
+        if (st != KDA_OK) return st;
+    }
+
+    kda::DecodeArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta_raw = beta_raw; a.A_log = A_log; a.dt_bias = dt_bias;
+    a.scale = scale; a.lower_bound = lower_bound; a.state = state; a.o = o;
+    a.B = B; a.H = H; a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = o_dtype == KDA_BF16;
+    a.stream = (hipStream_t)stream;
+    a.z = z; a.norm_w = norm_weight; a.norm_eps = norm_eps;
+    hipError_t e = kda::launch_decode(a);
+    if (e != hipSuccess) return hip_fail(e, name);
+    return ok();
+}
+
 }  // namespace
 
 extern "C" {
 
-int kda_version(void) { return 100; }
+int kda_version(void) { return 101; }
 
 const char *kda_status_string(kda_status_t s) {
     switch (s) {
@@ -183,6 +225,7 @@ kda_status_t kda_chunk_fwd_inter(KDA_CHUNK_PARAMS) {
     return chunk_fwd_stages(2, "kda_chunk_fwd_inter", KDA_CHUNK_ARGS);
 }
 
+
 kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
                              const float *g, const float *beta_raw,
                              const float *A_log, const float *dt_bias,
@@ -190,26 +233,43 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
                              float *state, void *o, kda_dtype_t o_dtype,
                              int32_t B, int32_t H, int32_t K, int32_t V,
                              kda_dtype_t in_dtype, void *stream) {
-    if (B < 1) return fail(KDA_ERR_INVALID_ARG, "B must be >= 1");
-    kda_status_t st = check_common(H, K, V, scale, lower_bound, in_dtype, o_dtype);
-    if (st != KDA_OK) return st;
-    if (!q || !k || !v || !g || !beta_raw || !A_log || !dt_bias || !state || !o)
-        return fail(KDA_ERR_INVALID_ARG, "a required pointer is NULL");
-    if ((int64_t)B * H > ((int64_t)1 << 31) - 1)
-        return fail(KDA_ERR_INVALID_ARG, "B * H too large");
-    st = check_aligned16({{q, "q"}, {k, "k"}, {v, "v"}, {g, "g"}, {dt_bias, "dt_bias"},
-                          {state, "state"}, {o, "o"}});
-    if (st != KDA_OK) return st;
-    if (((uintptr_t)beta_raw & 3) != 0 || ((uintptr_t)A_log & 3) != 0)
-        return fail(KDA_ERR_INVALID_ARG, "beta_raw and A_log must be 4-byte aligned");
+    return decode_step_impl(q, k, v, g, beta_raw, A_log, dt_bias, scale, lower_bound, state, o,
+                            o_dtype, B, H, K, V, in_dtype, stream, nullptr, nullptr, 0.f,
+                            "kda_decode_step launch");
+}
 
-    kda::DecodeArgs a;
-    a.q = q; a.k = k; a.v = v; a.g = g; a.beta_raw = beta_raw; a.A_log = A_log; a.dt_bias = dt_bias;
-    a.scale = scale; a.lower_bound = lower_bound; a.state = state; a.o = o;
-    a.B = B; a.H = H; a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = o_dtype == KDA_BF16;
-    a.stream = (hipStream_t)stream;
-    hipError_t e = kda::launch_decode(a);
-    if (e != hipSuccess) return hip_fail(e, "kda_decode_step launch");
+kda_status_t kda_decode_step_gated(const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta_raw,
+                                   const float *A_log, const float *dt_bias,
+                                   float scale, float lower_bound,
+                                   float *state, void *o, kda_dtype_t o_dtype,
+                                   int32_t B, int32_t H, int32_t K, int32_t V,
+                                   kda_dtype_t in_dtype,
+                                   const void *z, const float *norm_weight, float norm_eps,
+                                   void *stream) {
+    if (!z) return fail(KDA_ERR_INVALID_ARG, "z is NULL");
+    return decode_step_impl(q, k, v, g, beta_raw, A_log, dt_bias, scale, lower_bound, state, o,
+                            o_dtype, B, H, K, V, in_dtype, stream, z, norm_weight, norm_eps,
+                            "kda_decode_step_gated launch");
+}
+
+kda_status_t kda_output_norm_gate(const void *o, const void *z, const float *weight, float eps,
+                                  int64_t rows, int32_t D, kda_dtype_t io_dtype, void *y,
+                                  void *stream) {
+    if (rows < 0) return fail(KDA_ERR_INVALID_ARG, "rows must be >= 0");
+    if (D != 128) return fail(KDA_ERR_UNSUPPORTED, "only D = 128 is supported (got " + std::to_string(D) + ")");
+    if (!valid_dtype(io_dtype)) return fail(KDA_ERR_UNSUPPORTED, "unknown dtype");
+    if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(KDA_ERR_INVALID_ARG, "eps must be finite and > 0");
+    if (rows == 0) return ok();                 // nothing to read or write (pointers may be NULL)
+    if (!o || !z || !weight || !y) return fail(KDA_ERR_INVALID_ARG, "a required pointer is NULL");
+    if ((rows + 15) / 16 > (int64_t)0x7fffffff) return fail(KDA_ERR_INVALID_ARG, "rows too large");
+    kda_status_t st = check_aligned16({{o, "o"}, {z, "z"}, {weight, "weight"}, {y, "y"}});
+    if (st != KDA_OK) return st;
+    kda::NormGateArgs a;
+    a.o = o; a.z = z; a.w = weight; a.eps = eps; a.rows = rows; a.bf16 = io_dtype == KDA_BF16;
+    a.y = y; a.stream = (hipStream_t)stream;
+    hipError_t e = kda::launch_norm_gate(a);
+    if (e != hipSuccess) return hip_fail(e, "kda_output_norm_gate launch");
     return ok();
 }
 

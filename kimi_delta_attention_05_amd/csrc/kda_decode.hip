@@ -24,13 +24,13 @@
 
 namespace kda {
 
-template <typename Tin, typename Tout>
+template <typename Tin, typename Tout, bool GATED>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta_raw,
     const float *__restrict__ A_log, const float *__restrict__ dt_bias,
     float scale, float lower_bound, float *__restrict__ state, Tout *__restrict__ o,
-    int H)
+    int H, const Tin *__restrict__ zg, const float *__restrict__ norm_w, float norm_eps)
 {
     const int bh = blockIdx.x;                 // request * H + head
     const int h = bh % H;
@@ -106,19 +106,35 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         if (j == 0) so[row] = a + u * kq;
     }
     lds_barrier();
-    if (threadIdx.x < kHeadDim / 2) {
+    if (threadIdx.x < kHeadDim / 2) {            // wave 0, two outputs per lane
         const int i = 2 * threadIdx.x;
-        o[tb + i] = from_f32<Tout>(so[i]);
-        o[tb + i + 1] = from_f32<Tout>(so[i + 1]);
+        float y0 = so[i], y1 = so[i + 1];
+        if constexpr (GATED) {
+            // output epilogue (kimi_k3 FusedKDAChunkwise page, "Output handling"):
+            // RMS norm over the head's 128 outputs, channel weight, sigmoid gate
+            const float ms = wave_sum(y0 * y0 + y1 * y1) * (1.0f / kHeadDim);
+            const float r = rsqrtf(ms + norm_eps);
+            y0 = y0 * r * norm_w[i] * sigmoid_f(to_f32(zg[tb + i]));
+            y1 = y1 * r * norm_w[i + 1] * sigmoid_f(to_f32(zg[tb + i + 1]));
+        }
+        o[tb + i] = from_f32<Tout>(y0);
+        o[tb + i + 1] = from_f32<Tout>(y1);
     }
 }
 
 template <typename Tin, typename Tout>
 static hipError_t launch_decode_t(const DecodeArgs &a) {
     dim3 grid((unsigned)(a.B * a.H));
-    decode_step_kernel<Tin, Tout><<<grid, 256, 0, a.stream>>>(
-        (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v, a.g, a.beta_raw,
-        a.A_log, a.dt_bias, a.scale, a.lower_bound, a.state, (Tout *)a.o, a.H);
+    if (a.z)
+        decode_step_kernel<Tin, Tout, true><<<grid, 256, 0, a.stream>>>(
+            (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v, a.g, a.beta_raw,
+            a.A_log, a.dt_bias, a.scale, a.lower_bound, a.state, (Tout *)a.o, a.H,
+            (const Tin *)a.z, a.norm_w, a.norm_eps);
+    else
+        decode_step_kernel<Tin, Tout, false><<<grid, 256, 0, a.stream>>>(
+            (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v, a.g, a.beta_raw,
+            a.A_log, a.dt_bias, a.scale, a.lower_bound, a.state, (Tout *)a.o, a.H,
+            nullptr, nullptr, 0.f);
     return hipGetLastError();
 }
 

@@ -1,0 +1,66 @@
+// Output epilogue of the attention block (kimi_k3 FusedKDAChunkwise page,
+// "Output handling"): each output row of 128 features is RMS-normalised,
+// scaled by a per-channel weight and multiplied by a sigmoid output gate,
+//   y = o / sqrt(mean(o^2) + eps) * weight * sigmoid(z).
+//
+// One 16-lane DPP row per output row, 8 features per lane (16-byte loads and
+// stores of bf16, 32 bytes of fp32), 16 rows per 256-thread workgroup: every
+// instruction moves whole consecutive rows. HBM-bound: o, z read once, y
+// written once.
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <typename T>
+__device__ __forceinline__ void store8(T *p, const float (&x)[8]);
+template <>
+__device__ __forceinline__ void store8<float>(float *p, const float (&x)[8]) {
+    ((f32x4 *)p)[0] = f32x4{x[0], x[1], x[2], x[3]};
+    ((f32x4 *)p)[1] = f32x4{x[4], x[5], x[6], x[7]};
+}
+template <>
+__device__ __forceinline__ void store8<__bf16>(__bf16 *p, const float (&x)[8]) {
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (__bf16)x[e];
+    *(bf16x8 *)p = v;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void norm_gate_kernel(const T *__restrict__ o, const T *__restrict__ z,
+                                                        const float *__restrict__ w, float eps,
+                                                        int64_t rows, T *y)
+{
+    const int j = threadIdx.x & 15;                    // features 8j .. 8j + 7
+    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const bool valid = row < rows;
+    const size_t base = (size_t)(valid ? row : rows - 1) * kHeadDim + 8 * j;   // rows >= 1
+    float x[8], g[8], wv[8];
+    load8(o + base, x);
+    load8(z + base, g);
+    load8(w + 8 * j, wv);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+    ss = row16_sum(ss);
+    const float r = rsqrtf(ss * (1.0f / kHeadDim) + eps);
+    float out[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = x[e] * r * wv[e] * sigmoid_f(g[e]);
+    if (valid) store8<T>(y + base, out);
+}
+
+hipError_t launch_norm_gate(const NormGateArgs &a) {
+    if (a.rows <= 0) return hipSuccess;
+    const int64_t blocks = (a.rows + 15) / 16;
+    if (a.bf16)
+        norm_gate_kernel<__bf16><<<(unsigned)blocks, 256, 0, a.stream>>>(
+            (const __bf16 *)a.o, (const __bf16 *)a.z, a.w, a.eps, a.rows, (__bf16 *)a.y);
+    else
+        norm_gate_kernel<float><<<(unsigned)blocks, 256, 0, a.stream>>>(
+            (const float *)a.o, (const float *)a.z, a.w, a.eps, a.rows, (float *)a.y);
+    return hipGetLastError();
+}
+
+}  // namespace kda

@@ -16,6 +16,22 @@ struct DecodeArgs {
     int B, H;
     bool in_bf16, out_bf16;
     hipStream_t stream;
+    // output epilogue fused into the store (z == nullptr: none): RMS norm with
+    // channel weight norm_w, then the sigmoid gate of logits z (input dtype)
+    const void *z = nullptr;
+    const float *norm_w = nullptr;
+    float norm_eps = 0.f;
+};
+
+// Output epilogue over rows of 128 features: y = o / sqrt(mean(o^2) + eps) * w * sigmoid(z).
+struct NormGateArgs {
+    const void *o, *z;
+    const float *w;
+    float eps;
+    int64_t rows;
+    bool bf16;
+    void *y;
+    hipStream_t stream;
 };
 
 struct PrefillArgs {
@@ -94,6 +110,7 @@ size_t record_bytes(int chunk, bool precise);
 __host__ __device__ inline int64_t num_slots(int64_t T, int N, int chunk) { return T / chunk + N; }
 
 hipError_t launch_decode(const DecodeArgs &a);
+hipError_t launch_norm_gate(const NormGateArgs &a);
 hipError_t launch_prefill(const PrefillArgs &a);
 
 }  // namespace kda

@@ -24,7 +24,10 @@ KDA_F32, KDA_BF16 = 0, 1
 # Every symbol include/kda.h declares.
 EXPORTS = ("kda_version", "kda_status_string", "kda_last_error",
            "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_intra",
-           "kda_chunk_fwd_inter", "kda_decode_step", "kda_check_cu_seqlens")
+           "kda_chunk_fwd_inter", "kda_decode_step", "kda_decode_step_gated",
+           "kda_output_norm_gate", "kda_check_cu_seqlens")
+
+NORM_EPS = 1e-5   # default epsilon of the output norm (the pages give none)
 
 if not os.path.exists(LIB_PATH):
     raise ImportError("libkda.so not found at %s: build it with "
@@ -52,6 +55,11 @@ _STAGE_FN = {None: _lib.kda_chunk_fwd, "intra": _lib.kda_chunk_fwd_intra,
 _lib.kda_decode_step.restype = ctypes.c_int
 _lib.kda_decode_step.argtypes = [_P, _P, _P, _P, _P, _P, _P, _f32, _f32, _P, _P, ctypes.c_int,
                                  _i32, _i32, _i32, _i32, ctypes.c_int, _P]
+_lib.kda_decode_step_gated.restype = ctypes.c_int
+_lib.kda_decode_step_gated.argtypes = [_P, _P, _P, _P, _P, _P, _P, _f32, _f32, _P, _P, ctypes.c_int,
+                                       _i32, _i32, _i32, _i32, ctypes.c_int, _P, _P, _f32, _P]
+_lib.kda_output_norm_gate.restype = ctypes.c_int
+_lib.kda_output_norm_gate.argtypes = [_P, _P, _P, _f32, _i64, _i32, ctypes.c_int, _P, _P]
 _lib.kda_check_cu_seqlens.restype = ctypes.c_int
 _lib.kda_check_cu_seqlens.argtypes = [_P, _i32, _i64, _P]
 
@@ -185,11 +193,15 @@ def chunk_fwd(q, k, v, g, beta_raw, A_log, dt_bias, cu_seqlens, *, scale: float 
 
 def decode_step(q, k, v, g, beta_raw, A_log, dt_bias, state, *, scale: float = None,
                 lower_bound: float = -5.0, o_dtype=None,
-                out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                out: Optional[torch.Tensor] = None,
+                gate: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
+                norm_eps: float = NORM_EPS) -> torch.Tensor:
     """One T=1 decode step for B requests; `state` [B, H, 128, 128] fp32 is updated in place.
 
     q, k, v: [B, H, 128] bf16 or fp32; g: [B, H, 128] fp32; beta_raw: [B, H] fp32.
-    Returns o [B, H, 128] in o_dtype (default: q's dtype).
+    Returns o [B, H, 128] in o_dtype (default: q's dtype). With `gate` (logits
+    [B, H, 128] in q's dtype) and `norm_weight` ([128] fp32) the output epilogue
+    of output_norm_gate is fused into the store (kda_decode_step_gated).
     """
     B, H, K = q.shape
     V = v.shape[2]
@@ -207,12 +219,48 @@ def decode_step(q, k, v, g, beta_raw, A_log, dt_bias, state, *, scale: float = N
     if out is None:
         out = torch.empty((B, H, V), dtype=o_dtype, device=q.device)
     _dev(out, "out", o_dtype, (B, H, V))
-    st = _lib.kda_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
-                              beta_raw.data_ptr(), A_log.data_ptr(), dt_bias.data_ptr(),
-                              float(scale), float(lower_bound), state.data_ptr(),
-                              out.data_ptr(), _dt(out), B, H, K, V, _dt(q),
-                              _stream_ptr(q.device))
-    _check(st, "kda_decode_step")
+    if gate is None:
+        st = _lib.kda_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                                  beta_raw.data_ptr(), A_log.data_ptr(), dt_bias.data_ptr(),
+                                  float(scale), float(lower_bound), state.data_ptr(),
+                                  out.data_ptr(), _dt(out), B, H, K, V, _dt(q),
+                                  _stream_ptr(q.device))
+        _check(st, "kda_decode_step")
+        return out
+    _dev(gate, "gate", q.dtype, (B, H, V))
+    if norm_weight is None:
+        raise ValueError("norm_weight is required with gate")
+    _dev(norm_weight, "norm_weight", torch.float32, (V,))
+    st = _lib.kda_decode_step_gated(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                                    beta_raw.data_ptr(), A_log.data_ptr(), dt_bias.data_ptr(),
+                                    float(scale), float(lower_bound), state.data_ptr(),
+                                    out.data_ptr(), _dt(out), B, H, K, V, _dt(q),
+                                    gate.data_ptr(), norm_weight.data_ptr(), float(norm_eps),
+                                    _stream_ptr(q.device))
+    _check(st, "kda_decode_step_gated")
+    return out
+
+
+def output_norm_gate(o: torch.Tensor, gate: torch.Tensor, norm_weight: torch.Tensor, *,
+                     eps: float = NORM_EPS, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Output epilogue (kda_output_norm_gate): per-row RMS norm over the last axis
+    (128 features), channel weight, sigmoid gate.
+
+    o, gate: [..., 128] bf16 or fp32 (same dtype); norm_weight: [128] fp32.
+    Returns y with o's shape and dtype (`out` may be `o` itself).
+    """
+    D = o.shape[-1]
+    rows = o.numel() // D if D else 0
+    _dev(o, "o")
+    _dev(gate, "gate", o.dtype, tuple(o.shape))
+    _dev(norm_weight, "norm_weight", torch.float32, (D,))
+    if out is None:
+        out = torch.empty_like(o)
+    _dev(out, "out", o.dtype, tuple(o.shape))
+    st = _lib.kda_output_norm_gate(o.data_ptr(), gate.data_ptr(), norm_weight.data_ptr(),
+                                   float(eps), int(rows), int(D), _dt(o), out.data_ptr(),
+                                   _stream_ptr(o.device))
+    _check(st, "kda_output_norm_gate")
     return out
 
 

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol(kda):
     assert set(syms) == set(kda.EXPORTS)
     for s in syms:
         assert hasattr(kda.lib, s), s
-    assert kda.version() == 100
+    assert kda.version() == 101
 
 
 def test_status_strings(kda):
@@ -87,6 +87,52 @@ def decode_call(kda, **kw):
 ])
 def test_decode_rejects(kda, kw, status):
     assert decode_call(kda, **kw) == status
+
+
+def gated_call(kda, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, scale=0.088,
+             lb=-5.0, state=FAKE, o=FAKE, odt=kda.KDA_BF16, B=4, H=2, K=128, V=128,
+             dt=kda.KDA_BF16, z=FAKE, w=FAKE, eps=1e-5, stream=None)
+    a.update(kw)
+    return kda.lib.kda_decode_step_gated(a["q"], a["k"], a["v"], a["g"], a["beta"], a["A_log"],
+                                         a["dt_bias"], a["scale"], a["lb"], a["state"], a["o"],
+                                         a["odt"], a["B"], a["H"], a["K"], a["V"], a["dt"],
+                                         a["z"], a["w"], a["eps"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(z=None), 1), (dict(w=None), 1), (dict(eps=0.0), 1), (dict(eps=-1e-5), 1),
+    (dict(eps=float("inf")), 1), (dict(z=FAKE + 8), 1), (dict(w=FAKE + 4), 1),
+    (dict(K=64), 2), (dict(B=0), 1), (dict(state=None), 1), (dict(o=FAKE + 4), 1),
+])
+def test_decode_gated_rejects(kda, kw, status):
+    assert gated_call(kda, **kw) == status
+    assert kda.lib.kda_last_error()
+
+
+def norm_gate_call(kda, **kw):
+    a = dict(o=FAKE, z=FAKE, w=FAKE, eps=1e-5, rows=10, D=128, dt=kda.KDA_BF16, y=FAKE, stream=None)
+    a.update(kw)
+    return kda.lib.kda_output_norm_gate(a["o"], a["z"], a["w"], a["eps"], a["rows"], a["D"],
+                                        a["dt"], a["y"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(rows=-1), 1), (dict(D=64), 2), (dict(dt=9), 2), (dict(eps=0.0), 1),
+    (dict(eps=float("nan")), 1), (dict(o=None), 1), (dict(z=None), 1), (dict(w=None), 1),
+    (dict(y=None), 1), (dict(o=FAKE + 2), 1), (dict(z=FAKE + 8), 1), (dict(w=FAKE + 4), 1),
+    (dict(y=FAKE + 4), 1), (dict(rows=1 << 40), 1),
+])
+def test_output_norm_gate_rejects(kda, kw, status):
+    assert norm_gate_call(kda, **kw) == status
+    assert kda.lib.kda_last_error()
+
+
+def test_output_norm_gate_zero_rows_enqueues_nothing(kda):
+    # rows = 0 returns OK without touching memory or launching, NULL pointers included
+    assert norm_gate_call(kda, rows=0) == 0
+    assert norm_gate_call(kda, rows=0, o=None, z=None, w=None, y=None) == 0
+    assert norm_gate_call(kda, rows=0, D=64) == 2
 
 
 def test_workspace_size_arithmetic(kda):
