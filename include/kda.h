@@ -191,6 +191,35 @@ kda_status_t kda_decode_step_gated(const void *q, const void *k, const void *v,
                                    const void *z, const float *norm_weight, float norm_eps,
                                    void *stream);
 /*
+ * Serving form of the decode step: the states live in a pool of num_slots
+ * entries and request b uses entry slot_idx[b], so that a batch can be formed
+ * from any subset of live sequences without moving states (continuous
+ * batching); everything else as for kda_decode_step, with the output epilogue
+ * of kda_decode_step_gated when z is not NULL. Makes no allocation, copy or
+ * synchronisation, so it can be captured in a HIP graph and replayed with new
+ * contents in the same buffers.
+ *
+ * state_pool : [num_slots, H, 128, 128] fp32, 16-byte aligned; the entries
+ *              named by slot_idx are read and updated in place
+ * slot_idx   : DEVICE pointer to B int32 slot indices, 4-byte aligned. A
+ *              request whose index lies outside [0, num_slots) is padding: its
+ *              output row is written as zeros and no state is touched. Two
+ *              requests naming the same slot in one call race (undefined
+ *              result).
+ * z, norm_weight, norm_eps : as for kda_decode_step_gated, or z = NULL for the
+ *              plain step (norm_weight and norm_eps are then ignored)
+ */
+kda_status_t kda_decode_step_slots(const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta_raw,
+                                   const float *A_log, const float *dt_bias,
+                                   float scale, float lower_bound,
+                                   float *state_pool, int32_t num_slots, const int32_t *slot_idx,
+                                   void *o, kda_dtype_t o_dtype,
+                                   int32_t B, int32_t H, int32_t K, int32_t V,
+                                   kda_dtype_t in_dtype,
+                                   const void *z, const float *norm_weight, float norm_eps,
+                                   void *stream);
+/*
  * Output epilogue of the attention block (kimi_k3 FusedKDAChunkwise page,
  * "Output handling": the per-head output norm, then the sigmoid output gate
  * whose logits are a projection of the hidden states; that projection and the

@@ -68,6 +68,7 @@ kda_status_t decode_step_impl(const void *q, const void *k, const void *v,
                               int32_t B, int32_t H, int32_t K, int32_t V,
                               kda_dtype_t in_dtype, void *stream,
                               const void *z, const float *norm_weight, float norm_eps,
+                              const int32_t *slots, int32_t num_slots,
                               const char *name) {
     if (B < 1) return fail(KDA_ERR_INVALID_ARG, "B must be >= 1");
     kda_status_t st = check_common(H, K, V, scale, lower_bound, in_dtype, o_dtype);
@@ -96,6 +97,7 @@ kda_status_t decode_step_impl(const void *q, const void *k, const void *v,
     a.B = B; a.H = H; a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = o_dtype == KDA_BF16;
     a.stream = (hipStream_t)stream;
     a.z = z; a.norm_w = norm_weight; a.norm_eps = norm_eps;
+    a.slots = slots; a.num_slots = num_slots;
     hipError_t e = kda::launch_decode(a);
     if (e != hipSuccess) return hip_fail(e, name);
     return ok();
@@ -235,7 +237,7 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
                              kda_dtype_t in_dtype, void *stream) {
     return decode_step_impl(q, k, v, g, beta_raw, A_log, dt_bias, scale, lower_bound, state, o,
                             o_dtype, B, H, K, V, in_dtype, stream, nullptr, nullptr, 0.f,
-                            "kda_decode_step launch");
+                            nullptr, 0, "kda_decode_step launch");
 }
 
 kda_status_t kda_decode_step_gated(const void *q, const void *k, const void *v,
@@ -250,7 +252,27 @@ kda_status_t kda_decode_step_gated(const void *q, const void *k, const void *v,
     if (!z) return fail(KDA_ERR_INVALID_ARG, "z is NULL");
     return decode_step_impl(q, k, v, g, beta_raw, A_log, dt_bias, scale, lower_bound, state, o,
                             o_dtype, B, H, K, V, in_dtype, stream, z, norm_weight, norm_eps,
-                            "kda_decode_step_gated launch");
+                            nullptr, 0, "kda_decode_step_gated launch");
+}
+
+kda_status_t kda_decode_step_slots(const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta_raw,
+                                   const float *A_log, const float *dt_bias,
+                                   float scale, float lower_bound,
+                                   float *state_pool, int32_t num_slots, const int32_t *slot_idx,
+                                   void *o, kda_dtype_t o_dtype,
+                                   int32_t B, int32_t H, int32_t K, int32_t V,
+                                   kda_dtype_t in_dtype,
+                                   const void *z, const float *norm_weight, float norm_eps,
+                                   void *stream) {
+    if (num_slots < 1) return fail(KDA_ERR_INVALID_ARG, "num_slots must be >= 1");
+    if (!slot_idx) return fail(KDA_ERR_INVALID_ARG, "slot_idx is NULL");
+    if (((uintptr_t)slot_idx & 3) != 0) return fail(KDA_ERR_INVALID_ARG, "slot_idx must be 4-byte aligned");
+    if ((int64_t)num_slots * H > ((int64_t)1 << 31) - 1)
+        return fail(KDA_ERR_INVALID_ARG, "num_slots * H too large");
+    return decode_step_impl(q, k, v, g, beta_raw, A_log, dt_bias, scale, lower_bound, state_pool,
+                            o, o_dtype, B, H, K, V, in_dtype, stream, z, norm_weight, norm_eps,
+                            slot_idx, num_slots, "kda_decode_step_slots launch");
 }
 
 kda_status_t kda_output_norm_gate(const void *o, const void *z, const float *weight, float eps,

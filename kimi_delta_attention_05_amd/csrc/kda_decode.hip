@@ -30,7 +30,8 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const float *__restrict__ g, const float *__restrict__ beta_raw,
     const float *__restrict__ A_log, const float *__restrict__ dt_bias,
     float scale, float lower_bound, float *__restrict__ state, Tout *__restrict__ o,
-    int H, const Tin *__restrict__ zg, const float *__restrict__ norm_w, float norm_eps)
+    int H, const Tin *__restrict__ zg, const float *__restrict__ norm_w, float norm_eps,
+    const int32_t *__restrict__ slots, int num_slots)
 {
     const int bh = blockIdx.x;                 // request * H + head
     const int h = bh % H;
@@ -39,7 +40,20 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const int j = lane & 15;                   // channels 4j .. 4j+3 and 64+4j .. 64+4j+3
     const int r = lane >> 4;                   // row within the wave's 4 rows
 
-    f32x4 *S4 = reinterpret_cast<f32x4 *>(state + (size_t)bh * (kHeadDim * kHeadDim));
+    // state of this (request, head): row bh of the state array, or, with slot
+    // indices, row slots[request] * H + h of a state pool; a request whose slot
+    // lies outside [0, num_slots) is padding: its outputs are zero and no state
+    // is touched (the decision is uniform over the workgroup)
+    size_t sbh = (size_t)bh;
+    if (slots) {
+        const int sl = slots[bh / H];
+        if (sl < 0 || sl >= num_slots) {
+            if (threadIdx.x < kHeadDim) o[(size_t)bh * kHeadDim + threadIdx.x] = from_f32<Tout>(0.0f);
+            return;
+        }
+        sbh = (size_t)sl * H + h;
+    }
+    f32x4 *S4 = reinterpret_cast<f32x4 *>(state + sbh * (kHeadDim * kHeadDim));
 
     // Issue the state loads first: rows 16*it + 4*wave + r, 16-byte pieces j and 16+j.
     f32x4 st[8][2];
@@ -129,12 +143,12 @@ static hipError_t launch_decode_t(const DecodeArgs &a) {
         decode_step_kernel<Tin, Tout, true><<<grid, 256, 0, a.stream>>>(
             (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v, a.g, a.beta_raw,
             a.A_log, a.dt_bias, a.scale, a.lower_bound, a.state, (Tout *)a.o, a.H,
-            (const Tin *)a.z, a.norm_w, a.norm_eps);
+            (const Tin *)a.z, a.norm_w, a.norm_eps, a.slots, a.num_slots);
     else
         decode_step_kernel<Tin, Tout, false><<<grid, 256, 0, a.stream>>>(
             (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v, a.g, a.beta_raw,
             a.A_log, a.dt_bias, a.scale, a.lower_bound, a.state, (Tout *)a.o, a.H,
-            nullptr, nullptr, 0.f);
+            nullptr, nullptr, 0.f, a.slots, a.num_slots);
     return hipGetLastError();
 }
 

@@ -21,6 +21,10 @@ struct DecodeArgs {
     const void *z = nullptr;
     const float *norm_w = nullptr;
     float norm_eps = 0.f;
+    // state pool addressing (slots == nullptr: state is [B, H, V, K]): request b
+    // uses pool entry slots[b] (device int32), padding if outside [0, num_slots)
+    const int32_t *slots = nullptr;
+    int num_slots = 0;
 };
 
 // Output epilogue over rows of 128 features: y = o / sqrt(mean(o^2) + eps) * w * sigmoid(z).

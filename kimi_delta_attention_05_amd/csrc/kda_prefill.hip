@@ -36,6 +36,8 @@
 #include "kda_common.h"
 #include "kda_internal.h"
 
+#include <atomic>
+
 namespace kda {
 
 constexpr int KP = kHeadDim + 4;   // LDS row pitch (floats) of [C][128] tiles
@@ -1676,15 +1678,43 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
 
 // ---- launchers ----------------------------------------------------------------
 
+// Device queries and function attributes are settled on the first launch on
+// each device and cached, so that later launches (for instance under HIP graph
+// capture, after an eager warm-up call) make no runtime call besides the launch.
+constexpr int kMaxDevices = 64;
+
+static hipError_t cu_count(int &cus) {
+    static std::atomic<int> cache[kMaxDevices];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices && (cus = cache[dev].load(std::memory_order_relaxed)) > 0)
+        return hipSuccess;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess && dev >= 0 && dev < kMaxDevices) cache[dev].store(cus, std::memory_order_relaxed);
+    return e;
+}
+
+// One flag word per kernel: bit d set once the dynamic-LDS limit is set on device d.
+static hipError_t set_lds_limit(const void *fn, int lds, std::atomic<uint64_t> &done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < kMaxDevices) ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_relaxed);
+    return e;
+}
+
 template <int C, typename Tin, typename Tout>
 static hipError_t launch_prefill_t(const PrefillArgs &a) {
     constexpr bool PRECISE = std::is_same<Tin, float>::value;
     const int64_t slots = num_slots(a.T, a.N, C);
     if ((a.stages & 1) && slots > 0) {
         // persistent workgroups walking tiles blockIdx.x, blockIdx.x + gridDim.x, ...
-        int dev = 0, cus = 0;
-        hipError_t e = hipGetDevice(&dev);
-        if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+        int cus = 0;
+        hipError_t e = cu_count(cus);
         if (e != hipSuccess) return e;
         const int64_t ntiles = slots * a.H;
         if constexpr (C == 64 && !PRECISE) {
@@ -1702,8 +1732,8 @@ static hipError_t launch_prefill_t(const PrefillArgs &a) {
     if ((a.stages & 2) && nchains > 0) {
         using CFG = InterCfg<C, PRECISE>;
         const size_t lds = (size_t)CFG::NBUF * CFG::BUF;
-        hipError_t e = hipFuncSetAttribute((const void *)inter_kernel<C, Tout, PRECISE>,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        static std::atomic<uint64_t> lds_set{0};          // one flag word per kernel
+        hipError_t e = set_lds_limit((const void *)inter_kernel<C, Tout, PRECISE>, (int)lds, lds_set);
         if (e != hipSuccess) return e;
         const unsigned groups = (unsigned)(8 * 2 * ((nchains + 7) / 8));
         inter_kernel<C, Tout, PRECISE><<<groups, 256, lds, a.stream>>>(a, nchains);

@@ -25,7 +25,7 @@ KDA_F32, KDA_BF16 = 0, 1
 EXPORTS = ("kda_version", "kda_status_string", "kda_last_error",
            "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_intra",
            "kda_chunk_fwd_inter", "kda_decode_step", "kda_decode_step_gated",
-           "kda_output_norm_gate", "kda_check_cu_seqlens")
+           "kda_decode_step_slots", "kda_output_norm_gate", "kda_check_cu_seqlens")
 
 NORM_EPS = 1e-5   # default epsilon of the output norm (the pages give none)
 
@@ -58,6 +58,10 @@ _lib.kda_decode_step.argtypes = [_P, _P, _P, _P, _P, _P, _P, _f32, _f32, _P, _P,
 _lib.kda_decode_step_gated.restype = ctypes.c_int
 _lib.kda_decode_step_gated.argtypes = [_P, _P, _P, _P, _P, _P, _P, _f32, _f32, _P, _P, ctypes.c_int,
                                        _i32, _i32, _i32, _i32, ctypes.c_int, _P, _P, _f32, _P]
+_lib.kda_decode_step_slots.restype = ctypes.c_int
+_lib.kda_decode_step_slots.argtypes = [_P, _P, _P, _P, _P, _P, _P, _f32, _f32, _P, _i32, _P, _P,
+                                       ctypes.c_int, _i32, _i32, _i32, _i32, ctypes.c_int, _P, _P,
+                                       _f32, _P]
 _lib.kda_output_norm_gate.restype = ctypes.c_int
 _lib.kda_output_norm_gate.argtypes = [_P, _P, _P, _f32, _i64, _i32, ctypes.c_int, _P, _P]
 _lib.kda_check_cu_seqlens.restype = ctypes.c_int
@@ -195,13 +199,17 @@ def decode_step(q, k, v, g, beta_raw, A_log, dt_bias, state, *, scale: float = N
                 lower_bound: float = -5.0, o_dtype=None,
                 out: Optional[torch.Tensor] = None,
                 gate: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
-                norm_eps: float = NORM_EPS) -> torch.Tensor:
+                norm_eps: float = NORM_EPS,
+                slot_idx: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One T=1 decode step for B requests; `state` [B, H, 128, 128] fp32 is updated in place.
 
     q, k, v: [B, H, 128] bf16 or fp32; g: [B, H, 128] fp32; beta_raw: [B, H] fp32.
     Returns o [B, H, 128] in o_dtype (default: q's dtype). With `gate` (logits
     [B, H, 128] in q's dtype) and `norm_weight` ([128] fp32) the output epilogue
-    of output_norm_gate is fused into the store (kda_decode_step_gated).
+    of output_norm_gate is fused into the store (kda_decode_step_gated). With
+    `slot_idx` (int32 [B] on the GPU), `state` is a pool [S, H, 128, 128] and
+    request b uses entry slot_idx[b]; indices outside [0, S) mark padding
+    requests (zero output, no state touched) (kda_decode_step_slots).
     """
     B, H, K = q.shape
     V = v.shape[2]
@@ -214,11 +222,33 @@ def decode_step(q, k, v, g, beta_raw, A_log, dt_bias, state, *, scale: float = N
     _dev(beta_raw, "beta_raw", torch.float32, (B, H))
     _dev(A_log, "A_log", torch.float32, (H,))
     _dev(dt_bias, "dt_bias", torch.float32, (H, K))
-    _dev(state, "state", torch.float32, (B, H, V, K))
+    if slot_idx is None:
+        _dev(state, "state", torch.float32, (B, H, V, K))
+    else:
+        _dev(state, "state")
+        if state.dim() != 4 or tuple(state.shape[1:]) != (H, V, K) or state.dtype != torch.float32:
+            raise ValueError("state must be an fp32 pool [S, %d, %d, %d]" % (H, V, K))
+        _dev(slot_idx, "slot_idx", torch.int32, (B,))
     o_dtype = q.dtype if o_dtype is None else o_dtype
     if out is None:
         out = torch.empty((B, H, V), dtype=o_dtype, device=q.device)
     _dev(out, "out", o_dtype, (B, H, V))
+    if slot_idx is not None:
+        zp = wp = None
+        if gate is not None:
+            _dev(gate, "gate", q.dtype, (B, H, V))
+            if norm_weight is None:
+                raise ValueError("norm_weight is required with gate")
+            _dev(norm_weight, "norm_weight", torch.float32, (V,))
+            zp, wp = gate.data_ptr(), norm_weight.data_ptr()
+        st = _lib.kda_decode_step_slots(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                                        beta_raw.data_ptr(), A_log.data_ptr(), dt_bias.data_ptr(),
+                                        float(scale), float(lower_bound), state.data_ptr(),
+                                        int(state.shape[0]), slot_idx.data_ptr(), out.data_ptr(),
+                                        _dt(out), B, H, K, V, _dt(q), zp, wp, float(norm_eps),
+                                        _stream_ptr(q.device))
+        _check(st, "kda_decode_step_slots")
+        return out
     if gate is None:
         st = _lib.kda_decode_step(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
                                   beta_raw.data_ptr(), A_log.data_ptr(), dt_bias.data_ptr(),

@@ -110,6 +110,27 @@ def test_decode_gated_rejects(kda, kw, status):
     assert kda.lib.kda_last_error()
 
 
+def slots_call(kda, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, scale=0.088,
+             lb=-5.0, pool=FAKE, S=8, idx=FAKE, o=FAKE, odt=kda.KDA_BF16, B=4, H=2, K=128, V=128,
+             dt=kda.KDA_BF16, z=None, w=None, eps=1e-5, stream=None)
+    a.update(kw)
+    return kda.lib.kda_decode_step_slots(a["q"], a["k"], a["v"], a["g"], a["beta"], a["A_log"],
+                                         a["dt_bias"], a["scale"], a["lb"], a["pool"], a["S"],
+                                         a["idx"], a["o"], a["odt"], a["B"], a["H"], a["K"],
+                                         a["V"], a["dt"], a["z"], a["w"], a["eps"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(S=0), 1), (dict(idx=None), 1), (dict(idx=FAKE + 2), 1), (dict(pool=None), 1),
+    (dict(pool=FAKE + 4), 1), (dict(S=1 << 30, H=4), 1), (dict(z=FAKE), 1),
+    (dict(z=FAKE, w=FAKE, eps=0.0), 1), (dict(K=64), 2), (dict(B=0), 1),
+])
+def test_decode_slots_rejects(kda, kw, status):
+    assert slots_call(kda, **kw) == status
+    assert kda.lib.kda_last_error()
+
+
 def norm_gate_call(kda, **kw):
     a = dict(o=FAKE, z=FAKE, w=FAKE, eps=1e-5, rows=10, D=128, dt=kda.KDA_BF16, y=FAKE, stream=None)
     a.update(kw)
