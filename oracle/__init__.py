@@ -10,7 +10,9 @@ Formulations here:
   * `kda_chunked`   — the chunkwise WY form (chunked.py), derived separately and
     used to pin the recurrence and to check the GPU's intra-chunk stage;
   * `output_norm_gate` — the output epilogue (epilogue.py): per-head RMS norm
-    and sigmoid output gate applied to the recurrence's outputs.
+    and sigmoid output gate applied to the recurrence's outputs;
+  * `short_conv_silu` — the front end (shortconv.py): causal depthwise short
+    convolution + SiLU applied to q, k, v before the recurrence.
 """
 from __future__ import annotations
 
@@ -165,6 +167,7 @@ def kda_decode_steps(steps, state, A_log, dt_bias, *, scale: float,
 
 from .chunked import kda_chunked  # noqa: E402  (pure numpy, no library)
 from .epilogue import output_norm_gate  # noqa: E402  (pure numpy, no library)
+from .shortconv import short_conv_silu  # noqa: E402  (pure numpy, no library)
 
 __all__ = ["build", "kda_recurrent", "kda_decode_steps", "kda_chunked",
-           "output_norm_gate", "max_threads", "LOWER_BOUND", "L2_EPS"]
+           "output_norm_gate", "short_conv_silu", "max_threads", "LOWER_BOUND", "L2_EPS"]
