@@ -27,28 +27,29 @@ def silu(u):
 
 
 def short_conv_silu(x, w, cu_seqlens, *, state=None):
-    """x: [T, H, D]; w: [H, D, W]; cu_seqlens: [N+1]; state: [N, H, W-1, D] or None.
+    """x: [T, H, D]; w: [H, D, W]; cu_seqlens: [N+1]; state: [N, W-1, H, D] or None.
 
-    Returns (y [T, H, D], final_state [N, H, W-1, D]): the final state of a
-    sequence is its last W - 1 inputs, reaching back into its initial state
-    when the sequence is shorter than W - 1 (an empty sequence keeps it).
+    A conv state is W - 1 input rows, oldest first. Returns (y [T, H, D],
+    final_state [N, W-1, H, D]): the final state of a sequence is its last
+    W - 1 inputs, reaching back into its initial state when the sequence is
+    shorter than W - 1 (an empty sequence keeps it).
     """
     x, w, cu = _f64(x), _f64(w), _i64(cu_seqlens)
     T, H, D = x.shape
     W = w.shape[2]
     N = cu.shape[0] - 1
     assert w.shape == (H, D, W) and int(cu[-1]) == T
-    st = np.zeros((N, H, W - 1, D)) if state is None else _f64(state)
-    assert st.shape == (N, H, W - 1, D)
+    st = np.zeros((N, W - 1, H, D)) if state is None else _f64(state)
+    assert st.shape == (N, W - 1, H, D)
     y = np.zeros((T, H, D))
-    final = np.zeros((N, H, W - 1, D))
+    final = np.zeros((N, W - 1, H, D))
     for n in range(N):
         s0, s1 = int(cu[n]), int(cu[n + 1])
         # history rows (W - 1 of them) followed by the sequence's own inputs
-        seq = np.concatenate([st[n].transpose(1, 0, 2), x[s0:s1]], axis=0)   # [W-1+L, H, D]
+        seq = np.concatenate([st[n], x[s0:s1]], axis=0)                     # [W-1+L, H, D]
         for t in range(s1 - s0):
             win = seq[t:t + W]                                              # [W, H, D]
             pre = np.einsum("ihd,hdi->hd", win, w)
             y[s0 + t] = silu(pre)
-        final[n] = seq[seq.shape[0] - (W - 1):].transpose(1, 0, 2) if W > 1 else final[n]
+        final[n] = seq[seq.shape[0] - (W - 1):]
     return y, final

@@ -57,7 +57,7 @@ def test_packed_equals_separate_and_chaining():
     cu = np.concatenate([[0], np.cumsum(lens)])
     x = rng.standard_normal((int(cu[-1]), 3, 4))
     w = rng.standard_normal((3, 4, 4))
-    st = rng.standard_normal((4, 3, 3, 4))
+    st = rng.standard_normal((4, 3, 3, 4))   # [N, W-1, H, D]
     y, f = oracle.short_conv_silu(x, w, cu, state=st)
     for n in range(4):
         ys, fs = oracle.short_conv_silu(x[cu[n]:cu[n + 1]], w, np.array([0, lens[n]]), state=st[n:n + 1])
@@ -65,8 +65,8 @@ def test_packed_equals_separate_and_chaining():
         np.testing.assert_array_equal(f[n], fs[0])
     # the empty sequence keeps its state; the 2-token one keeps its last state row
     np.testing.assert_array_equal(f[1], st[1])
-    np.testing.assert_array_equal(f[2][:, 0], st[2][:, 2])
-    np.testing.assert_array_equal(f[2][:, 1:], x[cu[2]:cu[3]].transpose(1, 0, 2))
+    np.testing.assert_array_equal(f[2][0], st[2][2])
+    np.testing.assert_array_equal(f[2][1:], x[cu[2]:cu[3]])
     # splitting a sequence and passing the final state on gives the same outputs
     a, b = x[cu[3]:cu[3] + 4], x[cu[3] + 4:cu[4]]
     ya, fa = oracle.short_conv_silu(a, w, np.array([0, 4]), state=st[3:4])
@@ -90,7 +90,7 @@ def test_matches_library_depthwise_conv1d():
     ref = ref[0].T.reshape(T, H, D).numpy()
     y, f = oracle.short_conv_silu(x, w, np.array([0, T]))
     np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-14)
-    np.testing.assert_array_equal(f[0], x[T - 3:].transpose(1, 0, 2))
+    np.testing.assert_array_equal(f[0], x[T - 3:])
 
 
 def test_silu_values():
@@ -107,12 +107,12 @@ def test_pins_catch_planted_mistakes(mistake):
         T, H, D = x.shape
         W = w.shape[2]
         N = len(cu) - 1
-        st = np.zeros((N, H, W - 1, D)) if state is None else np.asarray(state, float)
+        st = np.zeros((N, W - 1, H, D)) if state is None else np.asarray(state, float)
         y = np.zeros_like(x)
-        fin = np.zeros((N, H, W - 1, D))
+        fin = np.zeros((N, W - 1, H, D))
         for n in range(N):
             s0, s1 = cu[n], cu[n + 1]
-            hist = st[n].transpose(1, 0, 2)
+            hist = st[n]
             if mistake == "no_restart" and s0 > 0:
                 hist = x[max(0, s0 - (W - 1)):s0]
                 if hist.shape[0] < W - 1:
@@ -124,7 +124,7 @@ def test_pins_catch_planted_mistakes(mistake):
                 ww = w[:, :, ::-1] if mistake == "tap_order" else w
                 pre = np.einsum("ihd,hdi->hd", seq[t:t + W], ww)
                 y[s0 + t] = pre if mistake == "no_activation" else silu(pre)
-            fin[n] = seq[seq.shape[0] - (W - 1):].transpose(1, 0, 2)
+            fin[n] = seq[seq.shape[0] - (W - 1):]
         return y, fin
 
     real = oracle.short_conv_silu
