@@ -241,6 +241,43 @@ kda_status_t kda_output_norm_gate(const void *o, const void *z, const float *wei
                                   int64_t rows, int32_t D, kda_dtype_t io_dtype, void *y,
                                   void *stream);
 /*
+ * Front end of the attention block (kimi_k3 FusedKDAChunkwise page, "CUDA-only
+ * forward and causal preprocessing": after the q, k, v projections each channel
+ * is left-padded by W - 1 along time, filtered by its own depthwise kernel and
+ * passed through SiLU). Call it once each for q, k and v, with their own
+ * weights. For each channel c and token t of packed sequence n:
+ *
+ *   y[t, c] = silu( sum_{i=0}^{W-1} weight[c, i] * x[t - (W - 1) + i, c] ),  silu(u) = u sigmoid(u)
+ *
+ * where the W - 1 positions before the sequence's first token are rows of its
+ * carried-in conv state (oldest first), or zeros when state_in is NULL; tap
+ * W - 1 multiplies the current token. Computed in fp32, rounded to nearest
+ * even when bf16.
+ *
+ * x         : total_tokens rows of `channels` elements in dtype, row stride
+ *             x_stride elements (>= channels, a multiple of 8; a slice of a
+ *             fused projection output can be passed as it is), 16-byte aligned
+ * weight    : [channels, W] fp32 (the layout of a grouped conv1d weight
+ *             [channels, 1, W]), 4-byte aligned
+ * W         : kernel size, 1 .. 4 (the page gives none)
+ * cu_seqlens: [num_seqs + 1] int64 DEVICE offsets, trusted as for kda_chunk_fwd
+ * channels  : H * 128 for one of q, k, v; a positive multiple of 8
+ * state_in  : [num_seqs, W - 1, channels] in dtype, or NULL (zero history)
+ * state_out : [num_seqs, W - 1, channels] in dtype, or NULL: each sequence's
+ *             last W - 1 inputs, reaching back into state_in for sequences
+ *             shorter than W - 1 (an empty sequence passes its state on). May
+ *             be state_in itself (updated in place). Both are ignored when W == 1.
+ * y         : [total_tokens, channels] in dtype, contiguous, 16-byte aligned
+ *
+ * y may not overlap x or a state, and state_out may not overlap x or partly
+ * overlap state_in: rejected with KDA_ERR_INVALID_ARG. total_tokens == 0 only
+ * passes states on (x and y may then be NULL).
+ */
+kda_status_t kda_short_conv(const void *x, int64_t x_stride, const float *weight, int32_t W,
+                            const int64_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                            int64_t channels, kda_dtype_t dtype, const void *state_in,
+                            void *state_out, void *y, void *stream);
+/*
  * Opt-in check of packed offsets (FlashInfer kda_backward page: offsets are
  * validated by one eager synchronisation, the launch path then trusts them).
  * Copies cu_seqlens to the host on `stream`, synchronises that stream and

@@ -18,6 +18,8 @@ stated for the five standard configurations:
   decode     : 256 requests, H=32, 64 consecutive T=1 steps, state ~ N(0, 0.1^2)
   epilogue   : output-gate logits ~ N(0, 2^2) in the token dtype and an output-norm
                weight ~ U(0.5, 1.5) (stand-ins for the model's projection and weight)
+  front end  : projection outputs ~ N(0, 1) in the token dtype, conv weights
+               ~ U(-1/sqrt(W), 1/sqrt(W)), carried-in conv states ~ N(0, 1)
 
 "N(0, s)" in the configuration text is read as standard deviation s.
 All values are drawn in fp32 from a CPU `torch.Generator` seeded with the
@@ -180,3 +182,23 @@ def make_epilogue(shape, *, token_dtype=torch.bfloat16, z_std=2.0, seed=0, D=V_D
     z = _randn(gen, tuple(shape), z_std).to(token_dtype)
     w = _uniform(gen, (D,), 0.5, 1.5)
     return z, w
+
+
+def make_short_conv(lengths, H, W, *, token_dtype=torch.bfloat16, with_state=True, seed=0,
+                    D=K_DIM):
+    """Synthetic inputs of the q/k/v front end for one of q, k, v: a projection
+    output x [T, H, D] ~ N(0, 1) in the token dtype, conv weights [H, D, W] fp32 ~
+    U(-1/sqrt(W), 1/sqrt(W)) (the default init range of a depthwise conv1d with
+    W taps), and carried-in conv states [N, W-1, H, D] ~ N(0, 1) in the token
+    dtype (or None). Returns (x, w, cu_seqlens, state)."""
+    gen = torch.Generator().manual_seed(int(seed))
+    lengths = [int(n) for n in lengths]
+    T, N = sum(lengths), len(lengths)
+    cu = torch.zeros(N + 1, dtype=torch.int64)
+    if N:
+        cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0)
+    x = _randn(gen, (T, H, D)).to(token_dtype)
+    bound = 1.0 / math.sqrt(W)
+    w = _uniform(gen, (H, D, W), -bound, bound)
+    state = _randn(gen, (N, W - 1, H, D)).to(token_dtype) if with_state else None
+    return x, w, cu, state

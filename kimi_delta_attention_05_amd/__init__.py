@@ -1,5 +1,6 @@
 """Kimi Delta Attention forward for AMD MI355X: Python binding of libkda.
 
+`short_conv` (the q/k/v front end: causal depthwise short conv + SiLU),
 `chunk_fwd` (chunkwise prefill over packed sequences), `decode_step` (batched
 T=1 step, optionally with the output epilogue fused) and `output_norm_gate`
 (the output epilogue: per-head RMS norm and sigmoid gate) call the HIP kernels
@@ -7,7 +8,7 @@ in libkda.so through its C ABI (include/kda.h). Importing the package fails if
 the library is not built.
 """
 from .kda import (KDAError, Workspace, check_cu_seqlens, chunk_fwd, decode_step,
-                  output_norm_gate, version, workspace_size, LIB_PATH, NORM_EPS)
+                  output_norm_gate, short_conv, version, workspace_size, LIB_PATH, NORM_EPS)
 
 __all__ = ["KDAError", "Workspace", "check_cu_seqlens", "chunk_fwd", "decode_step",
-           "output_norm_gate", "version", "workspace_size", "LIB_PATH", "NORM_EPS"]
+           "output_norm_gate", "short_conv", "version", "workspace_size", "LIB_PATH", "NORM_EPS"]

@@ -276,6 +276,23 @@ __device__ __forceinline__ void load8(const __bf16 *p, float (&x)[8]) {
     for (int e = 0; e < 8; ++e) x[e] = (float)a[e];
 }
 
+// 8 fp32 values stored as 8 consecutive elements (one 16- or 32-byte store;
+// bf16 rounds to nearest even).
+template <typename T>
+__device__ __forceinline__ void store8(T *p, const float (&x)[8]);
+template <>
+__device__ __forceinline__ void store8<float>(float *p, const float (&x)[8]) {
+    ((f32x4 *)p)[0] = f32x4{x[0], x[1], x[2], x[3]};
+    ((f32x4 *)p)[1] = f32x4{x[4], x[5], x[6], x[7]};
+}
+template <>
+__device__ __forceinline__ void store8<__bf16>(__bf16 *p, const float (&x)[8]) {
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (__bf16)x[e];
+    *(bf16x8 *)p = v;
+}
+
 // Power of two 2^e with e = ceil(log2(m)) - target, so that m * 2^-e <= 2^target;
 // returns 1 for m == 0 or non-finite m.
 __device__ __forceinline__ float pow2_scale_for(float m, int target) {

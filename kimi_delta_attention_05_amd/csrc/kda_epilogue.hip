@@ -13,21 +13,6 @@
 namespace kda {
 
 template <typename T>
-__device__ __forceinline__ void store8(T *p, const float (&x)[8]);
-template <>
-__device__ __forceinline__ void store8<float>(float *p, const float (&x)[8]) {
-    ((f32x4 *)p)[0] = f32x4{x[0], x[1], x[2], x[3]};
-    ((f32x4 *)p)[1] = f32x4{x[4], x[5], x[6], x[7]};
-}
-template <>
-__device__ __forceinline__ void store8<__bf16>(__bf16 *p, const float (&x)[8]) {
-    bf16x8 v;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (__bf16)x[e];
-    *(bf16x8 *)p = v;
-}
-
-template <typename T>
 __global__ __launch_bounds__(256) void norm_gate_kernel(const T *__restrict__ o, const T *__restrict__ z,
                                                         const float *__restrict__ w, float eps,
                                                         int64_t rows, T *y)

@@ -113,8 +113,30 @@ size_t record_bytes(int chunk, bool precise);
 // which is unique and below floor(T/C) + N for any valid offsets.
 __host__ __device__ inline int64_t num_slots(int64_t T, int N, int chunk) { return T / chunk + N; }
 
+// Front end: causal depthwise short conv + SiLU over `channels` channels.
+struct ShortConvArgs {
+    const void *x = nullptr;            // [T] rows of `channels`, row stride x_stride
+    int64_t x_stride = 0;               // elements
+    const float *w = nullptr;           // [channels, W]
+    int W = 0;                          // 1 .. 4
+    const int64_t *cu = nullptr;        // [N + 1] device offsets
+    int N = 0;
+    int64_t T = 0;
+    int64_t channels = 0;               // multiple of 8
+    const void *st_in = nullptr;        // [N, W - 1, channels] or NULL (zero history)
+    void *st_out = nullptr;             // [N, W - 1, channels] or NULL; may equal st_in
+    void *y = nullptr;                  // [T, channels]
+    bool bf16 = false;
+    hipStream_t stream = nullptr;
+};
+
+// Workgroups of the two front-end launches (for the host's size checks).
+int64_t short_conv_blocks(int64_t T, int64_t channels, bool bf16);
+int64_t short_conv_state_blocks(int64_t N, int64_t channels);
+
 hipError_t launch_decode(const DecodeArgs &a);
 hipError_t launch_norm_gate(const NormGateArgs &a);
 hipError_t launch_prefill(const PrefillArgs &a);
+hipError_t launch_short_conv(const ShortConvArgs &a);
 
 }  // namespace kda

@@ -1,0 +1,224 @@
+// Front end of the attention block (kimi_k3 FusedKDAChunkwise page, "CUDA-only
+// forward and causal preprocessing"): every channel of the q, k or v
+// projection is filtered along time by its own short causal kernel of W taps
+// (left padding of W - 1), then passed through SiLU:
+//
+//   y[t, c] = silu( sum_{i < W} w[c, i] * x[t - (W - 1) + i, c] ),   silu(u) = u sigmoid(u)
+//
+// Packed sequences restart the history at their first token: the W - 1
+// positions before it come from the sequence's carried-in conv state (its last
+// W - 1 inputs so far, oldest first), or are zero without one.
+//
+// Layout: x rows of `channels` elements with row stride x_stride (a q, k or v
+// slice of a fused projection can be passed as it is), y [T, channels]
+// contiguous, weights [channels, W] fp32, conv states [N, W - 1, channels] in
+// x's dtype.
+//
+// Work split (short_conv_kernel): a thread owns 8 consecutive channels of a
+// strip of S tokens; it loads the strip's S rows plus the W - 1 rows before it
+// into registers (16- or 32-byte loads, consecutive lanes on consecutive
+// channels) and slides the W-row window down the strip, so every input row is
+// read once per strip and every output row written once. HBM-bound. Strips of
+// one channel block follow each other on one XCD (blocks are dealt to the 8
+// XCDs round-robin), so the W - 1 halo rows of a strip were fetched into that
+// XCD's L2 by the strip before it. Tokens within W - 1 of a sequence start take
+// their missing taps from the conv state (a wave-uniform branch).
+//
+// final_state_kernel writes each sequence's final conv state, its last W - 1
+// inputs reaching back into the carried-in state for sequences shorter than
+// W - 1. It runs after short_conv_kernel on the same stream and each thread
+// reads all it needs before writing, so the output state may be the input
+// state (updated in place).
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int kConvThreads = 256;
+constexpr int kConvChanPerBlock = 8 * kConvThreads;
+
+template <typename T> struct ConvStrip;
+template <> struct ConvStrip<__bf16> { static constexpr int S = 32; };
+template <> struct ConvStrip<float> { static constexpr int S = 16; };
+
+// Sequence of token t: the n in [0, N) with cu[n] <= t < cu[n + 1] (empty
+// sequences are skipped). Wave-uniform arguments; needs 0 <= t < cu[N].
+__device__ __forceinline__ int seq_of(const int64_t *cu, int N, int64_t t) {
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] <= t) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+}
+
+// Logical work item of physical block b. Blocks are dealt to the 8 XCDs
+// round-robin (b mod 8); XCD x is given the contiguous logical range
+// [x * per, (x + 1) * per), walked in order, where logical ids run over
+// strips fastest: consecutive strips of a channel block share an L2.
+__device__ __forceinline__ int64_t xcd_logical(int64_t b, int64_t per) {
+    return (b & 7) * per + (b >> 3);
+}
+
+template <typename T, int W>
+__global__ __launch_bounds__(kConvThreads) void short_conv_kernel(
+    const T *__restrict__ x, int64_t x_stride, const float *__restrict__ w,
+    const int64_t *__restrict__ cu, int N, int64_t T_total, int64_t channels,
+    int64_t nstrips, int64_t per_xcd, int64_t nlogical,
+    const T *__restrict__ st_in, T *__restrict__ y)
+{
+    constexpr int S = ConvStrip<T>::S;
+    const int64_t L = xcd_logical(blockIdx.x, per_xcd);
+    if (L >= nlogical) return;
+    const int64_t cb = L / nstrips;
+    const int64_t strip = L - cb * nstrips;
+    const int64_t c = cb * kConvChanPerBlock + 8 * (int64_t)threadIdx.x;
+    if (c >= channels) return;                       // channels % 8 == 0: whole groups
+    const int64_t t0 = strip * S;
+
+    float wt[W][8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+#pragma unroll
+        for (int i = 0; i < W; ++i) wt[i][e] = w[(c + e) * W + i];
+    }
+
+    // rows t0 - (W - 1) .. t0 + S - 1; rows outside [0, T) read as zero and
+    // are never used for an output (a row before 0 lies before the first
+    // sequence start; a row at or past T belongs to no output token)
+    Vec8<T> xr[S + W - 1];            // kept packed until used
+#pragma unroll
+    for (int r = 0; r < S + W - 1; ++r) {
+        const int64_t t = t0 - (W - 1) + r;
+        if (t >= 0 && t < T_total) xr[r].load(x + t * x_stride + c);
+        else xr[r].zero();
+    }
+
+    int n = seq_of(cu, N, t0);
+    int64_t s0 = cu[n], s1 = cu[n + 1];
+#pragma unroll
+    for (int j = 0; j < S; ++j) {
+        const int64_t t = t0 + j;
+        if (t >= T_total) break;
+        while (t >= s1) { ++n; s0 = s1; s1 = cu[n + 1]; }
+        float acc[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[e] = wt[W - 1][e] * xr[j + W - 1][e];
+        if (t - s0 >= W - 1) {
+#pragma unroll
+            for (int i = 0; i < W - 1; ++i) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = fmaf(wt[i][e], xr[j + i][e], acc[e]);
+            }
+        } else {
+            // within W - 1 of the sequence start: taps before it read the
+            // sequence's conv state row (p - s0 + W - 1), or zero
+#pragma unroll
+            for (int i = 0; i < W - 1; ++i) {
+                const int64_t p = t - (W - 1) + i;
+                float hv[8];
+                if (p >= s0) {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) hv[e] = xr[j + i][e];
+                } else if (st_in) {
+                    load8(st_in + ((int64_t)n * (W - 1) + (p - s0 + W - 1)) * channels + c, hv);
+                } else {
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) hv[e] = 0.f;
+                }
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[e] = fmaf(wt[i][e], hv[e], acc[e]);
+            }
+        }
+        float out[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) out[e] = acc[e] * sigmoid_f(acc[e]);
+        store8<T>(y + t * channels + c, out);
+    }
+}
+
+// One thread per (sequence, 8 channels): final state row r of sequence n is
+// input position len - (W - 1) + r of the sequence, taken from the carried-in
+// state (or zero) when that position is negative.
+template <typename T, int W>
+__global__ __launch_bounds__(kConvThreads) void final_state_kernel(
+    const T *__restrict__ x, int64_t x_stride, const int64_t *__restrict__ cu, int N,
+    int64_t channels, int64_t ncb, const T *st_in, T *st_out)
+{
+    const int64_t n = blockIdx.x / ncb;
+    const int64_t cb = blockIdx.x - n * ncb;
+    const int64_t c = cb * kConvChanPerBlock + 8 * (int64_t)threadIdx.x;
+    if (n >= N || c >= channels) return;
+    const int64_t s0 = cu[n], len = cu[n + 1] - s0;
+    float rows[W - 1][8];
+#pragma unroll
+    for (int r = 0; r < W - 1; ++r) {
+        const int64_t p = len - (W - 1) + r;
+        if (p >= 0) {
+            load8(x + (s0 + p) * x_stride + c, rows[r]);
+        } else if (st_in) {
+            load8(st_in + (n * (W - 1) + (W - 1) + p) * channels + c, rows[r]);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) rows[r][e] = 0.f;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < W - 1; ++r) store8<T>(st_out + (n * (W - 1) + r) * channels + c, rows[r]);
+}
+
+template <typename T, int W>
+hipError_t launch_conv_w(const ShortConvArgs &a) {
+    constexpr int S = ConvStrip<T>::S;
+    const int64_t ncb = (a.channels + kConvChanPerBlock - 1) / kConvChanPerBlock;
+    if (a.T > 0) {
+        const int64_t nstrips = (a.T + S - 1) / S;
+        const int64_t nlogical = nstrips * ncb;
+        const int64_t per = (nlogical + 7) / 8;
+        short_conv_kernel<T, W><<<(unsigned)(8 * per), kConvThreads, 0, a.stream>>>(
+            (const T *)a.x, a.x_stride, a.w, a.cu, a.N, a.T, a.channels, nstrips, per, nlogical,
+            (const T *)a.st_in, (T *)a.y);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if constexpr (W > 1) {
+        if (a.st_out) {
+            final_state_kernel<T, W><<<(unsigned)(a.N * ncb), kConvThreads, 0, a.stream>>>(
+                (const T *)a.x, a.x_stride, a.cu, a.N, a.channels, ncb, (const T *)a.st_in,
+                (T *)a.st_out);
+            return hipGetLastError();
+        }
+    }
+    return hipSuccess;
+}
+
+template <typename T>
+hipError_t launch_conv_t(const ShortConvArgs &a) {
+    switch (a.W) {
+        case 1: return launch_conv_w<T, 1>(a);
+        case 2: return launch_conv_w<T, 2>(a);
+        case 3: return launch_conv_w<T, 3>(a);
+        case 4: return launch_conv_w<T, 4>(a);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+int64_t short_conv_blocks(int64_t T, int64_t channels, bool bf16) {
+    const int S = bf16 ? ConvStrip<__bf16>::S : ConvStrip<float>::S;
+    const int64_t ncb = (channels + kConvChanPerBlock - 1) / kConvChanPerBlock;
+    return 8 * ((((T + S - 1) / S) * ncb + 7) / 8);
+}
+
+int64_t short_conv_state_blocks(int64_t N, int64_t channels) {
+    return N * ((channels + kConvChanPerBlock - 1) / kConvChanPerBlock);
+}
+
+hipError_t launch_short_conv(const ShortConvArgs &a) {
+    return a.bf16 ? launch_conv_t<__bf16>(a) : launch_conv_t<float>(a);
+}
+
+}  // namespace kda

@@ -25,7 +25,8 @@ KDA_F32, KDA_BF16 = 0, 1
 EXPORTS = ("kda_version", "kda_status_string", "kda_last_error",
            "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_intra",
            "kda_chunk_fwd_inter", "kda_decode_step", "kda_decode_step_gated",
-           "kda_decode_step_slots", "kda_output_norm_gate", "kda_check_cu_seqlens")
+           "kda_decode_step_slots", "kda_output_norm_gate", "kda_short_conv",
+           "kda_check_cu_seqlens")
 
 NORM_EPS = 1e-5   # default epsilon of the output norm (the pages give none)
 
@@ -64,6 +65,9 @@ _lib.kda_decode_step_slots.argtypes = [_P, _P, _P, _P, _P, _P, _P, _f32, _f32, _
                                        _f32, _P]
 _lib.kda_output_norm_gate.restype = ctypes.c_int
 _lib.kda_output_norm_gate.argtypes = [_P, _P, _P, _f32, _i64, _i32, ctypes.c_int, _P, _P]
+_lib.kda_short_conv.restype = ctypes.c_int
+_lib.kda_short_conv.argtypes = [_P, _i64, _P, _i32, _P, _i32, _i64, _i64, ctypes.c_int, _P, _P,
+                                _P, _P]
 _lib.kda_check_cu_seqlens.restype = ctypes.c_int
 _lib.kda_check_cu_seqlens.argtypes = [_P, _i32, _i64, _P]
 
@@ -292,6 +296,50 @@ def output_norm_gate(o: torch.Tensor, gate: torch.Tensor, norm_weight: torch.Ten
                                    _stream_ptr(o.device))
     _check(st, "kda_output_norm_gate")
     return out
+
+
+def short_conv(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tensor, *,
+               initial_state: Optional[torch.Tensor] = None, output_final_state: bool = False,
+               final_state: Optional[torch.Tensor] = None,
+               out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Front end for one of q, k, v (kda_short_conv): causal depthwise short
+    conv along time over packed sequences, then SiLU.
+
+    x: [T, H, 128] or [T, C] bf16 or fp32; the token axis may be strided (a
+    slice of a fused projection output), the rest must be contiguous.
+    weight: [H, 128, W] or [C, W] fp32 (W <= 4). cu_seqlens: [N+1] int64 on the GPU.
+    initial_state / final_state: [N, W-1, *x.shape[1:]] in x's dtype (the last
+    W - 1 inputs of each sequence so far, oldest first); final_state may be
+    initial_state itself. Returns (y with x's shape, contiguous; final_state or None).
+    """
+    if not isinstance(x, torch.Tensor) or not x.is_cuda:
+        raise RuntimeError("x must be a GPU tensor (libkda has no CPU path)")
+    T = x.shape[0]
+    feat = tuple(x.shape[1:])
+    C = int(math.prod(feat))
+    N = cu_seqlens.numel() - 1
+    if x.dim() < 2 or (T > 0 and x[0].numel() > 0 and not x[0].is_contiguous()):
+        raise ValueError("x must be [T, ...] with contiguous rows")
+    stride = x.stride(0) if T > 1 else C
+    W = weight.shape[-1]
+    _dev(weight, "weight", torch.float32, feat + (W,))
+    _dev(cu_seqlens, "cu_seqlens", torch.int64, (N + 1,))
+    sshape = (N, W - 1) + feat
+    si = so = None
+    if initial_state is not None:
+        si = _dev(initial_state, "initial_state", x.dtype, sshape)
+    if output_final_state or final_state is not None:
+        if final_state is None:
+            final_state = torch.empty(sshape, dtype=x.dtype, device=x.device)
+        so = _dev(final_state, "final_state", x.dtype, sshape)
+    if out is None:
+        out = torch.empty((T,) + feat, dtype=x.dtype, device=x.device)
+    _dev(out, "out", x.dtype, (T,) + feat)
+    st = _lib.kda_short_conv(x.data_ptr() if T else None, int(stride), weight.data_ptr(), int(W),
+                             cu_seqlens.data_ptr(), N, int(T), C, _dt(x), si, so,
+                             out.data_ptr() if T else None, _stream_ptr(x.device))
+    _check(st, "kda_short_conv")
+    return out, final_state
 
 
 def check_cu_seqlens(cu_seqlens: torch.Tensor, total_tokens: int) -> None:

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol(kda):
     assert set(syms) == set(kda.EXPORTS)
     for s in syms:
         assert hasattr(kda.lib, s), s
-    assert kda.version() == 101
+    assert kda.version() == 102
 
 
 def test_status_strings(kda):
@@ -154,6 +154,36 @@ def test_output_norm_gate_zero_rows_enqueues_nothing(kda):
     assert norm_gate_call(kda, rows=0) == 0
     assert norm_gate_call(kda, rows=0, o=None, z=None, w=None, y=None) == 0
     assert norm_gate_call(kda, rows=0, D=64) == 2
+
+
+def short_conv_call(kda, **kw):
+    a = dict(x=FAKE, xs=256, w=FAKE, W=4, cu=FAKE, N=2, T=100, C=256, dt=kda.KDA_BF16,
+             si=None, so=None, y=1 << 30, stream=None)
+    a.update(kw)
+    return kda.lib.kda_short_conv(a["x"], a["xs"], a["w"], a["W"], a["cu"], a["N"], a["T"],
+                                  a["C"], a["dt"], a["si"], a["so"], a["y"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), 1), (dict(T=-1), 1), (dict(W=0), 2), (dict(W=5), 2), (dict(C=0), 1),
+    (dict(C=12), 1), (dict(xs=128), 1), (dict(xs=260), 1), (dict(dt=5), 2), (dict(cu=None), 1),
+    (dict(w=None), 1), (dict(x=None), 1), (dict(y=None), 1), (dict(x=FAKE + 8), 1),
+    (dict(y=FAKE * 4 + 2), 1), (dict(si=FAKE + 4), 1), (dict(w=FAKE + 2), 1), (dict(cu=FAKE + 4), 1),
+    # y overlapping x (bf16 rows of 256 elements: x spans 99 * 512 + 512 bytes)
+    (dict(y=FAKE), 1), (dict(y=FAKE + 99 * 512), 1),
+    # y overlapping a state; the final state overlapping x or part of the initial state
+    (dict(si=1 << 29, y=(1 << 29) + 512), 1), (dict(so=FAKE + 256 * 2 * 3), 1),
+    (dict(si=1 << 29, so=(1 << 29) + 512), 1),
+    (dict(C=1 << 40, xs=1 << 40), 1),
+])
+def test_short_conv_rejects(kda, kw, status):
+    assert short_conv_call(kda, **kw) == status
+    assert kda.lib.kda_last_error()
+
+
+def test_short_conv_nothing_to_do(kda):
+    # no tokens and W = 1 (no state to pass on): OK with no launch, NULL x and y accepted
+    assert short_conv_call(kda, T=0, W=1, x=None, y=None, so=FAKE) == 0
 
 
 def test_workspace_size_arithmetic(kda):
