@@ -47,6 +47,8 @@ KERNEL_SOURCES = {
     "intra_kernel": ("kda_prefill.hip", "kda_common.h", "kda_internal.h"),
     "inter_kernel": ("kda_prefill.hip", "kda_common.h", "kda_internal.h"),
     "decode_step_kernel": ("kda_decode.hip", "kda_common.h", "kda_internal.h"),
+    "short_conv_kernel": ("kda_shortconv.hip", "kda_common.h", "kda_internal.h"),
+    "norm_gate_kernel": ("kda_epilogue.hip", "kda_common.h", "kda_internal.h"),
 }
 
 
@@ -206,6 +208,7 @@ def main():
     }
 
     line["epilogue"] = epilogue_timing(kda, o, dsteps, dA, ddt, dstate, dd.scale, dout)
+    line["front_end"] = front_end_timing(kda, (q, k, v), cu)
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(p, dd)
@@ -253,9 +256,51 @@ def epilogue_timing(kda, o, dsteps, dA, ddt, dstate, dscale, dout, reps=20):
     ms_gated = timed(lambda i: dec(i, True))
     gb = ng_bytes / (ms_ng * 1e-3) / 1e9
     return {"norm_gate_kernel": {"rows": rows, "us": round(ms_ng * 1e3, 2), "alg_bytes": ng_bytes,
-                                 "achieved_GBs": round(gb, 1), "frac": round(gb / HBM_PEAK_GBS, 4)},
+                                 "achieved_GBs": round(gb, 1), "frac": round(gb / HBM_PEAK_GBS, 4),
+                                 "traffic": measured_traffic("norm_gate_kernel")},
             "decode_step_gated_us": round(ms_gated * 1e3, 2),
             "decode_step_plain_us": round(ms_plain * 1e3, 2)}
+
+
+def front_end_timing(kda, qkv, cu, W=4, reps=20):
+    """The q/k/v front end (causal depthwise short conv of W taps + SiLU),
+    measured beside the step and not part of it: one launch each for q, k and v
+    of the prefill workload (T*H*128 bf16 channels in and out, conv states
+    carried in and out), as a model runs it before the recurrence."""
+    import torch
+    import kda_inputs
+    T, H, Dk = qkv[0].shape
+    N = cu.numel() - 1
+    ws, sts, outs, fins = [], [], [], []
+    for i in range(3):
+        _, w, _, st = kda_inputs.make_short_conv([0] * N, H, W, seed=2100 + i)
+        ws.append(w.to(qkv[0].device))
+        sts.append(st.to(qkv[0].device))
+        outs.append(torch.empty_like(qkv[i]))
+        fins.append(torch.empty_like(sts[-1]))
+
+    def run(i):
+        kda.short_conv(qkv[i], ws[i], cu, initial_state=sts[i], final_state=fins[i], out=outs[i])
+
+    for _ in range(3):
+        for i in range(3):
+            run(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * reps + 1)]
+    ev[0].record()
+    for r in range(reps):
+        for i in range(3):
+            run(i)
+            ev[3 * r + i + 1].record()
+    torch.cuda.synchronize()
+    ms = sum(ev[j].elapsed_time(ev[j + 1]) for j in range(3 * reps)) / (3 * reps)
+    C = H * Dk
+    nbytes = 2 * T * C * 2 + C * W * 4 + 2 * N * (W - 1) * C * 2    # x in, y out, weights, states
+    gb = nbytes / (ms * 1e-3) / 1e9
+    return {"short_conv_kernel": {"tokens": T, "channels": C, "W": W, "launches_per_layer": 3,
+                                  "us": round(ms * 1e3, 2), "alg_bytes": nbytes,
+                                  "achieved_GBs": round(gb, 1), "frac": round(gb / HBM_PEAK_GBS, 4),
+                                  "traffic": measured_traffic("short_conv_kernel")}}
 
 
 def copy_calibration(nbytes=1 << 30, reps=3):

@@ -127,6 +127,7 @@ template <> struct Vec8<__bf16> {
         for (int e = 0; e < 8; ++e) v[e] = (__bf16)0.0f;
     }
     __device__ __forceinline__ float operator[](int e) const { return (float)v[e]; }
+    __device__ __forceinline__ void store(__bf16 *p) const { *(bf16x8 *)p = v; }
 };
 template <> struct Vec8<float> {
     f32x4 a, b;
@@ -136,6 +137,10 @@ template <> struct Vec8<float> {
     }
     __device__ __forceinline__ void zero() { a = f32x4{0.f, 0.f, 0.f, 0.f}; b = a; }
     __device__ __forceinline__ float operator[](int e) const { return e < 4 ? a[e] : b[e - 4]; }
+    __device__ __forceinline__ void store(float *p) const {
+        ((f32x4 *)p)[0] = a;
+        ((f32x4 *)p)[1] = b;
+    }
 };
 
 // ---- cross-lane reductions ---------------------------------------------------

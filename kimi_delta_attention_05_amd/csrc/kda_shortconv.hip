@@ -18,17 +18,22 @@
 // strip of S tokens; it loads the strip's S rows plus the W - 1 rows before it
 // into registers (16- or 32-byte loads, consecutive lanes on consecutive
 // channels) and slides the W-row window down the strip, so every input row is
-// read once per strip and every output row written once. HBM-bound. Strips of
-// one channel block follow each other on one XCD (blocks are dealt to the 8
-// XCDs round-robin), so the W - 1 halo rows of a strip were fetched into that
-// XCD's L2 by the strip before it. Tokens within W - 1 of a sequence start take
-// their missing taps from the conv state (a wave-uniform branch).
+// read once per strip, converted to fp32 once, and every output row written
+// once. HBM-bound. Strips of one channel block follow each other on one XCD
+// (blocks are dealt to the 8 XCDs round-robin), so the W - 1 halo rows of a
+// strip were fetched into that XCD's L2 by the strip before it. The few strips
+// that touch a sequence start (or the end of the input) take a general path
+// (chosen per strip, uniform over the workgroup) that gathers each token's
+// window row by row, with the taps before the start read from the conv state.
 //
-// final_state_kernel writes each sequence's final conv state, its last W - 1
-// inputs reaching back into the carried-in state for sequences shorter than
-// W - 1. It runs after short_conv_kernel on the same stream and each thread
-// reads all it needs before writing, so the output state may be the input
-// state (updated in place).
+// Final conv states (each sequence's last W - 1 inputs, reaching back into the
+// carried-in state for sequences shorter than W - 1) are written by the thread
+// that handles the sequence's last token, from its window; empty sequences are
+// passed on by the strip that owns their start offset. When the final state
+// replaces the carried-in state in place, strips could overwrite a state that
+// another strip still has to read, so final_state_kernel writes them instead,
+// after short_conv_kernel on the same stream, each thread reading all it needs
+// before writing.
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -40,7 +45,7 @@ constexpr int kConvThreads = 256;
 constexpr int kConvChanPerBlock = 8 * kConvThreads;
 
 template <typename T> struct ConvStrip;
-template <> struct ConvStrip<__bf16> { static constexpr int S = 32; };
+template <> struct ConvStrip<__bf16> { static constexpr int S = 16; };
 template <> struct ConvStrip<float> { static constexpr int S = 16; };
 
 // Sequence of token t: the n in [0, N) with cu[n] <= t < cu[n + 1] (empty
@@ -62,12 +67,44 @@ __device__ __forceinline__ int64_t xcd_logical(int64_t b, int64_t per) {
     return (b & 7) * per + (b >> 3);
 }
 
+// silu(u) = u / (1 + e^-u): exp2 of -u log2(e), then the reciprocal. For very
+// negative u the exponential overflows to +inf and the reciprocal to 0, which
+// is the limit, so no range split is needed.
+__device__ __forceinline__ float silu_f(float u) {
+    return u * fast_rcp(1.0f + fast_exp2(-u * kLog2e));
+}
+
+template <int W>
+__device__ __forceinline__ void conv_silu_store_prep(const float (&wt)[W][8], const float (&win)[W][8],
+                                                     float (&out)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        float acc = wt[W - 1][e] * win[W - 1][e];
+#pragma unroll
+        for (int i = 0; i < W - 1; ++i) acc = fmaf(wt[i][e], win[i][e], acc);
+        out[e] = silu_f(acc);
+    }
+}
+
+// Final conv state of an empty sequence m: its carried-in state, or zeros.
+template <typename T, int W>
+__device__ __forceinline__ void pass_state_on_w(const T *st_in, T *st_out, int m, int64_t channels,
+                                                int64_t c) {
+#pragma unroll
+    for (int r = 0; r < W - 1; ++r) {
+        const int64_t off = ((int64_t)m * (W - 1) + r) * channels + c;
+        Vec8<T> v;
+        if (st_in) v.load(st_in + off); else v.zero();
+        v.store(st_out + off);
+    }
+}
+
 template <typename T, int W>
 __global__ __launch_bounds__(kConvThreads) void short_conv_kernel(
     const T *__restrict__ x, int64_t x_stride, const float *__restrict__ w,
     const int64_t *__restrict__ cu, int N, int64_t T_total, int64_t channels,
     int64_t nstrips, int64_t per_xcd, int64_t nlogical,
-    const T *__restrict__ st_in, T *__restrict__ y)
+    const T *__restrict__ st_in, T *__restrict__ st_out, T *__restrict__ y)
 {
     constexpr int S = ConvStrip<T>::S;
     const int64_t L = xcd_logical(blockIdx.x, per_xcd);
@@ -85,57 +122,98 @@ __global__ __launch_bounds__(kConvThreads) void short_conv_kernel(
         for (int i = 0; i < W; ++i) wt[i][e] = w[(c + e) * W + i];
     }
 
-    // rows t0 - (W - 1) .. t0 + S - 1; rows outside [0, T) read as zero and
-    // are never used for an output (a row before 0 lies before the first
-    // sequence start; a row at or past T belongs to no output token)
-    Vec8<T> xr[S + W - 1];            // kept packed until used
+    int n = seq_of(cu, N, t0);
+    int64_t s0 = cu[n], s1 = cu[n + 1];
+
+    if (t0 + S < T_total && t0 - s0 >= W - 1 && t0 + S <= s1) {
+        // Every window of the strip lies inside one sequence: a plain sliding
+        // window. Rows t0 - (W - 1) .. t0 + S - 1 are loaded up front (kept
+        // packed) and each is converted to fp32 once, as it enters the window.
+        Vec8<T> xr[S + W - 1];
+#pragma unroll
+        for (int r = 0; r < S + W - 1; ++r) xr[r].load(x + (t0 - (W - 1) + r) * x_stride + c);
+        // keep every load of the strip ahead of the arithmetic: left to itself
+        // the scheduler sinks them next to their uses to save registers, which
+        // exposes one memory latency per token
+        __builtin_amdgcn_sched_barrier(0);
+        float win[W][8];
+#pragma unroll
+        for (int i = 0; i < W - 1; ++i) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) win[i][e] = xr[i][e];
+        }
+#pragma unroll
+        for (int j = 0; j < S; ++j) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) win[W - 1][e] = xr[j + W - 1][e];
+            float out[8];
+            conv_silu_store_prep<W>(wt, win, out);
+            store8<T>(y + (t0 + j) * channels + c, out);
+#pragma unroll
+            for (int i = 0; i < W - 1; ++i) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e) win[i][e] = win[i + 1][e];
+            }
+        }
+        // the strip ends its sequence: the final conv state is its last W - 1 rows
+        if (st_out && t0 + S == s1) {
+#pragma unroll
+            for (int r = 0; r < W - 1; ++r) xr[S + r].store(st_out + ((int64_t)n * (W - 1) + r) * channels + c);
+        }
+        return;
+    }
+
+    // General strip (a sequence starts within W - 1 rows before or inside it,
+    // or it is the last, partial strip): the strip's rows are still loaded up
+    // front (rows outside [0, T) read as zero and are never used), and each
+    // token assembles its window tap by tap; positions before its sequence's
+    // start read the conv state row (p - s0 + W - 1) of that sequence, or zero.
+    Vec8<T> xr[S + W - 1];
 #pragma unroll
     for (int r = 0; r < S + W - 1; ++r) {
         const int64_t t = t0 - (W - 1) + r;
         if (t >= 0 && t < T_total) xr[r].load(x + t * x_stride + c);
         else xr[r].zero();
     }
-
-    int n = seq_of(cu, N, t0);
-    int64_t s0 = cu[n], s1 = cu[n + 1];
+    if (st_out) {
+        // empty sequences that start at t0 lie before n (the search skips them)
+        for (int m = n - 1; m >= 0 && cu[m] == t0; --m) pass_state_on_w<T, W>(st_in, st_out, m, channels, c);
+    }
 #pragma unroll
     for (int j = 0; j < S; ++j) {
         const int64_t t = t0 + j;
         if (t >= T_total) break;
-        while (t >= s1) { ++n; s0 = s1; s1 = cu[n + 1]; }
-        float acc[8];
+        while (t >= s1) {
+            ++n; s0 = s1; s1 = cu[n + 1];
+            if (st_out && s1 == s0) pass_state_on_w<T, W>(st_in, st_out, n, channels, c);   // empty
+        }
+        float win[W][8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) acc[e] = wt[W - 1][e] * xr[j + W - 1][e];
-        if (t - s0 >= W - 1) {
+        for (int i = 0; i < W; ++i) {
+            const int64_t p = t - (W - 1) + i;
+            if (p >= s0) {
 #pragma unroll
-            for (int i = 0; i < W - 1; ++i) {
+                for (int e = 0; e < 8; ++e) win[i][e] = xr[j + i][e];
+            } else if (st_in) {
+                load8(st_in + ((int64_t)n * (W - 1) + (p - s0 + W - 1)) * channels + c, win[i]);
+            } else {
 #pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] = fmaf(wt[i][e], xr[j + i][e], acc[e]);
-            }
-        } else {
-            // within W - 1 of the sequence start: taps before it read the
-            // sequence's conv state row (p - s0 + W - 1), or zero
-#pragma unroll
-            for (int i = 0; i < W - 1; ++i) {
-                const int64_t p = t - (W - 1) + i;
-                float hv[8];
-                if (p >= s0) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) hv[e] = xr[j + i][e];
-                } else if (st_in) {
-                    load8(st_in + ((int64_t)n * (W - 1) + (p - s0 + W - 1)) * channels + c, hv);
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) hv[e] = 0.f;
-                }
-#pragma unroll
-                for (int e = 0; e < 8; ++e) acc[e] = fmaf(wt[i][e], hv[e], acc[e]);
+                for (int e = 0; e < 8; ++e) win[i][e] = 0.f;
             }
         }
         float out[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) out[e] = acc[e] * sigmoid_f(acc[e]);
+        conv_silu_store_prep<W>(wt, win, out);
         store8<T>(y + t * channels + c, out);
+        if (st_out && t == s1 - 1) {
+            // last token of its sequence: the final conv state is the window's
+            // last W - 1 rows (reaching into the carried-in state if short)
+#pragma unroll
+            for (int r = 0; r < W - 1; ++r) store8<T>(st_out + ((int64_t)n * (W - 1) + r) * channels + c, win[r + 1]);
+        }
+    }
+    if (st_out && t0 + S >= T_total) {
+        // the last strip: sequences after the last token's one are empty
+        for (int m = n + 1; m < N; ++m) pass_state_on_w<T, W>(st_in, st_out, m, channels, c);
     }
 }
 
@@ -173,18 +251,22 @@ template <typename T, int W>
 hipError_t launch_conv_w(const ShortConvArgs &a) {
     constexpr int S = ConvStrip<T>::S;
     const int64_t ncb = (a.channels + kConvChanPerBlock - 1) / kConvChanPerBlock;
+    // the final conv state is written by the conv kernel itself unless it
+    // replaces the carried-in state in place (other strips may still read
+    // that) or there are no tokens: then a second kernel writes it afterwards
+    const bool fused_state = W > 1 && a.st_out && a.st_out != a.st_in && a.T > 0;
     if (a.T > 0) {
         const int64_t nstrips = (a.T + S - 1) / S;
         const int64_t nlogical = nstrips * ncb;
         const int64_t per = (nlogical + 7) / 8;
         short_conv_kernel<T, W><<<(unsigned)(8 * per), kConvThreads, 0, a.stream>>>(
             (const T *)a.x, a.x_stride, a.w, a.cu, a.N, a.T, a.channels, nstrips, per, nlogical,
-            (const T *)a.st_in, (T *)a.y);
+            (const T *)a.st_in, fused_state ? (T *)a.st_out : nullptr, (T *)a.y);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
     if constexpr (W > 1) {
-        if (a.st_out) {
+        if (a.st_out && !fused_state) {
             final_state_kernel<T, W><<<(unsigned)(a.N * ncb), kConvThreads, 0, a.stream>>>(
                 (const T *)a.x, a.x_stride, a.cu, a.N, a.channels, ncb, (const T *)a.st_in,
                 (T *)a.st_out);

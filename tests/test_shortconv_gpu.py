@@ -69,6 +69,25 @@ def test_short_conv_ragged_matches_oracle(kda, dtype, W, with_state):
     np.testing.assert_array_equal(to_np(f), fref)
 
 
+@pytest.mark.parametrize("lengths", [
+    [0, 0, 16, 0, 16, 0, 5, 0],     # empty sequences before the first token, at strip starts, last
+    [48, 20],                       # a sequence ending exactly at a strip end (not the last strip)
+    [48],                           # ... and at the end of the input
+    [16, 16, 16, 3],                # every sequence start on a strip start
+    [2, 1, 1, 2, 1, 40],            # starts closer together than the kernel size
+])
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("W", [2, 4])
+def test_short_conv_sequence_edges(kda, lengths, dtype, W):
+    for with_state in (False, True):
+        x, w, cu, st = kda_inputs.make_short_conv(lengths, 2, W, token_dtype=dtype,
+                                                  with_state=with_state, seed=60 + len(lengths))
+        y, f = run(kda, x, w, cu, st)
+        ref, fref = oracle.short_conv_silu(x, w, cu, state=st)
+        assert check_y(y, ref, x, w, st) <= 1.0, (lengths, with_state)
+        np.testing.assert_array_equal(to_np(f), fref)
+
+
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_short_conv_several_channel_blocks(kda, dtype):
     # 20 heads = 2560 channels: one full block of 2048 channels and a partial one
