@@ -12,7 +12,9 @@ Formulations here:
   * `output_norm_gate` — the output epilogue (epilogue.py): per-head RMS norm
     and sigmoid output gate applied to the recurrence's outputs;
   * `short_conv_silu` — the front end (shortconv.py): causal depthwise short
-    convolution + SiLU applied to q, k, v before the recurrence.
+    convolution + SiLU applied to q, k, v before the recurrence;
+  * `kda_backward` — the gradients of the recurrence (backward.py) for an
+    output adjoint and an optional final-state adjoint.
 """
 from __future__ import annotations
 
@@ -168,6 +170,7 @@ def kda_decode_steps(steps, state, A_log, dt_bias, *, scale: float,
 from .chunked import kda_chunked  # noqa: E402  (pure numpy, no library)
 from .epilogue import output_norm_gate  # noqa: E402  (pure numpy, no library)
 from .shortconv import short_conv_silu  # noqa: E402  (pure numpy, no library)
+from .backward import kda_backward  # noqa: E402  (pure numpy, no library)
 
 __all__ = ["build", "kda_recurrent", "kda_decode_steps", "kda_chunked",
-           "output_norm_gate", "short_conv_silu", "max_threads", "LOWER_BOUND", "L2_EPS"]
+           "output_norm_gate", "short_conv_silu", "kda_backward", "max_threads", "LOWER_BOUND", "L2_EPS"]
