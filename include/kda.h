@@ -278,6 +278,40 @@ kda_status_t kda_short_conv(const void *x, int64_t x_stride, const float *weight
                             int64_t channels, kda_dtype_t dtype, const void *state_in,
                             void *state_out, void *y, void *stream);
 /*
+ * Training backward of the recurrence (FlashInfer kda_backward page,
+ * "Supported contract": gradients for q, k, v, the raw gate, raw beta, A_log,
+ * dt_bias and the initial state, given the output adjoint; its persistent
+ * forward-checkpoint + reverse design). With S the state, the forward per
+ * token being S' = S diag(alpha), u = b (v - S' kh), S <- S' + u kh^T,
+ * o = S qh, the gradients are those of the loss sum(o * d_o) +
+ * sum(final_state * d_final_state) with respect to every input, computed in
+ * fp32 by a reverse sweep over states recomputed from chunk-boundary
+ * checkpoints (every 16 tokens of each sequence, kept in the workspace).
+ *
+ * Inputs as for kda_chunk_fwd (q, k, v in in_dtype; g, beta_raw, A_log,
+ * dt_bias, initial_state fp32; initial_state may be NULL = zero), plus
+ *   d_o           : [T, H, 128] output adjoint in do_dtype
+ *   d_final_state : [N, H, 128, 128] fp32 adjoint of the final state, or NULL (zero)
+ * Outputs, all fp32 and fully overwritten:
+ *   dq, dk, dg    : [T, H, 128]      dv : [T, H, 128]      dbeta : [T, H] (w.r.t. beta_raw)
+ *   dA_log        : [H]              ddt_bias : [H, 128]   (summed over all sequences)
+ *   d_initial_state : [N, H, 128, 128], or NULL to skip
+ * workspace: kda_backward_workspace_size() bytes, 256-byte aligned, caller
+ * owned; nothing in it needs initialising. H <= 65535. Sums run in a fixed
+ * order (no atomics): results repeat bit for bit.
+ */
+size_t kda_backward_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H,
+                                   int32_t K, int32_t V);
+kda_status_t kda_backward(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta_raw, const float *A_log, const float *dt_bias,
+                          float scale, float lower_bound, const int64_t *cu_seqlens,
+                          int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t K, int32_t V,
+                          kda_dtype_t in_dtype, const float *initial_state, const void *d_o,
+                          kda_dtype_t do_dtype, const float *d_final_state, float *dq, float *dk,
+                          float *dv, float *dg, float *dbeta, float *dA_log, float *ddt_bias,
+                          float *d_initial_state, void *workspace, size_t workspace_bytes,
+                          void *stream);
+/*
  * Opt-in check of packed offsets (FlashInfer kda_backward page: offsets are
  * validated by one eager synchronisation, the launch path then trusts them).
  * Copies cu_seqlens to the host on `stream`, synchronises that stream and

@@ -107,7 +107,7 @@ kda_status_t decode_step_impl(const void *q, const void *k, const void *v,
 
 extern "C" {
 
-int kda_version(void) { return 102; }
+int kda_version(void) { return 103; }
 
 const char *kda_status_string(kda_status_t s) {
     switch (s) {
@@ -341,6 +341,73 @@ kda_status_t kda_short_conv(const void *x, int64_t x_stride, const float *weight
     a.bf16 = bf16; a.stream = (hipStream_t)stream;
     hipError_t e = kda::launch_short_conv(a);
     if (e != hipSuccess) return hip_fail(e, "kda_short_conv launch");
+    return ok();
+}
+
+size_t kda_backward_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H,
+                                   int32_t K, int32_t V) {
+    if (total_tokens < 0 || num_seqs < 1 || H < 1 || H > 65535) {
+        fail(KDA_ERR_INVALID_ARG, "need total_tokens >= 0, num_seqs >= 1, 1 <= H <= 65535");
+        return 0;
+    }
+    if (K != 128 || V != 128) { fail(KDA_ERR_UNSUPPORTED, "only K = V = 128 is supported"); return 0; }
+    g_last_error.clear();
+    return kda::backward_layout(total_tokens, num_seqs, H).total;
+}
+
+kda_status_t kda_backward(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta_raw, const float *A_log, const float *dt_bias,
+                          float scale, float lower_bound, const int64_t *cu_seqlens,
+                          int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t K, int32_t V,
+                          kda_dtype_t in_dtype, const float *initial_state, const void *d_o,
+                          kda_dtype_t do_dtype, const float *d_final_state, float *dq, float *dk,
+                          float *dv, float *dg, float *dbeta, float *dA_log, float *ddt_bias,
+                          float *d_initial_state, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+    if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 1");
+    if (total_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens must be >= 0");
+    if (H > 65535) return fail(KDA_ERR_INVALID_ARG, "H must lie in [1, 65535]");
+    kda_status_t st = check_common(H, K, V, scale, lower_bound, in_dtype, do_dtype);
+    if (st != KDA_OK) return st;
+    if (!cu_seqlens || !A_log || !dt_bias || !dA_log || !ddt_bias)
+        return fail(KDA_ERR_INVALID_ARG, "cu_seqlens, A_log, dt_bias, dA_log and ddt_bias must not be NULL");
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta_raw || !d_o || !dq || !dk || !dv ||
+                             !dg || !dbeta))
+        return fail(KDA_ERR_INVALID_ARG, "a token tensor or its gradient is NULL");
+    if ((int64_t)num_seqs * H > (int64_t)1 << 28)
+        return fail(KDA_ERR_INVALID_ARG, "num_seqs * H too large");
+    if ((total_tokens + 15) / 16 > (int64_t)0x7fffffff)
+        return fail(KDA_ERR_INVALID_ARG, "total_tokens too large");
+    const size_t need = kda::backward_layout(total_tokens, num_seqs, H).total;
+    if (!workspace || workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes, got " +
+                                           std::to_string(workspace_bytes));
+    if (((uintptr_t)workspace & 255) != 0)
+        return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    st = check_aligned16({{q, "q"}, {k, "k"}, {v, "v"}, {g, "g"}, {dt_bias, "dt_bias"},
+                          {initial_state, "initial_state"}, {d_o, "d_o"},
+                          {d_final_state, "d_final_state"}, {dq, "dq"}, {dk, "dk"}, {dv, "dv"},
+                          {dg, "dg"}, {ddt_bias, "ddt_bias"}, {d_initial_state, "d_initial_state"}});
+    if (st != KDA_OK) return st;
+    if (((uintptr_t)beta_raw & 3) != 0 || ((uintptr_t)A_log & 3) != 0 ||
+        ((uintptr_t)dbeta & 3) != 0 || ((uintptr_t)dA_log & 3) != 0)
+        return fail(KDA_ERR_INVALID_ARG, "beta_raw, A_log, dbeta and dA_log must be 4-byte aligned");
+
+    const kda::BackwardLayout lay = kda::backward_layout(total_tokens, num_seqs, H);
+    kda::BackwardArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta_raw = beta_raw; a.A_log = A_log; a.dt_bias = dt_bias;
+    a.scale = scale; a.lower_bound = lower_bound; a.cu = cu_seqlens; a.N = num_seqs; a.H = H;
+    a.T = total_tokens; a.in_bf16 = in_dtype == KDA_BF16; a.do_bf16 = do_dtype == KDA_BF16;
+    a.h0 = initial_state; a.dout = d_o; a.dht = d_final_state;
+    a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dA_log = dA_log;
+    a.ddt_bias = ddt_bias; a.dh0 = d_initial_state;
+    unsigned char *ws = (unsigned char *)workspace;
+    a.ckpt = (float *)ws;
+    a.part = (float *)(ws + lay.ckpt_bytes);
+    a.pp = (float *)(ws + lay.ckpt_bytes + lay.part_bytes);
+    a.stream = (hipStream_t)stream;
+    hipError_t e = kda::launch_backward(a);
+    if (e != hipSuccess) return hip_fail(e, "kda_backward launch");
     return ok();
 }
 

@@ -130,6 +130,30 @@ struct ShortConvArgs {
     hipStream_t stream = nullptr;
 };
 
+// Training backward of the recurrence (all gradients fp32).
+struct BackwardArgs {
+    const void *q, *k, *v;              // [T, H, 128] input dtype
+    const float *g, *beta_raw, *A_log, *dt_bias;
+    float scale, lower_bound;
+    const int64_t *cu;                  // [N + 1]
+    int N, H;
+    int64_t T;
+    bool in_bf16, do_bf16;
+    const float *h0;                    // [N, H, 128, 128] or NULL (zero)
+    const void *dout;                   // [T, H, 128] output adjoint
+    const float *dht;                   // [N, H, 128, 128] final-state adjoint or NULL (zero)
+    float *dq, *dk, *dv, *dg, *dbeta, *dA_log, *ddt_bias;
+    float *dh0;                         // or NULL
+    float *ckpt, *part, *pp;            // workspace pieces (backward_layout)
+    hipStream_t stream;
+};
+
+struct BackwardLayout {
+    size_t ckpt_bytes, part_bytes, pp_bytes, total;
+};
+BackwardLayout backward_layout(int64_t T, int N, int H);
+hipError_t launch_backward(const BackwardArgs &a);
+
 // Workgroups of the two front-end launches (for the host's size checks).
 int64_t short_conv_blocks(int64_t T, int64_t channels, bool bf16);
 int64_t short_conv_state_blocks(int64_t N, int64_t channels);

@@ -26,7 +26,7 @@ EXPORTS = ("kda_version", "kda_status_string", "kda_last_error",
            "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_intra",
            "kda_chunk_fwd_inter", "kda_decode_step", "kda_decode_step_gated",
            "kda_decode_step_slots", "kda_output_norm_gate", "kda_short_conv",
-           "kda_check_cu_seqlens")
+           "kda_backward_workspace_size", "kda_backward", "kda_check_cu_seqlens")
 
 NORM_EPS = 1e-5   # default epsilon of the output norm (the pages give none)
 
@@ -68,6 +68,12 @@ _lib.kda_output_norm_gate.argtypes = [_P, _P, _P, _f32, _i64, _i32, ctypes.c_int
 _lib.kda_short_conv.restype = ctypes.c_int
 _lib.kda_short_conv.argtypes = [_P, _i64, _P, _i32, _P, _i32, _i64, _i64, ctypes.c_int, _P, _P,
                                 _P, _P]
+_lib.kda_backward_workspace_size.restype = _sz
+_lib.kda_backward_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32]
+_lib.kda_backward.restype = ctypes.c_int
+_lib.kda_backward.argtypes = [_P, _P, _P, _P, _P, _P, _P, _f32, _f32, _P, _i32, _i64, _i32, _i32,
+                              _i32, ctypes.c_int, _P, _P, ctypes.c_int, _P, _P, _P, _P, _P, _P,
+                              _P, _P, _P, _P, _sz, _P]
 _lib.kda_check_cu_seqlens.restype = ctypes.c_int
 _lib.kda_check_cu_seqlens.argtypes = [_P, _i32, _i64, _P]
 
@@ -340,6 +346,63 @@ def short_conv(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tensor, 
                              out.data_ptr() if T else None, _stream_ptr(x.device))
     _check(st, "kda_short_conv")
     return out, final_state
+
+
+def backward_workspace_size(total_tokens: int, num_seqs: int, H: int) -> int:
+    n = int(_lib.kda_backward_workspace_size(int(total_tokens), int(num_seqs), int(H), 128, 128))
+    if n == 0:
+        raise ValueError("kda_backward_workspace_size: " + _lib.kda_last_error().decode())
+    return n
+
+
+def backward(q, k, v, g, beta_raw, A_log, dt_bias, cu_seqlens, d_o, *, scale: float = None,
+             lower_bound: float = -5.0, initial_state: Optional[torch.Tensor] = None,
+             d_final_state: Optional[torch.Tensor] = None, need_d_initial_state: bool = True,
+             workspace: Optional[Workspace] = None) -> dict:
+    """Training backward of the recurrence (kda_backward): gradients of
+    sum(o * d_o) + sum(final_state * d_final_state) w.r.t. every input.
+
+    Inputs as chunk_fwd; d_o: [T, H, 128] bf16 or fp32; d_final_state: [N, H, 128, 128]
+    fp32 or None. Returns a dict of fp32 tensors dq, dk, dv, dg [T, H, 128], dbeta [T, H],
+    dA_log [H], ddt_bias [H, 128] and dh0 [N, H, 128, 128] (None unless requested).
+    """
+    T, H, K = q.shape
+    N = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    _dev(q, "q", shape=(T, H, K))
+    _dev(k, "k", dtype=q.dtype, shape=(T, H, K))
+    _dev(v, "v", dtype=q.dtype, shape=(T, H, K))
+    _dev(g, "g", torch.float32, (T, H, K))
+    _dev(beta_raw, "beta_raw", torch.float32, (T, H))
+    _dev(A_log, "A_log", torch.float32, (H,))
+    _dev(dt_bias, "dt_bias", torch.float32, (H, K))
+    _dev(cu_seqlens, "cu_seqlens", torch.int64, (N + 1,))
+    _dev(d_o, "d_o", shape=(T, H, K))
+    dev = q.device
+    h0p = None if initial_state is None else _dev(initial_state, "initial_state", torch.float32,
+                                                  (N, H, K, K))
+    dhtp = None if d_final_state is None else _dev(d_final_state, "d_final_state", torch.float32,
+                                                   (N, H, K, K))
+    f32 = dict(dtype=torch.float32, device=dev)
+    out = dict(dq=torch.empty((T, H, K), **f32), dk=torch.empty((T, H, K), **f32),
+               dv=torch.empty((T, H, K), **f32), dg=torch.empty((T, H, K), **f32),
+               dbeta=torch.empty((T, H), **f32), dA_log=torch.empty((H,), **f32),
+               ddt_bias=torch.empty((H, K), **f32),
+               dh0=torch.empty((N, H, K, K), **f32) if need_d_initial_state else None)
+    need = backward_workspace_size(T, N, H)
+    ws = (workspace or Workspace(dev)).get(need)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = _lib.kda_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                           beta_raw.data_ptr(), A_log.data_ptr(), dt_bias.data_ptr(), float(scale),
+                           float(lower_bound), cu_seqlens.data_ptr(), N, T, H, K, K, _dt(q), h0p,
+                           d_o.data_ptr(), _dt(d_o), dhtp, out["dq"].data_ptr(),
+                           out["dk"].data_ptr(), out["dv"].data_ptr(), out["dg"].data_ptr(),
+                           out["dbeta"].data_ptr(), out["dA_log"].data_ptr(),
+                           out["ddt_bias"].data_ptr(), ptr(out["dh0"]), ws.data_ptr(), ws.numel(),
+                           _stream_ptr(dev))
+    _check(st, "kda_backward")
+    return out
 
 
 def check_cu_seqlens(cu_seqlens: torch.Tensor, total_tokens: int) -> None:

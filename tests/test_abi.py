@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol(kda):
     assert set(syms) == set(kda.EXPORTS)
     for s in syms:
         assert hasattr(kda.lib, s), s
-    assert kda.version() == 102
+    assert kda.version() == 103
 
 
 def test_status_strings(kda):
@@ -184,6 +184,41 @@ def test_short_conv_rejects(kda, kw, status):
 def test_short_conv_nothing_to_do(kda):
     # no tokens and W = 1 (no state to pass on): OK with no launch, NULL x and y accepted
     assert short_conv_call(kda, T=0, W=1, x=None, y=None, so=FAKE) == 0
+
+
+def backward_call(kda, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, scale=0.088,
+             lb=-5.0, cu=FAKE, N=1, T=17, H=1, K=128, V=128, dt=kda.KDA_BF16, h0=None, do=FAKE,
+             dodt=kda.KDA_BF16, dht=None, dq=FAKE, dk=FAKE, dv=FAKE, dg=FAKE, dbeta=FAKE,
+             dA=FAKE, ddt=FAKE, dh0=None, ws=0x100000, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return kda.lib.kda_backward(a["q"], a["k"], a["v"], a["g"], a["beta"], a["A_log"],
+                                a["dt_bias"], a["scale"], a["lb"], a["cu"], a["N"], a["T"], a["H"],
+                                a["K"], a["V"], a["dt"], a["h0"], a["do"], a["dodt"], a["dht"],
+                                a["dq"], a["dk"], a["dv"], a["dg"], a["dbeta"], a["dA"], a["ddt"],
+                                a["dh0"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), 1), (dict(T=-1), 1), (dict(H=0), 1), (dict(H=65536), 1), (dict(K=64), 2),
+    (dict(dt=4), 2), (dict(dodt=4), 2), (dict(scale=0.0), 1), (dict(lb=1.0), 1),
+    (dict(cu=None), 1), (dict(dA=None), 1), (dict(ddt=None), 1), (dict(q=None), 1),
+    (dict(do=None), 1), (dict(dq=None), 1), (dict(dbeta=None), 1), (dict(ws=None), 3),
+    (dict(wsb=1024), 3), (dict(ws=0x100040), 3), (dict(dq=FAKE + 8), 1), (dict(dh0=FAKE + 4), 1),
+    (dict(dbeta=FAKE + 2), 1), (dict(N=1 << 20, H=1024), 1),
+])
+def test_backward_rejects(kda, kw, status):
+    assert backward_call(kda, **kw) == status
+    assert kda.lib.kda_last_error()
+
+
+def test_backward_workspace_size(kda):
+    # checkpoints (T/16 + N slots of 64 KiB per head) + per-block partials + parameter sums
+    a = kda.backward_workspace_size(8192, 1, 96)
+    assert a >= (8192 // 16 + 1) * 96 * 65536 + 8192 * 96 * 8 * 385 * 4
+    assert a % 256 == 0
+    with pytest.raises(ValueError):
+        kda.backward_workspace_size(16, 0, 1)
 
 
 def test_workspace_size_arithmetic(kda):
