@@ -209,6 +209,7 @@ def main():
 
     line["epilogue"] = epilogue_timing(kda, o, dsteps, dA, ddt, dstate, dd.scale, dout)
     line["front_end"] = front_end_timing(kda, (q, k, v), cu)
+    line["backward"] = backward_timing(kda, p, (q, k, v, g, beta_raw, A_log, dt_bias, cu, h0))
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(p, dd)
@@ -301,6 +302,47 @@ def front_end_timing(kda, qkv, cu, W=4, reps=20):
                                   "us": round(ms * 1e3, 2), "alg_bytes": nbytes,
                                   "achieved_GBs": round(gb, 1), "frac": round(gb / HBM_PEAK_GBS, 4),
                                   "traffic": measured_traffic("short_conv_kernel")}}
+
+
+FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector
+
+
+def backward_timing(kda, p, dev_inputs, reps=3):
+    """The training backward of the recurrence (kda_backward) on the prefill
+    workload, measured beside the step and not part of it: output adjoint bf16
+    [T, H, 128], final-state adjoint fp32, every gradient fp32."""
+    import torch
+    q, k, v, g, beta_raw, A_log, dt_bias, cu, h0 = dev_inputs
+    T, H, Dk = q.shape
+    N = cu.numel() - 1
+    gen = torch.Generator().manual_seed(2200)
+    d_o = torch.randn(T, H, Dk, generator=gen).to(torch.bfloat16).to(q.device)
+    dht = (torch.randn(N, H, Dk, Dk, generator=gen) * 0.1).to(q.device)
+    ws = kda.Workspace(q.device)
+
+    def run():
+        return kda.backward(q, k, v, g, beta_raw, A_log, dt_bias, cu, d_o, scale=p.scale,
+                            initial_state=h0, d_final_state=dht, workspace=ws)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    th = T * H
+    # arithmetic per token-head: 25 flops per state element (5 for the checkpoint
+    # forward, 5 for the recomputation, 15 for the reverse step) over 128 x 128
+    flops = th * 25 * Dk * Dk
+    tf = flops / (ms * 1e-3) / 1e12
+    return {"ms": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "workspace_bytes": kda.backward_workspace_size(T, N, H),
+            "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_VALU_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4),
+                         "alg_flops": flops}}
 
 
 def copy_calibration(nbytes=1 << 30, reps=3):

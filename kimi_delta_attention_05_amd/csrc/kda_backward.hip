@@ -64,6 +64,16 @@ __device__ __forceinline__ void store_lane8(float *row, int j, const float (&x)[
     *(f32x4 *)(row + 64 + 4 * j) = f32x4{x[4], x[5], x[6], x[7]};
 }
 
+// Sum over the four 16-lane rows of a wave (every lane gets the sum): the
+// gfx950 permlane swaps exchange lanes l and l ^ 32, then l and l ^ 16, in
+// VALU (no LDS round trip).
+__device__ __forceinline__ float rows4_sum(float x) {
+    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 // Workgroup b -> (sequence*H + head, row block). The 8 row blocks of one
 // (sequence, head) share its token data, so they go to one XCD (blocks are
 // dealt to the 8 XCDs round-robin by index).
@@ -181,7 +191,8 @@ __global__ __launch_bounds__(256) void bwd_reverse_kernel(
 
     __shared__ float sKh[kCk][kHeadDim], sQh[kCk][kHeadDim], sAl[kCk][kHeadDim];
     __shared__ float sB[kCk], sV[kCk][kBRows], sDo[kCk][kBRows], sU[kCk][kBRows], sW[kCk][kBRows];
-    __shared__ float sRed[2][kBRows][kPartCols];
+    // per-wave sums (over the wave's 4 rows) of the partials of 8 tokens
+    __shared__ float sRed[8][4][kPartCols];
 
     float dS[8];
     if (dht) load_lane8(dht + ((size_t)nh * kHeadDim + grow) * kHeadDim, j, dS);
@@ -274,22 +285,37 @@ __global__ __launch_bounds__(256) void bwd_reverse_kernel(
                 }
                 const size_t tb = ((size_t)t * H + h) * kHeadDim;
                 if (j == 0) dv[tb + grow] = bdu;
-                // row sums of the partials over the block's 16 rows
-                float(*red)[kPartCols] = sRed[i & 1];
+                // sums over the wave's 4 rows, kept per wave in LDS
+                float *red = &sRed[i & 7][wave][0];
+                float pb = rows4_sum(du * w);
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
-                    red[row][chan(j, e)] = pq[e];
-                    red[row][kHeadDim + chan(j, e)] = pk[e];
-                    red[row][2 * kHeadDim + chan(j, e)] = pa[e];
+                    pq[e] = rows4_sum(pq[e]);
+                    pk[e] = rows4_sum(pk[e]);
+                    pa[e] = rows4_sum(pa[e]);
                 }
-                if (j == 0) red[row][3 * kHeadDim] = du * w;
-                lds_barrier();
-                float *dst = part + ((size_t)((size_t)t * H + h) * kNVB + vb) * kPartCols;
-                for (int col = threadIdx.x; col < kPartCols; col += 256) {
-                    float sum = 0.f;
+                if (lane < 16) {
 #pragma unroll
-                    for (int rr = 0; rr < kBRows; ++rr) sum += red[rr][col];
-                    dst[col] = sum;
+                    for (int e = 0; e < 8; ++e) {
+                        red[chan(j, e)] = pq[e];
+                        red[kHeadDim + chan(j, e)] = pk[e];
+                        red[2 * kHeadDim + chan(j, e)] = pa[e];
+                    }
+                    if (j == 0) red[3 * kHeadDim] = pb;
+                }
+                // after tokens 8..L-1 and after tokens 0..: add the 4 waves'
+                // sums and store the block's row sums of the partials
+                if (i == 8 || i == 0) {
+                    const int ntok = (i == 8) ? L - 8 : (L < 8 ? L : 8);
+                    lds_barrier();
+                    for (int idx = threadIdx.x; idx < ntok * kPartCols; idx += 256) {
+                        const int ti = idx / kPartCols, col = idx - ti * kPartCols;
+                        const float sum = (sRed[ti][0][col] + sRed[ti][1][col]) +
+                                          (sRed[ti][2][col] + sRed[ti][3][col]);
+                        const size_t tt = (size_t)(c0 + i + ti);
+                        part[((tt * H + h) * kNVB + vb) * kPartCols + col] = sum;
+                    }
+                    lds_barrier();
                 }
             }
         }
