@@ -20,9 +20,10 @@
 //                       runs the forward and stores the state every 16 tokens
 //                       (the chunk-boundary checkpoints);
 //   bwd_reverse_kernel  same grid: walks the chunks backwards, recomputes the
-//                       16 states of a chunk from its checkpoint into
-//                       registers, runs the reverse steps, writes dv, dh0 and
-//                       each block's row sums of the per-token partials;
+//                       states of each half chunk (8 tokens) from the chunk's
+//                       checkpoint into registers, runs the reverse steps,
+//                       writes dv, dh0 and each block's row sums of the
+//                       per-token partials;
 //   bwd_finalize_kernel one workgroup per (16 tokens, head): adds the 8 blocks'
 //                       partials and applies the elementwise chains (dq, dk,
 //                       dg, dbeta), plus per-block sums for the parameters;
@@ -167,8 +168,30 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(
     }
 }
 
+// Forward step of one token on a state row (lane j's 8 channels); returns
+// w = v - S' kh for the row and updates S.
+__device__ __forceinline__ float fwd_row_step(float (&S)[8], const float *kh_row, const float *al_row,
+                                              int j, float b, float vv, float &u) {
+    float kh[8], al[8];
+    load_lane8(kh_row, j, kh);
+    load_lane8(al_row, j, al);
+    float p = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        S[e] *= al[e];
+        p = fmaf(S[e], kh[e], p);
+    }
+    const float w = vv - row16_sum(p);
+    u = b * w;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) S[e] = fmaf(u, kh[e], S[e]);
+    return w;
+}
+
+// Three workgroups per CU (at most 168 VGPRs and 53 KB of LDS each), so that
+// the 8 row blocks x heads of the benchmark shape are resident in one round.
 template <typename Tin, typename Tdo>
-__global__ __launch_bounds__(256) void bwd_reverse_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void bwd_reverse_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta_raw,
     const float *__restrict__ A_log, const float *__restrict__ dt_bias, float scale, float lb,
@@ -176,6 +199,8 @@ __global__ __launch_bounds__(256) void bwd_reverse_kernel(
     const Tdo *__restrict__ dout, const float *__restrict__ dht, float *__restrict__ dv,
     float *__restrict__ part, float *__restrict__ dh0)
 {
+    constexpr int kSub = 8;            // states kept in registers at a time
+    constexpr int kFlush = 4;          // tokens per flush of the per-wave sums
     int64_t nh;
     int vb;
     if (!bwd_block(blockIdx.x, (int64_t)N * H, nh, vb)) return;
@@ -191,8 +216,8 @@ __global__ __launch_bounds__(256) void bwd_reverse_kernel(
 
     __shared__ float sKh[kCk][kHeadDim], sQh[kCk][kHeadDim], sAl[kCk][kHeadDim];
     __shared__ float sB[kCk], sV[kCk][kBRows], sDo[kCk][kBRows], sU[kCk][kBRows], sW[kCk][kBRows];
-    // per-wave sums (over the wave's 4 rows) of the partials of 8 tokens
-    __shared__ float sRed[8][4][kPartCols];
+    // per-wave sums (over the wave's 4 rows) of the partials of kFlush tokens
+    __shared__ float sRed[kFlush][4][kPartCols];
 
     float dS[8];
     if (dht) load_lane8(dht + ((size_t)nh * kHeadDim + grow) * kHeadDim, j, dS);
@@ -207,8 +232,7 @@ __global__ __launch_bounds__(256) void bwd_reverse_kernel(
     for (int64_t c = nck - 1; c >= 0; --c) {
         const int64_t c0 = s0 + c * kCk;
         const int L = (int)(s1 - c0 < kCk ? s1 - c0 : kCk);
-        float S[8];
-        load_lane8(ckpt + (((size_t)(slot0 + c) * H + h) * kHeadDim + grow) * kHeadDim, j, S);
+        const float *ck = ckpt + (((size_t)(slot0 + c) * H + h) * kHeadDim + grow) * kHeadDim;
         if (gid < L) {
             const int64_t t = c0 + gid;
             const size_t tb = ((size_t)t * H + h) * kHeadDim;
@@ -231,91 +255,93 @@ __global__ __launch_bounds__(256) void bwd_reverse_kernel(
         }
         lds_barrier();
 
-        // forward through the chunk from its checkpoint, keeping the state
-        // before every token (registers) and u, v - S' kh per row (LDS)
-        float snap[kCk][8];
-#pragma unroll
-        for (int i = 0; i < kCk; ++i) {
-            if (i < L) {
-                float kh[8], al[8];
-                load_lane8(&sKh[i][0], j, kh);
-                load_lane8(&sAl[i][0], j, al);
-                float p = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    snap[i][e] = S[e];
-                    S[e] *= al[e];
-                    p = fmaf(S[e], kh[e], p);
+        // the chunk's two halves, last first: recompute the states before the
+        // half's tokens from the checkpoint (registers), then the reverse steps
+#pragma unroll 1
+        for (int half = 1; half >= 0; --half) {
+            const int i0 = half * kSub;
+            if (i0 < L) {
+                float S[8];
+                load_lane8(ck, j, S);
+                for (int i = 0; i < i0; ++i) {       // tokens before the half: states not kept
+                    float u;
+                    fwd_row_step(S, &sKh[i][0], &sAl[i][0], j, sB[i], sV[i][row], u);
                 }
-                const float w = sV[i][row] - row16_sum(p);
-                const float u = sB[i] * w;
+                float snap[kSub][8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) S[e] = fmaf(u, kh[e], S[e]);
-                if (j == 0) { sU[i][row] = u; sW[i][row] = w; }
-            }
-        }
-
-        // reverse steps
+                for (int ii = 0; ii < kSub; ++ii) {
+                    const int i = i0 + ii;
+                    if (i < L) {
 #pragma unroll
-        for (int i = kCk - 1; i >= 0; --i) {
-            if (i < L) {
-                const int64_t t = c0 + i;
-                float kh[8], al[8], qh[8];
-                load_lane8(&sKh[i][0], j, kh);
-                load_lane8(&sAl[i][0], j, al);
-                load_lane8(&sQh[i][0], j, qh);
-                const float b = sB[i], u = sU[i][row], w = sW[i][row], d_o = sDo[i][row];
-                float sp[8], pq[8], pk[8], pa[8];
-                float du = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    sp[e] = snap[i][e] * al[e];                  // S'
-                    pq[e] = d_o * fmaf(u, kh[e], sp[e]);        // do_v * S_t[v, :]
-                    dS[e] = fmaf(d_o, qh[e], dS[e]);
-                    du = fmaf(dS[e], kh[e], du);
-                }
-                du = row16_sum(du);
-                const float bdu = b * du;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pk[e] = u * dS[e] - bdu * sp[e];
-                    const float dsp = fmaf(-bdu, kh[e], dS[e]);
-                    pa[e] = dsp * snap[i][e];
-                    dS[e] = dsp * al[e];
-                }
-                const size_t tb = ((size_t)t * H + h) * kHeadDim;
-                if (j == 0) dv[tb + grow] = bdu;
-                // sums over the wave's 4 rows, kept per wave in LDS
-                float *red = &sRed[i & 7][wave][0];
-                float pb = rows4_sum(du * w);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    pq[e] = rows4_sum(pq[e]);
-                    pk[e] = rows4_sum(pk[e]);
-                    pa[e] = rows4_sum(pa[e]);
-                }
-                if (lane < 16) {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        red[chan(j, e)] = pq[e];
-                        red[kHeadDim + chan(j, e)] = pk[e];
-                        red[2 * kHeadDim + chan(j, e)] = pa[e];
+                        for (int e = 0; e < 8; ++e) snap[ii][e] = S[e];
+                        float u;
+                        const float w = fwd_row_step(S, &sKh[i][0], &sAl[i][0], j, sB[i], sV[i][row], u);
+                        if (j == 0) { sU[i][row] = u; sW[i][row] = w; }
                     }
-                    if (j == 0) red[3 * kHeadDim] = pb;
                 }
-                // after tokens 8..L-1 and after tokens 0..: add the 4 waves'
-                // sums and store the block's row sums of the partials
-                if (i == 8 || i == 0) {
-                    const int ntok = (i == 8) ? L - 8 : (L < 8 ? L : 8);
-                    lds_barrier();
-                    for (int idx = threadIdx.x; idx < ntok * kPartCols; idx += 256) {
-                        const int ti = idx / kPartCols, col = idx - ti * kPartCols;
-                        const float sum = (sRed[ti][0][col] + sRed[ti][1][col]) +
-                                          (sRed[ti][2][col] + sRed[ti][3][col]);
-                        const size_t tt = (size_t)(c0 + i + ti);
-                        part[((tt * H + h) * kNVB + vb) * kPartCols + col] = sum;
+#pragma unroll
+                for (int ii = kSub - 1; ii >= 0; --ii) {
+                    const int i = i0 + ii;
+                    if (i < L) {
+                        const int64_t t = c0 + i;
+                        float kh[8], al[8], qh[8];
+                        load_lane8(&sKh[i][0], j, kh);
+                        load_lane8(&sAl[i][0], j, al);
+                        load_lane8(&sQh[i][0], j, qh);
+                        const float b = sB[i], u = sU[i][row], w = sW[i][row], d_o = sDo[i][row];
+                        float sp[8], pq[8], pk[8], pa[8];
+                        float du = 0.f;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            sp[e] = snap[ii][e] * al[e];                 // S'
+                            pq[e] = d_o * fmaf(u, kh[e], sp[e]);        // do_v * S_t[v, :]
+                            dS[e] = fmaf(d_o, qh[e], dS[e]);
+                            du = fmaf(dS[e], kh[e], du);
+                        }
+                        du = row16_sum(du);
+                        const float bdu = b * du;
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            pk[e] = u * dS[e] - bdu * sp[e];
+                            const float dsp = fmaf(-bdu, kh[e], dS[e]);
+                            pa[e] = dsp * snap[ii][e];
+                            dS[e] = dsp * al[e];
+                        }
+                        const size_t tb = ((size_t)t * H + h) * kHeadDim;
+                        if (j == 0) dv[tb + grow] = bdu;
+                        // sums over the wave's 4 rows, kept per wave in LDS
+                        float *red = &sRed[i % kFlush][wave][0];
+                        const float pb = rows4_sum(du * w);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) {
+                            pq[e] = rows4_sum(pq[e]);
+                            pk[e] = rows4_sum(pk[e]);
+                            pa[e] = rows4_sum(pa[e]);
+                        }
+                        if (lane < 16) {
+#pragma unroll
+                            for (int e = 0; e < 8; ++e) {
+                                red[chan(j, e)] = pq[e];
+                                red[kHeadDim + chan(j, e)] = pk[e];
+                                red[2 * kHeadDim + chan(j, e)] = pa[e];
+                            }
+                            if (j == 0) red[3 * kHeadDim] = pb;
+                        }
+                        // after tokens i .. min(i + kFlush, L) - 1: add the 4
+                        // waves' sums and store the block's row sums
+                        if (i % kFlush == 0) {
+                            const int ntok = (L - i < kFlush) ? L - i : kFlush;
+                            lds_barrier();
+                            for (int idx = threadIdx.x; idx < ntok * kPartCols; idx += 256) {
+                                const int ti = idx / kPartCols, col = idx - ti * kPartCols;
+                                const float sum = (sRed[ti][0][col] + sRed[ti][1][col]) +
+                                                  (sRed[ti][2][col] + sRed[ti][3][col]);
+                                const size_t tt = (size_t)(c0 + i + ti);
+                                part[((tt * H + h) * kNVB + vb) * kPartCols + col] = sum;
+                            }
+                            lds_barrier();
+                        }
                     }
-                    lds_barrier();
                 }
             }
         }
