@@ -138,21 +138,39 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(
     float dtb[8];
     load_lane8(dt_bias + (size_t)h * kHeadDim, j, dtb);
 
+    // raw token data of the chunk's token `gid`, loaded one chunk ahead so that
+    // the loads of chunk c + 1 are in flight while chunk c runs
+    float kv[8], gv[8], braw = 0.f, vv = 0.f;
+    auto fetch = [&](int64_t c) {
+        const int64_t t = s0 + c * kCk + gid;
+        if (c < nck && t < s1) {
+            const size_t tb = ((size_t)t * H + h) * kHeadDim;
+            load_lane8(k + tb, j, kv);
+            load_lane8(g + tb, j, gv);
+            braw = beta_raw[(size_t)t * H + h];
+            vv = to_f32(v[tb + vb * kBRows + j]);
+        }
+    };
+    fetch(0);
     for (int64_t c = 0; c < nck; ++c) {
         const int64_t c0 = s0 + c * kCk;
         const int L = (int)(s1 - c0 < kCk ? s1 - c0 : kCk);
         store_lane8(ckpt + (((size_t)(slot0 + c) * H + h) * kHeadDim + grow) * kHeadDim, j, S);
         if (gid < L) {
-            const int64_t t = c0 + gid;
-            const size_t tb = ((size_t)t * H + h) * kHeadDim;
-            float kh[8], al[8];
-            key_and_decay(k, g, dtb, a_gate, lb, tb, j, kh, al);
+            float ss = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { sKh[gid][chan(j, e)] = kh[e]; sAl[gid][chan(j, e)] = al[e]; }
-            if (j == 0) sB[gid] = sigmoid_f(beta_raw[(size_t)t * H + h]);
-            sV[gid][j] = to_f32(v[tb + vb * kBRows + j]);
+            for (int e = 0; e < 8; ++e) ss = fmaf(kv[e], kv[e], ss);
+            const float rk = rsqrtf(row16_sum(ss) + kL2Eps);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                sKh[gid][chan(j, e)] = kv[e] * rk;
+                sAl[gid][chan(j, e)] = fast_exp2(lb * sigmoid_f(a_gate * (gv[e] + dtb[e])) * kLog2e);
+            }
+            if (j == 0) sB[gid] = sigmoid_f(braw);
+            sV[gid][j] = vv;
         }
         lds_barrier();
+        fetch(c + 1);
         for (int i = 0; i < L; ++i) {
             float kh[8], al[8];
             load_lane8(&sKh[i][0], j, kh);
