@@ -49,6 +49,9 @@ KERNEL_SOURCES = {
     "decode_step_kernel": ("kda_decode.hip", "kda_common.h", "kda_internal.h"),
     "short_conv_kernel": ("kda_shortconv.hip", "kda_common.h", "kda_internal.h"),
     "norm_gate_kernel": ("kda_epilogue.hip", "kda_common.h", "kda_internal.h"),
+    "bwd_ckpt_kernel": ("kda_backward.hip", "kda_common.h", "kda_internal.h"),
+    "bwd_reverse_kernel": ("kda_backward.hip", "kda_common.h", "kda_internal.h"),
+    "bwd_finalize_kernel": ("kda_backward.hip", "kda_common.h", "kda_internal.h"),
 }
 
 
@@ -340,6 +343,8 @@ def backward_timing(kda, p, dev_inputs, reps=3):
     tf = flops / (ms * 1e-3) / 1e12
     return {"ms": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
             "workspace_bytes": kda.backward_workspace_size(T, N, H),
+            "traffic": {kn: measured_traffic(kn) for kn in
+                        ("bwd_ckpt_kernel", "bwd_reverse_kernel", "bwd_finalize_kernel")},
             "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_VALU_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4),
                          "alg_flops": flops}}
