@@ -75,6 +75,21 @@ __device__ __forceinline__ float rows4_sum(float x) {
     return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
+// Four values reduced over the wave's four 16-lane rows at once: a 32-lane
+// swap and add leaves a's half sums in lanes 0-31 and b's in 32-63 (c and d
+// likewise in a second register), a 16-lane swap and add of those two then
+// leaves in row 0 the full sum of a, in row 1 that of c, in row 2 b, in row 3
+// d (each at the lane's own position in its row): 3 swaps + 3 adds for four
+// sums instead of 8 + 8.
+__device__ __forceinline__ float quad_rows_sum(float a, float b, float c, float d) {
+    const auto ab = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
+    const auto cd = __builtin_amdgcn_permlane32_swap(__float_as_uint(c), __float_as_uint(d), false, false);
+    const float x = __uint_as_float(ab[0]) + __uint_as_float(ab[1]);
+    const float y = __uint_as_float(cd[0]) + __uint_as_float(cd[1]);
+    const auto xy = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    return __uint_as_float(xy[0]) + __uint_as_float(xy[1]);
+}
+
 // Workgroup b -> (sequence*H + head, row block). The 8 row blocks of one
 // (sequence, head) share its token data, so they go to one XCD (blocks are
 // dealt to the 8 XCDs round-robin by index).
@@ -327,24 +342,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
                         }
                         const size_t tb = ((size_t)t * H + h) * kHeadDim;
                         if (j == 0) dv[tb + grow] = bdu;
-                        // sums over the wave's 4 rows, kept per wave in LDS
+                        // sums over the wave's 4 rows, kept per wave in LDS: each
+                        // quad_rows_sum leaves in row r the sum of its value at
+                        // offset qo = 0, 2, 1, 3 (rows 0..3), so every lane
+                        // stores one sum per quad
                         float *red = &sRed[i % kFlush][wave][0];
                         const float pb = rows4_sum(du * w);
+                        const int qo = (lane >> 4) == 1 ? 2 : ((lane >> 4) == 2 ? 1 : (lane >> 4));
 #pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            pq[e] = rows4_sum(pq[e]);
-                            pk[e] = rows4_sum(pk[e]);
-                            pa[e] = rows4_sum(pa[e]);
+                        for (int hq = 0; hq < 2; ++hq) {
+                            const int e0 = 4 * hq;
+                            const int cidx = 64 * hq + 4 * j + qo;          // chan(j, e0 + qo)
+                            red[cidx] = quad_rows_sum(pq[e0], pq[e0 + 1], pq[e0 + 2], pq[e0 + 3]);
+                            red[kHeadDim + cidx] = quad_rows_sum(pk[e0], pk[e0 + 1], pk[e0 + 2], pk[e0 + 3]);
+                            red[2 * kHeadDim + cidx] = quad_rows_sum(pa[e0], pa[e0 + 1], pa[e0 + 2], pa[e0 + 3]);
                         }
-                        if (lane < 16) {
-#pragma unroll
-                            for (int e = 0; e < 8; ++e) {
-                                red[chan(j, e)] = pq[e];
-                                red[kHeadDim + chan(j, e)] = pk[e];
-                                red[2 * kHeadDim + chan(j, e)] = pa[e];
-                            }
-                            if (j == 0) red[3 * kHeadDim] = pb;
-                        }
+                        if (lane == 0) red[3 * kHeadDim] = pb;
                         // after tokens i .. min(i + kFlush, L) - 1: add the 4
                         // waves' sums and store the block's row sums
                         if (i % kFlush == 0) {
