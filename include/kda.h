@@ -312,6 +312,53 @@ kda_status_t kda_backward(const void *q, const void *k, const void *v, const flo
                           float *d_initial_state, void *workspace, size_t workspace_bytes,
                           void *stream);
 /*
+ * Grouped value heads (FlashKDA issue page, "Proposed scope": grouped value
+ * heads). H value heads share H_qk query/key heads, H a multiple of H_qk: value
+ * head h reads q and k of head h / (H / H_qk). v, g, beta_raw, the states and
+ * the outputs keep H heads; q and k are [T, H_qk, 128] (decode: [B, H_qk, 128]).
+ * The same computation as the ungrouped call with q and k repeated H / H_qk
+ * times along the head axis; H_qk == H is the ungrouped call. Everything else
+ * as for kda_chunk_fwd, kda_decode_step_slots / _gated / plain, and
+ * kda_backward; H_qk that does not divide H is rejected with
+ * KDA_ERR_INVALID_ARG. In kda_backward_grouped dq and dk are [T, H_qk, 128],
+ * summed over the value heads of each group.
+ *
+ * kda_decode_step_grouped covers the three decode forms: slot_idx NULL for a
+ * state [B, H, 128, 128] (num_slots ignored), else a pool of num_slots entries
+ * addressed as in kda_decode_step_slots; z NULL for no output epilogue.
+ */
+kda_status_t kda_chunk_fwd_grouped(const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta_raw,
+                                   const float *A_log, const float *dt_bias,
+                                   float scale, float lower_bound,
+                                   const int64_t *cu_seqlens, int32_t num_seqs,
+                                   int64_t total_tokens, int32_t H, int32_t K, int32_t V,
+                                   int32_t chunk_size, kda_dtype_t in_dtype,
+                                   const float *initial_state, float *final_state,
+                                   void *o, kda_dtype_t o_dtype,
+                                   void *workspace, size_t workspace_bytes, void *stream,
+                                   int32_t H_qk);
+kda_status_t kda_decode_step_grouped(const void *q, const void *k, const void *v,
+                                     const float *g, const float *beta_raw,
+                                     const float *A_log, const float *dt_bias,
+                                     float scale, float lower_bound,
+                                     float *state, int32_t num_slots, const int32_t *slot_idx,
+                                     void *o, kda_dtype_t o_dtype,
+                                     int32_t B, int32_t H, int32_t H_qk, int32_t K, int32_t V,
+                                     kda_dtype_t in_dtype,
+                                     const void *z, const float *norm_weight, float norm_eps,
+                                     void *stream);
+kda_status_t kda_backward_grouped(const void *q, const void *k, const void *v, const float *g,
+                                  const float *beta_raw, const float *A_log, const float *dt_bias,
+                                  float scale, float lower_bound, const int64_t *cu_seqlens,
+                                  int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t H_qk,
+                                  int32_t K, int32_t V, kda_dtype_t in_dtype,
+                                  const float *initial_state, const void *d_o, kda_dtype_t do_dtype,
+                                  const float *d_final_state, float *dq, float *dk, float *dv,
+                                  float *dg, float *dbeta, float *dA_log, float *ddt_bias,
+                                  float *d_initial_state, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+/*
  * Opt-in check of packed offsets (FlashInfer kda_backward page: offsets are
  * validated by one eager synchronisation, the launch path then trusts them).
  * Copies cu_seqlens to the host on `stream`, synchronises that stream and

@@ -55,6 +55,14 @@ kda_status_t check_aligned16(std::initializer_list<std::pair<const void *, const
     return KDA_OK;
 }
 
+// Grouped value heads: H value heads share H_qk q/k heads, H a multiple of H_qk.
+kda_status_t check_groups(int64_t H, int64_t H_qk) {
+    if (H_qk < 1 || H_qk > H || H % H_qk != 0)
+        return fail(KDA_ERR_INVALID_ARG, "H_qk must divide H (got H=" + std::to_string(H) +
+                                             ", H_qk=" + std::to_string(H_qk) + ")");
+    return KDA_OK;
+}
+
 kda_status_t hip_fail(hipError_t e, const char *where) {
     return fail(KDA_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
 }
@@ -69,9 +77,11 @@ kda_status_t decode_step_impl(const void *q, const void *k, const void *v,
                               kda_dtype_t in_dtype, void *stream,
                               const void *z, const float *norm_weight, float norm_eps,
                               const int32_t *slots, int32_t num_slots,
-                              const char *name) {
+                              const char *name, int32_t H_qk) {
     if (B < 1) return fail(KDA_ERR_INVALID_ARG, "B must be >= 1");
     kda_status_t st = check_common(H, K, V, scale, lower_bound, in_dtype, o_dtype);
+    if (st != KDA_OK) return st;
+    st = check_groups(H, H_qk);
     if (st != KDA_OK) return st;
     if (!q || !k || !v || !g || !beta_raw || !A_log || !dt_bias || !state || !o)
         return fail(KDA_ERR_INVALID_ARG, "a required pointer is NULL");
@@ -97,7 +107,7 @@ kda_status_t decode_step_impl(const void *q, const void *k, const void *v,
     a.B = B; a.H = H; a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = o_dtype == KDA_BF16;
     a.stream = (hipStream_t)stream;
     a.z = z; a.norm_w = norm_weight; a.norm_eps = norm_eps;
-    a.slots = slots; a.num_slots = num_slots;
+    a.slots = slots; a.num_slots = num_slots; a.Hk = H_qk;
     hipError_t e = kda::launch_decode(a);
     if (e != hipSuccess) return hip_fail(e, name);
     return ok();
@@ -107,7 +117,7 @@ kda_status_t decode_step_impl(const void *q, const void *k, const void *v,
 
 extern "C" {
 
-int kda_version(void) { return 103; }
+int kda_version(void) { return 104; }
 
 const char *kda_status_string(kda_status_t s) {
     switch (s) {
@@ -156,10 +166,12 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
                               const float *initial_state, float *final_state,
                               void *o, kda_dtype_t o_dtype,
                               void *workspace, size_t workspace_bytes,
-                              void *stream) {
+                              void *stream, int32_t H_qk) {
     if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 1");
     if (total_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens must be >= 0");
     kda_status_t st = check_common(H, K, V, scale, lower_bound, in_dtype, o_dtype);
+    if (st != KDA_OK) return st;
+    st = check_groups(H, H_qk);
     if (st != KDA_OK) return st;
     if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64)
         return fail(KDA_ERR_UNSUPPORTED, "chunk_size must be 16, 32 or 64");
@@ -188,7 +200,8 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
     kda::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta_raw = beta_raw; a.A_log = A_log; a.dt_bias = dt_bias;
     a.scale = scale; a.lower_bound = lower_bound;
-    a.cu_seqlens = cu_seqlens; a.N = num_seqs; a.T = total_tokens; a.H = H; a.chunk = chunk_size;
+    a.cu_seqlens = cu_seqlens; a.N = num_seqs; a.T = total_tokens; a.H = H; a.Hk = H_qk;
+    a.chunk = chunk_size;
     a.h0 = initial_state; a.ht = final_state; a.o = o;
     a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = o_dtype == KDA_BF16;
     a.ws = (unsigned char *)workspace;
@@ -216,15 +229,41 @@ extern "C" {
         void *workspace, size_t workspace_bytes, void *stream
 
 kda_status_t kda_chunk_fwd(KDA_CHUNK_PARAMS) {
-    return chunk_fwd_stages(3, "kda_chunk_fwd", KDA_CHUNK_ARGS);
+    return chunk_fwd_stages(3, "kda_chunk_fwd", KDA_CHUNK_ARGS, H);
 }
 
 kda_status_t kda_chunk_fwd_intra(KDA_CHUNK_PARAMS) {
-    return chunk_fwd_stages(1, "kda_chunk_fwd_intra", KDA_CHUNK_ARGS);
+    return chunk_fwd_stages(1, "kda_chunk_fwd_intra", KDA_CHUNK_ARGS, H);
 }
 
 kda_status_t kda_chunk_fwd_inter(KDA_CHUNK_PARAMS) {
-    return chunk_fwd_stages(2, "kda_chunk_fwd_inter", KDA_CHUNK_ARGS);
+    return chunk_fwd_stages(2, "kda_chunk_fwd_inter", KDA_CHUNK_ARGS, H);
+}
+
+kda_status_t kda_chunk_fwd_grouped(KDA_CHUNK_PARAMS, int32_t H_qk) {
+    return chunk_fwd_stages(3, "kda_chunk_fwd_grouped", KDA_CHUNK_ARGS, H_qk);
+}
+
+kda_status_t kda_decode_step_grouped(const void *q, const void *k, const void *v,
+                                     const float *g, const float *beta_raw,
+                                     const float *A_log, const float *dt_bias,
+                                     float scale, float lower_bound,
+                                     float *state, int32_t num_slots, const int32_t *slot_idx,
+                                     void *o, kda_dtype_t o_dtype,
+                                     int32_t B, int32_t H, int32_t H_qk, int32_t K, int32_t V,
+                                     kda_dtype_t in_dtype,
+                                     const void *z, const float *norm_weight, float norm_eps,
+                                     void *stream) {
+    if (slot_idx) {
+        if (num_slots < 1) return fail(KDA_ERR_INVALID_ARG, "num_slots must be >= 1");
+        if (((uintptr_t)slot_idx & 3) != 0) return fail(KDA_ERR_INVALID_ARG, "slot_idx must be 4-byte aligned");
+        if ((int64_t)num_slots * H > ((int64_t)1 << 31) - 1)
+            return fail(KDA_ERR_INVALID_ARG, "num_slots * H too large");
+    }
+    return decode_step_impl(q, k, v, g, beta_raw, A_log, dt_bias, scale, lower_bound, state, o,
+                            o_dtype, B, H, K, V, in_dtype, stream, z, norm_weight, norm_eps,
+                            slot_idx, slot_idx ? num_slots : 0, "kda_decode_step_grouped launch",
+                            H_qk);
 }
 
 
@@ -237,7 +276,7 @@ kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
                              kda_dtype_t in_dtype, void *stream) {
     return decode_step_impl(q, k, v, g, beta_raw, A_log, dt_bias, scale, lower_bound, state, o,
                             o_dtype, B, H, K, V, in_dtype, stream, nullptr, nullptr, 0.f,
-                            nullptr, 0, "kda_decode_step launch");
+                            nullptr, 0, "kda_decode_step launch", H);
 }
 
 kda_status_t kda_decode_step_gated(const void *q, const void *k, const void *v,
@@ -252,7 +291,7 @@ kda_status_t kda_decode_step_gated(const void *q, const void *k, const void *v,
     if (!z) return fail(KDA_ERR_INVALID_ARG, "z is NULL");
     return decode_step_impl(q, k, v, g, beta_raw, A_log, dt_bias, scale, lower_bound, state, o,
                             o_dtype, B, H, K, V, in_dtype, stream, z, norm_weight, norm_eps,
-                            nullptr, 0, "kda_decode_step_gated launch");
+                            nullptr, 0, "kda_decode_step_gated launch", H);
 }
 
 kda_status_t kda_decode_step_slots(const void *q, const void *k, const void *v,
@@ -272,7 +311,7 @@ kda_status_t kda_decode_step_slots(const void *q, const void *k, const void *v,
         return fail(KDA_ERR_INVALID_ARG, "num_slots * H too large");
     return decode_step_impl(q, k, v, g, beta_raw, A_log, dt_bias, scale, lower_bound, state_pool,
                             o, o_dtype, B, H, K, V, in_dtype, stream, z, norm_weight, norm_eps,
-                            slot_idx, num_slots, "kda_decode_step_slots launch");
+                            slot_idx, num_slots, "kda_decode_step_slots launch", H);
 }
 
 kda_status_t kda_output_norm_gate(const void *o, const void *z, const float *weight, float eps,
@@ -355,19 +394,22 @@ size_t kda_backward_workspace_size(int64_t total_tokens, int32_t num_seqs, int32
     return kda::backward_layout(total_tokens, num_seqs, H).total;
 }
 
-kda_status_t kda_backward(const void *q, const void *k, const void *v, const float *g,
-                          const float *beta_raw, const float *A_log, const float *dt_bias,
-                          float scale, float lower_bound, const int64_t *cu_seqlens,
-                          int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t K, int32_t V,
-                          kda_dtype_t in_dtype, const float *initial_state, const void *d_o,
-                          kda_dtype_t do_dtype, const float *d_final_state, float *dq, float *dk,
-                          float *dv, float *dg, float *dbeta, float *dA_log, float *ddt_bias,
-                          float *d_initial_state, void *workspace, size_t workspace_bytes,
-                          void *stream) {
+kda_status_t kda_backward_grouped(const void *q, const void *k, const void *v, const float *g,
+                                  const float *beta_raw, const float *A_log, const float *dt_bias,
+                                  float scale, float lower_bound, const int64_t *cu_seqlens,
+                                  int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t H_qk,
+                                  int32_t K, int32_t V, kda_dtype_t in_dtype,
+                                  const float *initial_state, const void *d_o, kda_dtype_t do_dtype,
+                                  const float *d_final_state, float *dq, float *dk, float *dv,
+                                  float *dg, float *dbeta, float *dA_log, float *ddt_bias,
+                                  float *d_initial_state, void *workspace, size_t workspace_bytes,
+                                  void *stream) {
     if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 1");
     if (total_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens must be >= 0");
     if (H > 65535) return fail(KDA_ERR_INVALID_ARG, "H must lie in [1, 65535]");
     kda_status_t st = check_common(H, K, V, scale, lower_bound, in_dtype, do_dtype);
+    if (st != KDA_OK) return st;
+    st = check_groups(H, H_qk);
     if (st != KDA_OK) return st;
     if (!cu_seqlens || !A_log || !dt_bias || !dA_log || !ddt_bias)
         return fail(KDA_ERR_INVALID_ARG, "cu_seqlens, A_log, dt_bias, dA_log and ddt_bias must not be NULL");
@@ -397,7 +439,7 @@ kda_status_t kda_backward(const void *q, const void *k, const void *v, const flo
     kda::BackwardArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta_raw = beta_raw; a.A_log = A_log; a.dt_bias = dt_bias;
     a.scale = scale; a.lower_bound = lower_bound; a.cu = cu_seqlens; a.N = num_seqs; a.H = H;
-    a.T = total_tokens; a.in_bf16 = in_dtype == KDA_BF16; a.do_bf16 = do_dtype == KDA_BF16;
+    a.Hk = H_qk; a.T = total_tokens; a.in_bf16 = in_dtype == KDA_BF16; a.do_bf16 = do_dtype == KDA_BF16;
     a.h0 = initial_state; a.dout = d_o; a.dht = d_final_state;
     a.dq = dq; a.dk = dk; a.dv = dv; a.dg = dg; a.dbeta = dbeta; a.dA_log = dA_log;
     a.ddt_bias = ddt_bias; a.dh0 = d_initial_state;
@@ -409,6 +451,22 @@ kda_status_t kda_backward(const void *q, const void *k, const void *v, const flo
     hipError_t e = kda::launch_backward(a);
     if (e != hipSuccess) return hip_fail(e, "kda_backward launch");
     return ok();
+}
+
+kda_status_t kda_backward(const void *q, const void *k, const void *v, const float *g,
+                          const float *beta_raw, const float *A_log, const float *dt_bias,
+                          float scale, float lower_bound, const int64_t *cu_seqlens,
+                          int32_t num_seqs, int64_t total_tokens, int32_t H, int32_t K, int32_t V,
+                          kda_dtype_t in_dtype, const float *initial_state, const void *d_o,
+                          kda_dtype_t do_dtype, const float *d_final_state, float *dq, float *dk,
+                          float *dv, float *dg, float *dbeta, float *dA_log, float *ddt_bias,
+                          float *d_initial_state, void *workspace, size_t workspace_bytes,
+                          void *stream) {
+    return kda_backward_grouped(q, k, v, g, beta_raw, A_log, dt_bias, scale, lower_bound,
+                                cu_seqlens, num_seqs, total_tokens, H, H, K, V, in_dtype,
+                                initial_state, d_o, do_dtype, d_final_state, dq, dk, dv, dg, dbeta,
+                                dA_log, ddt_bias, d_initial_state, workspace, workspace_bytes,
+                                stream);
 }
 
 kda_status_t kda_check_cu_seqlens(const int64_t *cu_seqlens, int32_t num_seqs,

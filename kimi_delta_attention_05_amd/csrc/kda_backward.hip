@@ -104,10 +104,10 @@ __device__ __forceinline__ bool bwd_block(int64_t b, int64_t NH, int64_t &nh, in
 // Per-token transforms of token t for lane j's channels (one DPP row per token).
 template <typename Tin>
 __device__ __forceinline__ void key_and_decay(const Tin *k, const float *g, const float (&dtb)[8],
-                                              float a_gate, float lb, size_t tb, int j,
+                                              float a_gate, float lb, size_t tb, size_t tbk, int j,
                                               float (&kh)[8], float (&al)[8]) {
     float kv[8], gv[8];
-    load_lane8(k + tb, j, kv);
+    load_lane8(k + tbk, j, kv);
     load_lane8(g + tb, j, gv);
     float ss = 0.f;
 #pragma unroll
@@ -125,7 +125,7 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(
     const Tin *__restrict__ k, const Tin *__restrict__ v, const float *__restrict__ g,
     const float *__restrict__ beta_raw, const float *__restrict__ A_log,
     const float *__restrict__ dt_bias, float lb, const int64_t *__restrict__ cu, int N, int H,
-    const float *__restrict__ h0, float *__restrict__ ckpt)
+    int Hk, const float *__restrict__ h0, float *__restrict__ ckpt)
 {
     int64_t nh;
     int vb;
@@ -160,7 +160,7 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(
         const int64_t t = s0 + c * kCk + gid;
         if (c < nck && t < s1) {
             const size_t tb = ((size_t)t * H + h) * kHeadDim;
-            load_lane8(k + tb, j, kv);
+            load_lane8(k + ((size_t)t * Hk + h / (H / Hk)) * kHeadDim, j, kv);
             load_lane8(g + tb, j, gv);
             braw = beta_raw[(size_t)t * H + h];
             vv = to_f32(v[tb + vb * kBRows + j]);
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta_raw,
     const float *__restrict__ A_log, const float *__restrict__ dt_bias, float scale, float lb,
-    const int64_t *__restrict__ cu, int N, int H, const float *__restrict__ ckpt,
+    const int64_t *__restrict__ cu, int N, int H, int Hk, const float *__restrict__ ckpt,
     const Tdo *__restrict__ dout, const float *__restrict__ dht, float *__restrict__ dv,
     float *__restrict__ part, float *__restrict__ dh0)
 {
@@ -269,9 +269,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
         if (gid < L) {
             const int64_t t = c0 + gid;
             const size_t tb = ((size_t)t * H + h) * kHeadDim;
+            const size_t tbk = ((size_t)t * Hk + h / (H / Hk)) * kHeadDim;
             float kh[8], al[8], qv[8];
-            key_and_decay(k, g, dtb, a_gate, lb, tb, j, kh, al);
-            load_lane8(q + tb, j, qv);
+            key_and_decay(k, g, dtb, a_gate, lb, tb, tbk, j, kh, al);
+            load_lane8(q + tbk, j, qv);
             float ss = 0.f;
 #pragma unroll
             for (int e = 0; e < 8; ++e) ss = fmaf(qv[e], qv[e], ss);
@@ -381,49 +382,92 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
     if (dh0) store_lane8(dh0 + ((size_t)nh * kHeadDim + grow) * kHeadDim, j, dS);
 }
 
-// One DPP row per token, 16 tokens per workgroup, one head per grid row.
+// One DPP row per token, 16 tokens per workgroup, one q/k head per grid row:
+// the value heads that share the q/k head (grouped value heads) add their dqh
+// and dkh before the normalisations' chains; dg and dbeta are per value head.
 template <typename Tin>
 __global__ __launch_bounds__(256) void bwd_finalize_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta_raw, const float *__restrict__ A_log,
-    const float *__restrict__ dt_bias, float scale, float lb, int64_t T, int H,
+    const float *__restrict__ dt_bias, float scale, float lb, int64_t T, int H, int Hk,
     const float *__restrict__ part, float *__restrict__ dq, float *__restrict__ dk,
     float *__restrict__ dg, float *__restrict__ dbeta, float *__restrict__ pp)
 {
-    const int h = blockIdx.y;
+    const int hk = blockIdx.y;
+    const int G = H / Hk;
     const int64_t tblk = blockIdx.x;
     const int j = threadIdx.x & 15, gid = threadIdx.x >> 4;
     const int64_t t = tblk * 16 + gid;
+    const bool valid = t < T;
     __shared__ float sP[16][kHeadDim + 1];
 
-    float dgv[8];
-    float cA = 0.f;
-    if (t < T) {
-        const size_t tb = ((size_t)t * H + h) * kHeadDim;
-        const float *src = part + (size_t)((size_t)t * H + h) * kNVB * kPartCols;
-        float dqh[8], dkh[8], dal[8];
-        float db = 0.f;
+    float dqh[8], dkh[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) { dqh[e] = 0.f; dkh[e] = 0.f; dal[e] = 0.f; }
+    for (int e = 0; e < 8; ++e) { dqh[e] = 0.f; dkh[e] = 0.f; }
+    for (int gg = 0; gg < G; ++gg) {
+        const int h = hk * G + gg;
+        float dgv[8];
+        float cA = 0.f;
+        if (valid) {
+            const size_t tb = ((size_t)t * H + h) * kHeadDim;
+            const float *src = part + (size_t)((size_t)t * H + h) * kNVB * kPartCols;
+            float dal[8];
+            float db = 0.f;
 #pragma unroll
-        for (int b = 0; b < kNVB; ++b) {
-            float x[8];
-            load_lane8(src + b * kPartCols, j, x);
+            for (int e = 0; e < 8; ++e) dal[e] = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) dqh[e] += x[e];
-            load_lane8(src + b * kPartCols + kHeadDim, j, x);
+            for (int b = 0; b < kNVB; ++b) {
+                float x[8];
+                load_lane8(src + b * kPartCols, j, x);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) dkh[e] += x[e];
-            load_lane8(src + b * kPartCols + 2 * kHeadDim, j, x);
+                for (int e = 0; e < 8; ++e) dqh[e] += x[e];
+                load_lane8(src + b * kPartCols + kHeadDim, j, x);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) dal[e] += x[e];
-            db += src[b * kPartCols + 3 * kHeadDim];
+                for (int e = 0; e < 8; ++e) dkh[e] += x[e];
+                load_lane8(src + b * kPartCols + 2 * kHeadDim, j, x);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) dal[e] += x[e];
+                db += src[b * kPartCols + 3 * kHeadDim];
+            }
+            float gv[8], dtb[8];
+            load_lane8(g + tb, j, gv);
+            load_lane8(dt_bias + (size_t)h * kHeadDim, j, dtb);
+            const float a_gate = fast_exp2(A_log[h] * kLog2e);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float sg = sigmoid_f(a_gate * (gv[e] + dtb[e]));
+                const float al = fast_exp2(lb * sg * kLog2e);
+                dgv[e] = dal[e] * al * lb * sg * (1.0f - sg) * a_gate;
+                cA = fmaf(dgv[e], gv[e] + dtb[e], cA);
+            }
+            store_lane8(dg + tb, j, dgv);
+            cA = row16_sum(cA);
+            if (j == 0) {
+                const float bb = sigmoid_f(beta_raw[(size_t)t * H + h]);
+                dbeta[(size_t)t * H + h] = db * bb * (1.0f - bb);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dgv[e] = 0.f;
         }
-        float qv[8], kv[8], gv[8], dtb[8];
-        load_lane8(q + tb, j, qv);
-        load_lane8(k + tb, j, kv);
-        load_lane8(g + tb, j, gv);
-        load_lane8(dt_bias + (size_t)h * kHeadDim, j, dtb);
+        // this value head's sums over the 16 tokens, for the parameters
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sP[gid][chan(j, e)] = dgv[e];
+        if (j == 0) sP[gid][kHeadDim] = cA;
+        lds_barrier();
+        if (threadIdx.x <= kHeadDim) {
+            float sum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum += sP[r][threadIdx.x];
+            pp[((size_t)tblk * H + h) * (kHeadDim + 1) + threadIdx.x] = sum;
+        }
+        lds_barrier();
+    }
+    if (valid) {
+        const size_t tbk = ((size_t)t * Hk + hk) * kHeadDim;
+        float qv[8], kv[8];
+        load_lane8(q + tbk, j, qv);
+        load_lane8(k + tbk, j, kv);
         float sq = 0.f, sk = 0.f, qd = 0.f, kd = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -435,38 +479,14 @@ __global__ __launch_bounds__(256) void bwd_finalize_kernel(
         sq = row16_sum(sq); sk = row16_sum(sk); qd = row16_sum(qd); kd = row16_sum(kd);
         const float rq = rsqrtf(sq + kL2Eps), rk = rsqrtf(sk + kL2Eps);
         const float cq = rq * rq * rq * qd, ck = rk * rk * rk * kd;
-        const float a_gate = fast_exp2(A_log[h] * kLog2e);
         float dqo[8], dko[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             dqo[e] = scale * (rq * dqh[e] - cq * qv[e]);
             dko[e] = rk * dkh[e] - ck * kv[e];
-            const float sg = sigmoid_f(a_gate * (gv[e] + dtb[e]));
-            const float al = fast_exp2(lb * sg * kLog2e);
-            dgv[e] = dal[e] * al * lb * sg * (1.0f - sg) * a_gate;
-            cA = fmaf(dgv[e], gv[e] + dtb[e], cA);
         }
-        store_lane8(dq + tb, j, dqo);
-        store_lane8(dk + tb, j, dko);
-        store_lane8(dg + tb, j, dgv);
-        cA = row16_sum(cA);
-        if (j == 0) {
-            const float bb = sigmoid_f(beta_raw[(size_t)t * H + h]);
-            dbeta[(size_t)t * H + h] = db * bb * (1.0f - bb);
-        }
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dgv[e] = 0.f;
-    }
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sP[gid][chan(j, e)] = dgv[e];
-    if (j == 0) sP[gid][kHeadDim] = cA;
-    lds_barrier();
-    if (threadIdx.x <= kHeadDim) {
-        float s = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s += sP[r][threadIdx.x];
-        pp[((size_t)tblk * H + h) * (kHeadDim + 1) + threadIdx.x] = s;
+        store_lane8(dq + tbk, j, dqo);
+        store_lane8(dk + tbk, j, dko);
     }
 }
 
@@ -496,24 +516,25 @@ __global__ __launch_bounds__(256) void bwd_param_kernel(const float *__restrict_
 
 template <typename Tin, typename Tdo>
 hipError_t launch_backward_t(const BackwardArgs &a) {
+    const int Hk = a.Hk > 0 ? a.Hk : a.H;   // q/k heads (grouped value heads)
     const int64_t NH = (int64_t)a.N * a.H;
     const unsigned grid = (unsigned)(((NH + 7) / 8) * 64);
     bwd_ckpt_kernel<Tin><<<grid, 256, 0, a.stream>>>(
         (const Tin *)a.k, (const Tin *)a.v, a.g, a.beta_raw, a.A_log, a.dt_bias, a.lower_bound,
-        a.cu, a.N, a.H, a.h0, a.ckpt);
+        a.cu, a.N, a.H, Hk, a.h0, a.ckpt);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     bwd_reverse_kernel<Tin, Tdo><<<grid, 256, 0, a.stream>>>(
         (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v, a.g, a.beta_raw, a.A_log,
-        a.dt_bias, a.scale, a.lower_bound, a.cu, a.N, a.H, a.ckpt, (const Tdo *)a.dout, a.dht,
+        a.dt_bias, a.scale, a.lower_bound, a.cu, a.N, a.H, Hk, a.ckpt, (const Tdo *)a.dout, a.dht,
         a.dv, a.part, a.dh0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t ntb = (a.T + 15) / 16;
     if (ntb > 0) {
-        bwd_finalize_kernel<Tin><<<dim3((unsigned)ntb, (unsigned)a.H), 256, 0, a.stream>>>(
+        bwd_finalize_kernel<Tin><<<dim3((unsigned)ntb, (unsigned)Hk), 256, 0, a.stream>>>(
             (const Tin *)a.q, (const Tin *)a.k, a.g, a.beta_raw, a.A_log, a.dt_bias, a.scale,
-            a.lower_bound, a.T, a.H, a.part, a.dq, a.dk, a.dg, a.dbeta, a.pp);
+            a.lower_bound, a.T, a.H, Hk, a.part, a.dq, a.dk, a.dg, a.dbeta, a.pp);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const float *__restrict__ A_log, const float *__restrict__ dt_bias,
     float scale, float lower_bound, float *__restrict__ state, Tout *__restrict__ o,
     int H, const Tin *__restrict__ zg, const float *__restrict__ norm_w, float norm_eps,
-    const int32_t *__restrict__ slots, int num_slots)
+    const int32_t *__restrict__ slots, int num_slots, int Hk)
 {
     const int bh = blockIdx.x;                 // request * H + head
     const int h = bh % H;
@@ -67,14 +67,16 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     // Per-token vectors for this lane's 8 channels (each 16-lane row holds all 128):
     // entry e is channel ch(e) = 4j + e for e < 4 and 64 + 4j + (e - 4) otherwise.
     const size_t tb = (size_t)bh * kHeadDim;
+    // q and k of the request's q/k head h / (H / Hk) (grouped value heads; Hk = H without)
+    const size_t tbk = ((size_t)(bh / H) * Hk + h / (H / Hk)) * kHeadDim;
     float qv[8], kv[8], al[8];
     const float a_gate = fast_exp2(A_log[h] * kLog2e);
     float sqq = 0.f, skk = 0.f, sqk = 0.f;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
         const int ch = (e < 4) ? 4 * j + e : 64 + 4 * j + (e - 4);
-        qv[e] = to_f32(q[tb + ch]);
-        kv[e] = to_f32(k[tb + ch]);
+        qv[e] = to_f32(q[tbk + ch]);
+        kv[e] = to_f32(k[tbk + ch]);
         sqq += qv[e] * qv[e];
         skk += kv[e] * kv[e];
         sqk += qv[e] * kv[e];
@@ -143,12 +145,12 @@ static hipError_t launch_decode_t(const DecodeArgs &a) {
         decode_step_kernel<Tin, Tout, true><<<grid, 256, 0, a.stream>>>(
             (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v, a.g, a.beta_raw,
             a.A_log, a.dt_bias, a.scale, a.lower_bound, a.state, (Tout *)a.o, a.H,
-            (const Tin *)a.z, a.norm_w, a.norm_eps, a.slots, a.num_slots);
+            (const Tin *)a.z, a.norm_w, a.norm_eps, a.slots, a.num_slots, a.Hk > 0 ? a.Hk : a.H);
     else
         decode_step_kernel<Tin, Tout, false><<<grid, 256, 0, a.stream>>>(
             (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v, a.g, a.beta_raw,
             a.A_log, a.dt_bias, a.scale, a.lower_bound, a.state, (Tout *)a.o, a.H,
-            nullptr, nullptr, 0.f, a.slots, a.num_slots);
+            nullptr, nullptr, 0.f, a.slots, a.num_slots, a.Hk > 0 ? a.Hk : a.H);
     return hipGetLastError();
 }
 

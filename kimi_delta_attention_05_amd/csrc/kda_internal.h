@@ -14,6 +14,7 @@ struct DecodeArgs {
     float *state;
     void *o;
     int B, H;
+    int Hk = 0;                         // q/k heads (grouped value heads), as PrefillArgs
     bool in_bf16, out_bf16;
     hipStream_t stream;
     // output epilogue fused into the store (z == nullptr: none): RMS norm with
@@ -45,7 +46,8 @@ struct PrefillArgs {
     const int64_t *cu_seqlens;
     int N;
     int64_t T;
-    int H;
+    int H;               // value heads (v, g, beta, states, o)
+    int Hk = 0;          // q/k heads (H a multiple of it; value head h reads q/k head h / (H / Hk))
     int chunk;
     const float *h0;
     float *ht;
@@ -137,6 +139,7 @@ struct BackwardArgs {
     float scale, lower_bound;
     const int64_t *cu;                  // [N + 1]
     int N, H;
+    int Hk = 0;                         // q/k heads (grouped value heads), as PrefillArgs
     int64_t T;
     bool in_bf16, do_bf16;
     const float *h0;                    // [N, H, 128, 128] or NULL (zero)

@@ -205,12 +205,15 @@ __device__ __forceinline__ void stage_raw(const PrefillArgs &p, int h, int64_t t
     constexpr int P0 = PART == 1 ? 2 * RL::NQ16 : 0;
     constexpr int P1 = PART == 0 ? 2 * RL::NQ16 : 3 * RL::NQ16 + RL::NG16;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    // resources over rows t0 .. t0 + L - 1 of head h (token stride H rows)
+    // resources over rows t0 .. t0 + L - 1 of head h (token stride H rows; q and k
+    // of its q/k head h / (H / Hk), token stride Hk rows)
     const size_t row0 = (size_t)t0 * p.H + h;
+    const size_t rowk0 = (size_t)t0 * p.Hk + h / (p.H / p.Hk);
     const uint32_t hq = (uint32_t)p.H * RB, hg = (uint32_t)p.H * 512u;
+    const uint32_t hk = (uint32_t)p.Hk * RB;
     const uint32_t span = (uint32_t)(L - 1);
-    const i32x4 rq = make_rsrc((const unsigned char *)p.q + row0 * RB, span * hq + RB);
-    const i32x4 rk = make_rsrc((const unsigned char *)p.k + row0 * RB, span * hq + RB);
+    const i32x4 rq = make_rsrc((const unsigned char *)p.q + rowk0 * RB, span * hk + RB);
+    const i32x4 rk = make_rsrc((const unsigned char *)p.k + rowk0 * RB, span * hk + RB);
     const i32x4 rv = make_rsrc((const unsigned char *)p.v + row0 * RB, span * hq + RB);
     const i32x4 rg = make_rsrc(p.g + row0 * kHeadDim, span * hg + 512u);
 #pragma unroll
@@ -222,7 +225,7 @@ __device__ __forceinline__ void stage_raw(const PrefillArgs &p, int h, int64_t t
             const int arr = wbase / RL::NQ16;
             const uint32_t w = idx % (uint32_t)RL::NQ16;
             const uint32_t t = min(w / (uint32_t)PPR, span);
-            const uint32_t off = t * hq + (w % (uint32_t)PPR) * 16u;
+            const uint32_t off = t * (arr == 2 ? hq : hk) + (w % (uint32_t)PPR) * 16u;
             copy16_to_lds(arr == 0 ? rq : arr == 1 ? rk : rv, off, 0, lds + (size_t)wbase * 16);
         } else {
             const uint32_t w = idx - 3u * RL::NQ16;
@@ -374,8 +377,9 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
             } else {
                 const int tc = rv ? t : Lc - 1;
                 const size_t row = (size_t)(t0c + tc) * H + h;
-                rq.load((const Tin *)p.q + row * kHeadDim + c8);
-                rk.load((const Tin *)p.k + row * kHeadDim + c8);
+                const size_t rowk = (size_t)(t0c + tc) * p.Hk + h / (H / p.Hk);
+                rq.load((const Tin *)p.q + rowk * kHeadDim + c8);
+                rk.load((const Tin *)p.k + rowk * kHeadDim + c8);
                 rvv.load((const Tin *)p.v + row * kHeadDim + c8);
                 rg.load(p.g + row * kHeadDim + c8);
                 rb = p.beta_raw[row];
@@ -1265,8 +1269,9 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) graw[s][hf] = *(const f32x4 *)(gr + chan(s, hf));
         const float2 dt2 = *(const float2 *)(p.dt_bias + (size_t)h * kHeadDim + 2 * lane);
-        const Tin *qr = (const Tin *)p.q + row * kHeadDim;
-        const Tin *kr = (const Tin *)p.k + row * kHeadDim;
+        const size_t rowk = (size_t)(t0 + (rv ? r : L - 1)) * p.Hk + h / (H / p.Hk);
+        const Tin *qr = (const Tin *)p.q + rowk * kHeadDim;
+        const Tin *kr = (const Tin *)p.k + rowk * kHeadDim;
         const Tin *vr = (const Tin *)p.v + row * kHeadDim;
         bf16x8 qraw[4], kraw[4], vraw[4];
 #pragma unroll
@@ -1749,7 +1754,9 @@ static hipError_t launch_prefill_c(const PrefillArgs &a) {
     return a.out_bf16 ? launch_prefill_t<C, float, __bf16>(a) : launch_prefill_t<C, float, float>(a);
 }
 
-hipError_t launch_prefill(const PrefillArgs &a) {
+hipError_t launch_prefill(const PrefillArgs &args) {
+    PrefillArgs a = args;
+    if (a.Hk <= 0) a.Hk = a.H;          // no grouping: one q/k head per value head
     switch (a.chunk) {
         case 16: return launch_prefill_c<16>(a);
         case 32: return launch_prefill_c<32>(a);

@@ -26,7 +26,8 @@ EXPORTS = ("kda_version", "kda_status_string", "kda_last_error",
            "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_intra",
            "kda_chunk_fwd_inter", "kda_decode_step", "kda_decode_step_gated",
            "kda_decode_step_slots", "kda_output_norm_gate", "kda_short_conv",
-           "kda_backward_workspace_size", "kda_backward", "kda_check_cu_seqlens")
+           "kda_backward_workspace_size", "kda_backward", "kda_chunk_fwd_grouped",
+           "kda_decode_step_grouped", "kda_backward_grouped", "kda_check_cu_seqlens")
 
 NORM_EPS = 1e-5   # default epsilon of the output norm (the pages give none)
 
@@ -51,6 +52,8 @@ for _name in ("kda_chunk_fwd", "kda_chunk_fwd_intra", "kda_chunk_fwd_inter"):
     getattr(_lib, _name).argtypes = [_P, _P, _P, _P, _P, _P, _P, _f32, _f32, _P, _i32, _i64,
                                      _i32, _i32, _i32, _i32, ctypes.c_int, _P, _P, _P,
                                      ctypes.c_int, _P, _sz, _P]
+_lib.kda_chunk_fwd_grouped.restype = ctypes.c_int
+_lib.kda_chunk_fwd_grouped.argtypes = _lib.kda_chunk_fwd.argtypes + [_i32]
 _STAGE_FN = {None: _lib.kda_chunk_fwd, "intra": _lib.kda_chunk_fwd_intra,
              "inter": _lib.kda_chunk_fwd_inter}
 _lib.kda_decode_step.restype = ctypes.c_int
@@ -74,6 +77,14 @@ _lib.kda_backward.restype = ctypes.c_int
 _lib.kda_backward.argtypes = [_P, _P, _P, _P, _P, _P, _P, _f32, _f32, _P, _i32, _i64, _i32, _i32,
                               _i32, ctypes.c_int, _P, _P, ctypes.c_int, _P, _P, _P, _P, _P, _P,
                               _P, _P, _P, _P, _sz, _P]
+_lib.kda_decode_step_grouped.restype = ctypes.c_int
+_lib.kda_decode_step_grouped.argtypes = [_P, _P, _P, _P, _P, _P, _P, _f32, _f32, _P, _i32, _P, _P,
+                                         ctypes.c_int, _i32, _i32, _i32, _i32, _i32, ctypes.c_int,
+                                         _P, _P, _f32, _P]
+_lib.kda_backward_grouped.restype = ctypes.c_int
+_lib.kda_backward_grouped.argtypes = [_P, _P, _P, _P, _P, _P, _P, _f32, _f32, _P, _i32, _i64, _i32,
+                                      _i32, _i32, _i32, ctypes.c_int, _P, _P, ctypes.c_int, _P, _P,
+                                      _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
 _lib.kda_check_cu_seqlens.restype = ctypes.c_int
 _lib.kda_check_cu_seqlens.argtypes = [_P, _i32, _i64, _P]
 
@@ -157,21 +168,22 @@ def chunk_fwd(q, k, v, g, beta_raw, A_log, dt_bias, cu_seqlens, *, scale: float 
               stage: Optional[str] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise KDA prefill over packed sequences (libkda kda_chunk_fwd).
 
-    q, k, v: [T, H, 128] bf16 or fp32 (same dtype); g: [T, H, 128] fp32;
+    q, k: [T, H_qk, 128] and v: [T, H, 128], bf16 or fp32 (same dtype); H_qk < H
+    (a divisor) selects grouped value heads (kda_chunk_fwd_grouped); g: [T, H, 128] fp32;
     beta_raw: [T, H] fp32; A_log: [H] fp32; dt_bias: [H, 128] fp32;
     cu_seqlens: [N+1] int64 on the GPU; initial_state: [N, H, 128, 128] fp32 or None.
     Returns (o [T, H, 128] in o_dtype (default: q's dtype), final_state or None).
     stage: None runs both kernels; "intra" / "inter" run one stage (kda_chunk_fwd_intra /
     kda_chunk_fwd_inter), which must share the same workspace and arguments.
     """
-    T, H, K = q.shape
-    V = v.shape[2]
+    T, Hqk, K = q.shape
+    H, V = v.shape[1], v.shape[2]          # value heads (grouped value heads: a multiple of Hqk)
     N = cu_seqlens.numel() - 1
     in_dt = _dt(q)
     if scale is None:
         scale = 1.0 / math.sqrt(K)
-    _dev(q, "q", shape=(T, H, K))
-    _dev(k, "k", dtype=q.dtype, shape=(T, H, K))
+    _dev(q, "q", shape=(T, Hqk, K))
+    _dev(k, "k", dtype=q.dtype, shape=(T, Hqk, K))
     _dev(v, "v", dtype=q.dtype, shape=(T, H, V))
     _dev(g, "g", torch.float32, (T, H, K))
     _dev(beta_raw, "beta_raw", torch.float32, (T, H))
@@ -195,12 +207,17 @@ def chunk_fwd(q, k, v, g, beta_raw, A_log, dt_bias, cu_seqlens, *, scale: float 
         final_state = None
     need = workspace_size(T, N, H, chunk_size, q.dtype, K, V)
     ws = (workspace or Workspace(device)).get(need)
-    fn = _STAGE_FN[stage]
-    st = fn(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
-                            beta_raw.data_ptr(), A_log.data_ptr(), dt_bias.data_ptr(),
-                            float(scale), float(lower_bound), cu_seqlens.data_ptr(), N, T,
-                            H, K, V, int(chunk_size), in_dt, h0_ptr, ht_ptr, o_ptr,
-                            _dt(out), ws.data_ptr(), ws.numel(), _stream_ptr(device))
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta_raw.data_ptr(),
+            A_log.data_ptr(), dt_bias.data_ptr(), float(scale), float(lower_bound),
+            cu_seqlens.data_ptr(), N, T, H, K, V, int(chunk_size), in_dt, h0_ptr, ht_ptr, o_ptr,
+            _dt(out), ws.data_ptr(), ws.numel(), _stream_ptr(device))
+    if Hqk != H:
+        if stage is not None:
+            raise ValueError("grouped value heads run both stages (stage must be None)")
+        fn, args = _lib.kda_chunk_fwd_grouped, args + (Hqk,)
+    else:
+        fn = _STAGE_FN[stage]
+    st = fn(*args)
     _check(st, fn.__name__)
     return out, final_state
 
@@ -213,7 +230,8 @@ def decode_step(q, k, v, g, beta_raw, A_log, dt_bias, state, *, scale: float = N
                 slot_idx: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One T=1 decode step for B requests; `state` [B, H, 128, 128] fp32 is updated in place.
 
-    q, k, v: [B, H, 128] bf16 or fp32; g: [B, H, 128] fp32; beta_raw: [B, H] fp32.
+    q, k: [B, H_qk, 128] and v: [B, H, 128], bf16 or fp32 (H_qk < H: grouped value heads,
+    kda_decode_step_grouped); g: [B, H, 128] fp32; beta_raw: [B, H] fp32.
     Returns o [B, H, 128] in o_dtype (default: q's dtype). With `gate` (logits
     [B, H, 128] in q's dtype) and `norm_weight` ([128] fp32) the output epilogue
     of output_norm_gate is fused into the store (kda_decode_step_gated). With
@@ -221,12 +239,12 @@ def decode_step(q, k, v, g, beta_raw, A_log, dt_bias, state, *, scale: float = N
     request b uses entry slot_idx[b]; indices outside [0, S) mark padding
     requests (zero output, no state touched) (kda_decode_step_slots).
     """
-    B, H, K = q.shape
-    V = v.shape[2]
+    B, Hqk, K = q.shape
+    H, V = v.shape[1], v.shape[2]
     if scale is None:
         scale = 1.0 / math.sqrt(K)
-    _dev(q, "q", shape=(B, H, K))
-    _dev(k, "k", dtype=q.dtype, shape=(B, H, K))
+    _dev(q, "q", shape=(B, Hqk, K))
+    _dev(k, "k", dtype=q.dtype, shape=(B, Hqk, K))
     _dev(v, "v", dtype=q.dtype, shape=(B, H, V))
     _dev(g, "g", torch.float32, (B, H, K))
     _dev(beta_raw, "beta_raw", torch.float32, (B, H))
@@ -243,6 +261,22 @@ def decode_step(q, k, v, g, beta_raw, A_log, dt_bias, state, *, scale: float = N
     if out is None:
         out = torch.empty((B, H, V), dtype=o_dtype, device=q.device)
     _dev(out, "out", o_dtype, (B, H, V))
+    if Hqk != H:
+        zp = wp = None
+        if gate is not None:
+            _dev(gate, "gate", q.dtype, (B, H, V))
+            if norm_weight is None:
+                raise ValueError("norm_weight is required with gate")
+            _dev(norm_weight, "norm_weight", torch.float32, (V,))
+            zp, wp = gate.data_ptr(), norm_weight.data_ptr()
+        st = _lib.kda_decode_step_grouped(
+            q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta_raw.data_ptr(),
+            A_log.data_ptr(), dt_bias.data_ptr(), float(scale), float(lower_bound),
+            state.data_ptr(), int(state.shape[0]) if slot_idx is not None else 0,
+            None if slot_idx is None else slot_idx.data_ptr(), out.data_ptr(), _dt(out), B, H,
+            Hqk, K, V, _dt(q), zp, wp, float(norm_eps), _stream_ptr(q.device))
+        _check(st, "kda_decode_step_grouped")
+        return out
     if slot_idx is not None:
         zp = wp = None
         if gate is not None:
@@ -362,16 +396,18 @@ def backward(q, k, v, g, beta_raw, A_log, dt_bias, cu_seqlens, d_o, *, scale: fl
     """Training backward of the recurrence (kda_backward): gradients of
     sum(o * d_o) + sum(final_state * d_final_state) w.r.t. every input.
 
-    Inputs as chunk_fwd; d_o: [T, H, 128] bf16 or fp32; d_final_state: [N, H, 128, 128]
+    Inputs as chunk_fwd (q, k may have fewer heads: grouped value heads, dq and dk then
+    [T, H_qk, 128]); d_o: [T, H, 128] bf16 or fp32; d_final_state: [N, H, 128, 128]
     fp32 or None. Returns a dict of fp32 tensors dq, dk, dv, dg [T, H, 128], dbeta [T, H],
     dA_log [H], ddt_bias [H, 128] and dh0 [N, H, 128, 128] (None unless requested).
     """
-    T, H, K = q.shape
+    T, Hqk, K = q.shape
+    H = v.shape[1]
     N = cu_seqlens.numel() - 1
     if scale is None:
         scale = 1.0 / math.sqrt(K)
-    _dev(q, "q", shape=(T, H, K))
-    _dev(k, "k", dtype=q.dtype, shape=(T, H, K))
+    _dev(q, "q", shape=(T, Hqk, K))
+    _dev(k, "k", dtype=q.dtype, shape=(T, Hqk, K))
     _dev(v, "v", dtype=q.dtype, shape=(T, H, K))
     _dev(g, "g", torch.float32, (T, H, K))
     _dev(beta_raw, "beta_raw", torch.float32, (T, H))
@@ -385,7 +421,7 @@ def backward(q, k, v, g, beta_raw, A_log, dt_bias, cu_seqlens, d_o, *, scale: fl
     dhtp = None if d_final_state is None else _dev(d_final_state, "d_final_state", torch.float32,
                                                    (N, H, K, K))
     f32 = dict(dtype=torch.float32, device=dev)
-    out = dict(dq=torch.empty((T, H, K), **f32), dk=torch.empty((T, H, K), **f32),
+    out = dict(dq=torch.empty((T, Hqk, K), **f32), dk=torch.empty((T, Hqk, K), **f32),
                dv=torch.empty((T, H, K), **f32), dg=torch.empty((T, H, K), **f32),
                dbeta=torch.empty((T, H), **f32), dA_log=torch.empty((H,), **f32),
                ddt_bias=torch.empty((H, K), **f32),
@@ -393,15 +429,15 @@ def backward(q, k, v, g, beta_raw, A_log, dt_bias, cu_seqlens, d_o, *, scale: fl
     need = backward_workspace_size(T, N, H)
     ws = (workspace or Workspace(dev)).get(need)
     ptr = lambda t: None if t is None else t.data_ptr()
-    st = _lib.kda_backward(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+    st = _lib.kda_backward_grouped(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
                            beta_raw.data_ptr(), A_log.data_ptr(), dt_bias.data_ptr(), float(scale),
-                           float(lower_bound), cu_seqlens.data_ptr(), N, T, H, K, K, _dt(q), h0p,
+                           float(lower_bound), cu_seqlens.data_ptr(), N, T, H, Hqk, K, K, _dt(q), h0p,
                            d_o.data_ptr(), _dt(d_o), dhtp, out["dq"].data_ptr(),
                            out["dk"].data_ptr(), out["dv"].data_ptr(), out["dg"].data_ptr(),
                            out["dbeta"].data_ptr(), out["dA_log"].data_ptr(),
                            out["ddt_bias"].data_ptr(), ptr(out["dh0"]), ws.data_ptr(), ws.numel(),
                            _stream_ptr(dev))
-    _check(st, "kda_backward")
+    _check(st, "kda_backward_grouped")
     return out
 
 

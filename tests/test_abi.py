@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol(kda):
     assert set(syms) == set(kda.EXPORTS)
     for s in syms:
         assert hasattr(kda.lib, s), s
-    assert kda.version() == 103
+    assert kda.version() == 104
 
 
 def test_status_strings(kda):
@@ -219,6 +219,29 @@ def test_backward_workspace_size(kda):
     assert a % 256 == 0
     with pytest.raises(ValueError):
         kda.backward_workspace_size(16, 0, 1)
+
+
+def test_grouped_entry_points_reject_bad_groups(kda):
+    # H_qk must divide H (validation runs before any HIP call)
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE)
+    for hqk in (0, 3, 5, 9, -1):
+        st = kda.lib.kda_chunk_fwd_grouped(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.088, -5.0,
+                                           FAKE, 1, 17, 8, 128, 128, 16, kda.KDA_F32, None, None,
+                                           FAKE, kda.KDA_F32, 0x100000, 1 << 40, None, hqk)
+        assert st == 1 and b"H_qk" in kda.lib.kda_last_error()
+        st = kda.lib.kda_decode_step_grouped(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.088, -5.0,
+                                             FAKE, 0, None, FAKE, kda.KDA_F32, 4, 8, hqk, 128, 128,
+                                             kda.KDA_BF16, None, None, 1e-5, None)
+        assert st == 1
+        st = backward_call_grouped(kda, hqk)
+        assert st == 1
+
+
+def backward_call_grouped(kda, hqk):
+    return kda.lib.kda_backward_grouped(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.088, -5.0, FAKE,
+                                        1, 17, 8, hqk, 128, 128, kda.KDA_BF16, None, FAKE,
+                                        kda.KDA_BF16, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                        None, 0x100000, 1 << 40, None)
 
 
 def test_workspace_size_arithmetic(kda):
