@@ -278,6 +278,26 @@ kda_status_t kda_short_conv(const void *x, int64_t x_stride, const float *weight
                             int64_t channels, kda_dtype_t dtype, const void *state_in,
                             void *state_out, void *y, void *stream);
 /*
+ * Serving form of kda_short_conv: the conv states live in a pool of num_slots
+ * entries and sequence n uses entry slot_idx[n], read as its carried-in state
+ * and replaced by its final state (one decode token per request is a sequence
+ * of length 1; a prefill chunk continues a request's earlier chunks). A
+ * sequence whose index lies outside [0, num_slots) is padding: its outputs are
+ * written as zeros and no state is read or written. Two sequences naming the
+ * same entry in one call race (undefined result).
+ *
+ * state_pool : [num_slots, W - 1, channels] in dtype, 16-byte aligned, updated
+ *              in place (ignored when W == 1); must not overlap x or y
+ * slot_idx   : DEVICE pointer to num_seqs int32 entries, 4-byte aligned
+ * Everything else as for kda_short_conv. Makes no allocation, copy or
+ * synchronisation.
+ */
+kda_status_t kda_short_conv_slots(const void *x, int64_t x_stride, const float *weight, int32_t W,
+                                  const int64_t *cu_seqlens, int32_t num_seqs,
+                                  int64_t total_tokens, int64_t channels, kda_dtype_t dtype,
+                                  void *state_pool, int32_t num_slots, const int32_t *slot_idx,
+                                  void *y, void *stream);
+/*
  * Training backward of the recurrence (FlashInfer kda_backward page,
  * "Supported contract": gradients for q, k, v, the raw gate, raw beta, A_log,
  * dt_bias and the initial state, given the output adjoint; its persistent

@@ -117,7 +117,7 @@ kda_status_t decode_step_impl(const void *q, const void *k, const void *v,
 
 extern "C" {
 
-int kda_version(void) { return 104; }
+int kda_version(void) { return 105; }
 
 const char *kda_status_string(kda_status_t s) {
     switch (s) {
@@ -380,6 +380,53 @@ kda_status_t kda_short_conv(const void *x, int64_t x_stride, const float *weight
     a.bf16 = bf16; a.stream = (hipStream_t)stream;
     hipError_t e = kda::launch_short_conv(a);
     if (e != hipSuccess) return hip_fail(e, "kda_short_conv launch");
+    return ok();
+}
+
+kda_status_t kda_short_conv_slots(const void *x, int64_t x_stride, const float *weight, int32_t W,
+                                  const int64_t *cu_seqlens, int32_t num_seqs,
+                                  int64_t total_tokens, int64_t channels, kda_dtype_t dtype,
+                                  void *state_pool, int32_t num_slots, const int32_t *slot_idx,
+                                  void *y, void *stream) {
+    if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 1");
+    if (total_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens must be >= 0");
+    if (W < 1 || W > 4) return fail(KDA_ERR_UNSUPPORTED, "kernel size W must lie in [1, 4] (got " + std::to_string(W) + ")");
+    if (channels < 8 || channels % 8 != 0)
+        return fail(KDA_ERR_INVALID_ARG, "channels must be a positive multiple of 8");
+    if (x_stride < channels || x_stride % 8 != 0)
+        return fail(KDA_ERR_INVALID_ARG, "x_stride must be a multiple of 8 and >= channels");
+    if (!valid_dtype(dtype)) return fail(KDA_ERR_UNSUPPORTED, "unknown dtype");
+    if (!cu_seqlens || !weight) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens and weight must not be NULL");
+    if (total_tokens > 0 && (!x || !y)) return fail(KDA_ERR_INVALID_ARG, "x and y must not be NULL");
+    if (num_slots < 1) return fail(KDA_ERR_INVALID_ARG, "num_slots must be >= 1");
+    if (!slot_idx) return fail(KDA_ERR_INVALID_ARG, "slot_idx is NULL");
+    if (((uintptr_t)slot_idx & 3) != 0) return fail(KDA_ERR_INVALID_ARG, "slot_idx must be 4-byte aligned");
+    if (W > 1 && !state_pool) return fail(KDA_ERR_INVALID_ARG, "state_pool is NULL");
+    if (W == 1) state_pool = nullptr;
+    kda_status_t st = check_aligned16({{x, "x"}, {y, "y"}, {state_pool, "state_pool"}});
+    if (st != KDA_OK) return st;
+    if (((uintptr_t)weight & 3) != 0 || ((uintptr_t)cu_seqlens & 7) != 0)
+        return fail(KDA_ERR_INVALID_ARG, "weight must be 4-byte and cu_seqlens 8-byte aligned");
+    const bool bf16 = dtype == KDA_BF16;
+    if (kda::short_conv_blocks(total_tokens, channels, bf16) > (int64_t)0x7fffffff ||
+        kda::short_conv_state_blocks(num_seqs, channels) > (int64_t)0x7fffffff)
+        return fail(KDA_ERR_INVALID_ARG, "total_tokens * channels too large for one launch");
+    const uintptr_t es = bf16 ? 2 : 4;
+    struct Range { uintptr_t lo, hi; };
+    auto range = [](const void *p, uintptr_t bytes) { return Range{(uintptr_t)p, (uintptr_t)p + bytes}; };
+    auto overlap = [](Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; };
+    const Range rx = total_tokens > 0 ? range(x, ((uintptr_t)(total_tokens - 1) * x_stride + channels) * es) : Range{0, 0};
+    const Range ry = total_tokens > 0 ? range(y, (uintptr_t)total_tokens * channels * es) : Range{0, 0};
+    const Range rp = state_pool ? range(state_pool, (uintptr_t)num_slots * (W - 1) * channels * es) : Range{0, 0};
+    if (overlap(ry, rx) || overlap(ry, rp) || overlap(rp, rx))
+        return fail(KDA_ERR_INVALID_ARG, "y, x and state_pool must not overlap");
+
+    kda::ShortConvArgs a;
+    a.x = x; a.x_stride = x_stride; a.w = weight; a.W = W; a.cu = cu_seqlens; a.N = num_seqs;
+    a.T = total_tokens; a.channels = channels; a.st_in = state_pool; a.st_out = state_pool; a.y = y;
+    a.slots = slot_idx; a.num_slots = num_slots; a.bf16 = bf16; a.stream = (hipStream_t)stream;
+    hipError_t e = kda::launch_short_conv(a);
+    if (e != hipSuccess) return hip_fail(e, "kda_short_conv_slots launch");
     return ok();
 }
 

@@ -128,6 +128,11 @@ struct ShortConvArgs {
     const void *st_in = nullptr;        // [N, W - 1, channels] or NULL (zero history)
     void *st_out = nullptr;             // [N, W - 1, channels] or NULL; may equal st_in
     void *y = nullptr;                  // [T, channels]
+    // state pool addressing (slots == nullptr: states indexed by sequence): sequence
+    // n uses pool entry slots[n] (device int32), padding if outside [0, num_slots);
+    // st_in == st_out == the pool
+    const int32_t *slots = nullptr;
+    int num_slots = 0;
     bool bf16 = false;
     hipStream_t stream = nullptr;
 };

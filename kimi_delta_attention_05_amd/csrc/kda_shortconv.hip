@@ -104,7 +104,8 @@ __global__ __launch_bounds__(kConvThreads) void short_conv_kernel(
     const T *__restrict__ x, int64_t x_stride, const float *__restrict__ w,
     const int64_t *__restrict__ cu, int N, int64_t T_total, int64_t channels,
     int64_t nstrips, int64_t per_xcd, int64_t nlogical,
-    const T *__restrict__ st_in, T *__restrict__ st_out, T *__restrict__ y)
+    const T *__restrict__ st_in, T *__restrict__ st_out, T *__restrict__ y,
+    const int32_t *__restrict__ slots, int num_slots)
 {
     constexpr int S = ConvStrip<T>::S;
     const int64_t L = xcd_logical(blockIdx.x, per_xcd);
@@ -125,7 +126,21 @@ __global__ __launch_bounds__(kConvThreads) void short_conv_kernel(
     int n = seq_of(cu, N, t0);
     int64_t s0 = cu[n], s1 = cu[n + 1];
 
+    // with a state pool, sequence n's conv state is pool entry slots[n]; an
+    // entry outside [0, num_slots) marks a padding sequence (zero outputs, no
+    // state read)
+    auto state_row = [&](int m) -> int64_t { return slots ? (int64_t)slots[m] : (int64_t)m; };
+    auto padding = [&](int m) -> bool {
+        return slots && (slots[m] < 0 || slots[m] >= num_slots);
+    };
+
     if (t0 + S < T_total && t0 - s0 >= W - 1 && t0 + S <= s1) {
+        if (padding(n)) {
+            const float zero[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int j = 0; j < S; ++j) store8<T>(y + (t0 + j) * channels + c, zero);
+            return;
+        }
         // Every window of the strip lies inside one sequence: a plain sliding
         // window. Rows t0 - (W - 1) .. t0 + S - 1 are loaded up front (kept
         // packed) and each is converted to fp32 once, as it enters the window.
@@ -187,6 +202,11 @@ __global__ __launch_bounds__(kConvThreads) void short_conv_kernel(
             ++n; s0 = s1; s1 = cu[n + 1];
             if (st_out && s1 == s0) pass_state_on_w<T, W>(st_in, st_out, n, channels, c);   // empty
         }
+        if (padding(n)) {
+            const float zero[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            store8<T>(y + t * channels + c, zero);
+            continue;
+        }
         float win[W][8];
 #pragma unroll
         for (int i = 0; i < W; ++i) {
@@ -195,7 +215,7 @@ __global__ __launch_bounds__(kConvThreads) void short_conv_kernel(
 #pragma unroll
                 for (int e = 0; e < 8; ++e) win[i][e] = xr[j + i][e];
             } else if (st_in) {
-                load8(st_in + ((int64_t)n * (W - 1) + (p - s0 + W - 1)) * channels + c, win[i]);
+                load8(st_in + (state_row(n) * (W - 1) + (p - s0 + W - 1)) * channels + c, win[i]);
             } else {
 #pragma unroll
                 for (int e = 0; e < 8; ++e) win[i][e] = 0.f;
@@ -223,12 +243,18 @@ __global__ __launch_bounds__(kConvThreads) void short_conv_kernel(
 template <typename T, int W>
 __global__ __launch_bounds__(kConvThreads) void final_state_kernel(
     const T *__restrict__ x, int64_t x_stride, const int64_t *__restrict__ cu, int N,
-    int64_t channels, int64_t ncb, const T *st_in, T *st_out)
+    int64_t channels, int64_t ncb, const T *st_in, T *st_out, const int32_t *slots,
+    int num_slots)
 {
     const int64_t n = blockIdx.x / ncb;
     const int64_t cb = blockIdx.x - n * ncb;
     const int64_t c = cb * kConvChanPerBlock + 8 * (int64_t)threadIdx.x;
     if (n >= N || c >= channels) return;
+    int64_t srow = n;                                 // state row: n, or its pool entry
+    if (slots) {
+        srow = slots[n];
+        if (srow < 0 || srow >= num_slots) return;    // padding: no state touched
+    }
     const int64_t s0 = cu[n], len = cu[n + 1] - s0;
     float rows[W - 1][8];
 #pragma unroll
@@ -237,14 +263,14 @@ __global__ __launch_bounds__(kConvThreads) void final_state_kernel(
         if (p >= 0) {
             load8(x + (s0 + p) * x_stride + c, rows[r]);
         } else if (st_in) {
-            load8(st_in + (n * (W - 1) + (W - 1) + p) * channels + c, rows[r]);
+            load8(st_in + (srow * (W - 1) + (W - 1) + p) * channels + c, rows[r]);
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) rows[r][e] = 0.f;
         }
     }
 #pragma unroll
-    for (int r = 0; r < W - 1; ++r) store8<T>(st_out + (n * (W - 1) + r) * channels + c, rows[r]);
+    for (int r = 0; r < W - 1; ++r) store8<T>(st_out + (srow * (W - 1) + r) * channels + c, rows[r]);
 }
 
 template <typename T, int W>
@@ -254,14 +280,15 @@ hipError_t launch_conv_w(const ShortConvArgs &a) {
     // the final conv state is written by the conv kernel itself unless it
     // replaces the carried-in state in place (other strips may still read
     // that) or there are no tokens: then a second kernel writes it afterwards
-    const bool fused_state = W > 1 && a.st_out && a.st_out != a.st_in && a.T > 0;
+    const bool fused_state = W > 1 && a.st_out && a.st_out != a.st_in && a.T > 0 && !a.slots;
     if (a.T > 0) {
         const int64_t nstrips = (a.T + S - 1) / S;
         const int64_t nlogical = nstrips * ncb;
         const int64_t per = (nlogical + 7) / 8;
         short_conv_kernel<T, W><<<(unsigned)(8 * per), kConvThreads, 0, a.stream>>>(
             (const T *)a.x, a.x_stride, a.w, a.cu, a.N, a.T, a.channels, nstrips, per, nlogical,
-            (const T *)a.st_in, fused_state ? (T *)a.st_out : nullptr, (T *)a.y);
+            (const T *)a.st_in, fused_state ? (T *)a.st_out : nullptr, (T *)a.y, a.slots,
+            a.num_slots);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -269,7 +296,7 @@ hipError_t launch_conv_w(const ShortConvArgs &a) {
         if (a.st_out && !fused_state) {
             final_state_kernel<T, W><<<(unsigned)(a.N * ncb), kConvThreads, 0, a.stream>>>(
                 (const T *)a.x, a.x_stride, a.cu, a.N, a.channels, ncb, (const T *)a.st_in,
-                (T *)a.st_out);
+                (T *)a.st_out, a.slots, a.num_slots);
             return hipGetLastError();
         }
     }

@@ -26,6 +26,7 @@ EXPORTS = ("kda_version", "kda_status_string", "kda_last_error",
            "kda_chunk_fwd_workspace_size", "kda_chunk_fwd", "kda_chunk_fwd_intra",
            "kda_chunk_fwd_inter", "kda_decode_step", "kda_decode_step_gated",
            "kda_decode_step_slots", "kda_output_norm_gate", "kda_short_conv",
+           "kda_short_conv_slots",
            "kda_backward_workspace_size", "kda_backward", "kda_chunk_fwd_grouped",
            "kda_decode_step_grouped", "kda_backward_grouped", "kda_check_cu_seqlens")
 
@@ -71,6 +72,9 @@ _lib.kda_output_norm_gate.argtypes = [_P, _P, _P, _f32, _i64, _i32, ctypes.c_int
 _lib.kda_short_conv.restype = ctypes.c_int
 _lib.kda_short_conv.argtypes = [_P, _i64, _P, _i32, _P, _i32, _i64, _i64, ctypes.c_int, _P, _P,
                                 _P, _P]
+_lib.kda_short_conv_slots.restype = ctypes.c_int
+_lib.kda_short_conv_slots.argtypes = [_P, _i64, _P, _i32, _P, _i32, _i64, _i64, ctypes.c_int, _P,
+                                      _i32, _P, _P, _P]
 _lib.kda_backward_workspace_size.restype = _sz
 _lib.kda_backward_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32]
 _lib.kda_backward.restype = ctypes.c_int
@@ -341,7 +345,9 @@ def output_norm_gate(o: torch.Tensor, gate: torch.Tensor, norm_weight: torch.Ten
 def short_conv(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tensor, *,
                initial_state: Optional[torch.Tensor] = None, output_final_state: bool = False,
                final_state: Optional[torch.Tensor] = None,
-               out: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+               out: Optional[torch.Tensor] = None, state_pool: Optional[torch.Tensor] = None,
+               slot_idx: Optional[torch.Tensor] = None
+               ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Front end for one of q, k, v (kda_short_conv): causal depthwise short
     conv along time over packed sequences, then SiLU.
 
@@ -351,9 +357,15 @@ def short_conv(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tensor, 
     initial_state / final_state: [N, W-1, *x.shape[1:]] in x's dtype (the last
     W - 1 inputs of each sequence so far, oldest first); final_state may be
     initial_state itself. Returns (y with x's shape, contiguous; final_state or None).
+    With `slot_idx` (int32 [N] on the GPU) the states live in `state_pool`
+    [S, W-1, *x.shape[1:]] instead, sequence n using entry slot_idx[n], updated in
+    place (kda_short_conv_slots); indices outside [0, S) mark padding sequences
+    (zero outputs, no state touched). Returns (y, state_pool).
     """
     if not isinstance(x, torch.Tensor) or not x.is_cuda:
         raise RuntimeError("x must be a GPU tensor (libkda has no CPU path)")
+    if slot_idx is not None:
+        return _short_conv_slots(x, weight, cu_seqlens, state_pool, slot_idx, out)
     T = x.shape[0]
     feat = tuple(x.shape[1:])
     C = int(math.prod(feat))
@@ -380,6 +392,35 @@ def short_conv(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: torch.Tensor, 
                              out.data_ptr() if T else None, _stream_ptr(x.device))
     _check(st, "kda_short_conv")
     return out, final_state
+
+
+def _short_conv_slots(x, weight, cu_seqlens, state_pool, slot_idx, out):
+    T = x.shape[0]
+    feat = tuple(x.shape[1:])
+    C = int(math.prod(feat))
+    N = cu_seqlens.numel() - 1
+    if x.dim() < 2 or (T > 0 and x[0].numel() > 0 and not x[0].is_contiguous()):
+        raise ValueError("x must be [T, ...] with contiguous rows")
+    stride = x.stride(0) if T > 1 else C
+    W = weight.shape[-1]
+    _dev(weight, "weight", torch.float32, feat + (W,))
+    _dev(cu_seqlens, "cu_seqlens", torch.int64, (N + 1,))
+    _dev(slot_idx, "slot_idx", torch.int32, (N,))
+    if state_pool is None:
+        raise ValueError("state_pool is required with slot_idx")
+    _dev(state_pool, "state_pool", x.dtype)
+    if tuple(state_pool.shape[1:]) != (W - 1,) + feat:
+        raise ValueError("state_pool must be [S, %d, %s]" % (W - 1, ", ".join(map(str, feat))))
+    if out is None:
+        out = torch.empty((T,) + feat, dtype=x.dtype, device=x.device)
+    _dev(out, "out", x.dtype, (T,) + feat)
+    st = _lib.kda_short_conv_slots(x.data_ptr() if T else None, int(stride), weight.data_ptr(),
+                                   int(W), cu_seqlens.data_ptr(), N, int(T), C, _dt(x),
+                                   state_pool.data_ptr() if state_pool.numel() else None,
+                                   int(state_pool.shape[0]), slot_idx.data_ptr(),
+                                   out.data_ptr() if T else None, _stream_ptr(x.device))
+    _check(st, "kda_short_conv_slots")
+    return out, state_pool
 
 
 def backward_workspace_size(total_tokens: int, num_seqs: int, H: int) -> int:

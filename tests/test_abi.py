@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol(kda):
     assert set(syms) == set(kda.EXPORTS)
     for s in syms:
         assert hasattr(kda.lib, s), s
-    assert kda.version() == 104
+    assert kda.version() == 105
 
 
 def test_status_strings(kda):
@@ -178,6 +178,25 @@ def short_conv_call(kda, **kw):
 ])
 def test_short_conv_rejects(kda, kw, status):
     assert short_conv_call(kda, **kw) == status
+    assert kda.lib.kda_last_error()
+
+
+def short_conv_slots_call(kda, **kw):
+    a = dict(x=FAKE, xs=256, w=FAKE, W=4, cu=FAKE, N=2, T=100, C=256, dt=kda.KDA_BF16,
+             pool=1 << 29, S=4, idx=1 << 28, y=1 << 30, stream=None)
+    a.update(kw)
+    return kda.lib.kda_short_conv_slots(a["x"], a["xs"], a["w"], a["W"], a["cu"], a["N"], a["T"],
+                                        a["C"], a["dt"], a["pool"], a["S"], a["idx"], a["y"],
+                                        a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), 1), (dict(W=5), 2), (dict(C=12), 1), (dict(S=0), 1), (dict(idx=None), 1),
+    (dict(idx=(1 << 28) + 2), 1), (dict(pool=None), 1), (dict(pool=(1 << 29) + 8), 1),
+    (dict(y=(1 << 29) + 64), 1), (dict(pool=FAKE + 512), 1), (dict(dt=3), 2),
+])
+def test_short_conv_slots_rejects(kda, kw, status):
+    assert short_conv_slots_call(kda, **kw) == status
     assert kda.lib.kda_last_error()
 
 

@@ -189,3 +189,37 @@ def test_front_end_then_prefill_then_epilogue(kda):
     print("front end + prefill + epilogue: o %.3e y %.3e" % (e_o, e_y), flush=True)
     assert e_o <= 2e-2 and e_y <= 2e-2
     assert max_err_rel_rms(ht, rht) <= 2e-2
+
+
+def test_short_conv_state_pool_serving(kda):
+    # a pool of conv states addressed per sequence: a prefill chunk of three
+    # requests, then four decode steps of one token each over a shuffled subset
+    # with a padding entry; against the oracle run per request with the pool
+    # entry as its carried-in state
+    H, W, S = 2, 4, 6
+    C = H * 128
+    gen = torch.Generator().manual_seed(21)
+    pool = torch.randn(S, W - 1, H, 128, generator=gen).to(torch.bfloat16)
+    w = kda_inputs.make_short_conv([1], H, W, seed=22)[1]
+    ref_pool = pool.clone()
+    pool_d = pool.to(DEV)
+    calls = [([5, 1, 12], [4, 0, 2]), ([1, 1, 1], [2, 4, 0]), ([1, 1, 1, 1], [0, 9, 4, 2]),
+             ([1, 1], [-1, 2]), ([1, 1, 1], [4, 0, 2])]
+    for step, (lens, slots) in enumerate(calls):
+        x = torch.randn(sum(lens), H, 128, generator=gen).to(torch.bfloat16)
+        cu = torch.tensor([0] + list(np.cumsum(lens)), dtype=torch.int64)
+        idx = torch.tensor(slots, dtype=torch.int32)
+        y, _ = kda.short_conv(x.to(DEV), w.to(DEV), cu.to(DEV), state_pool=pool_d,
+                              slot_idx=idx.to(DEV))
+        torch.cuda.synchronize()
+        yg = to_np(y)
+        for n, sl in enumerate(slots):
+            s0, s1 = int(cu[n]), int(cu[n + 1])
+            if not 0 <= sl < S:
+                assert not np.any(yg[s0:s1]), (step, n)          # padding: zero outputs
+                continue
+            ry, rf = oracle.short_conv_silu(x[s0:s1], w, np.array([0, s1 - s0]),
+                                            state=ref_pool[sl:sl + 1])
+            assert check_y(y[s0:s1], ry, x[s0:s1], w, ref_pool[sl:sl + 1]) <= 1.0, (step, n)
+            ref_pool[sl] = torch.from_numpy(rf[0]).to(torch.bfloat16)
+        np.testing.assert_array_equal(to_np(pool_d), to_np(ref_pool))
