@@ -298,6 +298,23 @@ __device__ __forceinline__ void store8<__bf16>(__bf16 *p, const float (&x)[8]) {
     *(bf16x8 *)p = v;
 }
 
+// The same as store8 with a non-temporal hint: for outputs that no later
+// access of the same kernel reads (streamed to HBM instead of kept in cache).
+template <typename T>
+__device__ __forceinline__ void store8_nt(T *p, const float (&x)[8]);
+template <>
+__device__ __forceinline__ void store8_nt<float>(float *p, const float (&x)[8]) {
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, (f32x4 *)p);
+    __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, (f32x4 *)p + 1);
+}
+template <>
+__device__ __forceinline__ void store8_nt<__bf16>(__bf16 *p, const float (&x)[8]) {
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (__bf16)x[e];
+    __builtin_nontemporal_store(v, (bf16x8 *)p);
+}
+
 // Power of two 2^e with e = ceil(log2(m)) - target, so that m * 2^-e <= 2^target;
 // returns 1 for m == 0 or non-finite m.
 __device__ __forceinline__ float pow2_scale_for(float m, int target) {

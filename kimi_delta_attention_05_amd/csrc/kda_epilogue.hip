@@ -33,7 +33,7 @@ __global__ __launch_bounds__(256) void norm_gate_kernel(const T *__restrict__ o,
     float out[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[e] = x[e] * r * wv[e] * sigmoid_f(g[e]);
-    if (valid) store8<T>(y + base, out);
+    if (valid) store8_nt<T>(y + base, out);
 }
 
 hipError_t launch_norm_gate(const NormGateArgs &a) {

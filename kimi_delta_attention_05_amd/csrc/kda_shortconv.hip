@@ -19,7 +19,8 @@
 // into registers (16- or 32-byte loads, consecutive lanes on consecutive
 // channels) and slides the W-row window down the strip, so every input row is
 // read once per strip, converted to fp32 once, and every output row written
-// once. HBM-bound. Strips of one channel block follow each other on one XCD
+// once, with non-temporal stores (no access of this kernel reads y, and the
+// stores then leave the inputs' lines in the caches). HBM-bound. Strips of one channel block follow each other on one XCD
 // (blocks are dealt to the 8 XCDs round-robin), so the W - 1 halo rows of a
 // strip were fetched into that XCD's L2 by the strip before it. The few strips
 // that touch a sequence start (or the end of the input) take a general path
@@ -163,7 +164,7 @@ __global__ __launch_bounds__(kConvThreads) void short_conv_kernel(
             for (int e = 0; e < 8; ++e) win[W - 1][e] = xr[j + W - 1][e];
             float out[8];
             conv_silu_store_prep<W>(wt, win, out);
-            store8<T>(y + (t0 + j) * channels + c, out);
+            store8_nt<T>(y + (t0 + j) * channels + c, out);
 #pragma unroll
             for (int i = 0; i < W - 1; ++i) {
 #pragma unroll
@@ -223,7 +224,7 @@ __global__ __launch_bounds__(kConvThreads) void short_conv_kernel(
         }
         float out[8];
         conv_silu_store_prep<W>(wt, win, out);
-        store8<T>(y + t * channels + c, out);
+        store8_nt<T>(y + t * channels + c, out);
         if (st_out && t == s1 - 1) {
             // last token of its sequence: the final conv state is the window's
             // last W - 1 rows (reaching into the carried-in state if short)
