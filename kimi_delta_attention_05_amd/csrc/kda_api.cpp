@@ -55,6 +55,39 @@ kda_status_t check_aligned16(std::initializer_list<std::pair<const void *, const
     return KDA_OK;
 }
 
+// Byte ranges of caller buffers, for the checks that outputs do not overlap
+// inputs other threads still read. A NULL pointer or zero size is empty.
+struct ByteRange {
+    uintptr_t lo = 0, hi = 0;
+};
+ByteRange byte_range(const void *p, uintptr_t bytes) {
+    return p && bytes ? ByteRange{(uintptr_t)p, (uintptr_t)p + bytes} : ByteRange{};
+}
+bool overlaps(ByteRange a, ByteRange b) { return a.lo < b.hi && b.lo < a.hi; }
+
+// Argument checks shared by the two front-end entry points.
+kda_status_t check_short_conv(const void *x, int64_t x_stride, const float *weight, int32_t W,
+                              const int64_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                              int64_t channels, kda_dtype_t dtype, const void *y) {
+    if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 1");
+    if (total_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens must be >= 0");
+    if (W < 1 || W > 4)
+        return fail(KDA_ERR_UNSUPPORTED, "kernel size W must lie in [1, 4] (got " + std::to_string(W) + ")");
+    if (channels < 8 || channels % 8 != 0)
+        return fail(KDA_ERR_INVALID_ARG, "channels must be a positive multiple of 8");
+    if (x_stride < channels || x_stride % 8 != 0)
+        return fail(KDA_ERR_INVALID_ARG, "x_stride must be a multiple of 8 and >= channels");
+    if (!valid_dtype(dtype)) return fail(KDA_ERR_UNSUPPORTED, "unknown dtype");
+    if (!cu_seqlens || !weight) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens and weight must not be NULL");
+    if (total_tokens > 0 && (!x || !y)) return fail(KDA_ERR_INVALID_ARG, "x and y must not be NULL");
+    if (((uintptr_t)weight & 3) != 0 || ((uintptr_t)cu_seqlens & 7) != 0)
+        return fail(KDA_ERR_INVALID_ARG, "weight must be 4-byte and cu_seqlens 8-byte aligned");
+    if (kda::short_conv_blocks(total_tokens, channels, dtype == KDA_BF16) > (int64_t)0x7fffffff ||
+        kda::short_conv_state_blocks(num_seqs, channels) > (int64_t)0x7fffffff)
+        return fail(KDA_ERR_INVALID_ARG, "total_tokens * channels too large for one launch");
+    return KDA_OK;
+}
+
 // Grouped value heads: H value heads share H_qk q/k heads, H a multiple of H_qk.
 kda_status_t check_groups(int64_t H, int64_t H_qk) {
     if (H_qk < 1 || H_qk > H || H % H_qk != 0)
@@ -338,40 +371,24 @@ kda_status_t kda_short_conv(const void *x, int64_t x_stride, const float *weight
                             const int64_t *cu_seqlens, int32_t num_seqs, int64_t total_tokens,
                             int64_t channels, kda_dtype_t dtype, const void *state_in,
                             void *state_out, void *y, void *stream) {
-    if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 1");
-    if (total_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens must be >= 0");
-    if (W < 1 || W > 4) return fail(KDA_ERR_UNSUPPORTED, "kernel size W must lie in [1, 4] (got " + std::to_string(W) + ")");
-    if (channels < 8 || channels % 8 != 0)
-        return fail(KDA_ERR_INVALID_ARG, "channels must be a positive multiple of 8");
-    if (x_stride < channels || x_stride % 8 != 0)
-        return fail(KDA_ERR_INVALID_ARG, "x_stride must be a multiple of 8 and >= channels");
-    if (!valid_dtype(dtype)) return fail(KDA_ERR_UNSUPPORTED, "unknown dtype");
-    if (!cu_seqlens || !weight) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens and weight must not be NULL");
-    if (total_tokens > 0 && (!x || !y)) return fail(KDA_ERR_INVALID_ARG, "x and y must not be NULL");
-    if (W == 1) { state_in = nullptr; state_out = nullptr; }   // no history to carry
-    kda_status_t st = check_aligned16({{x, "x"}, {y, "y"}, {state_in, "state_in"}, {state_out, "state_out"}});
+    kda_status_t st = check_short_conv(x, x_stride, weight, W, cu_seqlens, num_seqs, total_tokens,
+                                       channels, dtype, y);
     if (st != KDA_OK) return st;
-    if (((uintptr_t)weight & 3) != 0 || ((uintptr_t)cu_seqlens & 7) != 0)
-        return fail(KDA_ERR_INVALID_ARG, "weight must be 4-byte and cu_seqlens 8-byte aligned");
-    const bool bf16 = dtype == KDA_BF16;
-    if (kda::short_conv_blocks(total_tokens, channels, bf16) > (int64_t)0x7fffffff ||
-        kda::short_conv_state_blocks(num_seqs, channels) > (int64_t)0x7fffffff)
-        return fail(KDA_ERR_INVALID_ARG, "total_tokens * channels too large for one launch");
+    if (W == 1) { state_in = nullptr; state_out = nullptr; }   // no history to carry
+    st = check_aligned16({{x, "x"}, {y, "y"}, {state_in, "state_in"}, {state_out, "state_out"}});
+    if (st != KDA_OK) return st;
     // y is written while x and the carried-in state are read by other threads,
     // so no output may overlap an input; the final state may only be the
     // carried-in state itself (updated in place)
+    const bool bf16 = dtype == KDA_BF16;
     const uintptr_t es = bf16 ? 2 : 4;
-    struct Range { uintptr_t lo, hi; };
-    auto range = [](const void *p, uintptr_t bytes) { return Range{(uintptr_t)p, (uintptr_t)p + bytes}; };
-    auto overlap = [](Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; };
-    const Range rx = total_tokens > 0 ? range(x, ((uintptr_t)(total_tokens - 1) * x_stride + channels) * es) : Range{0, 0};
-    const Range ry = total_tokens > 0 ? range(y, (uintptr_t)total_tokens * channels * es) : Range{0, 0};
+    const ByteRange rx = total_tokens > 0 ? byte_range(x, ((uintptr_t)(total_tokens - 1) * x_stride + channels) * es) : ByteRange{};
+    const ByteRange ry = byte_range(y, (uintptr_t)total_tokens * channels * es);
     const uintptr_t sbytes = (uintptr_t)num_seqs * (W - 1) * channels * es;
-    const Range rsi = state_in ? range(state_in, sbytes) : Range{0, 0};
-    const Range rso = state_out ? range(state_out, sbytes) : Range{0, 0};
-    if (overlap(ry, rx) || overlap(ry, rsi) || overlap(ry, rso))
+    const ByteRange rsi = byte_range(state_in, sbytes), rso = byte_range(state_out, sbytes);
+    if (overlaps(ry, rx) || overlaps(ry, rsi) || overlaps(ry, rso))
         return fail(KDA_ERR_INVALID_ARG, "y must not overlap x or a conv state");
-    if (overlap(rso, rx) || (overlap(rso, rsi) && state_out != state_in))
+    if (overlaps(rso, rx) || (overlaps(rso, rsi) && state_out != state_in))
         return fail(KDA_ERR_INVALID_ARG, "state_out must not overlap x, and may overlap state_in only by being it");
 
     kda::ShortConvArgs a;
@@ -388,37 +405,22 @@ kda_status_t kda_short_conv_slots(const void *x, int64_t x_stride, const float *
                                   int64_t total_tokens, int64_t channels, kda_dtype_t dtype,
                                   void *state_pool, int32_t num_slots, const int32_t *slot_idx,
                                   void *y, void *stream) {
-    if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 1");
-    if (total_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens must be >= 0");
-    if (W < 1 || W > 4) return fail(KDA_ERR_UNSUPPORTED, "kernel size W must lie in [1, 4] (got " + std::to_string(W) + ")");
-    if (channels < 8 || channels % 8 != 0)
-        return fail(KDA_ERR_INVALID_ARG, "channels must be a positive multiple of 8");
-    if (x_stride < channels || x_stride % 8 != 0)
-        return fail(KDA_ERR_INVALID_ARG, "x_stride must be a multiple of 8 and >= channels");
-    if (!valid_dtype(dtype)) return fail(KDA_ERR_UNSUPPORTED, "unknown dtype");
-    if (!cu_seqlens || !weight) return fail(KDA_ERR_INVALID_ARG, "cu_seqlens and weight must not be NULL");
-    if (total_tokens > 0 && (!x || !y)) return fail(KDA_ERR_INVALID_ARG, "x and y must not be NULL");
+    kda_status_t st = check_short_conv(x, x_stride, weight, W, cu_seqlens, num_seqs, total_tokens,
+                                       channels, dtype, y);
+    if (st != KDA_OK) return st;
     if (num_slots < 1) return fail(KDA_ERR_INVALID_ARG, "num_slots must be >= 1");
     if (!slot_idx) return fail(KDA_ERR_INVALID_ARG, "slot_idx is NULL");
     if (((uintptr_t)slot_idx & 3) != 0) return fail(KDA_ERR_INVALID_ARG, "slot_idx must be 4-byte aligned");
     if (W > 1 && !state_pool) return fail(KDA_ERR_INVALID_ARG, "state_pool is NULL");
     if (W == 1) state_pool = nullptr;
-    kda_status_t st = check_aligned16({{x, "x"}, {y, "y"}, {state_pool, "state_pool"}});
+    st = check_aligned16({{x, "x"}, {y, "y"}, {state_pool, "state_pool"}});
     if (st != KDA_OK) return st;
-    if (((uintptr_t)weight & 3) != 0 || ((uintptr_t)cu_seqlens & 7) != 0)
-        return fail(KDA_ERR_INVALID_ARG, "weight must be 4-byte and cu_seqlens 8-byte aligned");
     const bool bf16 = dtype == KDA_BF16;
-    if (kda::short_conv_blocks(total_tokens, channels, bf16) > (int64_t)0x7fffffff ||
-        kda::short_conv_state_blocks(num_seqs, channels) > (int64_t)0x7fffffff)
-        return fail(KDA_ERR_INVALID_ARG, "total_tokens * channels too large for one launch");
     const uintptr_t es = bf16 ? 2 : 4;
-    struct Range { uintptr_t lo, hi; };
-    auto range = [](const void *p, uintptr_t bytes) { return Range{(uintptr_t)p, (uintptr_t)p + bytes}; };
-    auto overlap = [](Range a, Range b) { return a.lo < b.hi && b.lo < a.hi; };
-    const Range rx = total_tokens > 0 ? range(x, ((uintptr_t)(total_tokens - 1) * x_stride + channels) * es) : Range{0, 0};
-    const Range ry = total_tokens > 0 ? range(y, (uintptr_t)total_tokens * channels * es) : Range{0, 0};
-    const Range rp = state_pool ? range(state_pool, (uintptr_t)num_slots * (W - 1) * channels * es) : Range{0, 0};
-    if (overlap(ry, rx) || overlap(ry, rp) || overlap(rp, rx))
+    const ByteRange rx = total_tokens > 0 ? byte_range(x, ((uintptr_t)(total_tokens - 1) * x_stride + channels) * es) : ByteRange{};
+    const ByteRange ry = byte_range(y, (uintptr_t)total_tokens * channels * es);
+    const ByteRange rp = byte_range(state_pool, (uintptr_t)num_slots * (W - 1) * channels * es);
+    if (overlaps(ry, rx) || overlaps(ry, rp) || overlaps(rp, rx))
         return fail(KDA_ERR_INVALID_ARG, "y, x and state_pool must not overlap");
 
     kda::ShortConvArgs a;
