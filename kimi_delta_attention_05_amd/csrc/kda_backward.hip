@@ -186,16 +186,21 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(
         }
         lds_barrier();
         fetch(c + 1);
-        for (int i = 0; i < L; ++i) {
-            float kh[8], al[8];
-            load_lane8(&sKh[i][0], j, kh);
-            load_lane8(&sAl[i][0], j, al);
-            float p = 0.f;
+        // unrolled so that each token's LDS reads are issued ahead of the
+        // previous token's dependency chain
 #pragma unroll
-            for (int e = 0; e < 8; ++e) { S[e] *= al[e]; p = fmaf(S[e], kh[e], p); }
-            const float u = sB[i] * (sV[i][row] - row16_sum(p));
+        for (int i = 0; i < kCk; ++i) {
+            if (i < L) {
+                float kh[8], al[8];
+                load_lane8(&sKh[i][0], j, kh);
+                load_lane8(&sAl[i][0], j, al);
+                float p = 0.f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) S[e] = fmaf(u, kh[e], S[e]);
+                for (int e = 0; e < 8; ++e) { S[e] *= al[e]; p = fmaf(S[e], kh[e], p); }
+                const float u = sB[i] * (sV[i][row] - row16_sum(p));
+#pragma unroll
+                for (int e = 0; e < 8; ++e) S[e] = fmaf(u, kh[e], S[e]);
+            }
         }
         lds_barrier();
     }
@@ -297,9 +302,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) voi
             if (i0 < L) {
                 float S[8];
                 load_lane8(ck, j, S);
-                for (int i = 0; i < i0; ++i) {       // tokens before the half: states not kept
-                    float u;
-                    fwd_row_step(S, &sKh[i][0], &sAl[i][0], j, sB[i], sV[i][row], u);
+#pragma unroll
+                for (int i = 0; i < kSub; ++i) {     // tokens before the half: states not kept
+                    if (i < i0) {
+                        float u;
+                        fwd_row_step(S, &sKh[i][0], &sAl[i][0], j, sB[i], sV[i][row], u);
+                    }
                 }
                 float snap[kSub][8];
 #pragma unroll
