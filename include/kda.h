@@ -21,7 +21,8 @@
  *   q, k, g : [T, H, K]      v, o : [T, H, V]      beta_raw : [T, H]
  *   A_log   : [H] fp32       dt_bias : [H, K] fp32
  *   states  : [N, H, V, K] fp32 (value-first)
- * K and V must both be 128 (the contract's head dimension); 1 <= H <= 65536. g, beta_raw,
+ * K and V must both be 128 (the contract's head dimension; kda_recurrent_fwd
+ * takes 1..256); 1 <= H <= 65536. g, beta_raw,
  * A_log, dt_bias and the states are always fp32; q, k and v share the input
  * dtype; o has its own dtype.
  *
@@ -331,6 +332,31 @@ kda_status_t kda_backward(const void *q, const void *k, const void *v, const flo
                           float *dv, float *dg, float *dbeta, float *dA_log, float *ddt_bias,
                           float *d_initial_state, void *workspace, size_t workspace_bytes,
                           void *stream);
+/*
+ * Any head sizes (FlashKDA issue page, "Proposed scope": arbitrary key/value
+ * dimensions). The recurrence above for 1 <= K <= 256 and 1 <= V <= 256, computed
+ * token by token in fp32 by one kernel (the chunkwise path and the decode
+ * kernels require K = V = 128). Packed variable-length sequences with offsets
+ * cu_seqlens as for kda_chunk_fwd; grouped value heads as below (H_qk == H:
+ * ungrouped). A batched decode step is this call with cu_seqlens = [0, 1, ..., B]
+ * and the request states as initial_state / final_state.
+ *   q, k : [T, H_qk, K]   v, o : [T, H, V]   g : [T, H, K]   beta_raw : [T, H]
+ *   A_log : [H]   dt_bias : [H, K]   states : [N, H, V, K] fp32 (value-first)
+ * initial_state NULL = zero; final_state NULL = not written; final_state may be
+ * initial_state itself (updated in place; any other overlap is rejected).
+ * Pointers need only their element alignment (cu_seqlens 8 bytes). A sequence
+ * of length 0 writes no output and copies its initial state (or zeros) to
+ * final_state. Enqueued on `stream`; no workspace.
+ */
+kda_status_t kda_recurrent_fwd(const void *q, const void *k, const void *v,
+                               const float *g, const float *beta_raw,
+                               const float *A_log, const float *dt_bias,
+                               float scale, float lower_bound,
+                               const int64_t *cu_seqlens, int32_t num_seqs,
+                               int64_t total_tokens, int32_t H, int32_t H_qk,
+                               int32_t K, int32_t V, kda_dtype_t in_dtype,
+                               const float *initial_state, float *final_state,
+                               void *o, kda_dtype_t o_dtype, void *stream);
 /*
  * Grouped value heads (FlashKDA issue page, "Proposed scope": grouped value
  * heads). H value heads share H_qk query/key heads, H a multiple of H_qk: value

@@ -3,14 +3,16 @@
 `short_conv` (the q/k/v front end: causal depthwise short conv + SiLU),
 `chunk_fwd` (chunkwise prefill over packed sequences), `decode_step` (batched
 T=1 step, optionally with the output epilogue fused) and `output_norm_gate`
-(the output epilogue: per-head RMS norm and sigmoid gate) and `backward` (the
-training backward of the recurrence) call the HIP kernels
+(the output epilogue: per-head RMS norm and sigmoid gate), `backward` (the
+training backward of the recurrence) and `recurrent_fwd` (the forward for head
+sizes other than 128) call the HIP kernels
 in libkda.so through its C ABI (include/kda.h). Importing the package fails if
 the library is not built.
 """
 from .kda import (KDAError, Workspace, backward, backward_workspace_size, check_cu_seqlens,
                   chunk_fwd, decode_step,
-                  output_norm_gate, short_conv, version, workspace_size, LIB_PATH, NORM_EPS)
+                  output_norm_gate, recurrent_fwd, short_conv, version, workspace_size, LIB_PATH,
+                  NORM_EPS)
 
 __all__ = ["KDAError", "Workspace", "backward", "backward_workspace_size", "check_cu_seqlens", "chunk_fwd", "decode_step",
-           "output_norm_gate", "short_conv", "version", "workspace_size", "LIB_PATH", "NORM_EPS"]
+           "output_norm_gate", "recurrent_fwd", "short_conv", "version", "workspace_size", "LIB_PATH", "NORM_EPS"]

@@ -118,7 +118,7 @@ kda_status_t decode_step_impl(const void *q, const void *k, const void *v,
     if (st != KDA_OK) return st;
     if (!q || !k || !v || !g || !beta_raw || !A_log || !dt_bias || !state || !o)
         return fail(KDA_ERR_INVALID_ARG, "a required pointer is NULL");
-    if ((int64_t)B * H > ((int64_t)1 << 31) - 1)
+    if ((int64_t)B * H * 2 > ((int64_t)1 << 31) - 1)     // two workgroups per (request, head)
         return fail(KDA_ERR_INVALID_ARG, "B * H too large");
     st = check_aligned16({{q, "q"}, {k, "k"}, {v, "v"}, {g, "g"}, {dt_bias, "dt_bias"},
                           {state, "state"}, {o, "o"}});
@@ -150,7 +150,7 @@ kda_status_t decode_step_impl(const void *q, const void *k, const void *v,
 
 extern "C" {
 
-int kda_version(void) { return 105; }
+int kda_version(void) { return 106; }
 
 const char *kda_status_string(kda_status_t s) {
     switch (s) {
@@ -516,6 +516,58 @@ kda_status_t kda_backward(const void *q, const void *k, const void *v, const flo
                                 initial_state, d_o, do_dtype, d_final_state, dq, dk, dv, dg, dbeta,
                                 dA_log, ddt_bias, d_initial_state, workspace, workspace_bytes,
                                 stream);
+}
+
+kda_status_t kda_recurrent_fwd(const void *q, const void *k, const void *v,
+                               const float *g, const float *beta_raw,
+                               const float *A_log, const float *dt_bias,
+                               float scale, float lower_bound,
+                               const int64_t *cu_seqlens, int32_t num_seqs,
+                               int64_t total_tokens, int32_t H, int32_t H_qk,
+                               int32_t K, int32_t V, kda_dtype_t in_dtype,
+                               const float *initial_state, float *final_state,
+                               void *o, kda_dtype_t o_dtype, void *stream) {
+    if (H < 1 || H > 65536) return fail(KDA_ERR_INVALID_ARG, "H must lie in [1, 65536]");
+    kda_status_t st = check_groups(H, H_qk);
+    if (st != KDA_OK) return st;
+    if (K < 1 || K > 256 || V < 1 || V > 256)
+        return fail(KDA_ERR_UNSUPPORTED, "K and V must lie in [1, 256] (got K=" + std::to_string(K) +
+                                             ", V=" + std::to_string(V) + ")");
+    if (!(scale > 0.0f) || !std::isfinite(scale))
+        return fail(KDA_ERR_INVALID_ARG, "scale must be finite and > 0");
+    if (!(lower_bound >= -5.0f && lower_bound < 0.0f))
+        return fail(KDA_ERR_INVALID_ARG, "lower_bound must lie in [-5, 0)");
+    if (!valid_dtype(in_dtype)) return fail(KDA_ERR_UNSUPPORTED, "unknown input dtype");
+    if (!valid_dtype(o_dtype)) return fail(KDA_ERR_UNSUPPORTED, "unknown output dtype");
+    if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 1");
+    if (total_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens must be >= 0");
+    if (!A_log || !dt_bias || !cu_seqlens)
+        return fail(KDA_ERR_INVALID_ARG, "A_log, dt_bias and cu_seqlens must not be NULL");
+    if (total_tokens > 0 && (!q || !k || !v || !g || !beta_raw || !o))
+        return fail(KDA_ERR_INVALID_ARG, "a token pointer is NULL");
+    const uintptr_t te = in_dtype == KDA_BF16 ? 1 : 3, oe = o_dtype == KDA_BF16 ? 1 : 3;
+    if (((uintptr_t)q & te) || ((uintptr_t)k & te) || ((uintptr_t)v & te) || ((uintptr_t)o & oe) ||
+        ((uintptr_t)g & 3) || ((uintptr_t)beta_raw & 3) || ((uintptr_t)A_log & 3) ||
+        ((uintptr_t)dt_bias & 3) || ((uintptr_t)initial_state & 3) || ((uintptr_t)final_state & 3) ||
+        ((uintptr_t)cu_seqlens & 7))
+        return fail(KDA_ERR_INVALID_ARG, "a pointer is not aligned to its element size");
+    const size_t sbytes = (size_t)num_seqs * H * V * K * 4;
+    const ByteRange rsi = byte_range(initial_state, sbytes), rso = byte_range(final_state, sbytes);
+    if (overlaps(rsi, rso) && initial_state != final_state)
+        return fail(KDA_ERR_INVALID_ARG, "final_state may overlap initial_state only by being it");
+    if (kda::general_blocks(num_seqs, H, V) > (int64_t)0x7fffffff)
+        return fail(KDA_ERR_INVALID_ARG, "num_seqs * H * V too large for one launch");
+
+    kda::GeneralArgs a;
+    a.q = q; a.k = k; a.v = v; a.g = g; a.beta_raw = beta_raw; a.A_log = A_log; a.dt_bias = dt_bias;
+    a.scale = scale; a.lower_bound = lower_bound; a.cu_seqlens = cu_seqlens;
+    a.N = num_seqs; a.H = H; a.Hk = H_qk; a.K = K; a.V = V;
+    a.h0 = initial_state; a.ht = final_state; a.o = o;
+    a.in_bf16 = in_dtype == KDA_BF16; a.out_bf16 = o_dtype == KDA_BF16;
+    a.stream = (hipStream_t)stream;
+    const hipError_t e = kda::launch_recurrent_fwd(a);
+    if (e != hipSuccess) return hip_fail(e, "kda_recurrent_fwd launch");
+    return ok();
 }
 
 kda_status_t kda_check_cu_seqlens(const int64_t *cu_seqlens, int32_t num_seqs,

@@ -1,0 +1,177 @@
+// Recurrent KDA forward for any key and value head sizes (1..256 each).
+//
+// The chunkwise prefill and the decode kernels are built around K = V = 128
+// (the FlashInfer "kda_backward" contract's head dimension): their register
+// and LDS layouts follow from it. The FlashKDA issue page ("Proposed scope")
+// asks for arbitrary key/value dimensions as well; this kernel serves those
+// sizes with the token-by-token form of the recurrence, in fp32:
+//
+//   S <- S diag(alpha_t);  S <- S + b_t (v_t - S kh_t) kh_t^T;  o_t = S qh_t
+//
+// over packed variable-length sequences with optional initial and final
+// states. A batched decode step is the same call with every sequence one token
+// long (the state of request n is sequence n's state).
+//
+// One workgroup per (sequence, head, block of 16 state rows), 256 threads: a
+// 16-lane DPP row owns one state row v, lane j holding the key channels
+// j + 16 e (e < NE, NE = ceil(K / 16) rounded up to a power of two; channels
+// at or past K hold zero state and zero keys, queries and decay 1). Tokens go
+// in groups of 16: the workgroup turns a group's q, k, g, beta and v into
+// qh, kh, alpha, b in LDS (a DPP row per token), then each row runs the 16
+// steps, the two K-wide dot products being DPP row sums, and the group's
+// outputs leave through LDS as 16 contiguous values per token.
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int kGTok = 16;    // tokens per group
+constexpr int kGRows = 16;   // state rows per workgroup
+
+template <typename T> __device__ __forceinline__ T from_f32(float x);
+template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
+
+// Workgroup b -> (sequence * H + head, row block): the row blocks of one
+// (sequence, head) share its token data, so they go to one XCD (workgroups are
+// dealt to the 8 XCDs round-robin by index).
+__device__ __forceinline__ bool general_block(int64_t b, int64_t NH, int nvb, int64_t &nh, int &vb) {
+    const int x = (int)(b & 7);
+    const int64_t rest = b >> 3;
+    vb = (int)(rest % nvb);
+    nh = (rest / nvb) * 8 + x;
+    return nh < NH;
+}
+
+template <typename Tin, typename Tout, int NE>
+__global__ __launch_bounds__(256) void recurrent_fwd_kernel(GeneralArgs p)
+{
+    constexpr int KP = 16 * NE;                      // padded key width
+    const int H = p.H, K = p.K, V = p.V;
+    const int nvb = (V + kGRows - 1) / kGRows;
+    int64_t nh;
+    int vb;
+    if (!general_block(blockIdx.x, (int64_t)p.N * H, nvb, nh, vb)) return;
+    const int n = (int)(nh / H), h = (int)(nh % H);
+    const int hk = h / (H / p.Hk);
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int j = lane & 15;
+    const int row = 4 * wave + (lane >> 4);         // state row within the block
+    const int grow = vb * kGRows + row;             // state row v
+    const bool row_ok = grow < V;
+    const int gid = tid >> 4;                       // token of the group staged by this DPP row
+
+    __shared__ float sQ[kGTok][KP], sK[kGTok][KP], sA[kGTok][KP];
+    __shared__ float sB[kGTok], sV[kGTok][kGRows], sO[kGTok][kGRows];
+
+    const Tin *q = (const Tin *)p.q, *k = (const Tin *)p.k, *v = (const Tin *)p.v;
+    const size_t sbase = ((size_t)nh * V + (row_ok ? grow : 0)) * K;
+    float S[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        const int c = j + 16 * e;
+        S[e] = (p.h0 && row_ok && c < K) ? p.h0[sbase + c] : 0.0f;
+    }
+    const float a_gate = fast_exp2(p.A_log[h] * kLog2e);
+    const float lb2 = p.lower_bound * kLog2e;
+    float dtb[NE];
+#pragma unroll
+    for (int e = 0; e < NE; ++e) {
+        const int c = j + 16 * e;
+        dtb[e] = c < K ? p.dt_bias[(size_t)h * K + c] : 0.0f;
+    }
+
+    const int64_t s0 = p.cu_seqlens[n], s1 = p.cu_seqlens[n + 1];
+    for (int64_t t0 = s0; t0 < s1; t0 += kGTok) {
+        const int L = (int)(s1 - t0 < kGTok ? s1 - t0 : kGTok);
+        // ---- token transforms of the group -> LDS ----------------------------------
+        if (gid < L) {
+            const int64_t t = t0 + gid;
+            const size_t tq = ((size_t)t * p.Hk + hk) * K, tg = ((size_t)t * H + h) * K;
+            float qv[NE], kv[NE], ss_q = 0.f, ss_k = 0.f;
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                const int c = j + 16 * e;
+                qv[e] = c < K ? to_f32(q[tq + c]) : 0.0f;
+                kv[e] = c < K ? to_f32(k[tq + c]) : 0.0f;
+                ss_q = fmaf(qv[e], qv[e], ss_q);
+                ss_k = fmaf(kv[e], kv[e], ss_k);
+            }
+            const float rq = rsqrtf(row16_sum(ss_q) + kL2Eps) * p.scale;
+            const float rk = rsqrtf(row16_sum(ss_k) + kL2Eps);
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                const int c = j + 16 * e;
+                sQ[gid][c] = qv[e] * rq;
+                sK[gid][c] = kv[e] * rk;
+                sA[gid][c] = c < K ? fast_exp2(lb2 * sigmoid_f(a_gate * (p.g[tg + c] + dtb[e]))) : 1.0f;
+            }
+            if (j == 0) sB[gid] = sigmoid_f(p.beta_raw[(size_t)t * H + h]);
+            const int vr = vb * kGRows + j;
+            sV[gid][j] = vr < V ? to_f32(v[((size_t)t * H + h) * V + vr]) : 0.0f;
+        }
+        lds_barrier();
+        // ---- the group's steps, one state row per DPP row --------------------------
+        for (int i = 0; i < L; ++i) {
+            float sk = 0.f;
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                S[e] *= sA[i][j + 16 * e];
+                sk = fmaf(S[e], sK[i][j + 16 * e], sk);
+            }
+            const float u = sB[i] * (sV[i][row] - row16_sum(sk));
+            float sq = 0.f;
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
+                S[e] = fmaf(u, sK[i][j + 16 * e], S[e]);
+                sq = fmaf(S[e], sQ[i][j + 16 * e], sq);
+            }
+            sq = row16_sum(sq);
+            if (j == 0) sO[i][row] = sq;
+        }
+        lds_barrier();
+        // ---- outputs: 16 contiguous values per token -------------------------------
+        {
+            const int i = tid >> 4, r = tid & 15, vr = vb * kGRows + r;
+            if (i < L && vr < V)
+                ((Tout *)p.o)[((size_t)(t0 + i) * H + h) * V + vr] = from_f32<Tout>(sO[i][r]);
+        }
+    }
+    if (p.ht && row_ok) {
+#pragma unroll
+        for (int e = 0; e < NE; ++e) {
+            const int c = j + 16 * e;
+            if (c < K) p.ht[sbase + c] = S[e];
+        }
+    }
+}
+
+template <typename Tin, typename Tout>
+hipError_t launch_general_t(const GeneralArgs &a) {
+    const int nvb = (a.V + kGRows - 1) / kGRows;
+    const int64_t groups = ((int64_t)a.N * a.H + 7) / 8;
+    const dim3 grid((unsigned)(groups * 8 * nvb));
+    const int ne = (a.K + 15) / 16;
+    if (ne <= 1)      recurrent_fwd_kernel<Tin, Tout, 1><<<grid, 256, 0, a.stream>>>(a);
+    else if (ne <= 2) recurrent_fwd_kernel<Tin, Tout, 2><<<grid, 256, 0, a.stream>>>(a);
+    else if (ne <= 4) recurrent_fwd_kernel<Tin, Tout, 4><<<grid, 256, 0, a.stream>>>(a);
+    else if (ne <= 8) recurrent_fwd_kernel<Tin, Tout, 8><<<grid, 256, 0, a.stream>>>(a);
+    else              recurrent_fwd_kernel<Tin, Tout, 16><<<grid, 256, 0, a.stream>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+int64_t general_blocks(int64_t N, int64_t H, int V) {
+    return ((N * H + 7) / 8) * 8 * ((V + kGRows - 1) / kGRows);
+}
+
+hipError_t launch_recurrent_fwd(const GeneralArgs &a) {
+    if (a.in_bf16)
+        return a.out_bf16 ? launch_general_t<__bf16, __bf16>(a) : launch_general_t<__bf16, float>(a);
+    return a.out_bf16 ? launch_general_t<float, __bf16>(a) : launch_general_t<float, float>(a);
+}
+
+}  // namespace kda

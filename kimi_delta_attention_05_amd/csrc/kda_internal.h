@@ -166,6 +166,22 @@ hipError_t launch_backward(const BackwardArgs &a);
 int64_t short_conv_blocks(int64_t T, int64_t channels, bool bf16);
 int64_t short_conv_state_blocks(int64_t N, int64_t channels);
 
+// Recurrent forward for any head sizes K, V in [1, 256] (token by token, fp32).
+struct GeneralArgs {
+    const void *q, *k, *v;
+    const float *g, *beta_raw, *A_log, *dt_bias;
+    float scale, lower_bound;
+    const int64_t *cu_seqlens;
+    int N, H, Hk, K, V;
+    const float *h0;
+    float *ht;
+    void *o;
+    bool in_bf16, out_bf16;
+    hipStream_t stream;
+};
+int64_t general_blocks(int64_t N, int64_t H, int V);
+hipError_t launch_recurrent_fwd(const GeneralArgs &a);
+
 hipError_t launch_decode(const DecodeArgs &a);
 hipError_t launch_norm_gate(const NormGateArgs &a);
 hipError_t launch_prefill(const PrefillArgs &a);

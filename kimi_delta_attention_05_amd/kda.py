@@ -28,7 +28,8 @@ EXPORTS = ("kda_version", "kda_status_string", "kda_last_error",
            "kda_decode_step_slots", "kda_output_norm_gate", "kda_short_conv",
            "kda_short_conv_slots",
            "kda_backward_workspace_size", "kda_backward", "kda_chunk_fwd_grouped",
-           "kda_decode_step_grouped", "kda_backward_grouped", "kda_check_cu_seqlens")
+           "kda_decode_step_grouped", "kda_backward_grouped", "kda_recurrent_fwd",
+           "kda_check_cu_seqlens")
 
 NORM_EPS = 1e-5   # default epsilon of the output norm (the pages give none)
 
@@ -89,6 +90,10 @@ _lib.kda_backward_grouped.restype = ctypes.c_int
 _lib.kda_backward_grouped.argtypes = [_P, _P, _P, _P, _P, _P, _P, _f32, _f32, _P, _i32, _i64, _i32,
                                       _i32, _i32, _i32, ctypes.c_int, _P, _P, ctypes.c_int, _P, _P,
                                       _P, _P, _P, _P, _P, _P, _P, _P, _sz, _P]
+_lib.kda_recurrent_fwd.restype = ctypes.c_int
+_lib.kda_recurrent_fwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _f32, _f32, _P, _i32, _i64,
+                                   _i32, _i32, _i32, _i32, ctypes.c_int, _P, _P, _P,
+                                   ctypes.c_int, _P]
 _lib.kda_check_cu_seqlens.restype = ctypes.c_int
 _lib.kda_check_cu_seqlens.argtypes = [_P, _i32, _i64, _P]
 
@@ -480,6 +485,56 @@ def backward(q, k, v, g, beta_raw, A_log, dt_bias, cu_seqlens, d_o, *, scale: fl
                            _stream_ptr(dev))
     _check(st, "kda_backward_grouped")
     return out
+
+
+def recurrent_fwd(q, k, v, g, beta_raw, A_log, dt_bias, cu_seqlens, *, scale: float = None,
+                  lower_bound: float = -5.0, initial_state: Optional[torch.Tensor] = None,
+                  output_final_state: bool = True, final_state: Optional[torch.Tensor] = None,
+                  o_dtype=None, out: Optional[torch.Tensor] = None
+                  ) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """KDA forward for any head sizes 1 <= K, V <= 256 (libkda kda_recurrent_fwd).
+
+    q, k: [T, H_qk, K] and v: [T, H, V], bf16 or fp32 (same dtype), H_qk dividing H;
+    g: [T, H, K] fp32; beta_raw: [T, H] fp32; A_log: [H]; dt_bias: [H, K];
+    cu_seqlens: [N+1] int64 on the GPU; initial_state: [N, H, V, K] fp32 or None.
+    final_state may be initial_state itself (updated in place): a batched decode
+    step is this call with cu_seqlens = [0, 1, ..., B].
+    Returns (o [T, H, V] in o_dtype (default: q's dtype), final_state or None).
+    """
+    T, Hqk, K = q.shape
+    H, V = v.shape[1], v.shape[2]
+    N = cu_seqlens.numel() - 1
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    _dev(q, "q", shape=(T, Hqk, K))
+    _dev(k, "k", dtype=q.dtype, shape=(T, Hqk, K))
+    _dev(v, "v", dtype=q.dtype, shape=(T, H, V))
+    _dev(g, "g", torch.float32, (T, H, K))
+    _dev(beta_raw, "beta_raw", torch.float32, (T, H))
+    _dev(A_log, "A_log", torch.float32, (H,))
+    _dev(dt_bias, "dt_bias", torch.float32, (H, K))
+    _dev(cu_seqlens, "cu_seqlens", torch.int64, (N + 1,))
+    h0_ptr = None
+    if initial_state is not None:
+        h0_ptr = _dev(initial_state, "initial_state", torch.float32, (N, H, V, K))
+    o_dtype = q.dtype if o_dtype is None else o_dtype
+    if out is None:
+        out = torch.empty((T, H, V), dtype=o_dtype, device=q.device)
+    o_ptr = _dev(out, "out", o_dtype, (T, H, V))
+    ht_ptr = None
+    if output_final_state:
+        if final_state is None:
+            final_state = torch.empty((N, H, V, K), dtype=torch.float32, device=q.device)
+        ht_ptr = _dev(final_state, "final_state", torch.float32, (N, H, V, K))
+    else:
+        final_state = None
+    st = _lib.kda_recurrent_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
+                                beta_raw.data_ptr(), A_log.data_ptr(), dt_bias.data_ptr(),
+                                float(scale), float(lower_bound), cu_seqlens.data_ptr(), N, T, H,
+                                Hqk, K, V, _dt(q), h0_ptr, ht_ptr, o_ptr, _dt(out),
+                                _stream_ptr(q.device))
+    _check(st, "kda_recurrent_fwd")
+    return out, final_state
 
 
 def check_cu_seqlens(cu_seqlens: torch.Tensor, total_tokens: int) -> None:

@@ -27,7 +27,7 @@ def test_library_exports_every_declared_symbol(kda):
     assert set(syms) == set(kda.EXPORTS)
     for s in syms:
         assert hasattr(kda.lib, s), s
-    assert kda.version() == 105
+    assert kda.version() == 106
 
 
 def test_status_strings(kda):
@@ -261,6 +261,35 @@ def backward_call_grouped(kda, hqk):
                                         1, 17, 8, hqk, 128, 128, kda.KDA_BF16, None, FAKE,
                                         kda.KDA_BF16, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                         None, 0x100000, 1 << 40, None)
+
+
+def recurrent_call(kda, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, scale=0.125,
+             lb=-5.0, cu=FAKE, N=2, T=17, H=4, Hqk=4, K=64, V=48, dt=kda.KDA_F32, h0=FAKE,
+             ht=FAKE + (1 << 24), o=FAKE, odt=kda.KDA_F32, stream=None)
+    a.update(kw)
+    return kda.lib.kda_recurrent_fwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["A_log"],
+                                     a["dt_bias"], a["scale"], a["lb"], a["cu"], a["N"], a["T"],
+                                     a["H"], a["Hqk"], a["K"], a["V"], a["dt"], a["h0"], a["ht"],
+                                     a["o"], a["odt"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(K=0), 2), (dict(K=257), 2), (dict(V=0), 2), (dict(V=300), 2), (dict(dt=4), 2),
+    (dict(odt=9), 2),
+    (dict(N=0), 1), (dict(T=-1), 1), (dict(H=0), 1), (dict(H=65537), 1), (dict(Hqk=3), 1),
+    (dict(Hqk=0), 1), (dict(scale=0.0), 1), (dict(scale=float("inf")), 1), (dict(lb=0.0), 1),
+    (dict(lb=-7.0), 1), (dict(cu=None), 1), (dict(A_log=None), 1), (dict(dt_bias=None), 1),
+    (dict(q=None), 1), (dict(o=None), 1), (dict(beta=None), 1),
+    # element alignment (bf16 tokens 2 bytes, fp32 arrays 4, offsets 8)
+    (dict(q=FAKE + 2), 1), (dict(dt=1, v=FAKE + 1), 1), (dict(g=FAKE + 2), 1),
+    (dict(cu=FAKE + 4), 1), (dict(h0=FAKE + 2), 1), (dict(odt=1, o=FAKE + 1), 1),
+    # final state overlapping the initial state without being it
+    (dict(ht=FAKE + 64), 1),
+])
+def test_recurrent_fwd_rejects(kda, kw, status):
+    assert recurrent_call(kda, **kw) == status
+    assert kda.lib.kda_last_error()
 
 
 def test_workspace_size_arithmetic(kda):
