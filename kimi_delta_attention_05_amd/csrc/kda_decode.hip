@@ -1,5 +1,6 @@
-// Batched T=1 KDA decode step: one workgroup per (request, head), one pass
-// over the fp32 state.
+// Batched T=1 KDA decode step: one pass over the fp32 state, with the state
+// rows of a (request, head) split over 8 waves (two workgroups of 4 waves, or
+// one of 8 with the fused output epilogue, whose norm needs all 128 outputs).
 //
 // Per (request b, head h) the value-first state S[128][128] is read once and
 // written once. Every state row v is independent given the per-token vectors:
@@ -13,19 +14,19 @@
 // forward; batching every (request, head) pair into one launch follows its
 // batched decode. Transforms per the FlashInfer kda_backward contract.
 //
-// Thread layout: 256 threads = 4 waves; a DPP row of 16 lanes covers one state
-// row, lane j holding channels 4j .. 4j+3 and 64+4j .. 64+4j+3, so that each of
-// the two 16-byte loads (and stores) of a row covers 256 contiguous bytes: whole
-// cache lines per instruction. A wave covers 4 rows, the workgroup 16 rows per
-// iteration, 8 iterations for the 128 rows. All 16 loads of a lane are issued
-// before any arithmetic so that 64 KB per workgroup is in flight.
+// Thread layout: NW waves; a DPP row of 16 lanes covers one state row, lane j
+// holding channels 4j .. 4j+3 and 64+4j .. 64+4j+3, so that each of the two
+// 16-byte loads (and stores) of a row covers 256 contiguous bytes: whole cache
+// lines per instruction. A wave covers 4 rows per iteration, the workgroup
+// 4 NW, over NIT iterations. All loads of a lane are issued before any
+// arithmetic.
 #include "kda_common.h"
 #include "kda_internal.h"
 
 namespace kda {
 
-template <typename Tin, typename Tout, bool GATED>
-__global__ __launch_bounds__(256) void decode_step_kernel(
+template <typename Tin, typename Tout, bool GATED, int NIT, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_step_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
     const float *__restrict__ g, const float *__restrict__ beta_raw,
     const float *__restrict__ A_log, const float *__restrict__ dt_bias,
@@ -33,7 +34,11 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     int H, const Tin *__restrict__ zg, const float *__restrict__ norm_w, float norm_eps,
     const int32_t *__restrict__ slots, int num_slots, int Hk)
 {
-    const int bh = blockIdx.x;                 // request * H + head
+    constexpr int RPI = 4 * NW;                // rows per iteration
+    constexpr int NSPLIT = kHeadDim / (RPI * NIT);
+    const int bh = blockIdx.x / NSPLIT;        // request * H + head
+    const int part = blockIdx.x % NSPLIT;      // block of RPI NIT state rows
+    const int rbase = RPI * NIT * part;
     const int h = bh % H;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -48,7 +53,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     if (slots) {
         const int sl = slots[bh / H];
         if (sl < 0 || sl >= num_slots) {
-            if (threadIdx.x < kHeadDim) o[(size_t)bh * kHeadDim + threadIdx.x] = from_f32<Tout>(0.0f);
+            if (threadIdx.x < RPI * NIT) o[(size_t)bh * kHeadDim + rbase + threadIdx.x] = from_f32<Tout>(0.0f);
             return;
         }
         sbh = (size_t)sl * H + h;
@@ -56,10 +61,10 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     f32x4 *S4 = reinterpret_cast<f32x4 *>(state + sbh * (kHeadDim * kHeadDim));
 
     // Issue the state loads first: rows 16*it + 4*wave + r, 16-byte pieces j and 16+j.
-    f32x4 st[8][2];
+    f32x4 st[NIT][2];
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int row = 16 * it + 4 * wave + r;
+    for (int it = 0; it < NIT; ++it) {
+        const int row = rbase + RPI * it + 4 * wave + r;
         st[it][0] = __builtin_nontemporal_load(S4 + row * 32 + j);
         st[it][1] = __builtin_nontemporal_load(S4 + row * 32 + 16 + j);
     }
@@ -94,14 +99,14 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     for (int e = 0; e < 8; ++e) { qh[e] = qv[e] * rq; kh[e] = kv[e] * rk; }
     const float beta = sigmoid_f(beta_raw[bh]);
 
-    __shared__ float so[kHeadDim];             // outputs, stored coalesced at the end
-    float vrow[8];
+    __shared__ float so[RPI * NIT];            // outputs, stored coalesced at the end
+    float vrow[NIT];
 #pragma unroll
-    for (int it = 0; it < 8; ++it) vrow[it] = to_f32(v[tb + 16 * it + 4 * wave + r]);
+    for (int it = 0; it < NIT; ++it) vrow[it] = to_f32(v[tb + rbase + RPI * it + 4 * wave + r]);
 
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-        const int row = 16 * it + 4 * wave + r;
+    for (int it = 0; it < NIT; ++it) {
+        const int row = rbase + RPI * it + 4 * wave + r;
         float s[8] = {st[it][0][0], st[it][0][1], st[it][0][2], st[it][0][3],
                       st[it][1][0], st[it][1][1], st[it][1][2], st[it][1][3]};
         float a = 0.f, p = 0.f;
@@ -119,13 +124,14 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         const f32x4 s0 = {s[0], s[1], s[2], s[3]}, s1 = {s[4], s[5], s[6], s[7]};
         __builtin_nontemporal_store(s0, S4 + row * 32 + j);
         __builtin_nontemporal_store(s1, S4 + row * 32 + 16 + j);
-        if (j == 0) so[row] = a + u * kq;
+        if (j == 0) so[row - rbase] = a + u * kq;
     }
     lds_barrier();
-    if (threadIdx.x < kHeadDim / 2) {            // wave 0, two outputs per lane
+    if (threadIdx.x < RPI * NIT / 2) {           // wave 0, two outputs per lane
         const int i = 2 * threadIdx.x;
         float y0 = so[i], y1 = so[i + 1];
         if constexpr (GATED) {
+            static_assert(RPI * NIT == kHeadDim, "the epilogue needs the head's 128 outputs in one workgroup");
             // output epilogue (kimi_k3 FusedKDAChunkwise page, "Output handling"):
             // RMS norm over the head's 128 outputs, channel weight, sigmoid gate
             const float ms = wave_sum(y0 * y0 + y1 * y1) * (1.0f / kHeadDim);
@@ -133,24 +139,32 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
             y0 = y0 * r * norm_w[i] * sigmoid_f(to_f32(zg[tb + i]));
             y1 = y1 * r * norm_w[i + 1] * sigmoid_f(to_f32(zg[tb + i + 1]));
         }
-        o[tb + i] = from_f32<Tout>(y0);
-        o[tb + i + 1] = from_f32<Tout>(y1);
+        o[tb + rbase + i] = from_f32<Tout>(y0);
+        o[tb + rbase + i + 1] = from_f32<Tout>(y1);
     }
 }
 
+// The plain step runs two 4-wave workgroups per (request, head), 64 state rows
+// each; the step with the epilogue one 8-wave workgroup per (request, head), so
+// that the norm sees the head's 128 outputs. Both keep 8 state rows per wave
+// (68 VGPRs, 7 waves per SIMD). Measured at B = 256, H = 32: plain 181 us
+// (one 4-wave workgroup per head holding 128 rows: 198 us; the 8-wave form:
+// 192 us; four workgroups of 32 rows: 184 us), with the epilogue 193 us (the
+// 4-wave form over 128 rows: 201 us).
 template <typename Tin, typename Tout>
 static hipError_t launch_decode_t(const DecodeArgs &a) {
-    dim3 grid((unsigned)(a.B * a.H));
+    const unsigned bh = (unsigned)(a.B * a.H);
+    const int Hk = a.Hk > 0 ? a.Hk : a.H;
     if (a.z)
-        decode_step_kernel<Tin, Tout, true><<<grid, 256, 0, a.stream>>>(
+        decode_step_kernel<Tin, Tout, true, 4, 8><<<bh, 512, 0, a.stream>>>(
             (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v, a.g, a.beta_raw,
             a.A_log, a.dt_bias, a.scale, a.lower_bound, a.state, (Tout *)a.o, a.H,
-            (const Tin *)a.z, a.norm_w, a.norm_eps, a.slots, a.num_slots, a.Hk > 0 ? a.Hk : a.H);
+            (const Tin *)a.z, a.norm_w, a.norm_eps, a.slots, a.num_slots, Hk);
     else
-        decode_step_kernel<Tin, Tout, false><<<grid, 256, 0, a.stream>>>(
+        decode_step_kernel<Tin, Tout, false, 4, 4><<<2 * bh, 256, 0, a.stream>>>(
             (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v, a.g, a.beta_raw,
             a.A_log, a.dt_bias, a.scale, a.lower_bound, a.state, (Tout *)a.o, a.H,
-            nullptr, nullptr, 0.f, a.slots, a.num_slots, a.Hk > 0 ? a.Hk : a.H);
+            nullptr, nullptr, 0.f, a.slots, a.num_slots, Hk);
     return hipGetLastError();
 }
 
