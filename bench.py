@@ -213,6 +213,7 @@ def main():
     line["epilogue"] = epilogue_timing(kda, o, dsteps, dA, ddt, dstate, dd.scale, dout)
     line["front_end"] = front_end_timing(kda, (q, k, v), cu)
     line["backward"] = backward_timing(kda, p, (q, k, v, g, beta_raw, A_log, dt_bias, cu, h0))
+    line["any_head_size"] = general_timing(kda, dev)
     line["achievable"] = achievable_hbm(kernels)
 
     if not args.no_cpu_baseline:
@@ -349,6 +350,46 @@ def backward_timing(kda, p, dev_inputs, reps=3):
             "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_VALU_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4),
                          "alg_flops": flops}}
+
+
+def general_timing(kda, dev, T=8192, H=96, reps=3):
+    """The forward for head sizes other than 128 (kda_recurrent_fwd, token by
+    token in fp32), measured beside the step and not part of it: the prefill
+    workload's tokens and heads (one sequence, bf16 tokens, fp32 initial states)
+    at K = V = 64, and at K = V = 128 for comparison with the chunkwise path.
+    Arithmetic: 7 flops per state element and token (decay, the two dot
+    products, the update) against the fp32 vector peak."""
+    import torch
+    import kda_inputs
+    out = {}
+    for Kd in (64, 128):
+        p = kda_inputs.make_prefill([T], H, token_dtype=torch.bfloat16, g_std=2.0, h0_std=0.1,
+                                    seed=2300 + Kd, K=Kd, V=Kd)
+        args = [x.to(dev) for x in (p.q, p.k, p.v, p.g, p.beta_raw, p.A_log, p.dt_bias,
+                                    p.cu_seqlens)]
+        h0 = p.h0.to(dev)
+        o = torch.empty((T, H, Kd), dtype=torch.bfloat16, device=dev)
+        ht = torch.empty_like(h0)
+
+        def run():
+            kda.recurrent_fwd(*args, scale=p.scale, initial_state=h0, final_state=ht, out=o)
+
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        flops = T * H * 7 * Kd * Kd
+        tf = flops / (ms * 1e-3) / 1e12
+        out["K=V=%d" % Kd] = {"ms": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
+                              "roofline": {"bound": "alu", "achieved": round(tf, 2),
+                                           "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                           "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4)}}
+    return out
 
 
 def achievable_hbm(kernels, nbytes=1 << 30, reps=5):

@@ -16,10 +16,11 @@
 // 16-lane DPP row owns one state row v, lane j holding the key channels
 // j + 16 e (e < NE, NE = ceil(K / 16) rounded up to a power of two; channels
 // at or past K hold zero state and zero keys, queries and decay 1). Tokens go
-// in groups of 16: the workgroup turns a group's q, k, g, beta and v into
-// qh, kh, alpha, b in LDS (a DPP row per token), then each row runs the 16
-// steps, the two K-wide dot products being DPP row sums, and the group's
-// outputs leave through LDS as 16 contiguous values per token.
+// in groups of 16: the workgroup turns a group's q, k, g, beta and v (loaded
+// into registers while the previous group ran) into qh, kh, alpha, b in LDS (a
+// DPP row per token), then each row runs the 16 steps, the two K-wide dot
+// products being DPP row sums, and the group's outputs leave through LDS as 16
+// contiguous values per token.
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -84,18 +85,33 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(GeneralArgs p)
     }
 
     const int64_t s0 = p.cu_seqlens[n], s1 = p.cu_seqlens[n + 1];
-    for (int64_t t0 = s0; t0 < s1; t0 += kGTok) {
-        const int L = (int)(s1 - t0 < kGTok ? s1 - t0 : kGTok);
-        // ---- token transforms of the group -> LDS ----------------------------------
-        if (gid < L) {
-            const int64_t t = t0 + gid;
+    // raw token data of token `gid` of a group, loaded one group ahead so that the
+    // next group's loads are in flight while the current group's steps run
+    float qv[NE], kv[NE], gv[NE], braw = 0.f, vv = 0.f;
+    auto fetch = [&](int64_t t0) {
+        const int64_t t = t0 + gid;
+        if (t < s1) {
             const size_t tq = ((size_t)t * p.Hk + hk) * K, tg = ((size_t)t * H + h) * K;
-            float qv[NE], kv[NE], ss_q = 0.f, ss_k = 0.f;
 #pragma unroll
             for (int e = 0; e < NE; ++e) {
                 const int c = j + 16 * e;
                 qv[e] = c < K ? to_f32(q[tq + c]) : 0.0f;
                 kv[e] = c < K ? to_f32(k[tq + c]) : 0.0f;
+                gv[e] = c < K ? p.g[tg + c] : 0.0f;
+            }
+            braw = p.beta_raw[(size_t)t * H + h];
+            const int vr = vb * kGRows + j;
+            vv = vr < V ? to_f32(v[((size_t)t * H + h) * V + vr]) : 0.0f;
+        }
+    };
+    fetch(s0);
+    for (int64_t t0 = s0; t0 < s1; t0 += kGTok) {
+        const int L = (int)(s1 - t0 < kGTok ? s1 - t0 : kGTok);
+        // ---- token transforms of the group -> LDS ----------------------------------
+        if (gid < L) {
+            float ss_q = 0.f, ss_k = 0.f;
+#pragma unroll
+            for (int e = 0; e < NE; ++e) {
                 ss_q = fmaf(qv[e], qv[e], ss_q);
                 ss_k = fmaf(kv[e], kv[e], ss_k);
             }
@@ -106,15 +122,15 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(GeneralArgs p)
                 const int c = j + 16 * e;
                 sQ[gid][c] = qv[e] * rq;
                 sK[gid][c] = kv[e] * rk;
-                sA[gid][c] = c < K ? fast_exp2(lb2 * sigmoid_f(a_gate * (p.g[tg + c] + dtb[e]))) : 1.0f;
+                sA[gid][c] = c < K ? fast_exp2(lb2 * sigmoid_f(a_gate * (gv[e] + dtb[e]))) : 1.0f;
             }
-            if (j == 0) sB[gid] = sigmoid_f(p.beta_raw[(size_t)t * H + h]);
-            const int vr = vb * kGRows + j;
-            sV[gid][j] = vr < V ? to_f32(v[((size_t)t * H + h) * V + vr]) : 0.0f;
+            if (j == 0) sB[gid] = sigmoid_f(braw);
+            sV[gid][j] = vv;
         }
         lds_barrier();
+        fetch(t0 + kGTok);
         // ---- the group's steps, one state row per DPP row --------------------------
-        for (int i = 0; i < L; ++i) {
+        auto step = [&](int i) {
             float sk = 0.f;
 #pragma unroll
             for (int e = 0; e < NE; ++e) {
@@ -130,6 +146,14 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(GeneralArgs p)
             }
             sq = row16_sum(sq);
             if (j == 0) sO[i][row] = sq;
+        };
+        if (L == kGTok) {
+            // whole group: unrolled, so that the LDS reads of later steps are
+            // issued while earlier steps' dot products are still in flight
+#pragma unroll
+            for (int i = 0; i < kGTok; ++i) step(i);
+        } else {
+            for (int i = 0; i < L; ++i) step(i);
         }
         lds_barrier();
         // ---- outputs: 16 contiguous values per token -------------------------------
