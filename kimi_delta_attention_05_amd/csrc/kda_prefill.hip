@@ -1000,20 +1000,26 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
 
         // rescale the state when S / sigma leaves [2^4, 2^14] or sigma < us
         // (|Ub| / sigma <= 2^15 needs sigma >= us); both are powers of two
+        // (the wave maximum is formed only when a lane's own maximum says that
+        // a rescale may be due: two ballots instead of a reduction per chunk)
         if constexpr (!PRECISE) {
             float m = 0.f;
 #pragma unroll
             for (int kb = 0; kb < 8; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(S[kb][i]));
-            m = wave_max_nonneg(m);
-            float tgt = (m > 0.f) ? sigma * pow2_scale_for(m, 14) : (us > 0.f ? us : sigma);
-            if (tgt < us) tgt = us;
-            if (m > 16384.f || sigma < us || (m < 16.f && tgt < sigma)) {
-                const float r = sigma / tgt;
+            const bool any_big = __builtin_amdgcn_ballot_w64(m > 16384.f) != 0;
+            const bool all_small = __builtin_amdgcn_ballot_w64(!(m < 16.f)) == 0;
+            if (any_big || all_small || sigma < us) {
+                m = wave_max_nonneg(m);
+                float tgt = (m > 0.f) ? sigma * pow2_scale_for(m, 14) : (us > 0.f ? us : sigma);
+                if (tgt < us) tgt = us;
+                if (m > 16384.f || sigma < us || (m < 16.f && tgt < sigma)) {
+                    const float r = sigma / tgt;
 #pragma unroll
-                for (int kb = 0; kb < 8; ++kb) S[kb] *= r;
-                sigma = tgt;
+                    for (int kb = 0; kb < 8; ++kb) S[kb] *= r;
+                    sigma = tgt;
+                }
             }
         }
         // state operand: k-step s covers channels 32 s + 8 lg + e (tiles 2s, 2s+1); it is the
@@ -1072,8 +1078,8 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
             for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(U[tb][i]));
-            m = wave_max_nonneg(m);
-            if (m > 32768.f) {
+            if (__builtin_amdgcn_ballot_w64(m > 32768.f) != 0) {
+                m = wave_max_nonneg(m);
                 const float f = pow2_scale_for(m, 14), r = inv_pow2(f);
 #pragma unroll
                 for (int tb = 0; tb < NB; ++tb) { U[tb] *= r; O[tb] *= r; }
