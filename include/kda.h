@@ -21,8 +21,8 @@
  *   q, k, g : [T, H, K]      v, o : [T, H, V]      beta_raw : [T, H]
  *   A_log   : [H] fp32       dt_bias : [H, K] fp32
  *   states  : [N, H, V, K] fp32 (value-first)
- * K and V must both be 128 (the contract's head dimension; kda_recurrent_fwd
- * takes 1..256); 1 <= H <= 65536. g, beta_raw,
+ * K and V are 128 (the contract's head dimension) except where an entry point
+ * says otherwise (kda_chunk_fwd: 1..128, kda_recurrent_fwd: 1..256); 1 <= H <= 65536. g, beta_raw,
  * A_log, dt_bias and the states are always fp32; q, k and v share the input
  * dtype; o has its own dtype.
  *
@@ -106,6 +106,14 @@ size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t num_seqs,
  * stream       : hipStream_t to enqueue on (NULL = default stream).
  * A zero-length sequence writes no output rows and copies its initial state
  * (or zeros) to its final state. total_tokens = 0 is allowed.
+ *
+ * Head sizes below 128 (FlashKDA issue page, "Proposed scope": arbitrary
+ * key/value dimensions): K and V may each be 1..128, with q, k, g [T, H, K],
+ * v, o [T, H, V], dt_bias [H, K] and states [num_seqs, H, V, K]. The same
+ * kernels then run on copies padded with zeros to 128 key channels and 128
+ * value rows, which kda_chunk_fwd_workspace_size includes in the workspace:
+ * padded channels and rows stay exactly zero through the recurrence, so the
+ * result is that of the K x V problem.
  */
 kda_status_t kda_chunk_fwd(const void *q, const void *k, const void *v,
                            const float *g, const float *beta_raw,

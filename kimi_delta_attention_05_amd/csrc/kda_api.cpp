@@ -31,11 +31,13 @@ bool valid_dtype(kda_dtype_t d) { return d == KDA_F32 || d == KDA_BF16; }
 
 // Checks shared by both entry points. Returns KDA_OK or an error with detail.
 kda_status_t check_common(int64_t H, int32_t K, int32_t V, float scale, float lower_bound,
-                          kda_dtype_t in_dtype, kda_dtype_t o_dtype) {
+                          kda_dtype_t in_dtype, kda_dtype_t o_dtype, bool below_128 = false) {
     if (H < 1 || H > 65536) return fail(KDA_ERR_INVALID_ARG, "H must lie in [1, 65536]");
-    if (K != 128 || V != 128)
-        return fail(KDA_ERR_UNSUPPORTED, "only K = V = 128 is supported (got K=" +
-                                             std::to_string(K) + ", V=" + std::to_string(V) + ")");
+    if (below_128 ? (K < 1 || K > 128 || V < 1 || V > 128) : (K != 128 || V != 128))
+        return fail(KDA_ERR_UNSUPPORTED,
+                    std::string(below_128 ? "K and V must lie in [1, 128]" : "only K = V = 128 is supported") +
+                        " (got K=" + std::to_string(K) + ", V=" + std::to_string(V) +
+                        "; kda_recurrent_fwd takes any K, V up to 256)");
     if (!(scale > 0.0f) || !std::isfinite(scale))
         return fail(KDA_ERR_INVALID_ARG, "scale must be finite and > 0");
     if (!(lower_bound >= -5.0f && lower_bound < 0.0f))
@@ -98,6 +100,31 @@ kda_status_t check_groups(int64_t H, int64_t H_qk) {
 
 kda_status_t hip_fail(hipError_t e, const char *where) {
     return fail(KDA_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
+}
+
+// Head sizes below 128 run on the chunkwise kernels over copies of the inputs
+// padded with zeros to 128 key channels and 128 value rows, kept in the
+// workspace after the per-chunk records: padded key channels have k = q = 0
+// and padded value rows v = 0 and a zero initial state, so they stay exactly
+// zero through the recurrence and change neither the norms nor any dot
+// product of the real channels; the outputs and final states are the real
+// rows and channels of the padded results.
+struct PadLayout {
+    size_t q, k, v, g, dtb, state, o, end;
+};
+PadLayout pad_layout(int64_t T, int64_t N, int64_t H, kda_dtype_t in_dtype, size_t base) {
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t esz = in_dtype == KDA_BF16 ? 2 : 4, D = kda::kHeadDimHost;
+    PadLayout L;
+    L.q = up(base);
+    L.k = up(L.q + (size_t)T * H * D * esz);
+    L.v = up(L.k + (size_t)T * H * D * esz);
+    L.g = up(L.v + (size_t)T * H * D * esz);
+    L.dtb = up(L.g + (size_t)T * H * D * 4);
+    L.state = up(L.dtb + (size_t)H * D * 4);
+    L.o = up(L.state + (size_t)N * H * D * D * 4);
+    L.end = up(L.o + (size_t)T * H * D * 4);
+    return L;
 }
 
 // The decode step with an optional fused output epilogue (z == NULL: none).
@@ -172,7 +199,10 @@ size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t num_seqs, int3
         fail(KDA_ERR_INVALID_ARG, "need total_tokens >= 0, num_seqs >= 1, 1 <= H <= 65536");
         return 0;
     }
-    if (K != 128 || V != 128) { fail(KDA_ERR_UNSUPPORTED, "only K = V = 128 is supported"); return 0; }
+    if (K < 1 || K > 128 || V < 1 || V > 128) {
+        fail(KDA_ERR_UNSUPPORTED, "K and V must lie in [1, 128]");
+        return 0;
+    }
     if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) {
         fail(KDA_ERR_UNSUPPORTED, "chunk_size must be 16, 32 or 64");
         return 0;
@@ -180,8 +210,10 @@ size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t num_seqs, int3
     if (!valid_dtype(in_dtype)) { fail(KDA_ERR_UNSUPPORTED, "unknown input dtype"); return 0; }
     const size_t rec = kda::record_bytes(chunk_size, in_dtype == KDA_F32);
     const int64_t slots = kda::num_slots(total_tokens, num_seqs, chunk_size);
+    const size_t base = (size_t)slots * (size_t)H * rec + 256;
     g_last_error.clear();
-    return (size_t)slots * (size_t)H * rec + 256;
+    if (K == 128 && V == 128) return base;
+    return pad_layout(total_tokens, num_seqs, H, in_dtype, base).end;
 }
 
 }  // extern "C"
@@ -202,7 +234,7 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
                               void *stream, int32_t H_qk) {
     if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 1");
     if (total_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens must be >= 0");
-    kda_status_t st = check_common(H, K, V, scale, lower_bound, in_dtype, o_dtype);
+    kda_status_t st = check_common(H, K, V, scale, lower_bound, in_dtype, o_dtype, true);
     if (st != KDA_OK) return st;
     st = check_groups(H, H_qk);
     if (st != KDA_OK) return st;
@@ -240,8 +272,49 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
     a.ws = (unsigned char *)workspace;
     a.stream = (hipStream_t)stream;
     a.stages = stages;
-    hipError_t e = kda::launch_prefill(a);
+    if (K == 128 && V == 128) {
+        hipError_t e = kda::launch_prefill(a);
+        if (e != hipSuccess) return hip_fail(e, name);
+        return ok();
+    }
+
+    // below 128: the same kernels on zero-padded copies in the workspace
+    const int64_t D = kda::kHeadDimHost;
+    const int esz = in_dtype == KDA_BF16 ? 2 : 4, osz = o_dtype == KDA_BF16 ? 2 : 4;
+    const PadLayout P = pad_layout(total_tokens, num_seqs, H,
+                                   in_dtype, kda_chunk_fwd_workspace_size(total_tokens, num_seqs, H,
+                                                                          128, 128, chunk_size,
+                                                                          in_dtype));
+    unsigned char *ws = (unsigned char *)workspace;
+    hipStream_t s = a.stream;
+    const int64_t TH = total_tokens * H, THk = total_tokens * H_qk, NH = (int64_t)num_seqs * H;
+    hipError_t e = hipSuccess;
+    auto pad = [&](const void *src, int sc, int64_t rs, void *dst, int dc, int64_t rd, int64_t rows,
+                   int bytes) {
+        if (e == hipSuccess) e = kda::launch_pad_rows(src, sc, rs, dst, dc, rd, rows, bytes, s);
+    };
+    if (stages & 1) {
+        pad(q, K, 1, ws + P.q, D, 1, THk, esz);
+        pad(k, K, 1, ws + P.k, D, 1, THk, esz);
+        pad(v, V, 1, ws + P.v, D, 1, TH, esz);
+        pad(g, K, 1, ws + P.g, D, 1, TH, 4);
+        pad(dt_bias, K, 1, ws + P.dtb, D, 1, H, 4);
+    }
+    if ((stages & 2) && initial_state)                 // value rows widened to 128 as well
+        pad(initial_state, K, V, ws + P.state, D, D, NH * D, 4);
     if (e != hipSuccess) return hip_fail(e, name);
+    a.q = ws + P.q; a.k = ws + P.k; a.v = ws + P.v; a.g = (const float *)(ws + P.g);
+    a.dt_bias = (const float *)(ws + P.dtb);
+    a.h0 = initial_state ? (const float *)(ws + P.state) : nullptr;
+    a.ht = final_state ? (float *)(ws + P.state) : nullptr;     // read before written, per block
+    a.o = ws + P.o;
+    e = kda::launch_prefill(a);
+    if (e != hipSuccess) return hip_fail(e, name);
+    if (stages & 2) {
+        pad(ws + P.o, D, 1, o, V, 1, TH, osz);
+        if (final_state) pad(ws + P.state, D, D, final_state, K, V, NH * V, 4);
+        if (e != hipSuccess) return hip_fail(e, name);
+    }
     return ok();
 }
 

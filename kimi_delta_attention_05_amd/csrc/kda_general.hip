@@ -186,7 +186,44 @@ hipError_t launch_general_t(const GeneralArgs &a) {
     return hipGetLastError();
 }
 
+// Row copy with zero fill, for running head sizes below 128 on the chunkwise
+// kernels: destination row d (of dst_cols elements) is source row
+// (d / rd) * rs + d % rd when d % rd < rs, its first min(src_cols, dst_cols)
+// elements copied and the rest zero; otherwise the row is zero. rd = rs = 1
+// maps row to row (tokens, parameters); rd = 128, rs = V widens the value rows
+// of a state to 128, rd = V, rs = 128 narrows them back.
+template <typename E>
+__global__ __launch_bounds__(256) void pad_rows_kernel(const E *__restrict__ src, int src_cols,
+                                                       int64_t rs, E *__restrict__ dst,
+                                                       int dst_cols, int64_t rd, int64_t n)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
+        const int64_t d = i / dst_cols;
+        const int c = (int)(i - d * dst_cols);
+        const int64_t grp = d / rd, r = d - grp * rd;
+        E x = E(0);
+        if (r < rs && c < src_cols) x = src[(grp * rs + r) * src_cols + c];
+        dst[i] = x;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_pad_rows(const void *src, int src_cols, int64_t rs, void *dst, int dst_cols,
+                           int64_t rd, int64_t dst_rows, int elem_bytes, hipStream_t stream) {
+    const int64_t n = dst_rows * dst_cols;
+    if (n <= 0) return hipSuccess;
+    const int64_t blocks = (n + 255) / 256;
+    const unsigned grid = (unsigned)(blocks < 65536 ? blocks : 65536);
+    if (elem_bytes == 4)
+        pad_rows_kernel<uint32_t><<<grid, 256, 0, stream>>>((const uint32_t *)src, src_cols, rs,
+                                                            (uint32_t *)dst, dst_cols, rd, n);
+    else
+        pad_rows_kernel<uint16_t><<<grid, 256, 0, stream>>>((const uint16_t *)src, src_cols, rs,
+                                                            (uint16_t *)dst, dst_cols, rd, n);
+    return hipGetLastError();
+}
 
 int64_t general_blocks(int64_t N, int64_t H, int V) {
     return ((N * H + 7) / 8) * 8 * ((V + kGRows - 1) / kGRows);

@@ -7,6 +7,8 @@
 
 namespace kda {
 
+constexpr int kHeadDimHost = 128;    // the head size the chunkwise and decode kernels are built for
+
 struct DecodeArgs {
     const void *q, *k, *v;
     const float *g, *beta_raw, *A_log, *dt_bias;
@@ -180,6 +182,10 @@ struct GeneralArgs {
     hipStream_t stream;
 };
 int64_t general_blocks(int64_t N, int64_t H, int V);
+// dst row d = src row (d / rd) * rs + d % rd if d % rd < rs (first min(src_cols,
+// dst_cols) elements, zeros after), else zeros; elements of 2 or 4 bytes
+hipError_t launch_pad_rows(const void *src, int src_cols, int64_t rs, void *dst, int dst_cols,
+                           int64_t rd, int64_t dst_rows, int elem_bytes, hipStream_t stream);
 hipError_t launch_recurrent_fwd(const GeneralArgs &a);
 
 hipError_t launch_decode(const DecodeArgs &a);

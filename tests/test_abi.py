@@ -52,7 +52,8 @@ def chunk_call(kda, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(K=64), 2), (dict(V=256), 2), (dict(C=48), 2), (dict(C=128), 2), (dict(dt=7), 2),
+    (dict(K=129), 2), (dict(V=256), 2), (dict(K=0), 2), (dict(V=0), 2), (dict(C=48), 2),
+    (dict(C=128), 2), (dict(dt=7), 2),
     (dict(odt=3), 2),
     (dict(N=0), 1), (dict(T=-1), 1), (dict(H=0), 1), (dict(scale=0.0), 1),
     (dict(scale=float("nan")), 1), (dict(lb=0.0), 1), (dict(lb=-5.5), 1), (dict(lb=0.5), 1),
@@ -290,6 +291,20 @@ def recurrent_call(kda, **kw):
 def test_recurrent_fwd_rejects(kda, kw, status):
     assert recurrent_call(kda, **kw) == status
     assert kda.lib.kda_last_error()
+
+
+def test_workspace_size_below_128(kda):
+    # head sizes below 128 add zero-padded copies (q, k, v, g, dt_bias, states, o)
+    # after the records; 129 and 0 are rejected
+    import torch
+    T, N, H, C = 1000, 3, 4, 64
+    base = kda.workspace_size(T, N, H, C, torch.bfloat16)
+    padded = kda.workspace_size(T, N, H, C, torch.bfloat16, K=64, V=48)
+    assert padded >= base + T * H * 128 * (3 * 2 + 4 + 4) + N * H * 128 * 128 * 4 + H * 128 * 4
+    assert padded == kda.workspace_size(T, N, H, C, torch.bfloat16, K=1, V=1)
+    for K, V in ((129, 64), (64, 0)):
+        with pytest.raises(ValueError):
+            kda.workspace_size(T, N, H, C, torch.bfloat16, K=K, V=V)
 
 
 def test_workspace_size_arithmetic(kda):

@@ -8,7 +8,10 @@ tokens and 2e-2 for bf16 tokens (fp32 outputs, the literal metric), over
 packed ragged sequences with initial states, sizes that are and are not
 multiples of 16 (both the key lanes and the 16-row blocks end ragged), grouped
 value heads, empty sequences, in-place state update as a batched decode, and
-K = V = 128 against the chunkwise prefill."""
+K = V = 128 against the chunkwise prefill. Sizes up to 128 also run on the
+chunkwise prefill (kda_chunk_fwd over zero-padded copies in its workspace):
+the same parity bar over chunk sizes 16/32/64, both dtypes, grouped heads, the
+two stages called separately and the final state written over the initial one."""
 import numpy as np
 import pytest
 import torch
@@ -132,3 +135,70 @@ def test_general_repeats_bitwise(kda):
     o1, h1 = run(kda, p)
     o2, h2 = run(kda, p)
     assert torch.equal(o1, o2) and torch.equal(h1, h2)
+
+
+def run_chunked(kda, p, chunk, *, Hqk=None, h0=True, o_dtype=torch.float32, stages=False,
+                in_place=False):
+    d = prefill_to_device(p, DEV)
+    q, k = d["q"], d["k"]
+    if Hqk is not None:
+        G = p.H // Hqk
+        q, k = q[:, ::G].contiguous(), k[:, ::G].contiguous()
+    st0 = d["h0"] if h0 else None
+    kw = dict(scale=p.scale, chunk_size=chunk, initial_state=st0, o_dtype=o_dtype)
+    if in_place:
+        kw["final_state"] = st0
+    args = (q, k, d["v"], d["g"], d["beta_raw"], d["A_log"], d["dt_bias"], d["cu_seqlens"])
+    if stages:
+        ws = kda.Workspace(DEV)
+        o, ht = kda.chunk_fwd(*args, workspace=ws, stage="intra", **kw)
+        o, ht = kda.chunk_fwd(*args, workspace=ws, stage="inter", out=o, final_state=ht,
+                              **{x: y for x, y in kw.items() if x != "final_state"})
+    else:
+        o, ht = kda.chunk_fwd(*args, **kw)
+    torch.cuda.synchronize()
+    return o, ht
+
+
+@pytest.mark.parametrize("K,V,dtype,chunk", [
+    (64, 64, torch.bfloat16, 64), (64, 64, torch.float32, 32), (32, 96, torch.bfloat16, 64),
+    (100, 128, torch.float32, 16), (128, 48, torch.bfloat16, 64), (7, 5, torch.float32, 16),
+    (1, 1, torch.bfloat16, 32), (96, 17, torch.bfloat16, 16)])
+def test_chunked_below_128(kda, K, V, dtype, chunk):
+    p = kda_inputs.make_prefill([17, 33, 5, 70, 0, 64], 3, token_dtype=dtype, h0_std=0.1,
+                                seed=K * 3 + V + chunk, K=K, V=V, g_std=2.0, chunk=chunk)
+    o, ht = run_chunked(kda, p, chunk)
+    ro, rht = ref(p)
+    eo, eh = max_err_rel_rms(o, ro), max_err_rel_rms(ht, rht)
+    tol = 1e-4 if dtype == torch.float32 else 2e-2
+    print("chunked K=%d V=%d %s C=%d: o %.3e ht %.3e" % (K, V, dtype, chunk, eo, eh), flush=True)
+    assert o.shape == (p.T, 3, V) and ht.shape == (6, 3, V, K)
+    assert eo <= tol and eh <= tol
+
+
+def test_chunked_below_128_variants(kda):
+    """Grouped heads without initial states; the two stages called separately;
+    the final state written over the initial one; bf16 output."""
+    p = kda_inputs.make_prefill([40, 3, 90], 4, token_dtype=torch.bfloat16, h0_std=0.1, seed=31,
+                                K=64, V=80)
+    o, ht = run_chunked(kda, p, 64, Hqk=2, h0=False)
+    ro, rht = ref(p, h0=False, Hqk=2)
+    assert max_err_rel_rms(o, ro) <= 2e-2 and max_err_rel_rms(ht, rht) <= 2e-2
+    ro, rht = ref(p)
+    o1, h1 = run_chunked(kda, p, 32)
+    o2, h2 = run_chunked(kda, p, 32, stages=True)
+    assert torch.equal(o1, o2) and torch.equal(h1, h2)
+    o3, h3 = run_chunked(kda, p, 32, in_place=True)
+    assert torch.equal(o1, o3) and torch.equal(h1, h3)
+    o4, _ = run_chunked(kda, p, 32, o_dtype=torch.bfloat16)
+    assert max_err_bf16_out(o4, ro) <= 2e-2 and max_err_rel_rms(h1, rht) <= 2e-2
+
+
+def test_chunked_below_128_matches_recurrent(kda):
+    """Both paths compute the same function for K, V below 128 (fp32 tokens)."""
+    p = kda_inputs.make_prefill([130, 61], 2, token_dtype=torch.float32, h0_std=0.1, seed=33,
+                                K=64, V=64, chunk=64)
+    o1, h1 = run_chunked(kda, p, 64)
+    o2, h2 = run(kda, p)
+    assert max_err_rel_rms(o1, o2.cpu().double().numpy()) <= 2e-4
+    assert max_err_rel_rms(h1, h2.cpu().double().numpy()) <= 2e-4
