@@ -358,7 +358,8 @@ def general_timing(kda, dev, T=8192, H=96, reps=3):
     workload's tokens and heads (one sequence, bf16 tokens, fp32 initial states)
     at K = V = 64, and at K = V = 128 for comparison with the chunkwise path.
     Arithmetic: 7 flops per state element and token (decay, the two dot
-    products, the update) against the fp32 vector peak."""
+    products, the update) against the fp32 vector peak. At K = V = 64 the
+    chunkwise prefill over zero-padded copies is timed too."""
     import torch
     import kda_inputs
     out = {}
@@ -389,6 +390,24 @@ def general_timing(kda, dev, T=8192, H=96, reps=3):
                               "roofline": {"bound": "alu", "achieved": round(tf, 2),
                                            "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                                            "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4)}}
+        if Kd < D:
+            # the same problem on the chunkwise prefill (zero-padded copies to 128)
+            ws = kda.Workspace(dev)
+
+            def run_c():
+                kda.chunk_fwd(*args, scale=p.scale, chunk_size=64, initial_state=h0,
+                              final_state=ht, out=o, workspace=ws)
+
+            run_c()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(reps):
+                run_c()
+            e1.record()
+            torch.cuda.synchronize()
+            mc = e0.elapsed_time(e1) / reps
+            out["K=V=%d" % Kd]["chunked"] = {"ms": round(mc, 3),
+                                             "tokens_per_s": round(T / (mc * 1e-3), 1)}
     return out
 
 

@@ -195,16 +195,44 @@ hipError_t launch_general_t(const GeneralArgs &a) {
 template <typename E>
 __global__ __launch_bounds__(256) void pad_rows_kernel(const E *__restrict__ src, int src_cols,
                                                        int64_t rs, E *__restrict__ dst,
-                                                       int dst_cols, int64_t rd, int64_t n)
+                                                       int dst_cols, int64_t rd, int64_t rows,
+                                                       bool src_vec, bool dst_vec)
 {
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    // a thread moves NV consecutive elements (16 bytes) of a destination row,
+    // with 16-byte loads and stores where the rows are 16-byte aligned
+    constexpr int NV = 16 / sizeof(E);
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    union Piece { u32x4 v; E e[NV]; };
+    const int per_row = (dst_cols + NV - 1) / NV;
+    const int64_t n = rows * per_row, stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride) {
-        const int64_t d = i / dst_cols;
-        const int c = (int)(i - d * dst_cols);
-        const int64_t grp = d / rd, r = d - grp * rd;
-        E x = E(0);
-        if (r < rs && c < src_cols) x = src[(grp * rs + r) * src_cols + c];
-        dst[i] = x;
+        const int64_t d = i / per_row;
+        const int c0 = (int)(i - d * per_row) * NV;
+        int64_t grp = d, r = 0;
+        if (rd > 1) {
+            grp = d / rd;
+            r = d - grp * rd;
+        }
+        Piece x;
+        x.v = u32x4{0u, 0u, 0u, 0u};
+        if (r < rs) {
+            const E *sp = src + (grp * rs + r) * src_cols;
+            if (src_vec && c0 + NV <= src_cols) {
+                x.v = *(const u32x4 *)(sp + c0);
+            } else {
+#pragma unroll
+                for (int e = 0; e < NV; ++e)
+                    if (c0 + e < src_cols) x.e[e] = sp[c0 + e];
+            }
+        }
+        E *dp = dst + d * dst_cols;
+        if (dst_vec && c0 + NV <= dst_cols) {
+            *(u32x4 *)(dp + c0) = x.v;
+        } else {
+#pragma unroll
+            for (int e = 0; e < NV; ++e)
+                if (c0 + e < dst_cols) dp[c0 + e] = x.e[e];
+        }
     }
 }
 
@@ -212,16 +240,21 @@ __global__ __launch_bounds__(256) void pad_rows_kernel(const E *__restrict__ src
 
 hipError_t launch_pad_rows(const void *src, int src_cols, int64_t rs, void *dst, int dst_cols,
                            int64_t rd, int64_t dst_rows, int elem_bytes, hipStream_t stream) {
-    const int64_t n = dst_rows * dst_cols;
-    if (n <= 0) return hipSuccess;
+    if (dst_rows <= 0 || dst_cols <= 0) return hipSuccess;
+    const int nv = 16 / elem_bytes;
+    const int64_t n = dst_rows * ((dst_cols + nv - 1) / nv);
     const int64_t blocks = (n + 255) / 256;
-    const unsigned grid = (unsigned)(blocks < 65536 ? blocks : 65536);
+    const unsigned grid = (unsigned)(blocks < (1 << 16) ? blocks : (1 << 16));
+    const bool sv = ((int64_t)src_cols * elem_bytes) % 16 == 0 && ((uintptr_t)src & 15) == 0;
+    const bool dv = ((int64_t)dst_cols * elem_bytes) % 16 == 0 && ((uintptr_t)dst & 15) == 0;
     if (elem_bytes == 4)
         pad_rows_kernel<uint32_t><<<grid, 256, 0, stream>>>((const uint32_t *)src, src_cols, rs,
-                                                            (uint32_t *)dst, dst_cols, rd, n);
+                                                            (uint32_t *)dst, dst_cols, rd, dst_rows,
+                                                            sv, dv);
     else
         pad_rows_kernel<uint16_t><<<grid, 256, 0, stream>>>((const uint16_t *)src, src_cols, rs,
-                                                            (uint16_t *)dst, dst_cols, rd, n);
+                                                            (uint16_t *)dst, dst_cols, rd, dst_rows,
+                                                            sv, dv);
     return hipGetLastError();
 }
 
