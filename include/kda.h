@@ -22,7 +22,8 @@
  *   A_log   : [H] fp32       dt_bias : [H, K] fp32
  *   states  : [N, H, V, K] fp32 (value-first)
  * K and V are 128 (the contract's head dimension) except where an entry point
- * says otherwise (kda_chunk_fwd: 1..128, kda_recurrent_fwd: 1..256); 1 <= H <= 65536. g, beta_raw,
+ * says otherwise (kda_chunk_fwd: 1..128; kda_recurrent_fwd and the plain decode
+ * step: 1..256); 1 <= H <= 65536. g, beta_raw,
  * A_log, dt_bias and the states are always fp32; q, k and v share the input
  * dtype; o has its own dtype.
  *
@@ -171,6 +172,11 @@ kda_status_t kda_chunk_fwd_inter(const void *q, const void *k, const void *v,
  * state    : [B, H, 128, 128] fp32, read and updated in place
  * o        : [B, H, 128] in o_dtype
  * The state is read once and written once per step.
+ * Other head sizes (1 <= K, V <= 256, FlashKDA issue page, "Proposed scope"):
+ * q, k, g [B, H, K], v, o [B, H, V], state [B, H, V, K], run by the
+ * token-by-token kernel of kda_recurrent_fwd with one token per request; this
+ * and kda_decode_step_grouped without a state pool or epilogue accept them,
+ * the pool and epilogue forms return KDA_ERR_UNSUPPORTED.
  */
 kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
                              const float *g, const float *beta_raw,

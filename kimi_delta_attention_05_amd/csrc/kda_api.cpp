@@ -139,7 +139,11 @@ kda_status_t decode_step_impl(const void *q, const void *k, const void *v,
                               const int32_t *slots, int32_t num_slots,
                               const char *name, int32_t H_qk) {
     if (B < 1) return fail(KDA_ERR_INVALID_ARG, "B must be >= 1");
-    kda_status_t st = check_common(H, K, V, scale, lower_bound, in_dtype, o_dtype);
+    const bool general = (K != 128 || V != 128) && K >= 1 && K <= 256 && V >= 1 && V <= 256;
+    if (general && (z || slots))
+        return fail(KDA_ERR_UNSUPPORTED, "the state pool and the fused epilogue need K = V = 128");
+    kda_status_t st = check_common(H, general ? 128 : K, general ? 128 : V, scale, lower_bound,
+                                   in_dtype, o_dtype);
     if (st != KDA_OK) return st;
     st = check_groups(H, H_qk);
     if (st != KDA_OK) return st;
@@ -159,6 +163,23 @@ kda_status_t decode_step_impl(const void *q, const void *k, const void *v,
             return fail(KDA_ERR_INVALID_ARG, "norm_eps must be finite and > 0");
         st = check_aligned16({{z, "z"}, {norm_weight, "norm_weight"}});
         if (st != KDA_OK) return st;
+    }
+
+    if (general) {
+        // other head sizes: the token-by-token kernel with one token per request
+        // (no offsets: request n is sequence n), the state updated in place
+        if (kda::general_blocks(B, H, V) > (int64_t)0x7fffffff)
+            return fail(KDA_ERR_INVALID_ARG, "B * H * V too large for one launch");
+        kda::GeneralArgs ga;
+        ga.q = q; ga.k = k; ga.v = v; ga.g = g; ga.beta_raw = beta_raw; ga.A_log = A_log;
+        ga.dt_bias = dt_bias; ga.scale = scale; ga.lower_bound = lower_bound;
+        ga.cu_seqlens = nullptr; ga.N = B; ga.H = H; ga.Hk = H_qk; ga.K = K; ga.V = V;
+        ga.h0 = state; ga.ht = state; ga.o = o;
+        ga.in_bf16 = in_dtype == KDA_BF16; ga.out_bf16 = o_dtype == KDA_BF16;
+        ga.stream = (hipStream_t)stream;
+        const hipError_t e = kda::launch_recurrent_fwd(ga);
+        if (e != hipSuccess) return hip_fail(e, name);
+        return ok();
     }
 
     kda::DecodeArgs a;

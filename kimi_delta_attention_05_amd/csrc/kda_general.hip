@@ -84,7 +84,9 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(GeneralArgs p)
         dtb[e] = c < K ? p.dt_bias[(size_t)h * K + c] : 0.0f;
     }
 
-    const int64_t s0 = p.cu_seqlens[n], s1 = p.cu_seqlens[n + 1];
+    // no offsets (the decode step): sequence n is token n
+    const int64_t s0 = p.cu_seqlens ? p.cu_seqlens[n] : n;
+    const int64_t s1 = p.cu_seqlens ? p.cu_seqlens[n + 1] : n + 1;
     // raw token data of token `gid` of a group, loaded one group ahead so that the
     // next group's loads are in flight while the current group's steps run
     float qv[NE], kv[NE], gv[NE], braw = 0.f, vv = 0.f;

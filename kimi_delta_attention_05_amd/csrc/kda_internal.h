@@ -173,7 +173,7 @@ struct GeneralArgs {
     const void *q, *k, *v;
     const float *g, *beta_raw, *A_log, *dt_bias;
     float scale, lower_bound;
-    const int64_t *cu_seqlens;
+    const int64_t *cu_seqlens;          // nullptr: one token per sequence (sequence n = token n)
     int N, H, Hk, K, V;
     const float *h0;
     float *ht;

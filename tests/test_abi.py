@@ -81,7 +81,7 @@ def decode_call(kda, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(K=129), 2), (dict(V=64), 2), (dict(dt=5), 2), (dict(B=0), 1), (dict(H=-1), 1),
+    (dict(K=257), 2), (dict(V=0), 2), (dict(dt=5), 2), (dict(B=0), 1), (dict(H=-1), 1),
     (dict(state=None), 1), (dict(q=None), 1), (dict(lb=-6.0), 1), (dict(scale=-1.0), 1),
     (dict(state=FAKE + 4), 1), (dict(q=FAKE + 8), 1), (dict(o=FAKE + 4), 1),
     (dict(beta=FAKE + 2), 1), (dict(H=70000), 1),

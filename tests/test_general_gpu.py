@@ -202,3 +202,46 @@ def test_chunked_below_128_matches_recurrent(kda):
     o2, h2 = run(kda, p)
     assert max_err_rel_rms(o1, o2.cpu().double().numpy()) <= 2e-4
     assert max_err_rel_rms(h1, h2.cpu().double().numpy()) <= 2e-4
+
+
+@pytest.mark.parametrize("K,V,Hqk", [(64, 96, None), (48, 48, 1), (200, 16, None)])
+def test_decode_step_other_sizes(kda, K, V, Hqk):
+    """kda_decode_step (and its grouped form) at head sizes other than 128: the
+    state updated in place over several steps, against the oracle's steps."""
+    d = kda_inputs.make_decode(5, 3, 4, seed=K + V, K=K, V=V)
+    G = 3 if Hqk is None else 3 // Hqk
+    state = d.state.to(DEV).clone()
+    outs = []
+    for st in d.steps:
+        q, k = st["q"].to(DEV), st["k"].to(DEV)
+        if Hqk is not None:
+            q, k = q[:, ::G].contiguous(), k[:, ::G].contiguous()
+        outs.append(kda.decode_step(q, k, st["v"].to(DEV), st["g"].to(DEV),
+                                    st["beta_raw"].to(DEV), d.A_log.to(DEV), d.dt_bias.to(DEV),
+                                    state, scale=d.scale, o_dtype=torch.float32))
+    torch.cuda.synchronize()
+    steps = d.steps
+    if Hqk is not None:
+        steps = [dict(st, q=st["q"][:, ::G].repeat_interleave(G, dim=1),
+                      k=st["k"][:, ::G].repeat_interleave(G, dim=1)) for st in d.steps]
+    ref_outs, ref_state = oracle.kda_decode_steps(steps, d.state, d.A_log, d.dt_bias,
+                                                  scale=d.scale)
+    eo = max(max_err_rel_rms(a, b) for a, b in zip(outs, ref_outs))
+    eh = max_err_rel_rms(state, ref_state)
+    print("decode K=%d V=%d: o %.3e state %.3e" % (K, V, eo, eh), flush=True)
+    assert eo <= 2e-2 and eh <= 2e-2
+
+
+def test_decode_other_sizes_pool_and_epilogue_rejected(kda):
+    d = kda_inputs.make_decode(2, 2, 1, seed=3, K=64, V=64)
+    st = {k: v.to(DEV) for k, v in d.steps[0].items()}
+    state = d.state.to(DEV)
+    z = torch.zeros((2, 2, 64), dtype=st["q"].dtype, device=DEV)
+    w = torch.ones(64, device=DEV)
+    with pytest.raises(kda.KDAError):
+        kda.decode_step(st["q"], st["k"], st["v"], st["g"], st["beta_raw"], d.A_log.to(DEV),
+                        d.dt_bias.to(DEV), state, scale=d.scale, gate=z, norm_weight=w)
+    with pytest.raises(kda.KDAError):
+        kda.decode_step(st["q"], st["k"], st["v"], st["g"], st["beta_raw"], d.A_log.to(DEV),
+                        d.dt_bias.to(DEV), state, scale=d.scale,
+                        slot_idx=torch.zeros(2, dtype=torch.int32, device=DEV))
