@@ -22,8 +22,8 @@
  *   A_log   : [H] fp32       dt_bias : [H, K] fp32
  *   states  : [N, H, V, K] fp32 (value-first)
  * K and V are 128 (the contract's head dimension) except where an entry point
- * says otherwise (kda_chunk_fwd: 1..128; kda_recurrent_fwd and the plain decode
- * step: 1..256); 1 <= H <= 65536. g, beta_raw,
+ * says otherwise (kda_chunk_fwd and kda_backward: 1..128; kda_recurrent_fwd and
+ * the plain decode step: 1..256); 1 <= H <= 65536. g, beta_raw,
  * A_log, dt_bias and the states are always fp32; q, k and v share the input
  * dtype; o has its own dtype.
  *
@@ -334,6 +334,10 @@ kda_status_t kda_short_conv_slots(const void *x, int64_t x_stride, const float *
  * workspace: kda_backward_workspace_size() bytes, 256-byte aligned, caller
  * owned; nothing in it needs initialising. H <= 65535. Sums run in a fixed
  * order (no atomics): results repeat bit for bit.
+ * Head sizes below 128 (1 <= K, V <= 128; shapes as for kda_chunk_fwd, d_o
+ * [T, H, V], d_final_state and d_initial_state [N, H, V, K]): the same kernels
+ * on zero-padded copies in the workspace, as kda_chunk_fwd does; the gradients
+ * of the padded channels and rows are dropped.
  */
 size_t kda_backward_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H,
                                    int32_t K, int32_t V);

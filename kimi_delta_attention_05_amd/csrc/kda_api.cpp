@@ -127,6 +127,34 @@ PadLayout pad_layout(int64_t T, int64_t N, int64_t H, kda_dtype_t in_dtype, size
     return L;
 }
 
+// The backward's padded copies (head sizes below 128), after its own layout:
+// the inputs and adjoints widened to 128, and the gradients at 128 before they
+// are narrowed back into the caller's buffers.
+struct BwdPadLayout {
+    size_t q, k, v, g, dtb, h0, dout, dht, dq, dk, dv, dg, ddt, dh0, end;
+};
+BwdPadLayout bwd_pad_layout(int64_t T, int64_t N, int64_t H, size_t base) {
+    auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+    const size_t D = kda::kHeadDimHost, tok = (size_t)T * H * D * 4, st = (size_t)N * H * D * D * 4;
+    BwdPadLayout L;
+    L.q = up(base);
+    L.k = up(L.q + tok);
+    L.v = up(L.k + tok);
+    L.g = up(L.v + tok);
+    L.dtb = up(L.g + tok);
+    L.h0 = up(L.dtb + (size_t)H * D * 4);
+    L.dout = up(L.h0 + st);
+    L.dht = up(L.dout + tok);
+    L.dq = up(L.dht + st);
+    L.dk = up(L.dq + tok);
+    L.dv = up(L.dk + tok);
+    L.dg = up(L.dv + tok);
+    L.ddt = up(L.dg + tok);
+    L.dh0 = up(L.ddt + (size_t)H * D * 4);
+    L.end = up(L.dh0 + st);
+    return L;
+}
+
 // The decode step with an optional fused output epilogue (z == NULL: none).
 kda_status_t decode_step_impl(const void *q, const void *k, const void *v,
                               const float *g, const float *beta_raw,
@@ -532,9 +560,14 @@ size_t kda_backward_workspace_size(int64_t total_tokens, int32_t num_seqs, int32
         fail(KDA_ERR_INVALID_ARG, "need total_tokens >= 0, num_seqs >= 1, 1 <= H <= 65535");
         return 0;
     }
-    if (K != 128 || V != 128) { fail(KDA_ERR_UNSUPPORTED, "only K = V = 128 is supported"); return 0; }
+    if (K < 1 || K > 128 || V < 1 || V > 128) {
+        fail(KDA_ERR_UNSUPPORTED, "K and V must lie in [1, 128]");
+        return 0;
+    }
     g_last_error.clear();
-    return kda::backward_layout(total_tokens, num_seqs, H).total;
+    const size_t base = kda::backward_layout(total_tokens, num_seqs, H).total;
+    if (K == 128 && V == 128) return base;
+    return bwd_pad_layout(total_tokens, num_seqs, H, base).end;
 }
 
 kda_status_t kda_backward_grouped(const void *q, const void *k, const void *v, const float *g,
@@ -550,7 +583,7 @@ kda_status_t kda_backward_grouped(const void *q, const void *k, const void *v, c
     if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 1");
     if (total_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens must be >= 0");
     if (H > 65535) return fail(KDA_ERR_INVALID_ARG, "H must lie in [1, 65535]");
-    kda_status_t st = check_common(H, K, V, scale, lower_bound, in_dtype, do_dtype);
+    kda_status_t st = check_common(H, K, V, scale, lower_bound, in_dtype, do_dtype, true);
     if (st != KDA_OK) return st;
     st = check_groups(H, H_qk);
     if (st != KDA_OK) return st;
@@ -563,7 +596,7 @@ kda_status_t kda_backward_grouped(const void *q, const void *k, const void *v, c
         return fail(KDA_ERR_INVALID_ARG, "num_seqs * H too large");
     if ((total_tokens + 15) / 16 > (int64_t)0x7fffffff)
         return fail(KDA_ERR_INVALID_ARG, "total_tokens too large");
-    const size_t need = kda::backward_layout(total_tokens, num_seqs, H).total;
+    const size_t need = kda_backward_workspace_size(total_tokens, num_seqs, H, K, V);
     if (!workspace || workspace_bytes < need)
         return fail(KDA_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes, got " +
                                            std::to_string(workspace_bytes));
@@ -591,8 +624,51 @@ kda_status_t kda_backward_grouped(const void *q, const void *k, const void *v, c
     a.part = (float *)(ws + lay.ckpt_bytes);
     a.pp = (float *)(ws + lay.ckpt_bytes + lay.part_bytes);
     a.stream = (hipStream_t)stream;
-    hipError_t e = kda::launch_backward(a);
+    if (K == 128 && V == 128) {
+        hipError_t e = kda::launch_backward(a);
+        if (e != hipSuccess) return hip_fail(e, "kda_backward launch");
+        return ok();
+    }
+
+    // below 128: the same kernels on zero-padded copies (as kda_chunk_fwd). The
+    // padded channels and rows stay zero in the forward, so the gradients of
+    // the real inputs are those of the K x V problem; the padded ones are dropped.
+    const int64_t D = kda::kHeadDimHost;
+    const int esz = in_dtype == KDA_BF16 ? 2 : 4, dsz = do_dtype == KDA_BF16 ? 2 : 4;
+    const BwdPadLayout P = bwd_pad_layout(total_tokens, num_seqs, H, lay.total);
+    const int64_t TH = total_tokens * H, THk = total_tokens * H_qk, NH = (int64_t)num_seqs * H;
+    hipStream_t s = a.stream;
+    hipError_t e = hipSuccess;
+    auto pad = [&](const void *src, int sc, int64_t rs, void *dst, int dc, int64_t rd, int64_t rows,
+                   int bytes) {
+        if (e == hipSuccess) e = kda::launch_pad_rows(src, sc, rs, dst, dc, rd, rows, bytes, s);
+    };
+    pad(q, K, 1, ws + P.q, D, 1, THk, esz);
+    pad(k, K, 1, ws + P.k, D, 1, THk, esz);
+    pad(v, V, 1, ws + P.v, D, 1, TH, esz);
+    pad(g, K, 1, ws + P.g, D, 1, TH, 4);
+    pad(dt_bias, K, 1, ws + P.dtb, D, 1, H, 4);
+    if (initial_state) pad(initial_state, K, V, ws + P.h0, D, D, NH * D, 4);
+    pad(d_o, V, 1, ws + P.dout, D, 1, TH, dsz);
+    if (d_final_state) pad(d_final_state, K, V, ws + P.dht, D, D, NH * D, 4);
+    if (e != hipSuccess) return hip_fail(e, "kda_backward padding");
+    a.q = ws + P.q; a.k = ws + P.k; a.v = ws + P.v; a.g = (const float *)(ws + P.g);
+    a.dt_bias = (const float *)(ws + P.dtb);
+    a.h0 = initial_state ? (const float *)(ws + P.h0) : nullptr;
+    a.dout = ws + P.dout;
+    a.dht = d_final_state ? (const float *)(ws + P.dht) : nullptr;
+    a.dq = (float *)(ws + P.dq); a.dk = (float *)(ws + P.dk); a.dv = (float *)(ws + P.dv);
+    a.dg = (float *)(ws + P.dg); a.ddt_bias = (float *)(ws + P.ddt);
+    a.dh0 = d_initial_state ? (float *)(ws + P.dh0) : nullptr;
+    e = kda::launch_backward(a);
     if (e != hipSuccess) return hip_fail(e, "kda_backward launch");
+    pad(ws + P.dq, D, 1, dq, K, 1, THk, 4);
+    pad(ws + P.dk, D, 1, dk, K, 1, THk, 4);
+    pad(ws + P.dv, D, 1, dv, V, 1, TH, 4);
+    pad(ws + P.dg, D, 1, dg, K, 1, TH, 4);
+    pad(ws + P.ddt, D, 1, ddt_bias, K, 1, H, 4);
+    if (d_initial_state) pad(ws + P.dh0, D, D, d_initial_state, K, V, NH * V, 4);
+    if (e != hipSuccess) return hip_fail(e, "kda_backward padding");
     return ok();
 }
 

@@ -430,8 +430,10 @@ def _short_conv_slots(x, weight, cu_seqlens, state_pool, slot_idx, out):
     return out, state_pool
 
 
-def backward_workspace_size(total_tokens: int, num_seqs: int, H: int) -> int:
-    n = int(_lib.kda_backward_workspace_size(int(total_tokens), int(num_seqs), int(H), 128, 128))
+def backward_workspace_size(total_tokens: int, num_seqs: int, H: int, K: int = 128,
+                            V: int = 128) -> int:
+    n = int(_lib.kda_backward_workspace_size(int(total_tokens), int(num_seqs), int(H), int(K),
+                                             int(V)))
     if n == 0:
         raise ValueError("kda_backward_workspace_size: " + _lib.kda_last_error().decode())
     return n
@@ -445,41 +447,42 @@ def backward(q, k, v, g, beta_raw, A_log, dt_bias, cu_seqlens, d_o, *, scale: fl
     sum(o * d_o) + sum(final_state * d_final_state) w.r.t. every input.
 
     Inputs as chunk_fwd (q, k may have fewer heads: grouped value heads, dq and dk then
-    [T, H_qk, 128]); d_o: [T, H, 128] bf16 or fp32; d_final_state: [N, H, 128, 128]
-    fp32 or None. Returns a dict of fp32 tensors dq, dk, dv, dg [T, H, 128], dbeta [T, H],
-    dA_log [H], ddt_bias [H, 128] and dh0 [N, H, 128, 128] (None unless requested).
+    [T, H_qk, K]); d_o: [T, H, V] bf16 or fp32; d_final_state: [N, H, V, K]
+    fp32 or None. Returns a dict of fp32 tensors dq, dk, dg [T, H, K], dv [T, H, V],
+    dbeta [T, H], dA_log [H], ddt_bias [H, K] and dh0 [N, H, V, K] (None unless
+    requested). K = V = 128, or head sizes up to 128 (zero-padded inside the library).
     """
     T, Hqk, K = q.shape
-    H = v.shape[1]
+    H, V = v.shape[1], v.shape[2]
     N = cu_seqlens.numel() - 1
     if scale is None:
         scale = 1.0 / math.sqrt(K)
     _dev(q, "q", shape=(T, Hqk, K))
     _dev(k, "k", dtype=q.dtype, shape=(T, Hqk, K))
-    _dev(v, "v", dtype=q.dtype, shape=(T, H, K))
+    _dev(v, "v", dtype=q.dtype, shape=(T, H, V))
     _dev(g, "g", torch.float32, (T, H, K))
     _dev(beta_raw, "beta_raw", torch.float32, (T, H))
     _dev(A_log, "A_log", torch.float32, (H,))
     _dev(dt_bias, "dt_bias", torch.float32, (H, K))
     _dev(cu_seqlens, "cu_seqlens", torch.int64, (N + 1,))
-    _dev(d_o, "d_o", shape=(T, H, K))
+    _dev(d_o, "d_o", shape=(T, H, V))
     dev = q.device
     h0p = None if initial_state is None else _dev(initial_state, "initial_state", torch.float32,
-                                                  (N, H, K, K))
+                                                  (N, H, V, K))
     dhtp = None if d_final_state is None else _dev(d_final_state, "d_final_state", torch.float32,
-                                                   (N, H, K, K))
+                                                   (N, H, V, K))
     f32 = dict(dtype=torch.float32, device=dev)
     out = dict(dq=torch.empty((T, Hqk, K), **f32), dk=torch.empty((T, Hqk, K), **f32),
-               dv=torch.empty((T, H, K), **f32), dg=torch.empty((T, H, K), **f32),
+               dv=torch.empty((T, H, V), **f32), dg=torch.empty((T, H, K), **f32),
                dbeta=torch.empty((T, H), **f32), dA_log=torch.empty((H,), **f32),
                ddt_bias=torch.empty((H, K), **f32),
-               dh0=torch.empty((N, H, K, K), **f32) if need_d_initial_state else None)
-    need = backward_workspace_size(T, N, H)
+               dh0=torch.empty((N, H, V, K), **f32) if need_d_initial_state else None)
+    need = backward_workspace_size(T, N, H, K, V)
     ws = (workspace or Workspace(dev)).get(need)
     ptr = lambda t: None if t is None else t.data_ptr()
     st = _lib.kda_backward_grouped(q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(),
                            beta_raw.data_ptr(), A_log.data_ptr(), dt_bias.data_ptr(), float(scale),
-                           float(lower_bound), cu_seqlens.data_ptr(), N, T, H, Hqk, K, K, _dt(q), h0p,
+                           float(lower_bound), cu_seqlens.data_ptr(), N, T, H, Hqk, K, V, _dt(q), h0p,
                            d_o.data_ptr(), _dt(d_o), dhtp, out["dq"].data_ptr(),
                            out["dk"].data_ptr(), out["dv"].data_ptr(), out["dg"].data_ptr(),
                            out["dbeta"].data_ptr(), out["dA_log"].data_ptr(),

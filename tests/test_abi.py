@@ -220,7 +220,7 @@ def backward_call(kda, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(N=0), 1), (dict(T=-1), 1), (dict(H=0), 1), (dict(H=65536), 1), (dict(K=64), 2),
+    (dict(N=0), 1), (dict(T=-1), 1), (dict(H=0), 1), (dict(H=65536), 1), (dict(K=129), 2),
     (dict(dt=4), 2), (dict(dodt=4), 2), (dict(scale=0.0), 1), (dict(lb=1.0), 1),
     (dict(cu=None), 1), (dict(dA=None), 1), (dict(ddt=None), 1), (dict(q=None), 1),
     (dict(do=None), 1), (dict(dq=None), 1), (dict(dbeta=None), 1), (dict(ws=None), 3),

@@ -245,3 +245,40 @@ def test_decode_other_sizes_pool_and_epilogue_rejected(kda):
         kda.decode_step(st["q"], st["k"], st["v"], st["g"], st["beta_raw"], d.A_log.to(DEV),
                         d.dt_bias.to(DEV), state, scale=d.scale,
                         slot_idx=torch.zeros(2, dtype=torch.int32, device=DEV))
+
+
+@pytest.mark.parametrize("K,V,dtype,Hqk", [(64, 64, torch.bfloat16, None),
+                                           (32, 96, torch.float32, None),
+                                           (100, 20, torch.bfloat16, 1)])
+def test_backward_below_128(kda, K, V, dtype, Hqk):
+    """kda_backward at head sizes below 128 (zero-padded inside the library)
+    against the fp64 backward oracle, every gradient to 1e-4 of its rms."""
+    p = kda_inputs.make_prefill([20, 0, 45], 3, token_dtype=dtype, h0_std=0.1, seed=K + 2 * V,
+                                K=K, V=V)
+    gen = torch.Generator().manual_seed(K * V)
+    do = torch.randn(p.T, p.H, V, generator=gen).to(dtype)
+    dht = torch.randn(p.N, p.H, V, K, generator=gen) * 0.1
+    d = prefill_to_device(p, DEV)
+    q, k = d["q"], d["k"]
+    qr, kr = p.q, p.k
+    if Hqk is not None:
+        G = p.H // Hqk
+        q, k = q[:, ::G].contiguous(), k[:, ::G].contiguous()
+        qr = p.q[:, ::G].repeat_interleave(G, dim=1)
+        kr = p.k[:, ::G].repeat_interleave(G, dim=1)
+    r = kda.backward(q, k, d["v"], d["g"], d["beta_raw"], d["A_log"], d["dt_bias"],
+                     d["cu_seqlens"], do.to(DEV), scale=p.scale, initial_state=d["h0"],
+                     d_final_state=dht.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.kda_backward(qr, kr, p.v, p.g, p.beta_raw, p.A_log, p.dt_bias, p.cu_seqlens, do,
+                              scale=p.scale, h0=p.h0, dht=dht)
+    if Hqk is not None:
+        G = p.H // Hqk
+        for key in ("dq", "dk"):
+            ref[key] = ref[key].reshape(p.T, Hqk, G, K).sum(axis=2)
+    worst = {key: max_err_rel_rms(r[key], ref[key]) for key in
+             ("dq", "dk", "dv", "dg", "dbeta", "dA_log", "ddt_bias", "dh0")}
+    print("backward K=%d V=%d: %s" % (K, V, " ".join("%s=%.2e" % kv for kv in worst.items())),
+          flush=True)
+    assert r["dv"].shape == (p.T, p.H, V) and r["dh0"].shape == (p.N, p.H, V, K)
+    assert max(worst.values()) <= 1e-4, worst
