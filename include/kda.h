@@ -250,7 +250,9 @@ kda_status_t kda_decode_step_slots(const void *q, const void *k, const void *v,
  *           y may alias o
  * weight  : [128] fp32 (one weight vector shared by all heads), 16-byte aligned
  * eps     : finite and > 0 (the page gives no value)
- * rows    : >= 0 (0 enqueues nothing and accepts NULL pointers);  D : must be 128
+ * rows    : >= 0 (0 enqueues nothing and accepts NULL pointers);  D : 128, or any
+ *           width 1..256 for the outputs of other head sizes (o, z, y [rows, D],
+ *           weight [D]; a slower one-wave-per-row kernel)
  */
 kda_status_t kda_output_norm_gate(const void *o, const void *z, const float *weight, float eps,
                                   int64_t rows, int32_t D, kda_dtype_t io_dtype, void *y,

@@ -473,16 +473,16 @@ kda_status_t kda_output_norm_gate(const void *o, const void *z, const float *wei
                                   int64_t rows, int32_t D, kda_dtype_t io_dtype, void *y,
                                   void *stream) {
     if (rows < 0) return fail(KDA_ERR_INVALID_ARG, "rows must be >= 0");
-    if (D != 128) return fail(KDA_ERR_UNSUPPORTED, "only D = 128 is supported (got " + std::to_string(D) + ")");
+    if (D < 1 || D > 256) return fail(KDA_ERR_UNSUPPORTED, "D must lie in [1, 256] (got " + std::to_string(D) + ")");
     if (!valid_dtype(io_dtype)) return fail(KDA_ERR_UNSUPPORTED, "unknown dtype");
     if (!(eps > 0.0f) || !std::isfinite(eps)) return fail(KDA_ERR_INVALID_ARG, "eps must be finite and > 0");
     if (rows == 0) return ok();                 // nothing to read or write (pointers may be NULL)
     if (!o || !z || !weight || !y) return fail(KDA_ERR_INVALID_ARG, "a required pointer is NULL");
-    if ((rows + 15) / 16 > (int64_t)0x7fffffff) return fail(KDA_ERR_INVALID_ARG, "rows too large");
+    if ((rows + 3) / 4 > (int64_t)0x7fffffff) return fail(KDA_ERR_INVALID_ARG, "rows too large");
     kda_status_t st = check_aligned16({{o, "o"}, {z, "z"}, {weight, "weight"}, {y, "y"}});
     if (st != KDA_OK) return st;
     kda::NormGateArgs a;
-    a.o = o; a.z = z; a.w = weight; a.eps = eps; a.rows = rows; a.bf16 = io_dtype == KDA_BF16;
+    a.o = o; a.z = z; a.w = weight; a.eps = eps; a.rows = rows; a.D = D; a.bf16 = io_dtype == KDA_BF16;
     a.y = y; a.stream = (hipStream_t)stream;
     hipError_t e = kda::launch_norm_gate(a);
     if (e != hipSuccess) return hip_fail(e, "kda_output_norm_gate launch");

@@ -36,8 +36,46 @@ __global__ __launch_bounds__(256) void norm_gate_kernel(const T *__restrict__ o,
     if (valid) store8_nt<T>(y + base, out);
 }
 
+// Rows of any other width D <= 256 (head sizes other than 128): one wave per
+// row, lane l holding features l, l + 64, l + 128, l + 192 below D, the sum of
+// squares reduced over the wave.
+template <typename T>
+__global__ __launch_bounds__(256) void norm_gate_any_kernel(const T *__restrict__ o,
+                                                            const T *__restrict__ z,
+                                                            const float *__restrict__ w, float eps,
+                                                            int64_t rows, int D, T *y)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= rows) return;                        // the whole wave
+    const size_t base = (size_t)row * D;
+    float x[4], ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int c = lane + 64 * e;
+        x[e] = c < D ? to_f32(o[base + c]) : 0.0f;
+        ss = fmaf(x[e], x[e], ss);
+    }
+    const float r = rsqrtf(wave_sum(ss) / (float)D + eps);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const int c = lane + 64 * e;
+        if (c < D) y[base + c] = from_f32<T>(x[e] * r * w[c] * sigmoid_f(to_f32(z[base + c])));
+    }
+}
+
 hipError_t launch_norm_gate(const NormGateArgs &a) {
     if (a.rows <= 0) return hipSuccess;
+    if (a.D != kHeadDim) {
+        const int64_t blocks = (a.rows + 3) / 4;
+        if (a.bf16)
+            norm_gate_any_kernel<__bf16><<<(unsigned)blocks, 256, 0, a.stream>>>(
+                (const __bf16 *)a.o, (const __bf16 *)a.z, a.w, a.eps, a.rows, a.D, (__bf16 *)a.y);
+        else
+            norm_gate_any_kernel<float><<<(unsigned)blocks, 256, 0, a.stream>>>(
+                (const float *)a.o, (const float *)a.z, a.w, a.eps, a.rows, a.D, (float *)a.y);
+        return hipGetLastError();
+    }
     const int64_t blocks = (a.rows + 15) / 16;
     if (a.bf16)
         norm_gate_kernel<__bf16><<<(unsigned)blocks, 256, 0, a.stream>>>(

@@ -31,10 +31,6 @@ namespace {
 constexpr int kGTok = 16;    // tokens per group
 constexpr int kGRows = 16;   // state rows per workgroup
 
-template <typename T> __device__ __forceinline__ T from_f32(float x);
-template <> __device__ __forceinline__ float from_f32<float>(float x) { return x; }
-template <> __device__ __forceinline__ __bf16 from_f32<__bf16>(float x) { return (__bf16)x; }
-
 // Workgroup b -> (sequence * H + head, row block): the row blocks of one
 // (sequence, head) share its token data, so they go to one XCD (workgroups are
 // dealt to the 8 XCDs round-robin by index).

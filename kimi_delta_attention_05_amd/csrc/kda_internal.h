@@ -36,6 +36,7 @@ struct NormGateArgs {
     const float *w;
     float eps;
     int64_t rows;
+    int D = 128;                        // features per row (128, or any width up to 256)
     bool bf16;
     void *y;
     hipStream_t stream;

@@ -329,9 +329,9 @@ def decode_step(q, k, v, g, beta_raw, A_log, dt_bias, state, *, scale: float = N
 def output_norm_gate(o: torch.Tensor, gate: torch.Tensor, norm_weight: torch.Tensor, *,
                      eps: float = NORM_EPS, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Output epilogue (kda_output_norm_gate): per-row RMS norm over the last axis
-    (128 features), channel weight, sigmoid gate.
+    (128 features, or any width up to 256), channel weight, sigmoid gate.
 
-    o, gate: [..., 128] bf16 or fp32 (same dtype); norm_weight: [128] fp32.
+    o, gate: [..., D] bf16 or fp32 (same dtype); norm_weight: [D] fp32.
     Returns y with o's shape and dtype (`out` may be `o` itself).
     """
     D = o.shape[-1]

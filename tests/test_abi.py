@@ -140,7 +140,7 @@ def norm_gate_call(kda, **kw):
 
 
 @pytest.mark.parametrize("kw,status", [
-    (dict(rows=-1), 1), (dict(D=64), 2), (dict(dt=9), 2), (dict(eps=0.0), 1),
+    (dict(rows=-1), 1), (dict(D=257), 2), (dict(D=0), 2), (dict(dt=9), 2), (dict(eps=0.0), 1),
     (dict(eps=float("nan")), 1), (dict(o=None), 1), (dict(z=None), 1), (dict(w=None), 1),
     (dict(y=None), 1), (dict(o=FAKE + 2), 1), (dict(z=FAKE + 8), 1), (dict(w=FAKE + 4), 1),
     (dict(y=FAKE + 4), 1), (dict(rows=1 << 40), 1),
@@ -154,7 +154,7 @@ def test_output_norm_gate_zero_rows_enqueues_nothing(kda):
     # rows = 0 returns OK without touching memory or launching, NULL pointers included
     assert norm_gate_call(kda, rows=0) == 0
     assert norm_gate_call(kda, rows=0, o=None, z=None, w=None, y=None) == 0
-    assert norm_gate_call(kda, rows=0, D=64) == 2
+    assert norm_gate_call(kda, rows=0, D=300) == 2
 
 
 def short_conv_call(kda, **kw):

@@ -132,3 +132,20 @@ def test_norm_gate_bench_size_sampled(kda):
     idx = torch.cat([idx, torch.tensor([0, rows - 1])])
     ref = oracle.output_norm_gate(o[idx], z[idx], w, eps=EPS)
     assert max_err_bf16_out(y[idx], ref) <= 1e-5
+
+
+@pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
+@pytest.mark.parametrize("D,rows", [(64, 1001), (17, 5), (256, 63), (1, 9), (96, 4)])
+def test_norm_gate_other_widths(kda, dtype, D, rows):
+    """Rows of widths other than 128 (the outputs of other head sizes): the
+    one-wave-per-row kernel, same bar as the 128-wide kernel."""
+    gen = torch.Generator().manual_seed(950 + D + rows)
+    o = (torch.randn(rows, D, generator=gen) *
+         torch.exp(3 * torch.randn(rows, 1, generator=gen))).to(dtype)
+    z = (torch.randn(rows, D, generator=gen) * 2.0).to(dtype)
+    w = torch.rand(D, generator=gen) + 0.5
+    y = kda.output_norm_gate(o.to(DEV), z.to(DEV), w.to(DEV), eps=EPS)
+    torch.cuda.synchronize()
+    e = err(y, oracle.output_norm_gate(o, z, w, eps=EPS), dtype)
+    print("norm_gate D=%d rows=%d %s: %.3e" % (D, rows, dtype, e), flush=True)
+    assert y.shape == (rows, D) and e <= 1e-5
