@@ -68,3 +68,59 @@ def test_random_shape_parity(kda, seed):
     errs = [max_err_rel_rms(x, ref) for x, ref in ((o1, ro), (h1, rht), (o2, ro), (h2, rht))]
     print("errors chunked o %.2e ht %.2e, token-by-token o %.2e ht %.2e" % tuple(errs), flush=True)
     assert max(errs) <= tol, errs
+
+
+@pytest.mark.parametrize("seed", list(range(8)))
+def test_random_shape_backward(kda, seed):
+    """The training backward on random shapes, every gradient against the fp64
+    backward oracle at 1e-4 of its rms (fp32 arithmetic throughout)."""
+    c = draw(9000 + seed)
+    c["lengths"] = [min(x, 90) for x in c["lengths"]]        # the oracle's reverse sweep is slow
+    print("case", seed, c, flush=True)
+    p = kda_inputs.make_prefill(c["lengths"], c["H"], token_dtype=c["dtype"],
+                                h0_std=0.1 if c["h0"] else None, chunk=c["chunk"], seed=9500 + seed,
+                                K=c["K"], V=c["V"], g_std=c["g_std"])
+    gen = torch.Generator().manual_seed(9600 + seed)
+    do = torch.randn(p.T, p.H, c["V"], generator=gen).to(c["dtype"])
+    dht = torch.randn(p.N, p.H, c["V"], c["K"], generator=gen) * 0.1
+    G = c["H"] // c["Hqk"]
+    d = prefill_to_device(p, DEV)
+    q, k = d["q"][:, ::G].contiguous(), d["k"][:, ::G].contiguous()
+    r = kda.backward(q, k, d["v"], d["g"], d["beta_raw"], d["A_log"], d["dt_bias"],
+                     d["cu_seqlens"], do.to(DEV), scale=p.scale, initial_state=d["h0"],
+                     d_final_state=dht.to(DEV))
+    torch.cuda.synchronize()
+    qr = p.q[:, ::G].repeat_interleave(G, dim=1)
+    kr = p.k[:, ::G].repeat_interleave(G, dim=1)
+    ref = oracle.kda_backward(qr, kr, p.v, p.g, p.beta_raw, p.A_log, p.dt_bias, p.cu_seqlens, do,
+                              scale=p.scale, h0=p.h0, dht=dht)
+    for key in ("dq", "dk"):
+        ref[key] = ref[key].reshape(p.T, c["Hqk"], G, c["K"]).sum(axis=2)
+    keys = ("dq", "dk", "dv", "dg", "dbeta", "dA_log", "ddt_bias", "dh0")
+    worst = {key: max_err_rel_rms(r[key], ref[key]) for key in keys if ref[key].size}
+    print("backward errors", " ".join("%s=%.2e" % kv for kv in worst.items()), flush=True)
+    assert max(worst.values()) <= 1e-4, worst
+
+
+@pytest.mark.parametrize("seed", list(range(8)))
+def test_random_shape_decode(kda, seed):
+    """Decode steps on random batch sizes, head counts and head sizes (128 on the
+    decode kernel, other sizes on the token-by-token kernel), several steps."""
+    r = np.random.default_rng(9900 + seed)
+    B, H = int(r.integers(1, 40)), int(r.integers(1, 9))
+    K, V = (128, 128) if r.random() < 0.5 else (int(r.integers(1, 257)), int(r.integers(1, 257)))
+    d = kda_inputs.make_decode(B, H, 3, seed=9950 + seed, K=K, V=V)
+    state = d.state.to(DEV).clone()
+    outs = []
+    for st in d.steps:
+        outs.append(kda.decode_step(st["q"].to(DEV), st["k"].to(DEV), st["v"].to(DEV),
+                                    st["g"].to(DEV), st["beta_raw"].to(DEV), d.A_log.to(DEV),
+                                    d.dt_bias.to(DEV), state, scale=d.scale,
+                                    o_dtype=torch.float32))
+    torch.cuda.synchronize()
+    ref_outs, ref_state = oracle.kda_decode_steps(d.steps, d.state, d.A_log, d.dt_bias,
+                                                  scale=d.scale)
+    eo = max(max_err_rel_rms(a, b) for a, b in zip(outs, ref_outs))
+    eh = max_err_rel_rms(state, ref_state)
+    print("decode B=%d H=%d K=%d V=%d: o %.2e state %.2e" % (B, H, K, V, eo, eh), flush=True)
+    assert eo <= 2e-2 and eh <= 2e-2
