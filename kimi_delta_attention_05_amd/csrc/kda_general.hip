@@ -21,6 +21,10 @@
 // DPP row per token), then each row runs the 16 steps, the two K-wide dot
 // products being DPP row sums, and the group's outputs leave through LDS as 16
 // contiguous values per token.
+//
+// The file also holds the row copy with zero fill through which head sizes up
+// to 128 run on the chunkwise prefill and backward kernels instead (inputs
+// widened to 128 channels and rows with zeros, results narrowed back).
 #include "kda_common.h"
 #include "kda_internal.h"
 
