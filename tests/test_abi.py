@@ -307,6 +307,18 @@ def test_workspace_size_below_128(kda):
             kda.workspace_size(T, N, H, C, torch.bfloat16, K=K, V=V)
 
 
+def test_backward_workspace_size_below_128(kda):
+    # head sizes below 128 add the padded inputs, adjoints and gradients after the
+    # backward's own layout; 0 and 129 are rejected
+    T, N, H = 1000, 2, 3
+    base = kda.backward_workspace_size(T, N, H)
+    padded = kda.backward_workspace_size(T, N, H, K=64, V=32)
+    assert padded >= base + T * H * 128 * 4 * 9 + 3 * N * H * 128 * 128 * 4
+    for K, V in ((0, 64), (64, 129)):
+        with pytest.raises(ValueError):
+            kda.backward_workspace_size(T, N, H, K=K, V=V)
+
+
 def test_workspace_size_arithmetic(kda):
     # one record per (slot, head); slots = floor(T / C) + N
     for T, N, H, C in [(8192, 1, 96, 64), (8192, 6, 96, 64), (17, 1, 1, 16), (115, 3, 4, 32), (0, 2, 3, 64)]:
