@@ -174,9 +174,9 @@ kda_status_t kda_chunk_fwd_inter(const void *q, const void *k, const void *v,
  * The state is read once and written once per step.
  * Other head sizes (1 <= K, V <= 256, FlashKDA issue page, "Proposed scope"):
  * q, k, g [B, H, K], v, o [B, H, V], state [B, H, V, K], run by the
- * token-by-token kernel of kda_recurrent_fwd with one token per request; this
- * and kda_decode_step_grouped without a state pool or epilogue accept them,
- * the pool and epilogue forms return KDA_ERR_UNSUPPORTED.
+ * token-by-token kernel of kda_recurrent_fwd with one token per request; this,
+ * the state-pool form and kda_decode_step_grouped accept them, the forms with
+ * the fused epilogue return KDA_ERR_UNSUPPORTED.
  */
 kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
                              const float *g, const float *beta_raw,

@@ -168,8 +168,8 @@ kda_status_t decode_step_impl(const void *q, const void *k, const void *v,
                               const char *name, int32_t H_qk) {
     if (B < 1) return fail(KDA_ERR_INVALID_ARG, "B must be >= 1");
     const bool general = (K != 128 || V != 128) && K >= 1 && K <= 256 && V >= 1 && V <= 256;
-    if (general && (z || slots))
-        return fail(KDA_ERR_UNSUPPORTED, "the state pool and the fused epilogue need K = V = 128");
+    if (general && z)
+        return fail(KDA_ERR_UNSUPPORTED, "the fused epilogue needs K = V = 128");
     kda_status_t st = check_common(H, general ? 128 : K, general ? 128 : V, scale, lower_bound,
                                    in_dtype, o_dtype);
     if (st != KDA_OK) return st;
@@ -205,6 +205,7 @@ kda_status_t decode_step_impl(const void *q, const void *k, const void *v,
         ga.h0 = state; ga.ht = state; ga.o = o;
         ga.in_bf16 = in_dtype == KDA_BF16; ga.out_bf16 = o_dtype == KDA_BF16;
         ga.stream = (hipStream_t)stream;
+        ga.slots = slots; ga.num_slots = num_slots;
         const hipError_t e = kda::launch_recurrent_fwd(ga);
         if (e != hipSuccess) return hip_fail(e, name);
         return ok();

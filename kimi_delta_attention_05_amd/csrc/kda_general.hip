@@ -68,7 +68,19 @@ __global__ __launch_bounds__(256) void recurrent_fwd_kernel(GeneralArgs p)
     __shared__ float sB[kGTok], sV[kGTok][kGRows], sO[kGTok][kGRows];
 
     const Tin *q = (const Tin *)p.q, *k = (const Tin *)p.k, *v = (const Tin *)p.v;
-    const size_t sbase = ((size_t)nh * V + (row_ok ? grow : 0)) * K;
+    // with a state pool the state of request n is entry slots[n]; a request whose
+    // slot lies outside the pool is padding: zero outputs, no state touched
+    int64_t snh = nh;
+    if (p.slots) {
+        const int sl = p.slots[n];
+        if (sl < 0 || sl >= p.num_slots) {
+            const int vr = vb * kGRows + tid;
+            if (tid < kGRows && vr < V) ((Tout *)p.o)[(size_t)nh * V + vr] = from_f32<Tout>(0.0f);
+            return;
+        }
+        snh = (int64_t)sl * H + h;
+    }
+    const size_t sbase = ((size_t)snh * V + (row_ok ? grow : 0)) * K;
     float S[NE];
 #pragma unroll
     for (int e = 0; e < NE; ++e) {

@@ -181,6 +181,10 @@ struct GeneralArgs {
     void *o;
     bool in_bf16, out_bf16;
     hipStream_t stream;
+    // state pool (decode only, cu_seqlens == nullptr): sequence n's state is pool
+    // entry slots[n]; an entry outside [0, num_slots) marks a padding request
+    const int32_t *slots = nullptr;
+    int num_slots = 0;
 };
 int64_t general_blocks(int64_t N, int64_t H, int V);
 // dst row d = src row (d / rd) * rs + d % rd if d % rd < rs (first min(src_cols,

@@ -125,7 +125,7 @@ def slots_call(kda, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(S=0), 1), (dict(idx=None), 1), (dict(idx=FAKE + 2), 1), (dict(pool=None), 1),
     (dict(pool=FAKE + 4), 1), (dict(S=1 << 30, H=4), 1), (dict(z=FAKE), 1),
-    (dict(z=FAKE, w=FAKE, eps=0.0), 1), (dict(K=64), 2), (dict(B=0), 1),
+    (dict(z=FAKE, w=FAKE, eps=0.0), 1), (dict(K=257), 2), (dict(B=0), 1),
 ])
 def test_decode_slots_rejects(kda, kw, status):
     assert slots_call(kda, **kw) == status

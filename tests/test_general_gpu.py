@@ -232,7 +232,7 @@ def test_decode_step_other_sizes(kda, K, V, Hqk):
     assert eo <= 2e-2 and eh <= 2e-2
 
 
-def test_decode_other_sizes_pool_and_epilogue_rejected(kda):
+def test_decode_other_sizes_epilogue_rejected(kda):
     d = kda_inputs.make_decode(2, 2, 1, seed=3, K=64, V=64)
     st = {k: v.to(DEV) for k, v in d.steps[0].items()}
     state = d.state.to(DEV)
@@ -241,10 +241,34 @@ def test_decode_other_sizes_pool_and_epilogue_rejected(kda):
     with pytest.raises(kda.KDAError):
         kda.decode_step(st["q"], st["k"], st["v"], st["g"], st["beta_raw"], d.A_log.to(DEV),
                         d.dt_bias.to(DEV), state, scale=d.scale, gate=z, norm_weight=w)
-    with pytest.raises(kda.KDAError):
-        kda.decode_step(st["q"], st["k"], st["v"], st["g"], st["beta_raw"], d.A_log.to(DEV),
-                        d.dt_bias.to(DEV), state, scale=d.scale,
-                        slot_idx=torch.zeros(2, dtype=torch.int32, device=DEV))
+
+
+def test_decode_other_sizes_state_pool(kda):
+    """The serving decode over a state pool at K = 48, V = 80: request b uses pool
+    entry slot_idx[b]; the result equals the plain step on the gathered states,
+    bit for bit, the other pool entries are untouched and a padding request
+    (slot -1) gets zero outputs."""
+    B, H, S, K, V = 5, 3, 9, 48, 80
+    d = kda_inputs.make_decode(B, H, 2, seed=77, K=K, V=V)
+    gen = torch.Generator().manual_seed(78)
+    pool = (torch.randn(S, H, V, K, generator=gen) * 0.1).to(DEV)
+    slots = torch.tensor([4, 0, -1, 7, 2], dtype=torch.int32, device=DEV)
+    ref_state = pool[slots.clamp(min=0).long()].clone()
+    pool0 = pool.clone()
+    for st in d.steps:
+        args = [st[n].to(DEV) for n in ("q", "k", "v", "g", "beta_raw")]
+        o = kda.decode_step(*args, d.A_log.to(DEV), d.dt_bias.to(DEV), pool, scale=d.scale,
+                            o_dtype=torch.float32, slot_idx=slots)
+        o_ref = kda.decode_step(*args, d.A_log.to(DEV), d.dt_bias.to(DEV), ref_state,
+                                scale=d.scale, o_dtype=torch.float32)
+        torch.cuda.synchronize()
+        live = [0, 1, 3, 4]
+        assert torch.equal(o[live], o_ref[live])
+        assert torch.count_nonzero(o[2]) == 0
+    for b, sl in ((0, 4), (1, 0), (3, 7), (4, 2)):
+        assert torch.equal(pool[sl], ref_state[b])
+    for sl in (1, 3, 5, 6, 8):
+        assert torch.equal(pool[sl], pool0[sl])
 
 
 @pytest.mark.parametrize("K,V,dtype,Hqk", [(64, 64, torch.bfloat16, None),
