@@ -174,9 +174,10 @@ kda_status_t kda_chunk_fwd_inter(const void *q, const void *k, const void *v,
  * The state is read once and written once per step.
  * Other head sizes (1 <= K, V <= 256, FlashKDA issue page, "Proposed scope"):
  * q, k, g [B, H, K], v, o [B, H, V], state [B, H, V, K], run by the
- * token-by-token kernel of kda_recurrent_fwd with one token per request; this,
- * the state-pool form and kda_decode_step_grouped accept them, the forms with
- * the fused epilogue return KDA_ERR_UNSUPPORTED.
+ * token-by-token kernel of kda_recurrent_fwd with one token per request; every
+ * decode form accepts them (the output epilogue, whose row then spans several
+ * of the step's workgroups, runs as a second pass over o: norm_weight [V], z
+ * [B, H, V]; the rows (B * H) must fit 4 per workgroup in one launch).
  */
 kda_status_t kda_decode_step(const void *q, const void *k, const void *v,
                              const float *g, const float *beta_raw,

@@ -168,8 +168,6 @@ kda_status_t decode_step_impl(const void *q, const void *k, const void *v,
                               const char *name, int32_t H_qk) {
     if (B < 1) return fail(KDA_ERR_INVALID_ARG, "B must be >= 1");
     const bool general = (K != 128 || V != 128) && K >= 1 && K <= 256 && V >= 1 && V <= 256;
-    if (general && z)
-        return fail(KDA_ERR_UNSUPPORTED, "the fused epilogue needs K = V = 128");
     kda_status_t st = check_common(H, general ? 128 : K, general ? 128 : V, scale, lower_bound,
                                    in_dtype, o_dtype);
     if (st != KDA_OK) return st;
@@ -206,7 +204,17 @@ kda_status_t decode_step_impl(const void *q, const void *k, const void *v,
         ga.in_bf16 = in_dtype == KDA_BF16; ga.out_bf16 = o_dtype == KDA_BF16;
         ga.stream = (hipStream_t)stream;
         ga.slots = slots; ga.num_slots = num_slots;
-        const hipError_t e = kda::launch_recurrent_fwd(ga);
+        hipError_t e = kda::launch_recurrent_fwd(ga);
+        if (e == hipSuccess && z) {
+            // the output epilogue over each (request, head) row of V outputs, in
+            // place: the row spans several of the step's workgroups, so it runs
+            // as a second pass (padding requests' zero rows stay zero)
+            kda::NormGateArgs na;
+            na.o = o; na.z = z; na.w = norm_weight; na.eps = norm_eps; na.rows = (int64_t)B * H;
+            na.D = V; na.bf16 = o_dtype == KDA_BF16; na.z_bf16 = in_dtype == KDA_BF16; na.y = o;
+            na.stream = (hipStream_t)stream;
+            e = kda::launch_norm_gate(na);
+        }
         if (e != hipSuccess) return hip_fail(e, name);
         return ok();
     }
@@ -484,6 +492,7 @@ kda_status_t kda_output_norm_gate(const void *o, const void *z, const float *wei
     if (st != KDA_OK) return st;
     kda::NormGateArgs a;
     a.o = o; a.z = z; a.w = weight; a.eps = eps; a.rows = rows; a.D = D; a.bf16 = io_dtype == KDA_BF16;
+    a.z_bf16 = a.bf16;
     a.y = y; a.stream = (hipStream_t)stream;
     hipError_t e = kda::launch_norm_gate(a);
     if (e != hipSuccess) return hip_fail(e, "kda_output_norm_gate launch");

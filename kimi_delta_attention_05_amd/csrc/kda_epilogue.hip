@@ -39,9 +39,9 @@ __global__ __launch_bounds__(256) void norm_gate_kernel(const T *__restrict__ o,
 // Rows of any other width D <= 256 (head sizes other than 128): one wave per
 // row, lane l holding features l, l + 64, l + 128, l + 192 below D, the sum of
 // squares reduced over the wave.
-template <typename T>
+template <typename T, typename Z>
 __global__ __launch_bounds__(256) void norm_gate_any_kernel(const T *__restrict__ o,
-                                                            const T *__restrict__ z,
+                                                            const Z *__restrict__ z,
                                                             const float *__restrict__ w, float eps,
                                                             int64_t rows, int D, T *y)
 {
@@ -67,12 +67,18 @@ __global__ __launch_bounds__(256) void norm_gate_any_kernel(const T *__restrict_
 hipError_t launch_norm_gate(const NormGateArgs &a) {
     if (a.rows <= 0) return hipSuccess;
     if (a.D != kHeadDim) {
-        const int64_t blocks = (a.rows + 3) / 4;
-        if (a.bf16)
-            norm_gate_any_kernel<__bf16><<<(unsigned)blocks, 256, 0, a.stream>>>(
+        const unsigned blocks = (unsigned)((a.rows + 3) / 4);
+        if (a.bf16 && a.z_bf16)
+            norm_gate_any_kernel<__bf16, __bf16><<<blocks, 256, 0, a.stream>>>(
                 (const __bf16 *)a.o, (const __bf16 *)a.z, a.w, a.eps, a.rows, a.D, (__bf16 *)a.y);
+        else if (a.bf16)
+            norm_gate_any_kernel<__bf16, float><<<blocks, 256, 0, a.stream>>>(
+                (const __bf16 *)a.o, (const float *)a.z, a.w, a.eps, a.rows, a.D, (__bf16 *)a.y);
+        else if (a.z_bf16)
+            norm_gate_any_kernel<float, __bf16><<<blocks, 256, 0, a.stream>>>(
+                (const float *)a.o, (const __bf16 *)a.z, a.w, a.eps, a.rows, a.D, (float *)a.y);
         else
-            norm_gate_any_kernel<float><<<(unsigned)blocks, 256, 0, a.stream>>>(
+            norm_gate_any_kernel<float, float><<<blocks, 256, 0, a.stream>>>(
                 (const float *)a.o, (const float *)a.z, a.w, a.eps, a.rows, a.D, (float *)a.y);
         return hipGetLastError();
     }

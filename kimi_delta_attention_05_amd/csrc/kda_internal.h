@@ -38,6 +38,7 @@ struct NormGateArgs {
     int64_t rows;
     int D = 128;                        // features per row (128, or any width up to 256)
     bool bf16;
+    bool z_bf16 = false;                // dtype of z for widths other than 128 (else as o)
     void *y;
     hipStream_t stream;
 };

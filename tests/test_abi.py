@@ -104,7 +104,7 @@ def gated_call(kda, **kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(z=None), 1), (dict(w=None), 1), (dict(eps=0.0), 1), (dict(eps=-1e-5), 1),
     (dict(eps=float("inf")), 1), (dict(z=FAKE + 8), 1), (dict(w=FAKE + 4), 1),
-    (dict(K=64), 2), (dict(B=0), 1), (dict(state=None), 1), (dict(o=FAKE + 4), 1),
+    (dict(K=257), 2), (dict(B=0), 1), (dict(state=None), 1), (dict(o=FAKE + 4), 1),
 ])
 def test_decode_gated_rejects(kda, kw, status):
     assert gated_call(kda, **kw) == status

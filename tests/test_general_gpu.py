@@ -232,15 +232,36 @@ def test_decode_step_other_sizes(kda, K, V, Hqk):
     assert eo <= 2e-2 and eh <= 2e-2
 
 
-def test_decode_other_sizes_epilogue_rejected(kda):
-    d = kda_inputs.make_decode(2, 2, 1, seed=3, K=64, V=64)
-    st = {k: v.to(DEV) for k, v in d.steps[0].items()}
-    state = d.state.to(DEV)
-    z = torch.zeros((2, 2, 64), dtype=st["q"].dtype, device=DEV)
-    w = torch.ones(64, device=DEV)
-    with pytest.raises(kda.KDAError):
-        kda.decode_step(st["q"], st["k"], st["v"], st["g"], st["beta_raw"], d.A_log.to(DEV),
-                        d.dt_bias.to(DEV), state, scale=d.scale, gate=z, norm_weight=w)
+@pytest.mark.parametrize("o_dtype", [torch.float32, torch.bfloat16])
+def test_decode_other_sizes_with_epilogue(kda, o_dtype):
+    """The decode step with the output epilogue at K = 64, V = 96 (the epilogue as a
+    second pass over o): against the oracle's decode steps followed by the
+    oracle's norm and gate, over a state pool with a padding request."""
+    B, H, K, V = 4, 3, 64, 96
+    d = kda_inputs.make_decode(B, H, 3, seed=61, K=K, V=V)
+    gen = torch.Generator().manual_seed(62)
+    slots = torch.tensor([2, -1, 0, 5], dtype=torch.int32)
+    pool = (torch.randn(6, H, V, K, generator=gen) * 0.1)
+    w = torch.rand(V, generator=gen) + 0.5
+    pool_d = pool.to(DEV)
+    live = [0, 2, 3]
+    ref_state = pool[slots[live].long()].double().numpy()
+    for i, st in enumerate(d.steps):
+        z = (torch.randn(B, H, V, generator=gen) * 2.0).to(st["q"].dtype)
+        y = kda.decode_step(*(st[n].to(DEV) for n in ("q", "k", "v", "g", "beta_raw")),
+                            d.A_log.to(DEV), d.dt_bias.to(DEV), pool_d, scale=d.scale,
+                            o_dtype=o_dtype, gate=z.to(DEV), norm_weight=w.to(DEV),
+                            slot_idx=slots.to(DEV))
+        torch.cuda.synchronize()
+        sub = {n: st[n][live] for n in st}
+        ro, ref_state = oracle.kda_decode_steps([sub], ref_state, d.A_log, d.dt_bias,
+                                                scale=d.scale)
+        ry = oracle.output_norm_gate(ro[0], z[live], w, eps=kda.NORM_EPS)
+        e = (max_err_bf16_out(y[live], ry) if o_dtype == torch.bfloat16
+             else max_err_rel_rms(y[live], ry))
+        print("gated decode K=%d V=%d step %d: %.3e" % (K, V, i, e), flush=True)
+        assert e <= 2e-2 and torch.count_nonzero(y[1]) == 0
+    assert max_err_rel_rms(pool_d[[2, 0, 5]], ref_state) <= 2e-2
 
 
 def test_decode_other_sizes_state_pool(kda):
