@@ -100,17 +100,18 @@ def test_graph_capture_decode_slots(kda):
         assert torch.equal(gpool, ref_pool), rep
 
 
-@pytest.mark.parametrize("chunk", [32, 64])
-def test_graph_capture_prefill(kda, chunk):
-    """Capture chunk_fwd (intra + inter, caller workspace) and replay it on new
-    token values; every replay equals an eager call bit for bit."""
+@pytest.mark.parametrize("chunk,K,V", [(32, 128, 128), (64, 128, 128), (64, 64, 48)])
+def test_graph_capture_prefill(kda, chunk, K, V):
+    """Capture chunk_fwd (intra + inter, caller workspace; below 128 also the
+    zero-fill copies) and replay it on new token values; every replay equals an
+    eager call bit for bit."""
     lengths = [300, 0, 211, 64]
-    p = kda_inputs.make_prefill(lengths, 4, h0_std=0.1, chunk=chunk, seed=70)
+    p = kda_inputs.make_prefill(lengths, 4, h0_std=0.1, chunk=chunk, seed=70, K=K, V=V)
     names = ("q", "k", "v", "g", "beta_raw", "A_log", "dt_bias", "cu_seqlens", "h0")
     static = {n: getattr(p, n).to(DEV).clone() for n in names}
     ws = kda.Workspace(DEV)
-    o = torch.empty(p.T, 4, 128, dtype=torch.bfloat16, device=DEV)
-    ht = torch.empty(len(lengths), 4, 128, 128, dtype=torch.float32, device=DEV)
+    o = torch.empty(p.T, 4, V, dtype=torch.bfloat16, device=DEV)
+    ht = torch.empty(len(lengths), 4, V, K, dtype=torch.float32, device=DEV)
 
     def call(t, out_o, out_h, w):
         return kda.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta_raw"], t["A_log"],
@@ -129,7 +130,7 @@ def test_graph_capture_prefill(kda, chunk):
     torch.cuda.synchronize()
     ws2 = kda.Workspace(DEV)
     for rep in range(3):
-        q = kda_inputs.make_prefill(lengths, 4, h0_std=0.1, chunk=chunk, seed=80 + rep)
+        q = kda_inputs.make_prefill(lengths, 4, h0_std=0.1, chunk=chunk, seed=80 + rep, K=K, V=V)
         fresh = {n: getattr(q, n).to(DEV) for n in names}
         for n in names:
             static[n].copy_(fresh[n])
