@@ -213,6 +213,7 @@ def main():
     line["epilogue"] = epilogue_timing(kda, o, dsteps, dA, ddt, dstate, dd.scale, dout)
     line["front_end"] = front_end_timing(kda, (q, k, v), cu)
     line["backward"] = backward_timing(kda, p, (q, k, v, g, beta_raw, A_log, dt_bias, cu, h0))
+    line["other_prefill_configs"] = other_prefill_timing(kda, dev)
     line["any_head_size"] = general_timing(kda, dev)
     line["achievable"] = achievable_hbm(kernels)
 
@@ -350,6 +351,66 @@ def backward_timing(kda, p, dev_inputs, reps=3):
             "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_VALU_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4),
                          "alg_flops": flops}}
+
+
+def other_prefill_timing(kda, dev, reps=10):
+    """The prefill on the two other large workloads, beside the step and not
+    part of it: T=4096, H=32 (its ~0.2 GB of inputs fit in the 256 MB MALL, so it
+    is timed both back to back and with a 512 MB buffer written between runs)
+    and the packed six-sequence mix at H=96 (lengths 1300, 547, 2048, 963, 271,
+    3063). Each with its path HBM and MFMA fractions and its roofline fraction,
+    max(flops / MFMA peak, bytes / HBM peak) / time."""
+    import torch
+    import kda_inputs
+    out = {}
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    for name, p, cold in (("prefill T=4096 H=32", kda_inputs.prefill_4k(), True),
+                          ("prefill varlen six sequences H=96", kda_inputs.large_varlen(), False)):
+        args = [x.to(dev) for x in (p.q, p.k, p.v, p.g, p.beta_raw, p.A_log, p.dt_bias,
+                                    p.cu_seqlens)]
+        h0 = None if p.h0 is None else p.h0.to(dev)
+        o = torch.empty((p.T, p.H, D), dtype=torch.bfloat16, device=dev)
+        ht = torch.empty((p.N, p.H, D, D), dtype=torch.float32, device=dev)
+        ws = kda.Workspace(dev)
+
+        def run():
+            kda.chunk_fwd(*args, scale=p.scale, chunk_size=p.chunk, initial_state=h0, out=o,
+                          final_state=ht, workspace=ws)
+
+        def timed(between=None):
+            ts = []
+            for _ in range(reps):
+                if between is not None:
+                    between()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                run()
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            return sorted(ts)[len(ts) // 2]
+
+        run()
+        torch.cuda.synchronize()
+        th = p.T * p.H
+        nbytes = th * (4 * 2 * D + 4 * D + 4) + (2 if h0 is not None else 1) * p.N * p.H * D * D * 4
+        flops = th * prefill_flops_per_token_head(p.chunk)
+
+        def stats(ms):
+            t = ms * 1e-3
+            return {"ms": round(ms, 4), "tokens_per_s": round(p.T / t, 1),
+                    "hbm_frac_path": round(nbytes / t / 1e9 / HBM_PEAK_GBS, 4),
+                    "mfma_frac_path": round(flops / t / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4),
+                    "roofline_frac": round(max(flops / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+                                               nbytes / (HBM_PEAK_GBS * 1e9)) / t, 4)}
+
+        r = {"tokens": p.T, "heads": p.H, "sequences": p.N, "alg_bytes": nbytes, "alg_flops": flops}
+        r["warm"] = stats(timed())
+        if cold:
+            r["mall_flushed"] = stats(timed(lambda: flush.fill_(1)))
+        out[name] = r
+    del flush
+    return out
 
 
 def general_timing(kda, dev, T=8192, H=96, reps=3):

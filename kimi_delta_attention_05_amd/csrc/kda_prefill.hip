@@ -868,11 +868,32 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
 
     // workgroup -> (chain, half); both halves of a chain land on the same XCD
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-    const int chain = (local >> 1) * 8 + xcd;
+    int chain = (local >> 1) * 8 + xcd;
     const int vg = local & 1;
     if (chain >= nchains) return;
     const int H = p.H;
-    const int n = chain / H, h = chain % H;
+    int n = chain / H;
+    const int h = chain % H;
+    // Packed batches of up to 64 sequences take them longest first: the chains
+    // of rank r go to the r-th row of workgroups, so the longest chains start
+    // in the first round of workgroups (one per CU) and shorter ones fill in
+    // behind them instead of trailing at the end. Lane m ranks sequence m by
+    // length (ties by index); the lane holding rank n names the sequence.
+    if (p.N > 1 && p.N <= 64) {
+        const int lane = threadIdx.x & 63;
+        int rank = -1;
+        if (lane < p.N) {
+            const int64_t len_l = p.cu_seqlens[lane + 1] - p.cu_seqlens[lane];
+            rank = 0;
+            for (int m = 0; m < p.N; ++m) {
+                const int64_t len_m = p.cu_seqlens[m + 1] - p.cu_seqlens[m];
+                rank += (len_m > len_l || (len_m == len_l && m < lane)) ? 1 : 0;
+            }
+        }
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(rank == n);
+        n = hit ? (int)__builtin_ctzll(hit) : n;       // ranks are a permutation: one lane
+        chain = n * H + h;
+    }
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform
