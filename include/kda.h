@@ -48,7 +48,7 @@ extern "C" {
 typedef enum {
     KDA_OK = 0,
     KDA_ERR_INVALID_ARG = 1,   /* NULL pointer, negative size, bad scale or bound */
-    KDA_ERR_UNSUPPORTED = 2,   /* K or V != 128, chunk not in {16,32,64}, bad dtype */
+    KDA_ERR_UNSUPPORTED = 2,   /* head size outside the entry point's range, chunk not in {16,32,64}, bad dtype */
     KDA_ERR_WORKSPACE = 3,     /* workspace NULL or smaller than required */
     KDA_ERR_HIP = 4            /* a HIP launch or runtime call failed */
 } kda_status_t;
@@ -382,16 +382,16 @@ kda_status_t kda_recurrent_fwd(const void *q, const void *k, const void *v,
  * Grouped value heads (FlashKDA issue page, "Proposed scope": grouped value
  * heads). H value heads share H_qk query/key heads, H a multiple of H_qk: value
  * head h reads q and k of head h / (H / H_qk). v, g, beta_raw, the states and
- * the outputs keep H heads; q and k are [T, H_qk, 128] (decode: [B, H_qk, 128]).
+ * the outputs keep H heads; q and k are [T, H_qk, K] (decode: [B, H_qk, K]).
  * The same computation as the ungrouped call with q and k repeated H / H_qk
  * times along the head axis; H_qk == H is the ungrouped call. Everything else
  * as for kda_chunk_fwd, kda_decode_step_slots / _gated / plain, and
  * kda_backward; H_qk that does not divide H is rejected with
- * KDA_ERR_INVALID_ARG. In kda_backward_grouped dq and dk are [T, H_qk, 128],
+ * KDA_ERR_INVALID_ARG. In kda_backward_grouped dq and dk are [T, H_qk, K],
  * summed over the value heads of each group.
  *
  * kda_decode_step_grouped covers the three decode forms: slot_idx NULL for a
- * state [B, H, 128, 128] (num_slots ignored), else a pool of num_slots entries
+ * state [B, H, V, K] (num_slots ignored), else a pool of num_slots entries
  * addressed as in kda_decode_step_slots; z NULL for no output epilogue.
  */
 kda_status_t kda_chunk_fwd_grouped(const void *q, const void *k, const void *v,
