@@ -1,6 +1,7 @@
 // Batched T=1 KDA decode step: one pass over the fp32 state, with the state
-// rows of a (request, head) split over 8 waves (two workgroups of 4 waves, or
-// one of 8 with the fused output epilogue, whose norm needs all 128 outputs).
+// rows of a (request, head) split over 8 waves (two workgroups of 4 waves), or
+// over 16 waves of one workgroup with the fused output epilogue, whose norm
+// needs all 128 outputs.
 //
 // Per (request b, head h) the value-first state S[128][128] is read once and
 // written once. Every state row v is independent given the per-token vectors:
@@ -145,18 +146,18 @@ __global__ __launch_bounds__(64 * NW) void decode_step_kernel(
 }
 
 // The plain step runs two 4-wave workgroups per (request, head), 64 state rows
-// each; the step with the epilogue one 8-wave workgroup per (request, head), so
-// that the norm sees the head's 128 outputs. Both keep 8 state rows per wave
-// (68 VGPRs, 7 waves per SIMD). Measured at B = 256, H = 32: plain 181 us
-// (one 4-wave workgroup per head holding 128 rows: 198 us; the 8-wave form:
-// 192 us; four workgroups of 32 rows: 184 us), with the epilogue 193 us (the
-// 4-wave form over 128 rows: 201 us).
+// each (8 rows per wave, 68 VGPRs, 7 waves per SIMD); the step with the
+// epilogue one 16-wave workgroup per (request, head), 8 rows per wave (60
+// VGPRs), so that the norm sees the head's 128 outputs. Measured at B = 256,
+// H = 32: plain 181 us (one 4-wave workgroup per head holding 128 rows: 198 us;
+// the 8-wave form: 192 us; four workgroups of 32 rows: 184 us), with the
+// epilogue 182 us (8 waves of 16 rows: 194 us; 4 waves of 32 rows: 201 us).
 template <typename Tin, typename Tout>
 static hipError_t launch_decode_t(const DecodeArgs &a) {
     const unsigned bh = (unsigned)(a.B * a.H);
     const int Hk = a.Hk > 0 ? a.Hk : a.H;
     if (a.z)
-        decode_step_kernel<Tin, Tout, true, 4, 8><<<bh, 512, 0, a.stream>>>(
+        decode_step_kernel<Tin, Tout, true, 2, 16><<<bh, 1024, 0, a.stream>>>(
             (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v, a.g, a.beta_raw,
             a.A_log, a.dt_bias, a.scale, a.lower_bound, a.state, (Tout *)a.o, a.H,
             (const Tin *)a.z, a.norm_w, a.norm_eps, a.slots, a.num_slots, Hk);
