@@ -15,6 +15,7 @@ stated for the five standard configurations:
   prefill    : B=1, T=4096, H=32, bf16 q/k/v, g ~ N(0, 2^2), chunk 64
   large      : B=1, T=8192, H=96, bf16, g ~ N(0, 2^2), chunk 64, h0 ~ N(0, 0.1^2)
   large_varlen: packed lengths [1300, 547, 2048, 963, 271, 3063], H=96, as large
+  packed_8x1024: eight packed sequences of 1024 tokens, H=96, as large
   decode     : 256 requests, H=32, 64 consecutive T=1 steps, state ~ N(0, 0.1^2)
   epilogue   : output-gate logits ~ N(0, 2^2) in the token dtype and an output-norm
                weight ~ U(0.5, 1.5) (stand-ins for the model's projection and weight)
@@ -167,6 +168,11 @@ def large():
 def large_varlen():
     return make_prefill(LARGE_VARLEN_LENGTHS, 96, g_std=2.0, h0_std=0.1, chunk=64,
                         seed=1013, name="prefill varlen[1300..3063] H=96 bf16 C=64")
+
+
+def packed_8x1024():
+    return make_prefill([1024] * 8, 96, g_std=2.0, h0_std=0.1, chunk=64, seed=1014,
+                        name="prefill packed 8x1024 H=96 bf16 C=64")
 
 
 def decode(n_steps=64):

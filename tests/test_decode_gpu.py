@@ -72,15 +72,22 @@ def test_decode_deterministic(kda):
     assert all(torch.equal(x, y) for x, y in zip(a, b)) and torch.equal(sa, sb)
 
 
-def test_decode_256x32_64_steps(kda):
+@pytest.mark.parametrize("o_dtype", [None, torch.float32])
+def test_decode_256x32_64_steps(kda, o_dtype):
+    """The decode workload: 256 requests, H=32, 64 consecutive steps, state in
+    place. bf16 output is judged beyond its own storage rounding (raw error
+    printed); fp32 output under the literal metric, over all 64 steps' outputs
+    and the final state."""
     d = kda_inputs.decode(64)
-    outs, state = run_steps(kda, d)
+    outs, state = run_steps(kda, d, o_dtype=o_dtype)
     ref_outs, ref_state = oracle.kda_decode_steps(d.steps, d.state, d.A_log, d.dt_bias,
                                                   scale=d.scale)
     o_all = torch.stack(outs).cpu()
     ref_all = np.stack(ref_outs)
-    e_o = max_err_bf16_out(o_all, ref_all)
     raw = max_err_rel_rms(o_all, ref_all)
+    e_o = max_err_bf16_out(o_all, ref_all) if o_all.dtype == torch.bfloat16 else raw
     e_s = max_err_rel_rms(state, ref_state)
-    print("decode 256x32x64: o err %.3e (raw %.3e) state err %.3e" % (e_o, raw, e_s), flush=True)
+    print("decode 256x32x64 o %s: o err %.3e (raw %.3e) state err %.3e"
+          % (o_all.dtype, e_o, raw, e_s), flush=True)
+    assert np.all(np.isfinite(o_all.double().numpy()))
     assert e_o <= 2e-2 and e_s <= 2e-2

@@ -289,23 +289,55 @@ def test_intra_stage_matches_chunk_form(kda, dtype, chunk):
 
 
 # ---- the large workloads (last: slowest) -------------------------------------
+# Every workload runs twice: with bf16 output (judged beyond its own storage
+# rounding, raw error printed) and with fp32 output, where the literal metric
+# max|o - o_ref| / rms(o_ref) <= 2e-2 applies unchanged.
 
-def test_prefill_4k(kda):
-    p = kda_inputs.prefill_4k()
-    ref = oracle_of(p)
+def _both_outputs(kda, p, ref):
     o, ht = run_gpu(kda, p)
     check(p, o, ht, ref, p.name)
+    del o, ht
     o32, ht32 = run_gpu(kda, p, o_dtype=torch.float32)
     check(p, o32, ht32, ref, p.name + " fp32-out")
 
 
-def test_large(kda):
-    p = kda_inputs.large()
+def test_prefill_4k(kda):
+    p = kda_inputs.prefill_4k()
+    _both_outputs(kda, p, oracle_of(p))
+
+
+@pytest.mark.parametrize("T,H", [(17, 16), (1024, 4)])
+def test_contract_fixed_shapes(kda, golden_contract, T, H):
+    """The fixed shapes the FlashInfer kda_backward contract admits besides the
+    standard workloads (B=1, T=17, H=16 and B=1, T=1024, H=4), bf16 tokens,
+    random initial states, chunk 64."""
+    assert [1, T, H] in golden_contract["admitted_shapes"]["fixed"]
+    p = kda_inputs.make_prefill([T], H, g_std=2.0, h0_std=0.1, chunk=64, seed=1100 + H,
+                                name="contract T=%d H=%d bf16 C=64" % (T, H))
+    _both_outputs(kda, p, oracle_of(p))
+
+
+def test_contract_fixed_t17_h16_fp32(kda):
+    p = kda_inputs.make_prefill([17], 16, token_dtype=torch.float32, h0_std=0.1, chunk=16,
+                                seed=1116, name="contract T=17 H=16 fp32 C=16")
     o, ht = run_gpu(kda, p)
     check(p, o, ht, oracle_of(p), p.name)
+
+
+def test_large(kda):
+    p = kda_inputs.large()
+    _both_outputs(kda, p, oracle_of(p))
 
 
 def test_large_varlen(kda):
     p = kda_inputs.large_varlen()
-    o, ht = run_gpu(kda, p)
-    check(p, o, ht, oracle_of(p), p.name)
+    _both_outputs(kda, p, oracle_of(p))
+
+
+def test_contract_packed_8x1024_h96(kda, golden_contract):
+    """The contract's third packed shape: eight sequences of 1024 tokens at H=96
+    (768 chains of the inter-chunk kernel)."""
+    lengths = [1024] * 8
+    assert {"lengths": lengths, "H": 96} in golden_contract["admitted_shapes"]["packed"]
+    p = kda_inputs.packed_8x1024()
+    _both_outputs(kda, p, oracle_of(p))
