@@ -426,6 +426,31 @@ kda_status_t kda_backward_grouped(const void *q, const void *k, const void *v, c
                                   float *d_initial_state, void *workspace, size_t workspace_bytes,
                                   void *stream);
 /*
+ * kda_chunk_fwd without a caller workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Arguments and results as kda_chunk_fwd; the
+ * workspace is a fixed device array inside the library of 128 MiB per GPU
+ * (134217728 bytes), allocated when the library's code is loaded on a device
+ * and held until the process ends. Sizes whose
+ * kda_chunk_fwd_workspace_size exceeds it (e.g. T = 8192 at H = 12 fits,
+ * T = 8192 at H = 96 does not) are rejected with KDA_ERR_WORKSPACE before any
+ * HIP call. The call allocates nothing (no hipMalloc, hipFree or allocating
+ * library routine); its first call on a device looks up that device's copy of
+ * the array. Every call on one GPU shares that GPU's array and it keeps the
+ * last call's contents (the kernels rewrite everything they read, so nothing
+ * needs clearing): calls that overlap on one GPU (other streams, other
+ * threads) race and give undefined results; serialise them.
+ */
+kda_status_t kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta_raw,
+                                   const float *A_log, const float *dt_bias,
+                                   float scale, float lower_bound,
+                                   const int64_t *cu_seqlens, int32_t num_seqs,
+                                   int64_t total_tokens, int32_t H, int32_t K, int32_t V,
+                                   int32_t chunk_size, kda_dtype_t in_dtype,
+                                   const float *initial_state, float *final_state,
+                                   void *o, kda_dtype_t o_dtype, void *stream);
+/*
  * Opt-in check of packed offsets (FlashInfer kda_backward page: offsets are
  * validated by one eager synchronisation, the launch path then trusts them).
  * Copies cu_seqlens to the host on `stream`, synchronises that stream and

@@ -289,7 +289,7 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
                               const float *initial_state, float *final_state,
                               void *o, kda_dtype_t o_dtype,
                               void *workspace, size_t workspace_bytes,
-                              void *stream, int32_t H_qk) {
+                              void *stream, int32_t H_qk, bool fixed_scratch = false) {
     if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 1");
     if (total_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens must be >= 0");
     kda_status_t st = check_common(H, K, V, scale, lower_bound, in_dtype, o_dtype, true);
@@ -308,17 +308,33 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
         return fail(KDA_ERR_INVALID_ARG, "too many chunks for one launch");
     const size_t need = kda_chunk_fwd_workspace_size(total_tokens, num_seqs, H, K, V, chunk_size,
                                                      in_dtype);
-    if (!workspace || workspace_bytes < need)
-        return fail(KDA_ERR_WORKSPACE, "workspace needs " + std::to_string(need) + " bytes, got " +
-                                           std::to_string(workspace_bytes));
-    if (((uintptr_t)workspace & 255) != 0)
-        return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    if (fixed_scratch) {
+        if (need > kda::kNoAllocScratchBytes)
+            return fail(KDA_ERR_WORKSPACE,
+                        std::string(name) + ": these sizes need " + std::to_string(need) +
+                            " bytes of scratch, above its fixed " +
+                            std::to_string(kda::kNoAllocScratchBytes) +
+                            " bytes; call kda_chunk_fwd with a caller workspace");
+    } else {
+        if (!workspace || workspace_bytes < need)
+            return fail(KDA_ERR_WORKSPACE, "workspace needs " + std::to_string(need) +
+                                               " bytes, got " + std::to_string(workspace_bytes));
+        if (((uintptr_t)workspace & 255) != 0)
+            return fail(KDA_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+    }
     st = check_aligned16({{q, "q"}, {k, "k"}, {v, "v"}, {g, "g"}, {dt_bias, "dt_bias"},
                           {initial_state, "initial_state"}, {final_state, "final_state"},
                           {o, "o"}});
     if (st != KDA_OK) return st;
     if (((uintptr_t)beta_raw & 3) != 0 || ((uintptr_t)A_log & 3) != 0)
         return fail(KDA_ERR_INVALID_ARG, "beta_raw and A_log must be 4-byte aligned");
+    if (fixed_scratch) {
+        // every argument check has passed: the current device's copy of the
+        // library's fixed scratch array replaces the caller workspace
+        const hipError_t e = kda::noalloc_scratch(&workspace);
+        if (e != hipSuccess) return hip_fail(e, name);
+        workspace_bytes = kda::kNoAllocScratchBytes;
+    }
 
     kda::PrefillArgs a;
     a.q = q; a.k = k; a.v = v; a.g = g; a.beta_raw = beta_raw; a.A_log = A_log; a.dt_bias = dt_bias;
@@ -406,6 +422,21 @@ kda_status_t kda_chunk_fwd_inter(KDA_CHUNK_PARAMS) {
 
 kda_status_t kda_chunk_fwd_grouped(KDA_CHUNK_PARAMS, int32_t H_qk) {
     return chunk_fwd_stages(3, "kda_chunk_fwd_grouped", KDA_CHUNK_ARGS, H_qk);
+}
+
+kda_status_t kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
+                                   const float *g, const float *beta_raw,
+                                   const float *A_log, const float *dt_bias,
+                                   float scale, float lower_bound,
+                                   const int64_t *cu_seqlens, int32_t num_seqs,
+                                   int64_t total_tokens, int32_t H, int32_t K, int32_t V,
+                                   int32_t chunk_size, kda_dtype_t in_dtype,
+                                   const float *initial_state, float *final_state,
+                                   void *o, kda_dtype_t o_dtype, void *stream) {
+    return chunk_fwd_stages(3, "kda_chunk_fwd_noalloc", q, k, v, g, beta_raw, A_log, dt_bias,
+                            scale, lower_bound, cu_seqlens, num_seqs, total_tokens, H, K, V,
+                            chunk_size, in_dtype, initial_state, final_state, o, o_dtype,
+                            nullptr, 0, stream, H, /*fixed_scratch=*/true);
 }
 
 kda_status_t kda_decode_step_grouped(const void *q, const void *k, const void *v,

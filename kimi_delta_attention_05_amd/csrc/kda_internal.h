@@ -194,6 +194,12 @@ hipError_t launch_pad_rows(const void *src, int src_cols, int64_t rs, void *dst,
                            int64_t rd, int64_t dst_rows, int elem_bytes, hipStream_t stream);
 hipError_t launch_recurrent_fwd(const GeneralArgs &a);
 
+// Fixed scratch of kda_chunk_fwd_noalloc: a file-scope device array of this many
+// bytes per GPU; noalloc_scratch returns the current device's copy (looked up
+// once per device).
+constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;
+hipError_t noalloc_scratch(void **ptr);
+
 hipError_t launch_decode(const DecodeArgs &a);
 hipError_t launch_norm_gate(const NormGateArgs &a);
 hipError_t launch_prefill(const PrefillArgs &a);

@@ -29,7 +29,7 @@ EXPORTS = ("kda_version", "kda_status_string", "kda_last_error",
            "kda_short_conv_slots",
            "kda_backward_workspace_size", "kda_backward", "kda_chunk_fwd_grouped",
            "kda_decode_step_grouped", "kda_backward_grouped", "kda_recurrent_fwd",
-           "kda_check_cu_seqlens")
+           "kda_check_cu_seqlens", "kda_chunk_fwd_noalloc")
 
 NORM_EPS = 1e-5   # default epsilon of the output norm (the pages give none)
 
@@ -54,6 +54,9 @@ for _name in ("kda_chunk_fwd", "kda_chunk_fwd_intra", "kda_chunk_fwd_inter"):
     getattr(_lib, _name).argtypes = [_P, _P, _P, _P, _P, _P, _P, _f32, _f32, _P, _i32, _i64,
                                      _i32, _i32, _i32, _i32, ctypes.c_int, _P, _P, _P,
                                      ctypes.c_int, _P, _sz, _P]
+_lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
+_lib.kda_chunk_fwd_noalloc.argtypes = _lib.kda_chunk_fwd.argtypes[:21] + [_P]
+NOALLOC_SCRATCH_BYTES = 128 << 20    # the fixed scratch of kda_chunk_fwd_noalloc
 _lib.kda_chunk_fwd_grouped.restype = ctypes.c_int
 _lib.kda_chunk_fwd_grouped.argtypes = _lib.kda_chunk_fwd.argtypes + [_i32]
 _STAGE_FN = {None: _lib.kda_chunk_fwd, "intra": _lib.kda_chunk_fwd_intra,

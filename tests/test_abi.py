@@ -356,3 +356,37 @@ def test_no_cpu_fallback_in_product():
             src = open(os.path.join(pkg, name)).read()
             assert "oracle" not in src, name
             assert "kda_inputs" not in src, name
+
+
+def noalloc_call(kda, **kw):
+    args = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, A_log=FAKE, dt_bias=FAKE, scale=0.088,
+                lb=-5.0, cu=FAKE, N=1, T=17, H=1, K=128, V=128, C=16, dt=kda.KDA_F32, h0=None,
+                ht=None, o=FAKE, odt=kda.KDA_F32, stream=None)
+    args.update(kw)
+    return kda.lib.kda_chunk_fwd_noalloc(args["q"], args["k"], args["v"], args["g"], args["beta"],
+                                         args["A_log"], args["dt_bias"], args["scale"], args["lb"],
+                                         args["cu"], args["N"], args["T"], args["H"], args["K"],
+                                         args["V"], args["C"], args["dt"], args["h0"], args["ht"],
+                                         args["o"], args["odt"], args["stream"])
+
+
+@pytest.mark.parametrize("kw,status", [
+    # beyond the fixed scratch: the T=8192, H=96 prefill needs ~0.92 GB
+    (dict(T=8192, H=96, C=64, dt=1, odt=1), 3),
+    (dict(T=1 << 20, H=4, C=64), 3),
+    (dict(K=129), 2), (dict(C=48), 2), (dict(N=0), 1), (dict(q=None), 1), (dict(lb=0.0), 1),
+    (dict(q=FAKE + 8), 1),
+])
+def test_chunk_fwd_noalloc_rejects(kda, kw, status):
+    """Checked on the host before any HIP call, like every entry point."""
+    assert noalloc_call(kda, **kw) == status
+    msg = kda.lib.kda_last_error().decode()
+    assert msg
+    if status == 3:
+        assert "fixed 134217728 bytes" in msg, msg
+
+
+def test_noalloc_scratch_limit_covers_stated_shapes(kda):
+    """The header's examples: T = 8192 at H = 12 fits the fixed scratch, H = 96 does not."""
+    assert kda.workspace_size(8192, 1, 12, 64) <= kda.NOALLOC_SCRATCH_BYTES
+    assert kda.workspace_size(8192, 1, 96, 64) > kda.NOALLOC_SCRATCH_BYTES
