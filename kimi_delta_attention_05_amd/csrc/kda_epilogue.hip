@@ -12,8 +12,9 @@
 
 namespace kda {
 
+// o is not __restrict__: y may alias it (the epilogue applied in place).
 template <typename T>
-__global__ __launch_bounds__(256) void norm_gate_kernel(const T *__restrict__ o, const T *__restrict__ z,
+__global__ __launch_bounds__(256) void norm_gate_kernel(const T *o, const T *__restrict__ z,
                                                         const float *__restrict__ w, float eps,
                                                         int64_t rows, T *y)
 {
@@ -40,7 +41,7 @@ __global__ __launch_bounds__(256) void norm_gate_kernel(const T *__restrict__ o,
 // row, lane l holding features l, l + 64, l + 128, l + 192 below D, the sum of
 // squares reduced over the wave.
 template <typename T, typename Z>
-__global__ __launch_bounds__(256) void norm_gate_any_kernel(const T *__restrict__ o,
+__global__ __launch_bounds__(256) void norm_gate_any_kernel(const T *o,
                                                             const Z *__restrict__ z,
                                                             const float *__restrict__ w, float eps,
                                                             int64_t rows, int D, T *y)

@@ -251,7 +251,8 @@ def decode_step(q, k, v, g, beta_raw, A_log, dt_bias, state, *, scale: float = N
     request b uses entry slot_idx[b]; indices outside [0, S) mark padding
     requests (zero output, no state touched) (kda_decode_step_slots).
     Head sizes other than 128 (1 <= K, V <= 256: q, k, g [B, H, K], v [B, H, V],
-    state [B, H, V, K]) run on the token-by-token kernel (slot_idx allowed, gate not).
+    state [B, H, V, K]) run on the token-by-token kernel; slot_idx and gate are accepted
+    there too (norm_weight [V]), the epilogue then applied as a second pass over o.
     """
     B, Hqk, K = q.shape
     H, V = v.shape[1], v.shape[2]
