@@ -210,16 +210,54 @@ def main():
         "cpu_baseline": None,
     }
 
+    line["decode_64_consecutive"] = decode_consecutive_timing(kda, dd, dsteps, dA, ddt, dstate, dout)
     line["epilogue"] = epilogue_timing(kda, o, dsteps, dA, ddt, dstate, dd.scale, dout)
+    line["epilogue"].update(gated_prefill_timing(kda, p, (q, k, v, g, beta_raw, A_log, dt_bias, cu),
+                                                 h0, o, ht, ws))
     line["front_end"] = front_end_timing(kda, (q, k, v), cu)
     line["backward"] = backward_timing(kda, p, (q, k, v, g, beta_raw, A_log, dt_bias, cu, h0))
     line["other_prefill_configs"] = other_prefill_timing(kda, dev)
     line["any_head_size"] = general_timing(kda, dev)
-    line["achievable"] = achievable_hbm(kernels)
+    line["achievable"] = achievable_hbm(kda, kernels)
 
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(p, dd)
     print(json.dumps(line), flush=True)
+
+
+def decode_consecutive_timing(kda, dd, dsteps, dA, ddt, dstate, dout, reps=5):
+    """The decode workload as stated: 64 consecutive T=1 steps of the B=256, H=32
+    batch, back to back on one stream (state carried in place), timed with
+    events around the 64 launches; the median of `reps` such sequences, the state
+    restored from a pristine copy outside the timed region."""
+    import torch
+    pristine = dstate.clone()
+    B, HD, Dv = dout.shape
+    n = len(dsteps)
+
+    def run():
+        for st in dsteps:
+            kda.decode_step(st["q"], st["k"], st["v"], st["g"], st["beta_raw"], dA, ddt, dstate,
+                            scale=dd.scale, out=dout)
+
+    dstate.copy_(pristine)
+    run()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        dstate.copy_(pristine)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = sorted(ts)[len(ts) // 2] / n
+    nbytes = B * HD * (2 * Dv * Dv * 4 + 3 * 2 * Dv + 4 * Dv + 4 + 2 * Dv)
+    gb = nbytes / (ms * 1e-3) / 1e9
+    return {"steps": n, "us_per_step": round(ms * 1e3, 2),
+            "tokens_per_s": round(B / (ms * 1e-3), 1), "alg_bytes_per_step": nbytes,
+            "achieved_GBs": round(gb, 1), "hbm_frac": round(gb / HBM_PEAK_GBS, 4)}
 
 
 def epilogue_timing(kda, o, dsteps, dA, ddt, dstate, dscale, dout, reps=20):
@@ -267,6 +305,50 @@ def epilogue_timing(kda, o, dsteps, dA, ddt, dstate, dscale, dout, reps=20):
                                  "traffic": measured_traffic("norm_gate_kernel")},
             "decode_step_gated_us": round(ms_gated * 1e3, 2),
             "decode_step_plain_us": round(ms_plain * 1e3, 2)}
+
+
+def gated_prefill_timing(kda, p, args, h0, o, ht, ws, reps=10):
+    """The prefill with the output epilogue (per-head RMS norm + sigmoid gate,
+    kda_chunk_fwd_gated: the epilogue pass enqueued right after the inter-chunk
+    kernel, o still in the memory-side cache), beside the plain prefill and the
+    plain prefill followed by a separate epilogue call: the median of `reps`
+    calls each."""
+    import torch
+    import kda_inputs
+    T, H, Dv = o.shape
+    z, w = kda_inputs.make_epilogue((T, H, Dv), seed=2003)
+    z, w = z.to(o.device), w.to(o.device)
+    y = torch.empty_like(o)
+
+    def plain():
+        kda.chunk_fwd(*args, scale=p.scale, chunk_size=p.chunk, initial_state=h0, out=o,
+                      final_state=ht, workspace=ws)
+
+    def gated():
+        kda.chunk_fwd(*args, scale=p.scale, chunk_size=p.chunk, initial_state=h0, out=y,
+                      final_state=ht, workspace=ws, gate=z, norm_weight=w)
+
+    def separate():
+        plain()
+        kda.output_norm_gate(o, z, w, out=y)
+
+    def med(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1))
+        return sorted(ts)[len(ts) // 2]
+
+    mp, mg, ms = med(plain), med(gated), med(separate)
+    return {"prefill_plain_ms": round(mp, 4), "prefill_gated_ms": round(mg, 4),
+            "prefill_then_epilogue_call_ms": round(ms, 4),
+            "gated_over_plain": round(mg / mp, 4)}
 
 
 def front_end_timing(kda, qkv, cu, W=4, reps=20):
@@ -354,18 +436,19 @@ def backward_timing(kda, p, dev_inputs, reps=3):
 
 
 def other_prefill_timing(kda, dev, reps=10):
-    """The prefill on the two other large workloads, beside the step and not
+    """The prefill on the three other large workloads, beside the step and not
     part of it: T=4096, H=32 (its ~0.2 GB of inputs fit in the 256 MB MALL, so it
-    is timed both back to back and with a 512 MB buffer written between runs)
-    and the packed six-sequence mix at H=96 (lengths 1300, 547, 2048, 963, 271,
-    3063). Each with its path HBM and MFMA fractions and its roofline fraction,
+    is timed both back to back and with a 512 MB buffer written between runs),
+    the packed six-sequence mix at H=96 (lengths 1300, 547, 2048, 963, 271,
+    3063) and eight packed sequences of 1024 tokens at H=96. Each with its path HBM and MFMA fractions and its roofline fraction,
     max(flops / MFMA peak, bytes / HBM peak) / time."""
     import torch
     import kda_inputs
     out = {}
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
     for name, p, cold in (("prefill T=4096 H=32", kda_inputs.prefill_4k(), True),
-                          ("prefill varlen six sequences H=96", kda_inputs.large_varlen(), False)):
+                          ("prefill varlen six sequences H=96", kda_inputs.large_varlen(), False),
+                          ("prefill packed 8x1024 H=96", kda_inputs.packed_8x1024(), False)):
         args = [x.to(dev) for x in (p.q, p.k, p.v, p.g, p.beta_raw, p.A_log, p.dt_bias,
                                     p.cu_seqlens)]
         h0 = None if p.h0 is None else p.h0.to(dev)
@@ -472,60 +555,82 @@ def general_timing(kda, dev, T=8192, H=96, reps=3):
     return out
 
 
-def achievable_hbm(kernels, nbytes=1 << 30, reps=5):
-    """A measured streaming rate beside the published 8 TB/s: the best of a few
-    plain 1 GiB device-to-device copies by the runtime (bytes read + written per
-    second), and each hot-path kernel's algorithmic rate as a fraction of it. It
-    is a lower bound of what HBM sustains, not a ceiling: the decode kernel,
-    which also reads and writes equal amounts, runs faster than this copy; so
-    the fastest of this library's own kernels in the run is reported beside it,
-    with each kernel's fraction of that rate."""
+def achievable_hbm(kda, kernels, nbytes=1 << 30, reps=5):
+    """Measured streaming rates beside the published 8 TB/s: this library's own
+    streaming copy kernel (kda_stream_copy: 16-byte non-temporal loads and
+    stores) and the runtime's device-to-device copy, each the best of a few
+    1 GiB copies (bytes read + written per second), with each hot-path
+    kernel's algorithmic rate as a fraction of the own copy's. The fastest of
+    the hot-path kernels in the run is named too."""
     import torch
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
-    ev[0].record()
-    for i in range(reps):
-        dst.copy_(src)
-        ev[i + 1].record()
-    torch.cuda.synchronize()
-    ms = min(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
-    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+
+    def best(fn):
+        fn()
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for i in range(reps):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        return min(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
+
+    ms_rt = best(lambda: dst.copy_(src))
+    ms_own = best(lambda: kda.stream_copy(src, dst))
+    gbs_rt = 2 * nbytes / (ms_rt * 1e-3) / 1e9
+    gbs = 2 * nbytes / (ms_own * 1e-3) / 1e9
     del src, dst
-    # the fastest streaming rate this library's own kernels reach in the same run
-    best = max(kernels, key=lambda n: kernels[n]["achieved_GBs"])
-    bgbs = kernels[best]["achieved_GBs"]
-    return {"runtime_copy_GBs": round(gbs, 1), "copy_bytes": 2 * nbytes,
-            "kernel_frac_of_copy": {n: round(x["achieved_GBs"] / gbs, 4) for n, x in kernels.items()},
-            "best_own_kernel": {"kernel": best, "GBs": round(bgbs, 1)},
-            "kernel_frac_of_best_own": {n: round(x["achieved_GBs"] / bgbs, 4)
-                                        for n, x in kernels.items()}}
+    fastest = max(kernels, key=lambda n: kernels[n]["achieved_GBs"])
+    return {"own_copy_kernel": "stream_copy_kernel", "own_copy_GBs": round(gbs, 1),
+            "own_copy_frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "runtime_copy_GBs": round(gbs_rt, 1), "copy_bytes": 2 * nbytes,
+            "kernel_frac_of_own_copy": {n: round(x["achieved_GBs"] / gbs, 4)
+                                        for n, x in kernels.items()},
+            "fastest_hot_path_kernel": {"kernel": fastest,
+                                        "GBs": round(kernels[fastest]["achieved_GBs"], 1)}}
 
 
 def copy_calibration(nbytes=1 << 30, reps=3):
-    """A plain copy of known size: its FETCH_SIZE / WRITE_SIZE counter readings
-    give the factor that converts those counters to bytes on this GPU."""
+    """The library's streaming copy (stream_copy_kernel) over a buffer of known
+    size: its FETCH_SIZE / WRITE_SIZE counter readings give the factor that
+    converts those counters to bytes on this GPU."""
     import torch
+    import kimi_delta_attention_05_amd as kda
     src = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
     dst = torch.empty_like(src)
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     ev[0].record()
     for i in range(reps):
-        dst.copy_(src)
+        kda.stream_copy(src, dst)
         ev[i + 1].record()
     torch.cuda.synchronize()
     ms = min(ev[i].elapsed_time(ev[i + 1]) for i in range(reps))
-    print(json.dumps({"copy_bytes_read": nbytes, "copy_bytes_written": nbytes, "reps": reps,
-                      "best_ms": round(ms, 4), "GBs_read_plus_write": round(2 * nbytes / ms / 1e6, 1)}),
-          flush=True)
+    print(json.dumps({"kernel": "stream_copy_kernel", "copy_bytes_read": nbytes,
+                      "copy_bytes_written": nbytes, "reps": reps, "best_ms": round(ms, 4),
+                      "GBs_read_plus_write": round(2 * nbytes / ms / 1e6, 1)}), flush=True)
 
 
-def cpu_baseline(p, dd):
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(p, dd, heads_1t=8):
     """The fp64 oracle as it stands, on the host cores: the same prefill
-    (T=8192, H=96) once and two decode steps of the same batch."""
+    (T=8192, H=96) once and two decode steps of the same batch, on all the
+    threads OpenMP gives it; and on one thread, over the first `heads_1t` of the
+    96 heads of the prefill (a bounded sample, scaled to the whole prefill: the
+    heads are independent chains of equal length)."""
     import numpy as np
     import torch
     import oracle
@@ -549,11 +654,23 @@ def cpu_baseline(p, dd):
         _, state = oracle.kda_recurrent(*st, dA, ddt, cud, scale=dd.scale, h0=state)
     t_decode = (time.perf_counter() - t0) / len(dsteps)
     tokens = p.T + B
+    # one thread, a head sample of the prefill
+    hs = slice(0, heads_1t)
+    sub = [np.ascontiguousarray(a[:, hs]) for a in args[:5]] + \
+          [np.ascontiguousarray(args[5][hs]), np.ascontiguousarray(args[6][hs])]
+    log("cpu baseline: oracle prefill on 1 thread, %d of %d heads ..." % (heads_1t, p.H))
+    t0 = time.perf_counter()
+    oracle.kda_recurrent(*sub, cu, scale=p.scale, h0=np.ascontiguousarray(h0[:, hs]), nthreads=1)
+    t_1 = (time.perf_counter() - t0) * p.H / heads_1t
     return {"value": round(tokens / (t_prefill + t_decode), 1), "unit": "tokens/s",
-            "cores": threads, "kind": "oracle",
+            "cores": threads, "kind": "oracle", "cpu_model": cpu_model(),
             "sample": "one full prefill T=8192 H=96 (%.2f s) + mean of 2 decode steps "
                       "B=256 H=32 (%.2f s/step), fp64, OpenMP over (sequence, head) chains"
-                      % (t_prefill, t_decode)}
+                      % (t_prefill, t_decode),
+            "one_thread": {"prefill_tokens_per_s": round(p.T / t_1, 1),
+                           "sample": "prefill T=8192 over %d of %d heads on 1 thread, scaled "
+                                     "to all heads (%.2f s for the whole prefill)"
+                                     % (heads_1t, p.H, t_1)}}
 
 
 if __name__ == "__main__":

@@ -426,6 +426,42 @@ kda_status_t kda_backward_grouped(const void *q, const void *k, const void *v, c
                                   float *d_initial_state, void *workspace, size_t workspace_bytes,
                                   void *stream);
 /*
+ * kda_chunk_fwd with the output epilogue of kda_output_norm_gate applied in
+ * the o store (kimi_k3 FusedKDAChunkwise page, "Output handling": per-head norm
+ * of each output row, then the sigmoid output gate): o receives
+ *   y = o_kda / sqrt(mean(o_kda^2) + norm_eps) * norm_weight * sigmoid(z)
+ * computed in fp32 from the unrounded fp32 outputs (for bf16 o they are staged
+ * in the workspace, sized by kda_chunk_fwd_gated_workspace_size) and rounded
+ * once to o_dtype. z: [T, H, V] gate
+ * logits in in_dtype (must not overlap o; may be NULL only when
+ * total_tokens = 0); norm_weight: [V] fp32; norm_eps finite and > 0. Other
+ * arguments, layouts and errors as kda_chunk_fwd, with the workspace sized by
+ * kda_chunk_fwd_gated_workspace_size. The epilogue runs as a pass over the
+ * outputs, enqueued right after the inter-chunk kernel: the rows of one
+ * output come from two workgroups of that kernel (one per half of the state),
+ * so a whole row exists only once both have stored it, and o is then still in
+ * the memory-side cache.
+ */
+/* Workspace bytes kda_chunk_fwd_gated needs: kda_chunk_fwd_workspace_size, plus
+ * T * H * V * 4 bytes (after rounding that up to 256) when o_dtype is bf16,
+ * where the outputs are staged in fp32 for the epilogue so that the result is
+ * rounded once. 0 for invalid arguments. */
+size_t kda_chunk_fwd_gated_workspace_size(int64_t total_tokens, int32_t num_seqs,
+                                          int32_t H, int32_t K, int32_t V,
+                                          int32_t chunk_size, kda_dtype_t in_dtype,
+                                          kda_dtype_t o_dtype);
+kda_status_t kda_chunk_fwd_gated(const void *q, const void *k, const void *v,
+                                 const float *g, const float *beta_raw,
+                                 const float *A_log, const float *dt_bias,
+                                 float scale, float lower_bound,
+                                 const int64_t *cu_seqlens, int32_t num_seqs,
+                                 int64_t total_tokens, int32_t H, int32_t K, int32_t V,
+                                 int32_t chunk_size, kda_dtype_t in_dtype,
+                                 const float *initial_state, float *final_state,
+                                 void *o, kda_dtype_t o_dtype,
+                                 void *workspace, size_t workspace_bytes, void *stream,
+                                 const void *z, const float *norm_weight, float norm_eps);
+/*
  * kda_chunk_fwd without a caller workspace, for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc). Arguments and results as kda_chunk_fwd; the
@@ -450,6 +486,15 @@ kda_status_t kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
                                    int32_t chunk_size, kda_dtype_t in_dtype,
                                    const float *initial_state, float *final_state,
                                    void *o, kda_dtype_t o_dtype, void *stream);
+/*
+ * Streaming device copy of `bytes` bytes from src to dst on `stream`: the
+ * library's own read-once / write-once kernel (16-byte non-temporal loads and
+ * stores), used as the measured reference for the HBM rate the other kernels
+ * are compared with. bytes must be a multiple of 16, src and dst 16-byte
+ * aligned and not overlapping (else KDA_ERR_INVALID_ARG); bytes = 0 enqueues
+ * nothing.
+ */
+kda_status_t kda_stream_copy(const void *src, void *dst, size_t bytes, void *stream);
 /*
  * Opt-in check of packed offsets (FlashInfer kda_backward page: offsets are
  * validated by one eager synchronisation, the launch path then trusts them).

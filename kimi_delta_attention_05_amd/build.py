@@ -10,7 +10,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkda.so")
 SOURCES = ["kda_api.cpp", "kda_decode.hip", "kda_prefill.hip", "kda_epilogue.hip",
-           "kda_shortconv.hip", "kda_backward.hip", "kda_general.hip", "kda_noalloc.hip"]
+           "kda_shortconv.hip", "kda_backward.hip", "kda_general.hip", "kda_noalloc.hip",
+           "kda_copy.hip"]
 ARCH = os.environ.get("KDA_OFFLOAD_ARCH", "gfx950")
 
 

@@ -211,7 +211,8 @@ kda_status_t decode_step_impl(const void *q, const void *k, const void *v,
             // as a second pass (padding requests' zero rows stay zero)
             kda::NormGateArgs na;
             na.o = o; na.z = z; na.w = norm_weight; na.eps = norm_eps; na.rows = (int64_t)B * H;
-            na.D = V; na.bf16 = o_dtype == KDA_BF16; na.z_bf16 = in_dtype == KDA_BF16; na.y = o;
+            na.D = V; na.bf16 = o_dtype == KDA_BF16; na.z_bf16 = in_dtype == KDA_BF16;
+            na.y_bf16 = na.bf16; na.y = o;
             na.stream = (hipStream_t)stream;
             e = kda::launch_norm_gate(na);
         }
@@ -274,6 +275,18 @@ size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t num_seqs, int3
     return pad_layout(total_tokens, num_seqs, H, in_dtype, base).end;
 }
 
+size_t kda_chunk_fwd_gated_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H,
+                                          int32_t K, int32_t V, int32_t chunk_size,
+                                          kda_dtype_t in_dtype, kda_dtype_t o_dtype) {
+    const size_t base = kda_chunk_fwd_workspace_size(total_tokens, num_seqs, H, K, V, chunk_size,
+                                                     in_dtype);
+    if (base == 0) return 0;
+    if (!valid_dtype(o_dtype)) { fail(KDA_ERR_UNSUPPORTED, "unknown output dtype"); return 0; }
+    if (o_dtype != KDA_BF16) return base;
+    // bf16 results: the outputs are staged in fp32 for the epilogue
+    return ((base + 255) & ~(size_t)255) + (size_t)total_tokens * H * V * 4;
+}
+
 }  // extern "C"
 
 namespace {
@@ -289,7 +302,9 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
                               const float *initial_state, float *final_state,
                               void *o, kda_dtype_t o_dtype,
                               void *workspace, size_t workspace_bytes,
-                              void *stream, int32_t H_qk, bool fixed_scratch = false) {
+                              void *stream, int32_t H_qk, bool fixed_scratch = false,
+                              const void *z = nullptr, const float *norm_weight = nullptr,
+                              float norm_eps = 0.f) {
     if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 1");
     if (total_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens must be >= 0");
     kda_status_t st = check_common(H, K, V, scale, lower_bound, in_dtype, o_dtype, true);
@@ -306,8 +321,10 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
         return fail(KDA_ERR_INVALID_ARG, "num_seqs * H too large");
     if (kda::num_slots(total_tokens, num_seqs, chunk_size) > ((int64_t)1 << 31) - 1)
         return fail(KDA_ERR_INVALID_ARG, "too many chunks for one launch");
-    const size_t need = kda_chunk_fwd_workspace_size(total_tokens, num_seqs, H, K, V, chunk_size,
-                                                     in_dtype);
+    const size_t need = z ? kda_chunk_fwd_gated_workspace_size(total_tokens, num_seqs, H, K, V,
+                                                               chunk_size, in_dtype, o_dtype)
+                          : kda_chunk_fwd_workspace_size(total_tokens, num_seqs, H, K, V,
+                                                         chunk_size, in_dtype);
     if (fixed_scratch) {
         if (need > kda::kNoAllocScratchBytes)
             return fail(KDA_ERR_WORKSPACE,
@@ -328,6 +345,18 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
     if (st != KDA_OK) return st;
     if (((uintptr_t)beta_raw & 3) != 0 || ((uintptr_t)A_log & 3) != 0)
         return fail(KDA_ERR_INVALID_ARG, "beta_raw and A_log must be 4-byte aligned");
+    if (z) {
+        if (stages != 3) return fail(KDA_ERR_INVALID_ARG, "the output epilogue runs with both stages");
+        if (!norm_weight) return fail(KDA_ERR_INVALID_ARG, "norm_weight must not be NULL");
+        if (!(norm_eps > 0.0f) || !std::isfinite(norm_eps))
+            return fail(KDA_ERR_INVALID_ARG, "norm_eps must be finite and > 0");
+        st = check_aligned16({{z, "z"}, {norm_weight, "norm_weight"}});
+        if (st != KDA_OK) return st;
+        const uintptr_t esz = in_dtype == KDA_BF16 ? 2 : 4, osz = o_dtype == KDA_BF16 ? 2 : 4;
+        if (overlaps(byte_range(z, (uintptr_t)total_tokens * H * V * esz),
+                     byte_range(o, (uintptr_t)total_tokens * H * V * osz)))
+            return fail(KDA_ERR_INVALID_ARG, "z and o must not overlap");
+    }
     if (fixed_scratch) {
         // every argument check has passed: the current device's copy of the
         // library's fixed scratch array replaces the caller workspace
@@ -346,8 +375,32 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
     a.ws = (unsigned char *)workspace;
     a.stream = (hipStream_t)stream;
     a.stages = stages;
+    // The output epilogue, when asked for: a pass over the V-wide output rows,
+    // right after the inter-chunk kernel on the same stream (its outputs are
+    // still in the memory-side cache then). It reads the outputs unrounded:
+    // fp32 results in place, bf16 results from fp32 outputs staged in the
+    // workspace after the part kda_chunk_fwd uses, so that y is rounded once.
+    const bool stage_o = z && o_dtype == KDA_BF16;
+    unsigned char *const o32 =
+        stage_o ? (unsigned char *)workspace +
+                      ((kda_chunk_fwd_workspace_size(total_tokens, num_seqs, H, K, V, chunk_size,
+                                                     in_dtype) + 255) & ~(size_t)255)
+                : nullptr;
+    auto epilogue = [&]() -> hipError_t {
+        if (!z || total_tokens == 0) return hipSuccess;
+        kda::NormGateArgs ng;
+        ng.o = stage_o ? (const void *)o32 : o; ng.z = z; ng.w = norm_weight; ng.eps = norm_eps;
+        ng.rows = total_tokens * H; ng.D = V;
+        ng.bf16 = !stage_o && o_dtype == KDA_BF16; ng.z_bf16 = in_dtype == KDA_BF16;
+        ng.y_bf16 = o_dtype == KDA_BF16; ng.y = o;
+        ng.stream = (hipStream_t)stream;
+        return kda::launch_norm_gate(ng);
+    };
+    if (stage_o) a.out_bf16 = false;
     if (K == 128 && V == 128) {
+        if (stage_o) a.o = o32;
         hipError_t e = kda::launch_prefill(a);
+        if (e == hipSuccess) e = epilogue();
         if (e != hipSuccess) return hip_fail(e, name);
         return ok();
     }
@@ -385,8 +438,10 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
     e = kda::launch_prefill(a);
     if (e != hipSuccess) return hip_fail(e, name);
     if (stages & 2) {
-        pad(ws + P.o, D, 1, o, V, 1, TH, osz);
+        if (stage_o) pad(ws + P.o, D, 1, o32, V, 1, TH, 4);
+        else pad(ws + P.o, D, 1, o, V, 1, TH, osz);
         if (final_state) pad(ws + P.state, D, D, final_state, K, V, NH * V, 4);
+        if (e == hipSuccess) e = epilogue();
         if (e != hipSuccess) return hip_fail(e, name);
     }
     return ok();
@@ -422,6 +477,13 @@ kda_status_t kda_chunk_fwd_inter(KDA_CHUNK_PARAMS) {
 
 kda_status_t kda_chunk_fwd_grouped(KDA_CHUNK_PARAMS, int32_t H_qk) {
     return chunk_fwd_stages(3, "kda_chunk_fwd_grouped", KDA_CHUNK_ARGS, H_qk);
+}
+
+kda_status_t kda_chunk_fwd_gated(KDA_CHUNK_PARAMS, const void *z, const float *norm_weight,
+                                 float norm_eps) {
+    if (!z && total_tokens > 0) return fail(KDA_ERR_INVALID_ARG, "z must not be NULL");
+    return chunk_fwd_stages(3, "kda_chunk_fwd_gated", KDA_CHUNK_ARGS, H, false, z, norm_weight,
+                            norm_eps);
 }
 
 kda_status_t kda_chunk_fwd_noalloc(const void *q, const void *k, const void *v,
@@ -523,7 +585,7 @@ kda_status_t kda_output_norm_gate(const void *o, const void *z, const float *wei
     if (st != KDA_OK) return st;
     kda::NormGateArgs a;
     a.o = o; a.z = z; a.w = weight; a.eps = eps; a.rows = rows; a.D = D; a.bf16 = io_dtype == KDA_BF16;
-    a.z_bf16 = a.bf16;
+    a.z_bf16 = a.bf16; a.y_bf16 = a.bf16;
     a.y = y; a.stream = (hipStream_t)stream;
     hipError_t e = kda::launch_norm_gate(a);
     if (e != hipSuccess) return hip_fail(e, "kda_output_norm_gate launch");
@@ -778,6 +840,19 @@ kda_status_t kda_recurrent_fwd(const void *q, const void *k, const void *v,
     a.stream = (hipStream_t)stream;
     const hipError_t e = kda::launch_recurrent_fwd(a);
     if (e != hipSuccess) return hip_fail(e, "kda_recurrent_fwd launch");
+    return ok();
+}
+
+kda_status_t kda_stream_copy(const void *src, void *dst, size_t bytes, void *stream) {
+    if (bytes == 0) return ok();
+    if (!src || !dst) return fail(KDA_ERR_INVALID_ARG, "src and dst must not be NULL");
+    if (bytes % 16 != 0) return fail(KDA_ERR_INVALID_ARG, "bytes must be a multiple of 16");
+    kda_status_t st = check_aligned16({{src, "src"}, {dst, "dst"}});
+    if (st != KDA_OK) return st;
+    if (overlaps(byte_range(src, bytes), byte_range(dst, bytes)))
+        return fail(KDA_ERR_INVALID_ARG, "src and dst overlap");
+    const hipError_t e = kda::launch_stream_copy(src, dst, bytes, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_fail(e, "kda_stream_copy");
     return ok();
 }
 

@@ -6,17 +6,18 @@
 // One 16-lane DPP row per output row, 8 features per lane (16-byte loads and
 // stores of bf16, 32 bytes of fp32), 16 rows per 256-thread workgroup: every
 // instruction moves whole consecutive rows. HBM-bound: o, z read once, y
-// written once.
+// written once. The rows, the gate logits and the result each have their own
+// dtype (bf16 or fp32).
 #include "kda_common.h"
 #include "kda_internal.h"
 
 namespace kda {
 
 // o is not __restrict__: y may alias it (the epilogue applied in place).
-template <typename T>
-__global__ __launch_bounds__(256) void norm_gate_kernel(const T *o, const T *__restrict__ z,
+template <typename To, typename Tz, typename Ty>
+__global__ __launch_bounds__(256) void norm_gate_kernel(const To *o, const Tz *__restrict__ z,
                                                         const float *__restrict__ w, float eps,
-                                                        int64_t rows, T *y)
+                                                        int64_t rows, Ty *y)
 {
     const int j = threadIdx.x & 15;                    // features 8j .. 8j + 7
     const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
@@ -34,17 +35,17 @@ __global__ __launch_bounds__(256) void norm_gate_kernel(const T *o, const T *__r
     float out[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) out[e] = x[e] * r * wv[e] * sigmoid_f(g[e]);
-    if (valid) store8_nt<T>(y + base, out);
+    if (valid) store8_nt<Ty>(y + base, out);
 }
 
 // Rows of any other width D <= 256 (head sizes other than 128): one wave per
 // row, lane l holding features l, l + 64, l + 128, l + 192 below D, the sum of
 // squares reduced over the wave.
-template <typename T, typename Z>
-__global__ __launch_bounds__(256) void norm_gate_any_kernel(const T *o,
-                                                            const Z *__restrict__ z,
+template <typename To, typename Tz, typename Ty>
+__global__ __launch_bounds__(256) void norm_gate_any_kernel(const To *o,
+                                                            const Tz *__restrict__ z,
                                                             const float *__restrict__ w, float eps,
-                                                            int64_t rows, int D, T *y)
+                                                            int64_t rows, int D, Ty *y)
 {
     const int lane = threadIdx.x & 63;
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -61,36 +62,37 @@ __global__ __launch_bounds__(256) void norm_gate_any_kernel(const T *o,
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int c = lane + 64 * e;
-        if (c < D) y[base + c] = from_f32<T>(x[e] * r * w[c] * sigmoid_f(to_f32(z[base + c])));
+        if (c < D) y[base + c] = from_f32<Ty>(x[e] * r * w[c] * sigmoid_f(to_f32(z[base + c])));
     }
+}
+
+template <typename To, typename Tz, typename Ty>
+static hipError_t launch_norm_gate_t(const NormGateArgs &a) {
+    if (a.D != kHeadDim) {
+        const unsigned blocks = (unsigned)((a.rows + 3) / 4);
+        norm_gate_any_kernel<To, Tz, Ty><<<blocks, 256, 0, a.stream>>>(
+            (const To *)a.o, (const Tz *)a.z, a.w, a.eps, a.rows, a.D, (Ty *)a.y);
+    } else {
+        const int64_t blocks = (a.rows + 15) / 16;
+        norm_gate_kernel<To, Tz, Ty><<<(unsigned)blocks, 256, 0, a.stream>>>(
+            (const To *)a.o, (const Tz *)a.z, a.w, a.eps, a.rows, (Ty *)a.y);
+    }
+    return hipGetLastError();
+}
+
+template <typename To, typename Tz>
+static hipError_t launch_norm_gate_y(const NormGateArgs &a) {
+    return a.y_bf16 ? launch_norm_gate_t<To, Tz, __bf16>(a) : launch_norm_gate_t<To, Tz, float>(a);
+}
+
+template <typename To>
+static hipError_t launch_norm_gate_z(const NormGateArgs &a) {
+    return a.z_bf16 ? launch_norm_gate_y<To, __bf16>(a) : launch_norm_gate_y<To, float>(a);
 }
 
 hipError_t launch_norm_gate(const NormGateArgs &a) {
     if (a.rows <= 0) return hipSuccess;
-    if (a.D != kHeadDim) {
-        const unsigned blocks = (unsigned)((a.rows + 3) / 4);
-        if (a.bf16 && a.z_bf16)
-            norm_gate_any_kernel<__bf16, __bf16><<<blocks, 256, 0, a.stream>>>(
-                (const __bf16 *)a.o, (const __bf16 *)a.z, a.w, a.eps, a.rows, a.D, (__bf16 *)a.y);
-        else if (a.bf16)
-            norm_gate_any_kernel<__bf16, float><<<blocks, 256, 0, a.stream>>>(
-                (const __bf16 *)a.o, (const float *)a.z, a.w, a.eps, a.rows, a.D, (__bf16 *)a.y);
-        else if (a.z_bf16)
-            norm_gate_any_kernel<float, __bf16><<<blocks, 256, 0, a.stream>>>(
-                (const float *)a.o, (const __bf16 *)a.z, a.w, a.eps, a.rows, a.D, (float *)a.y);
-        else
-            norm_gate_any_kernel<float, float><<<blocks, 256, 0, a.stream>>>(
-                (const float *)a.o, (const float *)a.z, a.w, a.eps, a.rows, a.D, (float *)a.y);
-        return hipGetLastError();
-    }
-    const int64_t blocks = (a.rows + 15) / 16;
-    if (a.bf16)
-        norm_gate_kernel<__bf16><<<(unsigned)blocks, 256, 0, a.stream>>>(
-            (const __bf16 *)a.o, (const __bf16 *)a.z, a.w, a.eps, a.rows, (__bf16 *)a.y);
-    else
-        norm_gate_kernel<float><<<(unsigned)blocks, 256, 0, a.stream>>>(
-            (const float *)a.o, (const float *)a.z, a.w, a.eps, a.rows, (float *)a.y);
-    return hipGetLastError();
+    return a.bf16 ? launch_norm_gate_z<__bf16>(a) : launch_norm_gate_z<float>(a);
 }
 
 }  // namespace kda

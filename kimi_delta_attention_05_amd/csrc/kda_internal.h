@@ -37,8 +37,9 @@ struct NormGateArgs {
     float eps;
     int64_t rows;
     int D = 128;                        // features per row (128, or any width up to 256)
-    bool bf16;
-    bool z_bf16 = false;                // dtype of z for widths other than 128 (else as o)
+    bool bf16;                          // dtype of o
+    bool z_bf16 = false;                // dtype of z
+    bool y_bf16 = false;                // dtype of y
     void *y;
     hipStream_t stream;
 };
@@ -199,6 +200,8 @@ hipError_t launch_recurrent_fwd(const GeneralArgs &a);
 // once per device).
 constexpr size_t kNoAllocScratchBytes = (size_t)128 << 20;
 hipError_t noalloc_scratch(void **ptr);
+
+hipError_t launch_stream_copy(const void *src, void *dst, size_t bytes, hipStream_t stream);
 
 hipError_t launch_decode(const DecodeArgs &a);
 hipError_t launch_norm_gate(const NormGateArgs &a);

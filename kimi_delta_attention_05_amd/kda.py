@@ -29,7 +29,8 @@ EXPORTS = ("kda_version", "kda_status_string", "kda_last_error",
            "kda_short_conv_slots",
            "kda_backward_workspace_size", "kda_backward", "kda_chunk_fwd_grouped",
            "kda_decode_step_grouped", "kda_backward_grouped", "kda_recurrent_fwd",
-           "kda_check_cu_seqlens", "kda_chunk_fwd_noalloc")
+           "kda_check_cu_seqlens", "kda_chunk_fwd_noalloc", "kda_stream_copy",
+           "kda_chunk_fwd_gated", "kda_chunk_fwd_gated_workspace_size")
 
 NORM_EPS = 1e-5   # default epsilon of the output norm (the pages give none)
 
@@ -57,6 +58,11 @@ for _name in ("kda_chunk_fwd", "kda_chunk_fwd_intra", "kda_chunk_fwd_inter"):
 _lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
 _lib.kda_chunk_fwd_noalloc.argtypes = _lib.kda_chunk_fwd.argtypes[:21] + [_P]
 NOALLOC_SCRATCH_BYTES = 128 << 20    # the fixed scratch of kda_chunk_fwd_noalloc
+_lib.kda_chunk_fwd_gated_workspace_size.restype = _sz
+_lib.kda_chunk_fwd_gated_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32,
+                                                    ctypes.c_int, ctypes.c_int]
+_lib.kda_chunk_fwd_gated.restype = ctypes.c_int
+_lib.kda_chunk_fwd_gated.argtypes = _lib.kda_chunk_fwd.argtypes + [_P, _P, _f32]
 _lib.kda_chunk_fwd_grouped.restype = ctypes.c_int
 _lib.kda_chunk_fwd_grouped.argtypes = _lib.kda_chunk_fwd.argtypes + [_i32]
 _STAGE_FN = {None: _lib.kda_chunk_fwd, "intra": _lib.kda_chunk_fwd_intra,
@@ -97,6 +103,8 @@ _lib.kda_recurrent_fwd.restype = ctypes.c_int
 _lib.kda_recurrent_fwd.argtypes = [_P, _P, _P, _P, _P, _P, _P, _f32, _f32, _P, _i32, _i64,
                                    _i32, _i32, _i32, _i32, ctypes.c_int, _P, _P, _P,
                                    ctypes.c_int, _P]
+_lib.kda_stream_copy.restype = ctypes.c_int
+_lib.kda_stream_copy.argtypes = [_P, _P, _sz, _P]
 _lib.kda_check_cu_seqlens.restype = ctypes.c_int
 _lib.kda_check_cu_seqlens.argtypes = [_P, _i32, _i64, _P]
 
@@ -177,7 +185,9 @@ def chunk_fwd(q, k, v, g, beta_raw, A_log, dt_bias, cu_seqlens, *, scale: float 
               o_dtype=None, out: Optional[torch.Tensor] = None,
               final_state: Optional[torch.Tensor] = None,
               workspace: Optional[Workspace] = None,
-              stage: Optional[str] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+              stage: Optional[str] = None,
+              gate: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
+              norm_eps: float = NORM_EPS) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise KDA prefill over packed sequences (libkda kda_chunk_fwd).
 
     q, k: [T, H_qk, 128] and v: [T, H, 128], bf16 or fp32 (same dtype); H_qk < H
@@ -187,6 +197,9 @@ def chunk_fwd(q, k, v, g, beta_raw, A_log, dt_bias, cu_seqlens, *, scale: float 
     Returns (o [T, H, 128] in o_dtype (default: q's dtype), final_state or None).
     stage: None runs both kernels; "intra" / "inter" run one stage (kda_chunk_fwd_intra /
     kda_chunk_fwd_inter), which must share the same workspace and arguments.
+    With `gate` (logits [T, H, V] in q's dtype) and `norm_weight` ([V] fp32) the output
+    epilogue of output_norm_gate is applied in the o store (kda_chunk_fwd_gated) and the
+    returned o is its result.
     """
     T, Hqk, K = q.shape
     H, V = v.shape[1], v.shape[2]          # value heads (grouped value heads: a multiple of Hqk)
@@ -217,13 +230,29 @@ def chunk_fwd(q, k, v, g, beta_raw, A_log, dt_bias, cu_seqlens, *, scale: float 
         ht_ptr = _dev(final_state, "final_state", torch.float32, (N, H, V, K))
     else:
         final_state = None
-    need = workspace_size(T, N, H, chunk_size, q.dtype, K, V)
+    if gate is None:
+        need = workspace_size(T, N, H, chunk_size, q.dtype, K, V)
+    else:
+        need = int(_lib.kda_chunk_fwd_gated_workspace_size(T, N, H, K, V, int(chunk_size), in_dt,
+                                                           _dt(out)))
+        if need == 0:
+            raise ValueError("kda_chunk_fwd_gated_workspace_size: " +
+                             _lib.kda_last_error().decode())
     ws = (workspace or Workspace(device)).get(need)
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), g.data_ptr(), beta_raw.data_ptr(),
             A_log.data_ptr(), dt_bias.data_ptr(), float(scale), float(lower_bound),
             cu_seqlens.data_ptr(), N, T, H, K, V, int(chunk_size), in_dt, h0_ptr, ht_ptr, o_ptr,
             _dt(out), ws.data_ptr(), ws.numel(), _stream_ptr(device))
-    if Hqk != H:
+    if gate is not None:
+        if stage is not None or Hqk != H:
+            raise ValueError("the gated prefill runs both stages without grouped heads")
+        _dev(gate, "gate", q.dtype, (T, H, V))
+        if norm_weight is None:
+            raise ValueError("norm_weight is required with gate")
+        _dev(norm_weight, "norm_weight", torch.float32, (V,))
+        fn, args = _lib.kda_chunk_fwd_gated, args + (gate.data_ptr(), norm_weight.data_ptr(),
+                                                     float(norm_eps))
+    elif Hqk != H:
         if stage is not None:
             raise ValueError("grouped value heads run both stages (stage must be None)")
         fn, args = _lib.kda_chunk_fwd_grouped, args + (Hqk,)
@@ -553,3 +582,17 @@ def check_cu_seqlens(cu_seqlens: torch.Tensor, total_tokens: int) -> None:
     st = _lib.kda_check_cu_seqlens(cu_seqlens.data_ptr(), N, int(total_tokens),
                                    _stream_ptr(cu_seqlens.device))
     _check(st, "kda_check_cu_seqlens")
+
+
+def stream_copy(src: torch.Tensor, dst: torch.Tensor) -> torch.Tensor:
+    """Copy src into dst with the library's streaming kernel (kda_stream_copy):
+    the measured HBM reference of the benchmark. Both contiguous, same size in
+    bytes (a multiple of 16), on the GPU."""
+    _dev(src, "src")
+    _dev(dst, "dst")
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("src and dst must have the same size in bytes")
+    _check(_lib.kda_stream_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream_ptr(src.device)),
+           "kda_stream_copy")
+    return dst

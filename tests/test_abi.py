@@ -390,3 +390,41 @@ def test_noalloc_scratch_limit_covers_stated_shapes(kda):
     """The header's examples: T = 8192 at H = 12 fits the fixed scratch, H = 96 does not."""
     assert kda.workspace_size(8192, 1, 12, 64) <= kda.NOALLOC_SCRATCH_BYTES
     assert kda.workspace_size(8192, 1, 96, 64) > kda.NOALLOC_SCRATCH_BYTES
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(src=None), 1), (dict(dst=None), 1), (dict(n=17), 1), (dict(src=FAKE + 4), 1),
+    (dict(dst=FAKE + 8 + (1 << 20)), 1), (dict(dst=FAKE + 512), 1),   # misaligned; overlapping
+])
+def test_stream_copy_rejects(kda, kw, status):
+    a = dict(src=FAKE, dst=FAKE + (1 << 20), n=1024)
+    a.update(kw)
+    assert kda.lib.kda_stream_copy(a["src"], a["dst"], a["n"], None) == status
+    assert kda.lib.kda_last_error()
+
+
+def test_stream_copy_zero_bytes_enqueues_nothing(kda):
+    assert kda.lib.kda_stream_copy(None, None, 0, None) == 0
+
+
+def test_chunk_fwd_gated_rejects_before_any_hip_call(kda):
+    base = [FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 0.088, -5.0, FAKE, 1, 17, 1, 128, 128, 16,
+            kda.KDA_F32, None, None, FAKE, kda.KDA_F32, 0x100000, 1 << 40, None]
+    f = kda.lib.kda_chunk_fwd_gated
+    assert f(*base, None, FAKE, 1e-5) == 1                  # no z (T > 0)
+    assert f(*base, FAKE + (1 << 20), None, 1e-5) == 1      # no norm weight
+    assert f(*base, FAKE + (1 << 20), FAKE, 0.0) == 1       # eps must be > 0
+    assert f(*base, FAKE + (1 << 20) + 4, FAKE, 1e-5) == 1  # z misaligned
+    assert f(*base, FAKE, FAKE, 1e-5) == 1                  # z overlaps o
+
+
+def test_gated_workspace_size(kda):
+    f = kda.lib.kda_chunk_fwd_gated_workspace_size
+    base = kda.lib.kda_chunk_fwd_workspace_size(8192, 1, 96, 128, 128, 64, kda.KDA_BF16)
+    assert f(8192, 1, 96, 128, 128, 64, kda.KDA_BF16, kda.KDA_F32) == base
+    up = (base + 255) // 256 * 256
+    assert f(8192, 1, 96, 128, 128, 64, kda.KDA_BF16, kda.KDA_BF16) == up + 8192 * 96 * 128 * 4
+    assert f(100, 2, 3, 48, 80, 32, kda.KDA_F32, kda.KDA_BF16) > \
+        kda.lib.kda_chunk_fwd_workspace_size(100, 2, 3, 48, 80, 32, kda.KDA_F32)
+    assert f(8192, 1, 96, 128, 128, 64, kda.KDA_BF16, 7) == 0
+    assert f(8192, 1, 96, 129, 128, 64, kda.KDA_BF16, kda.KDA_BF16) == 0
