@@ -503,7 +503,7 @@ def general_timing(kda, dev, T=8192, H=96, reps=3):
     at K = V = 64, and at K = V = 128 for comparison with the chunkwise path.
     Arithmetic: 7 flops per state element and token (decay, the two dot
     products, the update) against the fp32 vector peak. At K = V = 64 the
-    chunkwise prefill over zero-padded copies is timed too."""
+    chunkwise prefill (kernels sized for 64) is timed too."""
     import torch
     import kda_inputs
     out = {}
@@ -535,7 +535,7 @@ def general_timing(kda, dev, T=8192, H=96, reps=3):
                                            "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                                            "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4)}}
         if Kd < D:
-            # the same problem on the chunkwise prefill (zero-padded copies to 128)
+            # the same problem on the chunkwise prefill (kernels sized for K = V = 64)
             ws = kda.Workspace(dev)
 
             def run_c():

@@ -102,7 +102,16 @@ kda_status_t hip_fail(hipError_t e, const char *where) {
     return fail(KDA_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
 }
 
-// Head sizes below 128 run on the chunkwise kernels over copies of the inputs
+// The head size the chunkwise kernels run at directly: 128, and 64 for K = V =
+// 64 with 64-row chunks of bf16 inputs (kernels sized for it); 0 when the
+// inputs are zero-padded to 128 instead.
+int native_head_size(int32_t K, int32_t V, int32_t chunk_size, kda_dtype_t in_dtype) {
+    if (K == 128 && V == 128) return 128;
+    if (K == 64 && V == 64 && chunk_size == 64 && in_dtype == KDA_BF16) return 64;
+    return 0;
+}
+
+// Other head sizes below 128 run on the chunkwise kernels over copies of the inputs
 // padded with zeros to 128 key channels and 128 value rows, kept in the
 // workspace after the per-chunk records: padded key channels have k = q = 0
 // and padded value rows v = 0 and a zero initial state, so they stay exactly
@@ -267,10 +276,12 @@ size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t num_seqs, int3
         return 0;
     }
     if (!valid_dtype(in_dtype)) { fail(KDA_ERR_UNSUPPORTED, "unknown input dtype"); return 0; }
-    const size_t rec = kda::record_bytes(chunk_size, in_dtype == KDA_F32);
     const int64_t slots = kda::num_slots(total_tokens, num_seqs, chunk_size);
-    const size_t base = (size_t)slots * (size_t)H * rec + 256;
     g_last_error.clear();
+    if (native_head_size(K, V, chunk_size, in_dtype) == 64)     // records sized for 64
+        return (size_t)slots * (size_t)H * kda::record_bytes(64, false, 64) + 256;
+    const size_t rec = kda::record_bytes(chunk_size, in_dtype == KDA_F32);
+    const size_t base = (size_t)slots * (size_t)H * rec + 256;
     if (K == 128 && V == 128) return base;
     return pad_layout(total_tokens, num_seqs, H, in_dtype, base).end;
 }
@@ -397,7 +408,9 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
         return kda::launch_norm_gate(ng);
     };
     if (stage_o) a.out_bf16 = false;
-    if (K == 128 && V == 128) {
+    const int native = native_head_size(K, V, chunk_size, in_dtype);
+    if (native) {
+        a.D = native;
         if (stage_o) a.o = o32;
         hipError_t e = kda::launch_prefill(a);
         if (e == hipSuccess) e = epilogue();

@@ -61,6 +61,7 @@ struct PrefillArgs {
     unsigned char *ws;
     hipStream_t stream;
     int stages;          // bit 0: intra-chunk kernel, bit 1: inter-chunk kernel
+    int D = 128;         // head size K = V: 128, or 64 (64-row chunks of bf16 inputs only)
 };
 
 // Geometry of one chunk of C rows (C = 16, 32 or 64).
@@ -96,25 +97,30 @@ struct ChunkGeom {
 // Tst and Tub are fp16 when the inputs are bf16 (W, qg, kg, M are bounded by 1
 // in magnitude; Ub is stored scaled so that it is bounded by 2^15) and fp32
 // when the inputs are fp32.
-template <int C, bool PRECISE>
+// The head size D (K = V = D) is 128 or, for the natively sized 64-row bf16
+// kernels, 64: the arrays above then hold D / 32 k-steps over key channels
+// (KS), D / 16 key-channel tiles of kg^T (KT) and D / 16 value blocks of Ub
+// (VT) instead of 4, 8 and 8.
+template <int C, bool PRECISE, int D = 128>
 struct Record {
     using G = ChunkGeom<C>;
+    static constexpr int KS = D / 32, KT = D / 16, VT = D / 16;
     static constexpr size_t ELT = PRECISE ? 4 : 2;
     static constexpr size_t FRAG = 64 * 8 * ELT;
     static constexpr size_t W_OFF = 0;
-    static constexpr size_t QG_OFF = W_OFF + (size_t)G::NB * 4 * FRAG;
-    static constexpr size_t KG_OFF = QG_OFF + (size_t)G::NB * 4 * FRAG;
-    static constexpr size_t M_OFF = KG_OFF + (size_t)8 * G::CS * FRAG;
+    static constexpr size_t QG_OFF = W_OFF + (size_t)G::NB * KS * FRAG;
+    static constexpr size_t KG_OFF = QG_OFF + (size_t)G::NB * KS * FRAG;
+    static constexpr size_t M_OFF = KG_OFF + (size_t)KT * G::CS * FRAG;
     static constexpr size_t GC_OFF = M_OFF + (size_t)G::NB * G::CS * FRAG;
-    static constexpr size_t UBS_OFF = GC_OFF + 128 * 4;
+    static constexpr size_t UBS_OFF = GC_OFF + D * 4;
     static constexpr size_t SHARED_BYTES = UBS_OFF + 16;
     static constexpr size_t UB_OFF = SHARED_BYTES;
     static constexpr size_t UB_ELT = PRECISE ? 4 : 2;
     static constexpr size_t UB_VB_BYTES = (size_t)G::NB * 64 * 4 * UB_ELT;
-    static constexpr size_t BYTES = UB_OFF + 8 * UB_VB_BYTES;
+    static constexpr size_t BYTES = UB_OFF + VT * UB_VB_BYTES;
 };
 
-size_t record_bytes(int chunk, bool precise);
+size_t record_bytes(int chunk, bool precise, int D = 128);
 
 // Number of chunk slots: chunk j of sequence n lives in slot floor(cu[n]/C) + n + j,
 // which is unique and below floor(T/C) + N for any valid offsets.

@@ -42,7 +42,9 @@ namespace kda {
 
 constexpr int KP = kHeadDim + 4;   // LDS row pitch (floats) of [C][128] tiles
 
-size_t record_bytes(int chunk, bool precise) {
+size_t record_bytes(int chunk, bool precise, int D) {
+    if (D == 64) return (chunk == 64 && !precise) ? Record<64, false, 64>::BYTES : 0;
+    if (D != 128) return 0;
     switch (chunk) {
         case 16: return precise ? Record<16, true>::BYTES : Record<16, false>::BYTES;
         case 32: return precise ? Record<32, true>::BYTES : Record<32, false>::BYTES;
@@ -832,9 +834,9 @@ __global__ __launch_bounds__(64 * kIntraWaves) void intra_kernel(PrefillArgs p, 
 // global -> LDS by the DMA path (no register staging), one chunk ahead into a
 // second buffer when two fit.
 // =============================================================================
-template <int C, bool PRECISE>
+template <int C, bool PRECISE, int D = 128>
 struct InterCfg {
-    using R = Record<C, PRECISE>;
+    using R = Record<C, PRECISE, D>;
     static constexpr int SH_BLOCKS = (int)((R::SHARED_BYTES + 1023) / 1024);   // 1 KiB copies
     static constexpr size_t UB_LDS = (size_t)SH_BLOCKS * 1024;   // this half's Ub in LDS
     static constexpr int UB_BLOCKS = (int)(4 * R::UB_VB_BYTES / 1024);
@@ -855,21 +857,23 @@ template <> __device__ __forceinline__ void store4<__bf16>(__bf16 *p, const f32x
     *(bf16x4 *)p = bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
 }
 
-template <int C, typename Tout, bool PRECISE>
+template <int C, typename Tout, bool PRECISE, int D = 128>
 __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
 {
     using G = ChunkGeom<C>;
-    using R = Record<C, PRECISE>;
+    using R = Record<C, PRECISE, D>;
     using F = Frag<PRECISE>;
     using FT = typename F::T;
-    using CFG = InterCfg<C, PRECISE>;
+    using CFG = InterCfg<C, PRECISE, D>;
     constexpr int NB = G::NB, CS = G::CS;
+    constexpr int KS = R::KS, KT = R::KT;
+    constexpr int HALVES = D / 64;                  // workgroups (64 state rows each) per chain
     extern __shared__ __align__(16) unsigned char smem[];
 
     // workgroup -> (chain, half); both halves of a chain land on the same XCD
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-    int chain = (local >> 1) * 8 + xcd;
-    const int vg = local & 1;
+    int chain = (HALVES == 2 ? (local >> 1) : local) * 8 + xcd;
+    const int vg = HALVES == 2 ? (local & 1) : 0;
     if (chain >= nchains) return;
     const int H = p.H;
     int n = chain / H;
@@ -910,14 +914,14 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
     // of the kg^T tiles it accumulates from). On the fp16 path the
     // registers hold S / sigma for a wave-uniform power of two sigma, chosen so
     // that S / sigma converts to fp16 without overflow and U / sigma too.
-    f32x4 S[8];
+    f32x4 S[KT];
     float sigma = 1.0f;
-    const size_t sbase = ((size_t)chain * kHeadDim + vrow) * kHeadDim;
+    const size_t sbase = ((size_t)chain * D + vrow) * D;
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) S[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < KT; ++kb) S[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (p.h0) {
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) S[kb] = *(const f32x4 *)(p.h0 + sbase + tile_chan(kb, 4 * lg));
+        for (int kb = 0; kb < KT; ++kb) S[kb] = *(const f32x4 *)(p.h0 + sbase + tile_chan(kb, 4 * lg));
     }
 
     // DMA copy of chunk jc's record into LDS buffer buf, in parts spread over
@@ -954,7 +958,7 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
     // end-of-chunk wait so that no earlier wait is placed on them. Every lane
     // issues every load (lanes past the share re-touch line 0), so that each
     // wave issues the same known number of memory instructions per chunk.
-    constexpr int SHL = (int)((R::SHARED_BYTES + 127) / 128), SHL2 = (SHL + 1) / 2;
+    constexpr int SHL = (int)((R::SHARED_BYTES + 127) / 128), SHL2 = (SHL + HALVES - 1) / HALVES;
     constexpr int UBL = (int)(4 * R::UB_VB_BYTES / 128);
     constexpr int NTOUCH = (SHL2 + UBL + 255) / 256;
     uint32_t touch_off[NTOUCH];
@@ -978,9 +982,9 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
     // at the end of the chunk; lanes whose row lies past the sequence end write
     // the same 16 bytes of the workspace's spare tail instead, so that every
     // lane issues every store (the end-of-chunk wait counts them)
-    Tout *__restrict__ o = (Tout *)p.o + ((size_t)(s0 + lr) * H + h) * kHeadDim + 16 * vb + 4 * lg;
+    Tout *__restrict__ o = (Tout *)p.o + ((size_t)(s0 + lr) * H + h) * D + 16 * vb + 4 * lg;
     Tout *const o_spare = (Tout *)(p.ws + (size_t)num_slots(p.T, p.N, C) * H * R::BYTES);
-    const size_t o_tb = (size_t)16 * H * kHeadDim, o_chunk = (size_t)C * H * kHeadDim;
+    const size_t o_tb = (size_t)16 * H * D, o_chunk = (size_t)C * H * D;
 
     if (nch > 0) {
         fetch(0, 0, 0, NCP);
@@ -998,9 +1002,9 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
 
         // operands are requested one 16-row tile ahead of the products using them
         auto frag = [&](size_t off, int idx) { return F::load(B + off + ((size_t)idx * 64 + lane) * F::BYTES); };
-        FT fw[2][4], fq[2][4];
+        FT fw[2][KS], fq[2][KS];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) { fw[0][s] = frag(R::W_OFF, s); fq[0][s] = frag(R::QG_OFF, s); }
+        for (int s = 0; s < KS; ++s) { fw[0][s] = frag(R::W_OFF, s); fq[0][s] = frag(R::QG_OFF, s); }
         f32x4 ub[NB];
         float us = 1.0f;
 #pragma unroll
@@ -1026,7 +1030,7 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
         if constexpr (!PRECISE) {
             float m = 0.f;
 #pragma unroll
-            for (int kb = 0; kb < 8; ++kb)
+            for (int kb = 0; kb < KT; ++kb)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(S[kb][i]));
             const bool any_big = __builtin_amdgcn_ballot_w64(m > 16384.f) != 0;
@@ -1038,16 +1042,16 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
                 if (m > 16384.f || sigma < us || (m < 16.f && tgt < sigma)) {
                     const float r = sigma / tgt;
 #pragma unroll
-                    for (int kb = 0; kb < 8; ++kb) S[kb] *= r;
+                    for (int kb = 0; kb < KT; ++kb) S[kb] *= r;
                     sigma = tgt;
                 }
             }
         }
         // state operand: k-step s covers channels 32 s + 8 lg + e (tiles 2s, 2s+1); it is the
         // B operand of W S^T (columns v) and the A operand of S qg^T (rows v)
-        FT bS[4];
+        FT bS[KS];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < KS; ++s) {
             float x[8] = {S[2 * s][0], S[2 * s][1], S[2 * s][2], S[2 * s][3],
                           S[2 * s + 1][0], S[2 * s + 1][1], S[2 * s + 1][2], S[2 * s + 1][3]};
             bS[s] = F::make(x, 1.0f);
@@ -1061,14 +1065,14 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
         for (int tb = 0; tb < NB; ++tb) {
             if (tb + 1 < NB) {
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    fw[(tb + 1) & 1][s] = frag(R::W_OFF, (tb + 1) * 4 + s);
-                    fq[(tb + 1) & 1][s] = frag(R::QG_OFF, (tb + 1) * 4 + s);
+                for (int s = 0; s < KS; ++s) {
+                    fw[(tb + 1) & 1][s] = frag(R::W_OFF, (tb + 1) * KS + s);
+                    fq[(tb + 1) & 1][s] = frag(R::QG_OFF, (tb + 1) * KS + s);
                 }
             }
             f32x4 aw = ub[tb] * ubf, aq = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+            for (int s = 0; s < KS; ++s) {
                 aw = F::mma(fw[tb & 1][s], bS[s], aw);
                 aq = F::mma(bS[s], fq[tb & 1][s], aq);
             }
@@ -1078,7 +1082,7 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
 
         // operands of the second products: M, then kg^T two key blocks ahead
         FT fm[NB][CS], fk[3][CS];
-        f32x4 gv[8];
+        f32x4 gv[KT];
 #pragma unroll
         for (int tb = 0; tb < NB; ++tb)
 #pragma unroll
@@ -1090,7 +1094,7 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
 #pragma unroll
             for (int s = 0; s < CS; ++s) fk[kb][s] = frag(R::KG_OFF, kb * CS + s);
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) gv[kb] = *(const f32x4 *)(B + R::GC_OFF + 4 * tile_chan(kb, 4 * lg));
+        for (int kb = 0; kb < KT; ++kb) gv[kb] = *(const f32x4 *)(B + R::GC_OFF + 4 * tile_chan(kb, 4 * lg));
 
         // U / sigma must fit fp16: otherwise raise sigma (rare)
         if constexpr (!PRECISE) {
@@ -1105,7 +1109,7 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
 #pragma unroll
                 for (int tb = 0; tb < NB; ++tb) { U[tb] *= r; O[tb] *= r; }
 #pragma unroll
-                for (int kb = 0; kb < 8; ++kb) S[kb] *= r;
+                for (int kb = 0; kb < KT; ++kb) S[kb] *= r;
                 sigma *= f;
             }
         }
@@ -1132,8 +1136,8 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
 
         // S^T <- diag(GamC) S^T + kg^T U
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-            if (kb + 2 < 8) {
+        for (int kb = 0; kb < KT; ++kb) {
+            if (kb + 2 < KT) {
 #pragma unroll
                 for (int s = 0; s < CS; ++s) fk[(kb + 2) % 3][s] = frag(R::KG_OFF, (kb + 2) * CS + s);
             }
@@ -1165,7 +1169,7 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
 
     if (p.ht) {
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
+        for (int kb = 0; kb < KT; ++kb)
             *(f32x4 *)(p.ht + sbase + tile_chan(kb, 4 * lg)) = S[kb] * sigma;
     }
 }
@@ -1187,37 +1191,41 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
 // Transposes between the row layout and the time-major operands of the W, Ub
 // and kg^T products go through MFMA with an identity factor (exact for fp16).
 // =============================================================================
-struct IntraRB {
+template <int D>
+struct IntraRB {                                          // D: head size (K = V), 128 or 64
+    static constexpr int KS = D / 32;                     // 32-channel k-steps
     static constexpr int AP = 68;                         // sA / sT row pitch (floats)
     static constexpr int TP = 72;                         // KE^T / V^T row pitch (halves)
     static constexpr int NFV = 6;                         // factor vectors per wave
     static constexpr size_t SA = 0;                       // float [64][AP]: A (beta-scaled, strictly lower)
     static constexpr size_t ST = SA + (size_t)64 * AP * 4;     // float [64][AP]: X = (I + A)^-1
-    static constexpr size_t SL0 = ST + (size_t)64 * AP * 4;    // float [4][128]: lambda of each block's row 0
-    static constexpr size_t SLE = SL0 + 4 * 128 * 4;           // float [4][128]: Lam at each block's row 15
-    static constexpr size_t SBETA = SLE + 4 * 128 * 4;         // float [64]
+    static constexpr size_t SL0 = ST + (size_t)64 * AP * 4;    // float [4][D]: lambda of each block's row 0
+    static constexpr size_t SLE = SL0 + 4 * D * 4;             // float [4][D]: Lam at each block's row 15
+    static constexpr size_t SBETA = SLE + 4 * D * 4;           // float [64]
     static constexpr size_t SVMAX = SBETA + 64 * 4;            // float [4]
-    static constexpr size_t SGB = SVMAX + 64;                  // float [4 waves][128]: gate offsets
-    static constexpr size_t U = SGB + 4 * 128 * 4;             // union of two uses:
-    static constexpr size_t FV = U;                            //  per-wave factor vectors [4][NFV][128]
-    static constexpr size_t RP = FV + (size_t)4 * NFV * 128 * 4;   //  R' fragments half8 [3][4][64]
-    static constexpr size_t SX = RP + (size_t)3 * 4 * 64 * 16;     //  inverse scratch [4][16][20]
-    static constexpr size_t KQ = SX + (size_t)4 * 16 * 20 * 4;     //  KP, QP fragments of block 3, half8 [2][4][64]
-    static constexpr size_t U1_END = KQ + (size_t)2 * 4 * 64 * 16;
-    static constexpr size_t KET = U;                           //  KE^T fp16 [128][TP] (after the inverse)
-    static constexpr size_t VT = KET + (size_t)128 * TP * 2;   //  V^T  fp16 [128][TP]
-    static constexpr size_t U2_END = VT + (size_t)128 * TP * 2;
+    static constexpr size_t SGB = SVMAX + 64;                  // float [4 waves][D]: gate offsets
+    static constexpr size_t U = SGB + 4 * D * 4;               // union of two uses:
+    static constexpr size_t FV = U;                            //  per-wave factor vectors [4][NFV][D]
+    static constexpr size_t RP = FV + (size_t)4 * NFV * D * 4;     //  R' fragments half8 [3][KS][64]
+    static constexpr size_t SX = RP + (size_t)3 * KS * 64 * 16;    //  inverse scratch [4][16][20]
+    static constexpr size_t KQ = SX + (size_t)4 * 16 * 20 * 4;     //  KP, QP fragments of block 3, half8 [2][KS][64]
+    static constexpr size_t U1_END = KQ + (size_t)2 * KS * 64 * 16;
+    static constexpr size_t KET = U;                           //  KE^T fp16 [D][TP] (after the inverse)
+    static constexpr size_t VT = KET + (size_t)D * TP * 2;     //  V^T  fp16 [D][TP]
+    static constexpr size_t U2_END = VT + (size_t)D * TP * 2;
     static constexpr size_t BYTES = U1_END > U2_END ? U1_END : U2_END;
 };
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
-template <typename Tin>
+template <typename Tin, int D = 128>
 __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t ntiles)
 {
     constexpr int C = 64, NB = 4, CS = 2;
-    using R = Record<C, false>;
-    using LY = IntraRB;
+    constexpr int KS = D / 32, KT = D / 16;   // 32-channel k-steps; 16-channel tiles (= value blocks)
+    constexpr int CPL = D / 64;               // channels of a per-channel vector each lane owns
+    using R = Record<C, false, D>;
+    using LY = IntraRB<D>;
     static_assert(std::is_same<Tin, __bf16>::value, "bf16 inputs");
 
     __shared__ __align__(16) unsigned char smem[LY::BYTES];
@@ -1243,16 +1251,16 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
     }
 
     // W and Ub results of the previous tile, stored once the next tile's loads are issued
-    half8 pw[4];
-    half4_t pu[8];
+    half8 pw[KS];
+    half4_t pu[KT];
     unsigned char *prec = nullptr;
     auto flush = [&](int b, int lane) {
         if (!prec) return;
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
-            *(half8 *)(prec + R::W_OFF + ((size_t)(b * 4 + s) * 64 + lane) * 16) = pw[s];
+        for (int s = 0; s < KS; ++s)
+            *(half8 *)(prec + R::W_OFF + ((size_t)(b * KS + s) * 64 + lane) * 16) = pw[s];
 #pragma unroll
-        for (int vb = 0; vb < 8; ++vb)
+        for (int vb = 0; vb < KT; ++vb)
             *(half4_t *)(prec + R::UB_OFF + ((size_t)(vb * NB + b) * 64 + lane) * 8) = pu[vb];
         prec = nullptr;
     };
@@ -1267,7 +1275,7 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
         asm volatile("" : "+s"(bw));
         const int b = bw;                           // this wave's 16-row block
         const int lane = tid & 63, lr = lane & 15, lg = lane >> 4;
-        float *fv = (float *)(smem + LY::FV) + (size_t)b * LY::NFV * 128;   // this wave's factor vectors
+        float *fv = (float *)(smem + LY::FV) + (size_t)b * LY::NFV * D;     // this wave's factor vectors
         // identity selectors: column c of tile 2s + half picks channel tile_chan(2s + half, c),
         // i.e. k-index (c / 4, 4 half + c % 4) of step s
         half8 id0, id1;
@@ -1289,20 +1297,27 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
         const int r = 16 * b + lr;                  // tile row of this lane
         const bool rv = r < L;
         const size_t row = (size_t)(t0 + (rv ? r : L - 1)) * H + h;
-        const float *gr = p.g + row * kHeadDim;
-        f32x4 graw[4][2];
+        const float *gr = p.g + row * D;
+        f32x4 graw[KS][2];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) graw[s][hf] = *(const f32x4 *)(gr + chan(s, hf));
-        const float2 dt2 = *(const float2 *)(p.dt_bias + (size_t)h * kHeadDim + 2 * lane);
+        float dtv[CPL];                              // dt_bias of channels CPL lane .. + CPL - 1
+        if constexpr (CPL == 2) {
+            const float2 d2 = *(const float2 *)(p.dt_bias + (size_t)h * D + 2 * lane);
+            dtv[0] = d2.x;
+            dtv[CPL - 1] = d2.y;
+        } else {
+            dtv[0] = p.dt_bias[(size_t)h * D + lane];
+        }
         const size_t rowk = (size_t)(t0 + (rv ? r : L - 1)) * p.Hk + h / (H / p.Hk);
-        const Tin *qr = (const Tin *)p.q + rowk * kHeadDim;
-        const Tin *kr = (const Tin *)p.k + rowk * kHeadDim;
-        const Tin *vr = (const Tin *)p.v + row * kHeadDim;
-        bf16x8 qraw[4], kraw[4], vraw[4];
+        const Tin *qr = (const Tin *)p.q + rowk * D;
+        const Tin *kr = (const Tin *)p.k + rowk * D;
+        const Tin *vr = (const Tin *)p.v + row * D;
+        bf16x8 qraw[KS], kraw[KS], vraw[KS];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < KS; ++s) {
             qraw[s] = *(const bf16x8 *)(qr + chan(s, 0));
             kraw[s] = *(const bf16x8 *)(kr + chan(s, 0));
             vraw[s] = *(const bf16x8 *)(vr + chan(s, 0));
@@ -1317,11 +1332,12 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
         const float ga = -fast_exp2(alog * kLog2e) * kLog2e;
         // ga * dt_bias per channel, spread to this lane's channels through this
         // wave's own LDS row (its LDS accesses complete in order)
-        float *sgb = (float *)(smem + LY::SGB) + b * 128;
-        *(float2 *)(sgb + 2 * lane) = float2{ga * dt2.x, ga * dt2.y};
-        float lam[4][8];
+        float *sgb = (float *)(smem + LY::SGB) + b * D;
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int c = 0; c < CPL; ++c) sgb[CPL * lane + c] = ga * dtv[c];
+        float lam[KS][8];
+#pragma unroll
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 const f32x4 gb = *(const f32x4 *)(sgb + chan(s, hf));
@@ -1333,46 +1349,46 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
             }
         if (lr == 0) {                               // lambda of the block's first row
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+            for (int s = 0; s < KS; ++s)
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf)
-                    *(f32x4 *)(sL0 + b * 128 + chan(s, hf)) =
+                    *(f32x4 *)(sL0 + b * D + chan(s, hf)) =
                         f32x4{lam[s][4 * hf], lam[s][4 * hf + 1], lam[s][4 * hf + 2], lam[s][4 * hf + 3]};
         }
         // Lam_r = sum_{s=1..r} lambda_s over the block: inclusive prefix sum across
         // the 16 lanes of the DPP row (row_shr d, out-of-row lanes read 0)
-        float Lm[4][8];
+        float Lm[KS][8];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int e = 0; e < 8; ++e) Lm[s][e] = (lr == 0) ? 0.0f : lam[s][e];
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int e = 0; e < 8; ++e) Lm[s][e] += dpp_f<0x111>(Lm[s][e]);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int e = 0; e < 8; ++e) Lm[s][e] += dpp_f<0x112>(Lm[s][e]);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int e = 0; e < 8; ++e) Lm[s][e] += dpp_f<0x114>(Lm[s][e]);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int e = 0; e < 8; ++e) Lm[s][e] += dpp_f<0x118>(Lm[s][e]);
         if (lr == 15) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+            for (int s = 0; s < KS; ++s)
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf)
-                    *(f32x4 *)(sLE + b * 128 + chan(s, hf)) =
+                    *(f32x4 *)(sLE + b * D + chan(s, hf)) =
                         f32x4{Lm[s][4 * hf], Lm[s][4 * hf + 1], Lm[s][4 * hf + 2], Lm[s][4 * hf + 3]};
         }
         float vmax = 0.0f;
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -1383,24 +1399,26 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
         // the previous tile's W / Ub, now behind this tile's loads in the memory queue
         flush(b, lane);
 
-        // ---- per-channel factors (lane: channels 2 lane, 2 lane + 1) ------------------
+        // ---- per-channel factors (lane: channels CPL lane .. CPL lane + CPL - 1) --------
         //   QF_b = e^{G_16b}                      (chunk-relative, row 16b included)
         //   KF_b = prod of the block totals after b
         //   Pe_b = 2^Lam_15 of block b
         //   X_bc = e^{G_16b - G_16c+15}, c < b
         {
-            float tot[NB][2], l0b[2], leb[2];
+            float tot[NB][CPL], l0b[CPL], leb[CPL];
 #pragma unroll
             for (int bb = 0; bb < NB; ++bb) {
-                const float2 x0 = *(const float2 *)(sL0 + bb * 128 + 2 * lane);
-                const float2 xe = *(const float2 *)(sLE + bb * 128 + 2 * lane);
-                tot[bb][0] = x0.x + xe.x;
-                tot[bb][1] = x0.y + xe.y;
-                if (bb == b) { l0b[0] = x0.x; l0b[1] = x0.y; leb[0] = xe.x; leb[1] = xe.y; }
-            }
-            float qf[2], kf[2], xs[NB][2], all[2];
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+                for (int c = 0; c < CPL; ++c) {
+                    const float x0 = sL0[bb * D + CPL * lane + c];
+                    const float xe = sLE[bb * D + CPL * lane + c];
+                    tot[bb][c] = x0 + xe;
+                    if (bb == b) { l0b[c] = x0; leb[c] = xe; }
+                }
+            }
+            float qf[CPL], kf[CPL], xs[NB][CPL], all[CPL];
+#pragma unroll
+            for (int i = 0; i < CPL; ++i) {
                 float pre = 0.f, suf = 0.f, sum = 0.f;
 #pragma unroll
                 for (int bb = 0; bb < NB; ++bb) {
@@ -1421,15 +1439,17 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
                     }
                 }
             }
-            *(float2 *)(fv + 0 * 128 + 2 * lane) = float2{fast_exp2(qf[0]), fast_exp2(qf[1])};
-            *(float2 *)(fv + 1 * 128 + 2 * lane) = float2{fast_exp2(kf[0]), fast_exp2(kf[1])};
-            *(float2 *)(fv + 2 * 128 + 2 * lane) = float2{fast_exp2(leb[0]), fast_exp2(leb[1])};
 #pragma unroll
-            for (int c = 0; c < NB - 1; ++c)
-                if (c < b)
-                    *(float2 *)(fv + (3 + c) * 128 + 2 * lane) = float2{fast_exp2(xs[c][0]), fast_exp2(xs[c][1])};
-            if (b == 0)                              // total decay of the chunk
-                *(float2 *)(rec + R::GC_OFF + 8 * lane) = float2{fast_exp2(all[0]), fast_exp2(all[1])};
+            for (int c = 0; c < CPL; ++c) {
+                fv[0 * D + CPL * lane + c] = fast_exp2(qf[c]);
+                fv[1 * D + CPL * lane + c] = fast_exp2(kf[c]);
+                fv[2 * D + CPL * lane + c] = fast_exp2(leb[c]);
+#pragma unroll
+                for (int cc = 0; cc < NB - 1; ++cc)
+                    if (cc < b) fv[(3 + cc) * D + CPL * lane + c] = fast_exp2(xs[cc][c]);
+                if (b == 0)                          // total decay of the chunk
+                    ((float *)(rec + R::GC_OFF))[CPL * lane + c] = fast_exp2(all[c]);
+            }
         }
         if (lg == 0) sBeta[r] = rv ? sigmoid_f(braw) : 0.0f;
         const float beta = rv ? sigmoid_f(braw) : 0.0f;
@@ -1443,12 +1463,12 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
         }
 
         // ---- row quantities: norms, decay products, fp16 operands ---------------------
-        float KP[4][8], QP[4][8], RI[4][8];
-        half8 ke16[4], v16[4];
+        float KP[KS][8], QP[KS][8], RI[KS][8];
+        half8 ke16[KS], v16[KS];
         {
             float sq = 0.f, sk = 0.f;
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+            for (int s = 0; s < KS; ++s)
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -1463,7 +1483,7 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
             sk += __shfl_xor(sk, 32);
             const float fq = rsqrtf(sq + kL2Eps) * p.scale, fk = rv ? rsqrtf(sk + kL2Eps) : 0.0f;
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+            for (int s = 0; s < KS; ++s)
 #pragma unroll
                 for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
@@ -1479,13 +1499,13 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
         }
         // qg, kg^T, KE and the R' operands of the off-diagonal blocks
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
+        for (int s = 0; s < KS; ++s) {
             float qf[8], kf[8], pe[8];
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
-                const f32x4 a = *(const f32x4 *)(fv + 0 * 128 + chan(s, hf));
-                const f32x4 k = *(const f32x4 *)(fv + 1 * 128 + chan(s, hf));
-                const f32x4 e = *(const f32x4 *)(fv + 2 * 128 + chan(s, hf));
+                const f32x4 a = *(const f32x4 *)(fv + 0 * D + chan(s, hf));
+                const f32x4 k = *(const f32x4 *)(fv + 1 * D + chan(s, hf));
+                const f32x4 e = *(const f32x4 *)(fv + 2 * D + chan(s, hf));
 #pragma unroll
                 for (int i = 0; i < 4; ++i) { qf[4 * hf + i] = a[i]; kf[4 * hf + i] = k[i]; pe[4 * hf + i] = e[i]; }
             }
@@ -1498,15 +1518,15 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
                 qg[e] = (_Float16)(QP[s][e] * qf[e]);        // qh e^{G_t}
                 ke16[s][e] = (_Float16)(KP[s][e] * qf[e]);   // kh e^{G_t}
             }
-            if (b < NB - 1) sRP[(b * 4 + s) * 64 + lane] = rp;
+            if (b < NB - 1) sRP[(b * KS + s) * 64 + lane] = rp;
             if (b == NB - 1) {          // left operands of the blocks (3, 0), (3, 1), computed by waves 0, 1
                 half8 kq, qq;
 #pragma unroll
                 for (int e = 0; e < 8; ++e) { kq[e] = (_Float16)KP[s][e]; qq[e] = (_Float16)QP[s][e]; }
                 sKQ[s * 64 + lane] = kq;
-                sKQ[(4 + s) * 64 + lane] = qq;
+                sKQ[(KS + s) * 64 + lane] = qq;
             }
-            *(half8 *)(rec + R::QG_OFF + ((size_t)(b * 4 + s) * 64 + lane) * 16) = qg;
+            *(half8 *)(rec + R::QG_OFF + ((size_t)(b * KS + s) * 64 + lane) * 16) = qg;
             // kg^T fragments (tile 2s + half, k-step b / 2): this block's rows are
             // positions 4 (b & 1) .. + 3 of each lane's 8
 #pragma unroll
@@ -1523,7 +1543,7 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
         {
             f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aM = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {               // diagonal block: fp32 MFMA (factors up to 2^108)
+            for (int s = 0; s < KS; ++s) {              // diagonal block: fp32 MFMA (factors up to 2^108)
                 aA = mfma_f32x8(RI[s], KP[s], aA);
                 aM = mfma_f32x8(RI[s], QP[s], aM);
             }
@@ -1549,10 +1569,10 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
         // wave at most instead of three)
         for (int c = (b == NB - 1 ? 2 : 0); c < b; ++c) {
             f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aM = {0.f, 0.f, 0.f, 0.f};
-            const float *xf = fv + (3 + c) * 128;
+            const float *xf = fv + (3 + c) * D;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const half8 rpc = sRP[(c * 4 + s) * 64 + lane];
+            for (int s = 0; s < KS; ++s) {
+                const half8 rpc = sRP[(c * KS + s) * 64 + lane];
                 const f32x4 x0 = *(const f32x4 *)(xf + chan(s, 0)), x1 = *(const f32x4 *)(xf + chan(s, 1));
                 half8 lk, lq;
 #pragma unroll
@@ -1572,11 +1592,11 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
         if (b < 2) {                                    // block (3, b) by its column owner
             constexpr int a = NB - 1;
             f32x4 aA = {0.f, 0.f, 0.f, 0.f}, aM = {0.f, 0.f, 0.f, 0.f};
-            const float *xf = (const float *)(smem + LY::FV) + (size_t)a * LY::NFV * 128 + (3 + b) * 128;
+            const float *xf = (const float *)(smem + LY::FV) + (size_t)a * LY::NFV * D + (3 + b) * D;
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+            for (int s = 0; s < KS; ++s) {
                 const f32x4 x0 = *(const f32x4 *)(xf + chan(s, 0)), x1 = *(const f32x4 *)(xf + chan(s, 1));
-                const f32x4 p0 = *(const f32x4 *)(fv + 2 * 128 + chan(s, 0)), p1 = *(const f32x4 *)(fv + 2 * 128 + chan(s, 1));
+                const f32x4 p0 = *(const f32x4 *)(fv + 2 * D + chan(s, 0)), p1 = *(const f32x4 *)(fv + 2 * D + chan(s, 1));
                 half8 rr;                                   // kh_j e^{G_48 - G_j}
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -1584,7 +1604,7 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
                     rr[i + 4] = (_Float16)(RI[s][i + 4] * (p1[i] * x1[i]));
                 }
                 aA = mfma_h(rr, sKQ[s * 64 + lane], aA);
-                aM = mfma_h(rr, sKQ[(4 + s) * 64 + lane], aM);
+                aM = mfma_h(rr, sKQ[(KS + s) * 64 + lane], aM);
             }
             // lane holds A[i][j] / M[i][j] for i = 48 + lr, j = 16b + 4lg + ii
             *(f32x4 *)&sA[16 * a + lr][16 * b + 4 * lg] = aA * sBeta[16 * a + lr];
@@ -1622,7 +1642,7 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
         }
         // KE^T and V^T (time-major fp16 rows per channel) for the W and Ub products
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+        for (int s = 0; s < KS; ++s)
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) {
                 const int ch = tile_chan(2 * s + hf, lr);
@@ -1677,9 +1697,9 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
                     for (int e = 0; e < 8; ++e) tf[sp][e] = (_Float16)0.0f;
                 }
             }
-            f32x4 aw[8];
+            f32x4 aw[KT];
 #pragma unroll
-            for (int cb = 0; cb < 8; ++cb) {
+            for (int cb = 0; cb < KT; ++cb) {
                 aw[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int sp = 0; sp < CS; ++sp)
@@ -1687,14 +1707,14 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
                         aw[cb] = mfma_h(*(const half8 *)(sKET + tile_chan(cb, lr) * LY::TP + 32 * sp + 8 * lg), tf[sp], aw[cb]);
             }
 #pragma unroll
-            for (int s = 0; s < 4; ++s)                 // W stored negated: U = Ub + (-W) S^T
+            for (int s = 0; s < KS; ++s)                // W stored negated: U = Ub + (-W) S^T
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     pw[s][i] = (_Float16)(-aw[2 * s][i]);
                     pw[s][i + 4] = (_Float16)(-aw[2 * s + 1][i]);
                 }
 #pragma unroll
-            for (int vb = 0; vb < 8; ++vb) {
+            for (int vb = 0; vb < KT; ++vb) {
                 f32x4 au = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int sp = 0; sp < CS; ++sp)
@@ -1739,9 +1759,10 @@ static hipError_t set_lds_limit(const void *fn, int lds, std::atomic<uint64_t> &
     return e;
 }
 
-template <int C, typename Tin, typename Tout>
+template <int C, typename Tin, typename Tout, int D>
 static hipError_t launch_prefill_t(const PrefillArgs &a) {
     constexpr bool PRECISE = std::is_same<Tin, float>::value;
+    static_assert(D == 128 || (C == 64 && !PRECISE), "head size 64: 64-row chunks of bf16 inputs");
     const int64_t slots = num_slots(a.T, a.N, C);
     if ((a.stages & 1) && slots > 0) {
         // workgroups walk the tiles blockIdx.x, blockIdx.x + gridDim.x, ...
@@ -1755,7 +1776,7 @@ static hipError_t launch_prefill_t(const PrefillArgs &a) {
             // the two on a CU drift out of phase; persistent workgroups walking
             // the tiles in step measured 7% slower at T=8192, H=96)
             const int64_t grid = ntiles < 0x7fffffff ? ntiles : 0x7fffffff;
-            intra64_kernel<Tin><<<(unsigned)grid, 256, 0, a.stream>>>(a, ntiles);
+            intra64_kernel<Tin, D><<<(unsigned)grid, 256, 0, a.stream>>>(a, ntiles);
         } else {
             // persistent (one per CU): each prefetches its next tile's inputs into LDS
             const int64_t grid = ntiles < (int64_t)cus ? ntiles : (int64_t)cus;
@@ -1766,13 +1787,14 @@ static hipError_t launch_prefill_t(const PrefillArgs &a) {
     }
     const int nchains = a.N * a.H;
     if ((a.stages & 2) && nchains > 0) {
-        using CFG = InterCfg<C, PRECISE>;
+        using CFG = InterCfg<C, PRECISE, D>;
         const size_t lds = (size_t)CFG::NBUF * CFG::BUF;
         static std::atomic<uint64_t> lds_set{0};          // one flag word per kernel
-        hipError_t e = set_lds_limit((const void *)inter_kernel<C, Tout, PRECISE>, (int)lds, lds_set);
+        hipError_t e = set_lds_limit((const void *)inter_kernel<C, Tout, PRECISE, D>, (int)lds, lds_set);
         if (e != hipSuccess) return e;
-        const unsigned groups = (unsigned)(8 * 2 * ((nchains + 7) / 8));
-        inter_kernel<C, Tout, PRECISE><<<groups, 256, lds, a.stream>>>(a, nchains);
+        // one workgroup per 64 state rows of a chain (two at D = 128)
+        const unsigned groups = (unsigned)(8 * (D / 64) * ((nchains + 7) / 8));
+        inter_kernel<C, Tout, PRECISE, D><<<groups, 256, lds, a.stream>>>(a, nchains);
         return hipGetLastError();
     }
     return hipSuccess;
@@ -1781,13 +1803,20 @@ static hipError_t launch_prefill_t(const PrefillArgs &a) {
 template <int C>
 static hipError_t launch_prefill_c(const PrefillArgs &a) {
     if (a.in_bf16)
-        return a.out_bf16 ? launch_prefill_t<C, __bf16, __bf16>(a) : launch_prefill_t<C, __bf16, float>(a);
-    return a.out_bf16 ? launch_prefill_t<C, float, __bf16>(a) : launch_prefill_t<C, float, float>(a);
+        return a.out_bf16 ? launch_prefill_t<C, __bf16, __bf16, 128>(a)
+                          : launch_prefill_t<C, __bf16, float, 128>(a);
+    return a.out_bf16 ? launch_prefill_t<C, float, __bf16, 128>(a) : launch_prefill_t<C, float, float, 128>(a);
 }
 
 hipError_t launch_prefill(const PrefillArgs &args) {
     PrefillArgs a = args;
     if (a.Hk <= 0) a.Hk = a.H;          // no grouping: one q/k head per value head
+    if (a.D == 64) {                    // natively sized kernels: 64-row chunks, bf16 inputs
+        if (a.chunk != 64 || !a.in_bf16) return hipErrorInvalidValue;
+        return a.out_bf16 ? launch_prefill_t<64, __bf16, __bf16, 64>(a)
+                          : launch_prefill_t<64, __bf16, float, 64>(a);
+    }
+    if (a.D != 128) return hipErrorInvalidValue;
     switch (a.chunk) {
         case 16: return launch_prefill_c<16>(a);
         case 32: return launch_prefill_c<32>(a);

@@ -428,3 +428,21 @@ def test_gated_workspace_size(kda):
         kda.lib.kda_chunk_fwd_workspace_size(100, 2, 3, 48, 80, 32, kda.KDA_F32)
     assert f(8192, 1, 96, 128, 128, 64, kda.KDA_BF16, 7) == 0
     assert f(8192, 1, 96, 129, 128, 64, kda.KDA_BF16, kda.KDA_BF16) == 0
+
+
+def test_workspace_size_native_64(kda):
+    """K = V = 64 with 64-row chunks of bf16 inputs runs on kernels sized for 64:
+    records only (no padded copies), each smaller than a 128-wide record; other
+    dtypes and chunk sizes at 64 keep the padded layout."""
+    import torch
+    T, N, H = 1000, 3, 4
+    slots = T // 64 + N
+    n64 = kda.workspace_size(T, N, H, 64, torch.bfloat16, K=64, V=64)
+    n128 = kda.workspace_size(T, N, H, 64, torch.bfloat16)
+    assert (n64 - 256) % (slots * H) == 0
+    rec64 = (n64 - 256) // (slots * H)
+    assert rec64 < (n128 - 256) // (slots * H)
+    # W, qg, kg (64 x 64 fp16 each), M (8 fragments), decay (64 fp32), scale, Ub (64 x 64)
+    assert rec64 == 3 * 64 * 64 * 2 + 8 * 1024 + 64 * 4 + 16 + 64 * 64 * 2
+    assert kda.workspace_size(T, N, H, 32, torch.bfloat16, K=64, V=64) > n128
+    assert kda.workspace_size(T, N, H, 64, torch.float32, K=64, V=64) > n128
