@@ -3,7 +3,10 @@ indices, and HIP-graph capture and replay of the decode and prefill calls.
 
 Slot indexing only changes where each request's state lives, so its results
 must equal, bit for bit, the plain decode step on the gathered states; graph
-replays must equal eager calls bit for bit (the kernels are deterministic)."""
+replays must equal eager calls bit for bit (the kernels are deterministic).
+Both forms are also checked directly against the fp64 oracle: the slot-indexed
+step's outputs and updated pool entries over consecutive steps, and every graph
+replay of the prefill and of the slot-indexed decode."""
 import pytest
 import torch
 
@@ -141,3 +144,147 @@ def test_graph_capture_prefill(kda, chunk, K, V):
         o_e, h_e = call(fresh, None, None, ws2)
         torch.cuda.synchronize()
         assert torch.equal(o_g, o_e) and torch.equal(h_g, h_e), rep
+
+
+# ---- the same serving forms anchored to the fp64 oracle -----------------------
+
+import numpy as np  # noqa: E402
+
+import oracle  # noqa: E402
+from helpers import max_err_bf16_out, max_err_rel_rms  # noqa: E402
+
+
+@pytest.mark.parametrize("in_dtype,gated", [(torch.float32, False), (torch.bfloat16, False),
+                                            (torch.bfloat16, True)])
+def test_decode_slots_against_oracle(kda, in_dtype, gated):
+    """Three consecutive slot-indexed steps over a pool (padding requests included,
+    different slot lists per step): every valid request's output and the pool's
+    updated entries against the oracle run on the gathered states; entries no
+    request names stay untouched. fp32 outputs (the step computes in fp32):
+    1e-5 of the rms; with the epilogue, y against the oracle's epilogue of its o."""
+    H, S = 3, 10
+    gen = torch.Generator().manual_seed(90)
+    pool0 = torch.randn(S, H, 128, 128, generator=gen) * 0.1
+    pool = pool0.to(DEV)
+    ref_pool = pool0.double().numpy().copy()
+    steps = [[7, 2, -1, 9, 0, 15], [2, 9, 4, 10, 7, -3], [0, 1, 2, 3, 4, 5]]
+    for i, slots in enumerate(steps):
+        B = len(slots)
+        d = kda_inputs.make_decode(B, H, 1, seed=91 + i)
+        st = d.steps[0]
+        cv = lambda x: x.to(in_dtype)
+        q, k, v = cv(st["q"]), cv(st["k"]), cv(st["v"])
+        kw = {}
+        if gated:
+            z, w = kda_inputs.make_epilogue((B, H, 128), token_dtype=in_dtype, seed=95 + i)
+            kw = dict(gate=z.to(DEV), norm_weight=w.to(DEV))
+        idx = torch.tensor(slots, dtype=torch.int32, device=DEV)
+        y = kda.decode_step(q.to(DEV), k.to(DEV), v.to(DEV), st["g"].to(DEV),
+                            st["beta_raw"].to(DEV), d.A_log.to(DEV), d.dt_bias.to(DEV), pool,
+                            scale=d.scale, slot_idx=idx, o_dtype=torch.float32, **kw)
+        torch.cuda.synchronize()
+        valid = [j for j, s in enumerate(slots) if 0 <= s < S]
+        vs = [slots[j] for j in valid]
+        sel = lambda x: x[valid]
+        o_ref, h_ref = oracle.kda_recurrent(sel(q), sel(k), sel(v), sel(st["g"]),
+                                            sel(st["beta_raw"]), d.A_log, d.dt_bias,
+                                            torch.arange(len(valid) + 1), scale=d.scale,
+                                            h0=ref_pool[vs])
+        if gated:
+            o_ref = oracle.output_norm_gate(o_ref, sel(z), w, eps=kda.NORM_EPS)
+        ref_pool[vs] = h_ref
+        e_o = max_err_rel_rms(y[valid], o_ref)
+        e_s = max_err_rel_rms(pool, ref_pool)
+        print("slots step %d %s gated=%s: o %.3e pool %.3e" % (i, in_dtype, gated, e_o, e_s),
+              flush=True)
+        assert e_o <= 1e-5 and e_s <= 1e-5
+        pad = [j for j, s in enumerate(slots) if not 0 <= s < S]
+        assert torch.all(y[pad] == 0)
+    never = [s for s in range(S) if all(s not in sl for sl in steps)]
+    assert torch.equal(pool[never].cpu(), pool0[never])
+
+
+def test_graph_replays_against_oracle(kda):
+    """Prefill and slot-indexed decode captured once and replayed on fresh inputs:
+    every replay against the oracle (the prefill's bf16 output beyond its storage
+    rounding at 2e-2, final states and the decode at the literal metric)."""
+    lengths = [300, 0, 211, 64]
+    p = kda_inputs.make_prefill(lengths, 4, h0_std=0.1, chunk=64, seed=100)
+    names = ("q", "k", "v", "g", "beta_raw", "A_log", "dt_bias", "cu_seqlens", "h0")
+    static = {n: getattr(p, n).to(DEV).clone() for n in names}
+    ws = kda.Workspace(DEV)
+    o = torch.empty(p.T, 4, 128, dtype=torch.bfloat16, device=DEV)
+    ht = torch.empty(len(lengths), 4, 128, 128, dtype=torch.float32, device=DEV)
+
+    def call(t):
+        kda.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta_raw"], t["A_log"], t["dt_bias"],
+                      t["cu_seqlens"], scale=p.scale, chunk_size=64, initial_state=t["h0"],
+                      out=o, final_state=ht, workspace=ws)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(static)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(static)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        q = kda_inputs.make_prefill(lengths, 4, g_std=2.0, h0_std=0.1, chunk=64, seed=101 + rep)
+        for n in names:
+            static[n].copy_(getattr(q, n).to(DEV))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        o_ref, h_ref = oracle.kda_recurrent(q.q, q.k, q.v, q.g, q.beta_raw, q.A_log, q.dt_bias,
+                                            q.cu_seqlens, scale=q.scale, h0=q.h0)
+        e_o, e_h = max_err_bf16_out(o, o_ref), max_err_rel_rms(ht, h_ref)
+        print("prefill replay %d: o %.3e ht %.3e" % (rep, e_o, e_h), flush=True)
+        assert e_o <= 2e-2 and e_h <= 2e-2
+        _ = torch.zeros(1, device=DEV) + 1              # eager work between replays
+
+    # decode over a pool, captured with its slot indices as a device tensor
+    H, S, B = 4, 12, 8
+    gen = torch.Generator().manual_seed(110)
+    pool0 = torch.randn(S, H, 128, 128, generator=gen) * 0.1
+    d0 = kda_inputs.make_decode(B, H, 1, seed=111)
+    st0 = d0.steps[0]
+    sd = [st0[n].to(DEV).clone() for n in ("q", "k", "v", "g", "beta_raw")]
+    A_log, dt_bias = d0.A_log.to(DEV), d0.dt_bias.to(DEV)
+    idx = torch.randperm(S, generator=gen)[:B].to(torch.int32).to(DEV)
+    pool = pool0.to(DEV)
+    out = torch.empty(B, H, 128, dtype=torch.float32, device=DEV)
+
+    def dec():
+        kda.decode_step(*sd, A_log, dt_bias, pool, scale=d0.scale, slot_idx=idx, out=out,
+                        o_dtype=torch.float32)
+
+    with torch.cuda.stream(s):
+        dec()                                           # eager warm-up (updates the pool)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g2 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g2):
+        dec()
+    torch.cuda.synchronize()
+    pool.copy_(pool0.to(DEV))
+    ref_pool = pool0.double().numpy().copy()
+    for rep in range(3):
+        dr = kda_inputs.make_decode(B, H, 1, seed=112 + rep)
+        for t, n in zip(sd, ("q", "k", "v", "g", "beta_raw")):
+            t.copy_(dr.steps[0][n].to(DEV))
+        sl = torch.randperm(S, generator=gen)[:B].to(torch.int32)
+        idx.copy_(sl.to(DEV))
+        torch.cuda.synchronize()
+        g2.replay()
+        torch.cuda.synchronize()
+        st = dr.steps[0]
+        o_ref, h_ref = oracle.kda_recurrent(st["q"], st["k"], st["v"], st["g"], st["beta_raw"],
+                                            d0.A_log, d0.dt_bias, torch.arange(B + 1),
+                                            scale=d0.scale, h0=ref_pool[sl.numpy()])
+        ref_pool[sl.numpy()] = h_ref
+        e_o, e_s = max_err_rel_rms(out, o_ref), max_err_rel_rms(pool, ref_pool)
+        print("decode replay %d: o %.3e pool %.3e" % (rep, e_o, e_s), flush=True)
+        assert e_o <= 1e-5 and e_s <= 1e-5
