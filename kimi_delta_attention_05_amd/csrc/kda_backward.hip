@@ -1,38 +1,58 @@
 // Training backward of the KDA recurrence (FlashInfer kda_backward page,
 // "Supported contract": gradients for q, k, v, the raw gate, raw beta, A_log,
-// dt_bias and the initial state, given the output adjoint; the persistent
-// forward-checkpoint and reverse kernels of its "Workspace and CUDA Graphs"
-// section; the kda-neuron-kernels commit log asks that the gradient be that of
-// the exact forward).
+// dt_bias and the initial state, given the output adjoint; its "Workspace and
+// CUDA Graphs" section: forward checkpoints in a caller workspace, then the
+// reverse pass; the kda-neuron-kernels commit log asks that the gradient be
+// that of the exact forward).
 //
 // Forward per token (S value-first [V][K], fp32):
-//   S' = S diag(alpha),  u = b (v - S' kh),  S <- S' + u kh^T,  o = S qh
-// Reverse per token, dS the adjoint of the state after the token:
-//   dS += do qh^T;  dqh = S^T do;  du = dS kh;  dkh = dS^T u - b S'^T du;
-//   dv = b du;  db = du . (v - S' kh);  dS' = dS - b du kh^T;
-//   dalpha = colsum(dS' * S_prev);  dS <- dS' diag(alpha)
-// then dq, dk through the L2 normalisations, dg, ddt_bias, dA_log through the
-// gate, dbeta through the sigmoid; dh0 is the adjoint left at the start.
+//   S' = S diag(alpha),  u = b (v - S' kh),  S <- S' + u kh^T,  o = S qh.
+// Over a chunk of L <= 16 tokens from the state S0 (G_t = the sum of the
+// log-decays lambda of the chunk's tokens up to t, Gam = e^G, GC = Gam of the
+// chunk's last token, SUF = GC / Gam = the product of the decays after t):
+//   KE = kh Gam, QG = qh Gam, KG = kh SUF, KI = kh / Gam             [L][K]
+//   P = KE KI^T, A = strict_lower(diag(b) P), M = lower(QG KI^T), X = (I + A)^-1,
+//   T = X diag(b), R = V - KE S0^T, U = T R, O = QG S0^T + M U,
+//   S1 = S0 diag(GC) + U^T KG.
+// Its adjoint, given dO and the adjoint dS1 of the state after the chunk:
+//   dU = M^T dO + KG dS1^T,  dR = T^T dU (= dv),
+//   dS0 = dS1 diag(GC) + dO^T QG - dR^T KE,
+// and, summed over the state rows v (the "partials"),
+//   dQG = dO S0,  dKG = U dS1,  dKE = -dR S0,  dM = lower(dO U^T),  dT = dU R^T,
+//   dGC = sum_v S0 * dS1;
+// then, per chunk and without the state: dX = dT diag(b), db = colsum(X * dT)
+// + rowsum(dA * P) with dA = strict_lower(-X^T dX X^T), dP = diag(b) dA,
+// dKE += dP KI, dQG += dM KI, dKI = dP^T KE + dM^T QG,
+// dkh = dKE Gam + dKG SUF + dKI / Gam, dqh = dQG Gam, and the log-decay adjoint
+// dlambda_t = sum_{s >= t} (dKE KE + dQG QG - dKI KI)_s + sum_{s < t} (dKG KG)_s
+// + GC dGC; then dq, dk through the L2 normalisations, dg, ddt_bias, dA_log
+// through the gate, dbeta through the sigmoid.
 //
-// Every state row v evolves on its own in both directions; only dqh, dkh,
-// dalpha and db sum over rows. Four launches:
-//   bwd_ckpt_kernel     one workgroup per (sequence, head, block of 16 rows)
-//                       runs the forward and stores the state every 16 tokens
-//                       (the chunk-boundary checkpoints);
-//   bwd_reverse_kernel  same grid: walks the chunks backwards, recomputes the
-//                       states of each half chunk (8 tokens) from the chunk's
-//                       checkpoint into registers, runs the reverse steps,
-//                       writes dv, dh0 and each block's row sums of the
-//                       per-token partials;
-//   bwd_finalize_kernel one workgroup per (16 tokens, head): adds the 8 blocks'
-//                       partials and applies the elementwise chains (dq, dk,
-//                       dg, dbeta), plus per-block sums for the parameters;
-//   bwd_param_kernel    one workgroup per head: ddt_bias and dA_log.
+// Five launches over 16-token chunks:
+//   bwd_prep_kernel        one workgroup per (chunk slot, head), chunk-parallel:
+//                          the chunk's operands KE, KG, QG, T, M^T, GC as a
+//                          record in the workspace;
+//   bwd_ckpt_kernel        one workgroup per (sequence, head, half of the state
+//                          rows), chunk-serial: the forward over the chunks (fp32
+//                          MFMA), storing the state at every chunk start;
+//   bwd_chunk_kernel       same grid, chunks backwards: dS in registers, dv,
+//                          dh0, and per chunk the partials summed over the
+//                          half's 64 state rows;
+//   bwd_chunk_final_kernel one workgroup per (chunk slot, q/k head): adds the two
+//                          halves' partials and finishes the chunk's gradients;
+//   bwd_param_kernel       one workgroup per head: ddt_bias and dA_log.
+// The chunk-serial kernels copy each chunk's record into LDS (DMA, one chunk
+// ahead, double-buffered) and load the next chunk's state rows while the
+// current chunk runs, so that a chunk's step is the MFMA work and two barriers.
 // No atomics: every sum has a fixed order, so results repeat bit for bit.
 //
-// Thread layout of the first two (the decode step's): 256 threads = 4 waves,
-// a 16-lane DPP row owns one state row, lane j holds channels 4j..4j+3 and
-// 64+4j..64+4j+3, so 128-wide dot products are row16 DPP sums.
+// Products are 16 x 16 x 16 tiles on the fp32 MFMA (exact fp32 products, fp32
+// accumulation), so the arithmetic is that of an fp32 reference. A wave owns 16
+// state rows; its operands stay in the MFMA register layouts, and a transposed
+// operand is produced by computing the transposed product (the accumulator of
+// X^T is the row operand of X) rather than by a pass through LDS.
+#include <atomic>
+
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -40,10 +60,13 @@ namespace kda {
 
 namespace {
 
-constexpr int kCk = 16;                          // checkpoint spacing (tokens)
-constexpr int kBRows = 16;                       // state rows per workgroup
-constexpr int kNVB = kHeadDim / kBRows;          // workgroups per (sequence, head)
-constexpr int kPartCols = 3 * kHeadDim + 1;      // dqh, dkh, dalpha partials, db
+constexpr int kCk = 16;                        // chunk length (tokens)
+constexpr int kTP = 132;                       // LDS pitch (floats) of [16][128] tiles
+constexpr int kSP = 20;                        // LDS pitch of [16][16] tiles
+constexpr int kTile = 16 * kTP, kSmall = 16 * kSP;
+constexpr int kPartChunk = 3 * 16 * kHeadDim + 2 * 16 * 16 + kHeadDim;   // partial floats per (chunk, head, half)
+constexpr int kPartRec = 7 * 256 * 4;          // their record (padded)
+static_assert(kPartChunk <= kPartRec, "partial record");
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
@@ -65,438 +88,639 @@ __device__ __forceinline__ void store_lane8(float *row, int j, const float (&x)[
     *(f32x4 *)(row + 64 + 4 * j) = f32x4{x[4], x[5], x[6], x[7]};
 }
 
-// Sum over the four 16-lane rows of a wave (every lane gets the sum): the
-// gfx950 permlane swaps exchange lanes l and l ^ 32, then l and l ^ 16, in
-// VALU (no LDS round trip).
-__device__ __forceinline__ float rows4_sum(float x) {
-    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+// Raw (unconverted) loads, so that a load issued one chunk ahead is waited for
+// only where its value is used.
+template <typename T> struct Vec4T;
+template <> struct Vec4T<float> { typedef f32x4 type; };
+template <> struct Vec4T<__bf16> { typedef bf16x4_t type; };
+template <typename T> using vec4 = typename Vec4T<T>::type;
+template <typename T> struct Raw8 { vec4<T> a, b; };
+
+template <typename T>
+__device__ __forceinline__ void raw8_load(Raw8<T> &r, const T *row, int j) {
+    r.a = *(const vec4<T> *)(row + 4 * j);
+    r.b = *(const vec4<T> *)(row + 64 + 4 * j);
+}
+template <typename T>
+__device__ __forceinline__ void raw8_get(const Raw8<T> &r, float (&x)[8]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { x[e] = (float)r.a[e]; x[e + 4] = (float)r.b[e]; }
+}
+template <typename T>
+__device__ __forceinline__ f32x4 f4(const vec4<T> &x) {
+    return f32x4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
 }
 
-// Four values reduced over the wave's four 16-lane rows at once: a 32-lane
-// swap and add leaves a's half sums in lanes 0-31 and b's in 32-63 (c and d
-// likewise in a second register), a 16-lane swap and add of those two then
-// leaves in row 0 the full sum of a, in row 1 that of c, in row 2 b, in row 3
-// d (each at the lane's own position in its row): 3 swaps + 3 adds for four
-// sums instead of 8 + 8.
-__device__ __forceinline__ float quad_rows_sum(float a, float b, float c, float d) {
-    const auto ab = __builtin_amdgcn_permlane32_swap(__float_as_uint(a), __float_as_uint(b), false, false);
-    const auto cd = __builtin_amdgcn_permlane32_swap(__float_as_uint(c), __float_as_uint(d), false, false);
-    const float x = __uint_as_float(ab[0]) + __uint_as_float(ab[1]);
-    const float y = __uint_as_float(cd[0]) + __uint_as_float(cd[1]);
-    const auto xy = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(y), false, false);
-    return __uint_as_float(xy[0]) + __uint_as_float(xy[1]);
+// 16x16x16 fp32 product on the fp32 MFMA (four 16x16x4 steps). `a` holds row lr
+// of the left factor at columns 4 lg .. 4 lg + 3 ("row layout"), `b` holds rows
+// 4 lg .. 4 lg + 3 of the right factor at column lr ("column layout", which is
+// also the accumulator layout of the result). The accumulator of a product
+// X^T therefore is X in row layout.
+__device__ __forceinline__ f32x4 bmm16(const f32x4 &a, const f32x4 &b, f32x4 acc) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[kk], b[kk], acc, 0, 0, 0);
+    return acc;
+}
+__device__ __forceinline__ f32x4 lds4(const float *p) { return *(const f32x4 *)p; }
+__device__ __forceinline__ f32x4 lds4col(const float *p, int ld) {   // p[0], p[ld], p[2 ld], p[3 ld]
+    return f32x4{p[0], p[ld], p[2 * ld], p[3 * ld]};
 }
 
-// Workgroup b -> (sequence*H + head, row block). The 8 row blocks of one
-// (sequence, head) share its token data, so they go to one XCD (blocks are
+// Workgroup -> (sequence * H + head, half of the state rows); the two halves of
+// one (sequence, head) share its token data and go to one XCD (workgroups are
 // dealt to the 8 XCDs round-robin by index).
-__device__ __forceinline__ bool bwd_block(int64_t b, int64_t NH, int64_t &nh, int &vb) {
-    const int x = (int)(b & 7);
-    const int64_t rest = b >> 3;
-    vb = (int)(rest & 7);
-    nh = (rest >> 3) * 8 + x;
+__device__ __forceinline__ bool half_block(int64_t b, int64_t NH, int64_t &nh, int &half) {
+    const int xcd = (int)(b & 7);
+    const int64_t local = b >> 3;
+    half = (int)(local & 1);
+    nh = (local >> 1) * 8 + xcd;
     return nh < NH;
 }
 
-// Per-token transforms of token t for lane j's channels (one DPP row per token).
-template <typename Tin>
-__device__ __forceinline__ void key_and_decay(const Tin *k, const float *g, const float (&dtb)[8],
-                                              float a_gate, float lb, size_t tb, size_t tbk, int j,
-                                              float (&kh)[8], float (&al)[8]) {
-    float kv[8], gv[8];
-    load_lane8(k + tbk, j, kv);
-    load_lane8(g + tb, j, gv);
-    float ss = 0.f;
+// ---- the chunk's operands --------------------------------------------------
+
+// Raw token data of one chunk for the thread (token gid, lane j of its DPP row).
+template <typename Tin, bool WITH_Q>
+struct TokIn {
+    Raw8<Tin> q, k;
+    Raw8<float> g;
+    float braw;
+};
+
+// Unconditional loads (no branch around them, so that the wait for a load
+// issued one chunk ahead stays exact): a token past the sequence end reads the
+// sequence's last token instead, and its values are ignored where used.
+template <typename Tin, bool WITH_Q>
+__device__ __forceinline__ void tok_load(TokIn<Tin, WITH_Q> &r, const Tin *q, const Tin *k,
+                                         const float *g, const float *beta_raw, int64_t c0,
+                                         int64_t s1, int H, int Hk, int h, int gid, int j) {
+    const int64_t t = c0 + gid < s1 ? c0 + gid : s1 - 1;
+    const size_t tbk = ((size_t)t * Hk + h / (H / Hk)) * kHeadDim;
+    if constexpr (WITH_Q) raw8_load(r.q, q + tbk, j);
+    raw8_load(r.k, k + tbk, j);
+    raw8_load(r.g, g + ((size_t)t * H + h) * kHeadDim, j);
+    r.braw = beta_raw[(size_t)t * H + h];
+}
+
+// Phase 1 (all threads, a DPP row per token): qh (scaled), kh and alpha of the
+// token into the QG, KE and KG tiles, beta into B. Tokens past the sequence end
+// act as q = k = 0, alpha = 1, beta = 0.
+template <typename LY, bool WITH_Q, typename Tin>
+__device__ __forceinline__ void operands_phase1(float *sm, const TokIn<Tin, WITH_Q> &r,
+                                                const float (&dtb)[8], float a_gate, float lb,
+                                                float scale, int L, int gid, int j) {
+    float qh[8], kh[8], al[8], bb = 0.f;
+    if (gid < L) {
+        float qv[8], kv[8], gv[8];
+        raw8_get(r.k, kv);
+        raw8_get(r.g, gv);
+        float sk = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) ss = fmaf(kv[e], kv[e], ss);
-    const float rk = rsqrtf(row16_sum(ss) + kL2Eps);
+        for (int e = 0; e < 8; ++e) sk = fmaf(kv[e], kv[e], sk);
+        const float rk = rsqrtf(row16_sum(sk) + kL2Eps);
+        if constexpr (WITH_Q) {
+            raw8_get(r.q, qv);
+            float sq = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sq = fmaf(qv[e], qv[e], sq);
+            const float rq = rsqrtf(row16_sum(sq) + kL2Eps) * scale;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) qh[e] = qv[e] * rq;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            kh[e] = kv[e] * rk;
+            al[e] = fast_exp2(lb * sigmoid_f(a_gate * (gv[e] + dtb[e])) * kLog2e);
+        }
+        bb = sigmoid_f(r.braw);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { qh[e] = 0.f; kh[e] = 0.f; al[e] = 1.f; }
+    }
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        kh[e] = kv[e] * rk;
-        al[e] = fast_exp2(lb * sigmoid_f(a_gate * (gv[e] + dtb[e])) * kLog2e);
+        if constexpr (WITH_Q) sm[LY::QG + gid * kTP + chan(j, e)] = qh[e];
+        sm[LY::KE + gid * kTP + chan(j, e)] = kh[e];
+        sm[LY::KG + gid * kTP + chan(j, e)] = al[e];
+    }
+    if (j == 0) sm[LY::B + gid] = bb;
+}
+
+// Phase 2 (a thread per key channel): the products of alpha along the chunk
+// (Gam_t up to and including t, SUF_t after t; products of at most 16 factors
+// >= e^-5, so Gam >= e^-80 and never subnormal), and KE, QG, KG, KI written in
+// place over the phase-1 values of the same column; GC into GC. With KEEP, Gam
+// and SUF also stay in the GAM and SUF tiles.
+template <typename LY, bool WITH_Q, bool KEEP>
+__device__ __forceinline__ void operands_phase2(float *sm, int tid) {
+    if (tid < kHeadDim) {
+        const int c = tid;
+        float al[16], kh[16], qh[16], gam[16], suf[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            al[t] = sm[LY::KG + t * kTP + c];
+            kh[t] = sm[LY::KE + t * kTP + c];
+            if constexpr (WITH_Q) qh[t] = sm[LY::QG + t * kTP + c];
+        }
+        float run = 1.f;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) { run *= al[t]; gam[t] = run; }
+        run = 1.f;
+#pragma unroll
+        for (int t = 15; t >= 0; --t) { suf[t] = run; run *= al[t]; }
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+            sm[LY::KE + t * kTP + c] = kh[t] * gam[t];
+            if constexpr (WITH_Q) sm[LY::QG + t * kTP + c] = qh[t] * gam[t];
+            sm[LY::KG + t * kTP + c] = kh[t] * suf[t];
+            sm[LY::KI + t * kTP + c] = kh[t] / gam[t];
+            if constexpr (KEEP) {
+                sm[LY::GAM + t * kTP + c] = gam[t];
+                sm[LY::SUF + t * kTP + c] = suf[t];
+            }
+        }
+        sm[LY::GC + c] = gam[15];
     }
 }
 
+// A = strict_lower(diag(b) P) with P = KE KI^T, from one wave (lane holds
+// P[4 lg + i][lr]); the product's strictly lower part also kept in P_out if set.
+template <typename LY>
+__device__ __forceinline__ void chunk_A(float *sm, int lane, float *P_out) {
+    const int lr = lane & 15, lg = lane >> 4;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+        acc = bmm16(lds4(sm + LY::KE + lr * kTP + 16 * kb + 4 * lg), lds4(sm + LY::KI + lr * kTP + 16 * kb + 4 * lg), acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 4 * lg + i;
+        sm[LY::A + r * kSP + lr] = (r > lr) ? sm[LY::B + r] * acc[i] : 0.f;
+        if (P_out) P_out[r * kSP + lr] = (r > lr) ? acc[i] : 0.f;
+    }
+}
+
+// Column jc of X = (I + A)^-1 by forward substitution (A strictly lower), in
+// registers: x[i] = delta(i, jc) - sum_{m < i} A[i][m] x[m].
+__device__ __forceinline__ void inverse_column(const float *A, int jc, float (&x)[16]) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        float acc = (i == jc) ? 1.f : 0.f;
+#pragma unroll
+        for (int m = 0; m < i; ++m) acc = fmaf(-A[i * kSP + m], x[m], acc);
+        x[i] = acc;
+    }
+}
+
+// The sequence and chunk whose operands live in `slot` (chunk c of sequence n
+// is in slot cu[n] / 16 + n + c): the last n with cu[n] / 16 + n <= slot. False
+// for a slot no chunk uses.
+__device__ __forceinline__ bool slot_chunk(const int64_t *cu, int N, int64_t slot, int &n,
+                                           int64_t &c) {
+    int lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (cu[mid] / kCk + mid <= slot) lo = mid;
+        else hi = mid - 1;
+    }
+    n = lo;
+    c = slot - (cu[n] / kCk + n);
+    return c >= 0 && c < (cu[n + 1] - cu[n] + kCk - 1) / kCk;
+}
+
+// ---- per-chunk operand records --------------------------------------------------
+
+// One record per (chunk slot, value head), written by bwd_prep_kernel and copied
+// whole into LDS by the chunk-serial kernels (the LDS layout is the record's;
+// offsets in floats, [16][128] tiles at pitch 132, [16][16] at pitch 20):
+//   KE, KG, T = X diag(b), GC        (the checkpoint pass copies these, 19 KiB)
+//   QG, MT = lower(QG KI^T)^T, B     (the reverse pass copies all of it, 28 KiB)
+struct OpRec {
+    static constexpr int KE = 0, KG = KE + kTile, T = KG + kTile, GC = T + kSmall;
+    static constexpr int QG = GC + kHeadDim, MT = QG + kTile, B = MT + kSmall;
+    static constexpr int END = 7168;                     // 28 blocks of 1 KiB
+    static constexpr int CKPT_BLOCKS = 19;               // blocks holding KE, KG, T, GC
+};
+static_assert(OpRec::B + 16 <= OpRec::END && OpRec::GC + kHeadDim <= 256 * OpRec::CKPT_BLOCKS,
+              "record layout");
+static_assert(OpRec::QG % 4 == 0 && OpRec::T % 4 == 0 && OpRec::GC % 4 == 0, "16-byte aligned tiles");
+
+// LDS of bwd_prep_kernel: the record, then KI and A.
+struct PrepLds {
+    static constexpr int KE = OpRec::KE, KG = OpRec::KG, T = OpRec::T, GC = OpRec::GC;
+    static constexpr int QG = OpRec::QG, MT = OpRec::MT, B = OpRec::B;
+    static constexpr int KI = OpRec::END, A = KI + kTile, END = A + kSmall;
+    static constexpr size_t BYTES = (size_t)END * 4;
+};
+
+// One workgroup per (chunk slot, value head), chunk-parallel: the chunk's
+// transforms and decays (operands_phase1/2), A and M (waves 0 and 1, MFMA),
+// X = (I + A)^-1 (wave 0), T = X diag(b), then the record written out.
 template <typename Tin>
-__global__ __launch_bounds__(256) void bwd_ckpt_kernel(
-    const Tin *__restrict__ k, const Tin *__restrict__ v, const float *__restrict__ g,
-    const float *__restrict__ beta_raw, const float *__restrict__ A_log,
-    const float *__restrict__ dt_bias, float lb, const int64_t *__restrict__ cu, int N, int H,
-    int Hk, const float *__restrict__ h0, float *__restrict__ ckpt)
-{
-    int64_t nh;
-    int vb;
-    if (!bwd_block(blockIdx.x, (int64_t)N * H, nh, vb)) return;
-    const int n = (int)(nh / H), h = (int)(nh % H);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int j = lane & 15;
-    const int row = 4 * wave + (lane >> 4);          // state row within the block
-    const int gid = threadIdx.x >> 4;                // token slot of the per-chunk transforms
-    const int grow = vb * kBRows + row;
-    const int64_t s0 = cu[n], s1 = cu[n + 1];
-    const int64_t nck = (s1 - s0 + kCk - 1) / kCk;
-    const int64_t slot0 = s0 / kCk + n;
-
-    __shared__ float sKh[kCk][kHeadDim], sAl[kCk][kHeadDim];
-    __shared__ float sB[kCk], sV[kCk][kBRows];
-
-    float S[8];
-    if (h0) load_lane8(h0 + ((size_t)nh * kHeadDim + grow) * kHeadDim, j, S);
-    else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) S[e] = 0.f;
-    }
-    const float a_gate = fast_exp2(A_log[h] * kLog2e);
-    float dtb[8];
-    load_lane8(dt_bias + (size_t)h * kHeadDim, j, dtb);
-
-    // raw token data of the chunk's token `gid`, loaded one chunk ahead so that
-    // the loads of chunk c + 1 are in flight while chunk c runs
-    float kv[8], gv[8], braw = 0.f, vv = 0.f;
-    auto fetch = [&](int64_t c) {
-        const int64_t t = s0 + c * kCk + gid;
-        if (c < nck && t < s1) {
-            const size_t tb = ((size_t)t * H + h) * kHeadDim;
-            load_lane8(k + ((size_t)t * Hk + h / (H / Hk)) * kHeadDim, j, kv);
-            load_lane8(g + tb, j, gv);
-            braw = beta_raw[(size_t)t * H + h];
-            vv = to_f32(v[tb + vb * kBRows + j]);
-        }
-    };
-    fetch(0);
-    for (int64_t c = 0; c < nck; ++c) {
-        const int64_t c0 = s0 + c * kCk;
-        const int L = (int)(s1 - c0 < kCk ? s1 - c0 : kCk);
-        store_lane8(ckpt + (((size_t)(slot0 + c) * H + h) * kHeadDim + grow) * kHeadDim, j, S);
-        if (gid < L) {
-            float ss = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss = fmaf(kv[e], kv[e], ss);
-            const float rk = rsqrtf(row16_sum(ss) + kL2Eps);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                sKh[gid][chan(j, e)] = kv[e] * rk;
-                sAl[gid][chan(j, e)] = fast_exp2(lb * sigmoid_f(a_gate * (gv[e] + dtb[e])) * kLog2e);
-            }
-            if (j == 0) sB[gid] = sigmoid_f(braw);
-            sV[gid][j] = vv;
-        }
-        lds_barrier();
-        fetch(c + 1);
-        // unrolled so that each token's LDS reads are issued ahead of the
-        // previous token's dependency chain
-#pragma unroll
-        for (int i = 0; i < kCk; ++i) {
-            if (i < L) {
-                float kh[8], al[8];
-                load_lane8(&sKh[i][0], j, kh);
-                load_lane8(&sAl[i][0], j, al);
-                float p = 0.f;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) { S[e] *= al[e]; p = fmaf(S[e], kh[e], p); }
-                const float u = sB[i] * (sV[i][row] - row16_sum(p));
-#pragma unroll
-                for (int e = 0; e < 8; ++e) S[e] = fmaf(u, kh[e], S[e]);
-            }
-        }
-        lds_barrier();
-    }
-}
-
-// Forward step of one token on a state row (lane j's 8 channels); returns
-// w = v - S' kh for the row and updates S.
-__device__ __forceinline__ float fwd_row_step(float (&S)[8], const float *kh_row, const float *al_row,
-                                              int j, float b, float vv, float &u) {
-    float kh[8], al[8];
-    load_lane8(kh_row, j, kh);
-    load_lane8(al_row, j, al);
-    float p = 0.f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        S[e] *= al[e];
-        p = fmaf(S[e], kh[e], p);
-    }
-    const float w = vv - row16_sum(p);
-    u = b * w;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) S[e] = fmaf(u, kh[e], S[e]);
-    return w;
-}
-
-// Three workgroups per CU (at most 168 VGPRs and 53 KB of LDS each), so that
-// the 8 row blocks x heads of the benchmark shape are resident in one round.
-template <typename Tin, typename Tdo>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3))) void bwd_reverse_kernel(
-    const Tin *__restrict__ q, const Tin *__restrict__ k, const Tin *__restrict__ v,
-    const float *__restrict__ g, const float *__restrict__ beta_raw,
-    const float *__restrict__ A_log, const float *__restrict__ dt_bias, float scale, float lb,
-    const int64_t *__restrict__ cu, int N, int H, int Hk, const float *__restrict__ ckpt,
-    const Tdo *__restrict__ dout, const float *__restrict__ dht, float *__restrict__ dv,
-    float *__restrict__ part, float *__restrict__ dh0)
-{
-    constexpr int kSub = 8;            // states kept in registers at a time
-    constexpr int kFlush = 4;          // tokens per flush of the per-wave sums
-    int64_t nh;
-    int vb;
-    if (!bwd_block(blockIdx.x, (int64_t)N * H, nh, vb)) return;
-    const int n = (int)(nh / H), h = (int)(nh % H);
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int j = lane & 15;
-    const int row = 4 * wave + (lane >> 4);
-    const int gid = threadIdx.x >> 4;
-    const int grow = vb * kBRows + row;
-    const int64_t s0 = cu[n], s1 = cu[n + 1];
-    const int64_t nck = (s1 - s0 + kCk - 1) / kCk;
-    const int64_t slot0 = s0 / kCk + n;
-
-    __shared__ float sKh[kCk][kHeadDim], sQh[kCk][kHeadDim], sAl[kCk][kHeadDim];
-    __shared__ float sB[kCk], sV[kCk][kBRows], sDo[kCk][kBRows], sU[kCk][kBRows], sW[kCk][kBRows];
-    // per-wave sums (over the wave's 4 rows) of the partials of kFlush tokens
-    __shared__ float sRed[kFlush][4][kPartCols];
-
-    float dS[8];
-    if (dht) load_lane8(dht + ((size_t)nh * kHeadDim + grow) * kHeadDim, j, dS);
-    else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) dS[e] = 0.f;
-    }
-    const float a_gate = fast_exp2(A_log[h] * kLog2e);
-    float dtb[8];
-    load_lane8(dt_bias + (size_t)h * kHeadDim, j, dtb);
-
-    for (int64_t c = nck - 1; c >= 0; --c) {
-        const int64_t c0 = s0 + c * kCk;
-        const int L = (int)(s1 - c0 < kCk ? s1 - c0 : kCk);
-        const float *ck = ckpt + (((size_t)(slot0 + c) * H + h) * kHeadDim + grow) * kHeadDim;
-        if (gid < L) {
-            const int64_t t = c0 + gid;
-            const size_t tb = ((size_t)t * H + h) * kHeadDim;
-            const size_t tbk = ((size_t)t * Hk + h / (H / Hk)) * kHeadDim;
-            float kh[8], al[8], qv[8];
-            key_and_decay(k, g, dtb, a_gate, lb, tb, tbk, j, kh, al);
-            load_lane8(q + tbk, j, qv);
-            float ss = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) ss = fmaf(qv[e], qv[e], ss);
-            const float rq = rsqrtf(row16_sum(ss) + kL2Eps) * scale;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                sKh[gid][chan(j, e)] = kh[e];
-                sAl[gid][chan(j, e)] = al[e];
-                sQh[gid][chan(j, e)] = qv[e] * rq;
-            }
-            if (j == 0) sB[gid] = sigmoid_f(beta_raw[(size_t)t * H + h]);
-            sV[gid][j] = to_f32(v[tb + vb * kBRows + j]);
-            sDo[gid][j] = to_f32(dout[tb + vb * kBRows + j]);
-        }
-        lds_barrier();
-
-        // the chunk's two halves, last first: recompute the states before the
-        // half's tokens from the checkpoint (registers), then the reverse steps
-#pragma unroll 1
-        for (int half = 1; half >= 0; --half) {
-            const int i0 = half * kSub;
-            if (i0 < L) {
-                float S[8];
-                load_lane8(ck, j, S);
-#pragma unroll
-                for (int i = 0; i < kSub; ++i) {     // tokens before the half: states not kept
-                    if (i < i0) {
-                        float u;
-                        fwd_row_step(S, &sKh[i][0], &sAl[i][0], j, sB[i], sV[i][row], u);
-                    }
-                }
-                float snap[kSub][8];
-#pragma unroll
-                for (int ii = 0; ii < kSub; ++ii) {
-                    const int i = i0 + ii;
-                    if (i < L) {
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) snap[ii][e] = S[e];
-                        float u;
-                        const float w = fwd_row_step(S, &sKh[i][0], &sAl[i][0], j, sB[i], sV[i][row], u);
-                        if (j == 0) { sU[i][row] = u; sW[i][row] = w; }
-                    }
-                }
-#pragma unroll
-                for (int ii = kSub - 1; ii >= 0; --ii) {
-                    const int i = i0 + ii;
-                    if (i < L) {
-                        const int64_t t = c0 + i;
-                        float kh[8], al[8], qh[8];
-                        load_lane8(&sKh[i][0], j, kh);
-                        load_lane8(&sAl[i][0], j, al);
-                        load_lane8(&sQh[i][0], j, qh);
-                        const float b = sB[i], u = sU[i][row], w = sW[i][row], d_o = sDo[i][row];
-                        float sp[8], pq[8], pk[8], pa[8];
-                        float du = 0.f;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            sp[e] = snap[ii][e] * al[e];                 // S'
-                            pq[e] = d_o * fmaf(u, kh[e], sp[e]);        // do_v * S_t[v, :]
-                            dS[e] = fmaf(d_o, qh[e], dS[e]);
-                            du = fmaf(dS[e], kh[e], du);
-                        }
-                        du = row16_sum(du);
-                        const float bdu = b * du;
-#pragma unroll
-                        for (int e = 0; e < 8; ++e) {
-                            pk[e] = u * dS[e] - bdu * sp[e];
-                            const float dsp = fmaf(-bdu, kh[e], dS[e]);
-                            pa[e] = dsp * snap[ii][e];
-                            dS[e] = dsp * al[e];
-                        }
-                        const size_t tb = ((size_t)t * H + h) * kHeadDim;
-                        if (j == 0) dv[tb + grow] = bdu;
-                        // sums over the wave's 4 rows, kept per wave in LDS: each
-                        // quad_rows_sum leaves in row r the sum of its value at
-                        // offset qo = 0, 2, 1, 3 (rows 0..3), so every lane
-                        // stores one sum per quad
-                        float *red = &sRed[i % kFlush][wave][0];
-                        const float pb = rows4_sum(du * w);
-                        const int qo = (lane >> 4) == 1 ? 2 : ((lane >> 4) == 2 ? 1 : (lane >> 4));
-#pragma unroll
-                        for (int hq = 0; hq < 2; ++hq) {
-                            const int e0 = 4 * hq;
-                            const int cidx = 64 * hq + 4 * j + qo;          // chan(j, e0 + qo)
-                            red[cidx] = quad_rows_sum(pq[e0], pq[e0 + 1], pq[e0 + 2], pq[e0 + 3]);
-                            red[kHeadDim + cidx] = quad_rows_sum(pk[e0], pk[e0 + 1], pk[e0 + 2], pk[e0 + 3]);
-                            red[2 * kHeadDim + cidx] = quad_rows_sum(pa[e0], pa[e0 + 1], pa[e0 + 2], pa[e0 + 3]);
-                        }
-                        if (lane == 0) red[3 * kHeadDim] = pb;
-                        // after tokens i .. min(i + kFlush, L) - 1: add the 4
-                        // waves' sums and store the block's row sums
-                        if (i % kFlush == 0) {
-                            const int ntok = (L - i < kFlush) ? L - i : kFlush;
-                            lds_barrier();
-                            for (int idx = threadIdx.x; idx < ntok * kPartCols; idx += 256) {
-                                const int ti = idx / kPartCols, col = idx - ti * kPartCols;
-                                const float sum = (sRed[ti][0][col] + sRed[ti][1][col]) +
-                                                  (sRed[ti][2][col] + sRed[ti][3][col]);
-                                const size_t tt = (size_t)(c0 + i + ti);
-                                part[((tt * H + h) * kNVB + vb) * kPartCols + col] = sum;
-                            }
-                            lds_barrier();
-                        }
-                    }
-                }
-            }
-        }
-        lds_barrier();
-    }
-    if (dh0) store_lane8(dh0 + ((size_t)nh * kHeadDim + grow) * kHeadDim, j, dS);
-}
-
-// One DPP row per token, 16 tokens per workgroup, one q/k head per grid row:
-// the value heads that share the q/k head (grouped value heads) add their dqh
-// and dkh before the normalisations' chains; dg and dbeta are per value head.
-template <typename Tin>
-__global__ __launch_bounds__(256) void bwd_finalize_kernel(
+__global__ __launch_bounds__(256) void bwd_prep_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta_raw, const float *__restrict__ A_log,
-    const float *__restrict__ dt_bias, float scale, float lb, int64_t T, int H, int Hk,
-    const float *__restrict__ part, float *__restrict__ dq, float *__restrict__ dk,
-    float *__restrict__ dg, float *__restrict__ dbeta, float *__restrict__ pp)
+    const float *__restrict__ dt_bias, float scale, float lb, const int64_t *__restrict__ cu, int N,
+    int H, int Hk, float *__restrict__ ops)
 {
-    const int hk = blockIdx.y;
-    const int G = H / Hk;
-    const int64_t tblk = blockIdx.x;
-    const int j = threadIdx.x & 15, gid = threadIdx.x >> 4;
-    const int64_t t = tblk * 16 + gid;
-    const bool valid = t < T;
-    __shared__ float sP[16][kHeadDim + 1];
-
-    float dqh[8], dkh[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) { dqh[e] = 0.f; dkh[e] = 0.f; }
-    for (int gg = 0; gg < G; ++gg) {
-        const int h = hk * G + gg;
-        float dgv[8];
-        float cA = 0.f;
-        if (valid) {
-            const size_t tb = ((size_t)t * H + h) * kHeadDim;
-            const float *src = part + (size_t)((size_t)t * H + h) * kNVB * kPartCols;
-            float dal[8];
-            float db = 0.f;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) dal[e] = 0.f;
-#pragma unroll
-            for (int b = 0; b < kNVB; ++b) {
-                float x[8];
-                load_lane8(src + b * kPartCols, j, x);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) dqh[e] += x[e];
-                load_lane8(src + b * kPartCols + kHeadDim, j, x);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) dkh[e] += x[e];
-                load_lane8(src + b * kPartCols + 2 * kHeadDim, j, x);
-#pragma unroll
-                for (int e = 0; e < 8; ++e) dal[e] += x[e];
-                db += src[b * kPartCols + 3 * kHeadDim];
-            }
-            float gv[8], dtb[8];
-            load_lane8(g + tb, j, gv);
-            load_lane8(dt_bias + (size_t)h * kHeadDim, j, dtb);
-            const float a_gate = fast_exp2(A_log[h] * kLog2e);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float sg = sigmoid_f(a_gate * (gv[e] + dtb[e]));
-                const float al = fast_exp2(lb * sg * kLog2e);
-                dgv[e] = dal[e] * al * lb * sg * (1.0f - sg) * a_gate;
-                cA = fmaf(dgv[e], gv[e] + dtb[e], cA);
-            }
-            store_lane8(dg + tb, j, dgv);
-            cA = row16_sum(cA);
-            if (j == 0) {
-                const float bb = sigmoid_f(beta_raw[(size_t)t * H + h]);
-                dbeta[(size_t)t * H + h] = db * bb * (1.0f - bb);
-            }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) dgv[e] = 0.f;
-        }
-        // this value head's sums over the 16 tokens, for the parameters
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sP[gid][chan(j, e)] = dgv[e];
-        if (j == 0) sP[gid][kHeadDim] = cA;
-        lds_barrier();
-        if (threadIdx.x <= kHeadDim) {
-            float sum = 0.f;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) sum += sP[r][threadIdx.x];
-            pp[((size_t)tblk * H + h) * (kHeadDim + 1) + threadIdx.x] = sum;
-        }
-        lds_barrier();
+    using LY = PrepLds;
+    extern __shared__ __align__(16) float sm[];
+    const int64_t slot = blockIdx.x;
+    const int h = blockIdx.y;
+    int n;
+    int64_t c;
+    if (!slot_chunk(cu, N, slot, n, c)) return;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int lr = lane & 15, lg = lane >> 4, gid = tid >> 4, j = tid & 15;
+    const int64_t s1 = cu[n + 1], c0 = cu[n] + c * kCk;
+    const int L = (int)(s1 - c0 < kCk ? s1 - c0 : kCk);
+    const float a_gate = fast_exp2(A_log[h] * kLog2e);
+    float dtb[8];
+    load_lane8(dt_bias + (size_t)h * kHeadDim, j, dtb);
+    {
+        TokIn<Tin, true> tk;
+        tok_load(tk, q, k, g, beta_raw, c0, s1, H, Hk, h, gid, j);
+        operands_phase1<LY, true>(sm, tk, dtb, a_gate, lb, scale, L, gid, j);
     }
-    if (valid) {
-        const size_t tbk = ((size_t)t * Hk + hk) * kHeadDim;
-        float qv[8], kv[8];
-        load_lane8(q + tbk, j, qv);
-        load_lane8(k + tbk, j, kv);
-        float sq = 0.f, sk = 0.f, qd = 0.f, kd = 0.f;
+    lds_barrier();
+    operands_phase2<LY, true, false>(sm, tid);
+    lds_barrier();
+    if (wave == 0) chunk_A<LY>(sm, lane, nullptr);
+    if (wave == 1) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            sq = fmaf(qv[e], qv[e], sq);
-            sk = fmaf(kv[e], kv[e], sk);
-            qd = fmaf(qv[e], dqh[e], qd);
-            kd = fmaf(kv[e], dkh[e], kd);
-        }
-        sq = row16_sum(sq); sk = row16_sum(sk); qd = row16_sum(qd); kd = row16_sum(kd);
-        const float rq = rsqrtf(sq + kL2Eps), rk = rsqrtf(sk + kL2Eps);
-        const float cq = rq * rq * rq * qd, ck = rk * rk * rk * kd;
-        float dqo[8], dko[8];
+        for (int kb = 0; kb < 8; ++kb)
+            acc = bmm16(lds4(sm + LY::QG + lr * kTP + 16 * kb + 4 * lg), lds4(sm + LY::KI + lr * kTP + 16 * kb + 4 * lg), acc);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            dqo[e] = scale * (rq * dqh[e] - cq * qv[e]);
-            dko[e] = rk * dkh[e] - ck * kv[e];
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * lg + i;
+            sm[LY::MT + lr * kSP + r] = (r >= lr) ? acc[i] : 0.f;
         }
-        store_lane8(dq + tbk, j, dqo);
-        store_lane8(dk + tbk, j, dko);
+    }
+    lds_barrier();
+    if (wave == 0) {
+        float x[16];
+        inverse_column(sm + LY::A, lr, x);
+        if (lg == 0) {
+            const float bj = sm[LY::B + lr];
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sm[LY::T + i * kSP + lr] = x[i] * bj;
+        }
+    }
+    lds_barrier();
+    f32x4 *dst = (f32x4 *)(ops + ((size_t)slot * H + h) * OpRec::END);
+#pragma unroll
+    for (int r = 0; r < OpRec::END / 1024; ++r) dst[tid + 256 * r] = lds4(sm + 4 * (tid + 256 * r));
+}
+
+// DMA copy of blocks [0, nblk) of a record into LDS: wave w copies the 1 KiB
+// blocks w, w + 4, ... (completion tracked by vmcnt; readers wait, then a barrier).
+template <int NBLK>
+__device__ __forceinline__ void copy_record(const float *rec, float *lds, int wave, int lane) {
+    const i32x4 r = make_rsrc(rec, (uint32_t)(OpRec::END * 4));
+#pragma unroll
+    for (int b = 0; b < (NBLK + 3) / 4; ++b) {
+        const int blk = 4 * b + wave;
+        if (4 * b + 3 < NBLK || blk < NBLK)
+            copy16_to_lds(r, 16u * (uint32_t)lane, 1024u * (uint32_t)blk, lds + 256 * blk);
     }
 }
+
+// Wait until at most N of this wave's vector memory operations are in flight
+// (they complete in issue order): N is split over the two vmcnt fields.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 0xF) | ((N >> 4) << 14));
+    asm volatile("" ::: "memory");
+}
+
+// ---- forward checkpoints ------------------------------------------------------
+
+// The state of 16 rows per wave in registers as the transposed accumulator
+// tiles Sa[kb][i] = S[vbase + lr][16 kb + 4 lg + i]; per chunk: the checkpoint,
+// R = V - KE S^T, U = T R, S^T <- diag(GC) S^T + KG^T U, with the next chunk's
+// operands copied into the other LDS buffer meanwhile.
+template <typename Tin>
+__global__ __launch_bounds__(256) void bwd_ckpt_kernel(
+    const Tin *__restrict__ v, const float *__restrict__ ops, const int64_t *__restrict__ cu,
+    int N, int H, const float *__restrict__ h0, float *__restrict__ ckpt)
+{
+    constexpr int BUF = 256 * OpRec::CKPT_BLOCKS;
+    extern __shared__ __align__(16) float sm[];
+    int64_t nh;
+    int half;
+    if (!half_block(blockIdx.x, (int64_t)N * H, nh, half)) return;
+    const int n = (int)(nh / H), h = (int)(nh % H);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    const int vbase = 64 * half + 16 * wave;
+    const int64_t s0 = cu[n], s1 = cu[n + 1];
+    const int64_t nch = (s1 - s0 + kCk - 1) / kCk;
+    const int64_t slot0 = s0 / kCk + n;
+    const float *rec0 = ops + ((size_t)slot0 * H + h) * OpRec::END;
+    const size_t rec_step = (size_t)H * OpRec::END;
+
+    f32x4 Sa[8];
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+        Sa[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (h0) Sa[kb] = *(const f32x4 *)(h0 + ((size_t)nh * kHeadDim + vbase + lr) * kHeadDim + 16 * kb + 4 * lg);
+    }
+    if (nch == 0) return;
+    // v[t = 4 lg + i][vbase + lr] of one chunk, loaded one chunk ahead
+    // (tokens past the sequence end read its last token, masked where used)
+    Tin vb[4];
+    auto fetch_v = [&](int64_t c) {
+        const int64_t c0 = s0 + c * kCk;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int64_t t = c0 + 4 * lg + i < s1 ? c0 + 4 * lg + i : s1 - 1;
+            vb[i] = v[((size_t)t * H + h) * kHeadDim + vbase + lr];
+        }
+    };
+    copy_record<OpRec::CKPT_BLOCKS>(rec0, sm, wave, lane);
+    fetch_v(0);
+    wait_vmem_le<0>();
+    lds_barrier();
+    for (int64_t c = 0; c < nch; ++c) {
+        const float *OP = sm + (c & 1) * BUF;
+        const int64_t c0 = s0 + c * kCk;
+        const int L = (int)(s1 - c0 < kCk ? s1 - c0 : kCk);
+        f32x4 Vb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) Vb[i] = 4 * lg + i < L ? (float)vb[i] : 0.f;
+        // the next chunk's operands (the last chunk's again at the end) and v
+        const int64_t cn = c + 1 < nch ? c + 1 : c;
+        copy_record<OpRec::CKPT_BLOCKS>(rec0 + cn * rec_step, sm + ((c + 1) & 1) * BUF, wave, lane);
+        fetch_v(cn);
+        float *ck = ckpt + ((size_t)(slot0 + c) * H + h) * kHeadDim * kHeadDim;
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+            *(f32x4 *)(ck + (size_t)(vbase + lr) * kHeadDim + 16 * kb + 4 * lg) = Sa[kb];
+        f32x4 R = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+            R = bmm16(lds4(OP + OpRec::KE + lr * kTP + 16 * kb + 4 * lg), Sa[kb], R);
+        R = Vb - R;
+        const f32x4 U = bmm16(lds4(OP + OpRec::T + lr * kSP + 4 * lg), R, f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+            Sa[kb] = bmm16(lds4col(OP + OpRec::KG + (4 * lg) * kTP + 16 * kb + lr, kTP), U,
+                           Sa[kb] * lds4(OP + OpRec::GC + 16 * kb + 4 * lg));
+        // the copy and the v loads landed (the 8 checkpoint stores may still be in flight)
+        wait_vmem_le<8>();
+        lds_barrier();
+    }
+}
+
+// ---- reverse pass -------------------------------------------------------------
+
+// LDS of bwd_chunk_kernel: two record buffers; dS1 of the workgroup's 64 state
+// rows [64][132]; and, for those rows, U, dR (row layouts), dU, R and dO
+// ([t][v] at pitch 68), shared so that each wave can form the partial sums of
+// its own 32 key columns over all 64 rows.
+struct ChunkLds {
+    static constexpr int SP = 68;
+    static constexpr int REC = 0, DS1 = 2 * OpRec::END;
+    static constexpr int US = DS1 + 64 * kTP, DRS = US + 16 * SP, DUS = DRS + 16 * SP;
+    static constexpr int RS = DUS + 16 * SP, DOS = RS + 16 * SP, END = DOS + 16 * SP;
+    static constexpr size_t BYTES = (size_t)END * 4;
+};
+static_assert(ChunkLds::BYTES <= 160 * 1024, "LDS budget");
+
+// The wave's inputs for one chunk: its own 16 state rows of S0 (row operand),
+// the column operand of S0 over the workgroup's 64 rows and the wave's 32 key
+// columns, dO and v of its rows.
+template <typename Tin, typename Tdo>
+struct ChainIn {
+    f32x4 S0a[8];          // S0[vbase + lr][16 kb + 4 lg + i]
+    f32x4 S0s[8];          // [2 vb + kt]: S0[64 half + 16 vb + 4 lg + i][32 wave + 16 kt + lr]
+    vec4<Tdo> dOa;         // dO[t = lr][vbase + 4 lg + i]
+    Tdo dOb[4];            // dO[t = 4 lg + i][vbase + lr]
+    Tin Vb[4];             // v[t = 4 lg + i][vbase + lr]
+};
+
+// Unconditional loads: tokens past the sequence end read its last token (masked where used).
+template <typename Tin, typename Tdo>
+__device__ __forceinline__ void chain_load(ChainIn<Tin, Tdo> &r, const float *ckpt, const Tdo *dout,
+                                           const Tin *v, int64_t slot, int64_t c0, int64_t s1,
+                                           int H, int h, int half, int wave, int lr, int lg) {
+    const int vbase = 64 * half + 16 * wave;
+    const float *ck = ckpt + ((size_t)slot * H + h) * kHeadDim * kHeadDim;
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb)
+        r.S0a[kb] = *(const f32x4 *)(ck + (size_t)(vbase + lr) * kHeadDim + 16 * kb + 4 * lg);
+#pragma unroll
+    for (int vb = 0; vb < 4; ++vb)
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                r.S0s[2 * vb + kt][i] = ck[(size_t)(64 * half + 16 * vb + 4 * lg + i) * kHeadDim + 32 * wave + 16 * kt + lr];
+    auto tok = [&](int t) { return c0 + t < s1 ? c0 + t : s1 - 1; };
+    r.dOa = *(const vec4<Tdo> *)(dout + ((size_t)tok(lr) * H + h) * kHeadDim + vbase + 4 * lg);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const size_t o = ((size_t)tok(4 * lg + i) * H + h) * kHeadDim + vbase + lr;
+        r.dOb[i] = dout[o];
+        r.Vb[i] = v[o];
+    }
+}
+
+template <typename Tin, typename Tdo>
+__global__ __launch_bounds__(256) void bwd_chunk_kernel(
+    const Tin *__restrict__ v, const float *__restrict__ ops, const int64_t *__restrict__ cu,
+    int N, int H, const float *__restrict__ ckpt, const Tdo *__restrict__ dout,
+    const float *__restrict__ dht, float *__restrict__ dv, float *__restrict__ part,
+    float *__restrict__ dh0)
+{
+    using LY = ChunkLds;
+    extern __shared__ __align__(16) float sm[];
+    int64_t nh;
+    int half;
+    if (!half_block(blockIdx.x, (int64_t)N * H, nh, half)) return;
+    const int n = (int)(nh / H), h = (int)(nh % H);
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const int lr = lane & 15, lg = lane >> 4;
+    const int vloc = 16 * wave, vbase = 64 * half + vloc;   // this wave's state rows
+    const int kcol = 32 * wave;                              // its key columns of the partials
+    const int64_t s0 = cu[n], s1 = cu[n + 1];
+    const int64_t nch = (s1 - s0 + kCk - 1) / kCk;
+    const int64_t slot0 = s0 / kCk + n;
+    const float *rec0 = ops + ((size_t)slot0 * H + h) * OpRec::END;
+    const size_t rec_step = (size_t)H * OpRec::END;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+    // dSa[kb]: the adjoint of the state after the current chunk, dS[vbase + lr][16 kb + 4 lg + i]
+    f32x4 dSa[8];
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) {
+        dSa[kb] = zero;
+        if (dht) dSa[kb] = *(const f32x4 *)(dht + ((size_t)nh * kHeadDim + vbase + lr) * kHeadDim + 16 * kb + 4 * lg);
+    }
+
+    // Every input of a chunk is loaded while the chunk after it runs: its
+    // record into the other LDS buffer, the state rows, dO and v alternately
+    // into two register sets (the loop is unrolled twice, so no register copy
+    // of a load in flight is ever needed).
+    ChainIn<Tin, Tdo> bufA, bufB;
+    auto chunk = [&](int64_t c, const ChainIn<Tin, Tdo> &cur, ChainIn<Tin, Tdo> &nxt, int rb)
+        __attribute__((always_inline)) {
+        const float *OP = sm + LY::REC + rb * OpRec::END;
+        const int64_t c0 = s0 + c * kCk;
+        const int L = (int)(s1 - c0 < kCk ? s1 - c0 : kCk);
+        {   // the chunk before (chunk 0 again in the last pass: the loads stay unconditional)
+            const int64_t cp = c > 0 ? c - 1 : 0;
+            copy_record<OpRec::END / 256>(rec0 + cp * rec_step, sm + LY::REC + (rb ^ 1) * OpRec::END, wave, lane);
+            chain_load(nxt, ckpt, dout, v, slot0 + cp, s0 + cp * kCk, s1, H, h, half, wave, lr, lg);
+        }
+        f32x4 Vf, dOb, dOa = f4<Tdo>(cur.dOa);
+        if (lr >= L) dOa = zero;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool in = 4 * lg + i < L;
+            Vf[i] = in ? (float)cur.Vb[i] : 0.f;
+            dOb[i] = in ? (float)cur.dOb[i] : 0.f;
+        }
+        // R = V - KE S0^T and KG dS1^T ([t][v] accumulators); dS1 shared
+        f32x4 R = zero, dUk = zero;
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) {
+            R = bmm16(lds4(OP + OpRec::KE + lr * kTP + 16 * kb + 4 * lg), cur.S0a[kb], R);
+            dUk = bmm16(lds4(OP + OpRec::KG + lr * kTP + 16 * kb + 4 * lg), dSa[kb], dUk);
+            *(f32x4 *)(sm + LY::DS1 + (vloc + lr) * kTP + 16 * kb + 4 * lg) = dSa[kb];
+        }
+        R = Vf - R;
+        // dS <- dS1 diag(GC) + QG^T dO
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+            dSa[kb] = bmm16(lds4col(OP + OpRec::QG + (4 * lg) * kTP + 16 * kb + lr, kTP), dOb,
+                            dSa[kb] * lds4(OP + OpRec::GC + 16 * kb + 4 * lg));
+        // U in row layout (the accumulator of U^T = R^T T^T); dU = M^T dO + KG dS1^T;
+        // dR = T^T dU (= dv) and its row layout (the accumulator of dR^T = dU^T T)
+        const f32x4 Trow = lds4(OP + OpRec::T + lr * kSP + 4 * lg);
+        const f32x4 Tcol = lds4col(OP + OpRec::T + (4 * lg) * kSP + lr, kSP);
+        const f32x4 Ua = bmm16(R, Trow, zero);
+        const f32x4 dU = bmm16(lds4col(OP + OpRec::MT + lr * kSP + 4 * lg, 1), dOb, dUk);
+        const f32x4 ndR = -bmm16(Tcol, dU, zero);
+        const f32x4 ndRa = -bmm16(dU, Tcol, zero);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            if (4 * lg + i < L) dv[((size_t)(c0 + 4 * lg + i) * H + h) * kHeadDim + vbase + lr] = -ndR[i];
+        // dS0^T = ... - KE^T dR
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+            dSa[kb] = bmm16(lds4col(OP + OpRec::KE + (4 * lg) * kTP + 16 * kb + lr, kTP), ndR, dSa[kb]);
+        // this wave's rows of U, -dR (row layouts), dU, R, dO ([t][v]) shared
+        *(f32x4 *)(sm + LY::US + lr * LY::SP + vloc + 4 * lg) = Ua;
+        *(f32x4 *)(sm + LY::DRS + lr * LY::SP + vloc + 4 * lg) = ndRa;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int o = (4 * lg + i) * LY::SP + vloc + lr;
+            sm[LY::DUS + o] = dU[i];
+            sm[LY::RS + o] = R[i];
+            sm[LY::DOS + o] = dOb[i];
+        }
+        lds_barrier();
+
+        // partials of key columns kcol .. kcol + 31, summed over the 64 rows:
+        // dQG = dO S0, dKG = U dS1, dKE = -dR S0 ([t][k] accumulators), dGC = sum_v S0 dS1
+        f32x4 pq[2] = {zero, zero}, pk[2] = {zero, zero}, pe[2] = {zero, zero};
+        float gs[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+        for (int vb = 0; vb < 4; ++vb) {
+            const f32x4 a_do = lds4(sm + LY::DOS + lr * LY::SP + 16 * vb + 4 * lg);
+            const f32x4 a_u = lds4(sm + LY::US + lr * LY::SP + 16 * vb + 4 * lg);
+            const f32x4 a_dr = lds4(sm + LY::DRS + lr * LY::SP + 16 * vb + 4 * lg);
+#pragma unroll
+            for (int kt = 0; kt < 2; ++kt) {
+                const f32x4 s0c = cur.S0s[2 * vb + kt];
+                const f32x4 ds1c = lds4col(sm + LY::DS1 + (16 * vb + 4 * lg) * kTP + kcol + 16 * kt + lr, kTP);
+                pq[kt] = bmm16(a_do, s0c, pq[kt]);
+                pk[kt] = bmm16(a_u, ds1c, pk[kt]);
+                pe[kt] = bmm16(a_dr, s0c, pe[kt]);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gs[kt][i] = fmaf(s0c[i], ds1c[i], gs[kt][i]);
+            }
+        }
+        float *dst = part + (((size_t)(slot0 + c) * H + h) * 2 + half) * kPartRec;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int o = (4 * lg + i) * kHeadDim + kcol + 16 * kt + lr;
+                dst[o] = pq[kt][i];
+                dst[2048 + o] = pk[kt][i];
+                dst[4096 + o] = pe[kt][i];
+            }
+        // dGC: the 16 rows 4 lg + i of each block summed over i, then over the four lane groups
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt) {
+            float x = (gs[kt][0] + gs[kt][1]) + (gs[kt][2] + gs[kt][3]);
+            const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+            x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+            const auto b2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+            x = __uint_as_float(b2[0]) + __uint_as_float(b2[1]);
+            if (lg == 0) dst[6656 + kcol + 16 * kt + lr] = x;
+        }
+        // dM = lower(dO U^T) (wave 0) and dT = dU R^T (wave 1) over the 64 rows
+        if (wave < 2) {
+            const int A_ = wave == 0 ? LY::DOS : LY::DUS, B_ = wave == 0 ? LY::US : LY::RS;
+            f32x4 acc = zero;
+#pragma unroll
+            for (int vb = 0; vb < 4; ++vb)
+                acc = bmm16(lds4(sm + A_ + lr * LY::SP + 16 * vb + 4 * lg), lds4(sm + B_ + lr * LY::SP + 16 * vb + 4 * lg), acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int r = 4 * lg + i;
+                dst[(wave == 0 ? 6144 : 6400) + r * 16 + lr] = (wave == 1 || r >= lr) ? acc[i] : 0.f;
+            }
+        }
+        // the next record and the chain loads landed (this chunk's partial
+        // stores, at least 24 per wave, may still be in flight); then the
+        // buffers and the shared rows are free for the next chunk
+        wait_vmem_le<24>();
+        lds_barrier();
+    };
+    int64_t c = nch - 1;
+    if (c >= 0) {
+        copy_record<OpRec::END / 256>(rec0 + c * rec_step, sm + LY::REC, wave, lane);
+        chain_load(bufA, ckpt, dout, v, slot0 + c, s0 + c * kCk, s1, H, h, half, wave, lr, lg);
+        wait_vmem_le<0>();
+        lds_barrier();
+    }
+    while (c >= 0) {
+        chunk(c, bufA, bufB, 0);
+        if (--c < 0) break;
+        chunk(c, bufB, bufA, 1);
+        --c;
+    }
+    if (dh0) {
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb)
+            *(f32x4 *)(dh0 + ((size_t)nh * kHeadDim + vbase + lr) * kHeadDim + 16 * kb + 4 * lg) = dSa[kb];
+    }
+}
+
+// LDS of bwd_chunk_final_kernel. GAM and SUF hold the decay products up to and
+// after each token, DG the per-token log-decay adjoint, EK dKG * KG and then
+// the per-token gate gradients (SP).
+struct FinalLds {
+    static constexpr int KE = 0, QG = KE + kTile, KG = QG + kTile, KI = KG + kTile;
+    static constexpr int SUF = KI + kTile, DG = SUF + kTile, GAM = DG + kTile, EK = GAM + kTile;
+    static constexpr int SP = EK;
+    static constexpr int A = EK + kTile, P = A + kSmall, X = P + kSmall, DM = X + kSmall;
+    static constexpr int DT = DM + kSmall, Y = DT + kSmall, DA = Y + kSmall;
+    static constexpr int GC = DA + kSmall, DGC = GC + kHeadDim, B = DGC + kHeadDim;
+    static constexpr int END = B + 16;
+    static constexpr size_t BYTES = (size_t)END * 4;
+};
+static_assert(FinalLds::BYTES <= 80 * 1024, "two workgroups per CU");
 
 // ddt_bias[h, c] = sum over tokens of dg; dA_log[h] = sum over tokens and
 // channels of dg * (g + dt_bias): the per-16-token sums added in token order,
@@ -522,31 +746,299 @@ __global__ __launch_bounds__(256) void bwd_param_kernel(const float *__restrict_
     }
 }
 
+// One workgroup per (chunk slot, q/k head): the value heads that share the
+// q/k head (grouped value heads) run one after the other and add their dqh and
+// dkh before the normalisations' chains. Per value head: the operands again
+// (the same code as bwd_chunk_kernel, so the same P and X), the two halves'
+// partials added, the small-matrix adjoints (dX, dA, dP, dbeta), then per
+// token row dKE, dQG, dKI, dkh, dqh and the log-decay adjoint, its reverse sum
+// over the chunk (a thread per channel), and the gate's chain.
+template <typename Tin>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void bwd_chunk_final_kernel(
+    const Tin *__restrict__ q, const Tin *__restrict__ k, const float *__restrict__ g,
+    const float *__restrict__ beta_raw, const float *__restrict__ A_log,
+    const float *__restrict__ dt_bias, float scale, float lb, const int64_t *__restrict__ cu, int N,
+    int H, int Hk, const float *__restrict__ part, float *__restrict__ dq, float *__restrict__ dk,
+    float *__restrict__ dg, float *__restrict__ dbeta, float *__restrict__ pp)
+{
+    using LY = FinalLds;
+    extern __shared__ __align__(16) float sm[];
+    const int64_t slot = blockIdx.x;
+    const int hk = blockIdx.y, G = H / Hk;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int gid = tid >> 4, j = tid & 15;
+    constexpr int NC = kHeadDim + 1;
+
+    int n;
+    int64_t c;
+    if (!slot_chunk(cu, N, slot, n, c)) {
+        // a slot no chunk uses: its parameter sums are zero
+        for (int gg = 0; gg < G; ++gg)
+            for (int col = tid; col < NC; col += 256) pp[((size_t)slot * H + hk * G + gg) * NC + col] = 0.f;
+        return;
+    }
+    const int64_t s0 = cu[n], s1 = cu[n + 1];
+    const int64_t c0 = s0 + c * kCk;
+    const int L = (int)(s1 - c0 < kCk ? s1 - c0 : kCk);
+
+    float dqh[8], dkh[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) { dqh[e] = 0.f; dkh[e] = 0.f; }
+    for (int gg = 0; gg < G; ++gg) {
+        const int h = hk * G + gg;
+        // the thread index taken as new in each pass, so that the many per-thread
+        // LDS offsets below are formed where they are used instead of being kept
+        // live (and spilled) across the loop
+        int tid = threadIdx.x;
+        asm volatile("" : "+v"(tid));
+        const int lane = tid & 63, gid = tid >> 4, j = tid & 15;
+        const float a_gate = fast_exp2(A_log[h] * kLog2e);
+        float dtb[8];
+        load_lane8(dt_bias + (size_t)h * kHeadDim, j, dtb);
+        // the two halves' partials (issued before the operands are formed)
+        const float *p0 = part + ((size_t)slot * H + h) * 2 * kPartRec, *p1 = p0 + kPartRec;
+        float pq[8], pk[8], pe[8];
+        {
+            float x0[8], x1[8];
+            load_lane8(p0 + gid * kHeadDim, j, x0);
+            load_lane8(p1 + gid * kHeadDim, j, x1);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pq[e] = x0[e] + x1[e];
+            load_lane8(p0 + 2048 + gid * kHeadDim, j, x0);
+            load_lane8(p1 + 2048 + gid * kHeadDim, j, x1);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pk[e] = x0[e] + x1[e];
+            load_lane8(p0 + 4096 + gid * kHeadDim, j, x0);
+            load_lane8(p1 + 4096 + gid * kHeadDim, j, x1);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) pe[e] = x0[e] + x1[e];
+        }
+        const float dMv = p0[6144 + tid] + p1[6144 + tid];
+        const float dTv = p0[6400 + tid] + p1[6400 + tid];
+        const float dGCv = tid < kHeadDim ? p0[6656 + tid] + p1[6656 + tid] : 0.f;
+
+        {
+            TokIn<Tin, true> tk;
+            tok_load(tk, q, k, g, beta_raw, c0, s1, H, Hk, h, gid, j);
+            operands_phase1<LY, true>(sm, tk, dtb, a_gate, lb, scale, L, gid, j);
+            lds_barrier();
+            operands_phase2<LY, true, true>(sm, tid);
+            lds_barrier();
+        }
+        sm[LY::DM + gid * kSP + j] = dMv;
+        sm[LY::DT + gid * kSP + j] = dTv;
+        if (tid < kHeadDim) sm[LY::DGC + tid] = dGCv;
+        if (wave == 0) chunk_A<LY>(sm, lane, sm + LY::P);
+        lds_barrier();
+        if (wave == 0 && lane < 16) {
+            float x[16];
+            inverse_column(sm + LY::A, lane, x);
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sm[LY::X + i * kSP + lane] = x[i];
+        }
+        lds_barrier();
+        // Y = dX X^T with dX = dT diag(b)
+        {
+            float y = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 16; ++jj)
+                y = fmaf(sm[LY::DT + gid * kSP + jj] * sm[LY::B + jj], sm[LY::X + j * kSP + jj], y);
+            sm[LY::Y + gid * kSP + j] = y;
+        }
+        lds_barrier();
+        // dA = strict_lower(-X^T Y)
+        {
+            float d = 0.f;
+            if (gid > j) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) d = fmaf(sm[LY::X + i * kSP + gid], sm[LY::Y + i * kSP + j], d);
+                d = -d;
+            }
+            sm[LY::DA + gid * kSP + j] = d;
+        }
+        lds_barrier();
+        if (tid < 16) {
+            // db_t = sum_i X[i][t] dT[i][t] + sum_{m < t} dA[t][m] P[t][m]
+            const int t = tid;
+            float db = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) db = fmaf(sm[LY::X + i * kSP + t], sm[LY::DT + i * kSP + t], db);
+#pragma unroll
+            for (int m = 0; m < 16; ++m) db = fmaf(sm[LY::DA + t * kSP + m], sm[LY::P + t * kSP + m], db);
+            if (t < L) {
+                const float bb = sm[LY::B + t];
+                dbeta[(size_t)(c0 + t) * H + h] = db * bb * (1.0f - bb);
+            }
+        }
+        // token row gid: dKE = dKE_p + dP KI, dQG = dQG_p + dM KI, dKI = dP^T KE + dM^T QG
+        // with dP = diag(b) dA
+        float dke[8], dqg[8], dki[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { dke[e] = pe[e]; dqg[e] = pq[e]; dki[e] = 0.f; }
+        {
+            const float bt = sm[LY::B + gid];
+#pragma unroll 2
+            for (int jj = 0; jj < 16; ++jj) {
+                const float dp = bt * sm[LY::DA + gid * kSP + jj];
+                const float dm = sm[LY::DM + gid * kSP + jj];
+                const float dpT = sm[LY::B + jj] * sm[LY::DA + jj * kSP + gid];
+                const float dmT = sm[LY::DM + jj * kSP + gid];
+                float ki[8], ke[8], qg[8];
+                load_lane8(sm + LY::KI + jj * kTP, j, ki);
+                load_lane8(sm + LY::KE + jj * kTP, j, ke);
+                load_lane8(sm + LY::QG + jj * kTP, j, qg);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    dke[e] = fmaf(dp, ki[e], dke[e]);
+                    dqg[e] = fmaf(dm, ki[e], dqg[e]);
+                    dki[e] = fmaf(dpT, ke[e], fmaf(dmT, qg[e], dki[e]));
+                }
+            }
+        }
+        {
+            float gam[8], suf[8], ke[8], qg[8], ki[8], kg[8], dgp[8], ek[8];
+            load_lane8(sm + LY::GAM + gid * kTP, j, gam);
+            load_lane8(sm + LY::SUF + gid * kTP, j, suf);
+            load_lane8(sm + LY::KE + gid * kTP, j, ke);
+            load_lane8(sm + LY::QG + gid * kTP, j, qg);
+            load_lane8(sm + LY::KI + gid * kTP, j, ki);
+            load_lane8(sm + LY::KG + gid * kTP, j, kg);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                dkh[e] += dke[e] * gam[e] + pk[e] * suf[e] + dki[e] / gam[e];
+                dqh[e] = fmaf(dqg[e], gam[e], dqh[e]);
+                dgp[e] = dke[e] * ke[e] + dqg[e] * qg[e] - dki[e] * ki[e];
+                ek[e] = pk[e] * kg[e];
+            }
+            store_lane8(sm + LY::DG + gid * kTP, j, dgp);
+            store_lane8(sm + LY::EK + gid * kTP, j, ek);
+        }
+        lds_barrier();
+        if (tid < kHeadDim) {
+            // dlambda_t = sum_{s >= t} DG_s + sum_{s < t} dKG_s KG_s + GC dGC
+            const int cc = tid;
+            float dgs[16], suffix[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) dgs[t] = sm[LY::DG + t * kTP + cc];
+            float run = 0.f;
+#pragma unroll
+            for (int t = 15; t >= 0; --t) { run += dgs[t]; suffix[t] = run; }
+            const float base = sm[LY::GC + cc] * sm[LY::DGC + cc];
+            float pre = 0.f;
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                sm[LY::DG + t * kTP + cc] = (suffix[t] + pre) + base;
+                pre += sm[LY::EK + t * kTP + cc];
+            }
+        }
+        lds_barrier();
+        float dgv[8];
+        float cA = 0.f;
+        if (gid < L) {
+            const size_t tb = ((size_t)(c0 + gid) * H + h) * kHeadDim;
+            float gv[8], dl[8];
+            load_lane8(g + tb, j, gv);
+            load_lane8(sm + LY::DG + gid * kTP, j, dl);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float sg = sigmoid_f(a_gate * (gv[e] + dtb[e]));
+                dgv[e] = dl[e] * lb * sg * (1.0f - sg) * a_gate;
+                cA = fmaf(dgv[e], gv[e] + dtb[e], cA);
+            }
+            store_lane8(dg + tb, j, dgv);
+            cA = row16_sum(cA);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) dgv[e] = 0.f;
+        }
+        // this value head's sums over the chunk's tokens, for the parameters
+        store_lane8(sm + LY::SP + gid * kTP, j, dgv);
+        if (j == 0) sm[LY::SP + gid * kTP + kHeadDim] = cA;
+        lds_barrier();
+        if (tid < NC) {
+            float sum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum += sm[LY::SP + r * kTP + tid];
+            pp[((size_t)slot * H + h) * NC + tid] = sum;
+        }
+        lds_barrier();
+    }
+    if (gid < L) {
+        const size_t tbk = ((size_t)(c0 + gid) * Hk + hk) * kHeadDim;
+        float qv[8], kv[8];
+        load_lane8(q + tbk, j, qv);
+        load_lane8(k + tbk, j, kv);
+        float sq = 0.f, sk = 0.f, qd = 0.f, kd = 0.f;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            sq = fmaf(qv[e], qv[e], sq);
+            sk = fmaf(kv[e], kv[e], sk);
+            qd = fmaf(qv[e], dqh[e], qd);
+            kd = fmaf(kv[e], dkh[e], kd);
+        }
+        sq = row16_sum(sq); sk = row16_sum(sk); qd = row16_sum(qd); kd = row16_sum(kd);
+        const float rq = rsqrtf(sq + kL2Eps), rk = rsqrtf(sk + kL2Eps);
+        const float cq = rq * rq * rq * qd, ck = rk * rk * rk * kd;
+        float dqo[8], dko[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            dqo[e] = scale * (rq * dqh[e] - cq * qv[e]);
+            dko[e] = rk * dkh[e] - ck * kv[e];
+        }
+        store_lane8(dq + tbk, j, dqo);
+        store_lane8(dk + tbk, j, dko);
+    }
+}
+
+// One flag word per kernel: bit d set once its dynamic-LDS limit is set on device d.
+hipError_t set_lds_limit(const void *fn, int lds, std::atomic<uint64_t> &done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t)1 << dev : 0;
+    if (bit && (done.load(std::memory_order_relaxed) & bit)) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_relaxed);
+    return e;
+}
+
 template <typename Tin, typename Tdo>
 hipError_t launch_backward_t(const BackwardArgs &a) {
     const int Hk = a.Hk > 0 ? a.Hk : a.H;   // q/k heads (grouped value heads)
     const int64_t NH = (int64_t)a.N * a.H;
-    const unsigned grid = (unsigned)(((NH + 7) / 8) * 64);
-    bwd_ckpt_kernel<Tin><<<grid, 256, 0, a.stream>>>(
-        (const Tin *)a.k, (const Tin *)a.v, a.g, a.beta_raw, a.A_log, a.dt_bias, a.lower_bound,
-        a.cu, a.N, a.H, Hk, a.h0, a.ckpt);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    bwd_reverse_kernel<Tin, Tdo><<<grid, 256, 0, a.stream>>>(
-        (const Tin *)a.q, (const Tin *)a.k, (const Tin *)a.v, a.g, a.beta_raw, a.A_log,
-        a.dt_bias, a.scale, a.lower_bound, a.cu, a.N, a.H, Hk, a.ckpt, (const Tdo *)a.dout, a.dht,
-        a.dv, a.part, a.dh0);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const int64_t ntb = (a.T + 15) / 16;
-    if (ntb > 0) {
-        bwd_finalize_kernel<Tin><<<dim3((unsigned)ntb, (unsigned)Hk), 256, 0, a.stream>>>(
+    const int64_t slots = num_slots(a.T, a.N, kCk);
+    const unsigned grid = (unsigned)(((NH + 7) / 8) * 16);
+    hipError_t e = hipSuccess;
+    if (slots > 0) {
+        bwd_prep_kernel<Tin><<<dim3((unsigned)slots, (unsigned)a.H), 256, PrepLds::BYTES, a.stream>>>(
             (const Tin *)a.q, (const Tin *)a.k, a.g, a.beta_raw, a.A_log, a.dt_bias, a.scale,
-            a.lower_bound, a.T, a.H, Hk, a.part, a.dq, a.dk, a.dg, a.dbeta, a.pp);
+            a.lower_bound, a.cu, a.N, a.H, Hk, a.ops);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    bwd_param_kernel<<<(unsigned)a.H, 256, 0, a.stream>>>(a.pp, ntb, a.H, a.dA_log, a.ddt_bias);
+    bwd_ckpt_kernel<Tin><<<grid, 256, 2 * 256 * OpRec::CKPT_BLOCKS * 4, a.stream>>>(
+        (const Tin *)a.v, a.ops, a.cu, a.N, a.H, a.h0, a.ckpt);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    static std::atomic<uint64_t> chunk_lds{0}, final_lds{0};
+    e = set_lds_limit((const void *)&bwd_chunk_kernel<Tin, Tdo>, (int)ChunkLds::BYTES, chunk_lds);
+    if (e != hipSuccess) return e;
+    bwd_chunk_kernel<Tin, Tdo><<<grid, 256, ChunkLds::BYTES, a.stream>>>(
+        (const Tin *)a.v, a.ops, a.cu, a.N, a.H, a.ckpt, (const Tdo *)a.dout, a.dht, a.dv, a.part,
+        a.dh0);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    e = set_lds_limit((const void *)&bwd_chunk_final_kernel<Tin>, (int)FinalLds::BYTES, final_lds);
+    if (e != hipSuccess) return e;
+    bwd_chunk_final_kernel<Tin><<<dim3((unsigned)slots, (unsigned)Hk), 256, FinalLds::BYTES, a.stream>>>(
+        (const Tin *)a.q, (const Tin *)a.k, a.g, a.beta_raw, a.A_log, a.dt_bias, a.scale,
+        a.lower_bound, a.cu, a.N, a.H, Hk, a.part, a.dq, a.dk, a.dg, a.dbeta, a.pp);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    bwd_param_kernel<<<(unsigned)a.H, 256, 0, a.stream>>>(a.pp, slots, a.H, a.dA_log, a.ddt_bias);
     return hipGetLastError();
 }
 
@@ -555,10 +1047,12 @@ hipError_t launch_backward_t(const BackwardArgs &a) {
 BackwardLayout backward_layout(int64_t T, int N, int H) {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     BackwardLayout l;
-    l.ckpt_bytes = up((size_t)(T / kCk + N) * H * kHeadDim * kHeadDim * 4);
-    l.part_bytes = up((size_t)T * H * kNVB * kPartCols * 4);
-    l.pp_bytes = up((size_t)((T + 15) / 16) * H * (kHeadDim + 1) * 4);
-    l.total = l.ckpt_bytes + l.part_bytes + l.pp_bytes;
+    const size_t slots = (size_t)num_slots(T, N, kCk);
+    l.ckpt_bytes = up(slots * H * kHeadDim * kHeadDim * 4);
+    l.part_bytes = up(slots * H * 2 * kPartRec * 4);
+    l.pp_bytes = up(slots * H * (kHeadDim + 1) * 4);
+    l.ops_bytes = up(slots * H * OpRec::END * 4);
+    l.total = l.ckpt_bytes + l.part_bytes + l.pp_bytes + l.ops_bytes;
     return l;
 }
 
