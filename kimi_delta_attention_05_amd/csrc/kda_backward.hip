@@ -65,7 +65,7 @@ constexpr int kTP = 132;                       // LDS pitch (floats) of [16][128
 constexpr int kSP = 20;                        // LDS pitch of [16][16] tiles
 constexpr int kTile = 16 * kTP, kSmall = 16 * kSP;
 constexpr int kPartChunk = 3 * 16 * kHeadDim + 2 * 16 * 16 + kHeadDim;   // partial floats per (chunk, head, half)
-constexpr int kPartRec = 7 * 256 * 4;          // their record (padded)
+constexpr int kPartRec = kPartChunk + 2 * 256;  // their record (dM, dT in two parts each)
 static_assert(kPartChunk <= kPartRec, "partial record");
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
@@ -401,12 +401,13 @@ __device__ __forceinline__ void wait_vmem_le() {
 
 // The state of 16 rows per wave in registers as the transposed accumulator
 // tiles Sa[kb][i] = S[vbase + lr][16 kb + 4 lg + i]; per chunk: the checkpoint,
-// R = V - KE S^T, U = T R, S^T <- diag(GC) S^T + KG^T U, with the next chunk's
-// operands copied into the other LDS buffer meanwhile.
+// R = V - KE S^T (also stored: the reverse pass reads it back), U = T R,
+// S^T <- diag(GC) S^T + KG^T U, with the next chunk's operands copied into the
+// other LDS buffer meanwhile.
 template <typename Tin>
 __global__ __launch_bounds__(256) void bwd_ckpt_kernel(
     const Tin *__restrict__ v, const float *__restrict__ ops, const int64_t *__restrict__ cu,
-    int N, int H, const float *__restrict__ h0, float *__restrict__ ckpt)
+    int N, int H, const float *__restrict__ h0, float *__restrict__ ckpt, float *__restrict__ rr)
 {
     constexpr int BUF = 256 * OpRec::CKPT_BLOCKS;
     extern __shared__ __align__(16) float sm[];
@@ -425,11 +426,16 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(
     const size_t rec_step = (size_t)H * OpRec::END;
 
     f32x4 Sa[8];
+    if (h0) {
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-        Sa[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (h0) Sa[kb] = *(const f32x4 *)(h0 + ((size_t)nh * kHeadDim + vbase + lr) * kHeadDim + 16 * kb + 4 * lg);
+        for (int kb = 0; kb < 8; ++kb)
+            Sa[kb] = *(const f32x4 *)(h0 + ((size_t)nh * kHeadDim + vbase + lr) * kHeadDim + 16 * kb + 4 * lg);
+    } else {
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) Sa[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) asm volatile("" ::"v"(Sa[kb]));   // settled before the chunk loop
     if (nch == 0) return;
     // v[t = 4 lg + i][vbase + lr] of one chunk, loaded one chunk ahead
     // (tokens past the sequence end read its last token, masked where used)
@@ -446,17 +452,25 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(
     fetch_v(0);
     wait_vmem_le<0>();
     lds_barrier();
-    for (int64_t c = 0; c < nch; ++c) {
-        const float *OP = sm + (c & 1) * BUF;
+    // v of the current chunk as floats (masked past the sequence end); each
+    // chunk converts the next chunk's values after its end-of-chunk wait, so
+    // that no load is waited for at the top of the loop
+    auto v_of = [&](int64_t c) {
         const int64_t c0 = s0 + c * kCk;
         const int L = (int)(s1 - c0 < kCk ? s1 - c0 : kCk);
-        f32x4 Vb;
+        f32x4 x;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) Vb[i] = 4 * lg + i < L ? (float)vb[i] : 0.f;
+        for (int i = 0; i < 4; ++i) x[i] = 4 * lg + i < L ? (float)vb[i] : 0.f;
+        return x;
+    };
+    f32x4 Vb = v_of(0);
+    for (int64_t c = 0; c < nch; ++c) {
+        const float *OP = sm + (c & 1) * BUF;
         // the next chunk's operands (the last chunk's again at the end) and v
         const int64_t cn = c + 1 < nch ? c + 1 : c;
         copy_record<OpRec::CKPT_BLOCKS>(rec0 + cn * rec_step, sm + ((c + 1) & 1) * BUF, wave, lane);
         fetch_v(cn);
+        asm volatile("" ::: "memory");   // keep the loads here, a whole chunk ahead of their use
         float *ck = ckpt + ((size_t)(slot0 + c) * H + h) * kHeadDim * kHeadDim;
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb)
@@ -471,8 +485,14 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(
         for (int kb = 0; kb < 8; ++kb)
             Sa[kb] = bmm16(lds4col(OP + OpRec::KG + (4 * lg) * kTP + 16 * kb + lr, kTP), U,
                            Sa[kb] * lds4(OP + OpRec::GC + 16 * kb + 4 * lg));
-        // the copy and the v loads landed (the 8 checkpoint stores may still be in flight)
-        wait_vmem_le<8>();
+        // R of this wave's rows kept for the reverse pass, in lane order (stored
+        // here rather than where it is formed: a store in the middle of the MFMA
+        // stream measurably stalls it)
+        *(f32x4 *)(rr + ((((size_t)(slot0 + c) * H + h) * 2 + half) * 4 + wave) * 256 + 4 * lane) = R;
+        // the copy and the v loads landed (the 9 stores may still be in flight)
+        wait_vmem_le<9>();
+        Vb = v_of(cn);
+        asm volatile("" ::"v"(Vb));
         lds_barrier();
     }
 }
@@ -492,28 +512,35 @@ struct ChunkLds {
 };
 static_assert(ChunkLds::BYTES <= 160 * 1024, "LDS budget");
 
-// The wave's inputs for one chunk: its own 16 state rows of S0 (row operand),
+// The wave's inputs for one chunk: R of its rows (from the checkpoint pass),
 // the column operand of S0 over the workgroup's 64 rows and the wave's 32 key
-// columns, dO and v of its rows.
-template <typename Tin, typename Tdo>
+// columns, and dO of its rows.
+template <typename Tdo>
 struct ChainIn {
-    f32x4 S0a[8];          // S0[vbase + lr][16 kb + 4 lg + i]
+    f32x4 R;               // R[t = 4 lg + i][vbase + lr]
     f32x4 S0s[8];          // [2 vb + kt]: S0[64 half + 16 vb + 4 lg + i][32 wave + 16 kt + lr]
     vec4<Tdo> dOa;         // dO[t = lr][vbase + 4 lg + i]
     Tdo dOb[4];            // dO[t = 4 lg + i][vbase + lr]
-    Tin Vb[4];             // v[t = 4 lg + i][vbase + lr]
 };
 
+template <typename Tdo>
+__device__ __forceinline__ void settle(const ChainIn<Tdo> &r) {
+    asm volatile("" ::"v"(r.R), "v"(r.dOa));
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) asm volatile("" ::"v"(r.S0s[kb]));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) asm volatile("" ::"v"((float)r.dOb[i]));
+}
+
 // Unconditional loads: tokens past the sequence end read its last token (masked where used).
-template <typename Tin, typename Tdo>
-__device__ __forceinline__ void chain_load(ChainIn<Tin, Tdo> &r, const float *ckpt, const Tdo *dout,
-                                           const Tin *v, int64_t slot, int64_t c0, int64_t s1,
-                                           int H, int h, int half, int wave, int lr, int lg) {
+template <typename Tdo>
+__device__ __forceinline__ void chain_load(ChainIn<Tdo> &r, const float *ckpt, const float *rr,
+                                           const Tdo *dout, int64_t slot, int64_t c0, int64_t s1,
+                                           int H, int h, int half, int wave, int lane) {
+    const int lr = lane & 15, lg = lane >> 4;
     const int vbase = 64 * half + 16 * wave;
     const float *ck = ckpt + ((size_t)slot * H + h) * kHeadDim * kHeadDim;
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb)
-        r.S0a[kb] = *(const f32x4 *)(ck + (size_t)(vbase + lr) * kHeadDim + 16 * kb + 4 * lg);
+    r.R = *(const f32x4 *)(rr + ((((size_t)slot * H + h) * 2 + half) * 4 + wave) * 256 + 4 * lane);
 #pragma unroll
     for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
@@ -524,17 +551,13 @@ __device__ __forceinline__ void chain_load(ChainIn<Tin, Tdo> &r, const float *ck
     auto tok = [&](int t) { return c0 + t < s1 ? c0 + t : s1 - 1; };
     r.dOa = *(const vec4<Tdo> *)(dout + ((size_t)tok(lr) * H + h) * kHeadDim + vbase + 4 * lg);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const size_t o = ((size_t)tok(4 * lg + i) * H + h) * kHeadDim + vbase + lr;
-        r.dOb[i] = dout[o];
-        r.Vb[i] = v[o];
-    }
+    for (int i = 0; i < 4; ++i) r.dOb[i] = dout[((size_t)tok(4 * lg + i) * H + h) * kHeadDim + vbase + lr];
 }
 
-template <typename Tin, typename Tdo>
+template <typename Tdo>
 __global__ __launch_bounds__(256) void bwd_chunk_kernel(
-    const Tin *__restrict__ v, const float *__restrict__ ops, const int64_t *__restrict__ cu,
-    int N, int H, const float *__restrict__ ckpt, const Tdo *__restrict__ dout,
+    const float *__restrict__ ops, const int64_t *__restrict__ cu, int N, int H,
+    const float *__restrict__ ckpt, const float *__restrict__ rr, const Tdo *__restrict__ dout,
     const float *__restrict__ dht, float *__restrict__ dv, float *__restrict__ part,
     float *__restrict__ dh0)
 {
@@ -558,18 +581,25 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
 
     // dSa[kb]: the adjoint of the state after the current chunk, dS[vbase + lr][16 kb + 4 lg + i]
     f32x4 dSa[8];
+    if (dht) {
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) {
-        dSa[kb] = zero;
-        if (dht) dSa[kb] = *(const f32x4 *)(dht + ((size_t)nh * kHeadDim + vbase + lr) * kHeadDim + 16 * kb + 4 * lg);
+        for (int kb = 0; kb < 8; ++kb)
+            dSa[kb] = *(const f32x4 *)(dht + ((size_t)nh * kHeadDim + vbase + lr) * kHeadDim + 16 * kb + 4 * lg);
+    } else {
+#pragma unroll
+        for (int kb = 0; kb < 8; ++kb) dSa[kb] = zero;
     }
+    // settled before the chunk loop (a wait placed inside it would also wait for
+    // the copies issued there)
+#pragma unroll
+    for (int kb = 0; kb < 8; ++kb) asm volatile("" ::"v"(dSa[kb]));
 
     // Every input of a chunk is loaded while the chunk after it runs: its
     // record into the other LDS buffer, the state rows, dO and v alternately
     // into two register sets (the loop is unrolled twice, so no register copy
     // of a load in flight is ever needed).
-    ChainIn<Tin, Tdo> bufA, bufB;
-    auto chunk = [&](int64_t c, const ChainIn<Tin, Tdo> &cur, ChainIn<Tin, Tdo> &nxt, int rb)
+    ChainIn<Tdo> bufA, bufB;
+    auto chunk = [&](int64_t c, const ChainIn<Tdo> &cur, ChainIn<Tdo> &nxt, int rb)
         __attribute__((always_inline)) {
         const float *OP = sm + LY::REC + rb * OpRec::END;
         const int64_t c0 = s0 + c * kCk;
@@ -577,25 +607,20 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
         {   // the chunk before (chunk 0 again in the last pass: the loads stay unconditional)
             const int64_t cp = c > 0 ? c - 1 : 0;
             copy_record<OpRec::END / 256>(rec0 + cp * rec_step, sm + LY::REC + (rb ^ 1) * OpRec::END, wave, lane);
-            chain_load(nxt, ckpt, dout, v, slot0 + cp, s0 + cp * kCk, s1, H, h, half, wave, lr, lg);
+            chain_load(nxt, ckpt, rr, dout, slot0 + cp, s0 + cp * kCk, s1, H, h, half, wave, lane);
         }
-        f32x4 Vf, dOb, dOa = f4<Tdo>(cur.dOa);
+        f32x4 dOb, dOa = f4<Tdo>(cur.dOa);
         if (lr >= L) dOa = zero;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool in = 4 * lg + i < L;
-            Vf[i] = in ? (float)cur.Vb[i] : 0.f;
-            dOb[i] = in ? (float)cur.dOb[i] : 0.f;
-        }
-        // R = V - KE S0^T and KG dS1^T ([t][v] accumulators); dS1 shared
-        f32x4 R = zero, dUk = zero;
+        for (int i = 0; i < 4; ++i) dOb[i] = 4 * lg + i < L ? (float)cur.dOb[i] : 0.f;
+        const f32x4 R = cur.R;   // V - KE S0^T ([t][v] accumulator; zero past the end)
+        // KG dS1^T ([t][v] accumulator); dS1 shared
+        f32x4 dUk = zero;
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) {
-            R = bmm16(lds4(OP + OpRec::KE + lr * kTP + 16 * kb + 4 * lg), cur.S0a[kb], R);
             dUk = bmm16(lds4(OP + OpRec::KG + lr * kTP + 16 * kb + 4 * lg), dSa[kb], dUk);
             *(f32x4 *)(sm + LY::DS1 + (vloc + lr) * kTP + 16 * kb + 4 * lg) = dSa[kb];
         }
-        R = Vf - R;
         // dS <- dS1 diag(GC) + QG^T dO
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb)
@@ -668,29 +693,38 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
             x = __uint_as_float(b2[0]) + __uint_as_float(b2[1]);
             if (lg == 0) dst[6656 + kcol + 16 * kt + lr] = x;
         }
-        // dM = lower(dO U^T) (wave 0) and dT = dU R^T (wave 1) over the 64 rows
-        if (wave < 2) {
-            const int A_ = wave == 0 ? LY::DOS : LY::DUS, B_ = wave == 0 ? LY::US : LY::RS;
+        // dM = lower(dO U^T) (waves 0, 1) and dT = dU R^T (waves 2, 3), each wave
+        // over 32 of the 64 rows (the final kernel adds the two parts)
+        {
+            const bool isM = wave < 2;
+            const int A_ = isM ? LY::DOS : LY::DUS, B_ = isM ? LY::US : LY::RS;
+            const int vb0 = 2 * (wave & 1);
             f32x4 acc = zero;
 #pragma unroll
-            for (int vb = 0; vb < 4; ++vb)
+            for (int vb = vb0; vb < vb0 + 2; ++vb)
                 acc = bmm16(lds4(sm + A_ + lr * LY::SP + 16 * vb + 4 * lg), lds4(sm + B_ + lr * LY::SP + 16 * vb + 4 * lg), acc);
+            const int off = (isM ? 6144 : 6400) + (wave & 1) * 640;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 4 * lg + i;
-                dst[(wave == 0 ? 6144 : 6400) + r * 16 + lr] = (wave == 1 || r >= lr) ? acc[i] : 0.f;
+                dst[off + r * 16 + lr] = (!isM || r >= lr) ? acc[i] : 0.f;
             }
         }
         // the next record and the chain loads landed (this chunk's partial
         // stores, at least 24 per wave, may still be in flight); then the
         // buffers and the shared rows are free for the next chunk
         wait_vmem_le<24>();
+        // the next chunk's loads are known complete here: settling them now
+        // keeps the compiler from waiting for them at the next chunk's start,
+        // after the copy issued there (which it does not see: such a wait
+        // would wait for that copy as well)
+        settle(nxt);
         lds_barrier();
     };
     int64_t c = nch - 1;
     if (c >= 0) {
         copy_record<OpRec::END / 256>(rec0 + c * rec_step, sm + LY::REC, wave, lane);
-        chain_load(bufA, ckpt, dout, v, slot0 + c, s0 + c * kCk, s1, H, h, half, wave, lr, lg);
+        chain_load(bufA, ckpt, rr, dout, slot0 + c, s0 + c * kCk, s1, H, h, half, wave, lane);
         wait_vmem_le<0>();
         lds_barrier();
     }
@@ -814,8 +848,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 #pragma unroll
             for (int e = 0; e < 8; ++e) pe[e] = x0[e] + x1[e];
         }
-        const float dMv = p0[6144 + tid] + p1[6144 + tid];
-        const float dTv = p0[6400 + tid] + p1[6400 + tid];
+        // dM and dT: two parts per half (rows 0-31 and 32-63 of the half)
+        const float dMv = (p0[6144 + tid] + p0[6784 + tid]) + (p1[6144 + tid] + p1[6784 + tid]);
+        const float dTv = (p0[6400 + tid] + p0[7040 + tid]) + (p1[6400 + tid] + p1[7040 + tid]);
         const float dGCv = tid < kHeadDim ? p0[6656 + tid] + p1[6656 + tid] : 0.f;
 
         {
@@ -1018,16 +1053,15 @@ hipError_t launch_backward_t(const BackwardArgs &a) {
         if (e != hipSuccess) return e;
     }
     bwd_ckpt_kernel<Tin><<<grid, 256, 2 * 256 * OpRec::CKPT_BLOCKS * 4, a.stream>>>(
-        (const Tin *)a.v, a.ops, a.cu, a.N, a.H, a.h0, a.ckpt);
+        (const Tin *)a.v, a.ops, a.cu, a.N, a.H, a.h0, a.ckpt, a.rr);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
     static std::atomic<uint64_t> chunk_lds{0}, final_lds{0};
-    e = set_lds_limit((const void *)&bwd_chunk_kernel<Tin, Tdo>, (int)ChunkLds::BYTES, chunk_lds);
+    e = set_lds_limit((const void *)&bwd_chunk_kernel<Tdo>, (int)ChunkLds::BYTES, chunk_lds);
     if (e != hipSuccess) return e;
-    bwd_chunk_kernel<Tin, Tdo><<<grid, 256, ChunkLds::BYTES, a.stream>>>(
-        (const Tin *)a.v, a.ops, a.cu, a.N, a.H, a.ckpt, (const Tdo *)a.dout, a.dht, a.dv, a.part,
-        a.dh0);
+    bwd_chunk_kernel<Tdo><<<grid, 256, ChunkLds::BYTES, a.stream>>>(
+        a.ops, a.cu, a.N, a.H, a.ckpt, a.rr, (const Tdo *)a.dout, a.dht, a.dv, a.part, a.dh0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
@@ -1052,7 +1086,8 @@ BackwardLayout backward_layout(int64_t T, int N, int H) {
     l.part_bytes = up(slots * H * 2 * kPartRec * 4);
     l.pp_bytes = up(slots * H * (kHeadDim + 1) * 4);
     l.ops_bytes = up(slots * H * OpRec::END * 4);
-    l.total = l.ckpt_bytes + l.part_bytes + l.pp_bytes + l.ops_bytes;
+    l.rr_bytes = up(slots * H * 2 * 4 * 256 * 4);
+    l.total = l.ckpt_bytes + l.part_bytes + l.pp_bytes + l.ops_bytes + l.rr_bytes;
     return l;
 }
 
