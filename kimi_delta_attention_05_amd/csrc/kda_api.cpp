@@ -737,10 +737,9 @@ kda_status_t kda_backward_grouped(const void *q, const void *k, const void *v, c
     a.ddt_bias = ddt_bias; a.dh0 = d_initial_state;
     unsigned char *ws = (unsigned char *)workspace;
     a.ckpt = (float *)ws;
-    a.part = (float *)(ws + lay.ckpt_bytes);
-    a.pp = (float *)(ws + lay.ckpt_bytes + lay.part_bytes);
-    a.ops = (float *)(ws + lay.ckpt_bytes + lay.part_bytes + lay.pp_bytes);
-    a.rr = (float *)(ws + lay.ckpt_bytes + lay.part_bytes + lay.pp_bytes + lay.ops_bytes);
+    a.pp = (float *)(ws + lay.ckpt_bytes);
+    a.ops = (float *)(ws + lay.ckpt_bytes + lay.pp_bytes);
+    a.rr = (float *)(ws + lay.ckpt_bytes + lay.pp_bytes + lay.ops_bytes);
     a.stream = (hipStream_t)stream;
     if (K == 128 && V == 128) {
         hipError_t e = kda::launch_backward(a);

@@ -66,7 +66,8 @@ constexpr int kSP = 20;                        // LDS pitch of [16][16] tiles
 constexpr int kTile = 16 * kTP, kSmall = 16 * kSP;
 constexpr int kPartChunk = 3 * 16 * kHeadDim + 2 * 16 * 16 + kHeadDim;   // partial floats per (chunk, head, half)
 constexpr int kPartRec = kPartChunk + 2 * 256;  // their record (dM, dT in two parts each)
-static_assert(kPartChunk <= kPartRec, "partial record");
+static_assert(kPartChunk <= kPartRec && kPartRec <= 64 * kHeadDim,
+              "a half's partial record fits in its checkpoint rows");
 
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
@@ -210,7 +211,7 @@ __device__ __forceinline__ void operands_phase1(float *sm, const TokIn<Tin, WITH
 // (Gam_t up to and including t, SUF_t after t; products of at most 16 factors
 // >= e^-5, so Gam >= e^-80 and never subnormal), and KE, QG, KG, KI written in
 // place over the phase-1 values of the same column; GC into GC. With KEEP, Gam
-// and SUF also stay in the GAM and SUF tiles.
+// also stays in the GAM tile.
 template <typename LY, bool WITH_Q, bool KEEP>
 __device__ __forceinline__ void operands_phase2(float *sm, int tid) {
     if (tid < kHeadDim) {
@@ -234,10 +235,7 @@ __device__ __forceinline__ void operands_phase2(float *sm, int tid) {
             if constexpr (WITH_Q) sm[LY::QG + t * kTP + c] = qh[t] * gam[t];
             sm[LY::KG + t * kTP + c] = kh[t] * suf[t];
             sm[LY::KI + t * kTP + c] = kh[t] / gam[t];
-            if constexpr (KEEP) {
-                sm[LY::GAM + t * kTP + c] = gam[t];
-                sm[LY::SUF + t * kTP + c] = suf[t];
-            }
+            if constexpr (KEEP) sm[LY::GAM + t * kTP + c] = gam[t];
         }
         sm[LY::GC + c] = gam[15];
     }
@@ -557,9 +555,8 @@ __device__ __forceinline__ void chain_load(ChainIn<Tdo> &r, const float *ckpt, c
 template <typename Tdo>
 __global__ __launch_bounds__(256) void bwd_chunk_kernel(
     const float *__restrict__ ops, const int64_t *__restrict__ cu, int N, int H,
-    const float *__restrict__ ckpt, const float *__restrict__ rr, const Tdo *__restrict__ dout,
-    const float *__restrict__ dht, float *__restrict__ dv, float *__restrict__ part,
-    float *__restrict__ dh0)
+    float *ckpt, const float *__restrict__ rr, const Tdo *__restrict__ dout,
+    const float *__restrict__ dht, float *__restrict__ dv, float *__restrict__ dh0)
 {
     using LY = ChunkLds;
     extern __shared__ __align__(16) float sm[];
@@ -673,7 +670,9 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
                 for (int i = 0; i < 4; ++i) gs[kt][i] = fmaf(s0c[i], ds1c[i], gs[kt][i]);
             }
         }
-        float *dst = part + (((size_t)(slot0 + c) * H + h) * 2 + half) * kPartRec;
+        // over this half's checkpoint rows of the chunk, which this workgroup
+        // alone reads and has read (loaded during the chunk after)
+        float *dst = ckpt + ((size_t)(slot0 + c) * H + h) * kHeadDim * kHeadDim + (size_t)half * 64 * kHeadDim;
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -741,14 +740,15 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
     }
 }
 
-// LDS of bwd_chunk_final_kernel. GAM and SUF hold the decay products up to and
-// after each token, DG the per-token log-decay adjoint, EK dKG * KG and then
-// the per-token gate gradients (SP).
+// LDS of bwd_chunk_final_kernel. GAM holds the decay products up to each token;
+// XE, XQ, XI the products dP KI, dM KI, dKI, the first two then overwritten in
+// place by the per-token log-decay adjoint (DG) and dKG * KG (EK), which in turn
+// becomes the per-token gate gradients (SP).
 struct FinalLds {
     static constexpr int KE = 0, QG = KE + kTile, KG = QG + kTile, KI = KG + kTile;
-    static constexpr int SUF = KI + kTile, DG = SUF + kTile, GAM = DG + kTile, EK = GAM + kTile;
-    static constexpr int SP = EK;
-    static constexpr int A = EK + kTile, P = A + kSmall, X = P + kSmall, DM = X + kSmall;
+    static constexpr int XI = KI + kTile, XE = XI + kTile, GAM = XE + kTile, XQ = GAM + kTile;
+    static constexpr int DG = XE, EK = XQ, SP = EK;
+    static constexpr int A = XQ + kTile, P = A + kSmall, X = P + kSmall, DM = X + kSmall;
     static constexpr int DT = DM + kSmall, Y = DT + kSmall, DA = Y + kSmall;
     static constexpr int GC = DA + kSmall, DGC = GC + kHeadDim, B = DGC + kHeadDim;
     static constexpr int END = B + 16;
@@ -831,7 +831,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         float dtb[8];
         load_lane8(dt_bias + (size_t)h * kHeadDim, j, dtb);
         // the two halves' partials (issued before the operands are formed)
-        const float *p0 = part + ((size_t)slot * H + h) * 2 * kPartRec, *p1 = p0 + kPartRec;
+        const float *p0 = part + ((size_t)slot * H + h) * kHeadDim * kHeadDim, *p1 = p0 + 64 * kHeadDim;
         float pq[8], pk[8], pe[8];
         {
             float x0[8], x1[8];
@@ -906,44 +906,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
                 dbeta[(size_t)(c0 + t) * H + h] = db * bb * (1.0f - bb);
             }
         }
-        // token row gid: dKE = dKE_p + dP KI, dQG = dQG_p + dM KI, dKI = dP^T KE + dM^T QG
-        // with dP = diag(b) dA
-        float dke[8], dqg[8], dki[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) { dke[e] = pe[e]; dqg[e] = pq[e]; dki[e] = 0.f; }
+        // dP KI, dM KI and dKI = dP^T KE + dM^T QG (dP = diag(b) dA) on the MFMA,
+        // wave w for the key columns 32 w .. 32 w + 31, into the XE, XQ, XI tiles
         {
-            const float bt = sm[LY::B + gid];
-#pragma unroll 2
-            for (int jj = 0; jj < 16; ++jj) {
-                const float dp = bt * sm[LY::DA + gid * kSP + jj];
-                const float dm = sm[LY::DM + gid * kSP + jj];
-                const float dpT = sm[LY::B + jj] * sm[LY::DA + jj * kSP + gid];
-                const float dmT = sm[LY::DM + jj * kSP + gid];
-                float ki[8], ke[8], qg[8];
-                load_lane8(sm + LY::KI + jj * kTP, j, ki);
-                load_lane8(sm + LY::KE + jj * kTP, j, ke);
-                load_lane8(sm + LY::QG + jj * kTP, j, qg);
+            const int lr = lane & 15, lg = lane >> 4;
+            const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+            const f32x4 dPr = lds4(sm + LY::DA + lr * kSP + 4 * lg) * sm[LY::B + lr];
+            const f32x4 dMr = lds4(sm + LY::DM + lr * kSP + 4 * lg);
+            const f32x4 dPc = lds4col(sm + LY::DA + (4 * lg) * kSP + lr, kSP) * lds4(sm + LY::B + 4 * lg);
+            const f32x4 dMc = lds4col(sm + LY::DM + (4 * lg) * kSP + lr, kSP);
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    dke[e] = fmaf(dp, ki[e], dke[e]);
-                    dqg[e] = fmaf(dm, ki[e], dqg[e]);
-                    dki[e] = fmaf(dpT, ke[e], fmaf(dmT, qg[e], dki[e]));
+            for (int kbi = 0; kbi < 2; ++kbi) {
+                const int col = 16 * (2 * wave + kbi) + lr;
+                const f32x4 kic = lds4col(sm + LY::KI + (4 * lg) * kTP + col, kTP);
+                const f32x4 kec = lds4col(sm + LY::KE + (4 * lg) * kTP + col, kTP);
+                const f32x4 qgc = lds4col(sm + LY::QG + (4 * lg) * kTP + col, kTP);
+                const f32x4 xe = bmm16(dPr, kic, z), xq = bmm16(dMr, kic, z);
+                const f32x4 xi = bmm16(dMc, qgc, bmm16(dPc, kec, z));
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int o = (4 * lg + i) * kTP + col;
+                    sm[LY::XE + o] = xe[i];
+                    sm[LY::XQ + o] = xq[i];
+                    sm[LY::XI + o] = xi[i];
                 }
             }
         }
+        lds_barrier();
+        // token row gid: dKE = dKE_p + dP KI, dQG = dQG_p + dM KI; dkh, dqh, the
+        // per-token log-decay adjoint DG and dKG * KG (EK), over XE and XQ in place
         {
-            float gam[8], suf[8], ke[8], qg[8], ki[8], kg[8], dgp[8], ek[8];
+            float xe[8], xq[8], dki[8], gam[8], gcv[8], ke[8], qg[8], ki[8], kg[8], dgp[8], ek[8];
+            load_lane8(sm + LY::XE + gid * kTP, j, xe);
+            load_lane8(sm + LY::XQ + gid * kTP, j, xq);
+            load_lane8(sm + LY::XI + gid * kTP, j, dki);
             load_lane8(sm + LY::GAM + gid * kTP, j, gam);
-            load_lane8(sm + LY::SUF + gid * kTP, j, suf);
+            load_lane8(sm + LY::GC, j, gcv);
             load_lane8(sm + LY::KE + gid * kTP, j, ke);
             load_lane8(sm + LY::QG + gid * kTP, j, qg);
             load_lane8(sm + LY::KI + gid * kTP, j, ki);
             load_lane8(sm + LY::KG + gid * kTP, j, kg);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                dkh[e] += dke[e] * gam[e] + pk[e] * suf[e] + dki[e] / gam[e];
-                dqh[e] = fmaf(dqg[e], gam[e], dqh[e]);
-                dgp[e] = dke[e] * ke[e] + dqg[e] * qg[e] - dki[e] * ki[e];
+                const float dke = pe[e] + xe[e], dqg = pq[e] + xq[e];
+                const float suf = gcv[e] / gam[e];     // the decay after the token
+                dkh[e] += dke * gam[e] + pk[e] * suf + dki[e] / gam[e];
+                dqh[e] = fmaf(dqg, gam[e], dqh[e]);
+                dgp[e] = dke * ke[e] + dqg * qg[e] - dki[e] * ki[e];
                 ek[e] = pk[e] * kg[e];
             }
             store_lane8(sm + LY::DG + gid * kTP, j, dgp);
@@ -1061,7 +1070,7 @@ hipError_t launch_backward_t(const BackwardArgs &a) {
     e = set_lds_limit((const void *)&bwd_chunk_kernel<Tdo>, (int)ChunkLds::BYTES, chunk_lds);
     if (e != hipSuccess) return e;
     bwd_chunk_kernel<Tdo><<<grid, 256, ChunkLds::BYTES, a.stream>>>(
-        a.ops, a.cu, a.N, a.H, a.ckpt, a.rr, (const Tdo *)a.dout, a.dht, a.dv, a.part, a.dh0);
+        a.ops, a.cu, a.N, a.H, a.ckpt, a.rr, (const Tdo *)a.dout, a.dht, a.dv, a.dh0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
 
@@ -1069,7 +1078,7 @@ hipError_t launch_backward_t(const BackwardArgs &a) {
     if (e != hipSuccess) return e;
     bwd_chunk_final_kernel<Tin><<<dim3((unsigned)slots, (unsigned)Hk), 256, FinalLds::BYTES, a.stream>>>(
         (const Tin *)a.q, (const Tin *)a.k, a.g, a.beta_raw, a.A_log, a.dt_bias, a.scale,
-        a.lower_bound, a.cu, a.N, a.H, Hk, a.part, a.dq, a.dk, a.dg, a.dbeta, a.pp);
+        a.lower_bound, a.cu, a.N, a.H, Hk, a.ckpt, a.dq, a.dk, a.dg, a.dbeta, a.pp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     bwd_param_kernel<<<(unsigned)a.H, 256, 0, a.stream>>>(a.pp, slots, a.H, a.dA_log, a.ddt_bias);
@@ -1082,12 +1091,12 @@ BackwardLayout backward_layout(int64_t T, int N, int H) {
     auto up = [](size_t x) { return (x + 255) / 256 * 256; };
     BackwardLayout l;
     const size_t slots = (size_t)num_slots(T, N, kCk);
+    // (the reverse pass's partial records reuse the checkpoint rows)
     l.ckpt_bytes = up(slots * H * kHeadDim * kHeadDim * 4);
-    l.part_bytes = up(slots * H * 2 * kPartRec * 4);
     l.pp_bytes = up(slots * H * (kHeadDim + 1) * 4);
     l.ops_bytes = up(slots * H * OpRec::END * 4);
     l.rr_bytes = up(slots * H * 2 * 4 * 256 * 4);
-    l.total = l.ckpt_bytes + l.part_bytes + l.pp_bytes + l.ops_bytes + l.rr_bytes;
+    l.total = l.ckpt_bytes + l.pp_bytes + l.ops_bytes + l.rr_bytes;
     return l;
 }
 

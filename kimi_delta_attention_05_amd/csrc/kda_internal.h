@@ -163,12 +163,12 @@ struct BackwardArgs {
     const float *dht;                   // [N, H, 128, 128] final-state adjoint or NULL (zero)
     float *dq, *dk, *dv, *dg, *dbeta, *dA_log, *ddt_bias;
     float *dh0;                         // or NULL
-    float *ckpt, *part, *pp, *ops, *rr; // workspace pieces (backward_layout)
+    float *ckpt, *pp, *ops, *rr;        // workspace pieces (backward_layout)
     hipStream_t stream;
 };
 
 struct BackwardLayout {
-    size_t ckpt_bytes, part_bytes, pp_bytes, ops_bytes, rr_bytes, total;
+    size_t ckpt_bytes, pp_bytes, ops_bytes, rr_bytes, total;
 };
 BackwardLayout backward_layout(int64_t T, int N, int H);
 hipError_t launch_backward(const BackwardArgs &a);
