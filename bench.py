@@ -49,10 +49,22 @@ KERNEL_SOURCES = {
     "decode_step_kernel": ("kda_decode.hip", "kda_common.h", "kda_internal.h"),
     "short_conv_kernel": ("kda_shortconv.hip", "kda_common.h", "kda_internal.h"),
     "norm_gate_kernel": ("kda_epilogue.hip", "kda_common.h", "kda_internal.h"),
+    "bwd_prep_kernel": ("kda_backward.hip", "kda_common.h", "kda_internal.h"),
     "bwd_ckpt_kernel": ("kda_backward.hip", "kda_common.h", "kda_internal.h"),
-    "bwd_reverse_kernel": ("kda_backward.hip", "kda_common.h", "kda_internal.h"),
-    "bwd_finalize_kernel": ("kda_backward.hip", "kda_common.h", "kda_internal.h"),
+    "bwd_chunk_kernel": ("kda_backward.hip", "kda_common.h", "kda_internal.h"),
+    "bwd_chunk_final_kernel": ("kda_backward.hip", "kda_common.h", "kda_internal.h"),
+    "bwd_param_kernel": ("kda_backward.hip", "kda_common.h", "kda_internal.h"),
 }
+
+# fp32 MFMA arithmetic of the chunked backward per 16-token chunk and head
+# (K = V = 128), as its kernels execute it: the operand record (KE KI^T,
+# QG KI^T), the checkpoint pass (KE S^T, T R, KG^T U), the reverse pass (KG dS^T,
+# QG^T dO, KE^T dR, the partials dO S, U dS, dR S, and six 16x16x128 products),
+# the finalize (dP KI, dM KI, dP^T KE, dM^T QG)
+BWD_FLOPS_PER_CHUNK_HEAD = (2 * 16 * 16 * D * 2          # prep
+                            + 2 * 16 * D * D * 2 + 16 * 16 * D * 2   # checkpoint
+                            + 6 * 16 * D * D * 2 + 6 * 16 * 16 * D * 2   # reverse
+                            + 4 * 16 * 16 * D * 2)       # finalize
 
 
 def measured_traffic(kernel):
@@ -393,6 +405,7 @@ def front_end_timing(kda, qkv, cu, W=4, reps=20):
 
 
 FP32_VALU_PEAK_TFLOPS = 157.3   # MI355X fp32 vector
+FP32_MFMA_PEAK_TFLOPS = 157.3   # MI355X dense fp32 MFMA
 
 
 def backward_timing(kda, p, dev_inputs, reps=3):
@@ -421,18 +434,18 @@ def backward_timing(kda, p, dev_inputs, reps=3):
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / reps
-    th = T * H
-    # arithmetic per token-head: 25 flops per state element (5 for the checkpoint
-    # forward, 5 for the recomputation, 15 for the reverse step) over 128 x 128
-    flops = th * 25 * Dk * Dk
+    cu_h = cu.cpu().tolist()
+    chunks = sum((cu_h[i + 1] - cu_h[i] + 15) // 16 for i in range(N))
+    flops = chunks * H * BWD_FLOPS_PER_CHUNK_HEAD
     tf = flops / (ms * 1e-3) / 1e12
     return {"ms": round(ms, 3), "tokens_per_s": round(T / (ms * 1e-3), 1),
             "workspace_bytes": kda.backward_workspace_size(T, N, H),
             "traffic": {kn: measured_traffic(kn) for kn in
-                        ("bwd_ckpt_kernel", "bwd_reverse_kernel", "bwd_finalize_kernel")},
-            "roofline": {"bound": "alu", "achieved": round(tf, 2), "peak": FP32_VALU_PEAK_TFLOPS,
-                         "unit": "TFLOP/s", "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4),
-                         "alg_flops": flops}}
+                        ("bwd_prep_kernel", "bwd_ckpt_kernel", "bwd_chunk_kernel",
+                         "bwd_chunk_final_kernel")},
+            "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": FP32_MFMA_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(tf / FP32_MFMA_PEAK_TFLOPS, 4),
+                         "alg_flops": flops, "dtype": "f32"}}
 
 
 def other_prefill_timing(kda, dev, reps=10):

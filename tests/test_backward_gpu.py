@@ -1,11 +1,13 @@
 """Parity of libkda's training backward (kda_backward) with the fp64 backward
 oracle (GPU).
 
-The backward runs entirely in fp32 (no MFMA, no reduced-precision operands),
-so every gradient is held to 1e-4 of its rms (fp32 roundoff is 6e-8; the
-reverse sweep adds a few roundings per token along state adjoints that the
-decay keeps bounded, and the parameter gradients sum up to T*128 terms in
-blocks of 16 and then in sequence), and to bitwise repetition between runs."""
+The backward runs entirely in fp32 (fp32 MFMA products and sums, no
+reduced-precision operands), so every gradient is held to 1e-4 of its rms (fp32
+roundoff is 6e-8; the reverse pass adds a few roundings per 16-token chunk along
+state adjoints that the decay keeps bounded, a token's log-decay adjoint sums
+up to 16 per-chunk terms each rounded to fp32 over 128 state rows, and the
+parameter gradients sum up to T*128 terms in blocks of 16 and then in
+sequence), and to bitwise repetition between runs."""
 import numpy as np
 import pytest
 import torch
