@@ -769,6 +769,7 @@ __global__ __launch_bounds__(256) void bwd_param_kernel(const float *__restrict_
     for (int col = threadIdx.x; col < 2 * NC; col += 256) {
         const int c = col % NC, half = col / NC;
         float s = 0.f;
+#pragma unroll 8
         for (int64_t b = half; b < ntb; b += 2) s += pp[((size_t)b * H + h) * NC + c];
         sAcc[half][c] = s;
     }
@@ -819,6 +820,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     float dqh[8], dkh[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) { dqh[e] = 0.f; dkh[e] = 0.f; }
+    TokIn<Tin, true> tk;
     for (int gg = 0; gg < G; ++gg) {
         const int h = hk * G + gg;
         // the thread index taken as new in each pass, so that the many per-thread
@@ -853,14 +855,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const float dTv = (p0[6400 + tid] + p0[7040 + tid]) + (p1[6400 + tid] + p1[7040 + tid]);
         const float dGCv = tid < kHeadDim ? p0[6656 + tid] + p1[6656 + tid] : 0.f;
 
-        {
-            TokIn<Tin, true> tk;
-            tok_load(tk, q, k, g, beta_raw, c0, s1, H, Hk, h, gid, j);
-            operands_phase1<LY, true>(sm, tk, dtb, a_gate, lb, scale, L, gid, j);
-            lds_barrier();
-            operands_phase2<LY, true, true>(sm, tid);
-            lds_barrier();
-        }
+        // the token rows are kept (tk) for the gate chain below and for the dq, dk
+        // chains after the loop, instead of being read again
+        tok_load(tk, q, k, g, beta_raw, c0, s1, H, Hk, h, gid, j);
+        operands_phase1<LY, true>(sm, tk, dtb, a_gate, lb, scale, L, gid, j);
+        lds_barrier();
+        operands_phase2<LY, true, true>(sm, tid);
+        lds_barrier();
         sm[LY::DM + gid * kSP + j] = dMv;
         sm[LY::DT + gid * kSP + j] = dTv;
         if (tid < kHeadDim) sm[LY::DGC + tid] = dGCv;
@@ -982,7 +983,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         if (gid < L) {
             const size_t tb = ((size_t)(c0 + gid) * H + h) * kHeadDim;
             float gv[8], dl[8];
-            load_lane8(g + tb, j, gv);
+            raw8_get(tk.g, gv);
             load_lane8(sm + LY::DG + gid * kTP, j, dl);
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -1011,8 +1012,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     if (gid < L) {
         const size_t tbk = ((size_t)(c0 + gid) * Hk + hk) * kHeadDim;
         float qv[8], kv[8];
-        load_lane8(q + tbk, j, qv);
-        load_lane8(k + tbk, j, kv);
+        raw8_get(tk.q, qv);
+        raw8_get(tk.k, kv);
         float sq = 0.f, sk = 0.f, qd = 0.f, kd = 0.f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
