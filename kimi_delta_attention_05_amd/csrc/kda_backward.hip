@@ -380,8 +380,11 @@ __device__ __forceinline__ void copy_record(const float *rec, float *lds, int wa
 #pragma unroll
     for (int b = 0; b < (NBLK + 3) / 4; ++b) {
         const int blk = 4 * b + wave;
-        if (4 * b + 3 < NBLK || blk < NBLK)
-            copy16_to_lds(r, 16u * (uint32_t)lane, 1024u * (uint32_t)blk, lds + 256 * blk);
+        if (4 * b + 3 < NBLK || blk < NBLK) {
+            // wave-uniform by construction; made scalar explicitly for the copy's operands
+            const int sblk = __builtin_amdgcn_readfirstlane(blk);
+            copy16_to_lds(r, 16u * (uint32_t)lane, 1024u * (uint32_t)sblk, lds + 256 * sblk);
+        }
     }
 }
 
@@ -497,66 +500,86 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(
 
 // ---- reverse pass -------------------------------------------------------------
 
-// LDS of bwd_chunk_kernel: two record buffers; dS1 of the workgroup's 64 state
-// rows [64][132]; and, for those rows, U, dR (row layouts), dU, R and dO
-// ([t][v] at pitch 68), shared so that each wave can form the partial sums of
-// its own 32 key columns over all 64 rows.
+// LDS of bwd_chunk_kernel: two record buffers, and two buffers of the rows
+// the chain waves share with the partial waves: dS1 of the workgroup's 64
+// state rows [64][132], and U, -dR (row layouts), dU and R ([t][v]) at pitch 68.
 struct ChunkLds {
     static constexpr int SP = 68;
-    static constexpr int REC = 0, DS1 = 2 * OpRec::END;
-    static constexpr int US = DS1 + 64 * kTP, DRS = US + 16 * SP, DUS = DRS + 16 * SP;
-    static constexpr int RS = DUS + 16 * SP, DOS = RS + 16 * SP, END = DOS + 16 * SP;
+    static constexpr int REC = 0, SH = 2 * OpRec::END;
+    static constexpr int DS1 = 0, US = DS1 + 64 * kTP, DRS = US + 16 * SP, DUS = DRS + 16 * SP;
+    static constexpr int RS = DUS + 16 * SP, SHB = RS + 16 * SP;     // one share buffer
+    static constexpr int END = SH + 2 * SHB;
     static constexpr size_t BYTES = (size_t)END * 4;
 };
 static_assert(ChunkLds::BYTES <= 160 * 1024, "LDS budget");
 
-// The wave's inputs for one chunk: R of its rows (from the checkpoint pass),
-// the column operand of S0 over the workgroup's 64 rows and the wave's 32 key
-// columns, and dO of its rows.
+// A chain wave's inputs for one chunk: R of its rows (from the checkpoint pass)
+// and dO of its rows in the column layout.
 template <typename Tdo>
 struct ChainIn {
     f32x4 R;               // R[t = 4 lg + i][vbase + lr]
-    f32x4 S0s[8];          // [2 vb + kt]: S0[64 half + 16 vb + 4 lg + i][32 wave + 16 kt + lr]
-    vec4<Tdo> dOa;         // dO[t = lr][vbase + 4 lg + i]
     Tdo dOb[4];            // dO[t = 4 lg + i][vbase + lr]
+};
+// A partial wave's inputs: the column operand of S0 over the workgroup's 64 rows
+// and the wave's 32 key columns, and dO of the 64 rows in the row layout.
+template <typename Tdo>
+struct PartIn {
+    f32x4 S0s[8];          // [2 vb + kt]: S0[64 half + 16 vb + 4 lg + i][kcol + 16 kt + lr]
+    vec4<Tdo> dOr[4];      // [vb]: dO[t = lr][64 half + 16 vb + 4 lg + kk]
 };
 
 template <typename Tdo>
 __device__ __forceinline__ void settle(const ChainIn<Tdo> &r) {
-    asm volatile("" ::"v"(r.R), "v"(r.dOa));
-#pragma unroll
-    for (int kb = 0; kb < 8; ++kb) asm volatile("" ::"v"(r.S0s[kb]));
+    asm volatile("" ::"v"(r.R));
 #pragma unroll
     for (int i = 0; i < 4; ++i) asm volatile("" ::"v"((float)r.dOb[i]));
 }
 
 // Unconditional loads: tokens past the sequence end read its last token (masked where used).
 template <typename Tdo>
-__device__ __forceinline__ void chain_load(ChainIn<Tdo> &r, const float *ckpt, const float *rr,
-                                           const Tdo *dout, int64_t slot, int64_t c0, int64_t s1,
-                                           int H, int h, int half, int wave, int lane) {
+__device__ __forceinline__ void chain_load(ChainIn<Tdo> &r, const float *rr, const Tdo *dout,
+                                           int64_t slot, int64_t c0, int64_t s1, int H, int h,
+                                           int half, int wave, int lane) {
     const int lr = lane & 15, lg = lane >> 4;
     const int vbase = 64 * half + 16 * wave;
-    const float *ck = ckpt + ((size_t)slot * H + h) * kHeadDim * kHeadDim;
     r.R = *(const f32x4 *)(rr + ((((size_t)slot * H + h) * 2 + half) * 4 + wave) * 256 + 4 * lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t t = c0 + 4 * lg + i < s1 ? c0 + 4 * lg + i : s1 - 1;
+        r.dOb[i] = dout[((size_t)t * H + h) * kHeadDim + vbase + lr];
+    }
+}
+template <typename Tdo>
+__device__ __forceinline__ void part_load(PartIn<Tdo> &r, const float *ckpt, const Tdo *dout,
+                                          int64_t slot, int64_t c0, int64_t s1, int H, int h,
+                                          int half, int kcol, int lane) {
+    const int lr = lane & 15, lg = lane >> 4;
+    const float *ck = ckpt + ((size_t)slot * H + h) * kHeadDim * kHeadDim;
 #pragma unroll
     for (int vb = 0; vb < 4; ++vb)
 #pragma unroll
         for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                r.S0s[2 * vb + kt][i] = ck[(size_t)(64 * half + 16 * vb + 4 * lg + i) * kHeadDim + 32 * wave + 16 * kt + lr];
-    auto tok = [&](int t) { return c0 + t < s1 ? c0 + t : s1 - 1; };
-    r.dOa = *(const vec4<Tdo> *)(dout + ((size_t)tok(lr) * H + h) * kHeadDim + vbase + 4 * lg);
+                r.S0s[2 * vb + kt][i] = ck[(size_t)(64 * half + 16 * vb + 4 * lg + i) * kHeadDim + kcol + 16 * kt + lr];
+    const int64_t t = c0 + lr < s1 ? c0 + lr : s1 - 1;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.dOb[i] = dout[((size_t)tok(4 * lg + i) * H + h) * kHeadDim + vbase + lr];
+    for (int vb = 0; vb < 4; ++vb)
+        r.dOr[vb] = *(const vec4<Tdo> *)(dout + ((size_t)t * H + h) * kHeadDim + 64 * half + 16 * vb + 4 * lg);
 }
 
+// Eight waves per workgroup (sequence, head, half of the state rows). Waves 0-3
+// (the chain) carry dS for 16 rows each through chunk c: dU, dR (dv), dS0, and
+// write their rows of dS1, U, -dR, dU and R to a share buffer. Waves 4-7 (the
+// partials) meanwhile form the partial sums of chunk c + 1 from the other share
+// buffer, each for 32 key columns over the 64 rows, and write them over the
+// checkpoint rows of that chunk (which only they read, one step earlier). The
+// two MFMA streams share each SIMD; one barrier per step hands the buffers over.
 template <typename Tdo>
-__global__ __launch_bounds__(256) void bwd_chunk_kernel(
-    const float *__restrict__ ops, const int64_t *__restrict__ cu, int N, int H,
-    float *ckpt, const float *__restrict__ rr, const Tdo *__restrict__ dout,
-    const float *__restrict__ dht, float *__restrict__ dv, float *__restrict__ dh0)
+__global__ __launch_bounds__(512) void bwd_chunk_kernel(
+    const float *__restrict__ ops, const int64_t *__restrict__ cu, int N, int H, float *ckpt,
+    const float *__restrict__ rr, const Tdo *__restrict__ dout, const float *__restrict__ dht,
+    float *__restrict__ dv, float *__restrict__ dh0)
 {
     using LY = ChunkLds;
     extern __shared__ __align__(16) float sm[];
@@ -566,9 +589,11 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
     const int n = (int)(nh / H), h = (int)(nh % H);
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+    const bool chainw = wave < 4;
+    const int cw = __builtin_amdgcn_readfirstlane(wave & 3);  // index within the role
     const int lr = lane & 15, lg = lane >> 4;
-    const int vloc = 16 * wave, vbase = 64 * half + vloc;   // this wave's state rows
-    const int kcol = 32 * wave;                              // its key columns of the partials
+    const int vloc = 16 * cw, vbase = 64 * half + vloc;      // a chain wave's state rows
+    const int kcol = 32 * cw;                                // a partial wave's key columns
     const int64_t s0 = cu[n], s1 = cu[n + 1];
     const int64_t nch = (s1 - s0 + kCk - 1) / kCk;
     const int64_t slot0 = s0 / kCk + n;
@@ -576,9 +601,10 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
     const size_t rec_step = (size_t)H * OpRec::END;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-    // dSa[kb]: the adjoint of the state after the current chunk, dS[vbase + lr][16 kb + 4 lg + i]
+    // chain waves: dSa[kb] = dS[vbase + lr][16 kb + 4 lg + i], the adjoint of the
+    // state after the current chunk
     f32x4 dSa[8];
-    if (dht) {
+    if (chainw && dht) {
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb)
             dSa[kb] = *(const f32x4 *)(dht + ((size_t)nh * kHeadDim + vbase + lr) * kHeadDim + 16 * kb + 4 * lg);
@@ -586,157 +612,186 @@ __global__ __launch_bounds__(256) void bwd_chunk_kernel(
 #pragma unroll
         for (int kb = 0; kb < 8; ++kb) dSa[kb] = zero;
     }
-    // settled before the chunk loop (a wait placed inside it would also wait for
-    // the copies issued there)
 #pragma unroll
-    for (int kb = 0; kb < 8; ++kb) asm volatile("" ::"v"(dSa[kb]));
+    for (int kb = 0; kb < 8; ++kb) asm volatile("" ::"v"(dSa[kb]));   // settled before the loop
 
-    // Every input of a chunk is loaded while the chunk after it runs: its
-    // record into the other LDS buffer, the state rows, dO and v alternately
-    // into two register sets (the loop is unrolled twice, so no register copy
-    // of a load in flight is ever needed).
-    ChainIn<Tdo> bufA, bufB;
-    auto chunk = [&](int64_t c, const ChainIn<Tdo> &cur, ChainIn<Tdo> &nxt, int rb)
-        __attribute__((always_inline)) {
-        const float *OP = sm + LY::REC + rb * OpRec::END;
-        const int64_t c0 = s0 + c * kCk;
-        const int L = (int)(s1 - c0 < kCk ? s1 - c0 : kCk);
-        {   // the chunk before (chunk 0 again in the last pass: the loads stay unconditional)
-            const int64_t cp = c > 0 ? c - 1 : 0;
-            copy_record<OpRec::END / 256>(rec0 + cp * rec_step, sm + LY::REC + (rb ^ 1) * OpRec::END, wave, lane);
-            chain_load(nxt, ckpt, rr, dout, slot0 + cp, s0 + cp * kCk, s1, H, h, half, wave, lane);
-        }
-        f32x4 dOb, dOa = f4<Tdo>(cur.dOa);
-        if (lr >= L) dOa = zero;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) dOb[i] = 4 * lg + i < L ? (float)cur.dOb[i] : 0.f;
-        const f32x4 R = cur.R;   // V - KE S0^T ([t][v] accumulator; zero past the end)
-        // KG dS1^T ([t][v] accumulator); dS1 shared
-        f32x4 dUk = zero;
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb) {
-            dUk = bmm16(lds4(OP + OpRec::KG + lr * kTP + 16 * kb + 4 * lg), dSa[kb], dUk);
-            *(f32x4 *)(sm + LY::DS1 + (vloc + lr) * kTP + 16 * kb + 4 * lg) = dSa[kb];
-        }
-        // dS <- dS1 diag(GC) + QG^T dO
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
-            dSa[kb] = bmm16(lds4col(OP + OpRec::QG + (4 * lg) * kTP + 16 * kb + lr, kTP), dOb,
-                            dSa[kb] * lds4(OP + OpRec::GC + 16 * kb + 4 * lg));
-        // U in row layout (the accumulator of U^T = R^T T^T); dU = M^T dO + KG dS1^T;
-        // dR = T^T dU (= dv) and its row layout (the accumulator of dR^T = dU^T T)
-        const f32x4 Trow = lds4(OP + OpRec::T + lr * kSP + 4 * lg);
-        const f32x4 Tcol = lds4col(OP + OpRec::T + (4 * lg) * kSP + lr, kSP);
-        const f32x4 Ua = bmm16(R, Trow, zero);
-        const f32x4 dU = bmm16(lds4col(OP + OpRec::MT + lr * kSP + 4 * lg, 1), dOb, dUk);
-        const f32x4 ndR = -bmm16(Tcol, dU, zero);
-        const f32x4 ndRa = -bmm16(dU, Tcol, zero);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (4 * lg + i < L) dv[((size_t)(c0 + 4 * lg + i) * H + h) * kHeadDim + vbase + lr] = -ndR[i];
-        // dS0^T = ... - KE^T dR
-#pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
-            dSa[kb] = bmm16(lds4col(OP + OpRec::KE + (4 * lg) * kTP + 16 * kb + lr, kTP), ndR, dSa[kb]);
-        // this wave's rows of U, -dR (row layouts), dU, R, dO ([t][v]) shared
-        *(f32x4 *)(sm + LY::US + lr * LY::SP + vloc + 4 * lg) = Ua;
-        *(f32x4 *)(sm + LY::DRS + lr * LY::SP + vloc + 4 * lg) = ndRa;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int o = (4 * lg + i) * LY::SP + vloc + lr;
-            sm[LY::DUS + o] = dU[i];
-            sm[LY::RS + o] = R[i];
-            sm[LY::DOS + o] = dOb[i];
-        }
-        lds_barrier();
+    ChainIn<Tdo> cA, cB;
+    PartIn<Tdo> pA, pB;
+    if (chainw && nch > 0) {
+        const int64_t c = nch - 1;
+        copy_record<OpRec::END / 256>(rec0 + c * rec_step, sm + LY::REC, cw, lane);
+        chain_load(cA, rr, dout, slot0 + c, s0 + c * kCk, s1, H, h, half, cw, lane);
+        wait_vmem_le<0>();
+        settle(cA);
+    }
+    lds_barrier();
 
-        // partials of key columns kcol .. kcol + 31, summed over the 64 rows:
-        // dQG = dO S0, dKG = U dS1, dKE = -dR S0 ([t][k] accumulators), dGC = sum_v S0 dS1
-        f32x4 pq[2] = {zero, zero}, pk[2] = {zero, zero}, pe[2] = {zero, zero};
-        float gs[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-        for (int vb = 0; vb < 4; ++vb) {
-            const f32x4 a_do = lds4(sm + LY::DOS + lr * LY::SP + 16 * vb + 4 * lg);
-            const f32x4 a_u = lds4(sm + LY::US + lr * LY::SP + 16 * vb + 4 * lg);
-            const f32x4 a_dr = lds4(sm + LY::DRS + lr * LY::SP + 16 * vb + 4 * lg);
-#pragma unroll
-            for (int kt = 0; kt < 2; ++kt) {
-                const f32x4 s0c = cur.S0s[2 * vb + kt];
-                const f32x4 ds1c = lds4col(sm + LY::DS1 + (16 * vb + 4 * lg) * kTP + kcol + 16 * kt + lr, kTP);
-                pq[kt] = bmm16(a_do, s0c, pq[kt]);
-                pk[kt] = bmm16(a_u, ds1c, pk[kt]);
-                pe[kt] = bmm16(a_dr, s0c, pe[kt]);
-#pragma unroll
-                for (int i = 0; i < 4; ++i) gs[kt][i] = fmaf(s0c[i], ds1c[i], gs[kt][i]);
-            }
-        }
-        // over this half's checkpoint rows of the chunk, which this workgroup
-        // alone reads and has read (loaded during the chunk after)
-        float *dst = ckpt + ((size_t)(slot0 + c) * H + h) * kHeadDim * kHeadDim + (size_t)half * 64 * kHeadDim;
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int o = (4 * lg + i) * kHeadDim + kcol + 16 * kt + lr;
-                dst[o] = pq[kt][i];
-                dst[2048 + o] = pk[kt][i];
-                dst[4096 + o] = pe[kt][i];
-            }
-        // dGC: the 16 rows 4 lg + i of each block summed over i, then over the four lane groups
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt) {
-            float x = (gs[kt][0] + gs[kt][1]) + (gs[kt][2] + gs[kt][3]);
-            const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-            x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-            const auto b2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-            x = __uint_as_float(b2[0]) + __uint_as_float(b2[1]);
-            if (lg == 0) dst[6656 + kcol + 16 * kt + lr] = x;
-        }
-        // dM = lower(dO U^T) (waves 0, 1) and dT = dU R^T (waves 2, 3), each wave
-        // over 32 of the 64 rows (the final kernel adds the two parts)
+    // Step i: the chain on chunk nch - 1 - i, the partials on chunk nch - i; each
+    // role runs its own loop (so that neither keeps the other's registers live),
+    // with one barrier per step in both.
+    auto cstep = [&](int64_t i, ChainIn<Tdo> &ccur, ChainIn<Tdo> &cnxt) __attribute__((always_inline)) {
+        const int sb = (int)(i & 1);
         {
-            const bool isM = wave < 2;
-            const int A_ = isM ? LY::DOS : LY::DUS, B_ = isM ? LY::US : LY::RS;
-            const int vb0 = 2 * (wave & 1);
-            f32x4 acc = zero;
+            const int64_t c = nch - 1 - i;
+            if (c >= 0) {
+                const float *OP = sm + LY::REC + sb * OpRec::END;
+                float *SH = sm + LY::SH + sb * LY::SHB;
+                const int64_t c0 = s0 + c * kCk;
+                const int L = (int)(s1 - c0 < kCk ? s1 - c0 : kCk);
+                {   // the chunk before (chunk 0 again in the last pass: the loads stay unconditional)
+                    const int64_t cp = c > 0 ? c - 1 : 0;
+                    copy_record<OpRec::END / 256>(rec0 + cp * rec_step, sm + LY::REC + (sb ^ 1) * OpRec::END, cw, lane);
+                    chain_load(cnxt, rr, dout, slot0 + cp, s0 + cp * kCk, s1, H, h, half, cw, lane);
+                }
+                f32x4 dOb;
 #pragma unroll
-            for (int vb = vb0; vb < vb0 + 2; ++vb)
-                acc = bmm16(lds4(sm + A_ + lr * LY::SP + 16 * vb + 4 * lg), lds4(sm + B_ + lr * LY::SP + 16 * vb + 4 * lg), acc);
-            const int off = (isM ? 6144 : 6400) + (wave & 1) * 640;
+                for (int i2 = 0; i2 < 4; ++i2) dOb[i2] = 4 * lg + i2 < L ? (float)ccur.dOb[i2] : 0.f;
+                const f32x4 R = ccur.R;   // V - KE S0^T ([t][v] accumulator; zero past the end)
+                // KG dS1^T ([t][v] accumulator); dS1 shared
+                f32x4 dUk = zero;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int r = 4 * lg + i;
-                dst[off + r * 16 + lr] = (!isM || r >= lr) ? acc[i] : 0.f;
+                for (int kb = 0; kb < 8; ++kb) {
+                    dUk = bmm16(lds4(OP + OpRec::KG + lr * kTP + 16 * kb + 4 * lg), dSa[kb], dUk);
+                    *(f32x4 *)(SH + LY::DS1 + (vloc + lr) * kTP + 16 * kb + 4 * lg) = dSa[kb];
+                }
+                // dS <- dS1 diag(GC) + QG^T dO
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb)
+                    dSa[kb] = bmm16(lds4col(OP + OpRec::QG + (4 * lg) * kTP + 16 * kb + lr, kTP), dOb,
+                                    dSa[kb] * lds4(OP + OpRec::GC + 16 * kb + 4 * lg));
+                // U in row layout (the accumulator of U^T = R^T T^T); dU = M^T dO + KG dS1^T;
+                // dR = T^T dU (= dv) and its row layout (the accumulator of dR^T = dU^T T)
+                const f32x4 Trow = lds4(OP + OpRec::T + lr * kSP + 4 * lg);
+                const f32x4 Tcol = lds4col(OP + OpRec::T + (4 * lg) * kSP + lr, kSP);
+                const f32x4 Ua = bmm16(R, Trow, zero);
+                const f32x4 dU = bmm16(lds4(OP + OpRec::MT + lr * kSP + 4 * lg), dOb, dUk);
+                const f32x4 ndR = -bmm16(Tcol, dU, zero);
+                const f32x4 ndRa = -bmm16(dU, Tcol, zero);
+#pragma unroll
+                for (int i2 = 0; i2 < 4; ++i2)
+                    if (4 * lg + i2 < L) dv[((size_t)(c0 + 4 * lg + i2) * H + h) * kHeadDim + vbase + lr] = -ndR[i2];
+                // dS0^T = ... - KE^T dR
+#pragma unroll
+                for (int kb = 0; kb < 8; ++kb)
+                    dSa[kb] = bmm16(lds4col(OP + OpRec::KE + (4 * lg) * kTP + 16 * kb + lr, kTP), ndR, dSa[kb]);
+                // this wave's rows of U, -dR (row layouts), dU, R ([t][v]) shared
+                *(f32x4 *)(SH + LY::US + lr * LY::SP + vloc + 4 * lg) = Ua;
+                *(f32x4 *)(SH + LY::DRS + lr * LY::SP + vloc + 4 * lg) = ndRa;
+#pragma unroll
+                for (int i2 = 0; i2 < 4; ++i2) {
+                    const int o = (4 * lg + i2) * LY::SP + vloc + lr;
+                    SH[LY::DUS + o] = dU[i2];
+                    SH[LY::RS + o] = R[i2];
+                }
+                // the next record and inputs landed; settled here, where the
+                // hardware has them (the compiler does not see the record copy, so
+                // a wait it placed at the next step would wait for the next copy too)
+                wait_vmem_le<0>();
+                settle(cnxt);
             }
         }
-        // the next record and the chain loads landed (this chunk's partial
-        // stores, at least 24 per wave, may still be in flight); then the
-        // buffers and the shared rows are free for the next chunk
-        wait_vmem_le<24>();
-        // the next chunk's loads are known complete here: settling them now
-        // keeps the compiler from waiting for them at the next chunk's start,
-        // after the copy issued there (which it does not see: such a wait
-        // would wait for that copy as well)
-        settle(nxt);
         lds_barrier();
     };
-    int64_t c = nch - 1;
-    if (c >= 0) {
-        copy_record<OpRec::END / 256>(rec0 + c * rec_step, sm + LY::REC, wave, lane);
-        chain_load(bufA, ckpt, rr, dout, slot0 + c, s0 + c * kCk, s1, H, h, half, wave, lane);
-        wait_vmem_le<0>();
-        lds_barrier();
-    }
-    while (c >= 0) {
-        chunk(c, bufA, bufB, 0);
-        if (--c < 0) break;
-        chunk(c, bufB, bufA, 1);
-        --c;
-    }
-    if (dh0) {
+    auto pstep = [&](int64_t i, PartIn<Tdo> &pcur, PartIn<Tdo> &pnxt) __attribute__((always_inline)) {
+        const int sb = (int)(i & 1);
+        // lane indices taken as new in each step, so that the per-lane offsets are
+        // formed where they are used instead of being kept live (and spilled)
+        int lane = (int)threadIdx.x & 63;
+        asm volatile("" : "+v"(lane));
+        const int lr = lane & 15, lg = lane >> 4;
+        {
+            const int64_t cp = nch - i;            // the partials' chunk
+            if (nch - 1 - i >= 0)                  // inputs of the chunk after it, for the next step
+                part_load(pnxt, ckpt, dout, slot0 + (nch - 1 - i), s0 + (nch - 1 - i) * kCk, s1, H, h,
+                          half, kcol, lane);
+            if (cp <= nch - 1) {
+                const float *SH = sm + LY::SH + (sb ^ 1) * LY::SHB;
+                const int64_t c0 = s0 + cp * kCk;
+                const int L = (int)(s1 - c0 < kCk ? s1 - c0 : kCk);
+                f32x4 dOr[4];
 #pragma unroll
-        for (int kb = 0; kb < 8; ++kb)
-            *(f32x4 *)(dh0 + ((size_t)nh * kHeadDim + vbase + lr) * kHeadDim + 16 * kb + 4 * lg) = dSa[kb];
+                for (int vb = 0; vb < 4; ++vb) dOr[vb] = lr < L ? f4<Tdo>(pcur.dOr[vb]) : zero;
+                // dQG = dO S0, dKG = U dS1, dKE = -dR S0 ([t][k] accumulators), dGC = sum_v S0 dS1
+                f32x4 pq[2] = {zero, zero}, pk[2] = {zero, zero}, pe[2] = {zero, zero};
+                float gs[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+                for (int vb = 0; vb < 4; ++vb) {
+                    const f32x4 a_u = lds4(SH + LY::US + lr * LY::SP + 16 * vb + 4 * lg);
+                    const f32x4 a_dr = lds4(SH + LY::DRS + lr * LY::SP + 16 * vb + 4 * lg);
+#pragma unroll
+                    for (int kt = 0; kt < 2; ++kt) {
+                        const f32x4 s0c = pcur.S0s[2 * vb + kt];
+                        const f32x4 ds1c = lds4col(SH + LY::DS1 + (16 * vb + 4 * lg) * kTP + kcol + 16 * kt + lr, kTP);
+                        pq[kt] = bmm16(dOr[vb], s0c, pq[kt]);
+                        pk[kt] = bmm16(a_u, ds1c, pk[kt]);
+                        pe[kt] = bmm16(a_dr, s0c, pe[kt]);
+#pragma unroll
+                        for (int i2 = 0; i2 < 4; ++i2) gs[kt][i2] = fmaf(s0c[i2], ds1c[i2], gs[kt][i2]);
+                    }
+                }
+                // over this half's checkpoint rows of the chunk, which these waves
+                // alone read and have read (loaded one step earlier)
+                float *dst = ckpt + ((size_t)(slot0 + cp) * H + h) * kHeadDim * kHeadDim + (size_t)half * 64 * kHeadDim;
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+                    for (int i2 = 0; i2 < 4; ++i2) {
+                        const int o = (4 * lg + i2) * kHeadDim + kcol + 16 * kt + lr;
+                        dst[o] = pq[kt][i2];
+                        dst[2048 + o] = pk[kt][i2];
+                        dst[4096 + o] = pe[kt][i2];
+                    }
+                // dGC: the 16 rows 4 lg + i of each block summed over i, then over the four lane groups
+#pragma unroll
+                for (int kt = 0; kt < 2; ++kt) {
+                    float x = (gs[kt][0] + gs[kt][1]) + (gs[kt][2] + gs[kt][3]);
+                    const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+                    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+                    const auto b2 = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+                    x = __uint_as_float(b2[0]) + __uint_as_float(b2[1]);
+                    if (lg == 0) dst[6656 + kcol + 16 * kt + lr] = x;
+                }
+                // dM = lower(dO U^T) (waves 4, 5) and dT = dU R^T (waves 6, 7), each
+                // over 32 of the 64 rows (the final kernel adds the two parts)
+                {
+                    const bool isM = cw < 2;
+                    const int vb0 = 2 * (cw & 1);
+                    f32x4 acc = zero;
+#pragma unroll
+                    for (int vb = vb0; vb < vb0 + 2; ++vb) {
+                        const f32x4 a_ = isM ? dOr[vb] : lds4(SH + LY::DUS + lr * LY::SP + 16 * vb + 4 * lg);
+                        acc = bmm16(a_, lds4(SH + (isM ? LY::US : LY::RS) + lr * LY::SP + 16 * vb + 4 * lg), acc);
+                    }
+                    const int off = (isM ? 6144 : 6400) + (cw & 1) * 640;
+#pragma unroll
+                    for (int i2 = 0; i2 < 4; ++i2) {
+                        const int r = 4 * lg + i2;
+                        dst[off + r * 16 + lr] = (!isM || r >= lr) ? acc[i2] : 0.f;
+                    }
+                }
+            }
+        }
+        lds_barrier();
+    };
+    if (chainw) {
+        for (int64_t i = 0;; i += 2) {
+            cstep(i, cA, cB);
+            if (i + 1 > nch) break;
+            cstep(i + 1, cB, cA);
+            if (i + 2 > nch) break;
+        }
+        if (dh0) {
+#pragma unroll
+            for (int kb = 0; kb < 8; ++kb)
+                *(f32x4 *)(dh0 + ((size_t)nh * kHeadDim + vbase + lr) * kHeadDim + 16 * kb + 4 * lg) = dSa[kb];
+        }
+    } else {
+        for (int64_t i = 0;; i += 2) {
+            pstep(i, pA, pB);
+            if (i + 1 > nch) break;
+            pstep(i + 1, pB, pA);
+            if (i + 2 > nch) break;
+        }
     }
 }
 
@@ -1070,7 +1125,7 @@ hipError_t launch_backward_t(const BackwardArgs &a) {
     static std::atomic<uint64_t> chunk_lds{0}, final_lds{0};
     e = set_lds_limit((const void *)&bwd_chunk_kernel<Tdo>, (int)ChunkLds::BYTES, chunk_lds);
     if (e != hipSuccess) return e;
-    bwd_chunk_kernel<Tdo><<<grid, 256, ChunkLds::BYTES, a.stream>>>(
+    bwd_chunk_kernel<Tdo><<<grid, 512, ChunkLds::BYTES, a.stream>>>(
         a.ops, a.cu, a.N, a.H, a.ckpt, a.rr, (const Tdo *)a.dout, a.dht, a.dv, a.dh0);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
