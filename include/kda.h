@@ -436,22 +436,27 @@ kda_status_t kda_backward_grouped(const void *q, const void *k, const void *v, c
  * the o store (kimi_k3 FusedKDAChunkwise page, "Output handling": per-head norm
  * of each output row, then the sigmoid output gate): o receives
  *   y = o_kda / sqrt(mean(o_kda^2) + norm_eps) * norm_weight * sigmoid(z)
- * computed in fp32 from the unrounded fp32 outputs (for bf16 o they are staged
- * in the workspace, sized by kda_chunk_fwd_gated_workspace_size) and rounded
- * once to o_dtype. z: [T, H, V] gate
+ * computed in fp32 from the fp32 outputs and rounded once to o_dtype. z: [T, H, V] gate
  * logits in in_dtype (must not overlap o; may be NULL only when
  * total_tokens = 0); norm_weight: [V] fp32; norm_eps finite and > 0. Other
  * arguments, layouts and errors as kda_chunk_fwd, with the workspace sized by
- * kda_chunk_fwd_gated_workspace_size. The epilogue runs as a pass over the
- * outputs, enqueued right after the inter-chunk kernel: the rows of one
- * output come from two workgroups of that kernel (one per half of the state),
- * so a whole row exists only once both have stored it, and o is then still in
- * the memory-side cache.
+ * kda_chunk_fwd_gated_workspace_size. The rows of one output come from two
+ * workgroups of the inter-chunk kernel (one per half of the state). With
+ * K = V = 128, chunk_size 64 and bf16 inputs, when the batch's N * H chains
+ * fit the GPU at once (two workgroups each, one per CU), that kernel applies
+ * the epilogue itself: the two workgroups of a chain exchange their halves'
+ * row sums of squares through the workspace. Otherwise the epilogue is a pass
+ * over the outputs right after the inter-chunk kernel: fp32 results in
+ * place, bf16 results staged in the workspace, in fp32, or at K = V = 128,
+ * chunk 64, bf16 inputs in fp16 with a power-of-two scale per 16 features
+ * (each value then within 2^-11 of its 16 features' largest magnitude).
  */
-/* Workspace bytes kda_chunk_fwd_gated needs: kda_chunk_fwd_workspace_size, plus
- * T * H * V * 4 bytes (after rounding that up to 256) when o_dtype is bf16,
- * where the outputs are staged in fp32 for the epilogue so that the result is
- * rounded once. 0 for invalid arguments. */
+/* Workspace bytes kda_chunk_fwd_gated needs: kda_chunk_fwd_workspace_size,
+ * rounded up to 256, plus, at K = V = 128 with chunk_size 64 and bf16 inputs,
+ * the larger of the row-sum exchange (8 * 128 * H * (T / 64 + N) bytes) and,
+ * for bf16 o, the staged outputs (T * H * (2 V + V / 4) bytes); in other
+ * configurations, for bf16 o, T * H * V * 4 bytes of fp32 staging (nothing for
+ * fp32 o). 0 for invalid arguments. */
 size_t kda_chunk_fwd_gated_workspace_size(int64_t total_tokens, int32_t num_seqs,
                                           int32_t H, int32_t K, int32_t V,
                                           int32_t chunk_size, kda_dtype_t in_dtype,

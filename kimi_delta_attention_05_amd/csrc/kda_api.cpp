@@ -293,9 +293,20 @@ size_t kda_chunk_fwd_gated_workspace_size(int64_t total_tokens, int32_t num_seqs
                                                      in_dtype);
     if (base == 0) return 0;
     if (!valid_dtype(o_dtype)) { fail(KDA_ERR_UNSUPPORTED, "unknown output dtype"); return 0; }
-    if (o_dtype != KDA_BF16) return base;
-    // bf16 results: the outputs are staged in fp32 for the epilogue
-    return ((base + 255) & ~(size_t)255) + (size_t)total_tokens * H * V * 4;
+    const size_t rows = (size_t)total_tokens * H;
+    size_t extra = 0;
+    if (native_head_size(K, V, chunk_size, in_dtype) == 128 && chunk_size == 64 &&
+        in_dtype == KDA_BF16) {
+        // the epilogue fused in the inter-chunk kernel: its row-sum exchange; when
+        // the batch has too many sequences for that, bf16 results are staged in
+        // fp16 with a power-of-two scale per 16 features
+        const size_t xchg = (size_t)kda::num_slots(total_tokens, num_seqs, 64) * H * 128 * 8;
+        const size_t staged = o_dtype == KDA_BF16 ? rows * V * 2 + rows * (V / 16) * 4 : 0;
+        extra = xchg > staged ? xchg : staged;
+    } else if (o_dtype == KDA_BF16) {
+        extra = rows * V * 4;           // bf16 results staged in fp32
+    }
+    return extra ? ((base + 255) & ~(size_t)255) + extra : base;
 }
 
 }  // extern "C"
@@ -386,21 +397,41 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
     a.ws = (unsigned char *)workspace;
     a.stream = (hipStream_t)stream;
     a.stages = stages;
-    // The output epilogue, when asked for: a pass over the V-wide output rows,
-    // right after the inter-chunk kernel on the same stream (its outputs are
-    // still in the memory-side cache then). It reads the outputs unrounded:
-    // fp32 results in place, bf16 results from fp32 outputs staged in the
-    // workspace after the part kda_chunk_fwd uses, so that y is rounded once.
-    const bool stage_o = z && o_dtype == KDA_BF16;
-    unsigned char *const o32 =
-        stage_o ? (unsigned char *)workspace +
-                      ((kda_chunk_fwd_workspace_size(total_tokens, num_seqs, H, K, V, chunk_size,
-                                                     in_dtype) + 255) & ~(size_t)255)
-                : nullptr;
+    // The output epilogue, when asked for. The natively sized K = V = 128
+    // kernels with 64-row chunks of bf16 inputs apply it in the inter-chunk
+    // kernel when all of that kernel's workgroups fit the GPU at once (the two
+    // workgroups of a chain exchange row sums through the workspace, after the
+    // part kda_chunk_fwd uses). Otherwise it is a pass over the V-wide output
+    // rows right after the inter-chunk kernel on the same stream (the outputs
+    // are still in the memory-side cache then), reading them unrounded: fp32
+    // results in place, bf16 results staged in the workspace after the part
+    // kda_chunk_fwd uses, so that y is rounded once.
+    const int native = native_head_size(K, V, chunk_size, in_dtype);
+    unsigned char *const extra =
+        z ? (unsigned char *)workspace +
+                ((kda_chunk_fwd_workspace_size(total_tokens, num_seqs, H, K, V, chunk_size,
+                                               in_dtype) + 255) & ~(size_t)255)
+          : nullptr;
+    bool fuse = false;
+    if (z && native == 128 && total_tokens > 0) {
+        kda::PrefillArgs t = a;
+        t.D = native;
+        const hipError_t e = kda::prefill_gate_fusable(t, fuse);
+        if (e != hipSuccess) return hip_fail(e, name);
+    }
+    const bool stage_o = z && !fuse && o_dtype == KDA_BF16;
+    unsigned char *const o32 = stage_o ? extra : nullptr;
+    // The natively sized K = V = 128 kernels with 64-row chunks and bf16 inputs
+    // stage the outputs in half the bytes: fp16 with a power-of-two scale per
+    // 16-feature block of each row (T x H x 8 fp32 scales after the rows).
+    const bool stage_h = stage_o && native == 128 && chunk_size == 64 && in_dtype == KDA_BF16;
+    float *const o_sc =
+        stage_h ? (float *)(o32 + (size_t)total_tokens * H * V * sizeof(uint16_t)) : nullptr;
     auto epilogue = [&]() -> hipError_t {
-        if (!z || total_tokens == 0) return hipSuccess;
+        if (!z || fuse || total_tokens == 0) return hipSuccess;
         kda::NormGateArgs ng;
         ng.o = stage_o ? (const void *)o32 : o; ng.z = z; ng.w = norm_weight; ng.eps = norm_eps;
+        ng.o_scale = o_sc;
         ng.rows = total_tokens * H; ng.D = V;
         ng.bf16 = !stage_o && o_dtype == KDA_BF16; ng.z_bf16 = in_dtype == KDA_BF16;
         ng.y_bf16 = o_dtype == KDA_BF16; ng.y = o;
@@ -408,10 +439,14 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
         return kda::launch_norm_gate(ng);
     };
     if (stage_o) a.out_bf16 = false;
-    const int native = native_head_size(K, V, chunk_size, in_dtype);
     if (native) {
         a.D = native;
+        if (fuse) {
+            a.z = z; a.norm_w = norm_weight; a.norm_eps = norm_eps;
+            a.xchg = (uint64_t *)extra;
+        }
         if (stage_o) a.o = o32;
+        a.o_scale = o_sc;
         hipError_t e = kda::launch_prefill(a);
         if (e == hipSuccess) e = epilogue();
         if (e != hipSuccess) return hip_fail(e, name);

@@ -38,6 +38,40 @@ __global__ __launch_bounds__(256) void norm_gate_kernel(const To *o, const Tz *_
     if (valid) store8_nt<Ty>(y + base, out);
 }
 
+// Rows staged as fp16 by the chunkwise forward: each 16-feature block of a row
+// holds its values divided by a power of two, kept in sc[row][block]; lane j
+// takes the scale of block j / 2. The products with the scales are exact, so y
+// is rounded once, from the staged fp16 values.
+template <typename Tz, typename Ty>
+__global__ __launch_bounds__(256) void norm_gate_scaled_kernel(const _Float16 *__restrict__ o,
+                                                               const float *__restrict__ sc,
+                                                               const Tz *__restrict__ z,
+                                                               const float *__restrict__ w, float eps,
+                                                               int64_t rows, Ty *__restrict__ y)
+{
+    const int j = threadIdx.x & 15;
+    const int64_t row = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+    const bool valid = row < rows;
+    const size_t r0 = (size_t)(valid ? row : rows - 1);
+    const size_t base = r0 * kHeadDim + 8 * j;
+    const half8 h = *(const half8 *)(o + base);
+    const float s = sc[r0 * (kHeadDim / 16) + (j >> 1)];
+    float x[8], g[8], wv[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)h[e] * s;
+    load8(z + base, g);
+    load8(w + 8 * j, wv);
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ss = fmaf(x[e], x[e], ss);
+    ss = row16_sum(ss);
+    const float r = rsqrtf(ss * (1.0f / kHeadDim) + eps);
+    float out[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = x[e] * r * wv[e] * sigmoid_f(g[e]);
+    if (valid) store8_nt<Ty>(y + base, out);
+}
+
 // Rows of any other width D <= 256 (head sizes other than 128): one wave per
 // row, lane l holding features l, l + 64, l + 128, l + 192 below D, the sum of
 // squares reduced over the wave.
@@ -66,6 +100,15 @@ __global__ __launch_bounds__(256) void norm_gate_any_kernel(const To *o,
     }
 }
 
+template <typename Tz, typename Ty>
+static hipError_t launch_norm_gate_scaled_t(const NormGateArgs &a) {
+    if (a.D != kHeadDim) return hipErrorInvalidValue;
+    const int64_t blocks = (a.rows + 15) / 16;
+    norm_gate_scaled_kernel<Tz, Ty><<<(unsigned)blocks, 256, 0, a.stream>>>(
+        (const _Float16 *)a.o, a.o_scale, (const Tz *)a.z, a.w, a.eps, a.rows, (Ty *)a.y);
+    return hipGetLastError();
+}
+
 template <typename To, typename Tz, typename Ty>
 static hipError_t launch_norm_gate_t(const NormGateArgs &a) {
     if (a.D != kHeadDim) {
@@ -92,6 +135,12 @@ static hipError_t launch_norm_gate_z(const NormGateArgs &a) {
 
 hipError_t launch_norm_gate(const NormGateArgs &a) {
     if (a.rows <= 0) return hipSuccess;
+    if (a.o_scale) {                    // fp16 rows with block scales
+        if (a.z_bf16) return a.y_bf16 ? launch_norm_gate_scaled_t<__bf16, __bf16>(a)
+                                      : launch_norm_gate_scaled_t<__bf16, float>(a);
+        return a.y_bf16 ? launch_norm_gate_scaled_t<float, __bf16>(a)
+                        : launch_norm_gate_scaled_t<float, float>(a);
+    }
     return a.bf16 ? launch_norm_gate_z<__bf16>(a) : launch_norm_gate_z<float>(a);
 }
 

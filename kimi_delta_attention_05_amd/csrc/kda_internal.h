@@ -38,6 +38,9 @@ struct NormGateArgs {
     int64_t rows;
     int D = 128;                        // features per row (128, or any width up to 256)
     bool bf16;                          // dtype of o
+    // when set (D = 128): o is fp16, each row's 16-value block to be multiplied by
+    // o_scale [rows, 8]
+    const float *o_scale = nullptr;
     bool z_bf16 = false;                // dtype of z
     bool y_bf16 = false;                // dtype of y
     void *y;
@@ -62,6 +65,17 @@ struct PrefillArgs {
     hipStream_t stream;
     int stages;          // bit 0: intra-chunk kernel, bit 1: inter-chunk kernel
     int D = 128;         // head size K = V: 128, or 64 (64-row chunks of bf16 inputs only)
+    // when set (D = 128, 64-row chunks, bf16 inputs): o is fp16, each row's 16-value
+    // block divided by the power of two in o_scale [T, H, D / 16]
+    float *o_scale = nullptr;
+    // when z is set (D = 128, 64-row chunks, bf16 inputs, both stages; see
+    // prefill_gate_fusable): o receives y = o / sqrt(mean(o^2) + norm_eps) *
+    // norm_w * sigmoid(z) per row, z [T, H, 128] bf16, norm_w [128]; xchg: the
+    // halves' row-sum exchange, num_slots * H * 128 words of workspace
+    const void *z = nullptr;
+    const float *norm_w = nullptr;
+    float norm_eps = 0.f;
+    uint64_t *xchg = nullptr;
 };
 
 // Geometry of one chunk of C rows (C = 16, 32 or 64).
@@ -211,6 +225,7 @@ hipError_t launch_stream_copy(const void *src, void *dst, size_t bytes, hipStrea
 
 hipError_t launch_decode(const DecodeArgs &a);
 hipError_t launch_norm_gate(const NormGateArgs &a);
+hipError_t prefill_gate_fusable(const PrefillArgs &a, bool &fusable);
 hipError_t launch_prefill(const PrefillArgs &a);
 hipError_t launch_short_conv(const ShortConvArgs &a);
 

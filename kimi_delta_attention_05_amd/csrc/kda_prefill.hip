@@ -857,8 +857,32 @@ template <> __device__ __forceinline__ void store4<__bf16>(__bf16 *p, const f32x
     *(bf16x4 *)p = bf16x4{(__bf16)x[0], (__bf16)x[1], (__bf16)x[2], (__bf16)x[3]};
 }
 
-template <int C, typename Tout, bool PRECISE, int D = 128>
-__global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
+// Polls of the other half's row sums before a fused epilogue gives up (about a
+// second): the workgroup's outputs are then NaN rather than a hang.
+constexpr int kXchgSpin = 1 << 20;
+
+// GATE (64-row chunks of bf16 inputs, D = 128): the output epilogue fused in
+// (kimi_k3 FusedKDAChunkwise page, "Output handling": per-row RMS norm over the
+// 128 features, channel weight, sigmoid output gate). A row's features come
+// from the two workgroups of its chain, 64 each, so its sum of squares is
+// completed across them. A fifth wave per workgroup does that, one chunk step
+// behind the four state waves each time:
+//   step j     the state waves leave chunk j's partial sums of squares in LDS
+//              and keep its outputs x = O sigma in registers;
+//   step j + 1 the fifth wave adds up this half's sums and posts them for the
+//              other workgroup (a (sum, tag) word per row in the workspace,
+//              zeroed before the launch);
+//   step j + 2 it asks for the other half's sums (posted a step earlier) and
+//              loads the chunk's gate logits;
+//   step j + 3 it forms r = 1 / sqrt(mean(o^2) + eps) per row and leaves r and
+//              the logits in LDS;
+//   step j + 4 the state waves store y = x r w sigmoid(z).
+// Every load has a whole step to arrive: the exchange goes through the
+// device-coherent level of the memory hierarchy (the two workgroups need not
+// share an L2). The two workgroups of a chain must be resident at the same
+// time: the launch keeps the whole grid within one round of workgroups.
+template <int C, typename Tout, bool PRECISE, int D = 128, bool GATE = false>
+__global__ __launch_bounds__(GATE ? 320 : 256) void inter_kernel(PrefillArgs p, int nchains)
 {
     using G = ChunkGeom<C>;
     using R = Record<C, PRECISE, D>;
@@ -909,6 +933,92 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
     const int64_t len = p.cu_seqlens[n + 1] - s0;
     const int nch = (int)((len + C - 1) / C);
     const int64_t slot0 = s0 / C + n;
+
+    // fused epilogue, after the record buffers: the state waves' partial row
+    // sums [2][64 rows][4 waves][4 column groups], the rows' inverse rms
+    // [2][64] and a chunk's gate logits for this half [2][64 rows][64] (bf16)
+    float *const ssw = (float *)(smem + CFG::NBUF * CFG::BUF);
+    float *const rinv = ssw + 2 * 64 * 16;
+    unsigned char *const szb = (unsigned char *)(rinv + 2 * 64);
+    if constexpr (GATE) {
+        static_assert(D == 128 && HALVES == 2 && CFG::NBUF == 2, "fused epilogue: two halves, two buffers");
+        if (wave == 4) {
+            // The fifth wave: one barrier per state-wave step 0 .. nch + 2 (the
+            // state waves' last step, nch + 3, has none). In step jc it posts this
+            // half's row sums of chunk jc - 1 and asks for the other half's of
+            // chunk jc - 2 (posted a step earlier); in step jc + 1 it forms their
+            // r from the answer and leaves chunk jc - 2's gate logits in LDS.
+            // (Forming sigmoid(z) here measured slower: this wave shares a SIMD
+            // with a state wave, whose arithmetic it then delays.) Every step issues the
+            // same loads and stores (steps without a chunk use chunk 0 and a
+            // spare word), so that the waits the compiler places for them count
+            // right and leave them in flight across the step.
+            if (nch <= 0) return;
+            lds_barrier();
+            uint64_t *const xc = p.xchg + ((size_t)slot0 * H + h) * 128 + lane;
+            const size_t xstep = (size_t)H * 128;
+            uint64_t *const spare = (uint64_t *)(p.ws + (size_t)num_slots(p.T, p.N, C) * H * R::BYTES + 128);
+            bool gave_up = false;       // after one wait ran out, no more waiting
+            // gate rows of a chunk, eight per load: lane holds row 8 c + lane / 8,
+            // columns 8 (lane % 8) .. + 7 of this half
+            i32x4 zv[8];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) zv[c] = i32x4{0, 0, 0, 0};
+            uint64_t other = 0;
+            float own_a = 0.f, own_b = 0.f;     // this half's sums of chunks jc - 3, jc - 2
+            for (int jc = 0; jc <= nch + 2; ++jc) {
+                // chunk jc - 3's gate, loaded in the last step, into LDS buffer (jc - 3) & 1
+                unsigned char *const dst = szb + ((jc + 1) & 1) * 8192 + 16 * lane;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) *(i32x4 *)(dst + 1024 * c) = zv[c];
+                // r of chunk jc - 3 from the other half's answer
+                if (jc >= 3) {
+                    const int j = jc - 3;
+                    const uint32_t tag = (uint32_t)j + 1u;
+                    if (__builtin_amdgcn_ballot_w64((uint32_t)(other >> 32) != tag) != 0) {
+                        const uint64_t *const eo = xc + (size_t)j * xstep + 64 * (vg ^ 1);
+                        for (int it = 0;; ++it) {
+                            if (gave_up || it >= kXchgSpin) { other = 0x7fc00000u; gave_up = true; break; }
+                            __builtin_amdgcn_s_sleep(1);
+                            other = __hip_atomic_load(eo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                            if (__builtin_amdgcn_ballot_w64((uint32_t)(other >> 32) != tag) == 0) break;
+                        }
+                    }
+                    const float ot = __uint_as_float((uint32_t)other);
+                    const float tot = vg == 0 ? own_a + ot : ot + own_a;   // the same order in both
+                    rinv[(j & 1) * 64 + lane] = rsqrtf(tot * (1.0f / D) + p.norm_eps);
+                }
+                // the other half's sums of chunk jc - 2, asked for
+                const int jo = jc >= 2 ? jc - 2 : 0;
+                other = __hip_atomic_load(xc + (size_t)jo * xstep + 64 * (vg ^ 1), __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+                // chunk jc - 2's gate logits (rows past the sequence end repeat its last row)
+                const int64_t t0 = (int64_t)(jc < 2 ? 0 : (jc - 2 < nch ? jc - 2 : nch - 1)) * C;
+#pragma unroll
+                for (int c = 0; c < 8; ++c) {
+                    const int64_t t = t0 + 8 * c + (lane >> 3);
+                    zv[c] = *(const i32x4 *)((const __bf16 *)p.z + ((size_t)(s0 + (t < len ? t : len - 1)) * H + h) * D +
+                                             64 * vg + 8 * (lane & 7));
+                }
+                // this half's sums of chunk jc - 1, posted
+                const int jp = jc - 1;
+                const f32x4 *const pw = (const f32x4 *)(ssw + ((jp & 1) * 64 + lane) * 16);
+                f32x4 ps[4];
+#pragma unroll
+                for (int w4 = 0; w4 < 4; ++w4) ps[w4] = pw[w4];     // state wave w4's four column groups
+                float own = 0.f;
+#pragma unroll
+                for (int w4 = 0; w4 < 4; ++w4) own += (ps[w4][0] + ps[w4][1]) + (ps[w4][2] + ps[w4][3]);
+                __hip_atomic_store(jc >= 1 && jc <= nch ? xc + (size_t)jp * xstep + 64 * vg : spare,
+                                   ((uint64_t)(jp + 1) << 32) | __float_as_uint(own),
+                                   __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                own_a = own_b;
+                own_b = own;
+                lds_barrier();
+            }
+            return;
+        }
+    }
 
     // State S^T tiles: lane holds S[vrow][tile_chan(kb, 4 lg + i)] (the row order
     // of the kg^T tiles it accumulates from). On the fp16 path the
@@ -985,6 +1095,24 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
     Tout *__restrict__ o = (Tout *)p.o + ((size_t)(s0 + lr) * H + h) * D + 16 * vb + 4 * lg;
     Tout *const o_spare = (Tout *)(p.ws + (size_t)num_slots(p.T, p.N, C) * H * R::BYTES);
     const size_t o_tb = (size_t)16 * H * D, o_chunk = (size_t)C * H * D;
+    // fp16 outputs (staged for the output epilogue): each row's 16-value block
+    // vb is stored divided by a power-of-two scale (its largest magnitude below
+    // 2^15, so no overflow and half an fp16 ulp of the block's largest value),
+    // the scale in o_scale[row][vb]; the spare tail takes the scales of rows
+    // past the sequence end too
+    constexpr bool SCALED = std::is_same<Tout, _Float16>::value;
+    static_assert(!(SCALED && GATE), "the fused epilogue stores bf16 or fp32");
+    // fused epilogue: chunk j's outputs x (O sigma) wait four steps in xa .. xd
+    // (xn: the step's new chunk); the lane's four columns 16 vb + 4 lg + i of
+    // the norm weight
+    typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+    [[maybe_unused]] f32x4 xa[NB], xb[NB], xc[NB], xd[NB], xn[NB], wv = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int tb = 0; tb < NB; ++tb) xa[tb] = xb[tb] = xc[tb] = xd[tb] = xn[tb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (GATE) wv = *(const f32x4 *)(p.norm_w + 16 * vb + 4 * lg);
+    float *__restrict__ osc = SCALED ? p.o_scale + ((size_t)(s0 + lr) * H + h) * (D / 16) + vb : nullptr;
+    float *const osc_spare = (float *)o_spare + 16;
+    const size_t osc_tb = (size_t)16 * H * (D / 16), osc_chunk = (size_t)C * H * (D / 16);
 
     if (nch > 0) {
         fetch(0, 0, 0, NCP);
@@ -992,13 +1120,29 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
         wait_vmem();
         lds_barrier();
     }
-    for (int jc = 0; jc < nch; ++jc) {
+    // with the fused epilogue four more steps store the last four chunks' rows
+    const int nsteps = GATE ? (nch > 0 ? nch + 4 : 0) : nch;
+    for (int jc = 0; jc < nsteps; ++jc) {
         const int buf = (CFG::NBUF == 2) ? (jc & 1) : 0;
         const bool ahead = CFG::NBUF == 2 && jc + 1 < nch;
         const unsigned char *B = smem + (size_t)buf * CFG::BUF;
         const int L = (len - (int64_t)jc * C) < C ? (int)(len - (int64_t)jc * C) : C;
         if (ahead) fetch(jc + 1, buf ^ 1, 0, NCP);
-        touch(jc + 2 < nch ? jc + 2 : jc);
+        [[maybe_unused]] float ry[NB];
+        [[maybe_unused]] bf16x4_t zy[NB];
+        if constexpr (GATE) {
+            touch(jc + 2 < nch ? jc + 2 : nch - 1);   // every step issues the same loads
+            // r and z of the rows of chunk jc - 4, for the step's end
+            const int jy = jc - 4;
+#pragma unroll
+            for (int tb = 0; tb < NB; ++tb) {
+                ry[tb] = rinv[(jy & 1) * 64 + 16 * tb + lr];
+                zy[tb] = *(const bf16x4_t *)(szb + (jy & 1) * 8192 + (16 * tb + lr) * 128 + 32 * wave + 8 * lg);
+            }
+        } else {
+            touch(jc + 2 < nch ? jc + 2 : jc);
+        }
+        if (!GATE || jc < nch) {
 
         // operands are requested one 16-row tile ahead of the products using them
         auto frag = [&](size_t off, int idx) { return F::load(B + off + ((size_t)idx * 64 + lane) * F::BYTES); };
@@ -1147,19 +1291,67 @@ __global__ __launch_bounds__(256) void inter_kernel(PrefillArgs p, int nchains)
             S[kb] = acc;
         }
 
+        if constexpr (GATE) {
+            // keep x, leave its rows' 16-column sums of squares for the fifth wave
 #pragma unroll
-        for (int tb = 0; tb < NB; ++tb)
-            store4<Tout>(16 * tb + lr < L ? o + tb * o_tb : o_spare, O[tb] * sigma);
-        o += o_chunk;
-        if (jc + 1 < nch) {
+            for (int tb = 0; tb < NB; ++tb) {
+                const f32x4 x = O[tb] * sigma;
+                xn[tb] = x;
+                ssw[((jc & 1) * 64 + 16 * tb + lr) * 16 + 4 * wave + lg] =
+                    (x[0] * x[0] + x[1] * x[1]) + (x[2] * x[2] + x[3] * x[3]);
+            }
+        } else if constexpr (SCALED) {
+#pragma unroll
+            for (int tb = 0; tb < NB; ++tb) {
+                const f32x4 x = O[tb] * sigma;
+                // largest magnitude of the row's block: the lane's four values, then
+                // the four lanes lr + 16 lg holding the block's other values
+                float m = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+                const auto a32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+                m = fmaxf(__uint_as_float(a32[0]), __uint_as_float(a32[1]));
+                const auto a16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+                m = fmaxf(__uint_as_float(a16[0]), __uint_as_float(a16[1]));
+                const float sc = pow2_scale_for(m, 15), inv = inv_pow2(sc);
+                const bool in = 16 * tb + lr < L;
+                *(half4_t *)(in ? o + tb * o_tb : o_spare) =
+                    half4_t{(_Float16)(x[0] * inv), (_Float16)(x[1] * inv), (_Float16)(x[2] * inv), (_Float16)(x[3] * inv)};
+                *(in ? osc + tb * osc_tb : osc_spare) = sc;   // the four lanes of a block store the same value
+            }
+            osc += osc_chunk;
+        } else {
+#pragma unroll
+            for (int tb = 0; tb < NB; ++tb)
+                store4<Tout>(16 * tb + lr < L ? o + tb * o_tb : o_spare, O[tb] * sigma);
+        }
+        if constexpr (!GATE) o += o_chunk;
+        }   // the chunk's products
+        if constexpr (GATE) {
+            // rows of chunk jc - 4: y = x r w sigmoid(z), r and z (read at the
+            // step start) left by the fifth wave
+            const int jy = jc - 4;
+            const int Ly = jy < 0 ? 0 : ((len - (int64_t)jy * C) < C ? (int)(len - (int64_t)jy * C) : C);
+#pragma unroll
+            for (int tb = 0; tb < NB; ++tb) {
+                f32x4 y;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) y[i] = xa[tb][i] * ry[tb] * wv[i] * sigmoid_f((float)zy[tb][i]);
+                store4<Tout>(16 * tb + lr < Ly ? o + (size_t)jy * o_chunk + tb * o_tb : o_spare, y);
+            }
+#pragma unroll
+            for (int tb = 0; tb < NB; ++tb) { xa[tb] = xb[tb]; xb[tb] = xc[tb]; xc[tb] = xd[tb]; xd[tb] = xn[tb]; }
+            // the copies issued at the step start have landed; the NB output
+            // stores issued after them may still be in flight
+            if (jc + 1 < nch) wait_vmem_except<NB>();
+            if (jc <= nch + 2) lds_barrier();
+        } else if (jc + 1 < nch) {
             if (CFG::NBUF == 1) {
                 lds_barrier();            // everyone is done with the single buffer
                 fetch(jc + 1, 0, 0, NCP);
                 wait_vmem();
             } else {
                 // the copies and touches issued at the chunk start have landed; the
-                // NB output stores issued since (the newest) may still be in flight
-                wait_vmem_except<NB>();
+                // output stores issued since (the newest) may still be in flight
+                wait_vmem_except<(SCALED ? 2 : 1) * NB>();
             }
             lds_barrier();                // ... and everyone else's
         }
@@ -1748,6 +1940,11 @@ static hipError_t cu_count(int &cus) {
 }
 
 // One flag word per kernel: bit d set once the dynamic-LDS limit is set on device d.
+// Zeroes n 8-byte words (grid-stride).
+__global__ __launch_bounds__(256) void zero_words_kernel(uint64_t *p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0;
+}
+
 static hipError_t set_lds_limit(const void *fn, int lds, std::atomic<uint64_t> &done) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -1794,6 +1991,21 @@ static hipError_t launch_prefill_t(const PrefillArgs &a) {
         if (e != hipSuccess) return e;
         // one workgroup per 64 state rows of a chain (two at D = 128)
         const unsigned groups = (unsigned)(8 * (D / 64) * ((nchains + 7) / 8));
+        if constexpr (C == 64 && !PRECISE && D == 128 && !std::is_same<Tout, _Float16>::value) {
+            if (a.z) {                  // the fused output epilogue
+                constexpr size_t lds_g = CFG::NBUF * CFG::BUF + (2 * 64 * 16 + 2 * 64) * sizeof(float) + 2 * 8192;
+                static_assert(lds_g <= 160 * 1024, "LDS");
+                static std::atomic<uint64_t> lds_g_set{0};
+                e = set_lds_limit((const void *)inter_kernel<C, Tout, PRECISE, D, true>, (int)lds_g, lds_g_set);
+                if (e != hipSuccess) return e;
+                const size_t words = (size_t)num_slots(a.T, a.N, C) * a.H * 128;
+                zero_words_kernel<<<(unsigned)((words + 255) / 256 < 4096 ? (words + 255) / 256 : 4096), 256, 0,
+                                    a.stream>>>(a.xchg, words);
+                inter_kernel<C, Tout, PRECISE, D, true><<<groups, 320, lds_g, a.stream>>>(a, nchains);
+                return hipGetLastError();
+            }
+        }
+        if (a.z) return hipErrorInvalidValue;
         inter_kernel<C, Tout, PRECISE, D><<<groups, 256, lds, a.stream>>>(a, nchains);
         return hipGetLastError();
     }
@@ -1802,17 +2014,38 @@ static hipError_t launch_prefill_t(const PrefillArgs &a) {
 
 template <int C>
 static hipError_t launch_prefill_c(const PrefillArgs &a) {
+    if (a.o_scale) {                    // fp16 outputs with block scales: 64-row chunks, bf16 inputs
+        if constexpr (C == 64) {
+            if (a.in_bf16) return launch_prefill_t<C, __bf16, _Float16, 128>(a);
+        }
+        return hipErrorInvalidValue;
+    }
     if (a.in_bf16)
         return a.out_bf16 ? launch_prefill_t<C, __bf16, __bf16, 128>(a)
                           : launch_prefill_t<C, __bf16, float, 128>(a);
     return a.out_bf16 ? launch_prefill_t<C, float, __bf16, 128>(a) : launch_prefill_t<C, float, float, 128>(a);
 }
 
+// Whether kda_chunk_fwd's inter-chunk kernel can apply the output epilogue
+// itself: 64-row chunks of bf16 inputs at D = 128, and every workgroup of the
+// launch resident at once (one per CU: the two workgroups of a chain wait on
+// each other).
+hipError_t prefill_gate_fusable(const PrefillArgs &a, bool &fusable) {
+    fusable = false;
+    if (a.D != 128 || a.chunk != 64 || !a.in_bf16 || a.stages != 3) return hipSuccess;
+    int cus = 0;
+    const hipError_t e = cu_count(cus);
+    if (e != hipSuccess) return e;
+    const int64_t nchains = (int64_t)a.N * a.H;
+    fusable = 16 * ((nchains + 7) / 8) <= (int64_t)cus;
+    return hipSuccess;
+}
+
 hipError_t launch_prefill(const PrefillArgs &args) {
     PrefillArgs a = args;
     if (a.Hk <= 0) a.Hk = a.H;          // no grouping: one q/k head per value head
     if (a.D == 64) {                    // natively sized kernels: 64-row chunks, bf16 inputs
-        if (a.chunk != 64 || !a.in_bf16) return hipErrorInvalidValue;
+        if (a.chunk != 64 || !a.in_bf16 || a.o_scale) return hipErrorInvalidValue;
         return a.out_bf16 ? launch_prefill_t<64, __bf16, __bf16, 64>(a)
                           : launch_prefill_t<64, __bf16, float, 64>(a);
     }

@@ -425,9 +425,21 @@ def test_chunk_fwd_gated_rejects_before_any_hip_call(kda):
 def test_gated_workspace_size(kda):
     f = kda.lib.kda_chunk_fwd_gated_workspace_size
     base = kda.lib.kda_chunk_fwd_workspace_size(8192, 1, 96, 128, 128, 64, kda.KDA_BF16)
-    assert f(8192, 1, 96, 128, 128, 64, kda.KDA_BF16, kda.KDA_F32) == base
     up = (base + 255) // 256 * 256
-    assert f(8192, 1, 96, 128, 128, 64, kda.KDA_BF16, kda.KDA_BF16) == up + 8192 * 96 * 128 * 4
+    # fused epilogue: the halves' row-sum exchange, one 8-byte word per row of each
+    # chunk slot, head and half; bf16 results of the unfused pass staged in fp16
+    # with a 4-byte scale per 16 features, whichever is larger
+    xchg = (8192 // 64 + 1) * 96 * 128 * 8
+    assert f(8192, 1, 96, 128, 128, 64, kda.KDA_BF16, kda.KDA_F32) == up + xchg
+    assert f(8192, 1, 96, 128, 128, 64, kda.KDA_BF16, kda.KDA_BF16) == \
+        up + 8192 * 96 * (128 * 2 + 8 * 4)
+    b1 = kda.lib.kda_chunk_fwd_workspace_size(64, 64, 2, 128, 128, 64, kda.KDA_BF16)
+    assert f(64, 64, 2, 128, 128, 64, kda.KDA_BF16, kda.KDA_BF16) == \
+        (b1 + 255) // 256 * 256 + (64 // 64 + 64) * 2 * 128 * 8
+    b32 = kda.lib.kda_chunk_fwd_workspace_size(8192, 1, 96, 128, 128, 32, kda.KDA_BF16)
+    assert f(8192, 1, 96, 128, 128, 32, kda.KDA_BF16, kda.KDA_F32) == b32
+    assert f(8192, 1, 96, 128, 128, 32, kda.KDA_BF16, kda.KDA_BF16) == \
+        (b32 + 255) // 256 * 256 + 8192 * 96 * 128 * 4
     assert f(100, 2, 3, 48, 80, 32, kda.KDA_F32, kda.KDA_BF16) > \
         kda.lib.kda_chunk_fwd_workspace_size(100, 2, 3, 48, 80, 32, kda.KDA_F32)
     assert f(8192, 1, 96, 128, 128, 64, kda.KDA_BF16, 7) == 0

@@ -105,3 +105,65 @@ def test_gated_large(kda, o_dtype):
     """The T=8192, H=96 prefill with the epilogue."""
     p = kda_inputs.large()
     check(kda, p, o_dtype, "gated T=8192 H=96 o %s" % o_dtype, seed=1320)
+
+
+# 50 sequences of 3 heads: 150 chains, 304 workgroups of the inter-chunk kernel,
+# more than the 256 CUs hold at once, so the epilogue is not fused in it but runs
+# as a pass over staged outputs
+MANY = [1, 0, 77, 130, 64, 5] + [9, 70, 0, 33] * 11
+
+
+@pytest.mark.parametrize("o_dtype", [None, torch.float32])
+def test_gated_unfused(kda, o_dtype):
+    """A batch with too many sequences for the fused epilogue."""
+    p = kda_inputs.make_prefill(MANY, 3, g_std=2.0, h0_std=0.1, chunk=64, seed=1325)
+    check(kda, p, o_dtype, "gated unfused 50 sequences o %s" % o_dtype, seed=1326)
+
+
+def test_gated_fp16_staging(kda):
+    """bf16 outputs of the natively sized K = V = 128 kernels (64-row chunks,
+    bf16 tokens) when the epilogue is not fused (too many sequences): the
+    chunkwise forward stages o in fp16, each 16-feature block
+    of a row divided by a power of two, and the epilogue multiplies the scale
+    back. Against the prefill's fp32 o followed by the standalone fp32
+    epilogue, element by element within the staging bound: a staged value is
+    off by at most 2^-11 of its block's largest magnitude b, which moves
+    y = x r w sigmoid(z) by at most |w sigmoid(z)| r 2^-11 (b + |x| r m)
+    (m: the row's largest magnitude; the second term is the change of the
+    row's inverse rms r), plus y's own bf16 rounding. Heads scaled by 2^20
+    and 2^-20, one head's first block by 2^12 (a block scale, not a row scale,
+    keeps the other blocks exact to their own magnitude) and a sequence of
+    zeros (outputs exactly 0)."""
+    from helpers import bf16_half_ulp
+    p = kda_inputs.make_prefill(MANY, 3, g_std=2.0, h0_std=0.1, chunk=64, seed=1330)
+    v, h0 = p.v.to(torch.float32), p.h0.clone()
+    for h, f in ((0, 2.0 ** 20), (2, 2.0 ** -20)):
+        v[:, h] *= f
+        h0[:, h] *= f
+    v[:, 1, :16] *= 2.0 ** 12
+    h0[:, 1, :16] *= 2.0 ** 12
+    z0, z1 = int(p.cu_seqlens[4]), int(p.cu_seqlens[5])
+    v[z0:z1] = 0.0
+    h0[4] = 0.0
+    p.v, p.h0 = v.to(torch.bfloat16), h0           # power-of-two scalings: exact in bf16
+    z, w = kda_inputs.make_epilogue((p.T, p.H, 128), token_dtype=torch.bfloat16, seed=1331, D=128)
+    y, _ = run(kda, p, z, w)
+    assert y.dtype == torch.bfloat16
+    o32, _ = run(kda, p, z, w, o_dtype=torch.float32, gated=False)
+    y2 = kda.output_norm_gate(o32, z.to(DEV).to(torch.float32), w.to(DEV), eps=EPS)
+    torch.cuda.synchronize()
+    x = to_np(o32).astype(np.float64)
+    T, H = x.shape[:2]
+    ax = np.abs(x)
+    b = np.repeat(ax.reshape(T, H, 8, 16).max(-1), 16, axis=-1)
+    m = ax.max(-1, keepdims=True)
+    r = 1.0 / np.sqrt((x * x).mean(-1, keepdims=True) + EPS)
+    zs = to_np(z).astype(np.float64)
+    ws = np.abs(to_np(w).astype(np.float64)) / (1.0 + np.exp(-zs))
+    bound = ws * r * 2.0 ** -11 * (b + ax * r * m)
+    yg, yr = to_np(y).astype(np.float64), to_np(y2).astype(np.float64)
+    ex = np.abs(yg - yr) - bf16_half_ulp(yg) - 1e-6 * np.abs(yr)
+    ratio = float(np.max(ex / np.maximum(bound, 1e-300)))
+    print("fp16 staging: max excess over the bound's share %.3f" % ratio, flush=True)
+    assert np.all(ex <= 1.5 * bound)
+    assert np.all(yg[z0:z1] == 0.0)
