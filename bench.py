@@ -319,12 +319,12 @@ def epilogue_timing(kda, o, dsteps, dA, ddt, dstate, dscale, dout, reps=20):
             "decode_step_plain_us": round(ms_plain * 1e3, 2)}
 
 
-def gated_prefill_timing(kda, p, args, h0, o, ht, ws, reps=10):
+def gated_prefill_timing(kda, p, args, h0, o, ht, ws, reps=20):
     """The prefill with the output epilogue (per-head RMS norm + sigmoid gate,
-    kda_chunk_fwd_gated: the epilogue pass enqueued right after the inter-chunk
-    kernel, o still in the memory-side cache), beside the plain prefill and the
-    plain prefill followed by a separate epilogue call: the median of `reps`
-    calls each."""
+    kda_chunk_fwd_gated: at this size applied by the inter-chunk kernel itself),
+    beside the plain prefill and the plain prefill followed by a separate
+    epilogue call (which reads o back from the memory-side cache): the median
+    of `reps` calls each."""
     import torch
     import kda_inputs
     T, H, Dv = o.shape
@@ -344,20 +344,21 @@ def gated_prefill_timing(kda, p, args, h0, o, ht, ws, reps=10):
         plain()
         kda.output_norm_gate(o, z, w, out=y)
 
-    def med(fn):
+    # the three calls alternate, so that clock drift over the run affects each alike
+    fns = (plain, gated, separate)
+    for fn in fns:
         fn()
-        torch.cuda.synchronize()
-        ts = []
-        for _ in range(reps):
+    torch.cuda.synchronize()
+    ts = [[], [], []]
+    for _ in range(reps):
+        for i, fn in enumerate(fns):
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             e0.record()
             fn()
             e1.record()
             torch.cuda.synchronize()
-            ts.append(e0.elapsed_time(e1))
-        return sorted(ts)[len(ts) // 2]
-
-    mp, mg, ms = med(plain), med(gated), med(separate)
+            ts[i].append(e0.elapsed_time(e1))
+    mp, mg, ms = (sorted(t)[len(t) // 2] for t in ts)
     return {"prefill_plain_ms": round(mp, 4), "prefill_gated_ms": round(mg, 4),
             "prefill_then_epilogue_call_ms": round(ms, 4),
             "gated_over_plain": round(mg / mp, 4)}

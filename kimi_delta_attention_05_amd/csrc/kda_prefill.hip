@@ -1103,8 +1103,9 @@ __global__ __launch_bounds__(GATE ? 320 : 256) void inter_kernel(PrefillArgs p, 
     constexpr bool SCALED = std::is_same<Tout, _Float16>::value;
     static_assert(!(SCALED && GATE), "the fused epilogue stores bf16 or fp32");
     // fused epilogue: chunk j's outputs x (O sigma) wait four steps in xa .. xd
-    // (xn: the step's new chunk); the lane's four columns 16 vb + 4 lg + i of
-    // the norm weight
+    // (xn: the step's new chunk; a loop unrolled four times, which would keep
+    // them in place, needs more than the 256 registers); the lane's four
+    // columns 16 vb + 4 lg + i of the norm weight
     typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
     [[maybe_unused]] f32x4 xa[NB], xb[NB], xc[NB], xd[NB], xn[NB], wv = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1334,7 +1335,8 @@ __global__ __launch_bounds__(GATE ? 320 : 256) void inter_kernel(PrefillArgs p, 
             for (int tb = 0; tb < NB; ++tb) {
                 f32x4 y;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) y[i] = xa[tb][i] * ry[tb] * wv[i] * sigmoid_f((float)zy[tb][i]);
+                for (int i = 0; i < 4; ++i)     // sigmoid as 1 / (1 + 2^(-z log2 e)): 0 and 1 at the ends
+                    y[i] = xa[tb][i] * ry[tb] * wv[i] * fast_rcp(1.0f + fast_exp2(-kLog2e * (float)zy[tb][i]));
                 store4<Tout>(16 * tb + lr < Ly ? o + (size_t)jy * o_chunk + tb * o_tb : o_spare, y);
             }
 #pragma unroll
