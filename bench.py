@@ -46,6 +46,7 @@ def source_sha(*names):
 KERNEL_SOURCES = {
     "intra_kernel": ("kda_prefill.hip", "kda_common.h", "kda_internal.h"),
     "inter_kernel": ("kda_prefill.hip", "kda_common.h", "kda_internal.h"),
+    "inter_kernel_gated": ("kda_prefill.hip", "kda_common.h", "kda_internal.h"),
     "decode_step_kernel": ("kda_decode.hip", "kda_common.h", "kda_internal.h"),
     "short_conv_kernel": ("kda_shortconv.hip", "kda_common.h", "kda_internal.h"),
     "norm_gate_kernel": ("kda_epilogue.hip", "kda_common.h", "kda_internal.h"),
@@ -361,7 +362,8 @@ def gated_prefill_timing(kda, p, args, h0, o, ht, ws, reps=20):
     mp, mg, ms = (sorted(t)[len(t) // 2] for t in ts)
     return {"prefill_plain_ms": round(mp, 4), "prefill_gated_ms": round(mg, 4),
             "prefill_then_epilogue_call_ms": round(ms, 4),
-            "gated_over_plain": round(mg / mp, 4)}
+            "gated_over_plain": round(mg / mp, 4),
+            "inter_kernel_gated_traffic": measured_traffic("inter_kernel_gated")}
 
 
 def front_end_timing(kda, qkv, cu, W=4, reps=20):
