@@ -71,8 +71,7 @@ struct PrefillArgs {
     // when z is set (D = 128, 64-row chunks, bf16 inputs, both stages; see
     // prefill_gate_fusable): o receives y = o / sqrt(mean(o^2) + norm_eps) *
     // norm_w * sigmoid(z) per row, z [T, H, 128] bf16, norm_w [128]; xchg: the
-    // halves' row-sum exchange, num_slots * H * 128 words of workspace (zeroed
-    // by the intra-chunk kernel: the epilogue is fused only with both stages)
+    // halves' row-sum exchange, num_slots * H * 128 words of workspace
     const void *z = nullptr;
     const float *norm_w = nullptr;
     float norm_eps = 0.f;

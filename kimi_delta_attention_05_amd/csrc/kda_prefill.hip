@@ -871,7 +871,7 @@ constexpr int kXchgSpin = 1 << 20;
 //              and keep its outputs x = O sigma in registers;
 //   step j + 1 the fifth wave adds up this half's sums and posts them for the
 //              other workgroup (a (sum, tag) word per row in the workspace,
-//              zeroed by the intra-chunk kernel);
+//              zeroed before the launch);
 //   step j + 2 it asks for the other half's sums (posted a step earlier) and
 //              loads the chunk's gate logits;
 //   step j + 3 it forms r = 1 / sqrt(mean(o^2) + eps) per row and leaves r and
@@ -1518,10 +1518,6 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
         }
         const float braw = p.beta_raw[row];
         const float alog = *(const __attribute__((address_space(4))) float *)(p.A_log + h);
-        // with the output epilogue fused into the inter-chunk kernel: this chunk
-        // and head's row-sum exchange words start at zero (stored after the
-        // loads, so that waiting for those does not wait for this store)
-        if (p.xchg != nullptr && bw == 0) ((i32x4 *)(p.xchg + (size_t)ti * 128))[lane] = i32x4{0, 0, 0, 0};
 
 
         // ---- gates and block-local cumulative log-decay ------------------------------
@@ -1946,6 +1942,11 @@ static hipError_t cu_count(int &cus) {
 }
 
 // One flag word per kernel: bit d set once the dynamic-LDS limit is set on device d.
+// Zeroes n 8-byte words (grid-stride).
+__global__ __launch_bounds__(256) void zero_words_kernel(uint64_t *p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0;
+}
+
 static hipError_t set_lds_limit(const void *fn, int lds, std::atomic<uint64_t> &done) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
@@ -1999,9 +2000,9 @@ static hipError_t launch_prefill_t(const PrefillArgs &a) {
                 static std::atomic<uint64_t> lds_g_set{0};
                 e = set_lds_limit((const void *)inter_kernel<C, Tout, PRECISE, D, true>, (int)lds_g, lds_g_set);
                 if (e != hipSuccess) return e;
-                // (the intra-chunk kernel, launched before on this stream, zeroed the
-                // row-sum exchange words)
-                if (!(a.stages & 1)) return hipErrorInvalidValue;
+                const size_t words = (size_t)num_slots(a.T, a.N, C) * a.H * 128;
+                zero_words_kernel<<<(unsigned)((words + 255) / 256 < 4096 ? (words + 255) / 256 : 4096), 256, 0,
+                                    a.stream>>>(a.xchg, words);
                 inter_kernel<C, Tout, PRECISE, D, true><<<groups, 320, lds_g, a.stream>>>(a, nchains);
                 return hipGetLastError();
             }
