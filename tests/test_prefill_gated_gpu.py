@@ -167,3 +167,14 @@ def test_gated_fp16_staging(kda):
     print("fp16 staging: max excess over the bound's share %.3f" % ratio, flush=True)
     assert np.all(ex <= 1.5 * bound)
     assert np.all(yg[z0:z1] == 0.0)
+
+
+@pytest.mark.parametrize("N,H", [(32, 4), (17, 8)])
+def test_gated_fusion_boundary(kda, N, H):
+    """Either side of the fused epilogue's residency limit (128 chains: 32 x 4 is
+    fused, 17 x 8 = 136 is not): both paths against the oracle, with fp32 results
+    also against the prefill to fp32 o followed by the standalone epilogue."""
+    lengths = [(37 * i) % 150 for i in range(N)]
+    p = kda_inputs.make_prefill(lengths, H, g_std=2.0, h0_std=0.1, chunk=64, seed=1340 + N)
+    for o_dtype in (None, torch.float32):
+        check(kda, p, o_dtype, "gated N=%d H=%d o %s" % (N, H, o_dtype), seed=1341)
