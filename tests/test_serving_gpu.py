@@ -146,6 +146,58 @@ def test_graph_capture_prefill(kda, chunk, K, V):
         assert torch.equal(o_g, o_e) and torch.equal(h_g, h_e), rep
 
 
+@pytest.mark.parametrize("o_dtype", [torch.bfloat16, torch.float32])
+def test_graph_capture_prefill_gated(kda, o_dtype):
+    """Capture the gated prefill with the epilogue fused into the inter kernel
+    (the exchange words' fill, intra, inter with the fifth wave) and replay it on
+    new tokens and gate logits; every replay equals an eager call bit for bit
+    (the exchange words are cleared on every replay, so a replay never reads an
+    earlier one's row sums)."""
+    lengths = [300, 0, 211, 64]
+    H = 4
+    p = kda_inputs.make_prefill(lengths, H, h0_std=0.1, chunk=64, seed=71)
+    names = ("q", "k", "v", "g", "beta_raw", "A_log", "dt_bias", "cu_seqlens", "h0")
+    static = {n: getattr(p, n).to(DEV).clone() for n in names}
+    z, w = kda_inputs.make_epilogue((p.T, H, 128), seed=72)
+    static["z"], static["w"] = z.to(DEV), w.to(DEV)
+    ws = kda.Workspace(DEV)
+    y = torch.empty(p.T, H, 128, dtype=o_dtype, device=DEV)
+    ht = torch.empty(len(lengths), H, 128, 128, dtype=torch.float32, device=DEV)
+
+    def call(t, out_y, out_h, wsp):
+        return kda.chunk_fwd(t["q"], t["k"], t["v"], t["g"], t["beta_raw"], t["A_log"],
+                             t["dt_bias"], t["cu_seqlens"], scale=p.scale, chunk_size=64,
+                             initial_state=t["h0"], out=out_y, final_state=out_h, workspace=wsp,
+                             o_dtype=o_dtype, gate=t["z"], norm_weight=t["w"])
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(static, y, ht, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(static, y, ht, ws)
+    torch.cuda.synchronize()
+    ws2 = kda.Workspace(DEV)
+    for rep in range(3):
+        q = kda_inputs.make_prefill(lengths, H, h0_std=0.1, chunk=64, seed=90 + rep)
+        fresh = {n: getattr(q, n).to(DEV) for n in names}
+        z2, w2 = kda_inputs.make_epilogue((p.T, H, 128), seed=95 + rep)
+        fresh["z"], fresh["w"] = z2.to(DEV), w2.to(DEV)
+        for n in fresh:
+            static[n].copy_(fresh[n])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        y_g, h_g = y.clone(), ht.clone()
+        y_e, h_e = call(fresh, None, None, ws2)
+        torch.cuda.synchronize()
+        assert torch.isfinite(y_g.float()).all()
+        assert torch.equal(y_g, y_e) and torch.equal(h_g, h_e), rep
+
+
 # ---- the same serving forms anchored to the fp64 oracle -----------------------
 
 import numpy as np  # noqa: E402
