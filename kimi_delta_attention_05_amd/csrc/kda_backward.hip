@@ -714,8 +714,20 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
                 // dQG = dO S0, dKG = U dS1, dKE = -dR S0 ([t][k] accumulators), dGC = sum_v S0 dS1
                 f32x4 pq[2] = {zero, zero}, pk[2] = {zero, zero}, pe[2] = {zero, zero};
                 float gs[2][4] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+                // dM = lower(dO U^T) (waves 4, 5) and dT = dU R^T (waves 6, 7), each
+                // over 32 of the 64 rows (the final kernel adds the two parts): its
+                // two products interleaved with the others, so that their latency
+                // does not trail the step
+                const bool isM = cw < 2;
+                const int vb0 = 2 * (cw & 1);
+                f32x4 accM = zero;
 #pragma unroll
                 for (int vb = 0; vb < 4; ++vb) {
+                    if (vb & 1) {
+                        const int vm = vb0 + (vb >> 1);
+                        const f32x4 a_ = isM ? dOr[vm] : lds4(SH + LY::DUS + lr * LY::SP + 16 * vm + 4 * lg);
+                        accM = bmm16(a_, lds4(SH + (isM ? LY::US : LY::RS) + lr * LY::SP + 16 * vm + 4 * lg), accM);
+                    }
                     const f32x4 a_u = lds4(SH + LY::US + lr * LY::SP + 16 * vb + 4 * lg);
                     const f32x4 a_dr = lds4(SH + LY::DRS + lr * LY::SP + 16 * vb + 4 * lg);
 #pragma unroll
@@ -751,22 +763,12 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
                     x = __uint_as_float(b2[0]) + __uint_as_float(b2[1]);
                     if (lg == 0) dst[6656 + kcol + 16 * kt + lr] = x;
                 }
-                // dM = lower(dO U^T) (waves 4, 5) and dT = dU R^T (waves 6, 7), each
-                // over 32 of the 64 rows (the final kernel adds the two parts)
                 {
-                    const bool isM = cw < 2;
-                    const int vb0 = 2 * (cw & 1);
-                    f32x4 acc = zero;
-#pragma unroll
-                    for (int vb = vb0; vb < vb0 + 2; ++vb) {
-                        const f32x4 a_ = isM ? dOr[vb] : lds4(SH + LY::DUS + lr * LY::SP + 16 * vb + 4 * lg);
-                        acc = bmm16(a_, lds4(SH + (isM ? LY::US : LY::RS) + lr * LY::SP + 16 * vb + 4 * lg), acc);
-                    }
                     const int off = (isM ? 6144 : 6400) + (cw & 1) * 640;
 #pragma unroll
                     for (int i2 = 0; i2 < 4; ++i2) {
                         const int r = 4 * lg + i2;
-                        dst[off + r * 16 + lr] = (!isM || r >= lr) ? acc[i2] : 0.f;
+                        dst[off + r * 16 + lr] = (!isM || r >= lr) ? accM[i2] : 0.f;
                     }
                 }
             }
