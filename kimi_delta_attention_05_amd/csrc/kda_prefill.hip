@@ -1483,8 +1483,10 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
 
         int n = 0, L = 0;
         int64_t t0 = 0;
-        if (!locate_slot<C>(p.cu_seqlens, p.N, ti / H, n, t0, L)) continue;   // unused slot
-        const int h = (int)(ti % H);
+        // tile = slot * H + head (below 2^31: the launch checks it)
+        const uint32_t slot_u = (uint32_t)ti / (uint32_t)H;
+        if (!locate_slot<C>(p.cu_seqlens, p.N, (int64_t)slot_u, n, t0, L)) continue;   // unused slot
+        const int h = (int)((uint32_t)ti - slot_u * (uint32_t)H);
         unsigned char *rec = p.ws + (size_t)ti * R::BYTES;
 
         // ---- loads: gates first (consumed first), then q, k, v, beta ----------------
@@ -1530,6 +1532,7 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
 #pragma unroll
         for (int c = 0; c < CPL; ++c) sgb[CPL * lane + c] = ga * dtv[c];
         float lam[KS][8];
+        const float lbr = rv ? lb2 : 0.0f;           // rows past the chunk end: lambda = 0
 #pragma unroll
         for (int s = 0; s < KS; ++s)
 #pragma unroll
@@ -1538,7 +1541,7 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const float sg = fast_rcp(1.0f + fast_exp2(fmaf(graw[s][hf][i], ga, gb[i])));
-                    lam[s][4 * hf + i] = rv ? lb2 * sg : 0.0f;
+                    lam[s][4 * hf + i] = lbr * sg;
                 }
             }
         if (lr == 0) {                               // lambda of the block's first row
@@ -1660,17 +1663,18 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
         float KP[KS][8], QP[KS][8], RI[KS][8];
         half8 ke16[KS], v16[KS];
         {
+            // sums of squares two channels at a time on the bf16 dot product
+            // (exact products, fp32 sums)
             float sq = 0.f, sk = 0.f;
+            typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 #pragma unroll
             for (int s = 0; s < KS; ++s)
 #pragma unroll
-                for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const float qx = (float)qraw[s][4 * hf + i], kx = (float)kraw[s][4 * hf + i];
-                        sq = fmaf(qx, qx, sq);
-                        sk = fmaf(kx, kx, sk);
-                    }
+                for (int e = 0; e < 8; e += 2) {
+                    const bf16x2_t q2 = {qraw[s][e], qraw[s][e + 1]}, k2 = {kraw[s][e], kraw[s][e + 1]};
+                    sq = __builtin_amdgcn_fdot2_f32_bf16(q2, q2, sq, false);
+                    sk = __builtin_amdgcn_fdot2_f32_bf16(k2, k2, sk, false);
+                }
             sq += __shfl_xor(sq, 16);
             sq += __shfl_xor(sq, 32);
             sk += __shfl_xor(sk, 16);
@@ -1973,9 +1977,11 @@ static hipError_t launch_prefill_t(const PrefillArgs &a) {
             // register-blocked kernel, two workgroups per CU at a time: one
             // workgroup per tile (a new one starts wherever one finishes, so
             // the two on a CU drift out of phase; persistent workgroups walking
-            // the tiles in step measured 7% slower at T=8192, H=96)
-            const int64_t grid = ntiles < 0x7fffffff ? ntiles : 0x7fffffff;
-            intra64_kernel<Tin, D><<<(unsigned)grid, 256, 0, a.stream>>>(a, ntiles);
+            // the tiles in step measured 7% slower at T=8192, H=96); the kernel
+            // decodes tile indices in 32 bits (a workspace of 2^31 records would
+            // be over 100 TB)
+            if (ntiles > 0x7fffffff) return hipErrorInvalidValue;
+            intra64_kernel<Tin, D><<<(unsigned)ntiles, 256, 0, a.stream>>>(a, ntiles);
         } else {
             // persistent (one per CU): each prefetches its next tile's inputs into LDS
             const int64_t grid = ntiles < (int64_t)cus ? ntiles : (int64_t)cus;
