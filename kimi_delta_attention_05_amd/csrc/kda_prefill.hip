@@ -1583,13 +1583,21 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
                     *(f32x4 *)(sLE + b * D + chan(s, hf)) =
                         f32x4{Lm[s][4 * hf], Lm[s][4 * hf + 1], Lm[s][4 * hf + 2], Lm[s][4 * hf + 3]};
         }
-        float vmax = 0.0f;
+        // largest |v| of the lane on the bf16 bit patterns: with the sign cleared their
+        // unsigned order is the numeric order (two 16-bit lanes per instruction)
+        typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+        u16x2 vm2 = {0, 0};
 #pragma unroll
-        for (int s = 0; s < KS; ++s)
+        for (int s = 0; s < KS; ++s) {
+            typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+            const u32x4v w = __builtin_bit_cast(u32x4v, vraw[s]);
 #pragma unroll
-            for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) vmax = fmaxf(vmax, fabsf((float)vraw[s][4 * hf + i]));
+            for (int i = 0; i < 4; ++i) {
+                const u16x2 x = __builtin_bit_cast(u16x2, w[i] & 0x7fff7fffu);
+                vm2 = __builtin_elementwise_max(vm2, x);
+            }
+        }
+        float vmax = __uint_as_float((uint32_t)(vm2[0] > vm2[1] ? vm2[0] : vm2[1]) << 16);
         vmax = wave_max_nonneg(vmax);
         if (lane == 0) sVmax[b] = vmax;
         lds_barrier();                                                     // B1
@@ -1601,7 +1609,9 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
         //   KF_b = prod of the block totals after b
         //   Pe_b = 2^Lam_15 of block b
         //   X_bc = e^{G_16b - G_16c+15}, c < b
-        {
+        // (specialised on the wave's block b, so that its branches are resolved at compile time)
+        auto factors = [&](auto bc) {
+            constexpr int b = decltype(bc)::value;
             float tot[NB][CPL], l0b[CPL], leb[CPL];
 #pragma unroll
             for (int bb = 0; bb < NB; ++bb) {
@@ -1647,6 +1657,12 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
                 if (b == 0)                          // total decay of the chunk
                     ((float *)(rec + R::GC_OFF))[CPL * lane + c] = fast_exp2(all[c]);
             }
+        };
+        switch (b) {
+        case 0: factors(std::integral_constant<int, 0>{}); break;
+        case 1: factors(std::integral_constant<int, 1>{}); break;
+        case 2: factors(std::integral_constant<int, 2>{}); break;
+        default: factors(std::integral_constant<int, 3>{}); break;
         }
         if (lg == 0) sBeta[r] = rv ? sigmoid_f(braw) : 0.0f;
         const float beta = rv ? sigmoid_f(braw) : 0.0f;
