@@ -341,3 +341,38 @@ def test_contract_packed_8x1024_h96(kda, golden_contract):
     assert {"lengths": lengths, "H": 96} in golden_contract["admitted_shapes"]["packed"]
     p = kda_inputs.packed_8x1024()
     _both_outputs(kda, p, oracle_of(p))
+
+
+# ---- batch-size and length extremes ----------------------------------------------
+
+def _many_lengths():
+    rng = np.random.default_rng(5)
+    return [int(x) if rng.random() > 0.1 else 0 for x in rng.integers(1, 300, size=150)]
+
+
+@pytest.mark.parametrize("dtype,chunk", [(torch.bfloat16, 64), (torch.float32, 32)])
+def test_many_sequences(kda, dtype, chunk):
+    """150 packed sequences of 0 to 299 tokens (more sequences than the inter
+    kernel ranks by length), random initial states; fp32 output under the
+    literal metric."""
+    p = kda_inputs.make_prefill(_many_lengths(), 2, token_dtype=dtype, h0_std=0.1, chunk=chunk,
+                                seed=1501 if dtype == torch.bfloat16 else 1502,
+                                name="150 sequences %s C=%d" % (dtype, chunk))
+    o, ht = run_gpu(kda, p, o_dtype=torch.float32)
+    check(p, o, ht, oracle_of(p), p.name)
+
+
+@pytest.mark.parametrize("T,dtype,gshift", [(65536, torch.bfloat16, 0.0), (65536, torch.bfloat16, -10.0),
+                                            (32768, torch.float32, -10.0)])
+def test_long_sequence(kda, T, dtype, gshift):
+    """One sequence of 32768 or 65536 tokens (512 or 1024 chunk steps of the
+    state), H=2, with the gates as drawn or shifted by -10 so that the state
+    barely decays (lambda of about -2e-4 per token): the state's power-of-two
+    scaling over long chains. fp32 output under the literal metric."""
+    p = kda_inputs.make_prefill([T], 2, token_dtype=dtype, h0_std=0.1, chunk=64,
+                                seed=1503 + int(-gshift) + (T >> 14),
+                                name="T=%d %s gate shift %g" % (T, dtype, gshift))
+    if gshift:
+        p.g = p.g + gshift
+    o, ht = run_gpu(kda, p, o_dtype=torch.float32)
+    check(p, o, ht, oracle_of(p), p.name)
