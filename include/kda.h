@@ -328,8 +328,8 @@ kda_status_t kda_short_conv_slots(const void *x, int64_t x_stride, const float *
  * over 16-token chunks: a forward pass stores the state at every chunk start
  * in the workspace, a reverse pass carries the state adjoint across chunks, and
  * the per-chunk gradients follow from the chunk's operands and the reverse
- * pass's per-chunk sums. Workspace at T = 8192, N = 1, H = 96: 5.1 GB (per
- * 16-token chunk and head: the 64 KiB checkpoint, a 28 KiB operand record and
+ * pass's per-chunk sums. Workspace at T = 8192, N = 1, H = 96: 5.2 GB (per
+ * 16-token chunk and head: the 64 KiB checkpoint, a 30.5 KiB operand record and
  * 8 KiB of the forward's intermediate values).
  *
  * Inputs as for kda_chunk_fwd (q, k, v in in_dtype; g, beta_raw, A_log,

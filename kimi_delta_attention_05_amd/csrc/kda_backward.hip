@@ -30,8 +30,8 @@
 //
 // Five launches over 16-token chunks:
 //   bwd_prep_kernel        one workgroup per (chunk slot, head), chunk-parallel:
-//                          the chunk's operands KE, KG, QG, T, M^T, GC as a
-//                          record in the workspace;
+//                          the chunk's operands KE, KG, QG, T, M^T, GC, X, P as
+//                          a record in the workspace;
 //   bwd_ckpt_kernel        one workgroup per (sequence, head, half of the state
 //                          rows), chunk-serial: the forward over the chunks (fp32
 //                          MFMA), storing the state at every chunk start;
@@ -243,8 +243,9 @@ __device__ __forceinline__ void operands_phase2(float *sm, int tid) {
 
 // A = strict_lower(diag(b) P) with P = KE KI^T, from one wave (lane holds
 // P[4 lg + i][lr]); the product's strictly lower part also kept in P_out if set.
+// Returns the lane's accumulator (P[4 lg + i][lr], unmasked).
 template <typename LY>
-__device__ __forceinline__ void chunk_A(float *sm, int lane, float *P_out) {
+__device__ __forceinline__ f32x4 chunk_A(float *sm, int lane, float *P_out) {
     const int lr = lane & 15, lg = lane >> 4;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -256,6 +257,7 @@ __device__ __forceinline__ void chunk_A(float *sm, int lane, float *P_out) {
         sm[LY::A + r * kSP + lr] = (r > lr) ? sm[LY::B + r] * acc[i] : 0.f;
         if (P_out) P_out[r * kSP + lr] = (r > lr) ? acc[i] : 0.f;
     }
+    return acc;
 }
 
 // Column jc of X = (I + A)^-1 by forward substitution (A strictly lower), in
@@ -293,11 +295,15 @@ __device__ __forceinline__ bool slot_chunk(const int64_t *cu, int N, int64_t slo
 // offsets in floats, [16][128] tiles at pitch 132, [16][16] at pitch 20):
 //   KE, KG, T = X diag(b), GC        (the checkpoint pass copies these, 19 KiB)
 //   QG, MT = lower(QG KI^T)^T, B     (the reverse pass copies all of it, 28 KiB)
+// and after those, read only by the finalize kernel:
+//   X = (I + A)^-1, P = strict_lower(KE KI^T)   ([16][16] each at pitch 20)
 struct OpRec {
     static constexpr int KE = 0, KG = KE + kTile, T = KG + kTile, GC = T + kSmall;
     static constexpr int QG = GC + kHeadDim, MT = QG + kTile, B = MT + kSmall;
     static constexpr int END = 7168;                     // 28 blocks of 1 KiB
     static constexpr int CKPT_BLOCKS = 19;               // blocks holding KE, KG, T, GC
+    static constexpr int X = END, P = X + kSmall;
+    static constexpr int STRIDE = P + kSmall;            // floats per record
 };
 static_assert(OpRec::B + 16 <= OpRec::END && OpRec::GC + kHeadDim <= 256 * OpRec::CKPT_BLOCKS,
               "record layout");
@@ -308,12 +314,14 @@ struct PrepLds {
     static constexpr int KE = OpRec::KE, KG = OpRec::KG, T = OpRec::T, GC = OpRec::GC;
     static constexpr int QG = OpRec::QG, MT = OpRec::MT, B = OpRec::B;
     static constexpr int KI = OpRec::END, A = KI + kTile, END = A + kSmall;
+    static constexpr int XS = KI, PS = XS + kSmall;       // X, P once KI is no longer read
     static constexpr size_t BYTES = (size_t)END * 4;
 };
 
 // One workgroup per (chunk slot, value head), chunk-parallel: the chunk's
 // transforms and decays (operands_phase1/2), A and M (waves 0 and 1, MFMA),
-// X = (I + A)^-1 (wave 0), T = X diag(b), then the record written out.
+// X = (I + A)^-1 (wave 0), T = X diag(b), then the record written out, with X
+// and P (staged in the KI tile, which is no longer read by then) after it.
 template <typename Tin>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(
     const Tin *__restrict__ q, const Tin *__restrict__ k, const float *__restrict__ g,
@@ -344,7 +352,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
     lds_barrier();
     operands_phase2<LY, true, false>(sm, tid);
     lds_barrier();
-    if (wave == 0) chunk_A<LY>(sm, lane, nullptr);
+    f32x4 pacc = {0.f, 0.f, 0.f, 0.f};
+    if (wave == 0) pacc = chunk_A<LY>(sm, lane, nullptr);
     if (wave == 1) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -363,13 +372,22 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(
         if (lg == 0) {
             const float bj = sm[LY::B + lr];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) sm[LY::T + i * kSP + lr] = x[i] * bj;
+            for (int i = 0; i < 16; ++i) {
+                sm[LY::T + i * kSP + lr] = x[i] * bj;
+                sm[LY::XS + i * kSP + lr] = x[i];
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * lg + i;
+            sm[LY::PS + r * kSP + lr] = (r > lr) ? pacc[i] : 0.f;
         }
     }
     lds_barrier();
-    f32x4 *dst = (f32x4 *)(ops + ((size_t)slot * H + h) * OpRec::END);
+    f32x4 *dst = (f32x4 *)(ops + ((size_t)slot * H + h) * OpRec::STRIDE);
 #pragma unroll
     for (int r = 0; r < OpRec::END / 1024; ++r) dst[tid + 256 * r] = lds4(sm + 4 * (tid + 256 * r));
+    if (tid < 2 * kSmall / 4) dst[OpRec::X / 4 + tid] = lds4(sm + LY::XS + 4 * tid);
 }
 
 // DMA copy of blocks [0, nblk) of a record into LDS: wave w copies the 1 KiB
@@ -423,8 +441,8 @@ __global__ __launch_bounds__(256) void bwd_ckpt_kernel(
     const int64_t s0 = cu[n], s1 = cu[n + 1];
     const int64_t nch = (s1 - s0 + kCk - 1) / kCk;
     const int64_t slot0 = s0 / kCk + n;
-    const float *rec0 = ops + ((size_t)slot0 * H + h) * OpRec::END;
-    const size_t rec_step = (size_t)H * OpRec::END;
+    const float *rec0 = ops + ((size_t)slot0 * H + h) * OpRec::STRIDE;
+    const size_t rec_step = (size_t)H * OpRec::STRIDE;
 
     f32x4 Sa[8];
     if (h0) {
@@ -597,8 +615,8 @@ __global__ __launch_bounds__(512) void bwd_chunk_kernel(
     const int64_t s0 = cu[n], s1 = cu[n + 1];
     const int64_t nch = (s1 - s0 + kCk - 1) / kCk;
     const int64_t slot0 = s0 / kCk + n;
-    const float *rec0 = ops + ((size_t)slot0 * H + h) * OpRec::END;
-    const size_t rec_step = (size_t)H * OpRec::END;
+    const float *rec0 = ops + ((size_t)slot0 * H + h) * OpRec::STRIDE;
+    const size_t rec_step = (size_t)H * OpRec::STRIDE;
     const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
     // chain waves: dSa[kb] = dS[vbase + lr][16 kb + 4 lg + i], the adjoint of the
@@ -805,7 +823,7 @@ struct FinalLds {
     static constexpr int KE = 0, QG = KE + kTile, KG = QG + kTile, KI = KG + kTile;
     static constexpr int XI = KI + kTile, XE = XI + kTile, GAM = XE + kTile, XQ = GAM + kTile;
     static constexpr int DG = XE, EK = XQ, SP = EK;
-    static constexpr int A = XQ + kTile, P = A + kSmall, X = P + kSmall, DM = X + kSmall;
+    static constexpr int P = XQ + kTile, X = P + kSmall, DM = X + kSmall;
     static constexpr int DT = DM + kSmall, Y = DT + kSmall, DA = Y + kSmall;
     static constexpr int GC = DA + kSmall, DGC = GC + kHeadDim, B = DGC + kHeadDim;
     static constexpr int END = B + 16;
@@ -841,8 +859,9 @@ __global__ __launch_bounds__(256) void bwd_param_kernel(const float *__restrict_
 // One workgroup per (chunk slot, q/k head): the value heads that share the
 // q/k head (grouped value heads) run one after the other and add their dqh and
 // dkh before the normalisations' chains. Per value head: the operands again
-// (the same code as bwd_chunk_kernel, so the same P and X), the two halves'
-// partials added, the small-matrix adjoints (dX, dA, dP, dbeta), then per
+// (the same code as the operand kernel), X and P from the record that kernel
+// wrote (the values it formed, so the same as the passes between used), the
+// two halves' partials added, the small-matrix adjoints (dX, dA, dP, dbeta), then per
 // token row dKE, dQG, dKI, dkh, dqh and the log-decay adjoint, its reverse sum
 // over the chunk (a thread per channel), and the gate's chain.
 template <typename Tin>
@@ -850,8 +869,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const Tin *__restrict__ q, const Tin *__restrict__ k, const float *__restrict__ g,
     const float *__restrict__ beta_raw, const float *__restrict__ A_log,
     const float *__restrict__ dt_bias, float scale, float lb, const int64_t *__restrict__ cu, int N,
-    int H, int Hk, const float *__restrict__ part, float *__restrict__ dq, float *__restrict__ dk,
-    float *__restrict__ dg, float *__restrict__ dbeta, float *__restrict__ pp)
+    int H, int Hk, const float *__restrict__ part, const float *__restrict__ ops,
+    float *__restrict__ dq, float *__restrict__ dk, float *__restrict__ dg, float *__restrict__ dbeta,
+    float *__restrict__ pp)
 {
     using LY = FinalLds;
     extern __shared__ __align__(16) float sm[];
@@ -911,6 +931,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         const float dMv = (p0[6144 + tid] + p0[6784 + tid]) + (p1[6144 + tid] + p1[6784 + tid]);
         const float dTv = (p0[6400 + tid] + p0[7040 + tid]) + (p1[6400 + tid] + p1[7040 + tid]);
         const float dGCv = tid < kHeadDim ? p0[6656 + tid] + p1[6656 + tid] : 0.f;
+        // X and P of the chunk, as the operand kernel formed them (threads 0 .. 79: X,
+        // 80 .. 159: P, four values each)
+        f32x4 xp = {0.f, 0.f, 0.f, 0.f};
+        if (tid < 2 * kSmall / 4)
+            xp = ((const f32x4 *)(ops + ((size_t)slot * H + h) * OpRec::STRIDE + OpRec::X))[tid];
 
         // the token rows are kept (tk) for the gate chain below and for the dq, dk
         // chains after the loop, instead of being read again
@@ -922,14 +947,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         sm[LY::DM + gid * kSP + j] = dMv;
         sm[LY::DT + gid * kSP + j] = dTv;
         if (tid < kHeadDim) sm[LY::DGC + tid] = dGCv;
-        if (wave == 0) chunk_A<LY>(sm, lane, sm + LY::P);
-        lds_barrier();
-        if (wave == 0 && lane < 16) {
-            float x[16];
-            inverse_column(sm + LY::A, lane, x);
-#pragma unroll
-            for (int i = 0; i < 16; ++i) sm[LY::X + i * kSP + lane] = x[i];
-        }
+        if (tid < 2 * kSmall / 4)
+            *(f32x4 *)(sm + (tid < kSmall / 4 ? LY::X + 4 * tid : LY::P + 4 * (tid - kSmall / 4))) = xp;
         lds_barrier();
         // Y = dX X^T with dX = dT diag(b)
         {
@@ -1136,7 +1155,7 @@ hipError_t launch_backward_t(const BackwardArgs &a) {
     if (e != hipSuccess) return e;
     bwd_chunk_final_kernel<Tin><<<dim3((unsigned)slots, (unsigned)Hk), 256, FinalLds::BYTES, a.stream>>>(
         (const Tin *)a.q, (const Tin *)a.k, a.g, a.beta_raw, a.A_log, a.dt_bias, a.scale,
-        a.lower_bound, a.cu, a.N, a.H, Hk, a.ckpt, a.dq, a.dk, a.dg, a.dbeta, a.pp);
+        a.lower_bound, a.cu, a.N, a.H, Hk, a.ckpt, a.ops, a.dq, a.dk, a.dg, a.dbeta, a.pp);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     bwd_param_kernel<<<(unsigned)a.H, 256, 0, a.stream>>>(a.pp, slots, a.H, a.dA_log, a.ddt_bias);
@@ -1152,7 +1171,7 @@ BackwardLayout backward_layout(int64_t T, int N, int H) {
     // (the reverse pass's partial records reuse the checkpoint rows)
     l.ckpt_bytes = up(slots * H * kHeadDim * kHeadDim * 4);
     l.pp_bytes = up(slots * H * (kHeadDim + 1) * 4);
-    l.ops_bytes = up(slots * H * OpRec::END * 4);
+    l.ops_bytes = up(slots * H * OpRec::STRIDE * 4);
     l.rr_bytes = up(slots * H * 2 * 4 * 256 * 4);
     l.total = l.ckpt_bytes + l.pp_bytes + l.ops_bytes + l.rr_bytes;
     return l;

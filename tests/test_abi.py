@@ -235,9 +235,10 @@ def test_backward_rejects(kda, kw, status):
 def test_backward_workspace_size(kda):
     # per (16-token chunk slot, head): a 64 KiB state checkpoint (whose rows
     # then hold the reverse pass's partial sums), the chunk's operand record
-    # (7168 floats), R of the chunk (8 KiB), 129 parameter sums
+    # (7168 floats, then X and P: 2 x 320), R of the chunk (8 KiB), 129
+    # parameter sums
     slots = 8192 // 16 + 1
-    per = 65536 + 7168 * 4 + 8192 + 129 * 4
+    per = 65536 + (7168 + 640) * 4 + 8192 + 129 * 4
     a = kda.backward_workspace_size(8192, 1, 96)
     assert slots * 96 * per <= a < slots * 96 * per + 1024
     assert a % 256 == 0
