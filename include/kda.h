@@ -108,11 +108,13 @@ size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t num_seqs,
  * A zero-length sequence writes no output rows and copies its initial state
  * (or zeros) to its final state. total_tokens = 0 is allowed.
  *
- * Head sizes below 128 (FlashKDA issue page, "Proposed scope": arbitrary
+ * Other head sizes (FlashKDA issue page, "Proposed scope": arbitrary
  * key/value dimensions): K and V may each be 1..128, with q, k, g [T, H, K],
  * v, o [T, H, V], dt_bias [H, K] and states [num_seqs, H, V, K]. K = V = 64
- * with chunk_size 64 and bf16 inputs runs on kernels sized for 64. Other
- * sizes run the 128-wide kernels on copies padded with zeros to 128 key
+ * with chunk_size 64 and bf16 inputs runs on kernels sized for 64, and
+ * K = V = 256 with chunk_size 64 and bf16 inputs (the one size above 128 taken
+ * here; kda_recurrent_fwd takes any K, V up to 256) on kernels sized for 256.
+ * Other sizes run the 128-wide kernels on copies padded with zeros to 128 key
  * channels and 128 value rows, which kda_chunk_fwd_workspace_size includes in
  * the workspace: padded channels and rows stay exactly zero through the
  * recurrence, so the result is that of the K x V problem.

@@ -102,12 +102,12 @@ kda_status_t hip_fail(hipError_t e, const char *where) {
     return fail(KDA_ERR_HIP, std::string(where) + ": " + hipGetErrorString(e));
 }
 
-// The head size the chunkwise kernels run at directly: 128, and 64 for K = V =
-// 64 with 64-row chunks of bf16 inputs (kernels sized for it); 0 when the
-// inputs are zero-padded to 128 instead.
+// The head size the chunkwise kernels run at directly: 128, and 64 or 256 for
+// K = V = 64 or 256 with 64-row chunks of bf16 inputs (kernels sized for them);
+// 0 when the inputs are zero-padded to 128 instead.
 int native_head_size(int32_t K, int32_t V, int32_t chunk_size, kda_dtype_t in_dtype) {
     if (K == 128 && V == 128) return 128;
-    if (K == 64 && V == 64 && chunk_size == 64 && in_dtype == KDA_BF16) return 64;
+    if (K == V && (K == 64 || K == 256) && chunk_size == 64 && in_dtype == KDA_BF16) return K;
     return 0;
 }
 
@@ -267,8 +267,10 @@ size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t num_seqs, int3
         fail(KDA_ERR_INVALID_ARG, "need total_tokens >= 0, num_seqs >= 1, 1 <= H <= 65536");
         return 0;
     }
-    if (K < 1 || K > 128 || V < 1 || V > 128) {
-        fail(KDA_ERR_UNSUPPORTED, "K and V must lie in [1, 128]");
+    const bool big = native_head_size(K, V, chunk_size, in_dtype) == 256;
+    if (!big && (K < 1 || K > 128 || V < 1 || V > 128)) {
+        fail(KDA_ERR_UNSUPPORTED, "K and V must lie in [1, 128], or K = V = 256 with chunk_size 64 "
+                                  "and bf16 inputs");
         return 0;
     }
     if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) {
@@ -280,6 +282,8 @@ size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t num_seqs, int3
     g_last_error.clear();
     if (native_head_size(K, V, chunk_size, in_dtype) == 64)     // records sized for 64
         return (size_t)slots * (size_t)H * kda::record_bytes(64, false, 64) + 256;
+    if (big)                                                    // records sized for 256
+        return (size_t)slots * (size_t)H * kda::record_bytes(64, false, 256) + 256;
     const size_t rec = kda::record_bytes(chunk_size, in_dtype == KDA_F32);
     const size_t base = (size_t)slots * (size_t)H * rec + 256;
     if (K == 128 && V == 128) return base;
@@ -329,7 +333,9 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
                               float norm_eps = 0.f) {
     if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 1");
     if (total_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens must be >= 0");
-    kda_status_t st = check_common(H, K, V, scale, lower_bound, in_dtype, o_dtype, true);
+    const bool big = native_head_size(K, V, chunk_size, in_dtype) == 256;   // K = V = 256, sized kernels
+    kda_status_t st = check_common(H, big ? 128 : K, big ? 128 : V, scale, lower_bound, in_dtype,
+                                   o_dtype, true);
     if (st != KDA_OK) return st;
     st = check_groups(H, H_qk);
     if (st != KDA_OK) return st;

@@ -44,6 +44,7 @@ constexpr int KP = kHeadDim + 4;   // LDS row pitch (floats) of [C][128] tiles
 
 size_t record_bytes(int chunk, bool precise, int D) {
     if (D == 64) return (chunk == 64 && !precise) ? Record<64, false, 64>::BYTES : 0;
+    if (D == 256) return (chunk == 64 && !precise) ? Record<64, false, 256>::BYTES : 0;
     if (D != 128) return 0;
     switch (chunk) {
         case 16: return precise ? Record<16, true>::BYTES : Record<16, false>::BYTES;
@@ -896,8 +897,8 @@ __global__ __launch_bounds__(GATE ? 320 : 256) void inter_kernel(PrefillArgs p, 
 
     // workgroup -> (chain, half); both halves of a chain land on the same XCD
     const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
-    int chain = (HALVES == 2 ? (local >> 1) : local) * 8 + xcd;
-    const int vg = HALVES == 2 ? (local & 1) : 0;
+    int chain = (local / HALVES) * 8 + xcd;
+    const int vg = local % HALVES;
     if (chain >= nchains) return;
     const int H = p.H;
     int n = chain / H;
@@ -1386,7 +1387,7 @@ __global__ __launch_bounds__(GATE ? 320 : 256) void inter_kernel(PrefillArgs p, 
 // and kg^T products go through MFMA with an identity factor (exact for fp16).
 // =============================================================================
 template <int D>
-struct IntraRB {                                          // D: head size (K = V), 128 or 64
+struct IntraRB {                                          // D: head size (K = V), 256, 128 or 64
     static constexpr int KS = D / 32;                     // 32-channel k-steps
     static constexpr int AP = 68;                         // sA / sT row pitch (floats)
     static constexpr int TP = 72;                         // KE^T / V^T row pitch (halves)
@@ -1413,7 +1414,7 @@ struct IntraRB {                                          // D: head size (K = V
 typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
 
 template <typename Tin, int D = 128>
-__global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t ntiles)
+__global__ __launch_bounds__(256, D == 256 ? 1 : 2) void intra64_kernel(PrefillArgs p, int64_t ntiles)
 {
     constexpr int C = 64, NB = 4, CS = 2;
     constexpr int KS = D / 32, KT = D / 16;   // 32-channel k-steps; 16-channel tiles (= value blocks)
@@ -1500,7 +1501,11 @@ __global__ __launch_bounds__(256, 2) void intra64_kernel(PrefillArgs p, int64_t 
 #pragma unroll
             for (int hf = 0; hf < 2; ++hf) graw[s][hf] = *(const f32x4 *)(gr + chan(s, hf));
         float dtv[CPL];                              // dt_bias of channels CPL lane .. + CPL - 1
-        if constexpr (CPL == 2) {
+        if constexpr (CPL == 4) {
+            const f32x4 d4 = *(const f32x4 *)(p.dt_bias + (size_t)h * D + 4 * lane);
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) dtv[c] = d4[c];
+        } else if constexpr (CPL == 2) {
             const float2 d2 = *(const float2 *)(p.dt_bias + (size_t)h * D + 2 * lane);
             dtv[0] = d2.x;
             dtv[CPL - 1] = d2.y;
@@ -1981,7 +1986,8 @@ static hipError_t set_lds_limit(const void *fn, int lds, std::atomic<uint64_t> &
 template <int C, typename Tin, typename Tout, int D>
 static hipError_t launch_prefill_t(const PrefillArgs &a) {
     constexpr bool PRECISE = std::is_same<Tin, float>::value;
-    static_assert(D == 128 || (C == 64 && !PRECISE), "head size 64: 64-row chunks of bf16 inputs");
+    static_assert(D == 128 || (C == 64 && !PRECISE), "head sizes 64 and 256: 64-row chunks of bf16 inputs");
+    static_assert(IntraRB<D>::BYTES <= 160 * 1024, "intra-chunk LDS");
     const int64_t slots = num_slots(a.T, a.N, C);
     if ((a.stages & 1) && slots > 0) {
         // workgroups walk the tiles blockIdx.x, blockIdx.x + gridDim.x, ...
@@ -2072,6 +2078,11 @@ hipError_t launch_prefill(const PrefillArgs &args) {
         if (a.chunk != 64 || !a.in_bf16 || a.o_scale) return hipErrorInvalidValue;
         return a.out_bf16 ? launch_prefill_t<64, __bf16, __bf16, 64>(a)
                           : launch_prefill_t<64, __bf16, float, 64>(a);
+    }
+    if (a.D == 256) {                   // natively sized kernels: 64-row chunks, bf16 inputs
+        if (a.chunk != 64 || !a.in_bf16 || a.o_scale || a.z) return hipErrorInvalidValue;
+        return a.out_bf16 ? launch_prefill_t<64, __bf16, __bf16, 256>(a)
+                          : launch_prefill_t<64, __bf16, float, 256>(a);
     }
     if (a.D != 128) return hipErrorInvalidValue;
     switch (a.chunk) {

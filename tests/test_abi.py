@@ -53,6 +53,7 @@ def chunk_call(kda, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(K=129), 2), (dict(V=256), 2), (dict(K=0), 2), (dict(V=0), 2), (dict(C=48), 2),
+    (dict(K=256, V=256), 2), (dict(K=256, V=256, C=64), 2), (dict(K=256, V=128, C=64, dt=1), 2),
     (dict(C=128), 2), (dict(dt=7), 2),
     (dict(odt=3), 2),
     (dict(N=0), 1), (dict(T=-1), 1), (dict(H=0), 1), (dict(scale=0.0), 1),
@@ -463,3 +464,19 @@ def test_workspace_size_native_64(kda):
     assert rec64 == 3 * 64 * 64 * 2 + 8 * 1024 + 64 * 4 + 16 + 64 * 64 * 2
     assert kda.workspace_size(T, N, H, 32, torch.bfloat16, K=64, V=64) > n128
     assert kda.workspace_size(T, N, H, 64, torch.float32, K=64, V=64) > n128
+
+
+def test_workspace_size_native_256(kda):
+    """K = V = 256 with 64-row chunks of bf16 inputs runs on kernels sized for 256:
+    one record per chunk slot and head, no padded copies; other dtypes and chunk
+    sizes are rejected (the token-by-token forward takes them)."""
+    import torch
+    T, N, H = 1000, 3, 4
+    slots = T // 64 + N
+    n = kda.workspace_size(T, N, H, 64, torch.bfloat16, K=256, V=256)
+    assert (n - 256) % (slots * H) == 0
+    # W, qg, kg (64 x 256 fp16 each), M (8 fragments), decay (256 fp32), scale, Ub (64 x 256)
+    assert (n - 256) // (slots * H) == 3 * 64 * 256 * 2 + 8 * 1024 + 256 * 4 + 16 + 64 * 256 * 2
+    for C, dt in ((32, torch.bfloat16), (64, torch.float32)):
+        with pytest.raises(ValueError):
+            kda.workspace_size(T, N, H, C, dt, K=256, V=256)
