@@ -518,14 +518,15 @@ def general_timing(kda, dev, T=8192, H=96, reps=3):
     """The forward for head sizes other than 128 (kda_recurrent_fwd, token by
     token in fp32), measured beside the step and not part of it: the prefill
     workload's tokens and heads (one sequence, bf16 tokens, fp32 initial states)
-    at K = V = 64 and 256, and at K = V = 128 for comparison with the chunkwise
-    path. Arithmetic: 7 flops per state element and token (decay, the two dot
-    products, the update) against the fp32 vector peak. At K = V = 64 and 256
-    the chunkwise prefill (kernels sized for them) is timed too."""
+    at K = V = 64, 192 and 256, and at K = V = 128 for comparison with the
+    chunkwise path. Arithmetic: 7 flops per state element and token (decay, the
+    two dot products, the update) against the fp32 vector peak. At K = V = 64,
+    192 and 256 the chunkwise prefill is timed too (kernels sized for 64 and 256;
+    192 on the 256-wide kernels over copies padded with zeros)."""
     import torch
     import kda_inputs
     out = {}
-    for Kd in (64, 128, 256):
+    for Kd in (64, 128, 192, 256):
         p = kda_inputs.make_prefill([T], H, token_dtype=torch.bfloat16, g_std=2.0, h0_std=0.1,
                                     seed=2300 + Kd, K=Kd, V=Kd)
         args = [x.to(dev) for x in (p.q, p.k, p.v, p.g, p.beta_raw, p.A_log, p.dt_bias,
@@ -553,7 +554,7 @@ def general_timing(kda, dev, T=8192, H=96, reps=3):
                                            "peak": FP32_VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
                                            "frac": round(tf / FP32_VALU_PEAK_TFLOPS, 4)}}
         if Kd != D:
-            # the same problem on the chunkwise prefill (kernels sized for K = V = 64, 256)
+            # the same problem on the chunkwise prefill
             ws = kda.Workspace(dev)
 
             def run_c():

@@ -109,13 +109,14 @@ size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t num_seqs,
  * (or zeros) to its final state. total_tokens = 0 is allowed.
  *
  * Other head sizes (FlashKDA issue page, "Proposed scope": arbitrary
- * key/value dimensions): K and V may each be 1..128, with q, k, g [T, H, K],
+ * key/value dimensions): K and V may each be 1..128, and 1..256 with
+ * chunk_size 64 and bf16 inputs (otherwise KDA_ERR_UNSUPPORTED;
+ * kda_recurrent_fwd takes any K, V up to 256), with q, k, g [T, H, K],
  * v, o [T, H, V], dt_bias [H, K] and states [num_seqs, H, V, K]. K = V = 64
- * with chunk_size 64 and bf16 inputs runs on kernels sized for 64, and
- * K = V = 256 with chunk_size 64 and bf16 inputs (the one size above 128 taken
- * here; kda_recurrent_fwd takes any K, V up to 256) on kernels sized for 256.
- * Other sizes run the 128-wide kernels on copies padded with zeros to 128 key
- * channels and 128 value rows, which kda_chunk_fwd_workspace_size includes in
+ * and K = V = 256 with chunk_size 64 and bf16 inputs run on kernels sized
+ * for them. Other sizes run the 128-wide kernels (K, V <= 128) or the
+ * 256-wide ones (K or V above 128) on copies padded with zeros to that many
+ * key channels and value rows, which kda_chunk_fwd_workspace_size includes in
  * the workspace: padded channels and rows stay exactly zero through the
  * recurrence, so the result is that of the K x V problem.
  */

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <initializer_list>
@@ -111,19 +112,26 @@ int native_head_size(int32_t K, int32_t V, int32_t chunk_size, kda_dtype_t in_dt
     return 0;
 }
 
-// Other head sizes below 128 run on the chunkwise kernels over copies of the inputs
-// padded with zeros to 128 key channels and 128 value rows, kept in the
-// workspace after the per-chunk records: padded key channels have k = q = 0
-// and padded value rows v = 0 and a zero initial state, so they stay exactly
-// zero through the recurrence and change neither the norms nor any dot
-// product of the real channels; the outputs and final states are the real
-// rows and channels of the padded results.
+// Other head sizes run on the chunkwise kernels over copies of the inputs padded
+// with zeros to D key channels and D value rows, D = 128 when K, V <= 128 and
+// D = 256 above (64-row chunks of bf16 inputs only), kept in the workspace
+// after the per-chunk records: padded key channels have k = q = 0 and padded
+// value rows v = 0 and a zero initial state, so they stay exactly zero through
+// the recurrence and change neither the norms nor any dot product of the real
+// channels; the outputs and final states are the real rows and channels of the
+// padded results. 0: no chunkwise form for these sizes.
+int padded_head_size(int32_t K, int32_t V, int32_t chunk_size, kda_dtype_t in_dtype) {
+    if (K < 1 || V < 1 || K > 256 || V > 256) return 0;
+    if (K <= 128 && V <= 128) return 128;
+    return (chunk_size == 64 && in_dtype == KDA_BF16) ? 256 : 0;
+}
 struct PadLayout {
     size_t q, k, v, g, dtb, state, o, end;
 };
-PadLayout pad_layout(int64_t T, int64_t N, int64_t H, kda_dtype_t in_dtype, size_t base) {
+PadLayout pad_layout(int64_t T, int64_t N, int64_t H, kda_dtype_t in_dtype, size_t base,
+                     size_t D) {
     auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-    const size_t esz = in_dtype == KDA_BF16 ? 2 : 4, D = kda::kHeadDimHost;
+    const size_t esz = in_dtype == KDA_BF16 ? 2 : 4;
     PadLayout L;
     L.q = up(base);
     L.k = up(L.q + (size_t)T * H * D * esz);
@@ -267,27 +275,27 @@ size_t kda_chunk_fwd_workspace_size(int64_t total_tokens, int32_t num_seqs, int3
         fail(KDA_ERR_INVALID_ARG, "need total_tokens >= 0, num_seqs >= 1, 1 <= H <= 65536");
         return 0;
     }
-    const bool big = native_head_size(K, V, chunk_size, in_dtype) == 256;
-    if (!big && (K < 1 || K > 128 || V < 1 || V > 128)) {
-        fail(KDA_ERR_UNSUPPORTED, "K and V must lie in [1, 128], or K = V = 256 with chunk_size 64 "
-                                  "and bf16 inputs");
-        return 0;
-    }
     if (chunk_size != 16 && chunk_size != 32 && chunk_size != 64) {
         fail(KDA_ERR_UNSUPPORTED, "chunk_size must be 16, 32 or 64");
         return 0;
     }
     if (!valid_dtype(in_dtype)) { fail(KDA_ERR_UNSUPPORTED, "unknown input dtype"); return 0; }
+    const int native = native_head_size(K, V, chunk_size, in_dtype);
+    const int D = native ? native : padded_head_size(K, V, chunk_size, in_dtype);
+    if (D == 0) {
+        fail(KDA_ERR_UNSUPPORTED, "K and V must lie in [1, 128], or in [1, 256] with chunk_size 64 "
+                                  "and bf16 inputs");
+        return 0;
+    }
     const int64_t slots = kda::num_slots(total_tokens, num_seqs, chunk_size);
     g_last_error.clear();
-    if (native_head_size(K, V, chunk_size, in_dtype) == 64)     // records sized for 64
-        return (size_t)slots * (size_t)H * kda::record_bytes(64, false, 64) + 256;
-    if (big)                                                    // records sized for 256
-        return (size_t)slots * (size_t)H * kda::record_bytes(64, false, 256) + 256;
-    const size_t rec = kda::record_bytes(chunk_size, in_dtype == KDA_F32);
+    // records sized for the head size the kernels run at (64 and 256: 64-row
+    // chunks of bf16 inputs)
+    const size_t rec = D == 128 ? kda::record_bytes(chunk_size, in_dtype == KDA_F32)
+                                : kda::record_bytes(64, false, D);
     const size_t base = (size_t)slots * (size_t)H * rec + 256;
-    if (K == 128 && V == 128) return base;
-    return pad_layout(total_tokens, num_seqs, H, in_dtype, base).end;
+    if (native) return base;
+    return pad_layout(total_tokens, num_seqs, H, in_dtype, base, (size_t)D).end;
 }
 
 size_t kda_chunk_fwd_gated_workspace_size(int64_t total_tokens, int32_t num_seqs, int32_t H,
@@ -333,9 +341,15 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
                               float norm_eps = 0.f) {
     if (num_seqs < 1) return fail(KDA_ERR_INVALID_ARG, "num_seqs must be >= 1");
     if (total_tokens < 0) return fail(KDA_ERR_INVALID_ARG, "total_tokens must be >= 0");
-    const bool big = native_head_size(K, V, chunk_size, in_dtype) == 256;   // K = V = 256, sized kernels
-    kda_status_t st = check_common(H, big ? 128 : K, big ? 128 : V, scale, lower_bound, in_dtype,
-                                   o_dtype, true);
+    // the head size the kernels run at: K = V natively, or both padded to it
+    const int native = native_head_size(K, V, chunk_size, in_dtype);
+    const int D = native ? native : padded_head_size(K, V, chunk_size, in_dtype);
+    if (D == 0 && K >= 1 && V >= 1 && K <= 256 && V <= 256)
+        return fail(KDA_ERR_UNSUPPORTED, "K or V above 128 needs chunk_size 64 and bf16 inputs (got K=" +
+                                             std::to_string(K) + ", V=" + std::to_string(V) +
+                                             "; kda_recurrent_fwd takes any K, V up to 256)");
+    kda_status_t st = check_common(H, D == 256 ? std::min(K, 128) : K, D == 256 ? std::min(V, 128) : V,
+                                   scale, lower_bound, in_dtype, o_dtype, true);
     if (st != KDA_OK) return st;
     st = check_groups(H, H_qk);
     if (st != KDA_OK) return st;
@@ -412,7 +426,6 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
     // are still in the memory-side cache then), reading them unrounded: fp32
     // results in place, bf16 results staged in the workspace after the part
     // kda_chunk_fwd uses, so that y is rounded once.
-    const int native = native_head_size(K, V, chunk_size, in_dtype);
     unsigned char *const extra =
         z ? (unsigned char *)workspace +
                 ((kda_chunk_fwd_workspace_size(total_tokens, num_seqs, H, K, V, chunk_size,
@@ -459,13 +472,14 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
         return ok();
     }
 
-    // below 128: the same kernels on zero-padded copies in the workspace
-    const int64_t D = kda::kHeadDimHost;
+    // other sizes: the kernels for D on zero-padded copies in the workspace
+    a.D = D;
     const int esz = in_dtype == KDA_BF16 ? 2 : 4, osz = o_dtype == KDA_BF16 ? 2 : 4;
     const PadLayout P = pad_layout(total_tokens, num_seqs, H,
                                    in_dtype, kda_chunk_fwd_workspace_size(total_tokens, num_seqs, H,
-                                                                          128, 128, chunk_size,
-                                                                          in_dtype));
+                                                                          D, D, chunk_size,
+                                                                          in_dtype),
+                                   (size_t)D);
     unsigned char *ws = (unsigned char *)workspace;
     hipStream_t s = a.stream;
     const int64_t TH = total_tokens * H, THk = total_tokens * H_qk, NH = (int64_t)num_seqs * H;
@@ -481,7 +495,7 @@ kda_status_t chunk_fwd_stages(int stages, const char *name,
         pad(g, K, 1, ws + P.g, D, 1, TH, 4);
         pad(dt_bias, K, 1, ws + P.dtb, D, 1, H, 4);
     }
-    if ((stages & 2) && initial_state)                 // value rows widened to 128 as well
+    if ((stages & 2) && initial_state)                 // value rows widened to D as well
         pad(initial_state, K, V, ws + P.state, D, D, NH * D, 4);
     if (e != hipSuccess) return hip_fail(e, name);
     a.q = ws + P.q; a.k = ws + P.k; a.v = ws + P.v; a.g = (const float *)(ws + P.g);

@@ -64,7 +64,7 @@ struct PrefillArgs {
     unsigned char *ws;
     hipStream_t stream;
     int stages;          // bit 0: intra-chunk kernel, bit 1: inter-chunk kernel
-    int D = 128;         // head size K = V: 128, or 64 (64-row chunks of bf16 inputs only)
+    int D = 128;         // head size K = V: 128, or 64 or 256 (64-row chunks of bf16 inputs only)
     // when set (D = 128, 64-row chunks, bf16 inputs): o is fp16, each row's 16-value
     // block divided by the power of two in o_scale [T, H, D / 16]
     float *o_scale = nullptr;

@@ -53,7 +53,8 @@ def chunk_call(kda, **kw):
 
 @pytest.mark.parametrize("kw,status", [
     (dict(K=129), 2), (dict(V=256), 2), (dict(K=0), 2), (dict(V=0), 2), (dict(C=48), 2),
-    (dict(K=256, V=256), 2), (dict(K=256, V=256, C=64), 2), (dict(K=256, V=128, C=64, dt=1), 2),
+    (dict(K=256, V=256), 2), (dict(K=256, V=256, C=64), 2), (dict(K=257, V=128, C=64, dt=1), 2),
+    (dict(K=200, V=64, C=32, dt=1), 2), (dict(K=64, V=129, C=64), 2),
     (dict(C=128), 2), (dict(dt=7), 2),
     (dict(odt=3), 2),
     (dict(N=0), 1), (dict(T=-1), 1), (dict(H=0), 1), (dict(scale=0.0), 1),
@@ -301,16 +302,17 @@ def test_recurrent_fwd_rejects(kda, kw, status):
 
 def test_workspace_size_below_128(kda):
     # head sizes below 128 add zero-padded copies (q, k, v, g, dt_bias, states, o)
-    # after the records; 129 and 0 are rejected
+    # after the records; 0 and 257 are rejected, and 129 where the 256-wide kernels
+    # do not run (chunk_size 32)
     import torch
     T, N, H, C = 1000, 3, 4, 64
     base = kda.workspace_size(T, N, H, C, torch.bfloat16)
     padded = kda.workspace_size(T, N, H, C, torch.bfloat16, K=64, V=48)
     assert padded >= base + T * H * 128 * (3 * 2 + 4 + 4) + N * H * 128 * 128 * 4 + H * 128 * 4
     assert padded == kda.workspace_size(T, N, H, C, torch.bfloat16, K=1, V=1)
-    for K, V in ((129, 64), (64, 0)):
+    for K, V, Cx in ((129, 64, 32), (64, 0, C), (257, 64, C)):
         with pytest.raises(ValueError):
-            kda.workspace_size(T, N, H, C, torch.bfloat16, K=K, V=V)
+            kda.workspace_size(T, N, H, Cx, torch.bfloat16, K=K, V=V)
 
 
 def test_backward_workspace_size_below_128(kda):
@@ -445,7 +447,8 @@ def test_gated_workspace_size(kda):
     assert f(100, 2, 3, 48, 80, 32, kda.KDA_F32, kda.KDA_BF16) > \
         kda.lib.kda_chunk_fwd_workspace_size(100, 2, 3, 48, 80, 32, kda.KDA_F32)
     assert f(8192, 1, 96, 128, 128, 64, kda.KDA_BF16, 7) == 0
-    assert f(8192, 1, 96, 129, 128, 64, kda.KDA_BF16, kda.KDA_BF16) == 0
+    assert f(8192, 1, 96, 257, 128, 64, kda.KDA_BF16, kda.KDA_BF16) == 0
+    assert f(8192, 1, 96, 129, 128, 32, kda.KDA_BF16, kda.KDA_BF16) == 0
 
 
 def test_workspace_size_native_64(kda):
@@ -480,3 +483,22 @@ def test_workspace_size_native_256(kda):
     for C, dt in ((32, torch.bfloat16), (64, torch.float32)):
         with pytest.raises(ValueError):
             kda.workspace_size(T, N, H, C, dt, K=256, V=256)
+
+
+@pytest.mark.parametrize("K,V", [(192, 192), (129, 256), (256, 40), (1, 200)])
+def test_workspace_size_padded_256(kda, K, V):
+    """K or V above 128 (up to 256; 64-row chunks of bf16 inputs): the 256-wide
+    kernels' records, then the copies padded to 256 (q, k, v in bf16, g fp32,
+    dt_bias, states and the fp32 output staging), each 256-byte aligned."""
+    import torch
+    T, N, H = 1000, 3, 4
+    up = lambda x: (x + 255) // 256 * 256
+    rec = kda.workspace_size(T, N, H, 64, torch.bfloat16, K=256, V=256)
+    tok = T * H * 256
+    want = up(rec)
+    for nbytes in (tok * 2, tok * 2, tok * 2, tok * 4, H * 256 * 4, N * H * 256 * 256 * 4, tok * 4):
+        want = up(want + nbytes)
+    assert kda.workspace_size(T, N, H, 64, torch.bfloat16, K=K, V=V) == want
+    for C, dt in ((32, torch.bfloat16), (64, torch.float32)):
+        with pytest.raises(ValueError):
+            kda.workspace_size(T, N, H, C, dt, K=K, V=V)
