@@ -190,11 +190,14 @@ def chunk_fwd(q, k, v, g, beta_raw, A_log, dt_bias, cu_seqlens, *, scale: float 
               norm_eps: float = NORM_EPS) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """Chunkwise KDA prefill over packed sequences (libkda kda_chunk_fwd).
 
-    q, k: [T, H_qk, 128] and v: [T, H, 128], bf16 or fp32 (same dtype); H_qk < H
-    (a divisor) selects grouped value heads (kda_chunk_fwd_grouped); g: [T, H, 128] fp32;
-    beta_raw: [T, H] fp32; A_log: [H] fp32; dt_bias: [H, 128] fp32;
-    cu_seqlens: [N+1] int64 on the GPU; initial_state: [N, H, 128, 128] fp32 or None.
-    Returns (o [T, H, 128] in o_dtype (default: q's dtype), final_state or None).
+    q, k: [T, H_qk, K] and v: [T, H, V], bf16 or fp32 (same dtype); H_qk < H
+    (a divisor) selects grouped value heads (kda_chunk_fwd_grouped); g: [T, H, K] fp32;
+    beta_raw: [T, H] fp32; A_log: [H] fp32; dt_bias: [H, K] fp32;
+    cu_seqlens: [N+1] int64 on the GPU; initial_state: [N, H, V, K] fp32 or None.
+    Returns (o [T, H, V] in o_dtype (default: q's dtype), final_state or None).
+    Head sizes: K = V = 128; any 1 <= K, V <= 128; and 1 <= K, V <= 256 with
+    chunk_size 64 and bf16 inputs (the library rejects others with ValueError;
+    recurrent_fwd takes them).
     stage: None runs both kernels; "intra" / "inter" run one stage (kda_chunk_fwd_intra /
     kda_chunk_fwd_inter), which must share the same workspace and arguments.
     With `gate` (logits [T, H, V] in q's dtype) and `norm_weight` ([V] fp32) the output
