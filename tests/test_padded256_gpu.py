@@ -124,3 +124,44 @@ def test_padded256_large(kda):
     p = make([2048], 8, 192, 192, seed=1660, name="T=2048 H=8 K=V=192")
     o, ht = run(kda, p, torch.float32)
     check(o, ht, oracle_of(p), "padded 256 T=2048 H=8 K=V=192")
+
+
+def test_padded256_stages_split(kda):
+    """The two stage entry points (intra, then inter on the same workspace) give the
+    one-call result bit for bit at K = 200, V = 144."""
+    p = make([150, 97, 1], 2, 200, 144, seed=1670)
+    d = prefill_to_device(p, DEV)
+    args = (d["q"], d["k"], d["v"], d["g"], d["beta_raw"], d["A_log"], d["dt_bias"],
+            d["cu_seqlens"])
+    o, ht = kda.chunk_fwd(*args, scale=p.scale, chunk_size=64, initial_state=d["h0"])
+    ws = kda.Workspace(DEV)
+    o2 = torch.empty_like(o)
+    h2 = torch.empty_like(ht)
+    for stage in ("intra", "inter"):
+        kda.chunk_fwd(*args, scale=p.scale, chunk_size=64, initial_state=d["h0"], out=o2,
+                      final_state=h2, workspace=ws, stage=stage)
+    torch.cuda.synchronize()
+    assert torch.equal(o, o2) and torch.equal(ht, h2)
+
+
+@pytest.mark.parametrize("o_dtype", [None, torch.float32])
+@pytest.mark.parametrize("Kd", [192, 256])
+def test_full_size_sampled_heads(kda, Kd, o_dtype):
+    """The head-size leg bench.py times beside the step, at its size (T = 8192,
+    H = 96, K = V = 192 over padded copies and 256 natively; bf16 outputs as timed,
+    and fp32 outputs for the literal metric), checked on three sampled heads: heads
+    are independent, so the oracle runs on those heads' inputs alone."""
+    p = kda_inputs.make_prefill([8192], 96, token_dtype=torch.bfloat16, g_std=2.0, h0_std=0.1,
+                                seed=2300 + Kd, K=Kd, V=Kd)
+    d = prefill_to_device(p, DEV)
+    o, ht = kda.chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta_raw"], d["A_log"],
+                          d["dt_bias"], d["cu_seqlens"], scale=p.scale, chunk_size=64,
+                          initial_state=d["h0"], o_dtype=o_dtype)
+    torch.cuda.synchronize()
+    heads = [0, 37, 95]
+    o_s, ht_s = o[:, heads].cpu(), ht[:, heads].cpu()
+    del o, ht, d
+    ref = oracle.kda_recurrent(p.q[:, heads], p.k[:, heads], p.v[:, heads], p.g[:, heads],
+                               p.beta_raw[:, heads], p.A_log[heads], p.dt_bias[heads],
+                               p.cu_seqlens, scale=p.scale, h0=p.h0[:, heads])
+    check(o_s, ht_s, ref, "T=8192 H=96 K=V=%d o %s, heads %s" % (Kd, o_dtype, heads))
