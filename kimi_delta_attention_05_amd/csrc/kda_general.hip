@@ -195,7 +195,9 @@ hipError_t launch_general_t(const GeneralArgs &a) {
     if (ne <= 1)      recurrent_fwd_kernel<Tin, Tout, 1><<<grid, 256, 0, a.stream>>>(a);
     else if (ne <= 2) recurrent_fwd_kernel<Tin, Tout, 2><<<grid, 256, 0, a.stream>>>(a);
     else if (ne <= 4) recurrent_fwd_kernel<Tin, Tout, 4><<<grid, 256, 0, a.stream>>>(a);
+    else if (ne <= 6) recurrent_fwd_kernel<Tin, Tout, 6><<<grid, 256, 0, a.stream>>>(a);
     else if (ne <= 8) recurrent_fwd_kernel<Tin, Tout, 8><<<grid, 256, 0, a.stream>>>(a);
+    else if (ne <= 12) recurrent_fwd_kernel<Tin, Tout, 12><<<grid, 256, 0, a.stream>>>(a);
     else              recurrent_fwd_kernel<Tin, Tout, 16><<<grid, 256, 0, a.stream>>>(a);
     return hipGetLastError();
 }

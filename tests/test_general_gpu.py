@@ -54,7 +54,7 @@ def ref(p, h0=True, Hqk=None):
 
 
 @pytest.mark.parametrize("K,V", [(64, 64), (32, 96), (256, 48), (7, 5), (100, 130), (16, 256),
-                                 (1, 1)])
+                                 (1, 1), (96, 40), (150, 200), (192, 72)])
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16])
 def test_general_parity(kda, K, V, dtype):
     p = kda_inputs.make_prefill([17, 33, 5, 40], 3, token_dtype=dtype, h0_std=0.1, seed=K * 7 + V,
